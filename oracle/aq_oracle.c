@@ -1,0 +1,458 @@
+/*
+ * aq_oracle.c -- CPU reference ("oracle") for group-wise affine weight-only
+ * quantization and the matmul that consumes the packed form.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is used by the test-suite, by the
+ * smoke check and by the benchmark's CPU-baseline leg.  Nothing on the
+ * product path links, loads or calls it; it shares no code, header, table
+ * or helper with the HIP library.  It is deliberately plain and slow:
+ * every rounding decision is taken by exact comparisons in binary64, and
+ * every result follows the definitions below step by step.
+ *
+ * Sources (web pages; cited by title and section):
+ *  [MLXQ]  "Quantization" (metalworking, MLX notes): opening paragraph
+ *          (groups of 32/64/128 along a row, one scale + one bias +
+ *          2-8 bit codes), "Mechanics" (w ~= codes*scale + bias per group).
+ *  [QMLX]  "Quantizing a Model for MLX", section "What MLX quantization
+ *          stores" (contiguous groups, scale and offset chosen per group,
+ *          integers packed several to a machine word, fp16 scale and fp16
+ *          bias, 4.5 bits/weight at G=64, 4 bits).
+ *  [GPTQ]  "mlx-gptq", section "How it works" (the round-to-nearest grid
+ *          spans each group's min-max range).
+ *  [T10]   "Tutorial 10: Quantization", section 3 "Packing Multiple
+ *          Weights into One Word" (codes extracted with right shifts by
+ *          multiples of `bits` and a (1<<bits)-1 mask, i.e. least
+ *          significant bits first; dequantize = values*scales + biases in
+ *          float32, then cast), section 4 (container shapes
+ *          [out_features, in_features/group_size]), section 5 "Approach 1:
+ *          Dequantize Then Multiply" (y = x @ W^T on the dequantized W).
+ *
+ * Readings taken where the pages are silent (each is repeated in the
+ * design notes):
+ *  R1  bias = the group minimum rounded DOWN to fp16, so the bias never
+ *      exceeds a group member; scale = the smallest non-negative fp16 for
+ *      which the top grid point bias + (2^b-1)*scale reaches the group
+ *      maximum (i.e. the quotient (max-bias)/(2^b-1) rounded UP to fp16).
+ *  R2  code = index of the nearest grid point bias + q*scale,
+ *      q in [0, 2^b-1]; an exact tie goes to the even q.  scale == 0
+ *      (constant group) gives q = 0.  A group minimum of -0 is taken as +0.
+ *  R3  packing is one least-significant-bit-first bitstream per row: code
+ *      k of a row occupies bits [k*b, k*b+b) of the row, bit i of the
+ *      stream being bit (i mod 32) of little-endian uint32 word i/32.  For
+ *      b in {2,4,8} this is exactly the shift/mask decoder of [T10] s.3;
+ *      for b=3 eight codes fill three bytes.
+ *  R4  dequantize follows [T10] s.3 operation order: q*scale + bias
+ *      evaluated in binary32 (q*scale is exact, so only the add rounds),
+ *      then a round-to-nearest-even cast to the output type.
+ *  R5  matmul reference: y[m,n] = sum_k x[m,k] * w^[n,k] with w^ the exact
+ *      value q*scale + bias, products and sums in binary64; the companion
+ *      A[m,n] = sum_k |x[m,k] * w^[n,k]| scales the tolerance.
+ *  R6  gather (MoE): y[t,j,:] = x[t,:] @ W_{ids[t,j]}^T, one output per
+ *      (token, slot), no routing-weight combine.
+ *
+ * Exactness of the binary64 comparisons used below.  Every finite fp16
+ * value is an integer multiple of 2^-24 of magnitude < 2^16; q*s with
+ * q <= 255 is a multiple of 2^-24 below 2^24; (q+1/2)*s is a multiple of
+ * 2^-25 below 2^25.  Hence b + q*s and b + (q+1/2)*s are multiples of
+ * 2^-25 below 2^26 and fit in 51 significant bits: binary64 holds them
+ * exactly, and comparing them with a binary32 weight (also exact in
+ * binary64) is an exact comparison of real numbers.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define OR_OK 0
+#define OR_ERR_ARG (-1)
+#define OR_ERR_UNSUPPORTED (-2)
+#define OR_ERR_RANGE (-5)
+#define OR_ERR_INDEX (-6)
+
+/* output type tags (same meaning as the library's, defined independently) */
+#define OR_F32 0
+#define OR_F16 1
+#define OR_BF16 2
+
+#define HALF_MAX_FINITE_MAG 0x7BFFu /* 65504 */
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* ---------------------------------------------------------------------
+ * IEEE-754 binary16 and bfloat16, from their definitions.
+ * ------------------------------------------------------------------- */
+
+/* value of a binary16 bit pattern: 1 sign, 5 exponent (bias 15), 10
+ * fraction bits; exponent 0 = subnormal (fraction * 2^-24). */
+double oracle_half_to_double(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 31;
+  int f = h & 1023;
+  double v;
+  if (e == 0)
+    v = ldexp((double)f, -24);
+  else if (e == 31)
+    v = f ? NAN : INFINITY;
+  else
+    v = ldexp((double)(1024 + f), e - 25);
+  return sign ? -v : v;
+}
+
+/* value of a bfloat16 bit pattern: the upper half of a binary32. */
+double oracle_bf16_to_double(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* Non-negative binary16 magnitudes 0x0000..0x7BFF are ordered like their
+ * patterns, so the searches below are bisections over patterns. */
+
+/* largest finite fp16 <= x.  Returns OR_ERR_RANGE if x < -65504. */
+static int half_round_down(double x, uint16_t *out) {
+  if (!(x == x)) return OR_ERR_RANGE;
+  if (x >= 0.0) { /* -0.0 lands here too and becomes +0 */
+    /* largest p in [0, 0x7BFF] with value(p) <= x */
+    uint32_t lo = 0, hi = HALF_MAX_FINITE_MAG;
+    while (lo < hi) {
+      uint32_t mid = (lo + hi + 1) / 2;
+      if (oracle_half_to_double((uint16_t)mid) <= x) lo = mid; else hi = mid - 1;
+    }
+    *out = (uint16_t)lo;
+    return OR_OK;
+  }
+  /* x < 0: smallest magnitude p with value(p) >= -x, returned negated */
+  double mag = -x;
+  if (mag > oracle_half_to_double(HALF_MAX_FINITE_MAG)) return OR_ERR_RANGE;
+  uint32_t lo = 1, hi = HALF_MAX_FINITE_MAG;
+  while (lo < hi) {
+    uint32_t mid = (lo + hi) / 2;
+    if (oracle_half_to_double((uint16_t)mid) >= mag) hi = mid; else lo = mid + 1;
+  }
+  *out = (uint16_t)(0x8000u | lo);
+  return OR_OK;
+}
+
+/* Round-to-nearest-even of a finite double to binary16 (overflow to inf
+ * at and above 65520, the midpoint past the largest finite value). */
+uint16_t oracle_double_to_half_rne(double x) {
+  uint16_t sign = (x < 0 || (x == 0 && signbit(x))) ? 0x8000u : 0;
+  double mag = fabs(x);
+  if (mag >= 65520.0) return sign | 0x7C00u;
+  /* p = largest pattern with value(p) <= mag */
+  uint32_t lo = 0, hi = HALF_MAX_FINITE_MAG;
+  while (lo < hi) {
+    uint32_t mid = (lo + hi + 1) / 2;
+    if (oracle_half_to_double((uint16_t)mid) <= mag) lo = mid; else hi = mid - 1;
+  }
+  double below = oracle_half_to_double((uint16_t)lo);
+  if (below == mag || lo == 0x7C00u) return sign | (uint16_t)lo;
+  double above = (lo + 1 == 0x7C00u) ? 65536.0 : oracle_half_to_double((uint16_t)(lo + 1));
+  double d_lo = mag - below, d_hi = above - mag; /* exact: all on a fine grid */
+  uint32_t p;
+  if (d_lo < d_hi) p = lo;
+  else if (d_hi < d_lo) p = lo + 1;
+  else p = (lo & 1u) ? lo + 1 : lo; /* tie: even pattern */
+  return sign | (uint16_t)p;
+}
+
+/* Round-to-nearest-even of a binary32 value to bfloat16.  The two
+ * candidates are the binary32 values with the low 16 bits cleared (toward
+ * zero) and the next bfloat16 magnitude; past the largest finite bfloat16
+ * the next magnitude is 2^128 (infinity), as IEEE overflow rounding has it. */
+uint16_t oracle_float_to_bf16_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  if ((u & 0x7F800000u) == 0x7F800000u) /* inf stays inf, nan stays a quiet nan */
+    return (uint16_t)((u >> 16) | ((u & 0x007FFFFFu) ? 0x40u : 0));
+  uint32_t down = u & 0xFFFF0000u;
+  uint32_t up = down + 0x10000u;
+  float fd;
+  memcpy(&fd, &down, sizeof fd);
+  double vd = fabs((double)fd), vu;
+  if ((up & 0x7F800000u) == 0x7F800000u) {
+    vu = ldexp(1.0, 128);
+  } else {
+    float fu;
+    memcpy(&fu, &up, sizeof fu);
+    vu = fabs((double)fu);
+  }
+  double mag = fabs((double)f);
+  double dd = mag - vd, du = vu - mag; /* exact in binary64 */
+  if (dd < du) return (uint16_t)(down >> 16);
+  if (du < dd) return (uint16_t)(up >> 16);
+  return (uint16_t)(((down >> 16) & 1u) ? (up >> 16) : (down >> 16));
+}
+
+/* ---------------------------------------------------------------------
+ * Format arithmetic ([QMLX] "What MLX quantization stores"): per group of
+ * G weights, G*b bits of codes plus a 16-bit scale and a 16-bit bias.
+ * ------------------------------------------------------------------- */
+int64_t oracle_packed_words_per_row(int64_t K, int bits) { return K * bits / 32; }
+
+int64_t oracle_qweight_bytes(int64_t N, int64_t K, int group_size, int bits) {
+  return N * K * bits / 8 + N * (K / group_size) * 4;
+}
+
+static int check_shape(int64_t N, int64_t K, int G, int bits) {
+  if (N < 0 || K < 0) return OR_ERR_ARG;
+  if (G != 32 && G != 64 && G != 128) return OR_ERR_ARG;
+  if (bits < 2 || bits > 8) return OR_ERR_ARG;
+  if (K % G) return OR_ERR_ARG;
+  return OR_OK;
+}
+
+/* ---------------------------------------------------------------------
+ * Bitstream packing (reading R3), one bit at a time.
+ * ------------------------------------------------------------------- */
+static void put_code(uint32_t *row, int64_t k, int bits, uint32_t q) {
+  for (int i = 0; i < bits; ++i) {
+    int64_t pos = k * bits + i;
+    if ((q >> i) & 1u) row[pos / 32] |= (1u << (pos % 32));
+  }
+}
+
+static uint32_t get_code(const uint32_t *row, int64_t k, int bits) {
+  uint32_t q = 0;
+  for (int i = 0; i < bits; ++i) {
+    int64_t pos = k * bits + i;
+    q |= ((row[pos / 32] >> (pos % 32)) & 1u) << i;
+  }
+  return q;
+}
+
+/* pack an [N, K] array of codes (one per uint8) into [N, K*b/32] words */
+int oracle_pack(const uint8_t *q, int64_t N, int64_t K, int bits, uint32_t *codes) {
+  if (bits < 2 || bits > 8 || (K * bits) % 32) return OR_ERR_ARG;
+  int64_t wpr = K * bits / 32;
+  memset(codes, 0, (size_t)(N * wpr) * sizeof(uint32_t));
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) {
+      if (q[n * K + k] >> bits) return OR_ERR_RANGE;
+      put_code(codes + n * wpr, k, bits, q[n * K + k]);
+    }
+  return OR_OK;
+}
+
+int oracle_unpack(const uint32_t *codes, int64_t N, int64_t K, int bits, uint8_t *q) {
+  if (bits < 2 || bits > 8 || (K * bits) % 32) return OR_ERR_ARG;
+  int64_t wpr = K * bits / 32;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) q[n * K + k] = (uint8_t)get_code(codes + n * wpr, k, bits);
+  return OR_OK;
+}
+
+/* ---------------------------------------------------------------------
+ * Quantize one group (readings R1, R2).
+ * ------------------------------------------------------------------- */
+
+/* scale: smallest fp16 s >= 0 with bias + L*s >= hi (exact test). */
+static int group_scale(double bias, double hi, int L, uint16_t *s_out) {
+  if (bias >= hi) { *s_out = 0; return OR_OK; }
+  if (bias + L * oracle_half_to_double(HALF_MAX_FINITE_MAG) < hi) return OR_ERR_RANGE;
+  uint32_t lo = 0, up = HALF_MAX_FINITE_MAG;
+  while (lo < up) {
+    uint32_t mid = (lo + up) / 2;
+    if (bias + L * oracle_half_to_double((uint16_t)mid) >= hi) up = mid; else lo = mid + 1;
+  }
+  *s_out = (uint16_t)lo;
+  return OR_OK;
+}
+
+/* code: nearest grid index.  The grid points b + q*s increase with q, so
+ * the nearest one is the number of midpoints b + (j+1/2)*s (j = 0..L-1)
+ * lying strictly below w; found by bisection.  If w sits exactly on a
+ * midpoint between j and j+1, the even one of the two is taken. */
+static uint32_t group_code(double w, double b, double s, int L) {
+  if (s == 0.0) return 0;
+  int lo = 0, hi = L; /* answer = count of j in [0,L) with mid_j < w */
+  while (lo < hi) {
+    int j = (lo + hi) / 2;
+    double mid = b + (j + 0.5) * s;
+    if (mid < w) lo = j + 1; else hi = j;
+  }
+  uint32_t q = (uint32_t)lo;
+  if (q < (uint32_t)L && b + (q + 0.5) * s == w && (q & 1u)) q += 1;
+  return q;
+}
+
+/* Quantize W fp32 [N, K] row-major into codes [N, K*b/32] uint32, scales
+ * and biases [N, K/G] fp16 bits.  Returns OR_ERR_RANGE for a non-finite
+ * weight or a group whose bias/scale leave the fp16 range. */
+int oracle_quantize(const float *w, int64_t N, int64_t K, int G, int bits,
+                    uint32_t *codes, uint16_t *scales, uint16_t *biases) {
+  int st = check_shape(N, K, G, bits);
+  if (st) return st;
+  const int L = (1 << bits) - 1;
+  const int64_t wpr = K * bits / 32, ng = K / G;
+  int err = OR_OK;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    uint32_t *row = codes + n * wpr;
+    memset(row, 0, (size_t)wpr * sizeof(uint32_t));
+    for (int64_t g = 0; g < ng; ++g) {
+      const float *grp = w + n * K + g * G;
+      double lo = INFINITY, hi = -INFINITY;
+      int bad = 0;
+      for (int i = 0; i < G; ++i) {
+        double v = (double)grp[i];
+        if (!isfinite(v)) bad = 1;
+        if (v < lo) lo = v;
+        if (v > hi) hi = v;
+      }
+      uint16_t b16 = 0, s16 = 0;
+      if (!bad && half_round_down(lo, &b16) != OR_OK) bad = 1;
+      double b = oracle_half_to_double(b16);
+      if (!bad && group_scale(b, hi, L, &s16) != OR_OK) bad = 1;
+      if (bad) {
+#pragma omp critical
+        err = OR_ERR_RANGE;
+        continue;
+      }
+      double s = oracle_half_to_double(s16);
+      scales[n * ng + g] = s16;
+      biases[n * ng + g] = b16;
+      for (int i = 0; i < G; ++i)
+        put_code(row, g * G + i, bits, group_code((double)grp[i], b, s, L));
+    }
+  }
+  return err;
+}
+
+/* ---------------------------------------------------------------------
+ * Dequantize ([MLXQ] "Mechanics", [T10] s.3 and s.7; reading R4).
+ * ------------------------------------------------------------------- */
+
+/* exact dequantized values w^ = q*s + b as binary64, [N, K] */
+int oracle_dequantize_exact(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                            int64_t N, int64_t K, int G, int bits, double *out) {
+  int st = check_shape(N, K, G, bits);
+  if (st) return st;
+  const int64_t wpr = K * bits / 32, ng = K / G;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) {
+      double s = oracle_half_to_double(scales[n * ng + k / G]);
+      double b = oracle_half_to_double(biases[n * ng + k / G]);
+      out[n * K + k] = (double)get_code(codes + n * wpr, k, bits) * s + b;
+    }
+  return OR_OK;
+}
+
+/* dequantize to fp32 / fp16 / bf16 in the pages' order: binary32 result
+ * of q*s + b, then a round-to-nearest-even cast. */
+int oracle_dequantize(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                      int64_t N, int64_t K, int G, int bits, int out_dtype, void *out) {
+  int st = check_shape(N, K, G, bits);
+  if (st) return st;
+  if (out_dtype != OR_F32 && out_dtype != OR_F16 && out_dtype != OR_BF16) return OR_ERR_ARG;
+  const int64_t wpr = K * bits / 32, ng = K / G;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) {
+      double s = oracle_half_to_double(scales[n * ng + k / G]);
+      double b = oracle_half_to_double(biases[n * ng + k / G]);
+      /* q*s is exact in binary32; the binary32 sum rounds once, which is
+       * the binary64 exact value rounded to binary32 */
+      float v32 = (float)((double)get_code(codes + n * wpr, k, bits) * s + b);
+      if (out_dtype == OR_F32)
+        ((float *)out)[n * K + k] = v32;
+      else if (out_dtype == OR_F16)
+        ((uint16_t *)out)[n * K + k] = oracle_double_to_half_rne((double)v32);
+      else
+        ((uint16_t *)out)[n * K + k] = oracle_float_to_bf16_rne(v32);
+    }
+  return OR_OK;
+}
+
+/* ---------------------------------------------------------------------
+ * Matmul reference ([T10] s.5 Approach 1: dequantize then multiply;
+ * reading R5).  x holds the exact activation values as binary64.
+ * Only the output columns listed in `cols` (nc of them) are computed, so
+ * large shapes can be checked on a sample; y and A are [M, nc].
+ * ------------------------------------------------------------------- */
+int oracle_matmul_cols(const double *x, int64_t M, const uint32_t *codes, const uint16_t *scales,
+                       const uint16_t *biases, int64_t N, int64_t K, int G, int bits,
+                       const int64_t *cols, int64_t nc, double *y, double *A) {
+  int st = check_shape(N, K, G, bits);
+  if (st) return st;
+  for (int64_t c = 0; c < nc; ++c)
+    if (cols[c] < 0 || cols[c] >= N) return OR_ERR_INDEX;
+  const int64_t wpr = K * bits / 32, ng = K / G;
+  int err = OR_OK;
+#pragma omp parallel
+  {
+    double *wrow = (double *)malloc((size_t)(K > 0 ? K : 1) * sizeof(double));
+    if (!wrow) {
+#pragma omp critical
+      err = OR_ERR_ARG;
+    } else {
+#pragma omp for schedule(static)
+      for (int64_t c = 0; c < nc; ++c) {
+        int64_t n = cols[c];
+        /* dequantize row n on use */
+        for (int64_t k = 0; k < K; ++k) {
+          double s = oracle_half_to_double(scales[n * ng + k / G]);
+          double b = oracle_half_to_double(biases[n * ng + k / G]);
+          wrow[k] = (double)get_code(codes + n * wpr, k, bits) * s + b;
+        }
+        for (int64_t m = 0; m < M; ++m) {
+          double acc = 0.0, mag = 0.0;
+          for (int64_t k = 0; k < K; ++k) {
+            double p = x[m * K + k] * wrow[k];
+            acc += p;
+            mag += fabs(p);
+          }
+          y[m * nc + c] = acc;
+          A[m * nc + c] = mag;
+        }
+      }
+      free(wrow);
+    }
+  }
+  return err;
+}
+
+int oracle_matmul(const double *x, int64_t M, const uint32_t *codes, const uint16_t *scales,
+                  const uint16_t *biases, int64_t N, int64_t K, int G, int bits, double *y,
+                  double *A) {
+  int64_t *cols = (int64_t *)malloc((size_t)(N > 0 ? N : 1) * sizeof(int64_t));
+  if (!cols) return OR_ERR_ARG;
+  for (int64_t n = 0; n < N; ++n) cols[n] = n;
+  int st = oracle_matmul_cols(x, M, codes, scales, biases, N, K, G, bits, cols, N, y, A);
+  free(cols);
+  return st;
+}
+
+/* ---------------------------------------------------------------------
+ * Gather (MoE experts; [MLXQ] "gather variants"; reading R6).
+ * codes [E, N, K*b/32], scales/biases [E, N, K/G], ids [T, topk],
+ * x [T, K] exact values; y and A are [T, topk, N].
+ * ------------------------------------------------------------------- */
+int oracle_gather_matmul(const double *x, int64_t T, const uint32_t *codes, const uint16_t *scales,
+                         const uint16_t *biases, int64_t E, int64_t N, int64_t K,
+                         const int32_t *ids, int64_t topk, int G, int bits, double *y, double *A) {
+  int st = check_shape(N, K, G, bits);
+  if (st) return st;
+  for (int64_t i = 0; i < T * topk; ++i)
+    if (ids[i] < 0 || ids[i] >= E) return OR_ERR_INDEX;
+  const int64_t wpe = N * (K * bits / 32), spe = N * (K / G);
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t j = 0; j < topk; ++j) {
+      int64_t e = ids[t * topk + j];
+      st = oracle_matmul(x + t * K, 1, codes + e * wpe, scales + e * spe, biases + e * spe, N, K,
+                         G, bits, y + (t * topk + j) * N, A + (t * topk + j) * N);
+      if (st) return st;
+    }
+  return OR_OK;
+}

@@ -1,0 +1,120 @@
+"""Pins of the CPU reference matmul and gather.
+
+The reference follows "Tutorial 10: Quantization", section 5, Approach 1
+(dequantize, then multiply, y = x @ W^T), accumulating in binary64.  Pinned
+by: a dense numpy product on an independently decoded W (tiny shapes, every
+bit width and group size), the unit-vector special case (y = w^[:, k]), the
+one-group closed form y = G*b + s*sum(q), |y| <= A, and the reduction of the
+gather to per-pair products and to a plain matmul when all ids agree."""
+import numpy as np
+import pytest
+
+import oracle
+from group_wise_affine_aq_amd import inputs
+
+
+def _decode_f64(codes, scales, biases, K, G, bits):
+    # independent decode: treat each row as one big little-endian integer
+    N = codes.shape[0]
+    out = np.zeros((N, K))
+    s = scales.view(np.float16).astype(np.float64)
+    b = biases.view(np.float16).astype(np.float64)
+    for n in range(N):
+        big = int.from_bytes(codes[n].astype("<u4").tobytes(), "little")
+        for k in range(K):
+            q = (big >> (k * bits)) & ((1 << bits) - 1)
+            out[n, k] = q * s[n, k // G] + b[n, k // G]
+    return out
+
+
+@pytest.mark.parametrize("bits", range(2, 9))
+@pytest.mark.parametrize("G", [32, 64, 128])
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+def test_dense_product_tiny(bits, G, xdt):
+    M, N, K = 3, 5, 2 * G
+    w = inputs.weights(N, K, seed=4, key=(bits, G))
+    codes, scales, biases = oracle.quantize(w, G, bits)
+    x = inputs.from_bits(inputs.activations(M, K, xdt, seed=4, key=(bits, G)), xdt)
+    wd = _decode_f64(codes, scales, biases, K, G, bits)
+    assert np.array_equal(wd, oracle.dequantize_exact(codes, scales, biases, K, G, bits))
+    y, A = oracle.matmul(x, codes, scales, biases, K, G, bits)
+    assert np.allclose(y, x @ wd.T, rtol=1e-12, atol=1e-15)
+    assert np.allclose(A, np.abs(x) @ np.abs(wd).T, rtol=1e-12, atol=1e-15)
+    assert np.all(np.abs(y) <= A * (1 + 1e-12))
+    cols = np.array([4, 0, 2])
+    yc, Ac = oracle.matmul(x, codes, scales, biases, K, G, bits, cols=cols)
+    assert np.array_equal(yc, y[:, cols]) and np.array_equal(Ac, A[:, cols])
+
+
+def test_unit_vectors_give_columns():
+    G, bits, N, K = 64, 4, 6, 256
+    w = inputs.weights(N, K, seed=8)
+    codes, scales, biases = oracle.quantize(w, G, bits)
+    x = np.eye(K)
+    y, _ = oracle.matmul(x, codes, scales, biases, K, G, bits)
+    assert np.array_equal(y, oracle.dequantize_exact(codes, scales, biases, K, G, bits).T)
+
+
+def test_one_group_of_ones():
+    # x = 1 on group g, 0 elsewhere: y[n] = G*b[n,g] + s[n,g]*sum_k q[n,k]
+    G, bits, N, K = 32, 5, 4, 128
+    w = inputs.weights(N, K, seed=10)
+    codes, scales, biases = oracle.quantize(w, G, bits)
+    q = oracle.unpack(codes, K, bits).astype(np.int64)
+    for g in range(K // G):
+        x = np.zeros((1, K))
+        x[0, g * G:(g + 1) * G] = 1.0
+        y, _ = oracle.matmul(x, codes, scales, biases, K, G, bits)
+        s = scales[:, g].view(np.float16).astype(np.float64)
+        b = biases[:, g].view(np.float16).astype(np.float64)
+        assert np.allclose(y[0], G * b + s * q[:, g * G:(g + 1) * G].sum(1), rtol=1e-14, atol=0)
+
+
+def test_quantization_error_bounds_product():
+    # |x@W^T - x@W^^T| <= sum_k |x_k| s/2 (the per-element bound carried through)
+    G, bits, N, K = 64, 4, 8, 512
+    w = inputs.weights(N, K, seed=12)
+    codes, scales, biases = oracle.quantize(w, G, bits)
+    x = inputs.from_bits(inputs.activations(2, K, "f16", seed=12), "f16")
+    y, _ = oracle.matmul(x, codes, scales, biases, K, G, bits)
+    s = np.repeat(scales.view(np.float16).astype(np.float64), G, axis=1)
+    bound = np.abs(x) @ (s / 2).T
+    assert np.all(np.abs(x @ w.astype(np.float64).T - y) <= bound * (1 + 1e-12))
+
+
+def test_gather_reduces_to_pairs_and_to_matmul():
+    E, N, K, G, bits, T, topk = 5, 7, 128, 64, 4, 4, 3
+    ws = [inputs.weights(N, K, seed=13, key=(e,)) for e in range(E)]
+    q = [oracle.quantize(w, G, bits) for w in ws]
+    codes = np.stack([c for c, _, _ in q]); scales = np.stack([s for _, s, _ in q])
+    biases = np.stack([b for _, _, b in q])
+    x = inputs.from_bits(inputs.activations(T, K, "f16", seed=13), "f16")
+    ids = inputs.expert_ids(T, E, topk, seed=13)
+    y, A = oracle.gather_matmul(x, codes, scales, biases, ids, K, G, bits)
+    for t in range(T):
+        for j in range(topk):
+            e = ids[t, j]
+            yr, Ar = oracle.matmul(x[t:t + 1], codes[e], scales[e], biases[e], K, G, bits)
+            assert np.array_equal(y[t, j], yr[0]) and np.array_equal(A[t, j], Ar[0])
+    same = np.full((T, 1), 2, dtype=np.int32)
+    y1, _ = oracle.gather_matmul(x, codes, scales, biases, same, K, G, bits)
+    yr, _ = oracle.matmul(x, codes[2], scales[2], biases[2], K, G, bits)
+    assert np.array_equal(y1[:, 0, :], yr)
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.gather_matmul(x, codes, scales, biases, np.full((T, 1), E, np.int32), K, G, bits)
+    assert e.value.status == oracle.ERR_INDEX
+
+
+def test_tolerance_helper():
+    y_ref = np.array([1.0, -2.0]); A = np.array([512.0, 512.0])
+    ok, r = oracle.within_tolerance(y_ref + 1.0, y_ref, A)
+    assert ok and r <= 1.0
+    ok, r = oracle.within_tolerance(y_ref + 1.01, y_ref, A)
+    assert not ok and r > 1.0
+
+
+def test_expert_ids_distinct():
+    ids = inputs.expert_ids(32, 64, 6, seed=0)
+    assert ids.shape == (32, 6)
+    assert all(len(set(r)) == 6 for r in ids.tolist())
+    assert ids.min() >= 0 and ids.max() < 64
