@@ -1,0 +1,326 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized-matmul hot path on one MI355X.
+
+Headline workload (decode, M = 1): the four Llama-3-8B-shaped matrices
+W [4096,4096], [1024,4096], [14336,4096], [4096,14336] at 4 bits, G = 64,
+fp16 activations x [1, K] ~ N(0, 1), weights ~ N(0, 0.02) with 0.1% outliers
+x20, quantized on the device by aq_quantize.  One step = one y = x @ W^T per
+matrix through the shape dispatch (aq_quantized_matmul), each on a cold copy
+of its packed weights: the step rotates over enough distinct copies (>= 1 GiB
+of packed weights in total, four times the 256 MB last-level cache) that
+every launch streams its weights from HBM.  Steps are replayed from HIP
+graphs (one per copy) so host launch overhead stays off the device timeline.
+
+value = packed weight bytes (codes + scales + biases) of the timed steps /
+the timed wall interval on the device (effective weight GB/s, the metric's
+first part).  The JSON line also carries:
+  roofline      the decode matrix-vector kernel's achieved algorithmic
+                bytes/s (weights + x + y per launch / average launch duration,
+                timed live with HIP events on the launch stream) vs 8 TB/s;
+  cpu_baseline  the CPU reference computing the same step on the host cores;
+  qmm           the metric's second part: prefill Y = X @ W^T with X bf16
+                [2048, 8192] and W [28672, 8192] at 4-bit G=64 (plus 3-bit
+                G=64 and 2-bit G=32), TFLOP/s vs the 2.5 PFLOP/s dense bf16 peak.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "QMV M=1 effective weight GB/s (% of HBM peak); QMM TFLOP/s (% MFMA peak)"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+DECODE_SHAPES = [(4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336)]
+G, BITS = 64, 4
+PREFILL = dict(M=2048, N=28672, K=8192, settings=[(4, 64), (3, 64), (2, 32)])
+COLD_BYTES = 1 << 30
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
+    p.add_argument("--no-qmm", action="store_true", help="skip the prefill (QMM) section")
+    p.add_argument("--qmm-iters", type=int, default=20)
+    p.add_argument("--copy-probe", action="store_true",
+                   help="also run a plain 512 MiB device copy (counter calibration)")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+def _spin(torch):
+    """Keep the device busy briefly so the host can queue launches ahead."""
+    try:
+        torch.cuda._sleep(20_000_000)
+    except (AttributeError, RuntimeError):
+        pass
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the kernels shard by rows or experts, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import group_wise_affine_aq_amd as aq
+    from group_wise_affine_aq_amd import inputs
+
+    aq.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    props = torch.cuda.get_device_properties(dev)
+    print(f"# device: {props.name} ({getattr(props, 'gcnArchName', '?')}), "
+          f"{props.multi_processor_count} CUs", file=sys.stderr, flush=True)
+
+    # ---- decode workload ---------------------------------------------------------------
+    mats = []
+    for i, (N, K) in enumerate(DECODE_SHAPES):
+        w = inputs.weights_device(N, K, device=dev, seed=0, key=(1, i), outliers=True)
+        c, s, b = aq.aq_quantize(w, G, BITS)
+        del w
+        x = inputs.activations_device(1, K, "f16", device=dev, seed=0, key=(1, i))
+        y = torch.empty((1, N), dtype=torch.float16, device=dev)
+        wbytes = aq.aq_qweight_bytes(N, K, G, BITS)
+        mats.append(dict(N=N, K=K, packed=(c, s, b), x=x, y=y, wbytes=wbytes,
+                         algo_bytes=wbytes + 2 * K + 2 * N))
+    step_wbytes = sum(m["wbytes"] for m in mats)
+    copies = max(2, math.ceil(COLD_BYTES / step_wbytes))
+    sets = [[m["packed"] for m in mats]]
+    for _ in range(copies - 1):
+        sets.append([tuple(t.clone() for t in m["packed"]) for m in mats])
+    torch.cuda.synchronize()
+    print(f"# decode: {len(mats)} matrices, {step_wbytes} packed bytes/step, {copies} cold copies",
+          file=sys.stderr, flush=True)
+
+    def step(ci):
+        for m, (c, s, b) in zip(mats, sets[ci]):
+            aq.aq_quantized_matmul(m["x"], c, s, b, G, BITS, y=m["y"])
+
+    # one graph per copy: a replay is exactly one step
+    for ci in range(copies):  # eager pass first (also loads the kernels)
+        step(ci)
+    torch.cuda.synchronize()
+    graphs = []
+    gstream = torch.cuda.Stream()
+    with torch.cuda.stream(gstream):
+        for ci in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=gstream):
+                step(ci)
+            graphs.append(g)
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        graphs[i % copies].replay()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps --------------------------------------------------
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(args.steps):
+        graphs[i % copies].replay()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t0.elapsed_time(t1)
+    ms_per_step = ms_total / args.steps
+    value = step_wbytes * args.steps / (ms_total * 1e-3) / 1e9
+    print(f"# timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step (device), "
+          f"host wall {wall * 1e3 / args.steps:.2f} us/step", file=sys.stderr, flush=True)
+
+    # ---- per-kernel durations (HIP events on the launch stream) --------------------------
+    # A spin kernel keeps the device busy while the host queues every launch,
+    # so each event pair brackets back-to-back device work only.
+    reps = max(20, min(200, args.steps))
+    per_shape = []
+    for j, m in enumerate(mats):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        torch.cuda.synchronize()
+        _spin(torch)
+        for r in range(reps):
+            c, s, b = sets[r % copies][j]
+            evs[r][0].record(stream)
+            aq.aq_quantized_matmul(m["x"], c, s, b, G, BITS, y=m["y"])
+            evs[r][1].record(stream)
+        torch.cuda.synchronize()
+        durs = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)  # us
+        avg = sum(durs) / len(durs)
+        per_shape.append(dict(shape=[m["N"], m["K"]], weight_bytes=m["wbytes"],
+                              avg_us=round(avg, 3), median_us=round(durs[len(durs) // 2], 3),
+                              weight_gbs=round(m["wbytes"] / (avg * 1e-6) / 1e9, 1),
+                              pct_hbm=round(100 * m["wbytes"] / (avg * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)))
+        print(f"# QMV {m['N']}x{m['K']}: avg {avg:.2f} us, median {durs[len(durs)//2]:.2f} us, "
+              f"{per_shape[-1]['weight_gbs']} GB/s weights", file=sys.stderr, flush=True)
+    total_algo = sum(m["algo_bytes"] for m in mats)
+    total_us = sum(p["avg_us"] for p in per_shape)
+    achieved = total_algo / (total_us * 1e-6) / 1e9
+    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=_traffic(mats, per_shape),
+                    kernel="qmv_kernel<BITS=4, MB=1, f16>",
+                    launches_per_step=len(mats), avg_launch_us=round(total_us / len(mats), 3),
+                    algo_bytes_per_launch=round(total_algo / len(mats)))
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "decode QMV M=1, W [4096,4096] [1024,4096] [14336,4096] "
+                               "[4096,14336], 4-bit G=64, fp16 x, cold weights",
+                   "step_weight_bytes": step_wbytes, "cold_copies": copies,
+                   "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1)},
+        "roofline": roofline,
+        "per_shape": per_shape,
+    }
+
+    if args.copy_probe:
+        a = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        bb = torch.empty_like(a)
+        for _ in range(3):
+            bb.copy_(a)
+        torch.cuda.synchronize()
+
+    # ---- CPU baseline: the CPU reference on the same step -----------------------------------
+    if not args.no_cpu:
+        result["cpu_baseline"] = _cpu_baseline(mats, args.cpu_seconds)
+
+    # ---- prefill (QMM) ---------------------------------------------------------------------
+    if not args.no_qmm:
+        del graphs, sets
+        torch.cuda.synchronize()
+        result["qmm"] = _qmm(aq, inputs, dev, args.qmm_iters)
+
+    print(json.dumps(result), flush=True)
+
+
+def _traffic(mats, per_shape):
+    """HBM bytes per launch of the decode kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size),
+    or None when no summary for the current kernel source exists."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "qmv_decode_m1_traffic.txt")
+    src = os.path.join(ROOT, "group_wise_affine_aq_amd", "csrc", "aq_qmv.hip")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if kv.get("source_sha256_16") != sha:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def _cpu_baseline(mats, seconds):
+    import numpy as np
+    import torch
+
+    import oracle
+    from group_wise_affine_aq_amd import inputs as _inp
+
+    host = []
+    for m in mats:
+        c, s, b = m["packed"]
+        host.append((_inp.from_bits(m["x"].view(torch.int16).cpu().numpy().view(np.uint16), "f16"),
+                     c.cpu().numpy().view(np.uint32),
+                     s.view(torch.int16).cpu().numpy().view(np.uint16),
+                     b.view(torch.int16).cpu().numpy().view(np.uint16), m["K"]))
+    reps, t_start = 0, time.perf_counter()
+    while True:
+        for x, c, s, b, K in host:
+            oracle.matmul(x, c, s, b, K, G, BITS)
+        reps += 1
+        el = time.perf_counter() - t_start
+        if el >= seconds:
+            break
+    step_bytes = sum(m["wbytes"] for m in mats)
+    cpu_gbs = step_bytes * reps / el / 1e9
+    model = "?"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(cpu_gbs, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{reps} full decode step(s) (4 matrices, {step_bytes} packed weight bytes, "
+                      f"fp64 accumulation), {el:.1f} s on {model}"}
+
+
+def _qmm(aq, inputs, dev, iters):
+    import torch
+    M, N, K = PREFILL["M"], PREFILL["N"], PREFILL["K"]
+    x = inputs.activations_device(M, K, "bf16", device=dev, seed=0, key=(3,))
+    w = inputs.weights_device(N, K, device=dev, seed=0, key=(3,))
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    out = {"workload": f"prefill X bf16 [{M},{K}] x W [{N},{K}]", "flop": 2 * M * N * K}
+    flop = 2 * M * N * K
+    for bits, g in PREFILL["settings"]:
+        c, s, b = aq.aq_quantize(w, g, bits)
+        for _ in range(3):
+            aq.aq_qmm(x, c, s, b, g, bits, y=y)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(iters)]
+        _spin(torch)
+        for e0, e1 in evs:
+            e0.record()
+            aq.aq_qmm(x, c, s, b, g, bits, y=y)
+            e1.record()
+        torch.cuda.synchronize()
+        durs = sorted(a.elapsed_time(b) for a, b in evs)
+        avg = sum(durs) / len(durs)
+        tf = flop / (avg * 1e-3) / 1e12
+        out[f"b{bits}_g{g}"] = {"avg_ms": round(avg, 4), "tflops": round(tf, 1),
+                                "pct_mfma_peak": round(100 * tf / MFMA_BF16_PEAK_TFLOPS, 1)}
+        print(f"# QMM {bits}-bit G={g}: {avg:.3f} ms, {tf:.1f} TFLOP/s", file=sys.stderr,
+              flush=True)
+        del c, s, b
+    # dense bf16 GEMM on the library GEMM (hipBLASLt) at the same shape, for context
+    wd = w.to(torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(x, wd.T)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        torch.matmul(x, wd.T)
+    e1.record()
+    torch.cuda.synchronize()
+    avg = e0.elapsed_time(e1) / iters
+    out["dense_bf16_torch_matmul"] = {"avg_ms": round(avg, 4),
+                                      "tflops": round(flop / (avg * 1e-3) / 1e12, 1)}
+    out["peak_tflops"] = MFMA_BF16_PEAK_TFLOPS
+    return out
+
+
+if __name__ == "__main__":
+    main()

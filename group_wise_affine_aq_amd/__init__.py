@@ -1,0 +1,214 @@
+"""group_wise_affine_aq_amd -- group-wise affine weight-only quantization for
+AMD Instinct MI355X.
+
+Python binding over the C ABI of ``libaq.so`` (``include/aq.h``).  The
+functions here only marshal torch tensors (device memory, the current HIP
+stream) into the C entry points of the same names; every step of the
+computation runs in the library's HIP kernels.  There is no fallback: if the
+library has not been built, or a call fails, an exception is raised.
+
+Packed weights use the layout of the pages' container ("Tutorial 10:
+Quantization", s.4): codes uint32 [N, K*bits/32] (stored in torch as int32),
+scales and biases fp16 [N, K/group_size].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "AQError", "lib_path", "load_library", "aq_status_string", "aq_version", "aq_codes_words",
+    "aq_qweight_bytes", "aq_quantize", "aq_dequantize", "aq_qmv", "aq_qmm",
+    "aq_quantized_matmul", "aq_gather_qmv",
+]
+
+AQ_OK = 0
+AQ_F32, AQ_F16, AQ_BF16 = 0, 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libaq.so")
+
+
+class AQError(RuntimeError):
+    def __init__(self, status: int, fn: str):
+        msg = _lib.aq_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{fn}: {msg} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library():
+    """Load libaq.so (built by ``python -m group_wise_affine_aq_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"libaq.so not found at {path}; build it with "
+                           "`python -m group_wise_affine_aq_amd.build`")
+    lib = ctypes.CDLL(path)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    sigs = {
+        "aq_status_string": ([i32], ctypes.c_char_p),
+        "aq_version": ([], ctypes.c_char_p),
+        "aq_codes_words": ([i64, i32], i64),
+        "aq_qweight_bytes": ([i64, i64, i32, i32], i64),
+        "aq_quantize": ([vp, i32, i64, i64, i32, i32, vp, vp, vp, vp], i32),
+        "aq_dequantize": ([vp, vp, vp, i64, i64, i32, i32, vp, i32, vp], i32),
+        "aq_qmv": ([vp, i32, i64, vp, vp, vp, i64, i64, i32, i32, vp, vp], i32),
+        "aq_qmm": ([vp, i32, i64, vp, vp, vp, i64, i64, i32, i32, vp, vp], i32),
+        "aq_quantized_matmul": ([vp, i32, i64, vp, vp, vp, i64, i64, i32, i32, vp, vp], i32),
+        "aq_gather_qmv": ([vp, i32, i64, vp, vp, vp, i64, i64, i64, vp, i32, i32, i32, vp, vp],
+                          i32),
+    }
+    for name, (args, res) in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+# ---- host helpers -------------------------------------------------------------------
+def aq_status_string(status: int) -> str:
+    return load_library().aq_status_string(status).decode()
+
+
+def aq_version() -> str:
+    return load_library().aq_version().decode()
+
+
+def aq_codes_words(K: int, bits: int) -> int:
+    return int(load_library().aq_codes_words(K, bits))
+
+
+def aq_qweight_bytes(N: int, K: int, group_size: int, bits: int) -> int:
+    return int(load_library().aq_qweight_bytes(N, K, group_size, bits))
+
+
+# ---- marshalling -----------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float32: AQ_F32, torch.float16: AQ_F16, torch.bfloat16: AQ_BF16}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _torch_dtype(code: int):
+    torch = _torch()
+    return {AQ_F32: torch.float32, AQ_F16: torch.float16, AQ_BF16: torch.bfloat16}[code]
+
+
+def _dev(t, name):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(st: int, fn: str):
+    if st != AQ_OK:
+        raise AQError(st, fn)
+
+
+# ---- device operations -------------------------------------------------------------------
+def aq_quantize(w, group_size: int, bits: int, codes=None, scales=None, biases=None, stream=None):
+    """Quantize W [N, K] (fp32/fp16/bf16, device) -> (codes, scales, biases)."""
+    torch = _torch()
+    lib = load_library()
+    N, K = w.shape
+    if codes is None:
+        codes = torch.empty((N, K * bits // 32), dtype=torch.int32, device=w.device)
+    if scales is None:
+        scales = torch.empty((N, K // group_size), dtype=torch.float16, device=w.device)
+    if biases is None:
+        biases = torch.empty((N, K // group_size), dtype=torch.float16, device=w.device)
+    st = lib.aq_quantize(_dev(w, "w"), _dtype_code(w), N, K, group_size, bits,
+                         _dev(codes, "codes"), _dev(scales, "scales"), _dev(biases, "biases"),
+                         _stream(stream))
+    _check(st, "aq_quantize")
+    return codes, scales, biases
+
+
+def aq_dequantize(codes, scales, biases, group_size: int, bits: int, out_dtype=None, out=None,
+                  stream=None):
+    """Dequantize packed weights -> [N, K] in out_dtype (default fp16)."""
+    torch = _torch()
+    lib = load_library()
+    N = codes.shape[0]
+    K = scales.shape[1] * group_size
+    if out is None:
+        out = torch.empty((N, K), dtype=out_dtype or torch.float16, device=codes.device)
+    st = lib.aq_dequantize(_dev(codes, "codes"), _dev(scales, "scales"), _dev(biases, "biases"),
+                           N, K, group_size, bits, _dev(out, "out"), _dtype_code(out),
+                           _stream(stream))
+    _check(st, "aq_dequantize")
+    return out
+
+
+def _matmul(fname, x, codes, scales, biases, group_size, bits, y, stream):
+    torch = _torch()
+    lib = load_library()
+    M, K = x.shape
+    N = codes.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    st = getattr(lib, fname)(_dev(x, "x"), _dtype_code(x), M, _dev(codes, "codes"),
+                             _dev(scales, "scales"), _dev(biases, "biases"), N, K, group_size,
+                             bits, _dev(y, "y"), _stream(stream))
+    _check(st, fname)
+    return y
+
+
+def aq_qmv(x, codes, scales, biases, group_size: int, bits: int, y=None, stream=None):
+    """y = x @ W^T for x [M <= 8, K] (decode kernels)."""
+    return _matmul("aq_qmv", x, codes, scales, biases, group_size, bits, y, stream)
+
+
+def aq_qmm(x, codes, scales, biases, group_size: int, bits: int, y=None, stream=None):
+    """y = x @ W^T for any M (matrix-core kernel)."""
+    return _matmul("aq_qmm", x, codes, scales, biases, group_size, bits, y, stream)
+
+
+def aq_quantized_matmul(x, codes, scales, biases, group_size: int, bits: int, y=None,
+                        stream=None):
+    """y = x @ W^T with the kernel chosen per shape."""
+    return _matmul("aq_quantized_matmul", x, codes, scales, biases, group_size, bits, y, stream)
+
+
+def aq_gather_qmv(x, codes, scales, biases, ids, group_size: int, bits: int, y=None,
+                  stream=None):
+    """MoE: y[t, j, :] = x[t] @ W_{ids[t, j]}^T; codes [E, N, K*bits/32]."""
+    torch = _torch()
+    lib = load_library()
+    T, K = x.shape
+    E, N = codes.shape[0], codes.shape[1]
+    topk = ids.shape[1]
+    if y is None:
+        y = torch.empty((T, topk, N), dtype=x.dtype, device=x.device)
+    st = lib.aq_gather_qmv(_dev(x, "x"), _dtype_code(x), T, _dev(codes, "codes"),
+                           _dev(scales, "scales"), _dev(biases, "biases"), E, N, K,
+                           _dev(ids, "ids"), topk, group_size, bits, _dev(y, "y"),
+                           _stream(stream))
+    _check(st, "aq_gather_qmv")
+    return y

@@ -1,0 +1,153 @@
+// aq_api.cpp -- the extern "C" entry points of libaq (declared in include/aq.h):
+// host-side argument validation, shape dispatch and kernel launch.
+//
+// Validation runs entirely on the host and touches no HIP API, so a bad call
+// returns before anything is enqueued (and can be exercised on a machine
+// without a GPU).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "aq.h"
+#include "aq_internal.hpp"
+
+namespace {
+
+constexpr int64_t kMaxQmvRows = 8;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_format(int64_t N, int64_t K, int G, int bits) {
+  if (N < 1 || K < 1) return false;
+  if (G != 32 && G != 64 && G != 128) return false;
+  if (bits < 2 || bits > 8) return false;
+  if (K % G != 0) return false;
+  return true;
+}
+
+bool valid_act_dtype(int d) { return d == AQ_F16 || d == AQ_BF16; }
+
+aq_status from_hip(hipError_t e) { return e == hipSuccess ? AQ_OK : AQ_ERR_HIP; }
+
+aq_status check_weights(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases) {
+  if (!codes || !scales || !biases) return AQ_ERR_INVALID_ARG;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(biases)) return AQ_ERR_ALIGNMENT;
+  return AQ_OK;
+}
+
+aq_status check_matmul(const void *x, int x_dtype, int64_t M, const uint32_t *codes,
+                       const uint16_t *scales, const uint16_t *biases, int64_t N, int64_t K,
+                       int G, int bits, const void *y) {
+  if (!valid_format(N, K, G, bits) || M < 1 || !valid_act_dtype(x_dtype))
+    return AQ_ERR_INVALID_ARG;
+  if (!x || !y) return AQ_ERR_INVALID_ARG;
+  aq_status st = check_weights(codes, scales, biases);
+  if (st != AQ_OK) return st;
+  if (!aligned16(x) || !aligned16(y)) return AQ_ERR_ALIGNMENT;
+  return AQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *aq_status_string(aq_status status) {
+  switch (status) {
+    case AQ_OK: return "AQ_OK";
+    case AQ_ERR_INVALID_ARG: return "AQ_ERR_INVALID_ARG: invalid argument";
+    case AQ_ERR_UNSUPPORTED: return "AQ_ERR_UNSUPPORTED: not supported by this build";
+    case AQ_ERR_ALIGNMENT: return "AQ_ERR_ALIGNMENT: pointer not 16-byte aligned";
+    case AQ_ERR_HIP: return "AQ_ERR_HIP: HIP runtime error at launch";
+    case AQ_ERR_RANGE: return "AQ_ERR_RANGE: value out of range";
+    case AQ_ERR_INDEX: return "AQ_ERR_INDEX: index out of range";
+  }
+  return "unknown aq_status";
+}
+
+const char *aq_version(void) { return "libaq 0.1 (gfx950)"; }
+
+int64_t aq_codes_words(int64_t K, int bits) {
+  if (K < 0 || bits < 2 || bits > 8 || (K * bits) % 32 != 0) return -1;
+  return K * bits / 32;
+}
+
+int64_t aq_qweight_bytes(int64_t N, int64_t K, int group_size, int bits) {
+  if (N < 0 || K < 0 || (group_size != 32 && group_size != 64 && group_size != 128) || bits < 2 ||
+      bits > 8 || K % group_size != 0)
+    return -1;
+  return N * K * bits / 8 + N * (K / group_size) * 4;
+}
+
+aq_status aq_quantize(const void *w, aq_dtype w_dtype, int64_t N, int64_t K, int group_size,
+                      int bits, uint32_t *codes, uint16_t *scales, uint16_t *biases,
+                      void *stream) {
+  if (!valid_format(N, K, group_size, bits)) return AQ_ERR_INVALID_ARG;
+  if (w_dtype != AQ_F32 && w_dtype != AQ_F16 && w_dtype != AQ_BF16) return AQ_ERR_INVALID_ARG;
+  if (!w) return AQ_ERR_INVALID_ARG;
+  aq_status st = check_weights(codes, scales, biases);
+  if (st != AQ_OK) return st;
+  if (!aligned16(w)) return AQ_ERR_ALIGNMENT;
+  if (N * (K / 8) > (int64_t)0x7FFFFFFF * 256) return AQ_ERR_UNSUPPORTED;
+  return from_hip(aq::launch_quantize(w, (int)w_dtype, N, K, group_size, bits, codes, scales,
+                                      biases, static_cast<hipStream_t>(stream)));
+}
+
+aq_status aq_dequantize(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                        int64_t N, int64_t K, int group_size, int bits, void *out,
+                        aq_dtype out_dtype, void *stream) {
+  if (!valid_format(N, K, group_size, bits)) return AQ_ERR_INVALID_ARG;
+  if (out_dtype != AQ_F32 && out_dtype != AQ_F16 && out_dtype != AQ_BF16) return AQ_ERR_INVALID_ARG;
+  if (!out) return AQ_ERR_INVALID_ARG;
+  aq_status st = check_weights(codes, scales, biases);
+  if (st != AQ_OK) return st;
+  if (!aligned16(out)) return AQ_ERR_ALIGNMENT;
+  if (N * (K / 32) > (int64_t)0x7FFFFFFF * 256) return AQ_ERR_UNSUPPORTED;
+  return from_hip(aq::launch_dequantize(codes, scales, biases, N, K, group_size, bits, out,
+                                        (int)out_dtype, static_cast<hipStream_t>(stream)));
+}
+
+aq_status aq_qmv(const void *x, aq_dtype x_dtype, int64_t M, const uint32_t *codes,
+                 const uint16_t *scales, const uint16_t *biases, int64_t N, int64_t K,
+                 int group_size, int bits, void *y, void *stream) {
+  aq_status st = check_matmul(x, x_dtype, M, codes, scales, biases, N, K, group_size, bits, y);
+  if (st != AQ_OK) return st;
+  if (M > kMaxQmvRows) return AQ_ERR_INVALID_ARG;
+  return from_hip(aq::launch_qmv(x, (int)x_dtype, (int)M, codes, scales, biases, N, K, group_size,
+                                 bits, y, static_cast<hipStream_t>(stream)));
+}
+
+aq_status aq_qmm(const void *x, aq_dtype x_dtype, int64_t M, const uint32_t *codes,
+                 const uint16_t *scales, const uint16_t *biases, int64_t N, int64_t K,
+                 int group_size, int bits, void *y, void *stream) {
+  aq_status st = check_matmul(x, x_dtype, M, codes, scales, biases, N, K, group_size, bits, y);
+  if (st != AQ_OK) return st;
+  if (M > (int64_t)65535 * 128 || (N + 127) / 128 > 0x7FFFFFFF) return AQ_ERR_UNSUPPORTED;
+  return from_hip(aq::launch_qmm(x, (int)x_dtype, M, codes, scales, biases, N, K, group_size,
+                                 bits, y, static_cast<hipStream_t>(stream)));
+}
+
+aq_status aq_quantized_matmul(const void *x, aq_dtype x_dtype, int64_t M, const uint32_t *codes,
+                              const uint16_t *scales, const uint16_t *biases, int64_t N,
+                              int64_t K, int group_size, int bits, void *y, void *stream) {
+  if (M >= 1 && M <= kMaxQmvRows)
+    return aq_qmv(x, x_dtype, M, codes, scales, biases, N, K, group_size, bits, y, stream);
+  return aq_qmm(x, x_dtype, M, codes, scales, biases, N, K, group_size, bits, y, stream);
+}
+
+aq_status aq_gather_qmv(const void *x, aq_dtype x_dtype, int64_t T, const uint32_t *codes,
+                        const uint16_t *scales, const uint16_t *biases, int64_t E, int64_t N,
+                        int64_t K, const int32_t *ids, int topk, int group_size, int bits,
+                        void *y, void *stream) {
+  if (!valid_format(N, K, group_size, bits) || T < 1 || E < 1 || topk < 1 ||
+      !valid_act_dtype(x_dtype))
+    return AQ_ERR_INVALID_ARG;
+  if (!x || !y || !ids) return AQ_ERR_INVALID_ARG;
+  aq_status st = check_weights(codes, scales, biases);
+  if (st != AQ_OK) return st;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(ids)) return AQ_ERR_ALIGNMENT;
+  if (E > 65535 || T * topk > 0x7FFFFFFF) return AQ_ERR_UNSUPPORTED;
+  return from_hip(aq::launch_gather_qmv(x, (int)x_dtype, T, codes, scales, biases, E, N, K, ids,
+                                        topk, group_size, bits, y,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,35 @@
+// aq_internal.hpp -- kernel launchers behind the C ABI (arguments already
+// validated by aq_api.cpp).  Each returns hipSuccess or the launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace aq {
+
+enum XType { X_F32 = 0, X_F16 = 1, X_BF16 = 2 };
+
+hipError_t launch_quantize(const void *w, int w_dtype, int64_t N, int64_t K, int G, int bits,
+                           uint32_t *codes, uint16_t *scales, uint16_t *biases, hipStream_t s);
+
+hipError_t launch_dequantize(const uint32_t *codes, const uint16_t *scales,
+                             const uint16_t *biases, int64_t N, int64_t K, int G, int bits,
+                             void *out, int out_dtype, hipStream_t s);
+
+// y[M, N] = x[M, K] @ W^T for 1 <= M <= 8 (matrix-vector kernels)
+hipError_t launch_qmv(const void *x, int x_dtype, int M, const uint32_t *codes,
+                      const uint16_t *scales, const uint16_t *biases, int64_t N, int64_t K, int G,
+                      int bits, void *y, hipStream_t s);
+
+// mixture-of-experts gather: y[t, j, :] = x[t] @ W_{ids[t, j]}^T
+hipError_t launch_gather_qmv(const void *x, int x_dtype, int64_t T, const uint32_t *codes,
+                             const uint16_t *scales, const uint16_t *biases, int64_t E, int64_t N,
+                             int64_t K, const int32_t *ids, int topk, int G, int bits, void *y,
+                             hipStream_t s);
+
+// y[M, N] = x[M, K] @ W^T for any M (matrix-core kernel)
+hipError_t launch_qmm(const void *x, int x_dtype, int64_t M, const uint32_t *codes,
+                      const uint16_t *scales, const uint16_t *biases, int64_t N, int64_t K, int G,
+                      int bits, void *y, hipStream_t s);
+
+}  // namespace aq

@@ -1,0 +1,252 @@
+// aq_quant.hip -- quantize and dequantize kernels for gfx950.
+//
+// Quantize ("Quantizing a Model for MLX", "What MLX quantization stores":
+// per-group scale and offset; "mlx-gptq", "How it works": the grid spans the
+// group's min-max range; round-to-nearest): per group of G weights along a
+// row,
+//   b = largest fp16 <= min(w)            (bias never exceeds a member)
+//   s = smallest fp16 >= 0 with b + L*s >= max(w),   L = 2^bits - 1
+//   q = argmin_q |w - (b + q*s)|, ties to even q (q = 0 if s == 0)
+// Every decision is an exact comparison: b + L*s and the midpoints
+// b + (j+1/2)*s are multiples of 2^-25 below 2^26, exact in binary64, and the
+// binary32 weights are exact in binary64.  Approximate binary32 arithmetic
+// only proposes candidates that the exact tests then correct by one step.
+//
+// Dequantize ("Tutorial 10: Quantization", s.3/s.7): q*s + b in binary32
+// (one rounding, the product is exact), then round-to-nearest-even to the
+// output type.
+//
+// Thread mapping.  Quantize: one thread per 8 consecutive weights; their 8
+// codes fill exactly `bits` bytes at byte offset 8k/8*bits of the row, so
+// every thread stores whole bytes and no two threads share a byte.  A group
+// is G/8 adjacent lanes, reduced with lane shuffles.  Dequantize: one thread
+// per 32-code chunk (`bits` words).
+#include "aq_device.hpp"
+#include "aq_internal.hpp"
+
+namespace aq {
+namespace {
+
+__device__ __forceinline__ double h2d(uint16_t h) { return (double)f16_to_f32(h); }
+
+// next binary16 pattern towards -infinity
+__device__ __forceinline__ uint16_t f16_next_down(uint16_t h) {
+  if (h == 0) return 0x8001u;
+  return (h & 0x8000u) ? (uint16_t)(h + 1) : (uint16_t)(h - 1);
+}
+
+// largest binary16 value <= f; -0 is returned as +0
+__device__ __forceinline__ uint16_t f16_round_down(float f) {
+  uint16_t h = f32_to_f16_rne(f);  // nearest; at most one step above f
+  if (f16_to_f32(h) > f) h = f16_next_down(h);
+  return h == 0x8000u ? (uint16_t)0 : h;
+}
+
+// smallest binary16 s >= 0 with b + L*s >= hi (exact test in binary64)
+__device__ __forceinline__ uint16_t f16_scale_up(double b, float hi, int L) {
+  const double top = (double)hi;
+  if (b >= top) return 0;
+  const float t = (float)(top - b) / (float)L;  // candidate, within a step of the answer
+  uint16_t s = f32_to_f16_rne(t);
+  if (s > 0x7BFFu) s = 0x7BFFu;
+#pragma unroll
+  for (int it = 0; it < 3; ++it)
+    if (s < 0x7BFFu && b + L * h2d(s) < top) ++s;
+#pragma unroll
+  for (int it = 0; it < 3; ++it)
+    if (s > 0 && b + L * h2d((uint16_t)(s - 1)) >= top) --s;
+  return s;
+}
+
+// nearest grid index, ties to even.  mid(j) = b + (j + 1/2) s separates j, j+1.
+__device__ __forceinline__ uint32_t nearest_code(float w, double b, double s, float bf, float rs,
+                                                 int L) {
+  if (s == 0.0) return 0;
+  int q = (int)__builtin_rintf((w - bf) * rs);  // candidate, within one of the answer
+  q = q < 0 ? 0 : (q > L ? L : q);
+  const double wd = (double)w;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    if (q > 0) {
+      const double mid = b + ((double)q - 0.5) * s;
+      if (wd < mid || (wd == mid && (q & 1))) --q;
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    if (q < L) {
+      const double mid = b + ((double)q + 0.5) * s;
+      if (wd > mid || (wd == mid && (q & 1))) ++q;
+    }
+  }
+  return (uint32_t)q;
+}
+
+template <int WDT>
+__device__ __forceinline__ void load8(const void *__restrict__ base, int64_t e, float *v) {
+  if constexpr (WDT == X_F32) {
+    const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(base) + e);
+    float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    uint4 a = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(base) + e);
+    uint32_t u[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (WDT == X_F16) {
+        v[2 * i] = f16_to_f32((uint16_t)(u[i] & 0xFFFFu));
+        v[2 * i + 1] = f16_to_f32((uint16_t)(u[i] >> 16));
+      } else {
+        v[2 * i] = bf16_to_f32((uint16_t)(u[i] & 0xFFFFu));
+        v[2 * i + 1] = bf16_to_f32((uint16_t)(u[i] >> 16));
+      }
+    }
+  }
+}
+
+template <int WDT, int BITS>
+__global__ __launch_bounds__(256) void quantize_kernel(const void *__restrict__ w, int64_t N,
+                                                       int64_t K, int G,
+                                                       uint32_t *__restrict__ codes,
+                                                       uint16_t *__restrict__ scales,
+                                                       uint16_t *__restrict__ biases) {
+  const int64_t opr = K >> 3;  // 8-weight octets per row
+  const int64_t total = N * opr;
+  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool active = idx < total;
+  if (!active) idx = total - 1;  // whole groups are inactive together; keep loads in bounds
+  const int64_t n = idx / opr, o = idx - n * opr;
+
+  float v[8];
+  load8<WDT>(w, n * K + o * 8, v);
+  float lo = v[0], hi = v[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) { lo = fminf(lo, v[i]); hi = fmaxf(hi, v[i]); }
+  const int lanes = G >> 3;  // 4, 8 or 16 adjacent lanes hold one group
+  for (int d = 1; d < lanes; d <<= 1) {
+    lo = fminf(lo, __shfl_xor(lo, d));
+    hi = fmaxf(hi, __shfl_xor(hi, d));
+  }
+  constexpr int L = (1 << BITS) - 1;
+  const uint16_t b16 = f16_round_down(lo);
+  const double b = h2d(b16);
+  const uint16_t s16 = f16_scale_up(b, hi, L);
+  const double s = h2d(s16);
+  const float bf = (float)b;
+  const float rs = s16 ? __builtin_amdgcn_rcpf((float)s) : 0.f;
+
+  uint64_t packed = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    packed |= (uint64_t)nearest_code(v[i], b, s, bf, rs, L) << (BITS * i);
+
+  if (!active) return;
+  if ((o & (lanes - 1)) == 0) {
+    const int64_t gi = n * (K / G) + (o * 8) / G;
+    scales[gi] = s16;
+    biases[gi] = b16;
+  }
+  uint8_t *dst = reinterpret_cast<uint8_t *>(codes + n * (K * BITS / 32)) + o * BITS;
+  if constexpr (BITS == 8) {
+    *reinterpret_cast<uint2 *>(dst) = make_uint2((uint32_t)packed, (uint32_t)(packed >> 32));
+  } else if constexpr (BITS == 4) {
+    *reinterpret_cast<uint32_t *>(dst) = (uint32_t)packed;
+  } else if constexpr (BITS == 2) {
+    *reinterpret_cast<uint16_t *>(dst) = (uint16_t)packed;
+  } else if constexpr (BITS == 6) {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) reinterpret_cast<uint16_t *>(dst)[j] = (uint16_t)(packed >> (16 * j));
+  } else {
+#pragma unroll
+    for (int j = 0; j < BITS; ++j) dst[j] = (uint8_t)(packed >> (8 * j));
+  }
+}
+
+template <int BITS, int ODT>
+__global__ __launch_bounds__(256) void dequantize_kernel(const uint32_t *__restrict__ codes,
+                                                         const uint16_t *__restrict__ scales,
+                                                         const uint16_t *__restrict__ biases,
+                                                         int64_t N, int64_t K, int G,
+                                                         void *__restrict__ out) {
+  const int64_t cpr = K >> 5;  // chunks per row
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= N * cpr) return;
+  const int64_t n = idx / cpr, c = idx - n * cpr;
+  uint32_t wv[BITS];
+  load_chunk<BITS>(codes + n * (K * BITS / 32) + c * BITS, wv);
+  const int64_t gi = n * (K / G) + (c * 32) / G;
+  const float s = f16_to_f32(scales[gi]), b = f16_to_f32(biases[gi]);
+  float r[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) r[i] = __builtin_fmaf((float)chunk_code<BITS>(wv, i), s, b);
+  const int64_t e = n * K + c * 32;
+  if constexpr (ODT == X_F32) {
+    float4 *o = reinterpret_cast<float4 *>(reinterpret_cast<float *>(out) + e);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = make_float4(r[4 * j], r[4 * j + 1], r[4 * j + 2], r[4 * j + 3]);
+  } else {
+    uint32_t p[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t lo = ODT == X_F16 ? f32_to_f16_rne(r[2 * j]) : f32_to_bf16_rne(r[2 * j]);
+      const uint32_t hi = ODT == X_F16 ? f32_to_f16_rne(r[2 * j + 1]) : f32_to_bf16_rne(r[2 * j + 1]);
+      p[j] = lo | (hi << 16);
+    }
+    uint4 *o = reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out) + e);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = make_uint4(p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]);
+  }
+}
+
+template <int WDT>
+hipError_t quantize_w(const void *w, int64_t N, int64_t K, int G, int bits, uint32_t *codes,
+                      uint16_t *scales, uint16_t *biases, hipStream_t s) {
+  const int64_t total = N * (K / 8);
+  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+#define AQ_Q(B) case B: hipLaunchKernelGGL((quantize_kernel<WDT, B>), grid, block, 0, s, w, N, K, G, codes, scales, biases); break;
+  switch (bits) {
+    AQ_Q(2) AQ_Q(3) AQ_Q(4) AQ_Q(5) AQ_Q(6) AQ_Q(7) AQ_Q(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef AQ_Q
+  return hipGetLastError();
+}
+
+template <int ODT>
+hipError_t dequantize_o(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                        int64_t N, int64_t K, int G, int bits, void *out, hipStream_t s) {
+  const int64_t total = N * (K / 32);
+  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+#define AQ_D(B) case B: hipLaunchKernelGGL((dequantize_kernel<B, ODT>), grid, block, 0, s, codes, scales, biases, N, K, G, out); break;
+  switch (bits) {
+    AQ_D(2) AQ_D(3) AQ_D(4) AQ_D(5) AQ_D(6) AQ_D(7) AQ_D(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef AQ_D
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void *w, int w_dtype, int64_t N, int64_t K, int G, int bits,
+                           uint32_t *codes, uint16_t *scales, uint16_t *biases, hipStream_t s) {
+  switch (w_dtype) {
+    case X_F32: return quantize_w<X_F32>(w, N, K, G, bits, codes, scales, biases, s);
+    case X_F16: return quantize_w<X_F16>(w, N, K, G, bits, codes, scales, biases, s);
+    case X_BF16: return quantize_w<X_BF16>(w, N, K, G, bits, codes, scales, biases, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_dequantize(const uint32_t *codes, const uint16_t *scales,
+                             const uint16_t *biases, int64_t N, int64_t K, int G, int bits,
+                             void *out, int out_dtype, hipStream_t s) {
+  switch (out_dtype) {
+    case X_F32: return dequantize_o<X_F32>(codes, scales, biases, N, K, G, bits, out, s);
+    case X_F16: return dequantize_o<X_F16>(codes, scales, biases, N, K, G, bits, out, s);
+    case X_BF16: return dequantize_o<X_BF16>(codes, scales, biases, N, K, G, bits, out, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace aq

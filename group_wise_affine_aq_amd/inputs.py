@@ -95,3 +95,34 @@ def from_bits(bits: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     raise ValueError(dtype)
+
+
+# --- device-side generation for benchmark-sized inputs ----------------------------------
+def _torch_gen(device, seed: int, *key: int):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(np.random.SeedSequence(seed, spawn_key=key).generate_state(1)[0]))
+    return g
+
+
+def weights_device(N: int, K: int, *, device="cuda", seed: int = 0, key=(0,), std: float = 0.02,
+                   outliers: bool = False):
+    """Same distribution as ``weights`` drawn on the device with torch's seeded
+    generator (benchmark-sized matrices; the tests use the numpy streams)."""
+    import torch
+    g = _torch_gen(device, seed, ROLE_W, N, K, *key)
+    w = torch.randn((N, K), generator=g, device=device, dtype=torch.float32) * std
+    if outliers:
+        n_out = int(round(0.001 * N * K))
+        go = _torch_gen(device, seed, ROLE_OUTLIER, N, K, *key)
+        pos = torch.randperm(N * K, generator=go, device=device)[:n_out]
+        w.view(-1)[pos] *= 20.0
+    return w
+
+
+def activations_device(M: int, K: int, dtype: str, *, device="cuda", seed: int = 0, key=(0,)):
+    """x ~ N(0, 1) rounded to fp16/bf16 on the device (torch casts round to nearest even)."""
+    import torch
+    g = _torch_gen(device, seed, ROLE_X, M, K, *key)
+    x = torch.randn((M, K), generator=g, device=device, dtype=torch.float32)
+    return x.to(torch.float16 if dtype == "f16" else torch.bfloat16)

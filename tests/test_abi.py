@@ -1,0 +1,132 @@
+"""The C ABI of libaq: the library loads, exports every entry point that
+include/aq.h declares, and rejects bad arguments on the host before anything
+is enqueued (these calls never reach a kernel, so they run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import group_wise_affine_aq_amd as aq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "aq.h")
+
+OK, INVALID, UNSUPPORTED, ALIGN = 0, -1, -2, -3
+F32, F16, BF16 = 0, 1, 2
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(aq_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(aq.lib_path()):
+        pytest.skip("libaq.so not built (run python -m group_wise_affine_aq_amd.build)")
+    return aq.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("aq_quantize", "aq_dequantize", "aq_qmv", "aq_qmm", "aq_gather_qmv",
+              "aq_quantized_matmul", "aq_codes_words", "aq_qweight_bytes", "aq_status_string"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(aq.lib_path())
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_host_helpers(lib):
+    assert aq.aq_codes_words(4096, 4) == 512
+    assert aq.aq_codes_words(4096, 3) == 384
+    assert aq.aq_codes_words(33, 4) == -1
+    # 4.5 bits per weight at G=64, 4 bits ("Quantizing a Model for MLX")
+    assert aq.aq_qweight_bytes(4096, 14336, 64, 4) == 33030144
+    assert aq.aq_qweight_bytes(1, 70553706496, 64, 4) == 39686459904
+    assert aq.aq_qweight_bytes(10, 100, 64, 4) == -1
+    assert "INVALID" in aq.aq_status_string(INVALID)
+    assert aq.aq_version().startswith("libaq")
+
+
+P = 0x10000  # fake, 16-byte-aligned device addresses: never dereferenced
+MIS = 0x10002
+
+
+def qmv(lib, fn="aq_qmv", x=P, xdt=F16, M=1, codes=P, scales=P, biases=P, N=64, K=128, G=64,
+        bits=4, y=P):
+    return getattr(lib, fn)(x, xdt, M, codes, scales, biases, N, K, G, bits, y, None)
+
+
+@pytest.mark.parametrize("fn", ["aq_qmv", "aq_qmm", "aq_quantized_matmul"])
+def test_matmul_argument_errors(lib, fn):
+    assert qmv(lib, fn, bits=1) == INVALID
+    assert qmv(lib, fn, bits=9) == INVALID
+    assert qmv(lib, fn, G=16) == INVALID
+    assert qmv(lib, fn, G=48) == INVALID
+    assert qmv(lib, fn, K=96, G=64) == INVALID   # K % G != 0
+    assert qmv(lib, fn, N=0) == INVALID
+    assert qmv(lib, fn, K=0) == INVALID
+    assert qmv(lib, fn, M=0) == INVALID
+    assert qmv(lib, fn, xdt=F32) == INVALID
+    assert qmv(lib, fn, xdt=7) == INVALID
+    assert qmv(lib, fn, x=None) == INVALID
+    assert qmv(lib, fn, y=None) == INVALID
+    assert qmv(lib, fn, codes=None) == INVALID
+    assert qmv(lib, fn, scales=None) == INVALID
+    assert qmv(lib, fn, biases=None) == INVALID
+    assert qmv(lib, fn, x=MIS) == ALIGN
+    assert qmv(lib, fn, y=MIS) == ALIGN
+    assert qmv(lib, fn, codes=MIS) == ALIGN
+    assert qmv(lib, fn, scales=MIS) == ALIGN
+
+
+def test_qmv_rows_limit(lib):
+    assert qmv(lib, "aq_qmv", M=9) == INVALID
+
+
+def test_quantize_dequantize_argument_errors(lib):
+    q = lambda **k: lib.aq_quantize(k.get("w", P), k.get("dt", F32), k.get("N", 4), k.get("K", 64),
+                                    k.get("G", 64), k.get("bits", 4), k.get("codes", P),
+                                    k.get("scales", P), k.get("biases", P), None)
+    assert q(bits=0) == INVALID
+    assert q(G=256) == INVALID
+    assert q(K=100) == INVALID
+    assert q(dt=5) == INVALID
+    assert q(w=None) == INVALID
+    assert q(codes=None) == INVALID
+    assert q(w=MIS) == ALIGN
+    d = lambda **k: lib.aq_dequantize(k.get("codes", P), P, P, k.get("N", 4), k.get("K", 64), 64,
+                                      k.get("bits", 4), k.get("out", P), k.get("dt", F16), None)
+    assert d(bits=10) == INVALID
+    assert d(dt=9) == INVALID
+    assert d(out=None) == INVALID
+    assert d(out=MIS) == ALIGN
+    assert d(codes=MIS) == ALIGN
+
+
+def test_gather_argument_errors(lib):
+    g = lambda **k: lib.aq_gather_qmv(k.get("x", P), k.get("dt", F16), k.get("T", 4), P, P, P,
+                                      k.get("E", 8), 64, k.get("K", 128), k.get("ids", P),
+                                      k.get("topk", 2), k.get("G", 64), k.get("bits", 4),
+                                      k.get("y", P), None)
+    assert g(T=0) == INVALID
+    assert g(E=0) == INVALID
+    assert g(topk=0) == INVALID
+    assert g(ids=None) == INVALID
+    assert g(ids=MIS + 2) == ALIGN
+    assert g(K=100) == INVALID
+    assert g(dt=F32) == INVALID
+    assert g(E=70000) == UNSUPPORTED
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(aq, "_lib", None)
+    monkeypatch.setattr(aq, "lib_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="libaq.so not found"):
+        aq.load_library()

@@ -1,0 +1,271 @@
+"""GPU parity of every libaq entry point against the CPU reference, on seeded
+inputs at sizes the reference finishes in seconds, spanning several tiles,
+slices and ragged tails, across all bit widths, group sizes and dtypes.
+
+Bar: quantize and dequantize bit-exact; matmuls |y - y_ref| <= 2^-9*A + 1e-6
+per element with A = sum_k |x_k * w^_k| (w^ the reference's dequantized
+weight).  Inputs come only from the seeded generator and the reference."""
+import numpy as np
+import pytest
+
+import oracle
+from group_wise_affine_aq_amd import inputs
+from gpu_util import (bits_to_dev, out_bits, out_to_f64, packed_from_dev, packed_to_dev,
+                      to_dev, torch_dtype)
+
+pytestmark = pytest.mark.gpu
+
+ALL_BITS = [2, 3, 4, 5, 6, 7, 8]
+GROUP_FOR_BITS = {2: 32, 3: 64, 4: 64, 5: 128, 6: 32, 7: 64, 8: 128}
+
+
+@pytest.fixture(scope="module")
+def aq():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import group_wise_affine_aq_amd as mod
+    mod.load_library()
+    return mod
+
+
+def _quantized(N, K, G, bits, seed=0, outliers=True):
+    w = inputs.weights(N, K, seed=seed, key=(G, bits, 17), outliers=outliers)
+    return w, oracle.quantize(w, G, bits)
+
+
+def _assert_close(y_dev, y_ref, A, what):
+    ok, ratio = oracle.within_tolerance(out_to_f64(y_dev), y_ref, A)
+    assert ok, f"{what}: worst error/bound = {ratio:.3f}"
+    return ratio
+
+
+# ---- quantize -------------------------------------------------------------------------
+@pytest.mark.parametrize("bits", ALL_BITS)
+@pytest.mark.parametrize("G", [32, 64, 128])
+def test_quantize_bitexact_f32(aq, bits, G):
+    N, K = 37, 6 * G
+    w, (c, s, b) = _quantized(N, K, G, bits)
+    gc, gs, gb = packed_from_dev(*aq.aq_quantize(to_dev(w), G, bits))
+    assert np.array_equal(gs, s) and np.array_equal(gb, b)
+    assert np.array_equal(gc, c)
+
+
+@pytest.mark.parametrize("wdt", ["f16", "bf16"])
+@pytest.mark.parametrize("bits", [3, 4, 8])
+def test_quantize_bitexact_half_inputs(aq, wdt, bits):
+    G, N, K = 64, 29, 512
+    wb = inputs.to_bits(inputs.weights(N, K, seed=2, outliers=True), wdt)
+    w32 = inputs.from_bits(wb, wdt).astype(np.float32)  # exact widening
+    c, s, b = oracle.quantize(w32, G, bits)
+    gc, gs, gb = packed_from_dev(*aq.aq_quantize(bits_to_dev(wb, wdt), G, bits))
+    assert np.array_equal(gs, s) and np.array_equal(gb, b) and np.array_equal(gc, c)
+
+
+@pytest.mark.parametrize("bits", ALL_BITS)
+def test_quantize_edge_groups(aq, bits):
+    """Constant, zero and -0 groups, fp32 subnormals, exact half-step ties,
+    the fp16 range ends and groups spanning many binades."""
+    G = 32
+    L = (1 << bits) - 1
+    rng = np.random.default_rng(bits)
+    rows = []
+    rows.append(np.zeros(G))
+    rows.append(-np.zeros(G))
+    rows.append(np.full(G, 0.123))
+    rows.append(np.full(G, -7.5))
+    rows.append(rng.standard_normal(G) * 1e-40)          # binary32 subnormals
+    rows.append(rng.standard_normal(G) * 1e-6)           # fp16 subnormal range
+    rows.append(np.linspace(-65504.0, 60000.0, G))        # fp16 range ends
+    rows.append(rng.standard_normal(G) * 10.0 ** rng.integers(-8, 4, G))
+    s0, b0 = 2.0 ** -8, float(np.float16(-0.37))
+    j = rng.integers(0, L, G)
+    t = b0 + (j + 0.5) * s0                                # exact ties
+    t[0], t[1] = b0, b0 + L * s0
+    rows.append(t)
+    q = rng.integers(0, L + 1, G)
+    q[0], q[1] = 0, L
+    rows.append(b0 + q * s0)                               # exact grid points
+    w = np.array(rows, dtype=np.float32)
+    c, s, b = oracle.quantize(w, G, bits)
+    gc, gs, gb = packed_from_dev(*aq.aq_quantize(to_dev(w), G, bits))
+    assert np.array_equal(gb, b), np.argwhere(gb != b)
+    assert np.array_equal(gs, s), np.argwhere(gs != s)
+    assert np.array_equal(gc, c)
+
+
+# ---- dequantize -------------------------------------------------------------------------
+@pytest.mark.parametrize("bits", ALL_BITS)
+@pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
+def test_dequantize_bitexact(aq, bits, out):
+    G = GROUP_FOR_BITS[bits]
+    N, K = 23, 4 * G
+    _, (c, s, b) = _quantized(N, K, G, bits, seed=3)
+    code = {"f32": oracle.F32, "f16": oracle.F16, "bf16": oracle.BF16}[out]
+    ref = oracle.dequantize(c, s, b, K, G, bits, code)
+    got = aq.aq_dequantize(*packed_to_dev(c, s, b), G, bits, out_dtype=torch_dtype(out))
+    ref_bits = ref.view(np.uint32) if out == "f32" else ref
+    assert np.array_equal(out_bits(got), ref_bits)
+
+
+# ---- QMV (M <= 8) ---------------------------------------------------------------------------
+@pytest.mark.parametrize("bits", ALL_BITS)
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+def test_qmv_parity(aq, bits, M, xdt):
+    G = GROUP_FOR_BITS[bits]
+    N, K = 67, 4224 if G == 128 else 4160  # several slices at M=8, ragged tails
+    _, (c, s, b) = _quantized(N, K, G, bits, seed=4)
+    xb = inputs.activations(M, K, xdt, seed=4, key=(bits, M))
+    y_ref, A = oracle.matmul(inputs.from_bits(xb, xdt), c, s, b, K, G, bits)
+    y = aq.aq_qmv(bits_to_dev(xb, xdt), *packed_to_dev(c, s, b), G, bits)
+    _assert_close(y, y_ref, A, f"qmv b{bits} M{M} {xdt}")
+
+
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+@pytest.mark.parametrize("N,K,G", [(1, 32, 32), (1, 64, 64), (3, 128, 128), (200, 96, 32),
+                                   (129, 2048, 64), (5, 32768, 64)])
+def test_qmv_shapes(aq, xdt, N, K, G):
+    bits = 4
+    _, (c, s, b) = _quantized(N, K, G, bits, seed=5)
+    for M in (1, 4):
+        xb = inputs.activations(M, K, xdt, seed=5, key=(N, K, M))
+        y_ref, A = oracle.matmul(inputs.from_bits(xb, xdt), c, s, b, K, G, bits)
+        y = aq.aq_qmv(bits_to_dev(xb, xdt), *packed_to_dev(c, s, b), G, bits)
+        _assert_close(y, y_ref, A, f"qmv N{N} K{K} M{M}")
+
+
+def test_qmv_unit_vectors(aq):
+    """x = e_k picks column k of the dequantized matrix."""
+    G, bits, N, K = 64, 4, 40, 256
+    _, (c, s, b) = _quantized(N, K, G, bits, seed=6)
+    wd = oracle.dequantize_exact(c, s, b, K, G, bits)
+    for k in (0, 1, 7, 8, 63, 64, 200, 255):
+        xb = np.zeros((1, K), dtype=np.uint16)
+        xb[0, k] = 0x3C00  # 1.0 in fp16
+        y = out_to_f64(aq.aq_qmv(bits_to_dev(xb, "f16"), *packed_to_dev(c, s, b), G, bits))
+        assert np.all(np.abs(y[0] - wd[:, k]) <= np.ldexp(np.abs(wd[:, k]), -9) + 1e-6)
+
+
+# ---- QMM (any M) ---------------------------------------------------------------------------
+@pytest.mark.parametrize("bits", ALL_BITS)
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+def test_qmm_parity(aq, bits, xdt):
+    G = GROUP_FOR_BITS[bits]
+    M, N, K = 130, 200, 4224 if G == 128 else 4160
+    _, (c, s, b) = _quantized(N, K, G, bits, seed=7)
+    xb = inputs.activations(M, K, xdt, seed=7, key=(bits,))
+    y_ref, A = oracle.matmul(inputs.from_bits(xb, xdt), c, s, b, K, G, bits)
+    y = aq.aq_qmm(bits_to_dev(xb, xdt), *packed_to_dev(c, s, b), G, bits)
+    _assert_close(y, y_ref, A, f"qmm b{bits} {xdt}")
+
+
+@pytest.mark.parametrize("M,N,K,G", [(1, 1, 32, 32), (7, 33, 96, 32), (64, 128, 64, 64),
+                                     (257, 129, 160, 32), (33, 300, 1024, 128)])
+def test_qmm_shapes_f16(aq, M, N, K, G):
+    """Ragged tiles and K tails.  fp16: the dequantized weight (2^-11 relative)
+    and the fp16 output rounding keep the error under the bound for any input."""
+    bits, xdt = 4, "f16"
+    _, (c, s, b) = _quantized(N, K, G, bits, seed=8)
+    xb = inputs.activations(M, K, xdt, seed=8, key=(M, N, K))
+    y_ref, A = oracle.matmul(inputs.from_bits(xb, xdt), c, s, b, K, G, bits)
+    y = aq.aq_qmm(bits_to_dev(xb, xdt), *packed_to_dev(c, s, b), G, bits)
+    _assert_close(y, y_ref, A, f"qmm {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K,G", [(1, 1, 2048, 32), (7, 33, 2080, 32), (257, 129, 2112, 64),
+                                     (33, 300, 4096, 128)])
+def test_qmm_shapes_bf16(aq, M, N, K, G):
+    """bf16 at the workloads' depth (K >= 2048).  A bf16 output alone may be
+    off by 2^-8*|y|, which the bound 2^-9*A covers only while |y| <= A/2 -- true
+    for such K (|y|/A ~ 1/sqrt(K)), not for tiny K, for any kernel."""
+    bits, xdt = 4, "bf16"
+    _, (c, s, b) = _quantized(N, K, G, bits, seed=8)
+    xb = inputs.activations(M, K, xdt, seed=8, key=(M, N, K))
+    y_ref, A = oracle.matmul(inputs.from_bits(xb, xdt), c, s, b, K, G, bits)
+    y = aq.aq_qmm(bits_to_dev(xb, xdt), *packed_to_dev(c, s, b), G, bits)
+    _assert_close(y, y_ref, A, f"qmm {M}x{N}x{K}")
+
+
+def test_qmm_equals_gemm_of_dequantized(aq):
+    """The matrix-core path multiplies exactly the bf16 weights that
+    aq_dequantize produces (accumulation order aside)."""
+    import torch
+    G, bits, M, N, K = 64, 4, 96, 160, 512
+    _, (c, s, b) = _quantized(N, K, G, bits, seed=9)
+    xb = inputs.activations(M, K, "bf16", seed=9)
+    x = bits_to_dev(xb, "bf16")
+    dev = packed_to_dev(c, s, b)
+    wq = aq.aq_dequantize(*dev, G, bits, out_dtype=torch.bfloat16)
+    ref = (x.float() @ wq.float().T).double().cpu().numpy()
+    y = out_to_f64(aq.aq_qmm(x, *dev, G, bits))
+    assert np.max(np.abs(y - ref) / (np.abs(ref) + 1e-3)) < 2 ** -7
+
+
+# ---- dispatch ----------------------------------------------------------------------------------
+@pytest.mark.parametrize("M", [1, 3, 8, 9, 40])
+def test_quantized_matmul_dispatch(aq, M):
+    G, bits, N, K, xdt = 64, 4, 100, 640, "f16"
+    _, (c, s, b) = _quantized(N, K, G, bits, seed=10)
+    xb = inputs.activations(M, K, xdt, seed=10, key=(M,))
+    y_ref, A = oracle.matmul(inputs.from_bits(xb, xdt), c, s, b, K, G, bits)
+    y = aq.aq_quantized_matmul(bits_to_dev(xb, xdt), *packed_to_dev(c, s, b), G, bits)
+    _assert_close(y, y_ref, A, f"dispatch M{M}")
+
+
+# ---- gather (MoE) ---------------------------------------------------------------------------------
+def _experts(E, N, K, G, bits, seed):
+    q = [oracle.quantize(inputs.weights(N, K, seed=seed, key=(e, G, bits)), G, bits)
+         for e in range(E)]
+    return (np.stack([a for a, _, _ in q]), np.stack([s for _, s, _ in q]),
+            np.stack([b for _, _, b in q]))
+
+
+@pytest.mark.parametrize("bits", ALL_BITS)
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+def test_gather_parity(aq, bits, xdt):
+    G = GROUP_FOR_BITS[bits]
+    E, N, K, T, topk = 8, 100, 4 * G, 9, 3
+    c, s, b = _experts(E, N, K, G, bits, seed=11)
+    ids = inputs.expert_ids(T, E, topk, seed=11)
+    xb = inputs.activations(T, K, xdt, seed=11)
+    y_ref, A = oracle.gather_matmul(inputs.from_bits(xb, xdt), c, s, b, ids, K, G, bits)
+    y = aq.aq_gather_qmv(bits_to_dev(xb, xdt), *packed_to_dev(c, s, b), to_dev(ids), G, bits)
+    _assert_close(y, y_ref, A, f"gather b{bits} {xdt}")
+
+
+def test_gather_crowded_expert_and_bad_ids(aq):
+    """More tokens on one expert than one batch holds (processed in batches),
+    unused experts, and ids outside [0, E) (their rows come back zero)."""
+    G, bits, E, N, K, T, topk = 64, 4, 6, 70, 256, 21, 2
+    c, s, b = _experts(E, N, K, G, bits, seed=12)
+    ids = np.full((T, topk), 3, dtype=np.int32)
+    ids[:, 1] = 1
+    ids[5, 1] = 5
+    xb = inputs.activations(T, K, "f16", seed=12)
+    y_ref, A = oracle.gather_matmul(inputs.from_bits(xb, "f16"), c, s, b, ids, K, G, bits)
+    y = aq.aq_gather_qmv(bits_to_dev(xb, "f16"), *packed_to_dev(c, s, b), to_dev(ids), G, bits)
+    _assert_close(y, y_ref, A, "gather crowded")
+    bad = ids.copy()
+    bad[2, 0], bad[7, 1] = -1, E
+    import torch
+    yb = torch.full((T, topk, N), 7.0, dtype=torch.float16, device="cuda")
+    aq.aq_gather_qmv(bits_to_dev(xb, "f16"), *packed_to_dev(c, s, b), to_dev(bad), G, bits, y=yb)
+    yb = out_to_f64(yb)
+    assert np.all(yb[2, 0] == 0) and np.all(yb[7, 1] == 0)
+    keep = np.ones((T, topk), bool)
+    keep[2, 0] = keep[7, 1] = False
+    ok, _ = oracle.within_tolerance(yb[keep], y_ref[keep], A[keep])
+    assert ok
+
+
+def test_gather_all_same_expert_is_qmv(aq):
+    G, bits, E, N, K, T = 64, 4, 4, 90, 512, 8
+    c, s, b = _experts(E, N, K, G, bits, seed=13)
+    ids = np.full((T, 1), 2, dtype=np.int32)
+    xb = inputs.activations(T, K, "f16", seed=13)
+    dev = packed_to_dev(c, s, b)
+    yg = out_to_f64(aq.aq_gather_qmv(bits_to_dev(xb, "f16"), *dev, to_dev(ids), G, bits))
+    yq = out_to_f64(aq.aq_qmv(bits_to_dev(xb, "f16"), dev[0][2].contiguous(),
+                              dev[1][2].contiguous(), dev[2][2].contiguous(), G, bits))
+    assert np.array_equal(yg[:, 0, :], yq)
