@@ -120,7 +120,7 @@ aq_status aq_qmm(const void *x, aq_dtype x_dtype, int64_t M, const uint32_t *cod
                  int group_size, int bits, void *y, void *stream) {
   aq_status st = check_matmul(x, x_dtype, M, codes, scales, biases, N, K, group_size, bits, y);
   if (st != AQ_OK) return st;
-  if (M > (int64_t)65535 * 128 || (N + 127) / 128 > 0x7FFFFFFF) return AQ_ERR_UNSUPPORTED;
+  if (((M + 255) / 256) * ((N + 223) / 224) > 0x7FFFFFFF) return AQ_ERR_UNSUPPORTED;
   return from_hip(aq::launch_qmm(x, (int)x_dtype, M, codes, scales, biases, N, K, group_size,
                                  bits, y, static_cast<hipStream_t>(stream)));
 }
