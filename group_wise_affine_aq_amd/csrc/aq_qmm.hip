@@ -33,12 +33,24 @@ typedef float f32x16v __attribute__((ext_vector_type(16)));
 constexpr int BM = 256, BN = 224, BK = 64;
 constexpr int WM = 64, WN = 224;            // wave sub-tile
 constexpr int FM = WM / 32, FN = WN / 32;   // 32x32 blocks per wave: 2 x 7
-constexpr int kPitch = BK + 8;              // elements per LDS row (144 bytes)
 constexpr int kThreads = 256;
-constexpr int kXLoads = BM * BK / 8 / kThreads;      // 16-byte X loads per thread per step: 8
-constexpr int kWPerThread = 2;                       // 32-code chunks per thread per step
-constexpr int kWRows = kThreads * kWPerThread / 2;   // 256 LDS W rows; rows >= BN are never read
-constexpr int kStageElems = (BM + kWRows) * kPitch;
+// LDS: [X stage 0][X stage 1][W stage 0][W stage 1]
+constexpr int kXStage = BM * BK * 2;            // 32 KB: 128-byte rows, 16-byte units swizzled
+constexpr int kWPitch = (BK + 8) * 2;           // 144-byte W rows
+constexpr int kWRows = 256;                     // rows >= BN are written, never read
+constexpr int kWStage = kWRows * kWPitch;       // 36 KB
+constexpr int kLdsBytes = 2 * (kXStage + kWStage);
+constexpr int kXDma = BM * BK / 8 / kThreads;   // 16-byte X units per thread per step: 8
+constexpr int kWChunks = 2;                     // 32-code W chunks per thread per step
+
+// loads issued for one W chunk (codes, scale, bias)
+template <int BITS>
+constexpr int kChunkLoads = (BITS % 4 == 0 ? BITS / 4 : (BITS % 2 == 0 ? BITS / 2 : BITS)) + 2;
+
+// s_waitcnt immediate that waits until at most n vector-memory operations are
+// outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
+// left at their maxima)
+constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
 
 template <typename XT>
 __device__ __forceinline__ f32x16v mfma32(uint4 a, uint4 b, f32x16v c) {
@@ -62,101 +74,101 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   }
 }
 
-// 32 dequantized values of one chunk, packed in pairs of the activation type
-template <int BITS, typename XT>
-__device__ __forceinline__ void dequant_chunk(const uint32_t *w, float s, float b, uint32_t *p) {
+// v & 0x0F0F0F0F as an opaque operation, so that the byte-wise conversions
+// below stay v_cvt_f32_ubyte{0..3} instead of being folded into per-code
+// bit-field extracts
+__device__ __forceinline__ uint32_t nibbles(uint32_t v) {
+  uint32_t r;
+  asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(r) : "v"(v));
+  return r;
+}
+
+// Codes 8u .. 8u+7 of a 32-code chunk dequantized (q*s + b in binary32,
+// rounded to nearest even into the activation type) and packed in pairs.
+template <int BITS, typename XT, int U>
+__device__ __forceinline__ uint4 dequant8(const uint32_t *w, float s, float b) {
+  uint32_t p[4];
   if constexpr (BITS == 4) {
-    // bytes of lo hold codes 0,2,4,6 of a word, bytes of hi codes 1,3,5,7
+    const uint32_t lo = nibbles(w[U]), hi = nibbles(w[U] >> 4);  // codes 0,2,4,6 / 1,3,5,7
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t lo = w[j] & 0x0F0F0F0Fu, hi = (w[j] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float v0 = __builtin_fmaf((float)((lo >> (8 * e)) & 0xFFu), s, b);
-        const float v1 = __builtin_fmaf((float)((hi >> (8 * e)) & 0xFFu), s, b);
-        p[4 * j + e] = pack2<XT>(v0, v1);
-      }
-    }
+    for (int e = 0; e < 4; ++e)
+      p[e] = pack2<XT>(__builtin_fmaf((float)((lo >> (8 * e)) & 0xFFu), s, b),
+                       __builtin_fmaf((float)((hi >> (8 * e)) & 0xFFu), s, b));
   } else if constexpr (BITS == 8) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float v0 = __builtin_fmaf((float)(w[j] & 0xFFu), s, b);
-      const float v1 = __builtin_fmaf((float)((w[j] >> 8) & 0xFFu), s, b);
-      const float v2 = __builtin_fmaf((float)((w[j] >> 16) & 0xFFu), s, b);
-      const float v3 = __builtin_fmaf((float)(w[j] >> 24), s, b);
-      p[2 * j] = pack2<XT>(v0, v1);
-      p[2 * j + 1] = pack2<XT>(v2, v3);
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t v = w[2 * U + j];
+      p[2 * j] = pack2<XT>(__builtin_fmaf((float)(v & 0xFFu), s, b),
+                           __builtin_fmaf((float)((v >> 8) & 0xFFu), s, b));
+      p[2 * j + 1] = pack2<XT>(__builtin_fmaf((float)((v >> 16) & 0xFFu), s, b),
+                               __builtin_fmaf((float)(v >> 24), s, b));
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float v0 = __builtin_fmaf((float)chunk_code<BITS>(w, 2 * i), s, b);
-      const float v1 = __builtin_fmaf((float)chunk_code<BITS>(w, 2 * i + 1), s, b);
-      p[i] = pack2<XT>(v0, v1);
-    }
+    for (int e = 0; e < 4; ++e)
+      p[e] = pack2<XT>(__builtin_fmaf((float)chunk_code<BITS>(w, 8 * U + 2 * e), s, b),
+                       __builtin_fmaf((float)chunk_code<BITS>(w, 8 * U + 2 * e + 1), s, b));
   }
+  return make_uint4(p[0], p[1], p[2], p[3]);
 }
 
 // Buffer loads: a resource (base, size in bytes) per operand tile; offsets past
 // the size read as zero, so partial tiles need no branches.  0x00020000 is
-// the gfx9 descriptor word for untyped 32-bit data.
+// the gfx9 descriptor word for untyped 32-bit data.  The per-step part of an
+// address goes in the scalar offset.
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
   const int n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (bytes < 0 ? 0 : (int)bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, 0x00020000);
 }
-__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-  return make_uint4(v[0], v[1], v[2], v[3]);
-}
 template <int BITS>
-__device__ __forceinline__ void bload_chunk(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t *w) {
+__device__ __forceinline__ void bload_chunk(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                            uint32_t *w) {
   if constexpr (BITS % 4 == 0) {
 #pragma unroll
     for (int j = 0; j < BITS / 4; ++j) {
-      const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + 16 * j), 0, 0);
+      const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(voff + 16 * j), (int)soff, 0);
       w[4 * j] = v[0]; w[4 * j + 1] = v[1]; w[4 * j + 2] = v[2]; w[4 * j + 3] = v[3];
     }
   } else if constexpr (BITS % 2 == 0) {
 #pragma unroll
     for (int j = 0; j < BITS / 2; ++j) {
-      const u32x2v v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)(off + 8 * j), 0, 0);
+      const u32x2v v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)(voff + 8 * j), (int)soff, 0);
       w[2 * j] = v[0]; w[2 * j + 1] = v[1];
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < BITS; ++j) w[j] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(off + 4 * j), 0, 0);
+    for (int j = 0; j < BITS; ++j)
+      w[j] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(voff + 4 * j), (int)soff, 0);
   }
 }
 
-// Scheduling hint for one segment of 14 MFMAs: NR LDS reads among the first
-// slots, NV vector ALU instructions after each MFMA, NW LDS writes among the
-// last slots and NG global loads among the first.
+// one thread's W chunks of one K step, as loaded
+template <int BITS>
+struct WRegs {
+  uint32_t w[kWChunks][BITS];
+  uint32_t s[kWChunks], b[kWChunks];
+};
+
+// Scheduling hint for one segment of 14 MFMAs: NR LDS reads and NG global
+// loads among the first slots, NV vector ALU instructions after each MFMA,
+// NW LDS writes among the last slots.
 template <int NR, int NV, int NW, int NG>
 __device__ __forceinline__ void sched_segment() {
 #pragma unroll
   for (int i = 0; i < FM * FN; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (i < NG) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     if (NV > 0) __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
     if (i >= FM * FN - NW) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-    if (i < NG) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
   }
 }
-// vector instructions to dequantize one 32-code chunk (approximate)
+// vector instructions to dequantize 8 codes (approximate)
 template <int BITS>
-constexpr int kDequantValu = BITS == 4 ? 100 : (BITS == 8 ? 90 : 120);
-
-// registers holding one K step's global data for this thread
-struct XRegs {
-  uint4 x[kXLoads];  // 8 activation values each
-};
-template <int BITS>
-struct WRegs {
-  uint32_t w[kWPerThread][BITS];  // 32-code chunks
-  uint32_t s[kWPerThread], b[kWPerThread];
-};
+constexpr int kDequant8Valu = BITS == 4 ? 24 : (BITS == 8 ? 22 : 30);
 
 template <int BITS, typename XT>
 __global__ __launch_bounds__(kThreads) void qmm_kernel(const uint16_t *__restrict__ x, int64_t M,
@@ -166,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const uint16_t *__restric
                                                        int64_t N, int64_t K, int G,
                                                        uint16_t *__restrict__ y, int mtiles,
                                                        int ntiles) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // [2][(BM + BN) * kPitch]
+  extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave;
@@ -185,80 +197,69 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const uint16_t *__restric
   // operand tiles as buffer resources: rows past M or N read as zero
   const int64_t mrows = M - tile_m < BM ? M - tile_m : BM;
   const int64_t nrows = N - tile_n < BN ? N - tile_n : BN;
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + tile_m * K, mrows * K * 2);
+  const int xbytes = (int)(mrows * K * 2);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + tile_m * K, xbytes);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(codes + tile_n * wpr, nrows * wpr * 4);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(scales + tile_n * gpr, nrows * gpr * 2);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(biases + tile_n * gpr, nrows * gpr * 2);
 
   // K steps: when K % 64 == 32 the lone last chunk is processed first (step
-  // 0, masked in the prologue), so every step inside the loop is full.
+  // 0, masked in the prologue), so every later step is full.
   const bool ktail = (K % BK) != 0;
   auto kbase = [&](int st) -> int {  // first k of step st
     return ktail ? (st == 0 ? (int)K - 32 : (st - 1) * BK) : st * BK;
   };
 
-  auto load_x = [&](int st, XRegs &r) {
-    const int k0 = kbase(st);
+  // X: each step's 256 x 64 tile goes straight to LDS (16 bytes per lane per
+  // load, landing at consecutive 16-byte slots).  LDS row r holds the row's
+  // unit u at slot u ^ ((r >> 1) & 7), so the fragment reads below are free
+  // of bank conflicts; load i of wave w fills rows 8 (8w + i) .. +7.
+  uint32_t xvoff[kXDma], xvoff_tail[kXDma];
 #pragma unroll
-    for (int i = 0; i < kXLoads; ++i) {
-      const int idx = tid + kThreads * i;
-      const int row = idx >> 3, c8 = idx & 7;
-      r.x[i] = bload16(rx, (uint32_t)(row * K + k0 + c8 * 8) * 2u);
-    }
-  };
-  auto load_w = [&](int st, WRegs<BITS> &r) {
-    const int c0 = kbase(st) >> 5;
+  for (int i = 0; i < kXDma; ++i) {
+    const int row = 8 * (wave * kXDma + i) + (lane >> 3);
+    const int u = (lane & 7) ^ ((row >> 1) & 7);
+    xvoff[i] = (uint32_t)(row * K + u * 8) * 2u;
+    xvoff_tail[i] = u < 4 ? xvoff[i] : (uint32_t)xbytes;  // k past K: out of range, reads zero
+  }
+  auto dma_x = [&](int st, int buf, const uint32_t (&vo)[kXDma]) {
+    const uint32_t so = (uint32_t)kbase(st) * 2u;
 #pragma unroll
-    for (int i = 0; i < kWPerThread; ++i) {
-      const int ch = tid + kThreads * i;  // rows >= BN read zeros (outside the resource)
-      const int row = ch >> 1;
-      int c = c0 + (ch & 1);
-      c = c < nch ? c : nch - 1;  // only in the tail step; masked there
-      bload_chunk<BITS>(rw, (uint32_t)(row * wpr + c * BITS) * 4u, r.w[i]);
-      const uint32_t go = (uint32_t)(row * gpr + (c >> gshift)) * 2u;
-      r.s[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)go, 0, 0);
-      r.b[i] = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)go, 0, 0);
-    }
+    for (int i = 0; i < kXDma; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rx, (lds_void *)(smem + buf * kXStage + (wave * kXDma + i) * 1024), 16, (int)vo[i], (int)so,
+          0, 0);
   };
 
-  // write a step (X as loaded; W dequantized) into LDS buffer `buf`; with
-  // `tail` the second 32 k of the step (past K) are zeroed
-  auto store_x = [&](const XRegs &rxr, int buf, bool tail) {
-    uint16_t *lx = lds + buf * kStageElems;
+  // W: thread chunk c (0, 1) is LDS row (tid + 256 c) / 2, half (tid & 1)
+  uint32_t wvoff[kWChunks], svoff[kWChunks];
 #pragma unroll
-    for (int i = 0; i < kXLoads; ++i) {
-      const int idx = tid + kThreads * i;
-      const int row = idx >> 3, c8 = idx & 7;
-      const uint4 v = (tail && c8 >= 4) ? make_uint4(0, 0, 0, 0) : rxr.x[i];
-      *reinterpret_cast<uint4 *>(lx + row * kPitch + c8 * 8) = v;
-    }
+  for (int c = 0; c < kWChunks; ++c) {
+    const int ch = tid + kThreads * c, row = ch >> 1, half = ch & 1;
+    wvoff[c] = (uint32_t)(row * wpr + half * BITS) * 4u;
+    svoff[c] = (uint32_t)(row * gpr + (gshift == 0 ? half : 0)) * 2u;
+  }
+  auto load_w_chunk = [&](int st, int c, WRegs<BITS> &r) {
+    const int c0 = kbase(st) >> 5;
+    bload_chunk<BITS>(rw, wvoff[c], (uint32_t)(c0 * BITS) * 4u, r.w[c]);
+    const uint32_t so = (uint32_t)(c0 >> gshift) * 2u;
+    r.s[c] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)svoff[c], (int)so, 0);
+    r.b[c] = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)svoff[c], (int)so, 0);
   };
-  auto store_w_chunk = [&](const WRegs<BITS> &r, int i, int buf) {
-    uint16_t *lw = lds + buf * kStageElems + BM * kPitch;
-    const int ch = tid + kThreads * i;  // rows >= BN land in pad rows nobody reads
-    const int row = ch >> 1, half = ch & 1;
-    uint32_t p[16];
-    dequant_chunk<BITS, XT>(r.w[i], f16_to_f32((uint16_t)r.s[i]), f16_to_f32((uint16_t)r.b[i]), p);
-    uint4 *dst = reinterpret_cast<uint4 *>(lw + row * kPitch + half * 32);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      dst[j] = make_uint4(p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]);
+  char *const wst0 = smem + 2 * kXStage;
+  // dequantize codes 8u .. 8u+7 of chunk c into W stage `buf`
+  auto store_w8 = [&](const WRegs<BITS> &r, int c, auto ucon, int buf, bool zero) {
+    constexpr int U = decltype(ucon)::value;
+    const int ch = tid + kThreads * c, row = ch >> 1, half = ch & 1;
+    const uint4 v = dequant8<BITS, XT, U>(r.w[c], f16_to_f32((uint16_t)r.s[c]),
+                                          f16_to_f32((uint16_t)r.b[c]));
+    *reinterpret_cast<uint4 *>(wst0 + buf * kWStage + row * kWPitch + half * 64 + U * 16) =
+        zero ? make_uint4(0, 0, 0, 0) : v;
   };
-  auto store_w = [&](const WRegs<BITS> &r, int buf, bool tail) {
-    uint16_t *lw = lds + buf * kStageElems + BM * kPitch;
-#pragma unroll
-    for (int i = 0; i < kWPerThread; ++i) {
-      const int ch = tid + kThreads * i;
-      const int row = ch >> 1, half = ch & 1;
-      uint32_t p[16];
-      dequant_chunk<BITS, XT>(r.w[i], f16_to_f32((uint16_t)r.s[i]), f16_to_f32((uint16_t)r.b[i]), p);
-      uint4 *dst = reinterpret_cast<uint4 *>(lw + row * kPitch + half * 32);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        dst[j] = (tail && half) ? make_uint4(0, 0, 0, 0)
-                                : make_uint4(p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]);
-    }
-  };
+  using U0 = std::integral_constant<int, 0>;
+  using U1 = std::integral_constant<int, 1>;
+  using U2 = std::integral_constant<int, 2>;
+  using U3 = std::integral_constant<int, 3>;
 
   f32x16v acc[FM][FN];
 #pragma unroll
@@ -268,15 +269,21 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const uint16_t *__restric
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // fragment addressing: lane l supplies row (l % 32) of a block, k-group l / 32
-  const int frow = lane & 31, fk = (lane >> 5) * 8;
+  // fragments: lane l supplies row (l % 32) of a 32-row block and k units
+  // (l / 32) + 2 kk of the step (8 k each)
+  const int xrow = wm * WM + (lane & 31);
+  uint32_t xfo[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    xfo[kk] = (uint32_t)(xrow * 128 + ((((lane >> 5) + 2 * kk) ^ ((lane >> 1) & 7)) * 16));
+  const uint32_t wfo = (uint32_t)((lane & 31) * kWPitch + (lane >> 5) * 16);
   auto frag = [&](int buf, int kk, uint4(&a)[FM], uint4(&b)[FN]) {
-    const uint16_t *lx = lds + buf * kStageElems + (wm * WM + frow) * kPitch + fk + kk * 16;
-    const uint16_t *lw = lds + buf * kStageElems + BM * kPitch + frow * kPitch + fk + kk * 16;
+    const char *lx = smem + buf * kXStage + xfo[kk];
+    const char *lw = wst0 + buf * kWStage + wfo + kk * 32;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) a[i] = *reinterpret_cast<const uint4 *>(lx + i * 32 * kPitch);
+    for (int i = 0; i < FM; ++i) a[i] = *reinterpret_cast<const uint4 *>(lx + i * 32 * 128);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) b[j] = *reinterpret_cast<const uint4 *>(lw + j * 32 * kPitch);
+    for (int j = 0; j < FN; ++j) b[j] = *reinterpret_cast<const uint4 *>(lw + j * 32 * kWPitch);
   };
   auto mfma_kk = [&](const uint4(&a)[FM], const uint4(&b)[FN]) {
 #pragma unroll
@@ -285,63 +292,98 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const uint16_t *__restric
       for (int i = 0; i < FM; ++i) acc[i][j] = mfma32<XT>(a[i], b[j], acc[i][j]);
   };
 
-  // One K step from LDS buffer cb.  With one wave per SIMD, matrix-core and
+  WRegs<BITS> wr[2];  // W of step s lives in wr[s & 1]
+  auto last = [&](int st) { return st < ksteps ? st : ksteps - 1; };
+
+  // One K step st from LDS stage cb.  With one wave per SIMD, matrix-core and
   // vector work overlap only through this wave's own instruction order, so
-  // the step is cut into four fenced segments, one per 16-k slice: each
-  // issues the fragment reads of the next slice, then its 14 MFMAs with a
-  // share of the next step's work between them (X stores, dequantization of
-  // one W chunk and its stores, the global loads two steps ahead).
-  auto step = [&](int cb, XRegs &xn, WRegs<BITS> &wn, bool more, int stw, int stx) {
+  // the step is cut into four fenced segments, one per 16-k slice: each issues
+  // the fragment reads of the next slice, then its 14 MFMAs with a quarter of
+  // the next step's work between them.  With `more`, step st + 1 is prepared
+  // in stage cb ^ 1: its X by DMA at the start, its W (loaded a step ago)
+  // dequantized 8 codes at a time; the W registers are then reloaded for
+  // step st + 3.  The DMA is waited for before the step ends (the barrier
+  // after it publishes stage cb ^ 1); the W loads stay in flight.
+  auto step = [&](auto cbcon, bool more, int st) {
+    constexpr int cb = decltype(cbcon)::value;
+    WRegs<BITS> &wn = wr[(cb + 1) & 1];  // st has the parity of cb
     uint4 fa[2][FM], fb[2][FN];
     frag(cb, 0, fa[0], fb[0]);
     __builtin_amdgcn_sched_barrier(0);
     frag(cb, 1, fa[1], fb[1]);
+    if (more) dma_x(st + 1, cb ^ 1, xvoff);
     mfma_kk(fa[0], fb[0]);
-    if (more) store_x(xn, cb ^ 1, false);
-    sched_segment<FM + FN, 0, kXLoads, 0>();
+    if (more) {
+      store_w8(wn, 0, U0{}, cb ^ 1, false);
+      store_w8(wn, 0, U1{}, cb ^ 1, false);
+    }
+    sched_segment<FM + FN, 2 * kDequant8Valu<BITS> / (FM * FN), 2, kXDma>();
     __builtin_amdgcn_sched_barrier(0);
     frag(cb, 2, fa[0], fb[0]);
     mfma_kk(fa[1], fb[1]);
-    if (more) store_w_chunk(wn, 0, cb ^ 1);
-    sched_segment<FM + FN, kDequantValu<BITS> / (FM * FN), 4, 0>();
+    if (more) {
+      store_w8(wn, 0, U2{}, cb ^ 1, false);
+      store_w8(wn, 0, U3{}, cb ^ 1, false);
+      load_w_chunk(last(st + 3), 0, wn);
+    }
+    sched_segment<FM + FN, 2 * kDequant8Valu<BITS> / (FM * FN), 2, 0>();
     __builtin_amdgcn_sched_barrier(0);
     frag(cb, 3, fa[1], fb[1]);
     mfma_kk(fa[0], fb[0]);
-    if (more) store_w_chunk(wn, 1, cb ^ 1);
-    sched_segment<FM + FN, kDequantValu<BITS> / (FM * FN), 4, 0>();
+    if (more) {
+      store_w8(wn, 1, U0{}, cb ^ 1, false);
+      store_w8(wn, 1, U1{}, cb ^ 1, false);
+    }
+    sched_segment<FM + FN, 2 * kDequant8Valu<BITS> / (FM * FN), 2, 0>();
     __builtin_amdgcn_sched_barrier(0);
     mfma_kk(fa[1], fb[1]);
     if (more) {
-      load_w(stw, wn);
-      load_x(stx, xn);
+      store_w8(wn, 1, U2{}, cb ^ 1, false);
+      store_w8(wn, 1, U3{}, cb ^ 1, false);
+      load_w_chunk(last(st + 3), 1, wn);
     }
-    sched_segment<0, 0, 0, kXLoads + 6>();
+    sched_segment<0, 2 * kDequant8Valu<BITS> / (FM * FN), 2, 0>();
     __builtin_amdgcn_sched_barrier(0);
+    if (more) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kWChunks * kChunkLoads<BITS>));
   };
 
-  // prologue: step 0 in buffer 0; X of step 1 and W of steps 1, 2 in flight
-  XRegs xr;
-  WRegs<BITS> wr[2];
-  load_x(0, xr);
-  load_w(0, wr[0]);
-  store_x(xr, 0, ktail);
-  store_w(wr[0], 0, ktail);
-  auto last = [&](int st) { return st < ksteps ? st : ksteps - 1; };
-  load_x(last(1), xr);
-  load_w(last(1), wr[1]);
-  load_w(last(2), wr[0]);
+  // prologue: step 0 into stage 0 (masked past K when it is the tail chunk),
+  // W of steps 1 and 2 in flight
+  dma_x(0, 0, ktail ? xvoff_tail : xvoff);
+  load_w_chunk(0, 0, wr[0]);
+  load_w_chunk(0, 1, wr[0]);
+  load_w_chunk(last(1), 0, wr[1]);
+  load_w_chunk(last(1), 1, wr[1]);
+  const bool zhalf = ktail && (tid & 1);  // both chunks of a thread are in the same half
+  store_w8(wr[0], 0, U0{}, 0, zhalf);
+  store_w8(wr[0], 0, U1{}, 0, zhalf);
+  store_w8(wr[0], 0, U2{}, 0, zhalf);
+  store_w8(wr[0], 0, U3{}, 0, zhalf);
+  store_w8(wr[0], 1, U0{}, 0, zhalf);
+  store_w8(wr[0], 1, U1{}, 0, zhalf);
+  store_w8(wr[0], 1, U2{}, 0, zhalf);
+  store_w8(wr[0], 1, U3{}, 0, zhalf);
+  load_w_chunk(last(2), 0, wr[0]);
+  load_w_chunk(last(2), 1, wr[0]);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kWChunks * kChunkLoads<BITS>));
   __syncthreads();
 
-  // step st computes from buffer st & 1 while step st + 1 is written to the
-  // other buffer; past the last step the loads repeat it (branch-free body)
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
   int st = 0;
-  for (; st + 2 <= ksteps; st += 2) {
-    step(0, xr, wr[1], true, last(st + 3), last(st + 2));
+  for (; st + 2 < ksteps; st += 2) {
+    step(C0{}, true, st);
     __syncthreads();
-    step(1, xr, wr[0], true, last(st + 4), last(st + 3));
+    step(C1{}, true, st + 1);
     __syncthreads();
   }
-  if (st < ksteps) step(st & 1, xr, wr[0], false, 0, 0);  // odd step count: the last step
+  if (st + 1 < ksteps) {
+    step(C0{}, true, st);
+    __syncthreads();
+    step(C1{}, false, st + 1);
+  } else {
+    step(C0{}, false, st);
+  }
 
   // epilogue: accumulator r of lane l in a 32x32 block is row
   // 8*(r/4) + 4*(l/32) + r%4, column l % 32
@@ -363,7 +405,7 @@ hipError_t qmm_launch(const void *x, int64_t M, const uint32_t *codes, const uin
                       const uint16_t *biases, int64_t N, int64_t K, int G, void *y,
                       hipStream_t s) {
   auto kern = qmm_kernel<BITS, XT>;
-  const size_t lds = 2 * (size_t)kStageElems * sizeof(uint16_t);
+  const size_t lds = kLdsBytes;
   static bool attr = false;
   if (!attr) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -373,6 +415,7 @@ hipError_t qmm_launch(const void *x, int64_t M, const uint32_t *codes, const uin
   }
   const int64_t mt = (M + BM - 1) / BM, nt = (N + BN - 1) / BN;
   if (mt * nt > 0x7FFFFFFF || mt > 0x7FFFFFFF || nt > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if ((int64_t)BM * K * 2 > 0x7FFFFFFF) return hipErrorInvalidValue;  // 32-bit tile offsets
   hipLaunchKernelGGL(kern, dim3((unsigned)(mt * nt)), dim3(kThreads), lds, s, (const uint16_t *)x, M,
                      codes, scales, biases, N, K, G, (uint16_t *)y, (int)mt, (int)nt);
   return hipGetLastError();
