@@ -39,7 +39,7 @@ constexpr int kXStage = BM * BK * 2;            // 32 KB: 128-byte rows, 16-byte
 constexpr int kWPitch = (BK + 8) * 2;           // 144-byte W rows
 constexpr int kWRows = 256;                     // rows >= BN are written, never read
 constexpr int kWStage = kWRows * kWPitch;       // 36 KB
-constexpr int kLdsBytes = 2 * (kXStage + kWStage);
+static_assert(2 * (kXStage + kWStage) <= 160 * 1024, "LDS");
 constexpr int kXDma = BM * BK / 8 / kThreads;   // 16-byte X units per thread per step: 8
 constexpr int kWChunks = 2;                     // 32-code W chunks per thread per step
 
@@ -178,7 +178,10 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const uint16_t *__restric
                                                        int64_t N, int64_t K, int G,
                                                        uint16_t *__restrict__ y, int mtiles,
                                                        int ntiles) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  // four distinct LDS objects, so the compiler can tell the DMA target of a
+  // step from the buffers read and written beside it
+  __shared__ __attribute__((aligned(16))) char xs0[kXStage], xs1[kXStage];
+  __shared__ __attribute__((aligned(16))) char ws0[kWStage], ws1[kWStage];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave;
@@ -227,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const uint16_t *__restric
 #pragma unroll
     for (int i = 0; i < kXDma; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rx, (lds_void *)(smem + buf * kXStage + (wave * kXDma + i) * 1024), 16, (int)vo[i], (int)so,
+          rx, (lds_void *)((buf ? xs1 : xs0) + (wave * kXDma + i) * 1024), 16, (int)vo[i], (int)so,
           0, 0);
   };
 
@@ -246,14 +249,13 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const uint16_t *__restric
     r.s[c] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)svoff[c], (int)so, 0);
     r.b[c] = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)svoff[c], (int)so, 0);
   };
-  char *const wst0 = smem + 2 * kXStage;
   // dequantize codes 8u .. 8u+7 of chunk c into W stage `buf`
   auto store_w8 = [&](const WRegs<BITS> &r, int c, auto ucon, int buf, bool zero) {
     constexpr int U = decltype(ucon)::value;
     const int ch = tid + kThreads * c, row = ch >> 1, half = ch & 1;
     const uint4 v = dequant8<BITS, XT, U>(r.w[c], f16_to_f32((uint16_t)r.s[c]),
                                           f16_to_f32((uint16_t)r.b[c]));
-    *reinterpret_cast<uint4 *>(wst0 + buf * kWStage + row * kWPitch + half * 64 + U * 16) =
+    *reinterpret_cast<uint4 *>((buf ? ws1 : ws0) + row * kWPitch + half * 64 + U * 16) =
         zero ? make_uint4(0, 0, 0, 0) : v;
   };
   using U0 = std::integral_constant<int, 0>;
@@ -278,8 +280,8 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const uint16_t *__restric
     xfo[kk] = (uint32_t)(xrow * 128 + ((((lane >> 5) + 2 * kk) ^ ((lane >> 1) & 7)) * 16));
   const uint32_t wfo = (uint32_t)((lane & 31) * kWPitch + (lane >> 5) * 16);
   auto frag = [&](int buf, int kk, uint4(&a)[FM], uint4(&b)[FN]) {
-    const char *lx = smem + buf * kXStage + xfo[kk];
-    const char *lw = wst0 + buf * kWStage + wfo + kk * 32;
+    const char *lx = (buf ? xs1 : xs0) + xfo[kk];
+    const char *lw = (buf ? ws1 : ws0) + wfo + kk * 32;
 #pragma unroll
     for (int i = 0; i < FM; ++i) a[i] = *reinterpret_cast<const uint4 *>(lx + i * 32 * 128);
 #pragma unroll
@@ -405,18 +407,10 @@ hipError_t qmm_launch(const void *x, int64_t M, const uint32_t *codes, const uin
                       const uint16_t *biases, int64_t N, int64_t K, int G, void *y,
                       hipStream_t s) {
   auto kern = qmm_kernel<BITS, XT>;
-  const size_t lds = kLdsBytes;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
   const int64_t mt = (M + BM - 1) / BM, nt = (N + BN - 1) / BN;
   if (mt * nt > 0x7FFFFFFF || mt > 0x7FFFFFFF || nt > 0x7FFFFFFF) return hipErrorInvalidValue;
   if ((int64_t)BM * K * 2 > 0x7FFFFFFF) return hipErrorInvalidValue;  // 32-bit tile offsets
-  hipLaunchKernelGGL(kern, dim3((unsigned)(mt * nt)), dim3(kThreads), lds, s, (const uint16_t *)x, M,
+  hipLaunchKernelGGL(kern, dim3((unsigned)(mt * nt)), dim3(kThreads), 0, s, (const uint16_t *)x, M,
                      codes, scales, biases, N, K, G, (uint16_t *)y, (int)mt, (int)nt);
   return hipGetLastError();
 }
