@@ -9,14 +9,18 @@ matrix through the shape dispatch (aq_quantized_matmul), each on a cold copy
 of its packed weights: the step rotates over enough distinct copies (>= 1 GiB
 of packed weights in total, four times the 256 MB last-level cache) that
 every launch streams its weights from HBM.  Steps are replayed from HIP
-graphs (one per copy) so host launch overhead stays off the device timeline.
+graphs (one replay runs a step on every cold copy) so host launch overhead
+stays off the device timeline.
 
 value = packed weight bytes (codes + scales + biases) of the timed steps /
 the timed wall interval on the device (effective weight GB/s, the metric's
 first part).  The JSON line also carries:
-  roofline      the decode matrix-vector kernel's achieved algorithmic
-                bytes/s (weights + x + y per launch / average launch duration,
-                timed live with HIP events on the launch stream) vs 8 TB/s;
+  roofline      the dominant decode kernel's achieved algorithmic bytes/s
+                (weights + x + y per launch / average launch duration, timed
+                live with HIP events on the launch stream over graphs of
+                back-to-back launches) vs 8 TB/s, and its HBM traffic per
+                launch from the committed counter summary when it matches the
+                current kernel source;
   cpu_baseline  the CPU reference computing the same step on the host cores;
   qmm           the metric's second part: prefill Y = X @ W^T with X bf16
                 [2048, 8192] and W [28672, 8192] at 4-bit G=64 (plus 3-bit
@@ -113,22 +117,33 @@ def main():
         for m, (c, s, b) in zip(mats, sets[ci]):
             aq.aq_quantized_matmul(m["x"], c, s, b, G, BITS, y=m["y"])
 
-    # one graph per copy: a replay is exactly one step
+    # Steps are replayed from HIP graphs: `round_graph` holds one step on each
+    # cold copy in turn (a replay is `copies` steps), `step_graphs[ci]` one
+    # step on copy ci (for the remainder), so exactly K steps run.
     for ci in range(copies):  # eager pass first (also loads the kernels)
         step(ci)
     torch.cuda.synchronize()
-    graphs = []
     gstream = torch.cuda.Stream()
+    step_graphs = []
     with torch.cuda.stream(gstream):
+        round_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(round_graph, stream=gstream):
+            for ci in range(copies):
+                step(ci)
         for ci in range(copies):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=gstream):
                 step(ci)
-            graphs.append(g)
+            step_graphs.append(g)
     torch.cuda.synchronize()
 
-    for i in range(args.warmup):
-        graphs[i % copies].replay()
+    def run_steps(n):
+        for _ in range(n // copies):
+            round_graph.replay()
+        for ci in range(n % copies):
+            step_graphs[ci].replay()
+
+    run_steps(args.warmup)
     torch.cuda.synchronize()
 
     # ---- timed region: exactly K steps --------------------------------------------------
@@ -137,8 +152,7 @@ def main():
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record()
-    for i in range(args.steps):
-        graphs[i % copies].replay()
+    run_steps(args.steps)
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -148,38 +162,55 @@ def main():
     print(f"# timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step (device), "
           f"host wall {wall * 1e3 / args.steps:.2f} us/step", file=sys.stderr, flush=True)
 
-    # ---- per-kernel durations (HIP events on the launch stream) --------------------------
-    # A spin kernel keeps the device busy while the host queues every launch,
-    # so each event pair brackets back-to-back device work only.
-    reps = max(20, min(200, args.steps))
+    # ---- per-launch durations (HIP events on the launch stream) ---------------------------
+    # For each shape: one graph of `reps` back-to-back launches over the cold
+    # copies, replayed between two events on the launch stream; per-launch time
+    # = elapsed / reps.  It includes the dispatch gap between consecutive graph
+    # kernels, which kernel-trace durations leave out.
+    reps = 2 * copies
     per_shape = []
     for j, m in enumerate(mats):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(reps)]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(gstream):
+            with torch.cuda.graph(g, stream=gstream):
+                for r in range(reps):
+                    c, s, b = sets[r % copies][j]
+                    aq.aq_quantized_matmul(m["x"], c, s, b, G, BITS, y=m["y"])
         torch.cuda.synchronize()
-        _spin(torch)
-        for r in range(reps):
-            c, s, b = sets[r % copies][j]
-            evs[r][0].record(stream)
-            aq.aq_quantized_matmul(m["x"], c, s, b, G, BITS, y=m["y"])
-            evs[r][1].record(stream)
+        g.replay()
         torch.cuda.synchronize()
-        durs = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)  # us
+        durs = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            durs.append(e0.elapsed_time(e1) * 1e3 / reps)  # us per launch
+        del g
         avg = sum(durs) / len(durs)
+        cpl = -(-(m["K"] // 32) // 64)  # 64-chunk passes per row: the kernel's CPL
         per_shape.append(dict(shape=[m["N"], m["K"]], weight_bytes=m["wbytes"],
-                              avg_us=round(avg, 3), median_us=round(durs[len(durs) // 2], 3),
+                              algo_bytes=m["algo_bytes"], launches=reps * 5,
+                              kernel=f"qmv1_kernel<BITS={BITS}, f16, CPL={cpl}>",
+                              avg_us=round(avg, 3), min_us=round(min(durs), 3),
                               weight_gbs=round(m["wbytes"] / (avg * 1e-6) / 1e9, 1),
                               pct_hbm=round(100 * m["wbytes"] / (avg * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)))
-        print(f"# QMV {m['N']}x{m['K']}: avg {avg:.2f} us, median {durs[len(durs)//2]:.2f} us, "
+        print(f"# QMV {m['N']}x{m['K']} ({per_shape[-1]['kernel']}): {avg:.2f} us/launch in-graph, "
               f"{per_shape[-1]['weight_gbs']} GB/s weights", file=sys.stderr, flush=True)
-    total_algo = sum(m["algo_bytes"] for m in mats)
-    total_us = sum(p["avg_us"] for p in per_shape)
-    achieved = total_algo / (total_us * 1e-6) / 1e9
+    # the dominant kernel: the instantiation with the most device time per step
+    by_kernel = {}
+    for ps in per_shape:
+        by_kernel.setdefault(ps["kernel"], []).append(ps)
+    kname, group = max(by_kernel.items(), key=lambda kv: sum(p["avg_us"] for p in kv[1]))
+    g_algo = sum(p["algo_bytes"] for p in group)
+    g_us = sum(p["avg_us"] for p in group)
+    achieved = g_algo / (g_us * 1e-6) / 1e9
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=_traffic(mats, per_shape),
-                    kernel="qmv_kernel<BITS=4, MB=1, f16>",
-                    launches_per_step=len(mats), avg_launch_us=round(total_us / len(mats), 3),
-                    algo_bytes_per_launch=round(total_algo / len(mats)))
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=_traffic(kname, group),
+                    kernel=kname, shapes=[p["shape"] for p in group],
+                    launches_per_step=len(group), avg_launch_us=round(g_us / len(group), 3),
+                    algo_bytes_per_launch=round(g_algo / len(group)))
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -207,15 +238,15 @@ def main():
 
     # ---- prefill (QMM) ---------------------------------------------------------------------
     if not args.no_qmm:
-        del graphs, sets
+        del round_graph, step_graphs, sets
         torch.cuda.synchronize()
         result["qmm"] = _qmm(aq, inputs, dev, args.qmm_iters)
 
     print(json.dumps(result), flush=True)
 
 
-def _traffic(mats, per_shape):
-    """HBM bytes per launch of the decode kernel from the committed counter
+def _traffic(kname, group):
+    """HBM bytes per launch of the roofline kernel from the committed counter
     summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size),
     or None when no summary for the current kernel source exists."""
     import hashlib
@@ -229,7 +260,7 @@ def _traffic(mats, per_shape):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if kv.get("source_sha256_16") != sha:
+    if kv.get("source_sha256_16") != sha or kv.get("kernel") != kname:
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])

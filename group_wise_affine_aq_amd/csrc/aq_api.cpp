@@ -48,6 +48,24 @@ aq_status check_matmul(const void *x, int x_dtype, int64_t M, const uint32_t *co
 
 }  // namespace
 
+namespace aq {
+
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v <= 0)
+      v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+}  // namespace aq
+
 extern "C" {
 
 const char *aq_status_string(aq_status status) {

@@ -9,6 +9,9 @@ namespace aq {
 
 enum XType { X_F32 = 0, X_F16 = 1, X_BF16 = 2 };
 
+// compute units of the current device (cached per device)
+int device_cus();
+
 hipError_t launch_quantize(const void *w, int w_dtype, int64_t N, int64_t K, int G, int bits,
                            uint32_t *codes, uint16_t *scales, uint16_t *biases, hipStream_t s);
 

@@ -187,7 +187,8 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const uint16_t *__restric
   const int wm = wave;
 
   // XCD-aware tile order: block b runs on XCD b % 8; consecutive blocks of one
-  // XCD take consecutive tiles of a row-major (m, n) order, so they share m.
+  // XCD take consecutive tiles of a row-major (m, n) order, so they share m
+  // (the X row tile stays in that XCD's L2).
   const int tiles = mtiles * ntiles;
   int t = blockIdx.x;
   if ((tiles & 7) == 0) t = (t & 7) * (tiles >> 3) + (t >> 3);
@@ -209,9 +210,11 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const uint16_t *__restric
   // K steps: when K % 64 == 32 the lone last chunk is processed first (step
   // 0, masked in the prologue), so every later step is full.
   const bool ktail = (K % BK) != 0;
+  const int koff = ktail ? BK : 0;
   auto kbase = [&](int st) -> int {  // first k of step st
-    return ktail ? (st == 0 ? (int)K - 32 : (st - 1) * BK) : st * BK;
+    return ktail && st == 0 ? (int)K - 32 : st * BK - koff;
   };
+  auto kfull = [&](int st) -> int { return st * BK - koff; };  // st >= 1, branch-free
 
   // X: each step's 256 x 64 tile goes straight to LDS (16 bytes per lane per
   // load, landing at consecutive 16-byte slots).  LDS row r holds the row's
@@ -225,8 +228,8 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const uint16_t *__restric
     xvoff[i] = (uint32_t)(row * K + u * 8) * 2u;
     xvoff_tail[i] = u < 4 ? xvoff[i] : (uint32_t)xbytes;  // k past K: out of range, reads zero
   }
-  auto dma_x = [&](int st, int buf, const uint32_t (&vo)[kXDma]) {
-    const uint32_t so = (uint32_t)kbase(st) * 2u;
+  auto dma_x = [&](int k0, int buf, const uint32_t (&vo)[kXDma]) {
+    const uint32_t so = (uint32_t)k0 * 2u;
 #pragma unroll
     for (int i = 0; i < kXDma; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -242,8 +245,8 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const uint16_t *__restric
     wvoff[c] = (uint32_t)(row * wpr + half * BITS) * 4u;
     svoff[c] = (uint32_t)(row * gpr + (gshift == 0 ? half : 0)) * 2u;
   }
-  auto load_w_chunk = [&](int st, int c, WRegs<BITS> &r) {
-    const int c0 = kbase(st) >> 5;
+  auto load_w_chunk = [&](int k0, int c, WRegs<BITS> &r) {
+    const int c0 = k0 >> 5;
     bload_chunk<BITS>(rw, wvoff[c], (uint32_t)(c0 * BITS) * 4u, r.w[c]);
     const uint32_t so = (uint32_t)(c0 >> gshift) * 2u;
     r.s[c] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)svoff[c], (int)so, 0);
@@ -313,7 +316,7 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const uint16_t *__restric
     frag(cb, 0, fa[0], fb[0]);
     __builtin_amdgcn_sched_barrier(0);
     frag(cb, 1, fa[1], fb[1]);
-    if (more) dma_x(st + 1, cb ^ 1, xvoff);
+    if (more) dma_x(kfull(st + 1), cb ^ 1, xvoff);
     mfma_kk(fa[0], fb[0]);
     if (more) {
       store_w8(wn, 0, U0{}, cb ^ 1, false);
@@ -326,7 +329,7 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const uint16_t *__restric
     if (more) {
       store_w8(wn, 0, U2{}, cb ^ 1, false);
       store_w8(wn, 0, U3{}, cb ^ 1, false);
-      load_w_chunk(last(st + 3), 0, wn);
+      load_w_chunk(kfull(last(st + 3)), 0, wn);
     }
     sched_segment<FM + FN, 2 * kDequant8Valu<BITS> / (FM * FN), 2, 0>();
     __builtin_amdgcn_sched_barrier(0);
@@ -342,7 +345,7 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const uint16_t *__restric
     if (more) {
       store_w8(wn, 1, U2{}, cb ^ 1, false);
       store_w8(wn, 1, U3{}, cb ^ 1, false);
-      load_w_chunk(last(st + 3), 1, wn);
+      load_w_chunk(kfull(last(st + 3)), 1, wn);
     }
     sched_segment<0, 2 * kDequant8Valu<BITS> / (FM * FN), 2, 0>();
     __builtin_amdgcn_sched_barrier(0);
@@ -351,11 +354,11 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const uint16_t *__restric
 
   // prologue: step 0 into stage 0 (masked past K when it is the tail chunk),
   // W of steps 1 and 2 in flight
-  dma_x(0, 0, ktail ? xvoff_tail : xvoff);
-  load_w_chunk(0, 0, wr[0]);
-  load_w_chunk(0, 1, wr[0]);
-  load_w_chunk(last(1), 0, wr[1]);
-  load_w_chunk(last(1), 1, wr[1]);
+  dma_x(kbase(0), 0, ktail ? xvoff_tail : xvoff);
+  load_w_chunk(kbase(0), 0, wr[0]);
+  load_w_chunk(kbase(0), 1, wr[0]);
+  load_w_chunk(kbase(last(1)), 0, wr[1]);
+  load_w_chunk(kbase(last(1)), 1, wr[1]);
   const bool zhalf = ktail && (tid & 1);  // both chunks of a thread are in the same half
   store_w8(wr[0], 0, U0{}, 0, zhalf);
   store_w8(wr[0], 0, U1{}, 0, zhalf);
@@ -365,8 +368,8 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const uint16_t *__restric
   store_w8(wr[0], 1, U1{}, 0, zhalf);
   store_w8(wr[0], 1, U2{}, 0, zhalf);
   store_w8(wr[0], 1, U3{}, 0, zhalf);
-  load_w_chunk(last(2), 0, wr[0]);
-  load_w_chunk(last(2), 1, wr[0]);
+  load_w_chunk(kbase(last(2)), 0, wr[0]);
+  load_w_chunk(kbase(last(2)), 1, wr[0]);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kWChunks * kChunkLoads<BITS>));
   __syncthreads();
 
@@ -388,7 +391,8 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const uint16_t *__restric
   }
 
   // epilogue: accumulator r of lane l in a 32x32 block is row
-  // 8*(r/4) + 4*(l/32) + r%4, column l % 32
+  // 8*(r/4) + 4*(l/32) + r%4, column l % 32 (2-byte stores; staging the tile
+  // through LDS for 16-byte stores measured slower)
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll

@@ -748,19 +748,6 @@ constexpr int kRows = 2;  // rows per wave, sliced kernel and gather
 constexpr int kStreamWaves = AQ_STREAM_WAVES;  // one 16-wave workgroup per CU shares one x copy
 constexpr int kStreamLdsMax = 96 * 1024;
 
-int device_cus() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        v <= 0)
-      v = 256;
-    cus[dev] = v;
-  }
-  return cus[dev];
-}
 
 #ifndef AQ_STREAM_M1_DEPTH
 #define AQ_STREAM_M1_DEPTH 4
