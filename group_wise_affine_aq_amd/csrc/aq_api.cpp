@@ -13,6 +13,7 @@
 namespace {
 
 constexpr int64_t kMaxQmvRows = 8;
+constexpr int64_t kMaxQmmK = 0x7FFFFFFF / (256 * 2);  // 4194303
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -138,7 +139,9 @@ aq_status aq_qmm(const void *x, aq_dtype x_dtype, int64_t M, const uint32_t *cod
                  int group_size, int bits, void *y, void *stream) {
   aq_status st = check_matmul(x, x_dtype, M, codes, scales, biases, N, K, group_size, bits, y);
   if (st != AQ_OK) return st;
-  if (((M + 255) / 256) * ((N + 223) / 224) > 0x7FFFFFFF) return AQ_ERR_UNSUPPORTED;
+  // the kernel addresses a 256-row tile of x with 32-bit byte offsets
+  if (K > kMaxQmmK || ((M + 255) / 256) * ((N + 223) / 224) > 0x7FFFFFFF)
+    return AQ_ERR_UNSUPPORTED;
   return from_hip(aq::launch_qmm(x, (int)x_dtype, M, codes, scales, biases, N, K, group_size,
                                  bits, y, static_cast<hipStream_t>(stream)));
 }

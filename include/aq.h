@@ -121,8 +121,10 @@ aq_status aq_qmv(const void *x, aq_dtype x_dtype, int64_t M, const uint32_t *cod
 
 /* Quantized matrix-matrix product for prefill ("Quantization", metalworking,
  * QMM bullet): same operation and layouts as aq_qmv for any M >= 1.  Weight
- * tiles are dequantized to x_dtype (rounded to nearest even) and multiplied
- * on the matrix cores with binary32 accumulation. */
+ * tiles are dequantized to x_dtype (rounded to nearest even, the value
+ * aq_dequantize returns for that type) and multiplied on the matrix cores
+ * with binary32 accumulation.  AQ_ERR_UNSUPPORTED for K > 4194303 (a
+ * 256-row tile of x is addressed with 32-bit byte offsets). */
 aq_status aq_qmm(const void *x, aq_dtype x_dtype, int64_t M, const uint32_t *codes,
                  const uint16_t *scales, const uint16_t *biases, int64_t N, int64_t K,
                  int group_size, int bits, void *y, void *stream);

@@ -90,6 +90,12 @@ def test_qmv_rows_limit(lib):
     assert qmv(lib, "aq_qmv", M=9) == INVALID
 
 
+def test_qmm_depth_limit(lib):
+    # 256 rows of x must stay below 2^31 bytes: K <= 4194303
+    assert qmv(lib, "aq_qmm", M=16, K=4194304) == UNSUPPORTED
+    assert qmv(lib, "aq_quantized_matmul", M=16, K=4194304) == UNSUPPORTED
+
+
 def test_quantize_dequantize_argument_errors(lib):
     q = lambda **k: lib.aq_quantize(k.get("w", P), k.get("dt", F32), k.get("N", 4), k.get("K", 64),
                                     k.get("G", 64), k.get("bits", 4), k.get("codes", P),
