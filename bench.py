@@ -24,7 +24,11 @@ first part).  The JSON line also carries:
   cpu_baseline  the CPU reference computing the same step on the host cores;
   qmm           the metric's second part: prefill Y = X @ W^T with X bf16
                 [2048, 8192] and W [28672, 8192] at 4-bit G=64 (plus 3-bit
-                G=64 and 2-bit G=32), TFLOP/s vs the 2.5 PFLOP/s dense bf16 peak.
+                G=64 and 2-bit G=32), TFLOP/s vs the 2.5 PFLOP/s dense bf16 peak
+                and vs an MFMA-only loop measured on the device (with the
+                shader clock it runs at).
+Per decode shape the line also carries the time of a plain streaming read of
+the same bytes (same cold rotation and timing), a measured second denominator.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -198,6 +202,15 @@ def main():
                               pct_hbm=round(100 * m["wbytes"] / (avg * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)))
         print(f"# QMV {m['N']}x{m['K']} ({per_shape[-1]['kernel']}): {avg:.2f} us/launch in-graph, "
               f"{per_shape[-1]['weight_gbs']} GB/s weights", file=sys.stderr, flush=True)
+    # ---- second denominator: a plain streaming read of the same bytes -------------------
+    # Same cold rotation and the same graph timing, best of a few launch shapes.
+    for ps, m in zip(per_shape, mats):
+        ps["read_ceiling_us"] = round(_read_ceiling_us(aq, torch, m["wbytes"], stream), 3)
+        ps["read_ceiling_gbs"] = round(m["wbytes"] / (ps["read_ceiling_us"] * 1e-6) / 1e9, 1)
+        ps["frac_of_read_ceiling"] = round(ps["read_ceiling_us"] / ps["avg_us"], 3)
+        print(f"# plain read of {m['wbytes']} B: {ps['read_ceiling_us']:.2f} us "
+              f"({ps['read_ceiling_gbs']} GB/s); kernel at {ps['frac_of_read_ceiling']:.2f} of it",
+              file=sys.stderr, flush=True)
     # the dominant kernel: the instantiation with the most device time per step
     by_kernel = {}
     for ps in per_shape:
@@ -210,7 +223,10 @@ def main():
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=_traffic(kname, group),
                     kernel=kname, shapes=[p["shape"] for p in group],
                     launches_per_step=len(group), avg_launch_us=round(g_us / len(group), 3),
-                    algo_bytes_per_launch=round(g_algo / len(group)))
+                    algo_bytes_per_launch=round(g_algo / len(group)),
+                    read_ceiling_gbs=round(g_algo / (sum(p["read_ceiling_us"] for p in group)
+                                                     * 1e-6) / 1e9, 1),
+                    frac_of_read_ceiling=round(sum(p["read_ceiling_us"] for p in group) / g_us, 3))
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -243,6 +259,52 @@ def main():
         result["qmm"] = _qmm(aq, inputs, dev, args.qmm_iters)
 
     print(json.dumps(result), flush=True)
+
+
+def _read_ceiling_us(aq, torch, nbytes, stream):
+    """Per-launch time of a plain streaming read of nbytes cold bytes (graph of
+    back-to-back launches over >= 1 GiB of rotating buffers, HIP events)."""
+    copies = max(2, math.ceil(COLD_BYTES / nbytes))
+    bufs = [torch.empty(nbytes // 4, dtype=torch.int32, device=stream.device) for _ in range(copies)]
+    for b in bufs:
+        b.fill_(1)
+    sink = torch.zeros(4, dtype=torch.int32, device=stream.device)
+    best = float("inf")
+    gs = torch.cuda.Stream()
+    for blocks, unroll in ((512, 4), (1024, 4), (2048, 1), (512, 8)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(gs):
+            with torch.cuda.graph(g, stream=gs):
+                for i in range(copies):
+                    aq.aq_bench_stream_read(bufs[i], blocks, unroll, sink=sink)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e3 / copies)
+        del g
+    del bufs
+    torch.cuda.synchronize()
+    return best
+
+
+def _mfma_clock(aq, torch, cus):
+    """Shader clock and rate of an MFMA-only loop (one wave per SIMD on every CU)."""
+    iters = 20000
+    aq.aq_bench_mfma_clock(cus, 100)
+    torch.cuda.synchronize()
+    out = aq.aq_bench_mfma_clock(cus, iters)
+    torch.cuda.synchronize()
+    t = out.double().cpu()
+    secs = t[:, 1].mean().item() / 1e8
+    ghz = t[:, 0].mean().item() / secs / 1e9
+    tflops = 4 * cus * 14 * iters * 32768 / secs / 1e12
+    return round(ghz, 3), round(tflops, 1)
 
 
 def _traffic(kname, group):
@@ -316,7 +378,7 @@ def _qmm(aq, inputs, dev, iters):
     flop = 2 * M * N * K
     for bits, g in PREFILL["settings"]:
         c, s, b = aq.aq_quantize(w, g, bits)
-        for _ in range(3):
+        for _ in range(10):  # the clock settles over the first launches
             aq.aq_qmm(x, c, s, b, g, bits, y=y)
         torch.cuda.synchronize()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -329,15 +391,17 @@ def _qmm(aq, inputs, dev, iters):
         torch.cuda.synchronize()
         durs = sorted(a.elapsed_time(b) for a, b in evs)
         avg = sum(durs) / len(durs)
+        med = durs[len(durs) // 2]
         tf = flop / (avg * 1e-3) / 1e12
-        out[f"b{bits}_g{g}"] = {"avg_ms": round(avg, 4), "tflops": round(tf, 1),
+        out[f"b{bits}_g{g}"] = {"avg_ms": round(avg, 4), "median_ms": round(med, 4),
+                                "tflops": round(tf, 1),
                                 "pct_mfma_peak": round(100 * tf / MFMA_BF16_PEAK_TFLOPS, 1)}
-        print(f"# QMM {bits}-bit G={g}: {avg:.3f} ms, {tf:.1f} TFLOP/s", file=sys.stderr,
-              flush=True)
+        print(f"# QMM {bits}-bit G={g}: {avg:.3f} ms (median {med:.3f}), {tf:.1f} TFLOP/s",
+              file=sys.stderr, flush=True)
         del c, s, b
     # dense bf16 GEMM on the library GEMM (hipBLASLt) at the same shape, for context
     wd = w.to(torch.bfloat16)
-    for _ in range(3):
+    for _ in range(10):
         torch.matmul(x, wd.T)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -350,6 +414,13 @@ def _qmm(aq, inputs, dev, iters):
     out["dense_bf16_torch_matmul"] = {"avg_ms": round(avg, 4),
                                       "tflops": round(flop / (avg * 1e-3) / 1e12, 1)}
     out["peak_tflops"] = MFMA_BF16_PEAK_TFLOPS
+    # second denominator: an MFMA-only loop (no data movement) and the clock it runs at
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    ghz, tfl = _mfma_clock(aq, torch, cus)
+    out["mfma_only_loop"] = {"tflops": tfl, "sclk_ghz": ghz}
+    key = f"b{PREFILL['settings'][0][0]}_g{PREFILL['settings'][0][1]}"
+    out[key]["frac_of_mfma_only_loop"] = round(out[key]["tflops"] / tfl, 3)
+    print(f"# MFMA-only loop: {tfl:.1f} TFLOP/s at {ghz:.2f} GHz", file=sys.stderr, flush=True)
     return out
 
 

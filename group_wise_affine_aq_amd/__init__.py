@@ -65,6 +65,8 @@ def load_library():
         "aq_quantized_matmul": ([vp, i32, i64, vp, vp, vp, i64, i64, i32, i32, vp, vp], i32),
         "aq_gather_qmv": ([vp, i32, i64, vp, vp, vp, i64, i64, i64, vp, i32, i32, i32, vp, vp],
                           i32),
+        "aq_bench_stream_read": ([vp, i64, i32, i32, vp, vp], i32),
+        "aq_bench_mfma_clock": ([i32, i32, vp, vp], i32),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -212,3 +214,27 @@ def aq_gather_qmv(x, codes, scales, biases, ids, group_size: int, bits: int, y=N
                            _stream(stream))
     _check(st, "aq_gather_qmv")
     return y
+
+
+# ---- measurement helpers (include/aq_bench.h) ----------------------------------------------
+def aq_bench_stream_read(buf, blocks: int = 512, unroll: int = 4, sink=None, stream=None):
+    """Read all of the device tensor `buf` once with a plain streaming kernel."""
+    torch = _torch()
+    if sink is None:
+        sink = torch.zeros(4, dtype=torch.int32, device=buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    st = load_library().aq_bench_stream_read(_dev(buf, "buf"), nbytes, blocks, unroll,
+                                             _dev(sink, "sink"), _stream(stream))
+    _check(st, "aq_bench_stream_read")
+    return sink
+
+
+def aq_bench_mfma_clock(blocks: int, iters: int, out=None, stream=None):
+    """Per-wave (shader cycles, 100 MHz ticks) of an MFMA-only loop; int64 [4*blocks, 2]."""
+    torch = _torch()
+    if out is None:
+        out = torch.zeros((4 * blocks, 2), dtype=torch.int64, device=torch.device("cuda"))
+    st = load_library().aq_bench_mfma_clock(blocks, iters, _dev(out, "out"), _stream(stream))
+    _check(st, "aq_bench_mfma_clock")
+    return out
+

@@ -10,14 +10,14 @@ import pytest
 import group_wise_affine_aq_amd as aq
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "aq.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("aq.h", "aq_bench.h")]
 
 OK, INVALID, UNSUPPORTED, ALIGN = 0, -1, -2, -3
 F32, F16, BF16 = 0, 1, 2
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(aq_[a-z0-9_]+)\s*\(", text)))
 
@@ -88,6 +88,18 @@ def test_matmul_argument_errors(lib, fn):
 
 def test_qmv_rows_limit(lib):
     assert qmv(lib, "aq_qmv", M=9) == INVALID
+
+
+def test_bench_helper_argument_errors(lib):
+    assert lib.aq_bench_stream_read(P, 0, 512, 4, P, None) == INVALID
+    assert lib.aq_bench_stream_read(P, 24, 512, 4, P, None) == INVALID   # not a multiple of 16
+    assert lib.aq_bench_stream_read(P, 1024, 0, 4, P, None) == INVALID
+    assert lib.aq_bench_stream_read(P, 1024, 512, 3, P, None) == INVALID
+    assert lib.aq_bench_stream_read(None, 1024, 512, 4, P, None) == INVALID
+    assert lib.aq_bench_stream_read(MIS, 1024, 512, 4, P, None) == ALIGN
+    assert lib.aq_bench_mfma_clock(0, 10, P, None) == INVALID
+    assert lib.aq_bench_mfma_clock(4, 0, P, None) == INVALID
+    assert lib.aq_bench_mfma_clock(4, 10, None, None) == INVALID
 
 
 def test_qmm_depth_limit(lib):
