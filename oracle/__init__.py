@@ -66,6 +66,7 @@ def _load():
             "oracle_quantize": ([vp, i64, i64, i32, i32, vp, vp, vp], i32),
             "oracle_dequantize_exact": ([vp, vp, vp, i64, i64, i32, i32, vp], i32),
             "oracle_dequantize": ([vp, vp, vp, i64, i64, i32, i32, i32, vp], i32),
+            "oracle_embedding": ([vp, vp, vp, i64, i64, i32, i32, vp, i64, i32, vp], i32),
             "oracle_matmul_cols": ([vp, i64, vp, vp, vp, i64, i64, i32, i32, vp, i64, vp, vp], i32),
             "oracle_matmul": ([vp, i64, vp, vp, vp, i64, i64, i32, i32, vp, vp], i32),
             "oracle_gather_matmul": ([vp, i64, vp, vp, vp, i64, i64, i64, vp, i64, i32, i32, vp, vp],
@@ -170,6 +171,19 @@ def dequantize(codes, scales, biases, K: int, group_size: int, bits: int, out_dt
                                    out_dtype, _p(out))
     if st:
         raise OracleError(st, "dequantize")
+    return out
+
+
+def embedding(codes, scales, biases, ids, K: int, group_size: int, bits: int, out_dtype: int):
+    """Quantized embedding ("Tutorial 10", s.6): out[t] = dequantize(row ids[t]);
+    ids outside [0, V) give zero rows.  F32 -> float32, F16/BF16 -> uint16 bits."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32).reshape(-1)
+    V, T = codes.shape[0], ids.shape[0]
+    out = np.zeros((T, K), dtype=np.float32 if out_dtype == F32 else np.uint16)
+    st = _load().oracle_embedding(_p(codes), _p(scales), _p(biases), V, K, group_size, bits,
+                                  _p(ids), T, out_dtype, _p(out))
+    if st:
+        raise OracleError(st, "embedding")
     return out
 
 

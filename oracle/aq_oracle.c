@@ -25,7 +25,9 @@
  *          significant bits first; dequantize = values*scales + biases in
  *          float32, then cast), section 4 (container shapes
  *          [out_features, in_features/group_size]), section 5 "Approach 1:
- *          Dequantize Then Multiply" (y = x @ W^T on the dequantized W).
+ *          Dequantize Then Multiply" (y = x @ W^T on the dequantized W),
+ *          section 6 "Quantized Embeddings" (rows selected by token id,
+ *          then dequantized).
  *
  * Readings taken where the pages are silent (each is repeated in the
  * design notes):
@@ -49,6 +51,8 @@
  *      A[m,n] = sum_k |x[m,k] * w^[n,k]| scales the tolerance.
  *  R6  gather (MoE): y[t,j,:] = x[t,:] @ W_{ids[t,j]}^T, one output per
  *      (token, slot), no routing-weight combine.
+ *  R13 embedding ([T10] s.6): out[t,:] is row ids[t] dequantized as in R4;
+ *      an id outside the table gives a zero row.
  *
  * Exactness of the binary64 comparisons used below.  Every finite fp16
  * value is an integer multiple of 2^-24 of magnitude < 2^16; q*s with
@@ -351,6 +355,24 @@ int oracle_dequantize_exact(const uint32_t *codes, const uint16_t *scales, const
 
 /* dequantize to fp32 / fp16 / bf16 in the pages' order: binary32 result
  * of q*s + b, then a round-to-nearest-even cast. */
+/* One row: out_row[k] = q*s + b in binary32 (R4), then cast to out_dtype. */
+static void dequantize_row(const uint32_t *row, const uint16_t *srow, const uint16_t *brow,
+                           int64_t K, int G, int bits, int out_dtype, void *out, int64_t off) {
+  for (int64_t k = 0; k < K; ++k) {
+    double s = oracle_half_to_double(srow[k / G]);
+    double b = oracle_half_to_double(brow[k / G]);
+    /* q*s is exact in binary32; the binary32 sum rounds once, which is
+     * the binary64 exact value rounded to binary32 */
+    float v32 = (float)((double)get_code(row, k, bits) * s + b);
+    if (out_dtype == OR_F32)
+      ((float *)out)[off + k] = v32;
+    else if (out_dtype == OR_F16)
+      ((uint16_t *)out)[off + k] = oracle_double_to_half_rne((double)v32);
+    else
+      ((uint16_t *)out)[off + k] = oracle_float_to_bf16_rne(v32);
+  }
+}
+
 int oracle_dequantize(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
                       int64_t N, int64_t K, int G, int bits, int out_dtype, void *out) {
   int st = check_shape(N, K, G, bits);
@@ -359,19 +381,35 @@ int oracle_dequantize(const uint32_t *codes, const uint16_t *scales, const uint1
   const int64_t wpr = K * bits / 32, ng = K / G;
 #pragma omp parallel for schedule(static)
   for (int64_t n = 0; n < N; ++n)
-    for (int64_t k = 0; k < K; ++k) {
-      double s = oracle_half_to_double(scales[n * ng + k / G]);
-      double b = oracle_half_to_double(biases[n * ng + k / G]);
-      /* q*s is exact in binary32; the binary32 sum rounds once, which is
-       * the binary64 exact value rounded to binary32 */
-      float v32 = (float)((double)get_code(codes + n * wpr, k, bits) * s + b);
-      if (out_dtype == OR_F32)
-        ((float *)out)[n * K + k] = v32;
-      else if (out_dtype == OR_F16)
-        ((uint16_t *)out)[n * K + k] = oracle_double_to_half_rne((double)v32);
-      else
-        ((uint16_t *)out)[n * K + k] = oracle_float_to_bf16_rne(v32);
-    }
+    dequantize_row(codes + n * wpr, scales + n * ng, biases + n * ng, K, G, bits, out_dtype, out,
+                   n * K);
+  return OR_OK;
+}
+
+/* ---------------------------------------------------------------------
+ * Quantized embedding ([T10] s.6 "Quantized Embeddings"): a lookup by
+ * token id selects the packed row, its scales and its biases, and that row
+ * is dequantized as above.  out[t, :] = dequantize(row ids[t]).
+ * Reading R13: an id outside [0, V) selects no row and gives a zero row.
+ * ------------------------------------------------------------------- */
+int oracle_embedding(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                     int64_t V, int64_t K, int G, int bits, const int32_t *ids, int64_t T,
+                     int out_dtype, void *out) {
+  int st = check_shape(V, K, G, bits);
+  if (st) return st;
+  if (T < 0) return OR_ERR_ARG;
+  if (out_dtype != OR_F32 && out_dtype != OR_F16 && out_dtype != OR_BF16) return OR_ERR_ARG;
+  const int64_t wpr = K * bits / 32, ng = K / G;
+  const size_t esz = out_dtype == OR_F32 ? 4 : 2;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    const int64_t id = ids[t];
+    if (id < 0 || id >= V)
+      memset((char *)out + (size_t)(t * K) * esz, 0, (size_t)K * esz);
+    else
+      dequantize_row(codes + id * wpr, scales + id * ng, biases + id * ng, K, G, bits, out_dtype,
+                     out, t * K);
+  }
   return OR_OK;
 }
 
