@@ -29,6 +29,8 @@ first part).  The JSON line also carries:
                 shader clock it runs at).
 Per decode shape the line also carries the time of a plain streaming read of
 the same bytes (same cold rotation and timing), a measured second denominator.
+  embedding     quantized embedding lookups (rows of a [128256, 4096] 8-bit
+                table dequantized to bf16) for 1 and 2048 tokens.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -61,6 +63,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     p.add_argument("--no-qmm", action="store_true", help="skip the prefill (QMM) section")
+    p.add_argument("--no-embedding", action="store_true", help="skip the embedding section")
     p.add_argument("--qmm-iters", type=int, default=20)
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain 512 MiB device copy (counter calibration)")
@@ -252,9 +255,16 @@ def main():
     if not args.no_cpu:
         result["cpu_baseline"] = _cpu_baseline(mats, args.cpu_seconds)
 
+    # ---- quantized embedding ---------------------------------------------------------------
+    if not args.no_embedding:
+        del round_graph, step_graphs, sets
+        torch.cuda.synchronize()
+        result["embedding"] = _embedding(aq, inputs, dev, stream)
+
     # ---- prefill (QMM) ---------------------------------------------------------------------
     if not args.no_qmm:
-        del round_graph, step_graphs, sets
+        if args.no_embedding:
+            del round_graph, step_graphs, sets
         torch.cuda.synchronize()
         result["qmm"] = _qmm(aq, inputs, dev, args.qmm_iters)
 
@@ -366,6 +376,53 @@ def _cpu_baseline(mats, seconds):
             "kind": "oracle",
             "sample": f"{reps} full decode step(s) (4 matrices, {step_bytes} packed weight bytes, "
                       f"fp64 accumulation), {el:.1f} s on {model}"}
+
+
+def _embedding(aq, inputs, dev, stream):
+    """Quantized embedding lookup on a [128256, 4096] 8-bit G=128 table (541 MB,
+    more than the last-level cache), bf16 rows, T = 1 and T = 2048 tokens; each
+    launch of a graph of back-to-back launches uses its own seeded ids."""
+    import torch
+    cfg = inputs.WORKLOADS["embedding"]
+    (V, K), G, bits = cfg["shapes"][0], cfg["group_size"][0], cfg["bits"][0]
+    w = inputs.weights_device(V, K, device=dev, seed=0, key=(inputs.WORKLOAD_ID["embedding"],))
+    c, s, b = aq.aq_quantize(w, G, bits)
+    del w
+    out = {"workload": f"embedding table [{V},{K}] {bits}-bit G={G}, bf16 rows"}
+    reps = 32
+    gs = torch.cuda.Stream()
+    for T in cfg["tokens"]:
+        ids = [torch.from_numpy(inputs.token_ids(T, V, seed=r + 1,
+                                                 key=(inputs.WORKLOAD_ID["embedding"],))).to(dev)
+               for r in range(reps)]
+        o = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
+        aq.aq_embedding(ids[0], c, s, b, G, bits, out=o)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(gs):
+            with torch.cuda.graph(g, stream=gs):
+                for r in range(reps):
+                    aq.aq_embedding(ids[r], c, s, b, G, bits, out=o)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        durs = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            durs.append(e0.elapsed_time(e1) * 1e3 / reps)
+        us = sum(durs) / len(durs)
+        nbytes = T * (K * bits // 8 + (K // G) * 4) + T * K * 2 + T * 4
+        out[f"T{T}"] = {"avg_us": round(us, 3), "algo_bytes": nbytes,
+                        "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                        "pct_hbm": round(100 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
+        print(f"# embedding T={T}: {us:.2f} us/launch in-graph, {out[f'T{T}']['gbs']} GB/s "
+              f"(rows read + written)", file=sys.stderr, flush=True)
+        del g
+    return out
 
 
 def _qmm(aq, inputs, dev, iters):

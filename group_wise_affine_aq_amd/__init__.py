@@ -60,6 +60,7 @@ def load_library():
         "aq_qweight_bytes": ([i64, i64, i32, i32], i64),
         "aq_quantize": ([vp, i32, i64, i64, i32, i32, vp, vp, vp, vp], i32),
         "aq_dequantize": ([vp, vp, vp, i64, i64, i32, i32, vp, i32, vp], i32),
+        "aq_embedding": ([vp, vp, vp, i64, i64, i32, i32, vp, i64, vp, i32, vp], i32),
         "aq_qmv": ([vp, i32, i64, vp, vp, vp, i64, i64, i32, i32, vp, vp], i32),
         "aq_qmm": ([vp, i32, i64, vp, vp, vp, i64, i64, i32, i32, vp, vp], i32),
         "aq_quantized_matmul": ([vp, i32, i64, vp, vp, vp, i64, i64, i32, i32, vp, vp], i32),
@@ -165,6 +166,23 @@ def aq_dequantize(codes, scales, biases, group_size: int, bits: int, out_dtype=N
                            N, K, group_size, bits, _dev(out, "out"), _dtype_code(out),
                            _stream(stream))
     _check(st, "aq_dequantize")
+    return out
+
+
+def aq_embedding(ids, codes, scales, biases, group_size: int, bits: int, out_dtype=None,
+                 out=None, stream=None):
+    """Quantized embedding: out[t] = dequantize(table row ids[t]); ids int32 [T]."""
+    torch = _torch()
+    V = codes.shape[0]
+    K = scales.shape[1] * group_size
+    T = ids.numel()
+    if out is None:
+        out = torch.empty((T, K), dtype=out_dtype or torch.float16, device=codes.device)
+    st = load_library().aq_embedding(_dev(codes, "codes"), _dev(scales, "scales"),
+                                     _dev(biases, "biases"), V, K, group_size, bits,
+                                     _dev(ids, "ids"), T, _dev(out, "out"), _dtype_code(out),
+                                     _stream(stream))
+    _check(st, "aq_embedding")
     return out
 
 

@@ -124,6 +124,20 @@ aq_status aq_dequantize(const uint32_t *codes, const uint16_t *scales, const uin
                                         (int)out_dtype, static_cast<hipStream_t>(stream)));
 }
 
+aq_status aq_embedding(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                       int64_t V, int64_t K, int group_size, int bits, const int32_t *ids,
+                       int64_t T, void *out, aq_dtype out_dtype, void *stream) {
+  if (!valid_format(V, K, group_size, bits) || T < 1) return AQ_ERR_INVALID_ARG;
+  if (out_dtype != AQ_F32 && out_dtype != AQ_F16 && out_dtype != AQ_BF16) return AQ_ERR_INVALID_ARG;
+  if (!out || !ids) return AQ_ERR_INVALID_ARG;
+  aq_status st = check_weights(codes, scales, biases);
+  if (st != AQ_OK) return st;
+  if (!aligned16(out) || !aligned16(ids)) return AQ_ERR_ALIGNMENT;
+  if (T * (K / 32) > (int64_t)0x7FFFFFFF * 256) return AQ_ERR_UNSUPPORTED;
+  return from_hip(aq::launch_embedding(codes, scales, biases, V, K, group_size, bits, ids, T, out,
+                                       (int)out_dtype, static_cast<hipStream_t>(stream)));
+}
+
 aq_status aq_qmv(const void *x, aq_dtype x_dtype, int64_t M, const uint32_t *codes,
                  const uint16_t *scales, const uint16_t *biases, int64_t N, int64_t K,
                  int group_size, int bits, void *y, void *stream) {

@@ -19,6 +19,12 @@ hipError_t launch_dequantize(const uint32_t *codes, const uint16_t *scales,
                              const uint16_t *biases, int64_t N, int64_t K, int G, int bits,
                              void *out, int out_dtype, hipStream_t s);
 
+// quantized embedding: out[t, :] = dequantize(table row ids[t]), zero rows for
+// ids outside [0, V)
+hipError_t launch_embedding(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                            int64_t V, int64_t K, int G, int bits, const int32_t *ids, int64_t T,
+                            void *out, int out_dtype, hipStream_t s);
+
 // y[M, N] = x[M, K] @ W^T for 1 <= M <= 8 (matrix-vector kernels)
 hipError_t launch_qmv(const void *x, int x_dtype, int M, const uint32_t *codes,
                       const uint16_t *scales, const uint16_t *biases, int64_t N, int64_t K, int G,

@@ -162,24 +162,40 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void *__restrict__ 
   }
 }
 
-template <int BITS, int ODT>
+// One thread per 32-code chunk of an output row.  With GATHER (quantized
+// embedding, "Tutorial 10: Quantization", s.6) output row t is table row
+// ids[t] (N table rows, T output rows); an id outside [0, N) gives a zero row.
+template <int BITS, int ODT, bool GATHER>
 __global__ __launch_bounds__(256) void dequantize_kernel(const uint32_t *__restrict__ codes,
                                                          const uint16_t *__restrict__ scales,
                                                          const uint16_t *__restrict__ biases,
                                                          int64_t N, int64_t K, int G,
+                                                         const int32_t *__restrict__ ids, int64_t T,
                                                          void *__restrict__ out) {
   const int64_t cpr = K >> 5;  // chunks per row
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= N * cpr) return;
-  const int64_t n = idx / cpr, c = idx - n * cpr;
-  uint32_t wv[BITS];
-  load_chunk<BITS>(codes + n * (K * BITS / 32) + c * BITS, wv);
-  const int64_t gi = n * (K / G) + (c * 32) / G;
-  const float s = f16_to_f32(scales[gi]), b = f16_to_f32(biases[gi]);
+  if (idx >= (GATHER ? T : N) * cpr) return;
+  const int64_t t = idx / cpr, c = idx - t * cpr;
+  int64_t n = t;
+  bool zero = false;
+  if constexpr (GATHER) {
+    const int32_t id = ids[t];
+    zero = id < 0 || (int64_t)id >= N;
+    n = zero ? 0 : id;
+  }
   float r[32];
+  if (zero) {
 #pragma unroll
-  for (int i = 0; i < 32; ++i) r[i] = __builtin_fmaf((float)chunk_code<BITS>(wv, i), s, b);
-  const int64_t e = n * K + c * 32;
+    for (int i = 0; i < 32; ++i) r[i] = 0.f;
+  } else {
+    uint32_t wv[BITS];
+    load_chunk<BITS>(codes + n * (K * BITS / 32) + c * BITS, wv);
+    const int64_t gi = n * (K / G) + (c * 32) / G;
+    const float s = f16_to_f32(scales[gi]), b = f16_to_f32(biases[gi]);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) r[i] = __builtin_fmaf((float)chunk_code<BITS>(wv, i), s, b);
+  }
+  const int64_t e = t * K + c * 32;
   if constexpr (ODT == X_F32) {
     float4 *o = reinterpret_cast<float4 *>(reinterpret_cast<float *>(out) + e);
 #pragma unroll
@@ -212,18 +228,31 @@ hipError_t quantize_w(const void *w, int64_t N, int64_t K, int G, int bits, uint
   return hipGetLastError();
 }
 
-template <int ODT>
+template <int ODT, bool GATHER>
 hipError_t dequantize_o(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
-                        int64_t N, int64_t K, int G, int bits, void *out, hipStream_t s) {
-  const int64_t total = N * (K / 32);
+                        int64_t N, int64_t K, int G, int bits, const int32_t *ids, int64_t T,
+                        void *out, hipStream_t s) {
+  const int64_t total = (GATHER ? T : N) * (K / 32);
   const dim3 grid((unsigned)((total + 255) / 256)), block(256);
-#define AQ_D(B) case B: hipLaunchKernelGGL((dequantize_kernel<B, ODT>), grid, block, 0, s, codes, scales, biases, N, K, G, out); break;
+#define AQ_D(B) case B: hipLaunchKernelGGL((dequantize_kernel<B, ODT, GATHER>), grid, block, 0, s, codes, scales, biases, N, K, G, ids, T, out); break;
   switch (bits) {
     AQ_D(2) AQ_D(3) AQ_D(4) AQ_D(5) AQ_D(6) AQ_D(7) AQ_D(8)
     default: return hipErrorInvalidValue;
   }
 #undef AQ_D
   return hipGetLastError();
+}
+
+template <bool GATHER>
+hipError_t dequantize_dt(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                         int64_t N, int64_t K, int G, int bits, const int32_t *ids, int64_t T,
+                         void *out, int out_dtype, hipStream_t s) {
+  switch (out_dtype) {
+    case X_F32: return dequantize_o<X_F32, GATHER>(codes, scales, biases, N, K, G, bits, ids, T, out, s);
+    case X_F16: return dequantize_o<X_F16, GATHER>(codes, scales, biases, N, K, G, bits, ids, T, out, s);
+    case X_BF16: return dequantize_o<X_BF16, GATHER>(codes, scales, biases, N, K, G, bits, ids, T, out, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -241,12 +270,13 @@ hipError_t launch_quantize(const void *w, int w_dtype, int64_t N, int64_t K, int
 hipError_t launch_dequantize(const uint32_t *codes, const uint16_t *scales,
                              const uint16_t *biases, int64_t N, int64_t K, int G, int bits,
                              void *out, int out_dtype, hipStream_t s) {
-  switch (out_dtype) {
-    case X_F32: return dequantize_o<X_F32>(codes, scales, biases, N, K, G, bits, out, s);
-    case X_F16: return dequantize_o<X_F16>(codes, scales, biases, N, K, G, bits, out, s);
-    case X_BF16: return dequantize_o<X_BF16>(codes, scales, biases, N, K, G, bits, out, s);
-  }
-  return hipErrorInvalidValue;
+  return dequantize_dt<false>(codes, scales, biases, N, K, G, bits, nullptr, 0, out, out_dtype, s);
+}
+
+hipError_t launch_embedding(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                            int64_t V, int64_t K, int G, int bits, const int32_t *ids, int64_t T,
+                            void *out, int out_dtype, hipStream_t s) {
+  return dequantize_dt<true>(codes, scales, biases, V, K, G, bits, ids, T, out, out_dtype, s);
 }
 
 }  // namespace aq

@@ -23,6 +23,9 @@ the 70B MLP up-projection, an MoE expert stack):
   moe       64 experts W_e [1408, 2048] ~ N(0, 0.02) 4-bit G=64; x fp16
             [32, 2048] ~ N(0, 1); ids [32, 6] = first 6 of a seeded
             permutation of the 64 experts, per token
+  embedding table [128256, 4096] ~ N(0, 0.02) (a Llama-3-8B vocabulary) at
+            8-bit G=128; token ids uniform over the vocabulary, T = 1
+            (decode) and T = 2048 (prefill); bf16 output
 """
 from __future__ import annotations
 
@@ -41,6 +44,8 @@ WORKLOADS = {
                     x_dtype="bf16", outliers=False),
     "moe": dict(shapes=[(1408, 2048)], experts=64, tokens=32, topk=6, bits=[4], group_size=[64],
                 x_dtype="f16", outliers=False),
+    "embedding": dict(shapes=[(128256, 4096)], bits=[8], group_size=[128], tokens=[1, 2048],
+                      out_dtype="bf16", outliers=False),
 }
 WORKLOAD_ID = {name: i for i, name in enumerate(WORKLOADS)}
 
@@ -72,6 +77,11 @@ def expert_ids(T: int, E: int, topk: int, *, seed: int = 0, key=(0,)) -> np.ndar
     permutation of range(E) (distinct, uniformly chosen experts)."""
     r = _rng(seed, ROLE_IDS, T, E, topk, *key)
     return np.stack([r.permutation(E)[:topk] for _ in range(T)]).astype(np.int32)
+
+
+def token_ids(T: int, V: int, *, seed: int = 0, key=(0,)) -> np.ndarray:
+    """int32 [T] token ids, uniform over range(V) (with repeats)."""
+    return _rng(seed, ROLE_IDS, T, V, *key).integers(0, V, size=T).astype(np.int32)
 
 
 # --- number-format plumbing ------------------------------------------------------

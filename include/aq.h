@@ -108,6 +108,17 @@ aq_status aq_dequantize(const uint32_t *codes, const uint16_t *scales, const uin
                         int64_t N, int64_t K, int group_size, int bits, void *out,
                         aq_dtype out_dtype, void *stream);
 
+/* Quantized embedding lookup ("Tutorial 10: Quantization", s.6 "Quantized
+ * Embeddings"): the packed rows, scales and biases of the token ids are
+ * selected and dequantized exactly as aq_dequantize does:
+ *   out[t, :] = dequantize(row ids[t] of the V x K table), 0 <= t < T.
+ * codes/scales/biases: the table (device, layouts above, V rows).  ids:
+ * device int32 [T], T >= 1.  out: device [T, K] in out_dtype (AQ_F32, AQ_F16
+ * or AQ_BF16).  An id outside [0, V) reads nothing and gives a zero row. */
+aq_status aq_embedding(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                       int64_t V, int64_t K, int group_size, int bits, const int32_t *ids,
+                       int64_t T, void *out, aq_dtype out_dtype, void *stream);
+
 /* Quantized matrix-vector product for decode, y = x @ W^T with W given in
  * packed form and dequantized in registers on every use ("Quantization",
  * metalworking, QMV bullet; "Tutorial 10", s.5 Approach 2 with

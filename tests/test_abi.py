@@ -90,6 +90,23 @@ def test_qmv_rows_limit(lib):
     assert qmv(lib, "aq_qmv", M=9) == INVALID
 
 
+def test_embedding_argument_errors(lib):
+    def e(codes=P, scales=P, biases=P, V=100, K=128, G=64, bits=4, ids=P, T=3, out=P, dt=F16):
+        return lib.aq_embedding(codes, scales, biases, V, K, G, bits, ids, T, out, dt, None)
+    assert e(V=0) == INVALID
+    assert e(T=0) == INVALID
+    assert e(K=96) == INVALID
+    assert e(G=16) == INVALID
+    assert e(bits=9) == INVALID
+    assert e(dt=7) == INVALID
+    assert e(ids=None) == INVALID
+    assert e(out=None) == INVALID
+    assert e(codes=None) == INVALID
+    assert e(ids=MIS) == ALIGN
+    assert e(out=MIS) == ALIGN
+    assert e(scales=MIS) == ALIGN
+
+
 def test_bench_helper_argument_errors(lib):
     assert lib.aq_bench_stream_read(P, 0, 512, 4, P, None) == INVALID
     assert lib.aq_bench_stream_read(P, 24, 512, 4, P, None) == INVALID   # not a multiple of 16

@@ -108,6 +108,34 @@ def test_dequantize_bitexact(aq, bits, out):
     assert np.array_equal(out_bits(got), ref_bits)
 
 
+# ---- quantized embedding ---------------------------------------------------------------------
+@pytest.mark.parametrize("bits", ALL_BITS)
+@pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
+def test_embedding_bitexact(aq, bits, out):
+    G = GROUP_FOR_BITS[bits]
+    V, K = 41, 3 * G
+    _, (c, s, b) = _quantized(V, K, G, bits, seed=8)
+    ids = np.random.default_rng(bits).integers(0, V, size=300).astype(np.int32)
+    ids[[5, 77, 299]] = [-1, V, 2**31 - 1]  # outside the table: zero rows
+    code = {"f32": oracle.F32, "f16": oracle.F16, "bf16": oracle.BF16}[out]
+    ref = oracle.embedding(c, s, b, ids, K, G, bits, code)
+    got = aq.aq_embedding(to_dev(ids), *packed_to_dev(c, s, b), G, bits,
+                          out_dtype=torch_dtype(out))
+    ref_bits = ref.view(np.uint32) if out == "f32" else ref
+    assert np.array_equal(out_bits(got), ref_bits)
+
+
+@pytest.mark.parametrize("T", [1, 2, 7, 1025])
+def test_embedding_token_counts(aq, T):
+    V, K, G, bits = 50, 4096, 128, 8
+    _, (c, s, b) = _quantized(V, K, G, bits, seed=9)
+    ids = np.random.default_rng(T).integers(-2, V + 2, size=T).astype(np.int32)
+    ref = oracle.embedding(c, s, b, ids, K, G, bits, oracle.BF16)
+    got = aq.aq_embedding(to_dev(ids), *packed_to_dev(c, s, b), G, bits,
+                          out_dtype=torch_dtype("bf16"))
+    assert np.array_equal(out_bits(got), ref)
+
+
 # ---- QMV (M <= 8) ---------------------------------------------------------------------------
 @pytest.mark.parametrize("bits", ALL_BITS)
 @pytest.mark.parametrize("M", [1, 2, 3, 5, 8])

@@ -10,15 +10,17 @@ gather kernel for the experts).
   prefill  X bf16 [2048, 8192], W [28672, 8192] at 4-bit G=64, 3-bit G=64,
            2-bit G=32 (outputs compared on a seeded sample of rows x columns)
   moe      64 experts [1408, 2048] 4-bit G=64, x fp16 [32, 2048], ids [32, 6]
+  embedding table [128256, 4096] 8-bit G=128, T in {1, 2048} token ids, bf16 out
 
-Quantization is checked bit-exactly on every element; matmul outputs against
+Quantization is checked bit-exactly on every element (for the embedding table,
+on every row a token refers to); embedding rows bit-exactly; matmul outputs against
 |y - y_ref| <= 2^-9 * sum_k |x_k w^_k| + 1e-6."""
 import numpy as np
 import pytest
 
 import oracle
 from group_wise_affine_aq_amd import inputs
-from gpu_util import bits_to_dev, out_to_f64, packed_from_dev, packed_to_dev, to_dev
+from gpu_util import bits_to_dev, out_bits, out_to_f64, packed_from_dev, packed_to_dev, to_dev
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -122,3 +124,25 @@ def test_moe(aq):
     y_ref, A = oracle.gather_matmul(inputs.from_bits(xb, "f16"), c, s, b, ids, K, 64, 4)
     y = aq.aq_gather_qmv(bits_to_dev(xb, "f16"), *packed_to_dev(c, s, b), to_dev(ids), 64, 4)
     _close(out_to_f64(y), y_ref, A, "moe")
+
+
+def test_embedding(aq):
+    import torch
+    cfg = inputs.WORKLOADS["embedding"]
+    (V, K), G, bits = cfg["shapes"][0], cfg["group_size"][0], cfg["bits"][0]
+    w = inputs.weights_device(V, K, device=torch.device("cuda"), seed=0, key=(WID["embedding"],))
+    c, s, b = aq.aq_quantize(w, G, bits)
+    for T in cfg["tokens"]:
+        ids = inputs.token_ids(T, V, seed=0, key=(WID["embedding"],))
+        out = aq.aq_embedding(to_dev(ids), c, s, b, G, bits, out_dtype=torch.bfloat16)
+        # the rows the tokens refer to, quantized again by the reference
+        rows = np.unique(ids)
+        ri = torch.from_numpy(rows.astype(np.int64)).cuda()
+        cr, sr, br = oracle.quantize(w[ri].cpu().numpy(), G, bits)
+        got = packed_from_dev(c[ri].contiguous(), s[ri].contiguous(), b[ri].contiguous())
+        for name, x, y in zip(("codes", "scales", "biases"), got, (cr, sr, br)):
+            assert np.array_equal(x, y), f"{name} of referenced rows differ (T={T})"
+        ref = oracle.embedding(cr, sr, br, np.searchsorted(rows, ids).astype(np.int32), K, G,
+                               bits, oracle.BF16)
+        assert np.array_equal(out_bits(out), ref), f"embedding rows differ (T={T})"
+
