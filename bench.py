@@ -29,6 +29,10 @@ first part).  The JSON line also carries:
                 shader clock it runs at).
 Per decode shape the line also carries the time of a plain streaming read of
 the same bytes (same cold rotation and timing), a measured second denominator.
+  specdec, moe  the M = 2..8 matrix-vector kernels (bf16 x, [14336, 4096] and
+                [4096, 14336] at 4/64 and 8/128) and the MoE gather kernel
+                (32 tokens, top-6 of 64 experts), % of HBM per launch on cold
+                weights;
   embedding     quantized embedding lookups (rows of a [128256, 4096] 8-bit
                 table dequantized to bf16) for 1 and 2048 tokens.
 
@@ -64,6 +68,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     p.add_argument("--no-qmm", action="store_true", help="skip the prefill (QMM) section")
     p.add_argument("--no-embedding", action="store_true", help="skip the embedding section")
+    p.add_argument("--no-extra", action="store_true",
+                   help="skip the spec-decode (M = 2..8) and MoE gather sections")
     p.add_argument("--qmm-iters", type=int, default=20)
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain 512 MiB device copy (counter calibration)")
@@ -255,6 +261,11 @@ def main():
     if not args.no_cpu:
         result["cpu_baseline"] = _cpu_baseline(mats, args.cpu_seconds)
 
+    # ---- spec-decode (M = 2..8) and MoE gather: % of HBM per launch ------------------------
+    if not args.no_extra:
+        result["specdec"] = _specdec(aq, inputs, dev, stream)
+        result["moe"] = _moe(aq, inputs, dev, stream)
+
     # ---- quantized embedding ---------------------------------------------------------------
     if not args.no_embedding:
         del round_graph, step_graphs, sets
@@ -376,6 +387,102 @@ def _cpu_baseline(mats, seconds):
             "kind": "oracle",
             "sample": f"{reps} full decode step(s) (4 matrices, {step_bytes} packed weight bytes, "
                       f"fp64 accumulation), {el:.1f} s on {model}"}
+
+
+def _graph_us(torch, stream, launches, reps=5):
+    """Per-launch device time of `launches` (a list of callables) captured
+    back-to-back in one graph and replayed between HIP events."""
+    gs = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(gs):
+        with torch.cuda.graph(g, stream=gs):
+            for f in launches:
+                f()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    durs = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        durs.append(e0.elapsed_time(e1) * 1e3 / len(launches))
+    del g
+    return sum(durs) / len(durs)
+
+
+def _specdec(aq, inputs, dev, stream):
+    """Matrix-vector kernels for M = 2..8 rows (bf16), each launch on a cold
+    copy of the weights (>= 1 GiB rotated), per-launch time in a graph."""
+    import torch
+    cfg = inputs.WORKLOADS["specdec"]
+    wid = inputs.WORKLOAD_ID["specdec"]
+    out = {"workload": "spec-decode QMV, x bf16 [M, K], M in {2,3,4,6,8}, cold weights"}
+    for (N, K) in cfg["shapes"]:
+        w = inputs.weights_device(N, K, device=dev, seed=0, key=(wid,))
+        for bits, g in zip(cfg["bits"], cfg["group_size"]):
+            packed = aq.aq_quantize(w, g, bits)
+            wbytes = aq.aq_qweight_bytes(N, K, g, bits)
+            copies = max(2, math.ceil(COLD_BYTES / wbytes))
+            sets = [packed] + [tuple(t.clone() for t in packed) for _ in range(copies - 1)]
+            ceil_us = _read_ceiling_us(aq, torch, wbytes, stream)
+            rows = {}
+            for M in cfg["M"]:
+                x = inputs.activations_device(M, K, "bf16", device=dev, seed=0, key=(wid, N, M))
+                y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+                fs = [lambda c=c, s_=s_, b=b: aq.aq_quantized_matmul(x, c, s_, b, g, bits, y=y)
+                      for (c, s_, b) in sets]
+                us = _graph_us(torch, stream, fs)
+                gbs = wbytes / (us * 1e-6) / 1e9
+                rows[f"M{M}"] = {"avg_us": round(us, 3), "weight_gbs": round(gbs, 1),
+                                 "pct_hbm": round(100 * gbs / HBM_PEAK_GBS, 1),
+                                 "frac_of_read_ceiling": round(ceil_us / us, 3)}
+                print(f"# QMV {N}x{K} {bits}-bit G={g} M={M}: {us:.2f} us, {gbs:.0f} GB/s weights",
+                      file=sys.stderr, flush=True)
+            out[f"{N}x{K}_b{bits}_g{g}"] = dict(weight_bytes=wbytes,
+                                                read_ceiling_us=round(ceil_us, 3), **rows)
+            del sets, packed
+            torch.cuda.synchronize()
+        del w
+    return out
+
+
+def _moe(aq, inputs, dev, stream):
+    """Gather matrix-vector kernel: 32 tokens x top-6 of 64 experts [1408, 2048]
+    4-bit G=64; cold copies of the expert stack rotated (>= 1 GiB)."""
+    import numpy as np
+    import torch
+    cfg = inputs.WORKLOADS["moe"]
+    wid = inputs.WORKLOAD_ID["moe"]
+    (N, K), E, T, topk = cfg["shapes"][0], cfg["experts"], cfg["tokens"], cfg["topk"]
+    g, bits = cfg["group_size"][0], cfg["bits"][0]
+    parts = [aq.aq_quantize(inputs.weights_device(N, K, device=dev, seed=0, key=(wid, e)), g, bits)
+             for e in range(E)]
+    packed = tuple(torch.stack([p[i] for p in parts]) for i in range(3))
+    del parts
+    ids_np = inputs.expert_ids(T, E, topk, seed=0, key=(wid,))
+    ids = torch.from_numpy(ids_np).to(dev)
+    x = inputs.activations_device(T, K, "f16", device=dev, seed=0, key=(wid,))
+    y = torch.empty((T, topk, N), dtype=torch.float16, device=dev)
+    ebytes = aq.aq_qweight_bytes(N, K, g, bits)
+    copies = max(2, math.ceil(COLD_BYTES / (E * ebytes)))
+    sets = [packed] + [tuple(t.clone() for t in packed) for _ in range(copies - 1)]
+    fs = [lambda c=c, s_=s_, b=b: aq.aq_gather_qmv(x, c, s_, b, ids, g, bits, y=y)
+          for (c, s_, b) in sets]
+    us = _graph_us(torch, stream, fs)
+    used = len(np.unique(ids_np))
+    algo = used * ebytes + T * K * 2 + T * topk * N * 2 + T * topk * 4
+    gbs = algo / (us * 1e-6) / 1e9
+    print(f"# MoE gather ({used} of {E} experts used): {us:.2f} us, {gbs:.0f} GB/s algorithmic",
+          file=sys.stderr, flush=True)
+    del sets, packed
+    torch.cuda.synchronize()
+    return {"workload": f"MoE gather: {E} experts [{N},{K}] {bits}-bit G={g}, x fp16 [{T},{K}], "
+                        f"ids [{T},{topk}], cold weights",
+            "experts_used": used, "algo_bytes": algo, "avg_us": round(us, 3),
+            "gbs": round(gbs, 1), "pct_hbm": round(100 * gbs / HBM_PEAK_GBS, 1)}
 
 
 def _embedding(aq, inputs, dev, stream):

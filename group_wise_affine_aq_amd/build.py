@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libaq.so")
 ARCH = os.environ.get("AQ_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["aq_api.cpp", "aq_quant.hip", "aq_qmv.hip", "aq_qmm.hip", "aq_bench.hip"]
+SOURCES = ["aq_api.cpp", "aq_quant.hip", "aq_qmv.hip", "aq_qmvm.hip", "aq_qmm.hip", "aq_bench.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = [

@@ -144,6 +144,10 @@ aq_status aq_qmv(const void *x, aq_dtype x_dtype, int64_t M, const uint32_t *cod
   aq_status st = check_matmul(x, x_dtype, M, codes, scales, biases, N, K, group_size, bits, y);
   if (st != AQ_OK) return st;
   if (M > kMaxQmvRows) return AQ_ERR_INVALID_ARG;
+  // 2..8 rows of 4-bit codes: dot products on the matrix cores
+  if (aq::qmvm_supported((int)M, bits, N, K, group_size))
+    return from_hip(aq::launch_qmvm(x, (int)x_dtype, (int)M, codes, scales, biases, N, K,
+                                    group_size, y, static_cast<hipStream_t>(stream)));
   return from_hip(aq::launch_qmv(x, (int)x_dtype, (int)M, codes, scales, biases, N, K, group_size,
                                  bits, y, static_cast<hipStream_t>(stream)));
 }

@@ -74,22 +74,22 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   }
 }
 
-// v & 0x0F0F0F0F as an opaque operation, so that the byte-wise conversions
-// below stay v_cvt_f32_ubyte{0..3} instead of being folded into per-code
-// bit-field extracts
-__device__ __forceinline__ uint32_t nibbles(uint32_t v) {
-  uint32_t r;
-  asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(r) : "v"(v));
-  return r;
+// A register holding v that the optimizer cannot see through (an identity
+// DPP move).  ANDing codes with an opaque 0x0F0F0F0F keeps the byte-wise
+// conversions below as v_cvt_f32_ubyte{0..3} instead of letting them fold
+// into per-code bit-field extracts, while every instruction stays visible to
+// the compiler (and to its matrix-core hazard checks).
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xE4, 0xF, 0xF, false);
 }
 
 // Codes 8u .. 8u+7 of a 32-code chunk dequantized (q*s + b in binary32,
 // rounded to nearest even into the activation type) and packed in pairs.
 template <int BITS, typename XT, int U>
-__device__ __forceinline__ uint4 dequant8(const uint32_t *w, float s, float b) {
+__device__ __forceinline__ uint4 dequant8(const uint32_t *w, float s, float b, uint32_t nmask) {
   uint32_t p[4];
   if constexpr (BITS == 4) {
-    const uint32_t lo = nibbles(w[U]), hi = nibbles(w[U] >> 4);  // codes 0,2,4,6 / 1,3,5,7
+    const uint32_t lo = w[U] & nmask, hi = (w[U] >> 4) & nmask;  // codes 0,2,4,6 / 1,3,5,7
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       p[e] = pack2<XT>(__builtin_fmaf((float)((lo >> (8 * e)) & 0xFFu), s, b),
@@ -253,11 +253,12 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const uint16_t *__restric
     r.b[c] = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)svoff[c], (int)so, 0);
   };
   // dequantize codes 8u .. 8u+7 of chunk c into W stage `buf`
+  const uint32_t nmask = opaque(0x0F0F0F0Fu);
   auto store_w8 = [&](const WRegs<BITS> &r, int c, auto ucon, int buf, bool zero) {
     constexpr int U = decltype(ucon)::value;
     const int ch = tid + kThreads * c, row = ch >> 1, half = ch & 1;
     const uint4 v = dequant8<BITS, XT, U>(r.w[c], f16_to_f32((uint16_t)r.s[c]),
-                                          f16_to_f32((uint16_t)r.b[c]));
+                                          f16_to_f32((uint16_t)r.b[c]), nmask);
     *reinterpret_cast<uint4 *>((buf ? ws1 : ws0) + row * kWPitch + half * 64 + U * 16) =
         zero ? make_uint4(0, 0, 0, 0) : v;
   };

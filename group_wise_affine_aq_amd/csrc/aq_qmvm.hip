@@ -1,0 +1,347 @@
+// aq_qmvm.hip -- quantized matrix-vector product for a few rows (2 <= M <= 8)
+// on the gfx950 matrix cores, 4-bit codes.
+//
+// The operation is the QMV of "Quantization" (metalworking, MLX notes, QMV
+// bullet), y = x @ W^T with W packed, for the speculative-decoding widths
+// the same page discusses (its dispatch section: a wider QMV for M around
+// 3-6).  The vector-ALU kernels spend about 0.5 VALU lane-ops per weight per
+// row of x on the dot products, which makes M >= 4 VALU-bound on MI355X
+// (about 2.8 lane-ops per weight are available at full HBM bandwidth).
+// Here the dot products run on the matrix cores instead, with the integer
+// codes as one operand:
+//
+//  * v_mfma_f32_16x16x32_{bf16,f16}: A = x (16 rows, rows >= M read as
+//    zero), B = 16 rows of W, each code q entering as the exact value
+//    OFF + q (one v_and_or_b32 per pair: OFF = 128 in bf16, 1024 in fp16),
+//    so one MFMA over a 32-code chunk gives P = sum x * (OFF + q);
+//  * a second MFMA against a register of ones gives X = sum x over the same
+//    chunk, already in the output lane layout;
+//  * per group, y += s * (P - OFF * X) + b * X = s * P + (b - OFF * s) * X,
+//    the same identity the vector kernels apply (sum_k x (q s + b) over a
+//    group), in binary32;
+//  * codes arrive as 16-byte loads (lane quarter h reads chunk h of a 4-chunk
+//    step of its row) and a 4x4 transpose across the lane quarters
+//    (v_permlane32_swap, v_permlane16_swap) gives each quarter code word h of
+//    every chunk, which is the MFMA B-operand layout;
+//  * x is read straight from global memory (it stays in L2), one 16-byte load
+//    per lane carrying two chunks (M <= 8) or four (M <= 4) in the lanes of
+//    A-operand rows that only feed discarded output rows, moved into place by
+//    a DPP row rotation; its pairs are permuted to the order the unpack
+//    produces (code e with code e+4);
+//  * the workgroup's scales and biases (16 R whole rows, one contiguous range
+//    each) are staged in LDS once with 16-byte loads: per-group 2-byte
+//    loads from every lane cost more than all the rest of the kernel;
+//  * a workgroup of W waves covers 16 R rows; its waves split K and add their
+//    partial sums through LDS at the end (W chosen per shape so that the
+//    grid fills the chip with waves that each keep loads in flight).
+#include "aq_device.hpp"
+#include "aq_internal.hpp"
+
+namespace aq {
+namespace {
+
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8v __attribute__((ext_vector_type(8)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+constexpr int kStepK = 128;  // k per step: 4 chunks
+
+template <typename XT>
+struct mm_traits;
+template <>
+struct mm_traits<bf16_t> {
+  static constexpr uint32_t magic = 0x43004300u;  // bf16 128.0 in both halves
+  static constexpr uint32_t ones = 0x3F803F80u;   // bf16 1.0
+  static constexpr float off = 128.f;
+};
+template <>
+struct mm_traits<f16_t> {
+  static constexpr uint32_t magic = 0x64006400u;  // fp16 1024.0
+  static constexpr uint32_t ones = 0x3C003C00u;   // fp16 1.0
+  static constexpr float off = 1024.f;
+};
+
+template <typename XT>
+__device__ __forceinline__ f32x4v mfma16(uint4 a, uint4 b, f32x4v c) {
+  if constexpr (std::is_same<XT, bf16_t>::value)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, a),
+                                                   __builtin_bit_cast(bf16x8v, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8v, a),
+                                                  __builtin_bit_cast(f16x8v, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mk_rsrc(const void *base, int64_t bytes) {
+  const int n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (bytes < 0 ? 0 : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, 0x00020000);
+}
+
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xE4, 0xF, 0xF, false);
+}
+
+// 4x4 transpose of (lane quarter, register): afterwards quarter h holds in
+// r[j] what quarter j held in r[h]
+__device__ __forceinline__ void transpose4(uint32_t (&r)[4]) {
+  auto a = __builtin_amdgcn_permlane32_swap(r[0], r[2], false, false);
+  r[0] = a[0]; r[2] = a[1];
+  auto b = __builtin_amdgcn_permlane32_swap(r[1], r[3], false, false);
+  r[1] = b[0]; r[3] = b[1];
+  auto c = __builtin_amdgcn_permlane16_swap(r[0], r[1], false, false);
+  r[0] = c[0]; r[1] = c[1];
+  auto d = __builtin_amdgcn_permlane16_swap(r[2], r[3], false, false);
+  r[2] = d[0]; r[3] = d[1];
+}
+
+// 8 codes of a word -> 4 registers of (OFF + q_e, OFF + q_{e+4}) pairs.
+// Plain C on register-held constants: the compiler emits v_and_or_b32 and
+// tracks the MFMA operand hazards of the registers it writes (an inline-asm
+// write would be invisible to that check).
+__device__ __forceinline__ uint4 unpack_word(uint32_t w, uint32_t mask, uint32_t magic) {
+  uint32_t p[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) p[e] = ((w >> (4 * e)) & mask) | magic;
+  return make_uint4(p[0], p[1], p[2], p[3]);
+}
+
+// natural pairs (x0 x1)(x2 x3)(x4 x5)(x6 x7) -> (x0 x4)(x1 x5)(x2 x6)(x3 x7)
+__device__ __forceinline__ uint4 permute_x(uint4 v) {
+  return make_uint4(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u),  // lo16(x) | lo16(z) << 16
+                    __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),  // hi16(x) | hi16(z) << 16
+                    __builtin_amdgcn_perm(v.w, v.y, 0x05040100u),
+                    __builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
+}
+
+// one step (4 chunks) of one wave's K range, as loaded
+template <int R, int NXL>
+struct MStep {
+  uint32_t cw[R][4];   // quarter h: chunk c0 + h of rows 16 r + n16 (4-bit: 4 words)
+  uint4 xl[4 / NXL];   // x loads of the step, NXL chunks each (natural pair order)
+};
+
+// lane l of a row of 16 receives the value of lane (l + 16 - k) % 16 ... i.e. a
+// rotation of each 16-lane row by k (DPP row_ror)
+template <int K16>
+__device__ __forceinline__ uint4 row_ror(uint4 v) {
+  if constexpr (K16 == 0) return v;
+  constexpr int ctl = 0x120 + K16;
+  return make_uint4((uint32_t)__builtin_amdgcn_mov_dpp((int)v.x, ctl, 0xF, 0xF, false),
+                    (uint32_t)__builtin_amdgcn_mov_dpp((int)v.y, ctl, 0xF, 0xF, false),
+                    (uint32_t)__builtin_amdgcn_mov_dpp((int)v.z, ctl, 0xF, 0xF, false),
+                    (uint32_t)__builtin_amdgcn_mov_dpp((int)v.w, ctl, 0xF, 0xF, false));
+}
+
+template <typename XT, int R, int W, int GS, int XR>
+__global__ __launch_bounds__(64 * W) void qmvm_kernel(const uint16_t *__restrict__ x, int M,
+                                                      const uint32_t *__restrict__ codes,
+                                                      const uint16_t *__restrict__ scales,
+                                                      const uint16_t *__restrict__ biases,
+                                                      int64_t N, int64_t K, int kw,
+                                                      uint16_t *__restrict__ y) {
+  constexpr int CPG = 1 << GS;       // chunks per group (G = 32 CPG)
+  constexpr int NG = 4 / CPG;        // groups per step
+  // rows of x carried per chunk slot of a load: output rows >= M are
+  // discarded, so A-operand rows XR.. may hold anything and one 16-byte load
+  // per lane carries NXL = 16 / XR chunks (lanes XR s .. XR s + XR - 1 of a
+  // row of 16 hold chunk slot s); a row rotation moves a slot to lanes 0..
+  constexpr int NXL = 16 / XR;
+  __shared__ float part[W][R * 16][8];  // per wave: rows of W x the 8 rows of x
+  extern __shared__ __attribute__((aligned(16))) uint16_t sbl[];  // [2][16 R][gpr] scales, biases
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n16 = lane & 15, h = lane >> 4;
+  const int64_t row0 = (int64_t)blockIdx.x * (16 * R);
+  const int nch = (int)(K >> 5);
+  const int64_t wpr = (int64_t)nch * 4, gpr = nch >> GS;
+  const int64_t nrows = N - row0 < 16 * R ? N - row0 : 16 * R;
+  const int sb_off = (int)(16 * R * gpr);  // biases after scales in sbl
+
+  // buffer resources: rows past N and rows of x past M read as zero
+  const __amdgpu_buffer_rsrc_t rw = mk_rsrc(codes + row0 * wpr, nrows * wpr * 4);
+  const __amdgpu_buffer_rsrc_t rs = mk_rsrc(scales + row0 * gpr, nrows * gpr * 2);
+  const __amdgpu_buffer_rsrc_t rb = mk_rsrc(biases + row0 * gpr, nrows * gpr * 2);
+  const __amdgpu_buffer_rsrc_t rx = mk_rsrc(x, (int64_t)M * K * 2);
+
+  // constants in registers the optimizer cannot see through (identity DPP
+  // moves), so the unpack stays one v_and_or_b32 per pair
+  const uint32_t vmask = opaque(0x000F000Fu), vmagic = opaque(mm_traits<XT>::magic);
+  const uint32_t vones = opaque(mm_traits<XT>::ones);
+  const uint4 ones = make_uint4(vones, vones, vones, vones);
+  const float off = mm_traits<XT>::off;
+
+  // this wave's K range, whole steps of 4 chunks (each a whole number of groups)
+  const int c_beg = wave * (kw >> 5);
+  const int c_end = c_beg + (kw >> 5) < nch ? c_beg + (kw >> 5) : nch;
+
+  auto load = [&](int c0, MStep<R, NXL> &st) {
+    const bool inside = c0 + h < nch;  // chunks past K read as zero
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t o = (uint32_t)(((int64_t)(16 * r + n16) * wpr + (int64_t)(inside ? c0 + h : 0) * 4) * 4);
+      const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)o, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.cw[r][i] = inside ? v[i] : 0u;
+    }
+#pragma unroll
+    for (int t = 0; t < 4 / NXL; ++t) {
+      const int cx = c0 + t * NXL + n16 / XR;
+      const int c = cx < nch ? cx : 0;
+      const uint32_t o = (uint32_t)(((int64_t)(n16 % XR) * K + (int64_t)c * 32 + 8 * h) * 2);
+      const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)o, 0, 0);
+      st.xl[t] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+  };
+
+  f32x4v acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = (f32x4v){0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int c0, MStep<R, NXL> &st) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) transpose4(st.cw[r]);  // quarter h: word h of chunks c0 .. c0+3
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+      if (c0 + q * CPG >= c_end) break;  // past K (uniform)
+      f32x4v xg = (f32x4v){0.f, 0.f, 0.f, 0.f}, pg[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) pg[r] = (f32x4v){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int jj = 0; jj < CPG; ++jj) {
+        const int j = q * CPG + jj;
+        uint4 xr = st.xl[j / NXL];
+        if constexpr (NXL == 2) {
+          if (j % 2 == 1) xr = row_ror<8>(xr);
+        } else if constexpr (NXL == 4) {
+          if (j % 4 == 1) xr = row_ror<12>(xr);
+          if (j % 4 == 2) xr = row_ror<8>(xr);
+          if (j % 4 == 3) xr = row_ror<4>(xr);
+        }
+        const uint4 xa = c0 + j < nch ? permute_x(xr) : make_uint4(0, 0, 0, 0);
+        xg = mfma16<XT>(xa, ones, xg);
+#pragma unroll
+        for (int r = 0; r < R; ++r) pg[r] = mfma16<XT>(xa, unpack_word(st.cw[r][j], vmask, vmagic), pg[r]);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int g = (c0 >> GS) + q, li = (16 * r + n16) * (int)gpr + g;
+        const float sc = f16_to_f32(sbl[li]), bi = f16_to_f32(sbl[sb_off + li]);
+        const float bo = __builtin_fmaf(-off, sc, bi);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[r][e] = __builtin_fmaf(bo, xg[e], __builtin_fmaf(sc, pg[r][e], acc[r][e]));
+      }
+    }
+  };
+
+  // double-buffered: the next step's loads are in flight while this one
+  // computes.  The prefetch is unconditional (past the range it re-reads
+  // memory inside the matrix, or zeros past K): a load issued on only some
+  // paths would make the in-order load counter wait for everything in flight.
+  MStep<R, NXL> sa, sb;
+  if (c_beg < c_end) load(c_beg, sa);
+  // the workgroup's scales and biases (16 R whole rows: one contiguous,
+  // 16-byte aligned range each) go to LDS once, while the first loads fly
+  // (a load that crosses the end of the valid rows reads as zero as a whole,
+  // so whole 16-byte units inside it first, then 2-byte loads, zeros past it)
+  {
+    const int valid = (int)(nrows * gpr), total = 16 * R * (int)gpr;
+    const int full = valid >> 3;  // 16-byte units entirely inside the valid rows
+    for (int i = threadIdx.x; i < full; i += 64 * W) {
+      const u32x4v vs = __builtin_amdgcn_raw_buffer_load_b128(rs, i * 16, 0, 0);
+      const u32x4v vb = __builtin_amdgcn_raw_buffer_load_b128(rb, i * 16, 0, 0);
+      *reinterpret_cast<u32x4v *>(sbl + i * 8) = vs;
+      *reinterpret_cast<u32x4v *>(sbl + sb_off + i * 8) = vb;
+    }
+    for (int e = full * 8 + threadIdx.x; e < total; e += 64 * W) {
+      const bool in = e < valid;
+      sbl[e] = in ? (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rs, e * 2, 0, 0) : (uint16_t)0;
+      sbl[sb_off + e] = in ? (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rb, e * 2, 0, 0) : (uint16_t)0;
+    }
+    __syncthreads();
+  }
+  if (c_beg < c_end) {
+    int c0 = c_beg;
+    for (; c0 + 8 <= c_end; c0 += 8) {
+      load(c0 + 4, sb);
+      compute(c0, sa);
+      load(c0 + 8, sa);
+      compute(c0 + 4, sb);
+    }
+    if (c0 < c_end) {
+      load(c0 + 4, sb);
+      compute(c0, sa);
+      if (c0 + 4 < c_end) compute(c0 + 4, sb);
+    }
+  }
+
+  // lane (n16, h) holds rows m = 4 h + e of x against W row 16 r + n16
+  if (h < 2) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) part[wave][16 * r + n16][4 * h + e] = acc[r][e];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < R * 16 * 8; i += 64 * W) {
+    const int nn = i >> 3, m = i & 7;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) v += part[w][nn][m];
+    if (m < M && row0 + nn < N) y[(int64_t)m * N + row0 + nn] = xtraits<XT>::from_f32(v);
+  }
+}
+
+template <typename XT, int R, int W, int XR>
+hipError_t qmvm_go(const void *x, int M, const uint32_t *codes, const uint16_t *scales,
+                   const uint16_t *biases, int64_t N, int64_t K, int G, void *y, hipStream_t s) {
+  const int64_t steps = (K + kStepK - 1) / kStepK;
+  const int kw = (int)((steps + W - 1) / W) * kStepK;  // k per wave, whole steps
+  const int64_t blocks = (N + 16 * R - 1) / (16 * R);
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks), block(64 * W);
+  const size_t lds = (size_t)2 * 16 * R * (K / G) * 2;  // scales + biases of the rows
+  switch (G) {
+    case 32: hipLaunchKernelGGL((qmvm_kernel<XT, R, W, 0, XR>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y); break;
+    case 64: hipLaunchKernelGGL((qmvm_kernel<XT, R, W, 1, XR>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y); break;
+    case 128: hipLaunchKernelGGL((qmvm_kernel<XT, R, W, 2, XR>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool qmvm_supported(int M, int bits, int64_t N, int64_t K, int G) {
+  // scales and biases of 16 rows staged in LDS: at most 48 KB
+  return M >= 2 && M <= 8 && bits == 4 && N >= 1 && K >= 32 && 16 * K * 2 <= 0x7FFFFFFF &&
+         (int64_t)2 * 16 * (K / G) * 2 <= 48 * 1024;
+}
+
+hipError_t launch_qmvm(const void *x, int x_dtype, int M, const uint32_t *codes,
+                       const uint16_t *scales, const uint16_t *biases, int64_t N, int64_t K, int G,
+                       void *y, hipStream_t s) {
+  // 16 rows per workgroup (<= 128 VGPRs, so 4 waves per SIMD), and K split
+  // over W waves so that the grid has about four waves per SIMD: each wave
+  // keeps two steps of loads in flight, and the chip needs tens of KB in
+  // flight per CU to stream from HBM
+  const int64_t rowblocks = (N + 15) / 16;
+  const int64_t target = 4 * 4 * (int64_t)device_cus();
+  const int W = rowblocks * 2 >= target ? 2 : rowblocks * 4 >= target ? 4 : rowblocks * 8 >= target ? 8 : 16;
+#define AQ_QMVM_W(T, XR) \
+  switch (W) { \
+    case 2: return qmvm_go<T, 1, 2, XR>(x, M, codes, scales, biases, N, K, G, y, s); \
+    case 4: return qmvm_go<T, 1, 4, XR>(x, M, codes, scales, biases, N, K, G, y, s); \
+    case 8: return qmvm_go<T, 1, 8, XR>(x, M, codes, scales, biases, N, K, G, y, s); \
+    default: return qmvm_go<T, 1, 16, XR>(x, M, codes, scales, biases, N, K, G, y, s); \
+  }
+#define AQ_QMVM(T) \
+  if (M <= 4) { AQ_QMVM_W(T, 4) } else { AQ_QMVM_W(T, 8) }
+  if (x_dtype == X_BF16) { AQ_QMVM(bf16_t) }
+  if (x_dtype == X_F16) { AQ_QMVM(f16_t) }
+#undef AQ_QMVM_W
+#undef AQ_QMVM
+  return hipErrorInvalidValue;
+}
+
+}  // namespace aq

@@ -296,4 +296,9 @@ def test_gather_all_same_expert_is_qmv(aq):
     yg = out_to_f64(aq.aq_gather_qmv(bits_to_dev(xb, "f16"), *dev, to_dev(ids), G, bits))
     yq = out_to_f64(aq.aq_qmv(bits_to_dev(xb, "f16"), dev[0][2].contiguous(),
                               dev[1][2].contiguous(), dev[2][2].contiguous(), G, bits))
-    assert np.array_equal(yg[:, 0, :], yq)
+    # the two kernels sum in different orders (M = 8 runs on the matrix cores),
+    # so they agree through the reference, each within the bound
+    y_ref, A = oracle.matmul(inputs.from_bits(xb, "f16"), c[2], s[2], b[2], K, G, bits)
+    for got, what in ((yg[:, 0, :], "gather"), (yq, "qmv")):
+        ok, ratio = oracle.within_tolerance(got, y_ref, A)
+        assert ok, f"{what}: worst error/bound = {ratio:.3f}"
