@@ -33,6 +33,8 @@ the same bytes (same cold rotation and timing), a measured second denominator.
                 [4096, 14336] at 4/64 and 8/128) and the MoE gather kernel
                 (32 tokens, top-6 of 64 experts), % of HBM per launch on cold
                 weights;
+  quantize_dequantize  aq_quantize of the prefill-size matrix (fp32 in) and
+                aq_dequantize of it to bf16, % of HBM;
   embedding     quantized embedding lookups (rows of a [128256, 4096] 8-bit
                 table dequantized to bf16) for 1 and 2048 tokens.
 
@@ -266,6 +268,10 @@ def main():
         result["specdec"] = _specdec(aq, inputs, dev, stream)
         result["moe"] = _moe(aq, inputs, dev, stream)
 
+    # ---- quantize and dequantize (offline conversion, standalone decode) -------------------
+    if not args.no_extra:
+        result["quantize_dequantize"] = _quant_dequant(aq, inputs, dev, stream)
+
     # ---- quantized embedding ---------------------------------------------------------------
     if not args.no_embedding:
         del round_graph, step_graphs, sets
@@ -483,6 +489,34 @@ def _moe(aq, inputs, dev, stream):
                         f"ids [{T},{topk}], cold weights",
             "experts_used": used, "algo_bytes": algo, "avg_us": round(us, 3),
             "gbs": round(gbs, 1), "pct_hbm": round(100 * gbs / HBM_PEAK_GBS, 1)}
+
+
+def _quant_dequant(aq, inputs, dev, stream):
+    """aq_quantize on W [28672, 8192] fp32 (4-bit G=64) and aq_dequantize of the
+    result to bf16: each one pass over HBM, timed in graphs of back-to-back
+    launches."""
+    import torch
+    N, K, g, bits = PREFILL["N"], PREFILL["K"], 64, 4
+    w = inputs.weights_device(N, K, device=dev, seed=0, key=(inputs.WORKLOAD_ID["prefill"],))
+    c, s_, b = aq.aq_quantize(w, g, bits)
+    out = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    packed = aq.aq_qweight_bytes(N, K, g, bits)
+    res = {"workload": f"W [{N},{K}] fp32 -> 4-bit G=64 and back to bf16"}
+    us = _graph_us(torch, stream, [lambda: aq.aq_quantize(w, g, bits, codes=c, scales=s_, biases=b)] * 4)
+    nb = 4 * N * K + packed
+    res["quantize"] = {"avg_us": round(us, 2), "bytes": nb, "gbs": round(nb / (us * 1e-6) / 1e9, 1),
+                       "pct_hbm": round(100 * nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
+    us = _graph_us(torch, stream, [lambda: aq.aq_dequantize(c, s_, b, g, bits, out=out)] * 4)
+    nb = packed + 2 * N * K
+    res["dequantize_bf16"] = {"avg_us": round(us, 2), "bytes": nb,
+                              "gbs": round(nb / (us * 1e-6) / 1e9, 1),
+                              "pct_hbm": round(100 * nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
+    print(f"# quantize {res['quantize']['avg_us']:.1f} us ({res['quantize']['gbs']} GB/s), "
+          f"dequantize {res['dequantize_bf16']['avg_us']:.1f} us ({res['dequantize_bf16']['gbs']} GB/s)",
+          file=sys.stderr, flush=True)
+    del w, c, s_, b, out
+    torch.cuda.synchronize()
+    return res
 
 
 def _embedding(aq, inputs, dev, stream):

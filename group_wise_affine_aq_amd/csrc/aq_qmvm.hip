@@ -114,9 +114,9 @@ __device__ __forceinline__ uint4 permute_x(uint4 v) {
 }
 
 // one step (4 chunks) of one wave's K range, as loaded
-template <int R, int NXL>
+template <int NXL>
 struct MStep {
-  uint32_t cw[R][4];   // quarter h: chunk c0 + h of rows 16 r + n16 (4-bit: 4 words)
+  uint32_t cw[4];      // quarter h: chunk c0 + h of row n16 (4-bit: 4 words)
   uint4 xl[4 / NXL];   // x loads of the step, NXL chunks each (natural pair order)
 };
 
@@ -132,80 +132,86 @@ __device__ __forceinline__ uint4 row_ror(uint4 v) {
                     (uint32_t)__builtin_amdgcn_mov_dpp((int)v.w, ctl, 0xF, 0xF, false));
 }
 
-template <typename XT, int R, int W, int GS, int XR>
-__global__ __launch_bounds__(64 * W) void qmvm_kernel(const uint16_t *__restrict__ x, int M,
-                                                      const uint32_t *__restrict__ codes,
-                                                      const uint16_t *__restrict__ scales,
-                                                      const uint16_t *__restrict__ biases,
-                                                      int64_t N, int64_t K, int kw,
-                                                      uint16_t *__restrict__ y) {
-  constexpr int CPG = 1 << GS;       // chunks per group (G = 32 CPG)
-  constexpr int NG = 4 / CPG;        // groups per step
-  // rows of x carried per chunk slot of a load: output rows >= M are
-  // discarded, so A-operand rows XR.. may hold anything and one 16-byte load
-  // per lane carries NXL = 16 / XR chunks (lanes XR s .. XR s + XR - 1 of a
-  // row of 16 hold chunk slot s); a row rotation moves a slot to lanes 0..
-  constexpr int NXL = 16 / XR;
-  __shared__ float part[W][R * 16][8];  // per wave: rows of W x the 8 rows of x
-  extern __shared__ __attribute__((aligned(16))) uint16_t sbl[];  // [2][16 R][gpr] scales, biases
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n16 = lane & 15, h = lane >> 4;
-  const int64_t row0 = (int64_t)blockIdx.x * (16 * R);
-  const int nch = (int)(K >> 5);
-  const int64_t wpr = (int64_t)nch * 4, gpr = nch >> GS;
-  const int64_t nrows = N - row0 < 16 * R ? N - row0 : 16 * R;
-  const int sb_off = (int)(16 * R * gpr);  // biases after scales in sbl
+// One workgroup's share: 16 rows of W (rows past the matrix read as zero)
+// against up to XR rows of x, K split over its W waves.  GS: log2 of the
+// chunks per group.  XR: rows of x carried per chunk slot of an x load --
+// output rows >= XR are discarded, so A-operand rows XR.. may hold
+// anything, and one 16-byte load per lane carries NXL = 16 / XR chunks
+// (lanes XR s .. XR s + XR - 1 of a row of 16 hold chunk slot s); a row
+// rotation moves a slot to lanes 0.. .
+template <typename XT, int W, int GS, int XR>
+struct MBlock {
+  static constexpr int CPG = 1 << GS;  // chunks per group (G = 32 CPG)
+  static constexpr int NG = 4 / CPG;   // groups per step
+  static constexpr int NXL = 16 / XR;
 
-  // buffer resources: rows past N and rows of x past M read as zero
-  const __amdgpu_buffer_rsrc_t rw = mk_rsrc(codes + row0 * wpr, nrows * wpr * 4);
-  const __amdgpu_buffer_rsrc_t rs = mk_rsrc(scales + row0 * gpr, nrows * gpr * 2);
-  const __amdgpu_buffer_rsrc_t rb = mk_rsrc(biases + row0 * gpr, nrows * gpr * 2);
-  const __amdgpu_buffer_rsrc_t rx = mk_rsrc(x, (int64_t)M * K * 2);
+  __amdgpu_buffer_rsrc_t rw, rx;
+  const uint16_t *sbl;  // LDS: [2][16][gpr] scales, biases of the 16 rows
+  int64_t K, wpr, gpr;
+  int nch, n16, h, c_beg, c_end;
 
-  // constants in registers the optimizer cannot see through (identity DPP
-  // moves), so the unpack stays one v_and_or_b32 per pair
-  const uint32_t vmask = opaque(0x000F000Fu), vmagic = opaque(mm_traits<XT>::magic);
-  const uint32_t vones = opaque(mm_traits<XT>::ones);
-  const uint4 ones = make_uint4(vones, vones, vones, vones);
-  const float off = mm_traits<XT>::off;
+  __device__ void setup(const uint32_t *codes16, int64_t nrows, int64_t K_, int kw, int wave,
+                        int lane, const uint16_t *sbl_, __amdgpu_buffer_rsrc_t rx_) {
+    K = K_;
+    nch = (int)(K >> 5);
+    wpr = (int64_t)nch * 4;
+    gpr = nch >> GS;
+    n16 = lane & 15;
+    h = lane >> 4;
+    rw = mk_rsrc(codes16, nrows * wpr * 4);
+    rx = rx_;
+    sbl = sbl_;
+    // this wave's K range, whole steps of 4 chunks (each a whole number of groups)
+    c_beg = wave * (kw >> 5);
+    c_end = c_beg + (kw >> 5) < nch ? c_beg + (kw >> 5) : nch;
+  }
 
-  // this wave's K range, whole steps of 4 chunks (each a whole number of groups)
-  const int c_beg = wave * (kw >> 5);
-  const int c_end = c_beg + (kw >> 5) < nch ? c_beg + (kw >> 5) : nch;
-
-  auto load = [&](int c0, MStep<R, NXL> &st) {
-    const bool inside = c0 + h < nch;  // chunks past K read as zero
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const uint32_t o = (uint32_t)(((int64_t)(16 * r + n16) * wpr + (int64_t)(inside ? c0 + h : 0) * 4) * 4);
-      const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)o, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st.cw[r][i] = inside ? v[i] : 0u;
+  // scales and biases of the 16 rows (one contiguous, 16-byte aligned range
+  // each) to LDS with 16-byte loads; a load that crosses the end of the valid
+  // rows reads as zero as a whole, so whole units inside them first, then
+  // 2-byte loads, zeros past them.  The caller synchronizes.
+  static __device__ void stage_sb(const uint16_t *scales16, const uint16_t *biases16,
+                                  int64_t nrows, int64_t gpr_, uint16_t *sb) {
+    const __amdgpu_buffer_rsrc_t rs = mk_rsrc(scales16, nrows * gpr_ * 2);
+    const __amdgpu_buffer_rsrc_t rb = mk_rsrc(biases16, nrows * gpr_ * 2);
+    const int valid = (int)(nrows * gpr_), total = 16 * (int)gpr_;
+    const int full = valid >> 3;
+    for (int i = threadIdx.x; i < full; i += 64 * W) {
+      const u32x4v vs = __builtin_amdgcn_raw_buffer_load_b128(rs, i * 16, 0, 0);
+      const u32x4v vb = __builtin_amdgcn_raw_buffer_load_b128(rb, i * 16, 0, 0);
+      *reinterpret_cast<u32x4v *>(sb + i * 8) = vs;
+      *reinterpret_cast<u32x4v *>(sb + total + i * 8) = vb;
     }
+    for (int e = full * 8 + threadIdx.x; e < total; e += 64 * W) {
+      const bool in = e < valid;
+      sb[e] = in ? (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rs, e * 2, 0, 0) : (uint16_t)0;
+      sb[total + e] = in ? (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rb, e * 2, 0, 0) : (uint16_t)0;
+    }
+  }
+
+  __device__ void load(int c0, uint32_t xro, MStep<NXL> &st) const {
+    const bool inside = c0 + h < nch;  // chunks past K read as zero
+    const uint32_t o = (uint32_t)(((int64_t)n16 * wpr + (int64_t)(inside ? c0 + h : 0) * 4) * 4);
+    const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)o, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st.cw[i] = inside ? v[i] : 0u;
 #pragma unroll
     for (int t = 0; t < 4 / NXL; ++t) {
       const int cx = c0 + t * NXL + n16 / XR;
       const int c = cx < nch ? cx : 0;
-      const uint32_t o = (uint32_t)(((int64_t)(n16 % XR) * K + (int64_t)c * 32 + 8 * h) * 2);
-      const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)o, 0, 0);
-      st.xl[t] = make_uint4(v[0], v[1], v[2], v[3]);
+      const u32x4v u = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(xro + (uint32_t)(c * 32 + 8 * h) * 2u), 0, 0);
+      st.xl[t] = make_uint4(u[0], u[1], u[2], u[3]);
     }
-  };
+  }
 
-  f32x4v acc[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = (f32x4v){0.f, 0.f, 0.f, 0.f};
-
-  auto compute = [&](int c0, MStep<R, NXL> &st) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) transpose4(st.cw[r]);  // quarter h: word h of chunks c0 .. c0+3
+  __device__ void compute(int c0, MStep<NXL> &st, f32x4v &acc, uint32_t vmask, uint32_t vmagic,
+                          uint4 ones) const {
+    const float off = mm_traits<XT>::off;
+    transpose4(st.cw);  // quarter h: word h of chunks c0 .. c0+3
 #pragma unroll
     for (int q = 0; q < NG; ++q) {
       if (c0 + q * CPG >= c_end) break;  // past K (uniform)
-      f32x4v xg = (f32x4v){0.f, 0.f, 0.f, 0.f}, pg[R];
-#pragma unroll
-      for (int r = 0; r < R; ++r) pg[r] = (f32x4v){0.f, 0.f, 0.f, 0.f};
+      f32x4v xg = (f32x4v){0.f, 0.f, 0.f, 0.f}, pg = (f32x4v){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int jj = 0; jj < CPG; ++jj) {
         const int j = q * CPG + jj;
@@ -219,92 +225,196 @@ __global__ __launch_bounds__(64 * W) void qmvm_kernel(const uint16_t *__restrict
         }
         const uint4 xa = c0 + j < nch ? permute_x(xr) : make_uint4(0, 0, 0, 0);
         xg = mfma16<XT>(xa, ones, xg);
-#pragma unroll
-        for (int r = 0; r < R; ++r) pg[r] = mfma16<XT>(xa, unpack_word(st.cw[r][j], vmask, vmagic), pg[r]);
+        pg = mfma16<XT>(xa, unpack_word(st.cw[j], vmask, vmagic), pg);
       }
+      const int li = n16 * (int)gpr + (c0 >> GS) + q;
+      const float sc = f16_to_f32(sbl[li]), bi = f16_to_f32(sbl[16 * (int)gpr + li]);
+      const float bo = __builtin_fmaf(-off, sc, bi);
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int g = (c0 >> GS) + q, li = (16 * r + n16) * (int)gpr + g;
-        const float sc = f16_to_f32(sbl[li]), bi = f16_to_f32(sbl[sb_off + li]);
-        const float bo = __builtin_fmaf(-off, sc, bi);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc[r][e] = __builtin_fmaf(bo, xg[e], __builtin_fmaf(sc, pg[r][e], acc[r][e]));
-      }
+      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(bo, xg[e], __builtin_fmaf(sc, pg[e], acc[e]));
     }
-  };
-
-  // double-buffered: the next step's loads are in flight while this one
-  // computes.  The prefetch is unconditional (past the range it re-reads
-  // memory inside the matrix, or zeros past K): a load issued on only some
-  // paths would make the in-order load counter wait for everything in flight.
-  MStep<R, NXL> sa, sb;
-  if (c_beg < c_end) load(c_beg, sa);
-  // the workgroup's scales and biases (16 R whole rows: one contiguous,
-  // 16-byte aligned range each) go to LDS once, while the first loads fly
-  // (a load that crosses the end of the valid rows reads as zero as a whole,
-  // so whole 16-byte units inside it first, then 2-byte loads, zeros past it)
-  {
-    const int valid = (int)(nrows * gpr), total = 16 * R * (int)gpr;
-    const int full = valid >> 3;  // 16-byte units entirely inside the valid rows
-    for (int i = threadIdx.x; i < full; i += 64 * W) {
-      const u32x4v vs = __builtin_amdgcn_raw_buffer_load_b128(rs, i * 16, 0, 0);
-      const u32x4v vb = __builtin_amdgcn_raw_buffer_load_b128(rb, i * 16, 0, 0);
-      *reinterpret_cast<u32x4v *>(sbl + i * 8) = vs;
-      *reinterpret_cast<u32x4v *>(sbl + sb_off + i * 8) = vb;
-    }
-    for (int e = full * 8 + threadIdx.x; e < total; e += 64 * W) {
-      const bool in = e < valid;
-      sbl[e] = in ? (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rs, e * 2, 0, 0) : (uint16_t)0;
-      sbl[sb_off + e] = in ? (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rb, e * 2, 0, 0) : (uint16_t)0;
-    }
-    __syncthreads();
   }
-  if (c_beg < c_end) {
+
+  // partial sums of this wave's K range; lane (n16, h) gets output rows
+  // m = 4 h + e of x against W row n16.  xro: byte offset of the x row that
+  // chunk slot row (n16 % XR) carries (past the x resource: zeros).
+  __device__ f32x4v run(uint32_t xro) const {
+    const uint32_t vmask = opaque(0x000F000Fu), vmagic = opaque(mm_traits<XT>::magic);
+    const uint32_t vones = opaque(mm_traits<XT>::ones);
+    const uint4 ones = make_uint4(vones, vones, vones, vones);
+    f32x4v acc = (f32x4v){0.f, 0.f, 0.f, 0.f};
+    if (c_beg >= c_end) return acc;
+    // double-buffered: the next step's loads are in flight while this one
+    // computes.  The prefetch is unconditional (past the range it re-reads
+    // memory inside the matrix, or zeros past K): a load issued on only some
+    // paths would make the in-order load counter wait for everything in flight.
+    MStep<NXL> sa, sb;
+    load(c_beg, xro, sa);
     int c0 = c_beg;
     for (; c0 + 8 <= c_end; c0 += 8) {
-      load(c0 + 4, sb);
-      compute(c0, sa);
-      load(c0 + 8, sa);
-      compute(c0 + 4, sb);
+      load(c0 + 4, xro, sb);
+      compute(c0, sa, acc, vmask, vmagic, ones);
+      load(c0 + 8, xro, sa);
+      compute(c0 + 4, sb, acc, vmask, vmagic, ones);
     }
     if (c0 < c_end) {
-      load(c0 + 4, sb);
-      compute(c0, sa);
-      if (c0 + 4 < c_end) compute(c0 + 4, sb);
+      load(c0 + 4, xro, sb);
+      compute(c0, sa, acc, vmask, vmagic, ones);
+      if (c0 + 4 < c_end) compute(c0 + 4, sb, acc, vmask, vmagic, ones);
     }
+    return acc;
   }
+};
 
-  // lane (n16, h) holds rows m = 4 h + e of x against W row 16 r + n16
+// sum the W waves' partial sums (lanes h < 2 hold output rows 0..7) through
+// LDS; out(n, m, v) receives row n of the 16, x row m < 8, value v
+template <int W, typename F>
+__device__ __forceinline__ void reduce_out(float (&part)[W][16][8], int wave, int lane,
+                                           const f32x4v &acc, F out) {
+  const int n16 = lane & 15, h = lane >> 4;
   if (h < 2) {
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) part[wave][16 * r + n16][4 * h + e] = acc[r][e];
+    for (int e = 0; e < 4; ++e) part[wave][n16][4 * h + e] = acc[e];
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < R * 16 * 8; i += 64 * W) {
-    const int nn = i >> 3, m = i & 7;
+  for (int i = threadIdx.x; i < 16 * 8; i += 64 * W) {
     float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < W; ++w) v += part[w][nn][m];
-    if (m < M && row0 + nn < N) y[(int64_t)m * N + row0 + nn] = xtraits<XT>::from_f32(v);
+    for (int w = 0; w < W; ++w) v += part[w][i >> 3][i & 7];
+    out(i >> 3, i & 7, v);
   }
 }
 
-template <typename XT, int R, int W, int XR>
+template <typename XT, int W, int GS, int XR>
+__global__ __launch_bounds__(64 * W) void qmvm_kernel(const uint16_t *__restrict__ x, int M,
+                                                      const uint32_t *__restrict__ codes,
+                                                      const uint16_t *__restrict__ scales,
+                                                      const uint16_t *__restrict__ biases,
+                                                      int64_t N, int64_t K, int kw,
+                                                      uint16_t *__restrict__ y) {
+  __shared__ float part[W][16][8];
+  extern __shared__ __attribute__((aligned(16))) uint16_t sbl[];  // [2][16][gpr]
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t row0 = (int64_t)blockIdx.x * 16;
+  const int64_t nrows = N - row0 < 16 ? N - row0 : 16;
+  const int64_t gpr = (K >> 5) >> GS;
+  MBlock<XT, W, GS, XR> blk;
+  blk.setup(codes + row0 * (K >> 5) * 4, nrows, K, kw, wave, lane, sbl,
+            mk_rsrc(x, (int64_t)M * K * 2));  // rows of x past M read as zero
+  MBlock<XT, W, GS, XR>::stage_sb(scales + row0 * gpr, biases + row0 * gpr, nrows, gpr, sbl);
+  __syncthreads();
+  const f32x4v acc = blk.run((uint32_t)((int64_t)((lane & 15) % XR) * K * 2));
+  reduce_out<W>(part, wave, lane, acc, [&](int nn, int m, float v) {
+    if (m < M && row0 + nn < N) y[(int64_t)m * N + row0 + nn] = xtraits<XT>::from_f32(v);
+  });
+}
+
+// Mixture-of-experts gather ("Quantization", metalworking, gather variants
+// for MoE experts): y[t, j, :] = x[t] @ W_{ids[t, j]}^T.  One workgroup per
+// (16 rows, expert e) collects the (token, slot) pairs routed to e and runs
+// them in batches of up to 8 x rows through the matrix cores, so each
+// expert's rows are read once per batch of tokens that chose it (experts no
+// token chose are never read).  Pairs whose id is outside [0, E) get zero
+// rows, written by the workgroups of expert 0.
+constexpr int kGTile = 256;  // ids scanned per round
+
+template <typename XT, int W, int GS>
+__global__ __launch_bounds__(64 * W) void gather_qmvm_kernel(
+    const uint16_t *__restrict__ x, int64_t T, const uint32_t *__restrict__ codes,
+    const uint16_t *__restrict__ scales, const uint16_t *__restrict__ biases, int64_t E, int64_t N,
+    int64_t K, const int32_t *__restrict__ ids, int topk, int kw, uint16_t *__restrict__ y) {
+  __shared__ float part[W][16][8];
+  __shared__ int list[kGTile];
+  __shared__ int count;
+  extern __shared__ __attribute__((aligned(16))) uint16_t sbl[];  // [2][16][gpr]
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int e = blockIdx.y;
+  const int64_t row0 = (int64_t)blockIdx.x * 16;
+  const int64_t nrows = N - row0 < 16 ? N - row0 : 16;
+  const int64_t gpr = (K >> 5) >> GS, wpe = N * (K >> 5) * 4;
+  const int64_t total = T * topk;
+
+  // pairs with an id outside the table: zero rows (expert-0 workgroups)
+  if (e == 0)
+    for (int64_t p = threadIdx.x; p < total; p += 64 * W) {
+      const int32_t id = ids[p];
+      if (id < 0 || id >= E)
+        for (int nn = 0; nn < nrows; ++nn) y[p * N + row0 + nn] = 0;
+    }
+  // does any pair choose this expert?  (if not, nothing of it is read)
+  if (threadIdx.x == 0) count = 0;
+  __syncthreads();
+  for (int64_t p = threadIdx.x; p < total; p += 64 * W)
+    if (ids[p] == e) atomicAdd(&count, 1);
+  __syncthreads();
+  if (count == 0) return;
+
+  MBlock<XT, W, GS, 8> blk;
+  blk.setup(codes + e * wpe + row0 * (K >> 5) * 4, nrows, K, kw, wave, lane, sbl,
+            mk_rsrc(x, T * K * 2));
+  MBlock<XT, W, GS, 8>::stage_sb(scales + (e * N + row0) * gpr, biases + (e * N + row0) * gpr,
+                                 nrows, gpr, sbl);
+  for (int64_t t0 = 0; t0 < total; t0 += kGTile) {
+    __syncthreads();  // also publishes the staged scales before the first batch
+    if (threadIdx.x == 0) count = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < kGTile; i += 64 * W) {
+      const int64_t p = t0 + i;
+      if (p < total && ids[p] == e) list[atomicAdd(&count, 1)] = (int)i;
+    }
+    __syncthreads();
+    const int n = count;
+    for (int b0 = 0; b0 < n; b0 += 8) {
+      // slot row m = n16 % 8 carries pair list[b0 + m]; missing pairs read
+      // past the x resource (zeros)
+      const int m = lane & 7;
+      const uint32_t xro = b0 + m < n ? (uint32_t)(((t0 + list[b0 + m]) / topk) * K * 2)
+                                      : (uint32_t)(T * K * 2);
+      const f32x4v acc = blk.run(xro);
+      reduce_out<W>(part, wave, lane, acc, [&](int nn, int mm, float v) {
+        if (b0 + mm < n && row0 + nn < N)
+          y[(t0 + list[b0 + mm]) * N + row0 + nn] = xtraits<XT>::from_f32(v);
+      });
+      __syncthreads();  // part and list reused
+    }
+  }
+}
+
+template <typename XT, int W, int XR>
 hipError_t qmvm_go(const void *x, int M, const uint32_t *codes, const uint16_t *scales,
                    const uint16_t *biases, int64_t N, int64_t K, int G, void *y, hipStream_t s) {
   const int64_t steps = (K + kStepK - 1) / kStepK;
   const int kw = (int)((steps + W - 1) / W) * kStepK;  // k per wave, whole steps
-  const int64_t blocks = (N + 16 * R - 1) / (16 * R);
+  const int64_t blocks = (N + 15) / 16;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks), block(64 * W);
-  const size_t lds = (size_t)2 * 16 * R * (K / G) * 2;  // scales + biases of the rows
+  const size_t lds = (size_t)2 * 16 * (K / G) * 2;  // scales + biases of the rows
   switch (G) {
-    case 32: hipLaunchKernelGGL((qmvm_kernel<XT, R, W, 0, XR>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y); break;
-    case 64: hipLaunchKernelGGL((qmvm_kernel<XT, R, W, 1, XR>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y); break;
-    case 128: hipLaunchKernelGGL((qmvm_kernel<XT, R, W, 2, XR>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y); break;
+    case 32: hipLaunchKernelGGL((qmvm_kernel<XT, W, 0, XR>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y); break;
+    case 64: hipLaunchKernelGGL((qmvm_kernel<XT, W, 1, XR>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y); break;
+    case 128: hipLaunchKernelGGL((qmvm_kernel<XT, W, 2, XR>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename XT>
+hipError_t gather_go(const void *x, int64_t T, const uint32_t *codes, const uint16_t *scales,
+                     const uint16_t *biases, int64_t E, int64_t N, int64_t K,
+                     const int32_t *ids, int topk, int G, void *y, hipStream_t s) {
+  constexpr int W = 2;  // the grid has (rows / 16) x E workgroups: split K in two
+  const int64_t steps = (K + kStepK - 1) / kStepK;
+  const int kw = (int)((steps + W - 1) / W) * kStepK;
+  const int64_t blocks = (N + 15) / 16;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks, (unsigned)E), block(64 * W);
+  const size_t lds = (size_t)2 * 16 * (K / G) * 2;
+  switch (G) {
+    case 32: hipLaunchKernelGGL((gather_qmvm_kernel<XT, W, 0>), grid, block, lds, s, (const uint16_t *)x, T, codes, scales, biases, E, N, K, ids, topk, kw, (uint16_t *)y); break;
+    case 64: hipLaunchKernelGGL((gather_qmvm_kernel<XT, W, 1>), grid, block, lds, s, (const uint16_t *)x, T, codes, scales, biases, E, N, K, ids, topk, kw, (uint16_t *)y); break;
+    case 128: hipLaunchKernelGGL((gather_qmvm_kernel<XT, W, 2>), grid, block, lds, s, (const uint16_t *)x, T, codes, scales, biases, E, N, K, ids, topk, kw, (uint16_t *)y); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -330,18 +440,32 @@ hipError_t launch_qmvm(const void *x, int x_dtype, int M, const uint32_t *codes,
   const int W = rowblocks * 2 >= target ? 2 : rowblocks * 4 >= target ? 4 : rowblocks * 8 >= target ? 8 : 16;
 #define AQ_QMVM_W(T, XR) \
   switch (W) { \
-    case 2: return qmvm_go<T, 1, 2, XR>(x, M, codes, scales, biases, N, K, G, y, s); \
-    case 4: return qmvm_go<T, 1, 4, XR>(x, M, codes, scales, biases, N, K, G, y, s); \
-    case 8: return qmvm_go<T, 1, 8, XR>(x, M, codes, scales, biases, N, K, G, y, s); \
-    default: return qmvm_go<T, 1, 16, XR>(x, M, codes, scales, biases, N, K, G, y, s); \
+    case 2: return qmvm_go<T, 2, XR>(x, M, codes, scales, biases, N, K, G, y, s); \
+    case 4: return qmvm_go<T, 4, XR>(x, M, codes, scales, biases, N, K, G, y, s); \
+    case 8: return qmvm_go<T, 8, XR>(x, M, codes, scales, biases, N, K, G, y, s); \
+    default: return qmvm_go<T, 16, XR>(x, M, codes, scales, biases, N, K, G, y, s); \
   }
 #define AQ_QMVM(T) \
   if (M <= 4) { AQ_QMVM_W(T, 4) } else { AQ_QMVM_W(T, 8) }
   if (x_dtype == X_BF16) { AQ_QMVM(bf16_t) }
   if (x_dtype == X_F16) { AQ_QMVM(f16_t) }
-#undef AQ_QMVM_W
 #undef AQ_QMVM
+#undef AQ_QMVM_W
+  return hipErrorInvalidValue;
+}
+
+bool gather_qmvm_supported(int bits, int64_t K, int G) {
+  return bits == 4 && K >= 32 && (int64_t)2 * 16 * (K / G) * 2 <= 48 * 1024;
+}
+
+hipError_t launch_gather_qmvm(const void *x, int x_dtype, int64_t T, const uint32_t *codes,
+                              const uint16_t *scales, const uint16_t *biases, int64_t E, int64_t N,
+                              int64_t K, const int32_t *ids, int topk, int G, void *y,
+                              hipStream_t s) {
+  if (x_dtype == X_BF16) return gather_go<bf16_t>(x, T, codes, scales, biases, E, N, K, ids, topk, G, y, s);
+  if (x_dtype == X_F16) return gather_go<f16_t>(x, T, codes, scales, biases, E, N, K, ids, topk, G, y, s);
   return hipErrorInvalidValue;
 }
 
 }  // namespace aq
+
