@@ -144,10 +144,10 @@ aq_status aq_qmv(const void *x, aq_dtype x_dtype, int64_t M, const uint32_t *cod
   aq_status st = check_matmul(x, x_dtype, M, codes, scales, biases, N, K, group_size, bits, y);
   if (st != AQ_OK) return st;
   if (M > kMaxQmvRows) return AQ_ERR_INVALID_ARG;
-  // 2..8 rows of 4-bit codes: dot products on the matrix cores
+  // 2..8 rows of 4-bit or 8-bit codes: dot products on the matrix cores
   if (aq::qmvm_supported((int)M, bits, N, K, group_size))
     return from_hip(aq::launch_qmvm(x, (int)x_dtype, (int)M, codes, scales, biases, N, K,
-                                    group_size, y, static_cast<hipStream_t>(stream)));
+                                    group_size, bits, y, static_cast<hipStream_t>(stream)));
   return from_hip(aq::launch_qmv(x, (int)x_dtype, (int)M, codes, scales, biases, N, K, group_size,
                                  bits, y, static_cast<hipStream_t>(stream)));
 }
@@ -184,10 +184,10 @@ aq_status aq_gather_qmv(const void *x, aq_dtype x_dtype, int64_t T, const uint32
   if (st != AQ_OK) return st;
   if (!aligned16(x) || !aligned16(y) || !aligned16(ids)) return AQ_ERR_ALIGNMENT;
   if (E > 65535 || T * topk > 0x7FFFFFFF) return AQ_ERR_UNSUPPORTED;
-  // 4-bit codes: batches of routed tokens on the matrix cores
+  // 4-bit or 8-bit codes: batches of routed tokens on the matrix cores
   if (aq::gather_qmvm_supported(bits, K, group_size) && T * K * 2 <= 0x7FFFFFFF)
     return from_hip(aq::launch_gather_qmvm(x, (int)x_dtype, T, codes, scales, biases, E, N, K,
-                                           ids, topk, group_size, y,
+                                           ids, topk, group_size, bits, y,
                                            static_cast<hipStream_t>(stream)));
   return from_hip(aq::launch_gather_qmv(x, (int)x_dtype, T, codes, scales, biases, E, N, K, ids,
                                         topk, group_size, bits, y,

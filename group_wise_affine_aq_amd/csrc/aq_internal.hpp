@@ -30,19 +30,19 @@ hipError_t launch_qmv(const void *x, int x_dtype, int M, const uint32_t *codes,
                       const uint16_t *scales, const uint16_t *biases, int64_t N, int64_t K, int G,
                       int bits, void *y, hipStream_t s);
 
-// y[M, N] = x[M, K] @ W^T for a few rows on the matrix cores (4-bit codes);
-// qmvm_supported says which shapes it takes
+// y[M, N] = x[M, K] @ W^T for a few rows on the matrix cores (4-bit and
+// 8-bit codes); qmvm_supported says which shapes it takes
 bool qmvm_supported(int M, int bits, int64_t N, int64_t K, int G);
 hipError_t launch_qmvm(const void *x, int x_dtype, int M, const uint32_t *codes,
                        const uint16_t *scales, const uint16_t *biases, int64_t N, int64_t K, int G,
-                       void *y, hipStream_t s);
+                       int bits, void *y, hipStream_t s);
 
-// the same on the matrix cores for 4-bit codes (gather_qmvm_supported says
-// which shapes it takes)
+// the mixture-of-experts gather on the matrix cores (4-bit and 8-bit codes;
+// gather_qmvm_supported says which shapes it takes)
 bool gather_qmvm_supported(int bits, int64_t K, int G);
 hipError_t launch_gather_qmvm(const void *x, int x_dtype, int64_t T, const uint32_t *codes,
                               const uint16_t *scales, const uint16_t *biases, int64_t E, int64_t N,
-                              int64_t K, const int32_t *ids, int topk, int G, void *y,
+                              int64_t K, const int32_t *ids, int topk, int G, int bits, void *y,
                               hipStream_t s);
 
 // mixture-of-experts gather: y[t, j, :] = x[t] @ W_{ids[t, j]}^T

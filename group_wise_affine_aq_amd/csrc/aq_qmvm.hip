@@ -1,5 +1,5 @@
 // aq_qmvm.hip -- quantized matrix-vector product for a few rows (2 <= M <= 8)
-// on the gfx950 matrix cores, 4-bit codes.
+// on the gfx950 matrix cores, 4-bit and 8-bit codes.
 //
 // The operation is the QMV of "Quantization" (metalworking, MLX notes, QMV
 // bullet), y = x @ W^T with W packed, for the speculative-decoding widths
@@ -12,17 +12,27 @@
 //
 //  * v_mfma_f32_16x16x32_{bf16,f16}: A = x (16 rows, rows >= M read as
 //    zero), B = 16 rows of W, each code q entering as the exact value
-//    OFF + q (one v_and_or_b32 per pair: OFF = 128 in bf16, 1024 in fp16),
-//    so one MFMA over a 32-code chunk gives P = sum x * (OFF + q);
+//    OFF + q, so one MFMA over 32 codes gives P = sum x * (OFF + q).
+//    4-bit: one v_and_or_b32 per pair (OFF = 128 in bf16, 1024 in fp16).
+//    8-bit, fp16: one v_perm_b32 per pair puts the byte under an 0x64 high
+//    byte (OFF = 1024).  8-bit, bf16: bf16 has too few mantissa bits for
+//    that, so the byte goes through binary32 (v_cvt_f32_ubyte*, exact) and
+//    a packed round to bf16, also exact (OFF = 0);
 //  * a second MFMA against a register of ones gives X = sum x over the same
 //    chunk, already in the output lane layout;
 //  * per group, y += s * (P - OFF * X) + b * X = s * P + (b - OFF * s) * X,
 //    the same identity the vector kernels apply (sum_k x (q s + b) over a
 //    group), in binary32;
-//  * codes arrive as 16-byte loads (lane quarter h reads chunk h of a 4-chunk
-//    step of its row) and a 4x4 transpose across the lane quarters
+//  * codes arrive as 16-byte loads.  4-bit: lane quarter h reads chunk h of
+//    a 4-chunk step of its row, and a 4x4 transpose across the lane quarters
 //    (v_permlane32_swap, v_permlane16_swap) gives each quarter code word h of
-//    every chunk, which is the MFMA B-operand layout;
+//    every chunk, which is the MFMA B-operand layout.  8-bit: each of two
+//    loads covers two chunks; quarter h holds codes 16h .. 16h+15 of them,
+//    which already is the B layout of two MFMAs when a group spans both
+//    chunks (G >= 64); for G = 32 one v_permlane32_swap per register pair
+//    brings each MFMA back inside one chunk (quarter h then holds 8-code
+//    unit sigma(h) = (0, 2, 1, 3)[h] of it).  The MFMA's k order is free as
+//    long as x follows it, and x is loaded to match;
 //  * x is read straight from global memory (it stays in L2), one 16-byte load
 //    per lane carrying two chunks (M <= 8) or four (M <= 4) in the lanes of
 //    A-operand rows that only feed discarded output rows, moved into place by
@@ -41,24 +51,39 @@ namespace aq {
 namespace {
 
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8v __attribute__((ext_vector_type(8)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kStepK = 128;  // k per step: 4 chunks
 
-template <typename XT>
+// per (activation type, code width): the register constant of the unpack
+// and the offset OFF that every code value carries into the products
+template <typename XT, int BITS>
 struct mm_traits;
 template <>
-struct mm_traits<bf16_t> {
+struct mm_traits<bf16_t, 4> {
   static constexpr uint32_t magic = 0x43004300u;  // bf16 128.0 in both halves
   static constexpr uint32_t ones = 0x3F803F80u;   // bf16 1.0
   static constexpr float off = 128.f;
 };
 template <>
-struct mm_traits<f16_t> {
+struct mm_traits<f16_t, 4> {
   static constexpr uint32_t magic = 0x64006400u;  // fp16 1024.0
   static constexpr uint32_t ones = 0x3C003C00u;   // fp16 1.0
+  static constexpr float off = 1024.f;
+};
+template <>
+struct mm_traits<bf16_t, 8> {
+  static constexpr uint32_t magic = 0u;  // unused: codes are converted exactly
+  static constexpr uint32_t ones = 0x3F803F80u;
+  static constexpr float off = 0.f;
+};
+template <>
+struct mm_traits<f16_t, 8> {
+  static constexpr uint32_t magic = 0x64646464u;  // high bytes of fp16 1024 + q
+  static constexpr uint32_t ones = 0x3C003C00u;
   static constexpr float off = 1024.f;
 };
 
@@ -105,6 +130,31 @@ __device__ __forceinline__ uint4 unpack_word(uint32_t w, uint32_t mask, uint32_t
   return make_uint4(p[0], p[1], p[2], p[3]);
 }
 
+// 8 codes of two words (8-bit) -> 4 registers of (OFF + q_2e, OFF + q_2e+1)
+// pairs, in code order.  fp16: v_perm_b32 places bytes e, e+1 under the
+// 0x64 bytes of the magic register (fp16 0x64qq = 1024 + q exactly).  bf16:
+// unsigned byte to binary32 and a packed round to bf16, exact for q < 256.
+template <typename XT>
+__device__ __forceinline__ uint4 unpack_bytes(uint32_t w0, uint32_t w1, uint32_t magic) {
+  if constexpr (std::is_same<XT, f16_t>::value) {
+    return make_uint4(__builtin_amdgcn_perm(magic, w0, 0x04010400u),
+                      __builtin_amdgcn_perm(magic, w0, 0x04030402u),
+                      __builtin_amdgcn_perm(magic, w1, 0x04010400u),
+                      __builtin_amdgcn_perm(magic, w1, 0x04030402u));
+  } else {
+    uint32_t p[4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t w = i == 0 ? w0 : w1;
+      const bf16x2v lo = {(__bf16)(float)(w & 0xFFu), (__bf16)(float)((w >> 8) & 0xFFu)};
+      const bf16x2v hi = {(__bf16)(float)((w >> 16) & 0xFFu), (__bf16)(float)(w >> 24)};
+      p[2 * i] = __builtin_bit_cast(uint32_t, lo);
+      p[2 * i + 1] = __builtin_bit_cast(uint32_t, hi);
+    }
+    return make_uint4(p[0], p[1], p[2], p[3]);
+  }
+}
+
 // natural pairs (x0 x1)(x2 x3)(x4 x5)(x6 x7) -> (x0 x4)(x1 x5)(x2 x6)(x3 x7)
 __device__ __forceinline__ uint4 permute_x(uint4 v) {
   return make_uint4(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u),  // lo16(x) | lo16(z) << 16
@@ -114,10 +164,12 @@ __device__ __forceinline__ uint4 permute_x(uint4 v) {
 }
 
 // one step (4 chunks) of one wave's K range, as loaded
-template <int NXL>
+template <int NXL, int BITS>
 struct MStep {
-  uint32_t cw[4];      // quarter h: chunk c0 + h of row n16 (4-bit: 4 words)
-  uint4 xl[4 / NXL];   // x loads of the step, NXL chunks each (natural pair order)
+  // 4-bit: quarter h holds chunk c0 + h of row n16.  8-bit: words 4r .. 4r+3
+  // hold words 4 (h & 1) .. +3 of chunk c0 + 2r + (h >> 1)
+  uint32_t cw[BITS];
+  uint4 xl[4 / NXL];   // x loads of the step, NXL MFMA slots each (natural pair order)
 };
 
 // lane l of a row of 16 receives the value of lane (l + 16 - k) % 16 ... i.e. a
@@ -139,11 +191,26 @@ __device__ __forceinline__ uint4 row_ror(uint4 v) {
 // anything, and one 16-byte load per lane carries NXL = 16 / XR chunks
 // (lanes XR s .. XR s + XR - 1 of a row of 16 hold chunk slot s); a row
 // rotation moves a slot to lanes 0.. .
-template <typename XT, int W, int GS, int XR>
+template <typename XT, int BITS, int W, int GS, int XR>
 struct MBlock {
   static constexpr int CPG = 1 << GS;  // chunks per group (G = 32 CPG)
   static constexpr int NG = 4 / CPG;   // groups per step
   static constexpr int NXL = 16 / XR;
+  // 8-bit with a group inside each 32-code chunk: a lane-half swap per
+  // register pair keeps every MFMA inside one chunk (one group)
+  static constexpr bool kSwap = BITS == 8 && GS == 0;
+
+  // first chunk of the codes behind MFMA slot j of the step at chunk c0 (the
+  // slot is past K iff this chunk is), and quarter h's offset into its x row
+  // in elements, so that x follows the k order of the B operand
+  static __device__ __forceinline__ int slot_chunk(int c0, int j) {
+    return BITS == 8 && !kSwap ? c0 + 2 * (j >> 1) : c0 + j;
+  }
+  static __device__ __forceinline__ int slot_xoff(int cb, int j, int h) {
+    if constexpr (BITS == 4) return cb * 32 + 8 * h;
+    else if constexpr (kSwap) return cb * 32 + 8 * ((h >> 1) | ((h & 1) << 1));
+    else return cb * 32 + 16 * h + 8 * (j & 1);
+  }
 
   __amdgpu_buffer_rsrc_t rw, rx;
   const uint16_t *sbl;  // LDS: [2][16][gpr] scales, biases of the 16 rows
@@ -154,7 +221,7 @@ struct MBlock {
                         int lane, const uint16_t *sbl_, __amdgpu_buffer_rsrc_t rx_) {
     K = K_;
     nch = (int)(K >> 5);
-    wpr = (int64_t)nch * 4;
+    wpr = (int64_t)nch * BITS;  // a 32-code chunk is BITS words
     gpr = nch >> GS;
     n16 = lane & 15;
     h = lane >> 4;
@@ -189,25 +256,44 @@ struct MBlock {
     }
   }
 
-  __device__ void load(int c0, uint32_t xro, MStep<NXL> &st) const {
-    const bool inside = c0 + h < nch;  // chunks past K read as zero
-    const uint32_t o = (uint32_t)(((int64_t)n16 * wpr + (int64_t)(inside ? c0 + h : 0) * 4) * 4);
-    const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)o, 0, 0);
+  __device__ void load(int c0, uint32_t xro, MStep<NXL, BITS> &st) const {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) st.cw[i] = inside ? v[i] : 0u;
+    for (int r = 0; r < BITS / 4; ++r) {
+      // 4-bit: chunk c0 + h.  8-bit: words 4 (h & 1) .. of chunk c0 + 2r + (h >> 1)
+      const int ch = BITS == 4 ? c0 + h : c0 + 2 * r + (h >> 1);
+      const bool inside = ch < nch;  // chunks past K read as zero
+      const int64_t wo = BITS == 4 ? (int64_t)ch * 4 : (int64_t)ch * 8 + 4 * (h & 1);
+      const uint32_t o = (uint32_t)(((int64_t)n16 * wpr + (inside ? wo : 0)) * 4);
+      const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)o, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st.cw[4 * r + i] = inside ? v[i] : 0u;
+    }
 #pragma unroll
     for (int t = 0; t < 4 / NXL; ++t) {
-      const int cx = c0 + t * NXL + n16 / XR;
-      const int c = cx < nch ? cx : 0;
-      const u32x4v u = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(xro + (uint32_t)(c * 32 + 8 * h) * 2u), 0, 0);
+      const int j = t * NXL + n16 / XR;  // MFMA slot this lane's load carries
+      const int cb = slot_chunk(c0, j);
+      const int xo = cb < nch ? slot_xoff(cb, j, h) : 0;
+      const u32x4v u = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(xro + (uint32_t)xo * 2u), 0, 0);
       st.xl[t] = make_uint4(u[0], u[1], u[2], u[3]);
     }
   }
 
-  __device__ void compute(int c0, MStep<NXL> &st, f32x4v &acc, uint32_t vmask, uint32_t vmagic,
-                          uint4 ones) const {
-    const float off = mm_traits<XT>::off;
-    transpose4(st.cw);  // quarter h: word h of chunks c0 .. c0+3
+  __device__ void compute(int c0, MStep<NXL, BITS> &st, f32x4v &acc, uint32_t vmask,
+                          uint32_t vmagic, uint4 ones) const {
+    const float off = mm_traits<XT, BITS>::off;
+    if constexpr (BITS == 4) {
+      transpose4(st.cw);  // quarter h: word h of chunks c0 .. c0+3
+    } else if constexpr (kSwap) {
+      // quarters (0 1 | 2 3) of pair 0 and pair 1 -> pair 0 of chunk 2r, pair 1 of 2r+1
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          auto v = __builtin_amdgcn_permlane32_swap(st.cw[4 * r + i], st.cw[4 * r + 2 + i], false, false);
+          st.cw[4 * r + i] = v[0];
+          st.cw[4 * r + 2 + i] = v[1];
+        }
+    }
 #pragma unroll
     for (int q = 0; q < NG; ++q) {
       if (c0 + q * CPG >= c_end) break;  // past K (uniform)
@@ -223,9 +309,17 @@ struct MBlock {
           if (j % 4 == 2) xr = row_ror<8>(xr);
           if (j % 4 == 3) xr = row_ror<4>(xr);
         }
-        const uint4 xa = c0 + j < nch ? permute_x(xr) : make_uint4(0, 0, 0, 0);
+        uint4 xa, wb;
+        if constexpr (BITS == 4) {
+          xa = permute_x(xr);
+          wb = unpack_word(st.cw[j], vmask, vmagic);
+        } else {
+          xa = xr;
+          wb = unpack_bytes<XT>(st.cw[2 * j], st.cw[2 * j + 1], vmagic);
+        }
+        if (slot_chunk(c0, j) >= nch) xa = make_uint4(0, 0, 0, 0);
         xg = mfma16<XT>(xa, ones, xg);
-        pg = mfma16<XT>(xa, unpack_word(st.cw[j], vmask, vmagic), pg);
+        pg = mfma16<XT>(xa, wb, pg);
       }
       const int li = n16 * (int)gpr + (c0 >> GS) + q;
       const float sc = f16_to_f32(sbl[li]), bi = f16_to_f32(sbl[16 * (int)gpr + li]);
@@ -239,8 +333,8 @@ struct MBlock {
   // m = 4 h + e of x against W row n16.  xro: byte offset of the x row that
   // chunk slot row (n16 % XR) carries (past the x resource: zeros).
   __device__ f32x4v run(uint32_t xro) const {
-    const uint32_t vmask = opaque(0x000F000Fu), vmagic = opaque(mm_traits<XT>::magic);
-    const uint32_t vones = opaque(mm_traits<XT>::ones);
+    const uint32_t vmask = opaque(0x000F000Fu), vmagic = opaque(mm_traits<XT, BITS>::magic);
+    const uint32_t vones = opaque(mm_traits<XT, BITS>::ones);
     const uint4 ones = make_uint4(vones, vones, vones, vones);
     f32x4v acc = (f32x4v){0.f, 0.f, 0.f, 0.f};
     if (c_beg >= c_end) return acc;
@@ -248,7 +342,7 @@ struct MBlock {
     // computes.  The prefetch is unconditional (past the range it re-reads
     // memory inside the matrix, or zeros past K): a load issued on only some
     // paths would make the in-order load counter wait for everything in flight.
-    MStep<NXL> sa, sb;
+    MStep<NXL, BITS> sa, sb;
     load(c_beg, xro, sa);
     int c0 = c_beg;
     for (; c0 + 8 <= c_end; c0 += 8) {
@@ -285,7 +379,7 @@ __device__ __forceinline__ void reduce_out(float (&part)[W][16][8], int wave, in
   }
 }
 
-template <typename XT, int W, int GS, int XR>
+template <typename XT, int BITS, int W, int GS, int XR>
 __global__ __launch_bounds__(64 * W) void qmvm_kernel(const uint16_t *__restrict__ x, int M,
                                                       const uint32_t *__restrict__ codes,
                                                       const uint16_t *__restrict__ scales,
@@ -299,10 +393,10 @@ __global__ __launch_bounds__(64 * W) void qmvm_kernel(const uint16_t *__restrict
   const int64_t row0 = (int64_t)blockIdx.x * 16;
   const int64_t nrows = N - row0 < 16 ? N - row0 : 16;
   const int64_t gpr = (K >> 5) >> GS;
-  MBlock<XT, W, GS, XR> blk;
-  blk.setup(codes + row0 * (K >> 5) * 4, nrows, K, kw, wave, lane, sbl,
+  MBlock<XT, BITS, W, GS, XR> blk;
+  blk.setup(codes + row0 * (K >> 5) * BITS, nrows, K, kw, wave, lane, sbl,
             mk_rsrc(x, (int64_t)M * K * 2));  // rows of x past M read as zero
-  MBlock<XT, W, GS, XR>::stage_sb(scales + row0 * gpr, biases + row0 * gpr, nrows, gpr, sbl);
+  MBlock<XT, BITS, W, GS, XR>::stage_sb(scales + row0 * gpr, biases + row0 * gpr, nrows, gpr, sbl);
   __syncthreads();
   const f32x4v acc = blk.run((uint32_t)((int64_t)((lane & 15) % XR) * K * 2));
   reduce_out<W>(part, wave, lane, acc, [&](int nn, int m, float v) {
@@ -319,7 +413,7 @@ __global__ __launch_bounds__(64 * W) void qmvm_kernel(const uint16_t *__restrict
 // rows, written by the workgroups of expert 0.
 constexpr int kGTile = 256;  // ids scanned per round
 
-template <typename XT, int W, int GS>
+template <typename XT, int BITS, int W, int GS>
 __global__ __launch_bounds__(64 * W) void gather_qmvm_kernel(
     const uint16_t *__restrict__ x, int64_t T, const uint32_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ biases, int64_t E, int64_t N,
@@ -333,7 +427,7 @@ __global__ __launch_bounds__(64 * W) void gather_qmvm_kernel(
   const int e = blockIdx.y;
   const int64_t row0 = (int64_t)blockIdx.x * 16;
   const int64_t nrows = N - row0 < 16 ? N - row0 : 16;
-  const int64_t gpr = (K >> 5) >> GS, wpe = N * (K >> 5) * 4;
+  const int64_t gpr = (K >> 5) >> GS, wpe = N * (K >> 5) * BITS;
   const int64_t total = T * topk;
 
   // pairs with an id outside the table: zero rows (expert-0 workgroups)
@@ -351,10 +445,10 @@ __global__ __launch_bounds__(64 * W) void gather_qmvm_kernel(
   __syncthreads();
   if (count == 0) return;
 
-  MBlock<XT, W, GS, 8> blk;
-  blk.setup(codes + e * wpe + row0 * (K >> 5) * 4, nrows, K, kw, wave, lane, sbl,
+  MBlock<XT, BITS, W, GS, 8> blk;
+  blk.setup(codes + e * wpe + row0 * (K >> 5) * BITS, nrows, K, kw, wave, lane, sbl,
             mk_rsrc(x, T * K * 2));
-  MBlock<XT, W, GS, 8>::stage_sb(scales + (e * N + row0) * gpr, biases + (e * N + row0) * gpr,
+  MBlock<XT, BITS, W, GS, 8>::stage_sb(scales + (e * N + row0) * gpr, biases + (e * N + row0) * gpr,
                                  nrows, gpr, sbl);
   for (int64_t t0 = 0; t0 < total; t0 += kGTile) {
     __syncthreads();  // also publishes the staged scales before the first batch
@@ -382,7 +476,7 @@ __global__ __launch_bounds__(64 * W) void gather_qmvm_kernel(
   }
 }
 
-template <typename XT, int W, int XR>
+template <typename XT, int BITS, int W, int XR>
 hipError_t qmvm_go(const void *x, int M, const uint32_t *codes, const uint16_t *scales,
                    const uint16_t *biases, int64_t N, int64_t K, int G, void *y, hipStream_t s) {
   const int64_t steps = (K + kStepK - 1) / kStepK;
@@ -392,15 +486,15 @@ hipError_t qmvm_go(const void *x, int M, const uint32_t *codes, const uint16_t *
   const dim3 grid((unsigned)blocks), block(64 * W);
   const size_t lds = (size_t)2 * 16 * (K / G) * 2;  // scales + biases of the rows
   switch (G) {
-    case 32: hipLaunchKernelGGL((qmvm_kernel<XT, W, 0, XR>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y); break;
-    case 64: hipLaunchKernelGGL((qmvm_kernel<XT, W, 1, XR>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y); break;
-    case 128: hipLaunchKernelGGL((qmvm_kernel<XT, W, 2, XR>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y); break;
+    case 32: hipLaunchKernelGGL((qmvm_kernel<XT, BITS, W, 0, XR>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y); break;
+    case 64: hipLaunchKernelGGL((qmvm_kernel<XT, BITS, W, 1, XR>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y); break;
+    case 128: hipLaunchKernelGGL((qmvm_kernel<XT, BITS, W, 2, XR>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <typename XT>
+template <typename XT, int BITS>
 hipError_t gather_go(const void *x, int64_t T, const uint32_t *codes, const uint16_t *scales,
                      const uint16_t *biases, int64_t E, int64_t N, int64_t K,
                      const int32_t *ids, int topk, int G, void *y, hipStream_t s) {
@@ -412,9 +506,9 @@ hipError_t gather_go(const void *x, int64_t T, const uint32_t *codes, const uint
   const dim3 grid((unsigned)blocks, (unsigned)E), block(64 * W);
   const size_t lds = (size_t)2 * 16 * (K / G) * 2;
   switch (G) {
-    case 32: hipLaunchKernelGGL((gather_qmvm_kernel<XT, W, 0>), grid, block, lds, s, (const uint16_t *)x, T, codes, scales, biases, E, N, K, ids, topk, kw, (uint16_t *)y); break;
-    case 64: hipLaunchKernelGGL((gather_qmvm_kernel<XT, W, 1>), grid, block, lds, s, (const uint16_t *)x, T, codes, scales, biases, E, N, K, ids, topk, kw, (uint16_t *)y); break;
-    case 128: hipLaunchKernelGGL((gather_qmvm_kernel<XT, W, 2>), grid, block, lds, s, (const uint16_t *)x, T, codes, scales, biases, E, N, K, ids, topk, kw, (uint16_t *)y); break;
+    case 32: hipLaunchKernelGGL((gather_qmvm_kernel<XT, BITS, W, 0>), grid, block, lds, s, (const uint16_t *)x, T, codes, scales, biases, E, N, K, ids, topk, kw, (uint16_t *)y); break;
+    case 64: hipLaunchKernelGGL((gather_qmvm_kernel<XT, BITS, W, 1>), grid, block, lds, s, (const uint16_t *)x, T, codes, scales, biases, E, N, K, ids, topk, kw, (uint16_t *)y); break;
+    case 128: hipLaunchKernelGGL((gather_qmvm_kernel<XT, BITS, W, 2>), grid, block, lds, s, (const uint16_t *)x, T, codes, scales, biases, E, N, K, ids, topk, kw, (uint16_t *)y); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -424,13 +518,13 @@ hipError_t gather_go(const void *x, int64_t T, const uint32_t *codes, const uint
 
 bool qmvm_supported(int M, int bits, int64_t N, int64_t K, int G) {
   // scales and biases of 16 rows staged in LDS: at most 48 KB
-  return M >= 2 && M <= 8 && bits == 4 && N >= 1 && K >= 32 && 16 * K * 2 <= 0x7FFFFFFF &&
+  return M >= 2 && M <= 8 && (bits == 4 || bits == 8) && N >= 1 && K >= 32 && 16 * K * 2 <= 0x7FFFFFFF &&
          (int64_t)2 * 16 * (K / G) * 2 <= 48 * 1024;
 }
 
 hipError_t launch_qmvm(const void *x, int x_dtype, int M, const uint32_t *codes,
                        const uint16_t *scales, const uint16_t *biases, int64_t N, int64_t K, int G,
-                       void *y, hipStream_t s) {
+                       int bits, void *y, hipStream_t s) {
   // 16 rows per workgroup (<= 128 VGPRs, so 4 waves per SIMD), and K split
   // over W waves so that the grid has about four waves per SIMD: each wave
   // keeps two steps of loads in flight, and the chip needs tens of KB in
@@ -438,32 +532,39 @@ hipError_t launch_qmvm(const void *x, int x_dtype, int M, const uint32_t *codes,
   const int64_t rowblocks = (N + 15) / 16;
   const int64_t target = 4 * 4 * (int64_t)device_cus();
   const int W = rowblocks * 2 >= target ? 2 : rowblocks * 4 >= target ? 4 : rowblocks * 8 >= target ? 8 : 16;
-#define AQ_QMVM_W(T, XR) \
+#define AQ_QMVM_W(T, B, XR) \
   switch (W) { \
-    case 2: return qmvm_go<T, 2, XR>(x, M, codes, scales, biases, N, K, G, y, s); \
-    case 4: return qmvm_go<T, 4, XR>(x, M, codes, scales, biases, N, K, G, y, s); \
-    case 8: return qmvm_go<T, 8, XR>(x, M, codes, scales, biases, N, K, G, y, s); \
-    default: return qmvm_go<T, 16, XR>(x, M, codes, scales, biases, N, K, G, y, s); \
+    case 2: return qmvm_go<T, B, 2, XR>(x, M, codes, scales, biases, N, K, G, y, s); \
+    case 4: return qmvm_go<T, B, 4, XR>(x, M, codes, scales, biases, N, K, G, y, s); \
+    case 8: return qmvm_go<T, B, 8, XR>(x, M, codes, scales, biases, N, K, G, y, s); \
+    default: return qmvm_go<T, B, 16, XR>(x, M, codes, scales, biases, N, K, G, y, s); \
   }
+#define AQ_QMVM_B(T, B) \
+  if (M <= 4) { AQ_QMVM_W(T, B, 4) } else { AQ_QMVM_W(T, B, 8) }
 #define AQ_QMVM(T) \
-  if (M <= 4) { AQ_QMVM_W(T, 4) } else { AQ_QMVM_W(T, 8) }
+  if (bits == 4) { AQ_QMVM_B(T, 4) } else { AQ_QMVM_B(T, 8) }
   if (x_dtype == X_BF16) { AQ_QMVM(bf16_t) }
   if (x_dtype == X_F16) { AQ_QMVM(f16_t) }
 #undef AQ_QMVM
+#undef AQ_QMVM_B
 #undef AQ_QMVM_W
   return hipErrorInvalidValue;
 }
 
 bool gather_qmvm_supported(int bits, int64_t K, int G) {
-  return bits == 4 && K >= 32 && (int64_t)2 * 16 * (K / G) * 2 <= 48 * 1024;
+  return (bits == 4 || bits == 8) && K >= 32 && (int64_t)2 * 16 * (K / G) * 2 <= 48 * 1024;
 }
 
 hipError_t launch_gather_qmvm(const void *x, int x_dtype, int64_t T, const uint32_t *codes,
                               const uint16_t *scales, const uint16_t *biases, int64_t E, int64_t N,
-                              int64_t K, const int32_t *ids, int topk, int G, void *y,
-                              hipStream_t s) {
-  if (x_dtype == X_BF16) return gather_go<bf16_t>(x, T, codes, scales, biases, E, N, K, ids, topk, G, y, s);
-  if (x_dtype == X_F16) return gather_go<f16_t>(x, T, codes, scales, biases, E, N, K, ids, topk, G, y, s);
+                              int64_t K, const int32_t *ids, int topk, int G, int bits,
+                              void *y, hipStream_t s) {
+#define AQ_GATHER(XT) \
+  return bits == 4 ? gather_go<XT, 4>(x, T, codes, scales, biases, E, N, K, ids, topk, G, y, s) \
+                   : gather_go<XT, 8>(x, T, codes, scales, biases, E, N, K, ids, topk, G, y, s);
+  if (x_dtype == X_BF16) { AQ_GATHER(bf16_t) }
+  if (x_dtype == X_F16) { AQ_GATHER(f16_t) }
+#undef AQ_GATHER
   return hipErrorInvalidValue;
 }
 

@@ -163,6 +163,21 @@ def test_qmv_shapes(aq, xdt, N, K, G):
         _assert_close(y, y_ref, A, f"qmv N{N} K{K} M{M}")
 
 
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("G,K", [(32, 2144), (64, 2112), (128, 2176), (32, 96), (64, 64)])
+def test_qmv_few_rows_groups(aq, xdt, bits, G, K):
+    """2..8 rows (the matrix-core path) at every group size, K ragged against
+    the 128-code step and the per-wave K split, N ragged against 16-row tiles."""
+    N = 45
+    _, (c, s, b) = _quantized(N, K, G, bits, seed=14)
+    for M in (2, 4, 6, 8):
+        xb = inputs.activations(M, K, xdt, seed=14, key=(G, K, M, bits))
+        y_ref, A = oracle.matmul(inputs.from_bits(xb, xdt), c, s, b, K, G, bits)
+        y = aq.aq_qmv(bits_to_dev(xb, xdt), *packed_to_dev(c, s, b), G, bits)
+        _assert_close(y, y_ref, A, f"qmv b{bits} G{G} K{K} M{M} {xdt}")
+
+
 def test_qmv_unit_vectors(aq):
     """x = e_k picks column k of the dequantized matrix."""
     G, bits, N, K = 64, 4, 40, 256
@@ -260,6 +275,18 @@ def test_gather_parity(aq, bits, xdt):
     y_ref, A = oracle.gather_matmul(inputs.from_bits(xb, xdt), c, s, b, ids, K, G, bits)
     y = aq.aq_gather_qmv(bits_to_dev(xb, xdt), *packed_to_dev(c, s, b), to_dev(ids), G, bits)
     _assert_close(y, y_ref, A, f"gather b{bits} {xdt}")
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("G", [32, 64, 128])
+def test_gather_groups(aq, bits, G):
+    E, N, K, T, topk = 5, 37, 5 * G if G == 32 else 3 * G, 11, 2
+    c, s, b = _experts(E, N, K, G, bits, seed=15)
+    ids = inputs.expert_ids(T, E, topk, seed=15)
+    xb = inputs.activations(T, K, "bf16", seed=15)
+    y_ref, A = oracle.gather_matmul(inputs.from_bits(xb, "bf16"), c, s, b, ids, K, G, bits)
+    y = aq.aq_gather_qmv(bits_to_dev(xb, "bf16"), *packed_to_dev(c, s, b), to_dev(ids), G, bits)
+    _assert_close(y, y_ref, A, f"gather b{bits} G{G}")
 
 
 def test_gather_crowded_expert_and_bad_ids(aq):
