@@ -57,6 +57,12 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kStepK = 128;  // k per step: 4 chunks
+// steps of loads in flight per wave
+template <int BITS>
+constexpr int kDepth = 2;
+// a buffer offset past every resource (sizes are clamped to 2^31 - 1): the
+// load returns zeros without a memory access
+constexpr uint32_t kOutside = 0x80000000u;
 
 // per (activation type, code width): the register constant of the unpack
 // and the offset OFF that every code value carries into the products
@@ -164,11 +170,11 @@ __device__ __forceinline__ uint4 permute_x(uint4 v) {
 }
 
 // one step (4 chunks) of one wave's K range, as loaded
-template <int NXL, int BITS>
+template <int NXL, int BITS, int R>
 struct MStep {
-  // 4-bit: quarter h holds chunk c0 + h of row n16.  8-bit: words 4r .. 4r+3
-  // hold words 4 (h & 1) .. +3 of chunk c0 + 2r + (h >> 1)
-  uint32_t cw[BITS];
+  // per block of 16 rows.  4-bit: quarter h holds chunk c0 + h of row n16.
+  // 8-bit: words 4r .. 4r+3 hold words 4 (h & 1) .. +3 of chunk c0 + 2r + (h >> 1)
+  uint32_t cw[R][BITS];
   uint4 xl[4 / NXL];   // x loads of the step, NXL MFMA slots each (natural pair order)
 };
 
@@ -184,21 +190,26 @@ __device__ __forceinline__ uint4 row_ror(uint4 v) {
                     (uint32_t)__builtin_amdgcn_mov_dpp((int)v.w, ctl, 0xF, 0xF, false));
 }
 
-// One workgroup's share: 16 rows of W (rows past the matrix read as zero)
-// against up to XR rows of x, K split over its W waves.  GS: log2 of the
-// chunks per group.  XR: rows of x carried per chunk slot of an x load --
-// output rows >= XR are discarded, so A-operand rows XR.. may hold
-// anything, and one 16-byte load per lane carries NXL = 16 / XR chunks
-// (lanes XR s .. XR s + XR - 1 of a row of 16 hold chunk slot s); a row
-// rotation moves a slot to lanes 0.. .
-template <typename XT, int BITS, int W, int GS, int XR>
+// One workgroup's share: R blocks of 16 rows of W (rows past the matrix read
+// as zero) against up to XR rows of x, K split over its W waves.  Every wave
+// runs all R blocks over its K range, so each x load, its lane moves and the
+// sum-of-x MFMA serve R blocks: x comes from L2 once per 16 R rows, which
+// keeps its traffic (M / 4 of the 4-bit weight bytes per 16 rows) well below
+// the weights'.  GS: log2 of the chunks per group.  XR: rows of x carried per
+// chunk slot of an x load -- output rows >= XR are discarded, so A-operand
+// rows XR.. may hold anything, and one 16-byte load per lane carries
+// NXL = 16 / XR chunks (lanes XR s .. XR s + XR - 1 of a row of 16 hold chunk
+// slot s); a row rotation moves a slot to lanes 0.. .
+template <typename XT, int BITS, int W, int GS, int XR, int R>
 struct MBlock {
   static constexpr int CPG = 1 << GS;  // chunks per group (G = 32 CPG)
   static constexpr int NG = 4 / CPG;   // groups per step
   static constexpr int NXL = 16 / XR;
+  static constexpr int ROWS = 16 * R;
   // 8-bit with a group inside each 32-code chunk: a lane-half swap per
   // register pair keeps every MFMA inside one chunk (one group)
   static constexpr bool kSwap = BITS == 8 && GS == 0;
+  typedef MStep<NXL, BITS, R> Step;
 
   // first chunk of the codes behind MFMA slot j of the step at chunk c0 (the
   // slot is past K iff this chunk is), and quarter h's offset into its x row
@@ -213,11 +224,15 @@ struct MBlock {
   }
 
   __amdgpu_buffer_rsrc_t rw, rx;
-  const uint16_t *sbl;  // LDS: [2][16][gpr] scales, biases of the 16 rows
+  const uint16_t *sbl;  // LDS: [2][16 R][gpr] scales, biases of the rows
   int64_t K, wpr, gpr;
   int nch, n16, h, c_beg, c_end;
+  // per-lane parts of the load offsets (the step's part is a scalar offset):
+  // codes of block b; x of load t, and the chunk of its slot past c0
+  uint32_t wv[R], xb[4 / NXL];
+  int xj[4 / NXL];
 
-  __device__ void setup(const uint32_t *codes16, int64_t nrows, int64_t K_, int kw, int wave,
+  __device__ void setup(const uint32_t *codes_rows, int64_t nrows, int64_t K_, int kw, int wave,
                         int lane, const uint16_t *sbl_, __amdgpu_buffer_rsrc_t rx_) {
     K = K_;
     nch = (int)(K >> 5);
@@ -225,23 +240,39 @@ struct MBlock {
     gpr = nch >> GS;
     n16 = lane & 15;
     h = lane >> 4;
-    rw = mk_rsrc(codes16, nrows * wpr * 4);
+    rw = mk_rsrc(codes_rows, nrows * wpr * 4);
     rx = rx_;
     sbl = sbl_;
     // this wave's K range, whole steps of 4 chunks (each a whole number of groups)
     c_beg = wave * (kw >> 5);
     c_end = c_beg + (kw >> 5) < nch ? c_beg + (kw >> 5) : nch;
+    // 4-bit: quarter h reads chunk c0 + h (16 bytes each).  8-bit: load r of
+    // quarter h reads bytes 64 r + 16 h of the 128 at chunk c0
+#pragma unroll
+    for (int b = 0; b < R; ++b) wv[b] = (uint32_t)((int64_t)(16 * b + n16) * wpr * 4 + 16 * h);
+#pragma unroll
+    for (int t = 0; t < 4 / NXL; ++t) xj[t] = slot_chunk(0, t * NXL + n16 / XR);
   }
 
-  // scales and biases of the 16 rows (one contiguous, 16-byte aligned range
+  // x rows for the next run: xro is the byte offset of the x row that chunk
+  // slot row (n16 % XR) carries (past the x resource: zeros)
+  __device__ void set_x(uint32_t xro) {
+#pragma unroll
+    for (int t = 0; t < 4 / NXL; ++t) {
+      const int j = t * NXL + n16 / XR;  // MFMA slot this lane's load carries
+      xb[t] = xro + (uint32_t)slot_xoff(slot_chunk(0, j), j, h) * 2u;
+    }
+  }
+
+  // scales and biases of the rows (one contiguous, 16-byte aligned range
   // each) to LDS with 16-byte loads; a load that crosses the end of the valid
   // rows reads as zero as a whole, so whole units inside them first, then
   // 2-byte loads, zeros past them.  The caller synchronizes.
-  static __device__ void stage_sb(const uint16_t *scales16, const uint16_t *biases16,
+  static __device__ void stage_sb(const uint16_t *scales_rows, const uint16_t *biases_rows,
                                   int64_t nrows, int64_t gpr_, uint16_t *sb) {
-    const __amdgpu_buffer_rsrc_t rs = mk_rsrc(scales16, nrows * gpr_ * 2);
-    const __amdgpu_buffer_rsrc_t rb = mk_rsrc(biases16, nrows * gpr_ * 2);
-    const int valid = (int)(nrows * gpr_), total = 16 * (int)gpr_;
+    const __amdgpu_buffer_rsrc_t rs = mk_rsrc(scales_rows, nrows * gpr_ * 2);
+    const __amdgpu_buffer_rsrc_t rb = mk_rsrc(biases_rows, nrows * gpr_ * 2);
+    const int valid = (int)(nrows * gpr_), total = ROWS * (int)gpr_;
     const int full = valid >> 3;
     for (int i = threadIdx.x; i < full; i += 64 * W) {
       const u32x4v vs = __builtin_amdgcn_raw_buffer_load_b128(rs, i * 16, 0, 0);
@@ -256,177 +287,206 @@ struct MBlock {
     }
   }
 
-  __device__ void load(int c0, uint32_t xro, MStep<NXL, BITS> &st) const {
+  // The step at chunk c0.  A step past the wave's range reads outside every
+  // resource (zeros, no memory access).  In a step that ends past c_end (the
+  // end of K) the codes past it read the next row or zeros; their x is zero
+  // (its loads are checked per slot), so they add nothing.
+  __device__ void load(int c0, Step &st) const {
+    const uint32_t sw = c0 < c_end ? (uint32_t)c0 * (4 * BITS) : kOutside;
 #pragma unroll
-    for (int r = 0; r < BITS / 4; ++r) {
-      // 4-bit: chunk c0 + h.  8-bit: words 4 (h & 1) .. of chunk c0 + 2r + (h >> 1)
-      const int ch = BITS == 4 ? c0 + h : c0 + 2 * r + (h >> 1);
-      const bool inside = ch < nch;  // chunks past K read as zero
-      const int64_t wo = BITS == 4 ? (int64_t)ch * 4 : (int64_t)ch * 8 + 4 * (h & 1);
-      const uint32_t o = (uint32_t)(((int64_t)n16 * wpr + (inside ? wo : 0)) * 4);
-      const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)o, 0, 0);
+    for (int b = 0; b < R; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st.cw[4 * r + i] = inside ? v[i] : 0u;
-    }
+      for (int r = 0; r < BITS / 4; ++r) {
+        const u32x4v v = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)wv[b], (int)(sw + 64 * r), 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.cw[b][4 * r + i] = v[i];
+      }
+    const int lim = c_end - c0;
 #pragma unroll
     for (int t = 0; t < 4 / NXL; ++t) {
-      const int j = t * NXL + n16 / XR;  // MFMA slot this lane's load carries
-      const int cb = slot_chunk(c0, j);
-      const int xo = cb < nch ? slot_xoff(cb, j, h) : 0;
-      const u32x4v u = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(xro + (uint32_t)xo * 2u), 0, 0);
+      const uint32_t xo = xj[t] < lim ? xb[t] : kOutside;
+      const u32x4v u = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)xo, (int)((uint32_t)c0 * 64u), 0);
       st.xl[t] = make_uint4(u[0], u[1], u[2], u[3]);
     }
   }
 
-  __device__ void compute(int c0, MStep<NXL, BITS> &st, f32x4v &acc, uint32_t vmask,
-                          uint32_t vmagic, uint4 ones) const {
+  __device__ void compute(int c0, Step &st, f32x4v (&acc)[R], uint32_t vmask, uint32_t vmagic,
+                          uint4 ones) const {
     const float off = mm_traits<XT, BITS>::off;
-    if constexpr (BITS == 4) {
-      transpose4(st.cw);  // quarter h: word h of chunks c0 .. c0+3
-    } else if constexpr (kSwap) {
-      // quarters (0 1 | 2 3) of pair 0 and pair 1 -> pair 0 of chunk 2r, pair 1 of 2r+1
 #pragma unroll
-      for (int r = 0; r < 2; ++r)
+    for (int b = 0; b < R; ++b) {
+      if constexpr (BITS == 4) {
+        transpose4(st.cw[b]);  // quarter h: word h of chunks c0 .. c0+3
+      } else if constexpr (kSwap) {
+        // quarters (0 1 | 2 3) of pair 0 and pair 1 -> pair 0 of chunk 2r, pair 1 of 2r+1
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          auto v = __builtin_amdgcn_permlane32_swap(st.cw[4 * r + i], st.cw[4 * r + 2 + i], false, false);
-          st.cw[4 * r + i] = v[0];
-          st.cw[4 * r + 2 + i] = v[1];
-        }
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            auto v = __builtin_amdgcn_permlane32_swap(st.cw[b][4 * r + i], st.cw[b][4 * r + 2 + i],
+                                                      false, false);
+            st.cw[b][4 * r + i] = v[0];
+            st.cw[b][4 * r + 2 + i] = v[1];
+          }
+      }
     }
+    uint4 xp[4 / NXL];  // x loads in the k order of the B operand
+#pragma unroll
+    for (int t = 0; t < 4 / NXL; ++t) xp[t] = BITS == 4 ? permute_x(st.xl[t]) : st.xl[t];
 #pragma unroll
     for (int q = 0; q < NG; ++q) {
       if (c0 + q * CPG >= c_end) break;  // past K (uniform)
-      f32x4v xg = (f32x4v){0.f, 0.f, 0.f, 0.f}, pg = (f32x4v){0.f, 0.f, 0.f, 0.f};
+      f32x4v xg = (f32x4v){0.f, 0.f, 0.f, 0.f}, pg[R];
+#pragma unroll
+      for (int b = 0; b < R; ++b) pg[b] = (f32x4v){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int jj = 0; jj < CPG; ++jj) {
         const int j = q * CPG + jj;
-        uint4 xr = st.xl[j / NXL];
+        uint4 xa = xp[j / NXL];
         if constexpr (NXL == 2) {
-          if (j % 2 == 1) xr = row_ror<8>(xr);
+          if (j % 2 == 1) xa = row_ror<8>(xa);
         } else if constexpr (NXL == 4) {
-          if (j % 4 == 1) xr = row_ror<12>(xr);
-          if (j % 4 == 2) xr = row_ror<8>(xr);
-          if (j % 4 == 3) xr = row_ror<4>(xr);
+          if (j % 4 == 1) xa = row_ror<12>(xa);
+          if (j % 4 == 2) xa = row_ror<8>(xa);
+          if (j % 4 == 3) xa = row_ror<4>(xa);
         }
-        uint4 xa, wb;
-        if constexpr (BITS == 4) {
-          xa = permute_x(xr);
-          wb = unpack_word(st.cw[j], vmask, vmagic);
-        } else {
-          xa = xr;
-          wb = unpack_bytes<XT>(st.cw[2 * j], st.cw[2 * j + 1], vmagic);
-        }
-        if (slot_chunk(c0, j) >= nch) xa = make_uint4(0, 0, 0, 0);
         xg = mfma16<XT>(xa, ones, xg);
-        pg = mfma16<XT>(xa, wb, pg);
-      }
-      const int li = n16 * (int)gpr + (c0 >> GS) + q;
-      const float sc = f16_to_f32(sbl[li]), bi = f16_to_f32(sbl[16 * (int)gpr + li]);
-      const float bo = __builtin_fmaf(-off, sc, bi);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(bo, xg[e], __builtin_fmaf(sc, pg[e], acc[e]));
+        for (int b = 0; b < R; ++b) {
+          const uint4 wb = BITS == 4 ? unpack_word(st.cw[b][j], vmask, vmagic)
+                                     : unpack_bytes<XT>(st.cw[b][2 * j], st.cw[b][2 * j + 1], vmagic);
+          pg[b] = mfma16<XT>(xa, wb, pg[b]);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < R; ++b) {
+        const int li = (16 * b + n16) * (int)gpr + (c0 >> GS) + q;
+        const float sc = f16_to_f32(sbl[li]), bi = f16_to_f32(sbl[ROWS * (int)gpr + li]);
+        const float bo = __builtin_fmaf(-off, sc, bi);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[b][e] = __builtin_fmaf(bo, xg[e], __builtin_fmaf(sc, pg[b][e], acc[b][e]));
+      }
     }
   }
 
-  // partial sums of this wave's K range; lane (n16, h) gets output rows
-  // m = 4 h + e of x against W row n16.  xro: byte offset of the x row that
-  // chunk slot row (n16 % XR) carries (past the x resource: zeros).
-  __device__ f32x4v run(uint32_t xro) const {
+  // D steps of loads in flight per wave: the first D are issued by
+  // prologue() (before the caller waits for the staged scales, so the two
+  // memory round trips overlap), and each computed step is refilled with the
+  // step D ahead.  Every load is issued unconditionally, since a load on only
+  // some paths would make the in-order load counter wait for all in flight;
+  // past the wave's range the offset lies outside the resource, so the load
+  // returns zeros and touches no memory.
+  template <int D>
+  __device__ void prologue(uint32_t xro, Step (&st)[D]) {
+    set_x(xro);
+#pragma unroll
+    for (int d = 0; d < D; ++d) load(c_beg + 4 * d, st[d]);
+  }
+
+  // partial sums of this wave's K range; lane (n16, h) gets in acc[b] output
+  // rows m = 4 h + e of x against W row 16 b + n16
+  template <int D>
+  __device__ void finish(Step (&st)[D], f32x4v (&acc)[R]) const {
     const uint32_t vmask = opaque(0x000F000Fu), vmagic = opaque(mm_traits<XT, BITS>::magic);
     const uint32_t vones = opaque(mm_traits<XT, BITS>::ones);
     const uint4 ones = make_uint4(vones, vones, vones, vones);
-    f32x4v acc = (f32x4v){0.f, 0.f, 0.f, 0.f};
-    if (c_beg >= c_end) return acc;
-    // double-buffered: the next step's loads are in flight while this one
-    // computes.  The prefetch is unconditional (past the range it re-reads
-    // memory inside the matrix, or zeros past K): a load issued on only some
-    // paths would make the in-order load counter wait for everything in flight.
-    MStep<NXL, BITS> sa, sb;
-    load(c_beg, xro, sa);
-    int c0 = c_beg;
-    for (; c0 + 8 <= c_end; c0 += 8) {
-      load(c0 + 4, xro, sb);
-      compute(c0, sa, acc, vmask, vmagic, ones);
-      load(c0 + 8, xro, sa);
-      compute(c0 + 4, sb, acc, vmask, vmagic, ones);
+#pragma unroll
+    for (int b = 0; b < R; ++b) acc[b] = (f32x4v){0.f, 0.f, 0.f, 0.f};
+    for (int c0 = c_beg; c0 < c_end; c0 += 4 * D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        if (c0 + 4 * d < c_end) compute(c0 + 4 * d, st[d], acc, vmask, vmagic, ones);
+        load(c0 + 4 * (d + D), st[d]);
+      }
     }
-    if (c0 < c_end) {
-      load(c0 + 4, xro, sb);
-      compute(c0, sa, acc, vmask, vmagic, ones);
-      if (c0 + 4 < c_end) compute(c0 + 4, sb, acc, vmask, vmagic, ones);
-    }
-    return acc;
   }
 };
 
+// LDS of a workgroup: the staged scales and biases, and afterwards (behind a
+// barrier) the waves' partial sums in the same space
+inline size_t qmvm_lds_bytes(int W, int R, int64_t K, int G) {
+  const size_t sb = (size_t)2 * 16 * R * (K / G) * 2, part = (size_t)W * 16 * R * 8 * 4;
+  return sb > part ? sb : part;
+}
+
 // sum the W waves' partial sums (lanes h < 2 hold output rows 0..7) through
-// LDS; out(n, m, v) receives row n of the 16, x row m < 8, value v
-template <int W, typename F>
-__device__ __forceinline__ void reduce_out(float (&part)[W][16][8], int wave, int lane,
-                                           const f32x4v &acc, F out) {
+// LDS (part: [W][16 R][8] floats, free for this use); out(n, m, v) receives
+// row n of the 16 R, x row m < 8, value v
+template <int W, int R, typename F>
+__device__ __forceinline__ void reduce_out(float *part, int wave, int lane,
+                                           const f32x4v (&acc)[R], F out) {
   const int n16 = lane & 15, h = lane >> 4;
   if (h < 2) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) part[wave][n16][4 * h + e] = acc[e];
+    for (int b = 0; b < R; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) part[(wave * 16 * R + 16 * b + n16) * 8 + 4 * h + e] = acc[b][e];
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < 16 * 8; i += 64 * W) {
+  for (int i = threadIdx.x; i < 16 * R * 8; i += 64 * W) {
     float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < W; ++w) v += part[w][i >> 3][i & 7];
+    for (int w = 0; w < W; ++w) v += part[w * 16 * R * 8 + i];
     out(i >> 3, i & 7, v);
   }
 }
 
-template <typename XT, int BITS, int W, int GS, int XR>
+template <typename XT, int BITS, int W, int GS, int XR, int R>
 __global__ __launch_bounds__(64 * W) void qmvm_kernel(const uint16_t *__restrict__ x, int M,
                                                       const uint32_t *__restrict__ codes,
                                                       const uint16_t *__restrict__ scales,
                                                       const uint16_t *__restrict__ biases,
                                                       int64_t N, int64_t K, int kw,
                                                       uint16_t *__restrict__ y) {
-  __shared__ float part[W][16][8];
-  extern __shared__ __attribute__((aligned(16))) uint16_t sbl[];  // [2][16][gpr]
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // [2][16 R][gpr]; then partials
+  typedef MBlock<XT, BITS, W, GS, XR, R> Blk;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t row0 = (int64_t)blockIdx.x * 16;
-  const int64_t nrows = N - row0 < 16 ? N - row0 : 16;
+  const int64_t row0 = (int64_t)blockIdx.x * Blk::ROWS;
+  const int64_t nrows = N - row0 < Blk::ROWS ? N - row0 : Blk::ROWS;
   const int64_t gpr = (K >> 5) >> GS;
-  MBlock<XT, BITS, W, GS, XR> blk;
-  blk.setup(codes + row0 * (K >> 5) * BITS, nrows, K, kw, wave, lane, sbl,
+  Blk blk;
+  blk.setup(codes + row0 * (K >> 5) * BITS, nrows, K, kw, wave, lane, lds,
             mk_rsrc(x, (int64_t)M * K * 2));  // rows of x past M read as zero
-  MBlock<XT, BITS, W, GS, XR>::stage_sb(scales + row0 * gpr, biases + row0 * gpr, nrows, gpr, sbl);
+  const uint32_t xro = (uint32_t)((int64_t)((lane & 15) % XR) * K * 2);
+  constexpr int D = kDepth<BITS>;
+  typename Blk::Step st[D];
+  blk.template prologue<D>(xro, st);
+  Blk::stage_sb(scales + row0 * gpr, biases + row0 * gpr, nrows, gpr, lds);
   __syncthreads();
-  const f32x4v acc = blk.run((uint32_t)((int64_t)((lane & 15) % XR) * K * 2));
-  reduce_out<W>(part, wave, lane, acc, [&](int nn, int m, float v) {
+  f32x4v acc[R];
+  blk.template finish<D>(st, acc);
+  __syncthreads();  // every wave is done with the staged scales
+  reduce_out<W, R>(reinterpret_cast<float *>(lds), wave, lane, acc, [&](int nn, int m, float v) {
     if (m < M && row0 + nn < N) y[(int64_t)m * N + row0 + nn] = xtraits<XT>::from_f32(v);
   });
 }
 
 // Mixture-of-experts gather ("Quantization", metalworking, gather variants
 // for MoE experts): y[t, j, :] = x[t] @ W_{ids[t, j]}^T.  One workgroup per
-// (16 rows, expert e) collects the (token, slot) pairs routed to e and runs
+// (16 R rows, expert e) collects the (token, slot) pairs routed to e and runs
 // them in batches of up to 8 x rows through the matrix cores, so each
 // expert's rows are read once per batch of tokens that chose it (experts no
 // token chose are never read).  Pairs whose id is outside [0, E) get zero
 // rows, written by the workgroups of expert 0.
 constexpr int kGTile = 256;  // ids scanned per round
 
-template <typename XT, int BITS, int W, int GS>
+template <typename XT, int BITS, int W, int GS, int R>
 __global__ __launch_bounds__(64 * W) void gather_qmvm_kernel(
     const uint16_t *__restrict__ x, int64_t T, const uint32_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ biases, int64_t E, int64_t N,
     int64_t K, const int32_t *__restrict__ ids, int topk, int kw, uint16_t *__restrict__ y) {
-  __shared__ float part[W][16][8];
   __shared__ int list[kGTile];
   __shared__ int count;
-  extern __shared__ __attribute__((aligned(16))) uint16_t sbl[];  // [2][16][gpr]
+  __shared__ __attribute__((aligned(16))) float part[W * 16 * R * 8];
+  extern __shared__ __attribute__((aligned(16))) uint16_t sbl[];  // [2][16 R][gpr]
+  typedef MBlock<XT, BITS, W, GS, 8, R> Blk;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int e = blockIdx.y;
-  const int64_t row0 = (int64_t)blockIdx.x * 16;
-  const int64_t nrows = N - row0 < 16 ? N - row0 : 16;
+  const int64_t row0 = (int64_t)blockIdx.x * Blk::ROWS;
+  const int64_t nrows = N - row0 < Blk::ROWS ? N - row0 : Blk::ROWS;
   const int64_t gpr = (K >> 5) >> GS, wpe = N * (K >> 5) * BITS;
   const int64_t total = T * topk;
 
@@ -445,11 +505,11 @@ __global__ __launch_bounds__(64 * W) void gather_qmvm_kernel(
   __syncthreads();
   if (count == 0) return;
 
-  MBlock<XT, BITS, W, GS, 8> blk;
+  Blk blk;
   blk.setup(codes + e * wpe + row0 * (K >> 5) * BITS, nrows, K, kw, wave, lane, sbl,
             mk_rsrc(x, T * K * 2));
-  MBlock<XT, BITS, W, GS, 8>::stage_sb(scales + (e * N + row0) * gpr, biases + (e * N + row0) * gpr,
-                                 nrows, gpr, sbl);
+  Blk::stage_sb(scales + (e * N + row0) * gpr, biases + (e * N + row0) * gpr, nrows, gpr, sbl);
+  constexpr int D = kDepth<BITS>;
   for (int64_t t0 = 0; t0 < total; t0 += kGTile) {
     __syncthreads();  // also publishes the staged scales before the first batch
     if (threadIdx.x == 0) count = 0;
@@ -466,8 +526,11 @@ __global__ __launch_bounds__(64 * W) void gather_qmvm_kernel(
       const int m = lane & 7;
       const uint32_t xro = b0 + m < n ? (uint32_t)(((t0 + list[b0 + m]) / topk) * K * 2)
                                       : (uint32_t)(T * K * 2);
-      const f32x4v acc = blk.run(xro);
-      reduce_out<W>(part, wave, lane, acc, [&](int nn, int mm, float v) {
+      typename Blk::Step st[D];
+      blk.template prologue<D>(xro, st);
+      f32x4v acc[R];
+      blk.template finish<D>(st, acc);
+      reduce_out<W, R>(part, wave, lane, acc, [&](int nn, int mm, float v) {
         if (b0 + mm < n && row0 + nn < N)
           y[(t0 + list[b0 + mm]) * N + row0 + nn] = xtraits<XT>::from_f32(v);
       });
@@ -476,95 +539,118 @@ __global__ __launch_bounds__(64 * W) void gather_qmvm_kernel(
   }
 }
 
-template <typename XT, int BITS, int W, int XR>
+template <typename XT, int BITS, int W, int XR, int R>
 hipError_t qmvm_go(const void *x, int M, const uint32_t *codes, const uint16_t *scales,
                    const uint16_t *biases, int64_t N, int64_t K, int G, void *y, hipStream_t s) {
   const int64_t steps = (K + kStepK - 1) / kStepK;
   const int kw = (int)((steps + W - 1) / W) * kStepK;  // k per wave, whole steps
-  const int64_t blocks = (N + 15) / 16;
+  const int64_t blocks = (N + 16 * R - 1) / (16 * R);
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks), block(64 * W);
-  const size_t lds = (size_t)2 * 16 * (K / G) * 2;  // scales + biases of the rows
+  const size_t lds = qmvm_lds_bytes(W, R, K, G);
   switch (G) {
-    case 32: hipLaunchKernelGGL((qmvm_kernel<XT, BITS, W, 0, XR>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y); break;
-    case 64: hipLaunchKernelGGL((qmvm_kernel<XT, BITS, W, 1, XR>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y); break;
-    case 128: hipLaunchKernelGGL((qmvm_kernel<XT, BITS, W, 2, XR>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y); break;
+    case 32: hipLaunchKernelGGL((qmvm_kernel<XT, BITS, W, 0, XR, R>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y); break;
+    case 64: hipLaunchKernelGGL((qmvm_kernel<XT, BITS, W, 1, XR, R>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y); break;
+    case 128: hipLaunchKernelGGL((qmvm_kernel<XT, BITS, W, 2, XR, R>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <typename XT, int BITS>
+template <typename XT, int BITS, int R>
 hipError_t gather_go(const void *x, int64_t T, const uint32_t *codes, const uint16_t *scales,
                      const uint16_t *biases, int64_t E, int64_t N, int64_t K,
                      const int32_t *ids, int topk, int G, void *y, hipStream_t s) {
-  constexpr int W = 2;  // the grid has (rows / 16) x E workgroups: split K in two
+  constexpr int W = 2;  // the grid has (rows / 16 R) x E workgroups: split K in two
   const int64_t steps = (K + kStepK - 1) / kStepK;
   const int kw = (int)((steps + W - 1) / W) * kStepK;
-  const int64_t blocks = (N + 15) / 16;
+  const int64_t blocks = (N + 16 * R - 1) / (16 * R);
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks, (unsigned)E), block(64 * W);
-  const size_t lds = (size_t)2 * 16 * (K / G) * 2;
+  const size_t lds = (size_t)2 * 16 * R * (K / G) * 2;
   switch (G) {
-    case 32: hipLaunchKernelGGL((gather_qmvm_kernel<XT, BITS, W, 0>), grid, block, lds, s, (const uint16_t *)x, T, codes, scales, biases, E, N, K, ids, topk, kw, (uint16_t *)y); break;
-    case 64: hipLaunchKernelGGL((gather_qmvm_kernel<XT, BITS, W, 1>), grid, block, lds, s, (const uint16_t *)x, T, codes, scales, biases, E, N, K, ids, topk, kw, (uint16_t *)y); break;
-    case 128: hipLaunchKernelGGL((gather_qmvm_kernel<XT, BITS, W, 2>), grid, block, lds, s, (const uint16_t *)x, T, codes, scales, biases, E, N, K, ids, topk, kw, (uint16_t *)y); break;
+    case 32: hipLaunchKernelGGL((gather_qmvm_kernel<XT, BITS, W, 0, R>), grid, block, lds, s, (const uint16_t *)x, T, codes, scales, biases, E, N, K, ids, topk, kw, (uint16_t *)y); break;
+    case 64: hipLaunchKernelGGL((gather_qmvm_kernel<XT, BITS, W, 1, R>), grid, block, lds, s, (const uint16_t *)x, T, codes, scales, biases, E, N, K, ids, topk, kw, (uint16_t *)y); break;
+    case 128: hipLaunchKernelGGL((gather_qmvm_kernel<XT, BITS, W, 2, R>), grid, block, lds, s, (const uint16_t *)x, T, codes, scales, biases, E, N, K, ids, topk, kw, (uint16_t *)y); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
+
+// dynamic LDS of one workgroup at most (scales and biases of its rows)
+constexpr size_t kMaxStagedLds = 64 * 1024;
 
 }  // namespace
 
 bool qmvm_supported(int M, int bits, int64_t N, int64_t K, int G) {
-  // scales and biases of 16 rows staged in LDS: at most 48 KB
-  return M >= 2 && M <= 8 && (bits == 4 || bits == 8) && N >= 1 && K >= 32 && 16 * K * 2 <= 0x7FFFFFFF &&
-         (int64_t)2 * 16 * (K / G) * 2 <= 48 * 1024;
+  return M >= 2 && M <= 8 && (bits == 4 || bits == 8) && N >= 1 && K >= 32 &&
+         16 * K * 2 <= 0x7FFFFFFF && qmvm_lds_bytes(16, 1, K, G) <= kMaxStagedLds;
 }
 
 hipError_t launch_qmvm(const void *x, int x_dtype, int M, const uint32_t *codes,
                        const uint16_t *scales, const uint16_t *biases, int64_t N, int64_t K, int G,
                        int bits, void *y, hipStream_t s) {
-  // 16 rows per workgroup (<= 128 VGPRs, so 4 waves per SIMD), and K split
-  // over W waves so that the grid has about four waves per SIMD: each wave
-  // keeps two steps of loads in flight, and the chip needs tens of KB in
-  // flight per CU to stream from HBM
-  const int64_t rowblocks = (N + 15) / 16;
+  // Tall matrices: 2 blocks of 16 rows per workgroup (half the x loads per
+  // weight byte) with K split over 8 waves.  Otherwise one block, K split
+  // over W waves so that the grid has about four waves per SIMD (each wave
+  // then runs a few steps).  Measured on the MI355X at N x K = 14336 x 4096
+  // and 4096 x 14336, M = 2..8: more blocks per workgroup leave too few
+  // waves, deeper load pipelines gain nothing.
   const int64_t target = 4 * 4 * (int64_t)device_cus();
-  const int W = rowblocks * 2 >= target ? 2 : rowblocks * 4 >= target ? 4 : rowblocks * 8 >= target ? 8 : 16;
-#define AQ_QMVM_W(T, B, XR) \
+  const int R = N >= 8192 && qmvm_lds_bytes(8, 2, K, G) <= kMaxStagedLds ? 2 : 1;
+  const int64_t rowblocks = (N + 16 * R - 1) / (16 * R);
+  const int W = R == 2 ? 8
+                       : rowblocks * 2 >= target ? 2
+                       : rowblocks * 4 >= target ? 4
+                       : rowblocks * 8 >= target ? 8 : 16;
+#define AQ_QMVM_W(T, B, XR, RR) \
   switch (W) { \
-    case 2: return qmvm_go<T, B, 2, XR>(x, M, codes, scales, biases, N, K, G, y, s); \
-    case 4: return qmvm_go<T, B, 4, XR>(x, M, codes, scales, biases, N, K, G, y, s); \
-    case 8: return qmvm_go<T, B, 8, XR>(x, M, codes, scales, biases, N, K, G, y, s); \
-    default: return qmvm_go<T, B, 16, XR>(x, M, codes, scales, biases, N, K, G, y, s); \
+    case 2: return qmvm_go<T, B, 2, XR, RR>(x, M, codes, scales, biases, N, K, G, y, s); \
+    case 4: return qmvm_go<T, B, 4, XR, RR>(x, M, codes, scales, biases, N, K, G, y, s); \
+    case 8: return qmvm_go<T, B, 8, XR, RR>(x, M, codes, scales, biases, N, K, G, y, s); \
+    default: return qmvm_go<T, B, 16, XR, RR>(x, M, codes, scales, biases, N, K, G, y, s); \
   }
-#define AQ_QMVM_B(T, B) \
-  if (M <= 4) { AQ_QMVM_W(T, B, 4) } else { AQ_QMVM_W(T, B, 8) }
+#define AQ_QMVM_R(T, B, XR) \
+  if (R == 2) { return qmvm_go<T, B, 8, XR, 2>(x, M, codes, scales, biases, N, K, G, y, s); } \
+  else { AQ_QMVM_W(T, B, XR, 1) }
 #define AQ_QMVM(T) \
-  if (bits == 4) { AQ_QMVM_B(T, 4) } else { AQ_QMVM_B(T, 8) }
+  if (bits == 4) { \
+    if (M <= 4) { AQ_QMVM_R(T, 4, 4) } else { AQ_QMVM_R(T, 4, 8) } \
+  } else { \
+    if (M <= 4) { AQ_QMVM_R(T, 8, 4) } else { AQ_QMVM_R(T, 8, 8) } \
+  }
   if (x_dtype == X_BF16) { AQ_QMVM(bf16_t) }
   if (x_dtype == X_F16) { AQ_QMVM(f16_t) }
 #undef AQ_QMVM
-#undef AQ_QMVM_B
+#undef AQ_QMVM_R
 #undef AQ_QMVM_W
   return hipErrorInvalidValue;
 }
 
+// staged scales and biases of a gather workgroup of R blocks
+inline size_t gather_lds_bytes(int R, int64_t K, int G) { return (size_t)2 * 16 * R * (K / G) * 2; }
+
 bool gather_qmvm_supported(int bits, int64_t K, int G) {
-  return (bits == 4 || bits == 8) && K >= 32 && (int64_t)2 * 16 * (K / G) * 2 <= 48 * 1024;
+  return (bits == 4 || bits == 8) && K >= 32 && gather_lds_bytes(1, K, G) <= kMaxStagedLds;
 }
 
 hipError_t launch_gather_qmvm(const void *x, int x_dtype, int64_t T, const uint32_t *codes,
                               const uint16_t *scales, const uint16_t *biases, int64_t E, int64_t N,
                               int64_t K, const int32_t *ids, int topk, int G, int bits,
                               void *y, hipStream_t s) {
+  // 4 blocks of 16 rows per workgroup (the x rows of a batch are loaded once
+  // per 64 rows; the grid is (rows / 64) x experts), fewer if the staged
+  // scales would not fit
+#define AQ_GATHER_B(XT, B) \
+  if (gather_lds_bytes(4, K, G) <= kMaxStagedLds) return gather_go<XT, B, 4>(x, T, codes, scales, biases, E, N, K, ids, topk, G, y, s); \
+  if (gather_lds_bytes(2, K, G) <= kMaxStagedLds) return gather_go<XT, B, 2>(x, T, codes, scales, biases, E, N, K, ids, topk, G, y, s); \
+  return gather_go<XT, B, 1>(x, T, codes, scales, biases, E, N, K, ids, topk, G, y, s);
 #define AQ_GATHER(XT) \
-  return bits == 4 ? gather_go<XT, 4>(x, T, codes, scales, biases, E, N, K, ids, topk, G, y, s) \
-                   : gather_go<XT, 8>(x, T, codes, scales, biases, E, N, K, ids, topk, G, y, s);
+  if (bits == 4) { AQ_GATHER_B(XT, 4) } else { AQ_GATHER_B(XT, 8) }
   if (x_dtype == X_BF16) { AQ_GATHER(bf16_t) }
   if (x_dtype == X_F16) { AQ_GATHER(f16_t) }
 #undef AQ_GATHER
+#undef AQ_GATHER_B
   return hipErrorInvalidValue;
 }
 

@@ -178,6 +178,18 @@ def test_qmv_few_rows_groups(aq, xdt, bits, G, K):
         _assert_close(y, y_ref, A, f"qmv b{bits} G{G} K{K} M{M} {xdt}")
 
 
+@pytest.mark.parametrize("bits,G", [(4, 64), (8, 128), (8, 32)])
+def test_qmv_few_rows_tall(aq, bits, G):
+    """Tall matrices (two 16-row blocks per workgroup), rows ragged against 32."""
+    N, K = 8200, 256
+    _, (c, s, b) = _quantized(N, K, G, bits, seed=16)
+    for M in (3, 8):
+        xb = inputs.activations(M, K, "bf16", seed=16, key=(bits, G, M))
+        y_ref, A = oracle.matmul(inputs.from_bits(xb, "bf16"), c, s, b, K, G, bits)
+        y = aq.aq_qmv(bits_to_dev(xb, "bf16"), *packed_to_dev(c, s, b), G, bits)
+        _assert_close(y, y_ref, A, f"qmv tall b{bits} G{G} M{M}")
+
+
 def test_qmv_unit_vectors(aq):
     """x = e_k picks column k of the dequantized matrix."""
     G, bits, N, K = 64, 4, 40, 256
@@ -287,6 +299,18 @@ def test_gather_groups(aq, bits, G):
     y_ref, A = oracle.gather_matmul(inputs.from_bits(xb, "bf16"), c, s, b, ids, K, G, bits)
     y = aq.aq_gather_qmv(bits_to_dev(xb, "bf16"), *packed_to_dev(c, s, b), to_dev(ids), G, bits)
     _assert_close(y, y_ref, A, f"gather b{bits} G{G}")
+
+
+@pytest.mark.parametrize("K", [9600, 19200])
+def test_gather_long_rows(aq, K):
+    """Rows long enough that fewer 16-row blocks per workgroup fit the staged scales."""
+    G, bits, E, N, T, topk = 32, 4, 3, 40, 5, 2
+    c, s, b = _experts(E, N, K, G, bits, seed=17)
+    ids = inputs.expert_ids(T, E, topk, seed=17)
+    xb = inputs.activations(T, K, "f16", seed=17)
+    y_ref, A = oracle.gather_matmul(inputs.from_bits(xb, "f16"), c, s, b, ids, K, G, bits)
+    y = aq.aq_gather_qmv(bits_to_dev(xb, "f16"), *packed_to_dev(c, s, b), to_dev(ids), G, bits)
+    _assert_close(y, y_ref, A, f"gather K{K}")
 
 
 def test_gather_crowded_expert_and_bad_ids(aq):
