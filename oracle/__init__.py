@@ -64,6 +64,7 @@ def _load():
             "oracle_pack": ([vp, i64, i64, i32, vp], i32),
             "oracle_unpack": ([vp, i64, i64, i32, vp], i32),
             "oracle_quantize": ([vp, i64, i64, i32, i32, vp, vp, vp], i32),
+            "oracle_quantize_mse": ([vp, i64, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp], i32),
             "oracle_dequantize_exact": ([vp, vp, vp, i64, i64, i32, i32, vp], i32),
             "oracle_dequantize": ([vp, vp, vp, i64, i64, i32, i32, i32, vp], i32),
             "oracle_embedding": ([vp, vp, vp, i64, i64, i32, i32, vp, i64, i32, vp], i32),
@@ -149,6 +150,32 @@ def quantize(w: np.ndarray, group_size: int, bits: int):
     st = _load().oracle_quantize(_p(w), N, K, group_size, bits, _p(codes), _p(scales), _p(biases))
     if st:
         raise OracleError(st, "quantize")
+    return codes, scales, biases
+
+
+def quantize_mse(w: np.ndarray, group_size: int, bits: int, steps: int, only: int = -1,
+                 details: bool = False):
+    """Range-search quantizer (reading R14): candidates p_i = (100 - i)/100,
+    i < steps, shrink [min, max] to [p min, p max]; least binary64 squared error
+    wins.  only >= 0 evaluates that candidate alone.
+    -> (codes, scales, biases), plus (chosen int32 [N, K/G], errs float64
+    [N, K/G, steps]) when details."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    if K % group_size:
+        raise OracleError(ERR_ARG, "quantize_mse")
+    ng = K // group_size
+    codes = np.zeros((N, K * bits // 32), dtype=np.uint32)
+    scales = np.zeros((N, ng), dtype=np.uint16)
+    biases = np.zeros((N, ng), dtype=np.uint16)
+    chosen = np.zeros((N, ng), dtype=np.int32)
+    errs = np.full((N, ng, steps), np.nan, dtype=np.float64)
+    st = _load().oracle_quantize_mse(_p(w), N, K, group_size, bits, steps, only, _p(codes),
+                                     _p(scales), _p(biases), _p(chosen), _p(errs))
+    if st:
+        raise OracleError(st, "quantize_mse")
+    if details:
+        return codes, scales, biases, chosen, errs
     return codes, scales, biases
 
 

@@ -53,6 +53,16 @@
  *      (token, slot), no routing-weight combine.
  *  R13 embedding ([T10] s.6): out[t,:] is row ids[t] dequantized as in R4;
  *      an id outside the table gives a zero row.
+ *  R14 range search ([GPTQ] "How it works", the --mse grid search: a
+ *      group's min-max range is narrowed where clipping its extremes costs
+ *      less than the coarser step costs the other members).  The pages give
+ *      no grid and no error measure; taken here: candidates i = 0..steps-1
+ *      with p_i = (100 - i) / 100 (binary64 division), range
+ *      [p_i * min, p_i * max] (binary64 products), bias and scale from that
+ *      range by R1, codes by R2 against them (members outside the range
+ *      clip to 0 or 2^b-1), error = sum over the group, in member order,
+ *      of (w - (q*s + b))^2 in binary64.  The least error wins; an equal
+ *      error keeps the earlier (wider) candidate.  steps = 1 is R1/R2.
  *
  * Exactness of the binary64 comparisons used below.  Every finite fp16
  * value is an integer multiple of 2^-24 of magnitude < 2^16; q*s with
@@ -326,6 +336,73 @@ int oracle_quantize(const float *w, int64_t N, int64_t K, int G, int bits,
       double s = oracle_half_to_double(s16);
       scales[n * ng + g] = s16;
       biases[n * ng + g] = b16;
+      for (int i = 0; i < G; ++i)
+        put_code(row, g * G + i, bits, group_code((double)grp[i], b, s, L));
+    }
+  }
+  return err;
+}
+
+/* Range search (R14).  Same outputs as oracle_quantize, plus, when not
+ * NULL: chosen [N, K/G] (index of the winning candidate) and errs
+ * [N, K/G, steps] (every candidate's error).  only >= 0 evaluates that one
+ * candidate alone (for checking a result that picked it).  The range
+ * check of oracle_quantize applies to the full range (candidate 0); the
+ * narrower candidates then stay in range. */
+int oracle_quantize_mse(const float *w, int64_t N, int64_t K, int G, int bits, int steps, int only,
+                        uint32_t *codes, uint16_t *scales, uint16_t *biases, int32_t *chosen,
+                        double *errs) {
+  int st = check_shape(N, K, G, bits);
+  if (st) return st;
+  if (steps < 1 || steps > 50 || only >= steps) return OR_ERR_ARG;
+  const int L = (1 << bits) - 1;
+  const int64_t wpr = K * bits / 32, ng = K / G;
+  int err = OR_OK;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    uint32_t *row = codes + n * wpr;
+    memset(row, 0, (size_t)wpr * sizeof(uint32_t));
+    for (int64_t g = 0; g < ng; ++g) {
+      const float *grp = w + n * K + g * G;
+      double lo = INFINITY, hi = -INFINITY;
+      int bad = 0;
+      for (int i = 0; i < G; ++i) {
+        double v = (double)grp[i];
+        if (!isfinite(v)) bad = 1;
+        if (v < lo) lo = v;
+        if (v > hi) hi = v;
+      }
+      uint16_t b0 = 0, s0 = 0;
+      if (!bad && half_round_down(lo, &b0) != OR_OK) bad = 1;
+      if (!bad && group_scale(oracle_half_to_double(b0), hi, L, &s0) != OR_OK) bad = 1;
+      if (bad) {
+#pragma omp critical
+        err = OR_ERR_RANGE;
+        continue;
+      }
+      double best = INFINITY;
+      int best_i = -1;
+      uint16_t best_b = 0, best_s = 0;
+      for (int i = (only >= 0 ? only : 0); i < (only >= 0 ? only + 1 : steps); ++i) {
+        const double p = (double)(100 - i) / 100.0;
+        uint16_t b16 = 0, s16 = 0;
+        half_round_down(p * lo, &b16);
+        const double b = oracle_half_to_double(b16);
+        group_scale(b, p * hi, L, &s16);
+        const double s = oracle_half_to_double(s16);
+        double e = 0.0;
+        for (int k = 0; k < G; ++k) {
+          const double v = (double)grp[k];
+          const double d = v - (b + group_code(v, b, s, L) * s);
+          e += d * d;
+        }
+        if (errs) errs[(n * ng + g) * steps + i] = e;
+        if (e < best) { best = e; best_i = i; best_b = b16; best_s = s16; }
+      }
+      const double b = oracle_half_to_double(best_b), s = oracle_half_to_double(best_s);
+      scales[n * ng + g] = best_s;
+      biases[n * ng + g] = best_b;
+      if (chosen) chosen[n * ng + g] = best_i;
       for (int i = 0; i < G; ++i)
         put_code(row, g * G + i, bits, group_code((double)grp[i], b, s, L));
     }
