@@ -33,8 +33,9 @@ the same bytes (same cold rotation and timing), a measured second denominator.
                 [4096, 14336] at 4/64 and 8/128) and the MoE gather kernel
                 (32 tokens, top-6 of 64 experts), % of HBM per launch on cold
                 weights;
-  quantize_dequantize  aq_quantize of the prefill-size matrix (fp32 in) and
-                aq_dequantize of it to bf16, % of HBM;
+  quantize_dequantize  aq_quantize of the prefill-size matrix (fp32 in),
+                aq_dequantize of it to bf16 (% of HBM), and the range-search
+                aq_quantize_mse over 21 narrowed ranges;
   embedding     quantized embedding lookups (rows of a [128256, 4096] 8-bit
                 table dequantized to bf16) for 1 and 2048 tokens.
 
@@ -511,8 +512,17 @@ def _quant_dequant(aq, inputs, dev, stream):
     res["dequantize_bf16"] = {"avg_us": round(us, 2), "bytes": nb,
                               "gbs": round(nb / (us * 1e-6) / 1e9, 1),
                               "pct_hbm": round(100 * nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
+    # range search over 21 narrowed ranges (p = 1.00 .. 0.80), same matrix
+    steps = 21
+    us = _graph_us(torch, stream,
+                   [lambda: aq.aq_quantize_mse(w, g, bits, steps, codes=c, scales=s_, biases=b)] * 2)
+    nb = 4 * N * K + packed
+    res["quantize_mse"] = {"steps": steps, "avg_us": round(us, 2), "bytes": nb,
+                           "gbs": round(nb / (us * 1e-6) / 1e9, 1),
+                           "weights_per_s": round(N * K / (us * 1e-6), 1)}
     print(f"# quantize {res['quantize']['avg_us']:.1f} us ({res['quantize']['gbs']} GB/s), "
-          f"dequantize {res['dequantize_bf16']['avg_us']:.1f} us ({res['dequantize_bf16']['gbs']} GB/s)",
+          f"dequantize {res['dequantize_bf16']['avg_us']:.1f} us ({res['dequantize_bf16']['gbs']} GB/s), "
+          f"range-search quantize ({steps} ranges) {res['quantize_mse']['avg_us']:.1f} us",
           file=sys.stderr, flush=True)
     del w, c, s_, b, out
     torch.cuda.synchronize()

@@ -18,7 +18,7 @@ import os
 
 __all__ = [
     "AQError", "lib_path", "load_library", "aq_status_string", "aq_version", "aq_codes_words",
-    "aq_qweight_bytes", "aq_quantize", "aq_dequantize", "aq_qmv", "aq_qmm",
+    "aq_qweight_bytes", "aq_quantize", "aq_quantize_mse", "aq_dequantize", "aq_qmv", "aq_qmm",
     "aq_quantized_matmul", "aq_gather_qmv",
 ]
 
@@ -59,6 +59,7 @@ def load_library():
         "aq_codes_words": ([i64, i32], i64),
         "aq_qweight_bytes": ([i64, i64, i32, i32], i64),
         "aq_quantize": ([vp, i32, i64, i64, i32, i32, vp, vp, vp, vp], i32),
+        "aq_quantize_mse": ([vp, i32, i64, i64, i32, i32, i32, vp, vp, vp, vp], i32),
         "aq_dequantize": ([vp, vp, vp, i64, i64, i32, i32, vp, i32, vp], i32),
         "aq_embedding": ([vp, vp, vp, i64, i64, i32, i32, vp, i64, vp, i32, vp], i32),
         "aq_qmv": ([vp, i32, i64, vp, vp, vp, i64, i64, i32, i32, vp, vp], i32),
@@ -150,6 +151,25 @@ def aq_quantize(w, group_size: int, bits: int, codes=None, scales=None, biases=N
                          _dev(codes, "codes"), _dev(scales, "scales"), _dev(biases, "biases"),
                          _stream(stream))
     _check(st, "aq_quantize")
+    return codes, scales, biases
+
+
+def aq_quantize_mse(w, group_size: int, bits: int, steps: int, codes=None, scales=None,
+                    biases=None, stream=None):
+    """Range-search quantize W [N, K] over `steps` narrowed ranges -> (codes, scales, biases)."""
+    torch = _torch()
+    lib = load_library()
+    N, K = w.shape
+    if codes is None:
+        codes = torch.empty((N, K * bits // 32), dtype=torch.int32, device=w.device)
+    if scales is None:
+        scales = torch.empty((N, K // group_size), dtype=torch.float16, device=w.device)
+    if biases is None:
+        biases = torch.empty((N, K // group_size), dtype=torch.float16, device=w.device)
+    st = lib.aq_quantize_mse(_dev(w, "w"), _dtype_code(w), N, K, group_size, bits, steps,
+                             _dev(codes, "codes"), _dev(scales, "scales"), _dev(biases, "biases"),
+                             _stream(stream))
+    _check(st, "aq_quantize_mse")
     return codes, scales, biases
 
 

@@ -110,6 +110,20 @@ aq_status aq_quantize(const void *w, aq_dtype w_dtype, int64_t N, int64_t K, int
                                       biases, static_cast<hipStream_t>(stream)));
 }
 
+aq_status aq_quantize_mse(const void *w, aq_dtype w_dtype, int64_t N, int64_t K, int group_size,
+                          int bits, int steps, uint32_t *codes, uint16_t *scales, uint16_t *biases,
+                          void *stream) {
+  if (!valid_format(N, K, group_size, bits) || steps < 1 || steps > 50) return AQ_ERR_INVALID_ARG;
+  if (w_dtype != AQ_F32 && w_dtype != AQ_F16 && w_dtype != AQ_BF16) return AQ_ERR_INVALID_ARG;
+  if (!w) return AQ_ERR_INVALID_ARG;
+  aq_status st = check_weights(codes, scales, biases);
+  if (st != AQ_OK) return st;
+  if (!aligned16(w)) return AQ_ERR_ALIGNMENT;
+  if (N * (K / 8) > (int64_t)0x7FFFFFFF * 256) return AQ_ERR_UNSUPPORTED;
+  return from_hip(aq::launch_quantize_mse(w, (int)w_dtype, N, K, group_size, bits, steps, codes,
+                                          scales, biases, static_cast<hipStream_t>(stream)));
+}
+
 aq_status aq_dequantize(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
                         int64_t N, int64_t K, int group_size, int bits, void *out,
                         aq_dtype out_dtype, void *stream) {

@@ -15,6 +15,11 @@ int device_cus();
 hipError_t launch_quantize(const void *w, int w_dtype, int64_t N, int64_t K, int G, int bits,
                            uint32_t *codes, uint16_t *scales, uint16_t *biases, hipStream_t s);
 
+// range-search quantize: steps candidate ranges per group, least squared error
+hipError_t launch_quantize_mse(const void *w, int w_dtype, int64_t N, int64_t K, int G, int bits,
+                               int steps, uint32_t *codes, uint16_t *scales, uint16_t *biases,
+                               hipStream_t s);
+
 hipError_t launch_dequantize(const uint32_t *codes, const uint16_t *scales,
                              const uint16_t *biases, int64_t N, int64_t K, int G, int bits,
                              void *out, int out_dtype, hipStream_t s);

@@ -12,6 +12,13 @@
 // binary32 weights are exact in binary64.  Approximate binary32 arithmetic
 // only proposes candidates that the exact tests then correct by one step.
 //
+// Range search ("mlx-gptq", "How it works": the --mse grid search narrows a
+// group's min-max range where clipping the extremes costs less than the
+// coarser step costs the rest of the group): candidates i < steps shrink the
+// range to [p min, p max], p = (100 - i) / 100 (binary64), each quantized by
+// the rules above; the least binary64 sum of squared errors wins, an equal
+// one keeping the wider candidate.
+//
 // Dequantize ("Tutorial 10: Quantization", s.3/s.7): q*s + b in binary32
 // (one rounding, the product is exact), then round-to-nearest-even to the
 // output type.
@@ -42,9 +49,17 @@ __device__ __forceinline__ uint16_t f16_round_down(float f) {
   return h == 0x8000u ? (uint16_t)0 : h;
 }
 
-// smallest binary16 s >= 0 with b + L*s >= hi (exact test in binary64)
-__device__ __forceinline__ uint16_t f16_scale_up(double b, float hi, int L) {
-  const double top = (double)hi;
+// the same for a binary64 value: rounding to binary32 and then to binary16
+// preserves the order against every binary16 value, so the result is again
+// the answer or one step above it
+__device__ __forceinline__ uint16_t f16_round_down_d(double x) {
+  uint16_t h = f32_to_f16_rne((float)x);
+  if (h2d(h) > x) h = f16_next_down(h);
+  return h == 0x8000u ? (uint16_t)0 : h;
+}
+
+// smallest binary16 s >= 0 with b + L*s >= top (exact test in binary64)
+__device__ __forceinline__ uint16_t f16_scale_up(double b, double top, int L) {
   if (b >= top) return 0;
   const float t = (float)(top - b) / (float)L;  // candidate, within a step of the answer
   uint16_t s = f32_to_f16_rne(t);
@@ -130,7 +145,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void *__restrict__ 
   constexpr int L = (1 << BITS) - 1;
   const uint16_t b16 = f16_round_down(lo);
   const double b = h2d(b16);
-  const uint16_t s16 = f16_scale_up(b, hi, L);
+  const uint16_t s16 = f16_scale_up(b, (double)hi, L);
   const double s = h2d(s16);
   const float bf = (float)b;
   const float rs = s16 ? __builtin_amdgcn_rcpf((float)s) : 0.f;
@@ -160,6 +175,77 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void *__restrict__ 
 #pragma unroll
     for (int j = 0; j < BITS; ++j) dst[j] = (uint8_t)(packed >> (8 * j));
   }
+}
+
+// The range search: the thread mapping of quantize_kernel; every lane of a
+// group evaluates every candidate (its 8 codes and their squared errors, the
+// group sum by a butterfly, whose result is the same bits on every lane) and
+// keeps the best.
+template <int WDT, int BITS>
+__global__ __launch_bounds__(256) void quantize_mse_kernel(const void *__restrict__ w, int64_t N,
+                                                           int64_t K, int G, int steps,
+                                                           uint32_t *__restrict__ codes,
+                                                           uint16_t *__restrict__ scales,
+                                                           uint16_t *__restrict__ biases) {
+  const int64_t opr = K >> 3;
+  const int64_t total = N * opr;
+  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool active = idx < total;
+  if (!active) idx = total - 1;
+  const int64_t n = idx / opr, o = idx - n * opr;
+
+  float v[8];
+  load8<WDT>(w, n * K + o * 8, v);
+  float lo = v[0], hi = v[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) { lo = fminf(lo, v[i]); hi = fmaxf(hi, v[i]); }
+  const int lanes = G >> 3;
+  for (int d = 1; d < lanes; d <<= 1) {
+    lo = fminf(lo, __shfl_xor(lo, d));
+    hi = fmaxf(hi, __shfl_xor(hi, d));
+  }
+  constexpr int L = (1 << BITS) - 1;
+  double best = __builtin_inf();
+  uint16_t best_b = 0, best_s = 0;
+  uint64_t best_packed = 0;
+  for (int i = 0; i < steps; ++i) {
+    const double pr = (double)(100 - i) / 100.0;
+    const uint16_t b16 = f16_round_down_d(pr * (double)lo);
+    const double b = h2d(b16);
+    const uint16_t s16 = f16_scale_up(b, pr * (double)hi, L);
+    const double s = h2d(s16);
+    const float bf = (float)b;
+    const float rs = s16 ? __builtin_amdgcn_rcpf((float)s) : 0.f;
+    uint64_t packed = 0;
+    double e = 0.0;
+    {
+#pragma clang fp contract(off)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t q = nearest_code(v[k], b, s, bf, rs, L);
+        packed |= (uint64_t)q << (BITS * k);
+        const double dv = (double)v[k] - (b + (double)q * s);
+        e = e + dv * dv;
+      }
+      for (int d = 1; d < lanes; d <<= 1) e = e + __shfl_xor(e, d);
+    }
+    if (e < best) {
+      best = e;
+      best_b = b16;
+      best_s = s16;
+      best_packed = packed;
+    }
+  }
+
+  if (!active) return;
+  if ((o & (lanes - 1)) == 0) {
+    const int64_t gi = n * (K / G) + (o * 8) / G;
+    scales[gi] = best_s;
+    biases[gi] = best_b;
+  }
+  uint8_t *dst = reinterpret_cast<uint8_t *>(codes + n * (K * BITS / 32)) + o * BITS;
+#pragma unroll
+  for (int j = 0; j < BITS; ++j) dst[j] = (uint8_t)(best_packed >> (8 * j));
 }
 
 // One thread per 32-code chunk of an output row.  With GATHER (quantized
@@ -228,6 +314,20 @@ hipError_t quantize_w(const void *w, int64_t N, int64_t K, int G, int bits, uint
   return hipGetLastError();
 }
 
+template <int WDT>
+hipError_t quantize_mse_w(const void *w, int64_t N, int64_t K, int G, int bits, int steps,
+                          uint32_t *codes, uint16_t *scales, uint16_t *biases, hipStream_t s) {
+  const int64_t total = N * (K / 8);
+  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+#define AQ_Q(B) case B: hipLaunchKernelGGL((quantize_mse_kernel<WDT, B>), grid, block, 0, s, w, N, K, G, steps, codes, scales, biases); break;
+  switch (bits) {
+    AQ_Q(2) AQ_Q(3) AQ_Q(4) AQ_Q(5) AQ_Q(6) AQ_Q(7) AQ_Q(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef AQ_Q
+  return hipGetLastError();
+}
+
 template <int ODT, bool GATHER>
 hipError_t dequantize_o(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
                         int64_t N, int64_t K, int G, int bits, const int32_t *ids, int64_t T,
@@ -263,6 +363,17 @@ hipError_t launch_quantize(const void *w, int w_dtype, int64_t N, int64_t K, int
     case X_F32: return quantize_w<X_F32>(w, N, K, G, bits, codes, scales, biases, s);
     case X_F16: return quantize_w<X_F16>(w, N, K, G, bits, codes, scales, biases, s);
     case X_BF16: return quantize_w<X_BF16>(w, N, K, G, bits, codes, scales, biases, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_quantize_mse(const void *w, int w_dtype, int64_t N, int64_t K, int G, int bits,
+                               int steps, uint32_t *codes, uint16_t *scales, uint16_t *biases,
+                               hipStream_t s) {
+  switch (w_dtype) {
+    case X_F32: return quantize_mse_w<X_F32>(w, N, K, G, bits, steps, codes, scales, biases, s);
+    case X_F16: return quantize_mse_w<X_F16>(w, N, K, G, bits, steps, codes, scales, biases, s);
+    case X_BF16: return quantize_mse_w<X_BF16>(w, N, K, G, bits, steps, codes, scales, biases, s);
   }
   return hipErrorInvalidValue;
 }

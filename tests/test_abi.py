@@ -31,7 +31,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("aq_quantize", "aq_dequantize", "aq_qmv", "aq_qmm", "aq_gather_qmv",
+    for n in ("aq_quantize", "aq_quantize_mse", "aq_dequantize", "aq_qmv", "aq_qmm", "aq_gather_qmv",
               "aq_quantized_matmul", "aq_codes_words", "aq_qweight_bytes", "aq_status_string"):
         assert n in names
 
@@ -143,6 +143,17 @@ def test_quantize_dequantize_argument_errors(lib):
     assert d(out=None) == INVALID
     assert d(out=MIS) == ALIGN
     assert d(codes=MIS) == ALIGN
+
+
+def test_quantize_mse_argument_errors(lib):
+    q = lambda **k: lib.aq_quantize_mse(k.get("w", P), F32, 4, k.get("K", 64), 64, k.get("bits", 4),
+                                        k.get("steps", 20), P, P, k.get("biases", P), None)
+    assert q(steps=0) == INVALID
+    assert q(steps=51) == INVALID
+    assert q(bits=1) == INVALID
+    assert q(K=96) == INVALID
+    assert q(biases=None) == INVALID
+    assert q(w=MIS) == ALIGN
 
 
 def test_gather_argument_errors(lib):

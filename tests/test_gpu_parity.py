@@ -51,6 +51,55 @@ def test_quantize_bitexact_f32(aq, bits, G):
     assert np.array_equal(gc, c)
 
 
+def _check_mse(w, G, bits, steps, got):
+    """Range search: bit-exact with the reference wherever both pick the same
+    candidate; elsewhere the device's candidate must tie the least error up to
+    the rounding of the binary64 sums (the two add in different orders), and
+    its scale, bias and codes must be exactly the reference's for it."""
+    c, s, b, chosen, errs = oracle.quantize_mse(w, G, bits, steps, details=True)
+    gc, gs, gb = got
+    K = w.shape[1]
+    q_ref, q_dev = oracle.unpack(c, K, bits), oracle.unpack(gc, K, bits)
+    same = (gs == s) & (gb == b)
+    for n, g in zip(*np.nonzero(same)):
+        assert np.array_equal(q_dev[n, g * G:(g + 1) * G], q_ref[n, g * G:(g + 1) * G]), (n, g)
+    forced = {}
+    for n, g in zip(*np.nonzero(~same)):
+        for j in range(steps):
+            if j not in forced:
+                fc, fs, fb = oracle.quantize_mse(w, G, bits, steps, only=j)
+                forced[j] = (oracle.unpack(fc, K, bits), fs, fb)
+            fq, fs, fb = forced[j]
+            if fs[n, g] == gs[n, g] and fb[n, g] == gb[n, g]:
+                assert errs[n, g, j] <= errs[n, g].min() * (1 + 1e-12), (n, g, j)
+                assert np.array_equal(q_dev[n, g * G:(g + 1) * G], fq[n, g * G:(g + 1) * G])
+                break
+        else:
+            raise AssertionError(f"group {(n, g)}: device grid is no candidate")
+    return int((~same).sum())
+
+
+@pytest.mark.parametrize("bits", ALL_BITS)
+@pytest.mark.parametrize("G", [32, 64, 128])
+def test_quantize_mse(aq, bits, G):
+    N, K, steps = 37, 6 * G, 30
+    w = inputs.weights(N, K, seed=18, key=(G, bits), outliers=True)
+    got = packed_from_dev(*aq.aq_quantize_mse(to_dev(w), G, bits, steps))
+    assert _check_mse(w, G, bits, steps, got) <= N * K // G // 50
+
+
+def test_quantize_mse_one_step_and_half_inputs(aq):
+    G, bits, N, K = 64, 4, 29, 512
+    w = inputs.weights(N, K, seed=19, outliers=True)
+    got = packed_from_dev(*aq.aq_quantize_mse(to_dev(w), G, bits, 1))
+    for a, r in zip(got, oracle.quantize(w, G, bits)):
+        assert np.array_equal(a, r)
+    wb = inputs.to_bits(w, "bf16")
+    w32 = inputs.from_bits(wb, "bf16").astype(np.float32)
+    got = packed_from_dev(*aq.aq_quantize_mse(bits_to_dev(wb, "bf16"), G, 3, 50))
+    _check_mse(w32, G, 3, 50, got)
+
+
 @pytest.mark.parametrize("wdt", ["f16", "bf16"])
 @pytest.mark.parametrize("bits", [3, 4, 8])
 def test_quantize_bitexact_half_inputs(aq, wdt, bits):
@@ -92,6 +141,7 @@ def test_quantize_edge_groups(aq, bits):
     assert np.array_equal(gb, b), np.argwhere(gb != b)
     assert np.array_equal(gs, s), np.argwhere(gs != s)
     assert np.array_equal(gc, c)
+    _check_mse(w, G, bits, 50, packed_from_dev(*aq.aq_quantize_mse(to_dev(w), G, bits, 50)))
 
 
 # ---- dequantize -------------------------------------------------------------------------
