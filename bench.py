@@ -32,7 +32,8 @@ the same bytes (same cold rotation and timing), a measured second denominator.
   specdec, moe  the M = 2..8 matrix-vector kernels (bf16 x, [14336, 4096] and
                 [4096, 14336] at 4/64 and 8/128) and the MoE gather kernel
                 (32 tokens, top-6 of 64 experts), % of HBM per launch on cold
-                weights;
+                weights; plus the matrix-core gather on the same experts at
+                prefill size (2048 tokens, top-6), TFLOP/s;
   quantize_dequantize  aq_quantize of the prefill-size matrix (fp32 in),
                 aq_dequantize of it to bf16 (% of HBM), and the range-search
                 aq_quantize_mse over 21 narrowed ranges;
@@ -484,12 +485,28 @@ def _moe(aq, inputs, dev, stream):
     gbs = algo / (us * 1e-6) / 1e9
     print(f"# MoE gather ({used} of {E} experts used): {us:.2f} us, {gbs:.0f} GB/s algorithmic",
           file=sys.stderr, flush=True)
+    res = {"workload": f"MoE gather: {E} experts [{N},{K}] {bits}-bit G={g}, x fp16 [{T},{K}], "
+                       f"ids [{T},{topk}], cold weights",
+           "experts_used": used, "algo_bytes": algo, "avg_us": round(us, 3),
+           "gbs": round(gbs, 1), "pct_hbm": round(100 * gbs / HBM_PEAK_GBS, 1)}
+    # the same expert stack at prefill size on the matrix cores
+    Tp = cfg["prefill_tokens"]
+    ids_p = torch.from_numpy(inputs.expert_ids(Tp, E, topk, seed=0, key=(wid, 1))).to(dev)
+    xp = inputs.activations_device(Tp, K, "f16", device=dev, seed=0, key=(wid, 1))
+    yp = torch.empty((Tp, topk, N), dtype=torch.float16, device=dev)
+    fs = [lambda c=c, s_=s_, b=b: aq.aq_gather_qmm(xp, c, s_, b, ids_p, g, bits, y=yp)
+          for (c, s_, b) in sets[:4]]
+    us = _graph_us(torch, stream, fs)
+    flop = 2 * Tp * topk * N * K
+    tf = flop / (us * 1e-6) / 1e12
+    print(f"# MoE prefill gather ({Tp} tokens, top-{topk}): {us:.1f} us, {tf:.0f} TFLOP/s",
+          file=sys.stderr, flush=True)
+    res["prefill"] = {"workload": f"x fp16 [{Tp},{K}], ids [{Tp},{topk}], same experts",
+                      "avg_us": round(us, 2), "flop": flop, "tflops": round(tf, 1),
+                      "pct_mfma_peak": round(100 * tf / MFMA_BF16_PEAK_TFLOPS, 1)}
     del sets, packed
     torch.cuda.synchronize()
-    return {"workload": f"MoE gather: {E} experts [{N},{K}] {bits}-bit G={g}, x fp16 [{T},{K}], "
-                        f"ids [{T},{topk}], cold weights",
-            "experts_used": used, "algo_bytes": algo, "avg_us": round(us, 3),
-            "gbs": round(gbs, 1), "pct_hbm": round(100 * gbs / HBM_PEAK_GBS, 1)}
+    return res
 
 
 def _quant_dequant(aq, inputs, dev, stream):

@@ -19,7 +19,7 @@ import os
 __all__ = [
     "AQError", "lib_path", "load_library", "aq_status_string", "aq_version", "aq_codes_words",
     "aq_qweight_bytes", "aq_quantize", "aq_quantize_mse", "aq_dequantize", "aq_qmv", "aq_qmm",
-    "aq_quantized_matmul", "aq_gather_qmv",
+    "aq_quantized_matmul", "aq_gather_qmv", "aq_gather_qmm", "aq_gather_quantized_matmul",
 ]
 
 AQ_OK = 0
@@ -67,6 +67,10 @@ def load_library():
         "aq_quantized_matmul": ([vp, i32, i64, vp, vp, vp, i64, i64, i32, i32, vp, vp], i32),
         "aq_gather_qmv": ([vp, i32, i64, vp, vp, vp, i64, i64, i64, vp, i32, i32, i32, vp, vp],
                           i32),
+        "aq_gather_qmm": ([vp, i32, i64, vp, vp, vp, i64, i64, i64, vp, i32, i32, i32, vp, vp],
+                          i32),
+        "aq_gather_quantized_matmul": (
+            [vp, i32, i64, vp, vp, vp, i64, i64, i64, vp, i32, i32, i32, vp, vp], i32),
         "aq_bench_stream_read": ([vp, i64, i32, i32, vp, vp], i32),
         "aq_bench_mfma_clock": ([i32, i32, vp, vp], i32),
     }
@@ -239,6 +243,23 @@ def aq_quantized_matmul(x, codes, scales, biases, group_size: int, bits: int, y=
 def aq_gather_qmv(x, codes, scales, biases, ids, group_size: int, bits: int, y=None,
                   stream=None):
     """MoE: y[t, j, :] = x[t] @ W_{ids[t, j]}^T; codes [E, N, K*bits/32]."""
+    return _gather("aq_gather_qmv", x, codes, scales, biases, ids, group_size, bits, y, stream)
+
+
+def aq_gather_qmm(x, codes, scales, biases, ids, group_size: int, bits: int, y=None,
+                  stream=None):
+    """MoE at prefill size (matrix cores): same operation as aq_gather_qmv."""
+    return _gather("aq_gather_qmm", x, codes, scales, biases, ids, group_size, bits, y, stream)
+
+
+def aq_gather_quantized_matmul(x, codes, scales, biases, ids, group_size: int, bits: int, y=None,
+                               stream=None):
+    """MoE with the kernel chosen by routed rows per expert."""
+    return _gather("aq_gather_quantized_matmul", x, codes, scales, biases, ids, group_size, bits,
+                   y, stream)
+
+
+def _gather(name, x, codes, scales, biases, ids, group_size, bits, y, stream):
     torch = _torch()
     lib = load_library()
     T, K = x.shape
@@ -246,11 +267,11 @@ def aq_gather_qmv(x, codes, scales, biases, ids, group_size: int, bits: int, y=N
     topk = ids.shape[1]
     if y is None:
         y = torch.empty((T, topk, N), dtype=x.dtype, device=x.device)
-    st = lib.aq_gather_qmv(_dev(x, "x"), _dtype_code(x), T, _dev(codes, "codes"),
-                           _dev(scales, "scales"), _dev(biases, "biases"), E, N, K,
-                           _dev(ids, "ids"), topk, group_size, bits, _dev(y, "y"),
-                           _stream(stream))
-    _check(st, "aq_gather_qmv")
+    st = getattr(lib, name)(_dev(x, "x"), _dtype_code(x), T, _dev(codes, "codes"),
+                            _dev(scales, "scales"), _dev(biases, "biases"), E, N, K,
+                            _dev(ids, "ids"), topk, group_size, bits, _dev(y, "y"),
+                            _stream(stream))
+    _check(st, name)
     return y
 
 

@@ -186,10 +186,10 @@ aq_status aq_quantized_matmul(const void *x, aq_dtype x_dtype, int64_t M, const 
   return aq_qmm(x, x_dtype, M, codes, scales, biases, N, K, group_size, bits, y, stream);
 }
 
-aq_status aq_gather_qmv(const void *x, aq_dtype x_dtype, int64_t T, const uint32_t *codes,
-                        const uint16_t *scales, const uint16_t *biases, int64_t E, int64_t N,
-                        int64_t K, const int32_t *ids, int topk, int group_size, int bits,
-                        void *y, void *stream) {
+static aq_status check_gather(const void *x, aq_dtype x_dtype, int64_t T, const uint32_t *codes,
+                              const uint16_t *scales, const uint16_t *biases, int64_t E,
+                              int64_t N, int64_t K, const int32_t *ids, int topk, int group_size,
+                              int bits, const void *y) {
   if (!valid_format(N, K, group_size, bits) || T < 1 || E < 1 || topk < 1 ||
       !valid_act_dtype(x_dtype))
     return AQ_ERR_INVALID_ARG;
@@ -198,6 +198,41 @@ aq_status aq_gather_qmv(const void *x, aq_dtype x_dtype, int64_t T, const uint32
   if (st != AQ_OK) return st;
   if (!aligned16(x) || !aligned16(y) || !aligned16(ids)) return AQ_ERR_ALIGNMENT;
   if (E > 65535 || T * topk > 0x7FFFFFFF) return AQ_ERR_UNSUPPORTED;
+  return AQ_OK;
+}
+
+aq_status aq_gather_qmm(const void *x, aq_dtype x_dtype, int64_t T, const uint32_t *codes,
+                        const uint16_t *scales, const uint16_t *biases, int64_t E, int64_t N,
+                        int64_t K, const int32_t *ids, int topk, int group_size, int bits,
+                        void *y, void *stream) {
+  aq_status st = check_gather(x, x_dtype, T, codes, scales, biases, E, N, K, ids, topk,
+                              group_size, bits, y);
+  if (st != AQ_OK) return st;
+  if (T * K * 2 > 0x7FFFFFFF) return AQ_ERR_UNSUPPORTED;
+  return from_hip(aq::launch_gather_qmm(x, (int)x_dtype, T, codes, scales, biases, E, N, K, ids,
+                                        topk, group_size, bits, y,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+aq_status aq_gather_quantized_matmul(const void *x, aq_dtype x_dtype, int64_t T,
+                                     const uint32_t *codes, const uint16_t *scales,
+                                     const uint16_t *biases, int64_t E, int64_t N, int64_t K,
+                                     const int32_t *ids, int topk, int group_size, int bits,
+                                     void *y, void *stream) {
+  if (T >= 1 && topk >= 1 && E >= 1 && T * topk >= 32 * E && T * K * 2 <= 0x7FFFFFFF)
+    return aq_gather_qmm(x, x_dtype, T, codes, scales, biases, E, N, K, ids, topk, group_size,
+                         bits, y, stream);
+  return aq_gather_qmv(x, x_dtype, T, codes, scales, biases, E, N, K, ids, topk, group_size, bits,
+                       y, stream);
+}
+
+aq_status aq_gather_qmv(const void *x, aq_dtype x_dtype, int64_t T, const uint32_t *codes,
+                        const uint16_t *scales, const uint16_t *biases, int64_t E, int64_t N,
+                        int64_t K, const int32_t *ids, int topk, int group_size, int bits,
+                        void *y, void *stream) {
+  aq_status st = check_gather(x, x_dtype, T, codes, scales, biases, E, N, K, ids, topk,
+                              group_size, bits, y);
+  if (st != AQ_OK) return st;
   // 4-bit or 8-bit codes: batches of routed tokens on the matrix cores
   if (aq::gather_qmvm_supported(bits, K, group_size) && T * K * 2 <= 0x7FFFFFFF)
     return from_hip(aq::launch_gather_qmvm(x, (int)x_dtype, T, codes, scales, biases, E, N, K,

@@ -61,4 +61,11 @@ hipError_t launch_qmm(const void *x, int x_dtype, int64_t M, const uint32_t *cod
                       const uint16_t *scales, const uint16_t *biases, int64_t N, int64_t K, int G,
                       int bits, void *y, hipStream_t s);
 
+// mixture-of-experts gather at prefill size on the matrix cores: y[t, j, :] =
+// x[t] @ W_{ids[t, j]}^T, experts' pairs listed on the device
+hipError_t launch_gather_qmm(const void *x, int x_dtype, int64_t T, const uint32_t *codes,
+                             const uint16_t *scales, const uint16_t *biases, int64_t E, int64_t N,
+                             int64_t K, const int32_t *ids, int topk, int G, int bits, void *y,
+                             hipStream_t s);
+
 }  // namespace aq

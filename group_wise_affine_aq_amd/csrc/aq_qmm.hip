@@ -20,6 +20,13 @@
 //  * tiles are ordered so that the workgroups resident on one XCD (blocks
 //    are dealt to the 8 XCDs round-robin) share one row-tile of X in that
 //    XCD's L2.
+//
+// The gather variant ("Quantization", metalworking: gather variants of the
+// kernels for MoE experts, here at prefill size) computes y[t, j, :] =
+// x[t] @ W_{ids[t, j]}^T with the same tile engine: one workgroup per
+// (224-column tile, expert) scans the routing ids on the device, lists the
+// (token, slot) pairs routed to its expert in id order, and runs 256-row
+// tiles over that list, loading X rows by token and storing Y rows by pair.
 #include "aq_device.hpp"
 #include "aq_internal.hpp"
 
@@ -170,14 +177,45 @@ __device__ __forceinline__ void sched_segment() {
 template <int BITS>
 constexpr int kDequant8Valu = BITS == 4 ? 24 : (BITS == 8 ? 22 : 30);
 
-template <int BITS, typename XT>
+// routing of the gather variant: ids [T, topk] flattened, experts [0, E)
+struct Routing {
+  const int32_t *ids;
+  int64_t pairs;  // T * topk
+  int topk;
+  int64_t E;
+};
+// pairs of one expert listed per pass (the rest in later passes)
+constexpr int kGList = 4096;
+
+// block-wide exclusive prefix sum of v (256 threads); *total gets the sum
+__device__ __forceinline__ int block_exclusive_sum(int v, int *wsum, int *total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(incl, d);
+    if (lane >= d) incl += u;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) {
+    before += w < wave ? wsum[w] : 0;
+    all += wsum[w];
+  }
+  *total = all;
+  return before + incl - v;
+}
+
+template <int BITS, typename XT, bool GATHER>
 __global__ __launch_bounds__(kThreads) void qmm_kernel(const uint16_t *__restrict__ x, int64_t M,
                                                        const uint32_t *__restrict__ codes,
                                                        const uint16_t *__restrict__ scales,
                                                        const uint16_t *__restrict__ biases,
                                                        int64_t N, int64_t K, int G,
                                                        uint16_t *__restrict__ y, int mtiles,
-                                                       int ntiles) {
+                                                       int ntiles, Routing route) {
   // four distinct LDS objects, so the compiler can tell the DMA target of a
   // step from the buffers read and written beside it
   __shared__ __attribute__((aligned(16))) char xs0[kXStage], xs1[kXStage];
@@ -186,22 +224,34 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const uint16_t *__restric
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave;
 
-  // XCD-aware tile order: block b runs on XCD b % 8; consecutive blocks of one
-  // XCD take consecutive tiles of a row-major (m, n) order, so they share m
-  // (the X row tile stays in that XCD's L2).
-  const int tiles = mtiles * ntiles;
-  int t = blockIdx.x;
-  if ((tiles & 7) == 0) t = (t & 7) * (tiles >> 3) + (t >> 3);
-  const int64_t tile_m = (int64_t)(t / ntiles) * BM, tile_n = (int64_t)(t % ntiles) * BN;
-
   const int nch = (int)(K >> 5), gshift = __builtin_ctz((unsigned)G) - 5;
   const int64_t wpr = (int64_t)nch * BITS, gpr = nch >> gshift;
   const int ksteps = (int)((K + BK - 1) / BK);
 
-  // operand tiles as buffer resources: rows past M or N read as zero
+  int64_t tile_m = 0, tile_n;
+  int expert = 0;
+  if constexpr (!GATHER) {
+    // XCD-aware tile order: block b runs on XCD b % 8; consecutive blocks of
+    // one XCD take consecutive tiles of a row-major (m, n) order, so they
+    // share m (the X row tile stays in that XCD's L2).
+    const int tiles = mtiles * ntiles;
+    int t = blockIdx.x;
+    if ((tiles & 7) == 0) t = (t & 7) * (tiles >> 3) + (t >> 3);
+    tile_m = (int64_t)(t / ntiles) * BM;
+    tile_n = (int64_t)(t % ntiles) * BN;
+  } else {
+    tile_n = (int64_t)blockIdx.x * BN;
+    expert = blockIdx.y;
+    codes += expert * N * wpr;
+    scales += expert * N * gpr;
+    biases += expert * N * gpr;
+  }
+
+  // operand tiles as buffer resources: rows past M or N read as zero (the
+  // gather variant addresses all of x by token)
   const int64_t mrows = M - tile_m < BM ? M - tile_m : BM;
   const int64_t nrows = N - tile_n < BN ? N - tile_n : BN;
-  const int xbytes = (int)(mrows * K * 2);
+  const int xbytes = (int)((GATHER ? M : mrows) * K * 2);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + tile_m * K, xbytes);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(codes + tile_n * wpr, nrows * wpr * 4);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(scales + tile_n * gpr, nrows * gpr * 2);
@@ -221,13 +271,24 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const uint16_t *__restric
   // unit u at slot u ^ ((r >> 1) & 7), so the fragment reads below are free
   // of bank conflicts; load i of wave w fills rows 8 (8w + i) .. +7.
   uint32_t xvoff[kXDma], xvoff_tail[kXDma];
+  __shared__ int glist[GATHER ? kGList : 1];  // pairs of the expert in this pass
+  // row r of the tile at list position r0 is x row r (plain) or the token of
+  // pair glist[r0 + r] (gather); rows >= rows read as zero
+  auto set_rows = [&](int r0, int rows) {
 #pragma unroll
-  for (int i = 0; i < kXDma; ++i) {
-    const int row = 8 * (wave * kXDma + i) + (lane >> 3);
-    const int u = (lane & 7) ^ ((row >> 1) & 7);
-    xvoff[i] = (uint32_t)(row * K + u * 8) * 2u;
-    xvoff_tail[i] = u < 4 ? xvoff[i] : (uint32_t)xbytes;  // k past K: out of range, reads zero
-  }
+    for (int i = 0; i < kXDma; ++i) {
+      const int row = 8 * (wave * kXDma + i) + (lane >> 3);
+      const int u = (lane & 7) ^ ((row >> 1) & 7);
+      uint32_t ro;
+      if constexpr (GATHER)
+        ro = row < rows ? (uint32_t)((int64_t)(glist[r0 + row] / route.topk) * K * 2)
+                        : (uint32_t)xbytes;
+      else
+        ro = (uint32_t)(row * K * 2);
+      xvoff[i] = ro + (uint32_t)u * 16u;
+      xvoff_tail[i] = u < 4 ? xvoff[i] : (uint32_t)xbytes;  // k past K: out of range, reads zero
+    }
+  };
   auto dma_x = [&](int k0, int buf, const uint32_t (&vo)[kXDma]) {
     const uint32_t so = (uint32_t)k0 * 2u;
 #pragma unroll
@@ -267,6 +328,9 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const uint16_t *__restric
   using U2 = std::integral_constant<int, 2>;
   using U3 = std::integral_constant<int, 3>;
 
+  // one 256 x 224 tile: rows from list position r0 (gather) or x row tile_m
+  auto tile = [&](int r0, int rows) {
+  set_rows(r0, rows);
   f32x16v acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -394,6 +458,7 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const uint16_t *__restric
   // epilogue: accumulator r of lane l in a 32x32 block is row
   // 8*(r/4) + 4*(l/32) + r%4, column l % 32 (2-byte stores; staging the tile
   // through LDS for 16-byte stores measured slower)
+  if constexpr (!GATHER) {
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -405,19 +470,108 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const uint16_t *__restric
         if (m < M && n < N) y[m * N + n] = xtraits<XT>::from_f32(acc[i][j][r]);
       }
     }
+  } else {
+    // row lr of the tile is pair glist[r0 + lr]: y row of that (token, slot)
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int lr = wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (lr < rows) {
+          uint16_t *yr = y + (int64_t)glist[r0 + lr] * N;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int64_t n = tile_n + j * 32 + (lane & 31);
+            if (n < N) yr[n] = xtraits<XT>::from_f32(acc[i][j][r]);
+          }
+        }
+      }
+  }
+  };
+
+  if constexpr (!GATHER) {
+    tile(0, (int)mrows);
+  } else {
+    __shared__ int gsum[kThreads / 64 + 2];
+    const int64_t total = route.pairs;
+    // pairs whose id is outside [0, E): zero rows (written by expert 0)
+    if (expert == 0)
+      for (int64_t p = tid; p < total; p += kThreads) {
+        const int32_t id = route.ids[p];
+        if (id < 0 || id >= route.E)
+          for (int nn = 0; nn < nrows; ++nn) y[p * N + tile_n + nn] = 0;
+      }
+    // passes over the ids: each lists, in id order, the next kGList pairs
+    // routed to this expert (thread t scans a contiguous segment; a block
+    // prefix sum of the segment counts gives every match its rank)
+    int64_t pos = 0;
+    while (pos < total) {
+      const int64_t seg = (total - pos + kThreads - 1) / kThreads;
+      const int64_t a = pos + tid * seg, b = a + seg < total ? a + seg : total;
+      int cnt = 0;
+#pragma unroll 8
+      for (int64_t p = a; p < b; ++p) cnt += route.ids[p] == expert;
+      int found;
+      int rank = block_exclusive_sum(cnt, gsum, &found);
+      if (tid == 0) gsum[kThreads / 64] = -1;
+      __syncthreads();
+      if (cnt > 0)
+        for (int64_t p = a; p < b; ++p)
+          if (route.ids[p] == expert) {
+            if (rank < kGList) glist[rank] = (int)p;
+            else if (rank == kGList) gsum[kThreads / 64] = (int)p;  // first pair left over
+            ++rank;
+          }
+      __syncthreads();
+      const int listed = found < kGList ? found : kGList;
+      pos = found > kGList ? (int64_t)gsum[kThreads / 64] : total;
+      for (int r0 = 0; r0 < listed; r0 += BM) {
+        tile(r0, listed - r0 < BM ? listed - r0 : BM);
+        __syncthreads();  // LDS stages and the list are reused
+      }
+    }
+  }
 }
 
 template <int BITS, typename XT>
 hipError_t qmm_launch(const void *x, int64_t M, const uint32_t *codes, const uint16_t *scales,
                       const uint16_t *biases, int64_t N, int64_t K, int G, void *y,
                       hipStream_t s) {
-  auto kern = qmm_kernel<BITS, XT>;
+  auto kern = qmm_kernel<BITS, XT, false>;
   const int64_t mt = (M + BM - 1) / BM, nt = (N + BN - 1) / BN;
   if (mt * nt > 0x7FFFFFFF || mt > 0x7FFFFFFF || nt > 0x7FFFFFFF) return hipErrorInvalidValue;
   if ((int64_t)BM * K * 2 > 0x7FFFFFFF) return hipErrorInvalidValue;  // 32-bit tile offsets
   hipLaunchKernelGGL(kern, dim3((unsigned)(mt * nt)), dim3(kThreads), 0, s, (const uint16_t *)x, M,
-                     codes, scales, biases, N, K, G, (uint16_t *)y, (int)mt, (int)nt);
+                     codes, scales, biases, N, K, G, (uint16_t *)y, (int)mt, (int)nt, Routing{});
   return hipGetLastError();
+}
+
+template <int BITS, typename XT>
+hipError_t gather_qmm_launch(const void *x, int64_t T, const uint32_t *codes,
+                             const uint16_t *scales, const uint16_t *biases, int64_t E, int64_t N,
+                             int64_t K, const int32_t *ids, int topk, int G, void *y,
+                             hipStream_t s) {
+  auto kern = qmm_kernel<BITS, XT, true>;
+  const int64_t nt = (N + BN - 1) / BN;
+  // all of x is addressed with 32-bit byte offsets; pairs are listed as int
+  if (T * K * 2 > 0x7FFFFFFF || T * topk > 0x7FFFFFFF || nt > 0x7FFFFFFF || E > 65535)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kern, dim3((unsigned)nt, (unsigned)E), dim3(kThreads), 0, s,
+                     (const uint16_t *)x, T, codes, scales, biases, N, K, G, (uint16_t *)y, 0,
+                     (int)nt, Routing{ids, T * topk, topk, E});
+  return hipGetLastError();
+}
+
+template <typename XT>
+hipError_t gather_qmm_bits(const void *x, int64_t T, const uint32_t *codes, const uint16_t *scales,
+                           const uint16_t *biases, int64_t E, int64_t N, int64_t K,
+                           const int32_t *ids, int topk, int G, int bits, void *y, hipStream_t s) {
+  switch (bits) {
+#define AQ_GQ(B) case B: return gather_qmm_launch<B, XT>(x, T, codes, scales, biases, E, N, K, ids, topk, G, y, s);
+    AQ_GQ(2) AQ_GQ(3) AQ_GQ(4) AQ_GQ(5) AQ_GQ(6) AQ_GQ(7) AQ_GQ(8)
+#undef AQ_GQ
+  }
+  return hipErrorInvalidValue;
 }
 
 template <typename XT>
@@ -443,6 +597,17 @@ hipError_t launch_qmm(const void *x, int x_dtype, int64_t M, const uint32_t *cod
                       int bits, void *y, hipStream_t s) {
   if (x_dtype == X_F16) return qmm_bits<f16_t>(x, M, codes, scales, biases, N, K, G, bits, y, s);
   if (x_dtype == X_BF16) return qmm_bits<bf16_t>(x, M, codes, scales, biases, N, K, G, bits, y, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gather_qmm(const void *x, int x_dtype, int64_t T, const uint32_t *codes,
+                             const uint16_t *scales, const uint16_t *biases, int64_t E, int64_t N,
+                             int64_t K, const int32_t *ids, int topk, int G, int bits, void *y,
+                             hipStream_t s) {
+  if (x_dtype == X_F16)
+    return gather_qmm_bits<f16_t>(x, T, codes, scales, biases, E, N, K, ids, topk, G, bits, y, s);
+  if (x_dtype == X_BF16)
+    return gather_qmm_bits<bf16_t>(x, T, codes, scales, biases, E, N, K, ids, topk, G, bits, y, s);
   return hipErrorInvalidValue;
 }
 

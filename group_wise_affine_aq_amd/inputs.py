@@ -43,7 +43,7 @@ WORKLOADS = {
     "prefill": dict(shapes=[(28672, 8192)], bits=[4, 3, 2], group_size=[64, 64, 32], M=[2048],
                     x_dtype="bf16", outliers=False),
     "moe": dict(shapes=[(1408, 2048)], experts=64, tokens=32, topk=6, bits=[4], group_size=[64],
-                x_dtype="f16", outliers=False),
+                x_dtype="f16", outliers=False, prefill_tokens=2048),
     "embedding": dict(shapes=[(128256, 4096)], bits=[8], group_size=[128], tokens=[1, 2048],
                       out_dtype="bf16", outliers=False),
 }

@@ -178,6 +178,27 @@ aq_status aq_gather_qmv(const void *x, aq_dtype x_dtype, int64_t T, const uint32
                         int64_t K, const int32_t *ids, int topk, int group_size, int bits,
                         void *y, void *stream);
 
+/* The gather product at prefill size, on the matrix cores (the QMM engine
+ * of aq_qmm): same operation, arguments and layouts as aq_gather_qmv, for
+ * many tokens per expert.  The routing is resolved on the device: one
+ * workgroup per (224 columns, expert) lists the (token, slot) pairs routed
+ * to its expert and runs 256-row tiles of them, so each expert's weights are
+ * read once per 256 routed rows.  Weight tiles are rounded to x_dtype as in
+ * aq_qmm.  AQ_ERR_UNSUPPORTED if T*K*2 > 2^31-1 (x addressed with 32-bit
+ * byte offsets), E > 65535 or T*topk > 2^31-1. */
+aq_status aq_gather_qmm(const void *x, aq_dtype x_dtype, int64_t T, const uint32_t *codes,
+                        const uint16_t *scales, const uint16_t *biases, int64_t E, int64_t N,
+                        int64_t K, const int32_t *ids, int topk, int group_size, int bits,
+                        void *y, void *stream);
+
+/* Shape dispatch for the gather product: aq_gather_qmm when the routed rows
+ * average at least 32 per expert (T*topk >= 32*E), else aq_gather_qmv. */
+aq_status aq_gather_quantized_matmul(const void *x, aq_dtype x_dtype, int64_t T,
+                                     const uint32_t *codes, const uint16_t *scales,
+                                     const uint16_t *biases, int64_t E, int64_t N, int64_t K,
+                                     const int32_t *ids, int topk, int group_size, int bits,
+                                     void *y, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -169,6 +169,17 @@ def test_gather_argument_errors(lib):
     assert g(K=100) == INVALID
     assert g(dt=F32) == INVALID
     assert g(E=70000) == UNSUPPORTED
+    for name in ("aq_gather_qmm", "aq_gather_quantized_matmul"):
+        h = lambda **k: getattr(lib, name)(k.get("x", P), k.get("dt", F16), k.get("T", 4), P, P, P,
+                                           k.get("E", 8), 64, k.get("K", 128), k.get("ids", P),
+                                           k.get("topk", 2), 64, 4, k.get("y", P), None)
+        assert h(T=0) == INVALID
+        assert h(ids=None) == INVALID
+        assert h(y=MIS) == ALIGN
+        assert h(dt=F32) == INVALID
+    # x too large for 32-bit offsets on the matrix-core gather
+    assert lib.aq_gather_qmm(P, F16, 1 << 20, P, P, P, 8, 64, 1 << 11, P, 2, 64, 4, P,
+                             None) == UNSUPPORTED
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

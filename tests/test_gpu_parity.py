@@ -363,6 +363,70 @@ def test_gather_long_rows(aq, K):
     _assert_close(y, y_ref, A, f"gather K{K}")
 
 
+# ---- gather at prefill size (matrix cores) -------------------------------------------------
+@pytest.mark.parametrize("bits", ALL_BITS)
+@pytest.mark.parametrize("xdt,K", [("f16", 544), ("bf16", 2048)])
+def test_gather_qmm_parity(aq, bits, xdt, K):
+    """Several experts with ~180 routed rows each, N ragged against 224-column
+    tiles, K with a 32-code tail (fp16) or at bf16 depth."""
+    G = 32 if K % 64 else GROUP_FOR_BITS[bits]
+    E, N, T, topk = 5, 300, 300, 3
+    c, s, b = _experts(E, N, K, G, bits, seed=20)
+    ids = inputs.expert_ids(T, E, topk, seed=20)
+    xb = inputs.activations(T, K, xdt, seed=20, key=(bits, K))
+    y_ref, A = oracle.gather_matmul(inputs.from_bits(xb, xdt), c, s, b, ids, K, G, bits)
+    y = aq.aq_gather_qmm(bits_to_dev(xb, xdt), *packed_to_dev(c, s, b), to_dev(ids), G, bits)
+    _assert_close(y, y_ref, A, f"gather_qmm b{bits} {xdt} K{K}")
+
+
+def test_gather_qmm_crowded_and_bad_ids(aq):
+    """One expert with 1398 routed rows (six 256-row tiles), an unused expert,
+    and ids outside [0, E) (zero rows)."""
+    G, bits, E, N, K, T, topk = 64, 4, 3, 250, 256, 700, 2
+    c, s, b = _experts(E, N, K, G, bits, seed=21)
+    ids = np.ones((T, topk), dtype=np.int32)
+    ids[::7, 1] = 0
+    ids[3, 0], ids[10, 1] = -1, E
+    xb = inputs.activations(T, K, "f16", seed=21)
+    import torch
+    y = torch.full((T, topk, N), 7.0, dtype=torch.float16, device="cuda")
+    aq.aq_gather_qmm(bits_to_dev(xb, "f16"), *packed_to_dev(c, s, b), to_dev(ids), G, bits, y=y)
+    y = out_to_f64(y)
+    assert np.all(y[3, 0] == 0) and np.all(y[10, 1] == 0)
+    keep = (ids >= 0) & (ids < E)
+    safe = np.where(keep, ids, 0).astype(np.int32)
+    y_ref, A = oracle.gather_matmul(inputs.from_bits(xb, "f16"), c, s, b, safe, K, G, bits)
+    ok, ratio = oracle.within_tolerance(y[keep], y_ref[keep], A[keep])
+    assert ok, ratio
+
+
+def test_gather_qmm_more_pairs_than_one_list(aq):
+    """More pairs on one expert than one listing pass holds (4096): the scan
+    resumes where the list filled up."""
+    G, bits, E, N, K, T = 64, 4, 2, 40, 64, 4500
+    c, s, b = _experts(E, N, K, G, bits, seed=22)
+    ids = np.zeros((T, 1), dtype=np.int32)
+    ids[::5, 0] = 1
+    xb = inputs.activations(T, K, "f16", seed=22)
+    y_ref, A = oracle.gather_matmul(inputs.from_bits(xb, "f16"), c, s, b, ids, K, G, bits)
+    y = aq.aq_gather_qmm(bits_to_dev(xb, "f16"), *packed_to_dev(c, s, b), to_dev(ids), G, bits)
+    _assert_close(y, y_ref, A, "gather_qmm multi-pass")
+
+
+@pytest.mark.parametrize("T", [4, 200])
+def test_gather_dispatch(aq, T):
+    """Few rows per expert go to the matrix-vector gather, many to the
+    matrix-core gather; both agree with the reference."""
+    G, bits, E, N, K, topk = 64, 4, 8, 70, 256, 2
+    c, s, b = _experts(E, N, K, G, bits, seed=23)
+    ids = inputs.expert_ids(T, E, topk, seed=23)
+    xb = inputs.activations(T, K, "f16", seed=23)
+    y_ref, A = oracle.gather_matmul(inputs.from_bits(xb, "f16"), c, s, b, ids, K, G, bits)
+    y = aq.aq_gather_quantized_matmul(bits_to_dev(xb, "f16"), *packed_to_dev(c, s, b),
+                                      to_dev(ids), G, bits)
+    _assert_close(y, y_ref, A, f"gather dispatch T{T}")
+
+
 def test_gather_crowded_expert_and_bad_ids(aq):
     """More tokens on one expert than one batch holds (processed in batches),
     unused experts, and ids outside [0, E) (their rows come back zero)."""

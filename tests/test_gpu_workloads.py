@@ -9,7 +9,9 @@ gather kernel for the experts).
            x bf16 [M, K], M in {2,3,4,6,8}
   prefill  X bf16 [2048, 8192], W [28672, 8192] at 4-bit G=64, 3-bit G=64,
            2-bit G=32 (outputs compared on a seeded sample of rows x columns)
-  moe      64 experts [1408, 2048] 4-bit G=64, x fp16 [32, 2048], ids [32, 6]
+  moe      64 experts [1408, 2048] 4-bit G=64, x fp16 [32, 2048], ids [32, 6];
+           the same experts at prefill size, x fp16 [2048, 2048], ids [2048, 6]
+           (sampled rows)
   embedding table [128256, 4096] 8-bit G=128, T in {1, 2048} token ids, bf16 out
 
 Quantization is checked bit-exactly on every element (for the embedding table,
@@ -124,6 +126,29 @@ def test_moe(aq):
     y_ref, A = oracle.gather_matmul(inputs.from_bits(xb, "f16"), c, s, b, ids, K, 64, 4)
     y = aq.aq_gather_qmv(bits_to_dev(xb, "f16"), *packed_to_dev(c, s, b), to_dev(ids), 64, 4)
     _close(out_to_f64(y), y_ref, A, "moe")
+
+
+def test_moe_prefill(aq):
+    """The same expert stack at prefill size through the matrix-core gather:
+    2048 tokens top-6; 128 sampled (token, slot) rows checked against the
+    reference, all rows finite."""
+    cfg = inputs.WORKLOADS["moe"]
+    (N, K), E, T, topk = cfg["shapes"][0], cfg["experts"], cfg["prefill_tokens"], cfg["topk"]
+    packs = [oracle.quantize(inputs.weights(N, K, seed=0, key=(WID["moe"], e)), 64, 4)
+             for e in range(E)]
+    c = np.stack([p[0] for p in packs]); s = np.stack([p[1] for p in packs])
+    b = np.stack([p[2] for p in packs])
+    ids = inputs.expert_ids(T, E, topk, seed=0, key=(WID["moe"], 1))
+    xb = inputs.activations(T, K, "f16", seed=0, key=(WID["moe"], 1))
+    y = out_to_f64(aq.aq_gather_quantized_matmul(bits_to_dev(xb, "f16"), *packed_to_dev(c, s, b),
+                                                 to_dev(ids), 64, 4))
+    assert np.all(np.isfinite(y))
+    rng = np.random.default_rng(7)
+    t = rng.integers(0, T, 128)
+    j = rng.integers(0, topk, 128)
+    x = inputs.from_bits(xb, "f16")[t]
+    y_ref, A = oracle.gather_matmul(x, c, s, b, ids[t, j][:, None].astype(np.int32), K, 64, 4)
+    _close(y[t, j][:, None, :], y_ref, A, "moe prefill")
 
 
 def test_embedding(aq):
