@@ -206,10 +206,9 @@ def main():
             durs.append(e0.elapsed_time(e1) * 1e3 / reps)  # us per launch
         del g
         avg = sum(durs) / len(durs)
-        cpl = -(-(m["K"] // 32) // 64)  # 64-chunk passes per row: the kernel's CPL
         per_shape.append(dict(shape=[m["N"], m["K"]], weight_bytes=m["wbytes"],
                               algo_bytes=m["algo_bytes"], launches=reps * 5,
-                              kernel=f"qmv1_kernel<BITS={BITS}, f16, CPL={cpl}>",
+                              kernel=aq.aq_qmv_describe(1, m["N"], m["K"], G, BITS, "f16"),
                               avg_us=round(avg, 3), min_us=round(min(durs), 3),
                               weight_gbs=round(m["wbytes"] / (avg * 1e-6) / 1e9, 1),
                               pct_hbm=round(100 * m["wbytes"] / (avg * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)))

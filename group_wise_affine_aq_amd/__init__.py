@@ -60,6 +60,7 @@ def load_library():
         "aq_qweight_bytes": ([i64, i64, i32, i32], i64),
         "aq_quantize": ([vp, i32, i64, i64, i32, i32, vp, vp, vp, vp], i32),
         "aq_quantize_mse": ([vp, i32, i64, i64, i32, i32, i32, vp, vp, vp, vp], i32),
+        "aq_qmv_describe": ([i64, i64, i64, i32, i32, i32, ctypes.c_char_p, i32], i32),
         "aq_dequantize": ([vp, vp, vp, i64, i64, i32, i32, vp, i32, vp], i32),
         "aq_embedding": ([vp, vp, vp, i64, i64, i32, i32, vp, i64, vp, i32, vp], i32),
         "aq_qmv": ([vp, i32, i64, vp, vp, vp, i64, i64, i32, i32, vp, vp], i32),
@@ -156,6 +157,17 @@ def aq_quantize(w, group_size: int, bits: int, codes=None, scales=None, biases=N
                          _stream(stream))
     _check(st, "aq_quantize")
     return codes, scales, biases
+
+
+def aq_qmv_describe(M: int, N: int, K: int, group_size: int, bits: int, x_dtype="f16") -> str:
+    """Name and compile-time shape of the kernel aq_qmv launches for this shape."""
+    lib = load_library()
+    code = {"f16": AQ_F16, "bf16": AQ_BF16}[x_dtype]
+    buf = ctypes.create_string_buffer(160)
+    n = lib.aq_qmv_describe(M, N, K, group_size, bits, code, buf, len(buf))
+    if n < 0:
+        raise AQError(-1, "aq_qmv_describe")
+    return buf.value.decode()
 
 
 def aq_quantize_mse(w, group_size: int, bits: int, steps: int, codes=None, scales=None,

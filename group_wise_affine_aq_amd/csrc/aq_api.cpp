@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstdio>
+
 #include "aq.h"
 #include "aq_internal.hpp"
 
@@ -164,6 +166,27 @@ aq_status aq_qmv(const void *x, aq_dtype x_dtype, int64_t M, const uint32_t *cod
                                     group_size, bits, y, static_cast<hipStream_t>(stream)));
   return from_hip(aq::launch_qmv(x, (int)x_dtype, (int)M, codes, scales, biases, N, K, group_size,
                                  bits, y, static_cast<hipStream_t>(stream)));
+}
+
+int aq_qmv_describe(int64_t M, int64_t N, int64_t K, int group_size, int bits, aq_dtype x_dtype,
+                    char *buf, int len) {
+  if (!valid_format(N, K, group_size, bits) || M < 1 || M > kMaxQmvRows ||
+      !valid_act_dtype(x_dtype) || !buf || len < 1)
+    return -1;
+  const char *xt = x_dtype == AQ_F16 ? "f16" : "bf16";
+  if (M == 1 && K <= 8 * 2048) {
+    int cpl, ud, w;
+    aq::qmv1_shape(N, K, cpl, ud, w);
+    return snprintf(buf, (size_t)len, "qmv1_kernel<BITS=%d, %s, CPL=%d, UD=%d, W=%d>", bits, xt,
+                    cpl, ud, w);
+  }
+  if (aq::qmvm_supported((int)M, bits, N, K, group_size)) {
+    int R, W, XR;
+    aq::qmvm_shape((int)M, N, K, group_size, R, W, XR);
+    return snprintf(buf, (size_t)len, "qmvm_kernel<%s, BITS=%d, W=%d, G=%d, XR=%d, R=%d>", xt,
+                    bits, W, group_size, XR, R);
+  }
+  return snprintf(buf, (size_t)len, "qmv vector kernel<BITS=%d, %s, M=%d>", bits, xt, (int)M);
 }
 
 aq_status aq_qmm(const void *x, aq_dtype x_dtype, int64_t M, const uint32_t *codes,

@@ -766,10 +766,24 @@ template <> struct stream_shape<2> { static constexpr int R = 2, D = 4; };
 template <> struct stream_shape<4> { static constexpr int R = 4, D = 2; };
 template <> struct stream_shape<8> { static constexpr int R = 4, D = 2; };
 
-template <int BITS, typename XT, int CPL, int UD>
+}  // namespace
+
+// M = 1 kernel shape: CPL 64-chunk passes per row, UD rows in flight per
+// wave, W waves per workgroup.  Measured on the MI355X (cold weights): at
+// K = 4096, 8-wave workgroups for N > 2048 and one row in flight per wave past
+// N = 8192 (the waves then outnumber a CU's rows enough to keep its loads in
+// flight); at K = 14336, 8-wave workgroups.
+void qmv1_shape(int64_t N, int64_t K, int &cpl, int &ud, int &w) {
+  cpl = (int)((K / 32 + 63) / 64);
+  ud = cpl == 1 ? 4 : (cpl == 2 ? (N > 8192 ? 1 : 2) : 1);
+  w = (cpl == 2 && N > 2048) || cpl == 7 ? 8 : 4;
+}
+
+namespace {
+
+template <int BITS, typename XT, int CPL, int UD, int W = 4>
 hipError_t qmv1_launch(const void *x, const Weights &wt, int64_t N, int64_t K, int G, void *y,
                        hipStream_t s) {
-  constexpr int W = 4;
   auto kern = qmv1_kernel<BITS, XT, CPL, UD, W>;
   const size_t lds = (size_t)64 * CPL * kChunkLdsBytes + (size_t)W * kStreamRound * 2;
   static int per_cu = 0;  // resident workgroups per CU for this instantiation
@@ -791,14 +805,20 @@ hipError_t qmv1_launch(const void *x, const Weights &wt, int64_t N, int64_t K, i
 template <int BITS, typename XT>
 hipError_t qmv1_dispatch(const void *x, const Weights &wt, int64_t N, int64_t K, int G, void *y,
                          hipStream_t s) {
-  switch ((K / 32 + 63) / 64) {  // passes of 64 chunks per row
+  int cpl, ud, w;
+  qmv1_shape(N, K, cpl, ud, w);
+  switch (cpl) {
     case 1: return qmv1_launch<BITS, XT, 1, 4>(x, wt, N, K, G, y, s);
-    case 2: return qmv1_launch<BITS, XT, 2, 2>(x, wt, N, K, G, y, s);
+    case 2:
+      if (w == 8)
+        return ud == 1 ? qmv1_launch<BITS, XT, 2, 1, 8>(x, wt, N, K, G, y, s)
+                       : qmv1_launch<BITS, XT, 2, 2, 8>(x, wt, N, K, G, y, s);
+      return qmv1_launch<BITS, XT, 2, 2>(x, wt, N, K, G, y, s);
     case 3: return qmv1_launch<BITS, XT, 3, 1>(x, wt, N, K, G, y, s);
     case 4: return qmv1_launch<BITS, XT, 4, 1>(x, wt, N, K, G, y, s);
     case 5: return qmv1_launch<BITS, XT, 5, 1>(x, wt, N, K, G, y, s);
     case 6: return qmv1_launch<BITS, XT, 6, 1>(x, wt, N, K, G, y, s);
-    case 7: return qmv1_launch<BITS, XT, 7, 1>(x, wt, N, K, G, y, s);
+    case 7: return qmv1_launch<BITS, XT, 7, 1, 8>(x, wt, N, K, G, y, s);
     case 8: return qmv1_launch<BITS, XT, 8, 1>(x, wt, N, K, G, y, s);
   }
   return hipErrorInvalidValue;

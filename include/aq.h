@@ -147,6 +147,15 @@ aq_status aq_qmv(const void *x, aq_dtype x_dtype, int64_t M, const uint32_t *cod
                  const uint16_t *scales, const uint16_t *biases, int64_t N, int64_t K,
                  int group_size, int bits, void *y, void *stream);
 
+/* Which kernel aq_qmv (and aq_quantized_matmul for M <= 8) launches for this
+ * shape, as text: the kernel name and its compile-time shape (for reports and
+ * profiles), written to buf (host memory, len bytes, always NUL-terminated).
+ * Returns the length of the full text as snprintf does, or -1 for arguments
+ * aq_qmv would reject.  For 2 <= M <= 8 it may query the current device's
+ * compute-unit count. */
+int aq_qmv_describe(int64_t M, int64_t N, int64_t K, int group_size, int bits, aq_dtype x_dtype,
+                    char *buf, int len);
+
 /* Quantized matrix-matrix product for prefill ("Quantization", metalworking,
  * QMM bullet): same operation and layouts as aq_qmv for any M >= 1.  Weight
  * tiles are dequantized to x_dtype (rounded to nearest even, the value

@@ -145,6 +145,22 @@ def test_quantize_dequantize_argument_errors(lib):
     assert d(codes=MIS) == ALIGN
 
 
+def test_qmv_describe(lib):
+    d = aq.aq_qmv_describe
+    assert d(1, 4096, 4096, 64, 4).startswith("qmv1_kernel<BITS=4, f16, CPL=2")
+    assert d(1, 14336, 4096, 64, 4) != d(1, 1024, 4096, 64, 4)
+    assert "CPL=7" in d(1, 4096, 14336, 64, 4, "bf16")
+    assert d(4, 14336, 4096, 64, 4, "bf16").startswith("qmvm_kernel<bf16, BITS=4")
+    assert d(3, 100, 256, 64, 3).startswith("qmv vector kernel")
+    buf = ctypes.create_string_buffer(8)
+    n = lib.aq_qmv_describe(1, 4096, 4096, 64, 4, F16, buf, 8)
+    assert n > 8 and len(buf.value) == 7  # truncated, NUL-terminated
+    for bad in (dict(M=0), dict(M=9), dict(K=100), dict(bits=1)):
+        k = dict(M=1, K=4096, bits=4)
+        k.update(bad)
+        assert lib.aq_qmv_describe(k["M"], 64, k["K"], 64, k["bits"], F16, buf, 8) == -1
+
+
 def test_quantize_mse_argument_errors(lib):
     q = lambda **k: lib.aq_quantize_mse(k.get("w", P), F32, 4, k.get("K", 64), 64, k.get("bits", 4),
                                         k.get("steps", 20), P, P, k.get("biases", P), None)
