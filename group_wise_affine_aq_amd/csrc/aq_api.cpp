@@ -182,7 +182,7 @@ int aq_qmv_describe(int64_t M, int64_t N, int64_t K, int group_size, int bits, a
   }
   if (aq::qmvm_supported((int)M, bits, N, K, group_size)) {
     int R, W, XR;
-    aq::qmvm_shape((int)M, N, K, group_size, R, W, XR);
+    aq::qmvm_shape((int)M, bits, N, K, group_size, R, W, XR);
     return snprintf(buf, (size_t)len, "qmvm_kernel<%s, BITS=%d, W=%d, G=%d, XR=%d, R=%d>", xt,
                     bits, W, group_size, XR, R);
   }

@@ -39,7 +39,7 @@ hipError_t launch_qmv(const void *x, int x_dtype, int M, const uint32_t *codes,
 // 8-bit codes); qmvm_supported says which shapes it takes
 bool qmvm_supported(int M, int bits, int64_t N, int64_t K, int G);
 // launch shapes the kernels use (also reported by aq_qmv_describe)
-void qmvm_shape(int M, int64_t N, int64_t K, int G, int &R, int &W, int &XR);
+void qmvm_shape(int M, int bits, int64_t N, int64_t K, int G, int &R, int &W, int &XR);
 void qmv1_shape(int64_t N, int64_t K, int &cpl, int &ud, int &w);
 hipError_t launch_qmvm(const void *x, int x_dtype, int M, const uint32_t *codes,
                        const uint16_t *scales, const uint16_t *biases, int64_t N, int64_t K, int G,

@@ -587,13 +587,14 @@ bool qmvm_supported(int M, int bits, int64_t N, int64_t K, int G) {
          16 * K * 2 <= 0x7FFFFFFF && qmvm_lds_bytes(16, 1, K, G) <= kMaxStagedLds;
 }
 
-void qmvm_shape(int M, int64_t N, int64_t K, int G, int &R, int &W, int &XR) {
+void qmvm_shape(int M, int bits, int64_t N, int64_t K, int G, int &R, int &W, int &XR) {
   // Tall matrices: 2 blocks of 16 rows per workgroup (half the x loads per
   // weight byte) with K split over 8 waves.  Otherwise one block, K split
   // over W waves so that the grid has about four waves per SIMD (each wave
   // then runs a few steps).  Measured on the MI355X at N x K = 14336 x 4096
   // and 4096 x 14336, M = 2..8: more blocks per workgroup leave too few
-  // waves, deeper load pipelines gain nothing.
+  // waves, deeper load pipelines gain nothing; 8-bit steps carry twice the
+  // bytes and run best with half the waves.
   const int64_t target = 4 * 4 * (int64_t)device_cus();
   R = N >= 8192 && qmvm_lds_bytes(8, 2, K, G) <= kMaxStagedLds ? 2 : 1;
   const int64_t rowblocks = (N + 16 * R - 1) / (16 * R);
@@ -601,6 +602,7 @@ void qmvm_shape(int M, int64_t N, int64_t K, int G, int &R, int &W, int &XR) {
              : rowblocks * 2 >= target ? 2
              : rowblocks * 4 >= target ? 4
              : rowblocks * 8 >= target ? 8 : 16;
+  if (bits == 8 && W > 2) W /= 2;
   XR = M <= 4 ? 4 : 8;
 }
 
@@ -608,7 +610,7 @@ hipError_t launch_qmvm(const void *x, int x_dtype, int M, const uint32_t *codes,
                        const uint16_t *scales, const uint16_t *biases, int64_t N, int64_t K, int G,
                        int bits, void *y, hipStream_t s) {
   int R, W, XR;
-  qmvm_shape(M, N, K, G, R, W, XR);
+  qmvm_shape(M, bits, N, K, G, R, W, XR);
 #define AQ_QMVM_W(T, B, XR, RR) \
   switch (W) { \
     case 2: return qmvm_go<T, B, 2, XR, RR>(x, M, codes, scales, biases, N, K, G, y, s); \
@@ -617,8 +619,10 @@ hipError_t launch_qmvm(const void *x, int x_dtype, int M, const uint32_t *codes,
     default: return qmvm_go<T, B, 16, XR, RR>(x, M, codes, scales, biases, N, K, G, y, s); \
   }
 #define AQ_QMVM_R(T, B, XR) \
-  if (R == 2) { return qmvm_go<T, B, 8, XR, 2>(x, M, codes, scales, biases, N, K, G, y, s); } \
-  else { AQ_QMVM_W(T, B, XR, 1) }
+  if (R == 2) { \
+    if (W == 8) return qmvm_go<T, B, 8, XR, 2>(x, M, codes, scales, biases, N, K, G, y, s); \
+    return qmvm_go<T, B, 4, XR, 2>(x, M, codes, scales, biases, N, K, G, y, s); \
+  } else { AQ_QMVM_W(T, B, XR, 1) }
 #define AQ_QMVM(T) \
   if (bits == 4) { \
     if (XR == 4) { AQ_QMVM_R(T, 4, 4) } else { AQ_QMVM_R(T, 4, 8) } \
