@@ -57,9 +57,10 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kStepK = 128;  // k per step: 4 chunks
-// steps of loads in flight per wave
+// steps of loads in flight per wave (measured: a third step helps 8-bit
+// codes, whose steps are twice as long, and slows 4-bit ones)
 template <int BITS>
-constexpr int kDepth = 2;
+constexpr int kDepth = BITS == 8 ? 3 : 2;
 // a buffer offset past every resource (sizes are clamped to 2^31 - 1): the
 // load returns zeros without a memory access
 constexpr uint32_t kOutside = 0x80000000u;
@@ -310,6 +311,8 @@ struct MBlock {
     }
   }
 
+  // FULL: the step lies inside K (no group past its end to skip)
+  template <bool FULL>
   __device__ void compute(int c0, Step &st, f32x4v (&acc)[R], uint32_t vmask, uint32_t vmagic,
                           uint4 ones) const {
     const float off = mm_traits<XT, BITS>::off;
@@ -335,7 +338,7 @@ struct MBlock {
     for (int t = 0; t < 4 / NXL; ++t) xp[t] = BITS == 4 ? permute_x(st.xl[t]) : st.xl[t];
 #pragma unroll
     for (int q = 0; q < NG; ++q) {
-      if (c0 + q * CPG >= c_end) break;  // past K (uniform)
+      if (!FULL && c0 + q * CPG >= c_end) break;  // past K (uniform)
       f32x4v xg = (f32x4v){0.f, 0.f, 0.f, 0.f}, pg[R];
 #pragma unroll
       for (int b = 0; b < R; ++b) pg[b] = (f32x4v){0.f, 0.f, 0.f, 0.f};
@@ -393,13 +396,25 @@ struct MBlock {
     const uint4 ones = make_uint4(vones, vones, vones, vones);
 #pragma unroll
     for (int b = 0; b < R; ++b) acc[b] = (f32x4v){0.f, 0.f, 0.f, 0.f};
-    for (int c0 = c_beg; c0 < c_end; c0 += 4 * D) {
+    // steady state: all D buffered steps are whole steps inside the range, so
+    // the body has no branch (a branch around a step makes the compiler's
+    // load-counter bookkeeping wait for later steps' loads as well)
+    // (the scheduling barriers keep each refill where it is issued: sunk to
+    // the end of the body, the loads would arrive a step late)
+    int c0 = c_beg;
+    for (; c0 + 4 * D <= c_end; c0 += 4 * D) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
-        if (c0 + 4 * d < c_end) compute(c0 + 4 * d, st[d], acc, vmask, vmagic, ones);
+        compute<true>(c0 + 4 * d, st[d], acc, vmask, vmagic, ones);
+        __builtin_amdgcn_sched_barrier(0);
         load(c0 + 4 * (d + D), st[d]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+    // the last D steps or fewer (the final one may end past K)
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+      if (c0 + 4 * d < c_end) compute<false>(c0 + 4 * d, st[d], acc, vmask, vmagic, ones);
   }
 };
 
