@@ -55,6 +55,17 @@ typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8v __attribute__((ext_vector_type(8)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt immediate: at most n vector-memory operations outstanding (gfx9
+// encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima)
+constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4) | (15 << 8); }
+
+// LDS entries of one staged array (scales or biases) of `rows` rows: whole
+// 512-entry blocks, the unit one wave's 16-byte-per-lane copy fills
+__host__ __device__ constexpr int sb_entries(int rows, int64_t gpr) {
+  return (int)(((rows * gpr + 511) >> 9) << 9);
+}
 
 constexpr int kStepK = 128;  // k per step: 4 chunks
 // steps of loads in flight per wave (measured: a third step helps 8-bit
@@ -225,9 +236,9 @@ struct MBlock {
   }
 
   __amdgpu_buffer_rsrc_t rw, rx;
-  const uint16_t *sbl;  // LDS: [2][16 R][gpr] scales, biases of the rows
+  const uint16_t *sbl;  // LDS: scales [16 R][gpr], then at sbo the biases
   int64_t K, wpr, gpr;
-  int nch, n16, h, c_beg, c_end;
+  int nch, n16, h, c_beg, c_end, sbo;
   // per-lane parts of the load offsets (the step's part is a scalar offset):
   // codes of block b; x of load t, and the chunk of its slot past c0
   uint32_t wv[R], xb[4 / NXL];
@@ -244,6 +255,7 @@ struct MBlock {
     rw = mk_rsrc(codes_rows, nrows * wpr * 4);
     rx = rx_;
     sbl = sbl_;
+    sbo = sb_entries(ROWS, gpr);
     // this wave's K range, whole steps of 4 chunks (each a whole number of groups)
     c_beg = wave * (kw >> 5);
     c_end = c_beg + (kw >> 5) < nch ? c_beg + (kw >> 5) : nch;
@@ -265,33 +277,46 @@ struct MBlock {
     }
   }
 
-  // scales and biases of the rows (one contiguous, 16-byte aligned range
-  // each) to LDS with 16-byte loads; a load that crosses the end of the valid
-  // rows reads as zero as a whole, so whole units inside them first, then
-  // 2-byte loads, zeros past them.  The caller synchronizes.
+  // Scales and biases of the rows (one contiguous, 16-byte aligned range
+  // each) to LDS with loads that write LDS directly: one instruction per wave
+  // copies a block of 64 16-byte units (units past the valid rows read zero;
+  // each array's LDS area is whole blocks).  Nothing lands in registers, so
+  // the caller can issue its step loads behind these and wait for just these
+  // (stage_sb_wait) before the barrier.
   static __device__ void stage_sb(const uint16_t *scales_rows, const uint16_t *biases_rows,
-                                  int64_t nrows, int64_t gpr_, uint16_t *sb) {
+                                  int64_t nrows, int64_t gpr_, uint16_t *sb, int wave, int lane) {
     const __amdgpu_buffer_rsrc_t rs = mk_rsrc(scales_rows, nrows * gpr_ * 2);
     const __amdgpu_buffer_rsrc_t rb = mk_rsrc(biases_rows, nrows * gpr_ * 2);
-    const int valid = (int)(nrows * gpr_), total = ROWS * (int)gpr_;
-    const int full = valid >> 3;
-    for (int i = threadIdx.x; i < full; i += 64 * W) {
-      const u32x4v vs = __builtin_amdgcn_raw_buffer_load_b128(rs, i * 16, 0, 0);
-      const u32x4v vb = __builtin_amdgcn_raw_buffer_load_b128(rb, i * 16, 0, 0);
-      *reinterpret_cast<u32x4v *>(sb + i * 8) = vs;
-      *reinterpret_cast<u32x4v *>(sb + total + i * 8) = vb;
-    }
-    for (int e = full * 8 + threadIdx.x; e < total; e += 64 * W) {
-      const bool in = e < valid;
-      sb[e] = in ? (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rs, e * 2, 0, 0) : (uint16_t)0;
-      sb[total + e] = in ? (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rb, e * 2, 0, 0) : (uint16_t)0;
+    const int pad = sb_entries(ROWS, gpr_);
+    for (int blk = wave; blk < (pad >> 9); blk += W) {
+      const int off = (blk * 64 + lane) * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(sb + blk * 512), 16, off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void *)(sb + pad + blk * 512), 16, off, 0,
+                                               0, 0);
     }
   }
 
-  // The step at chunk c0.  A step past the wave's range reads outside every
-  // resource (zeros, no memory access).  In a step that ends past c_end (the
-  // end of K) the codes past it read the next row or zeros; their x is zero
-  // (its loads are checked per slot), so they add nothing.
+  // After the staging and `later` further loads of this thread: wait for the
+  // staging, then redo the one unit that straddles the end of the valid rows
+  // (a 16-byte load past the end reads zero as a whole), entry by entry.
+  // The caller synchronizes.
+  template <int later>
+  static __device__ void stage_sb_wait(const uint16_t *scales_rows, const uint16_t *biases_rows,
+                                       int64_t nrows, int64_t gpr_, uint16_t *sb) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(later));
+    const int valid = (int)(nrows * gpr_);
+    if (valid & 7) {  // uniform: only a workgroup with a partial block of rows
+      const __amdgpu_buffer_rsrc_t rs = mk_rsrc(scales_rows, nrows * gpr_ * 2);
+      const __amdgpu_buffer_rsrc_t rb = mk_rsrc(biases_rows, nrows * gpr_ * 2);
+      const int pad = sb_entries(ROWS, gpr_);
+      const int e = (valid & ~7) + (int)threadIdx.x;
+      if (threadIdx.x < 8 && e < valid) {
+        sb[e] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rs, e * 2, 0, 0);
+        sb[pad + e] = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rb, e * 2, 0, 0);
+      }
+    }
+  }
+
   __device__ void load(int c0, Step &st) const {
     const uint32_t sw = c0 < c_end ? (uint32_t)c0 * (4 * BITS) : kOutside;
 #pragma unroll
@@ -364,7 +389,7 @@ struct MBlock {
 #pragma unroll
       for (int b = 0; b < R; ++b) {
         const int li = (16 * b + n16) * (int)gpr + (c0 >> GS) + q;
-        const float sc = f16_to_f32(sbl[li]), bi = f16_to_f32(sbl[ROWS * (int)gpr + li]);
+        const float sc = f16_to_f32(sbl[li]), bi = f16_to_f32(sbl[sbo + li]);
         const float bo = __builtin_fmaf(-off, sc, bi);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -380,11 +405,17 @@ struct MBlock {
   // some paths would make the in-order load counter wait for all in flight;
   // past the wave's range the offset lies outside the resource, so the load
   // returns zeros and touches no memory.
+  // loads one prologue issues per thread
+  static constexpr int kStepLoads = R * (BITS / 4) + 4 / NXL;
+
   template <int D>
   __device__ void prologue(uint32_t xro, Step (&st)[D]) {
     set_x(xro);
 #pragma unroll
-    for (int d = 0; d < D; ++d) load(c_beg + 4 * d, st[d]);
+    for (int d = 0; d < D; ++d) {
+      load(c_beg + 4 * d, st[d]);
+      __builtin_amdgcn_sched_barrier(0);  // keep the steady-state load order
+    }
   }
 
   // partial sums of this wave's K range; lane (n16, h) gets in acc[b] output
@@ -421,7 +452,7 @@ struct MBlock {
 // LDS of a workgroup: the staged scales and biases, and afterwards (behind a
 // barrier) the waves' partial sums in the same space
 inline size_t qmvm_lds_bytes(int W, int R, int64_t K, int G) {
-  const size_t sb = (size_t)2 * 16 * R * (K / G) * 2, part = (size_t)W * 16 * R * 8 * 4;
+  const size_t sb = (size_t)2 * sb_entries(16 * R, K / G) * 2, part = (size_t)W * 16 * R * 8 * 4;
   return sb > part ? sb : part;
 }
 
@@ -467,8 +498,12 @@ __global__ __launch_bounds__(64 * W) void qmvm_kernel(const uint16_t *__restrict
   const uint32_t xro = (uint32_t)((int64_t)((lane & 15) % XR) * K * 2);
   constexpr int D = kDepth<BITS>;
   typename Blk::Step st[D];
+  // staging first, then the first steps' loads: one round trip covers both
+  Blk::stage_sb(scales + row0 * gpr, biases + row0 * gpr, nrows, gpr, lds, wave, lane);
+  __builtin_amdgcn_sched_barrier(0);
   blk.template prologue<D>(xro, st);
-  Blk::stage_sb(scales + row0 * gpr, biases + row0 * gpr, nrows, gpr, lds);
+  Blk::template stage_sb_wait<D * Blk::kStepLoads>(scales + row0 * gpr, biases + row0 * gpr,
+                                                   nrows, gpr, lds);
   __syncthreads();
   f32x4v acc[R];
   blk.template finish<D>(st, acc);
@@ -523,7 +558,10 @@ __global__ __launch_bounds__(64 * W) void gather_qmvm_kernel(
   Blk blk;
   blk.setup(codes + e * wpe + row0 * (K >> 5) * BITS, nrows, K, kw, wave, lane, sbl,
             mk_rsrc(x, T * K * 2));
-  Blk::stage_sb(scales + (e * N + row0) * gpr, biases + (e * N + row0) * gpr, nrows, gpr, sbl);
+  Blk::stage_sb(scales + (e * N + row0) * gpr, biases + (e * N + row0) * gpr, nrows, gpr, sbl,
+                wave, lane);
+  Blk::template stage_sb_wait<0>(scales + (e * N + row0) * gpr, biases + (e * N + row0) * gpr,
+                                 nrows, gpr, sbl);
   constexpr int D = kDepth<BITS>;
   for (int64_t t0 = 0; t0 < total; t0 += kGTile) {
     __syncthreads();  // also publishes the staged scales before the first batch
@@ -572,6 +610,11 @@ hipError_t qmvm_go(const void *x, int M, const uint32_t *codes, const uint16_t *
   return hipGetLastError();
 }
 
+// staged scales and biases of a gather workgroup of R blocks
+inline size_t gather_lds_bytes(int R, int64_t K, int G) {
+  return (size_t)2 * sb_entries(16 * R, K / G) * 2;
+}
+
 template <typename XT, int BITS, int R>
 hipError_t gather_go(const void *x, int64_t T, const uint32_t *codes, const uint16_t *scales,
                      const uint16_t *biases, int64_t E, int64_t N, int64_t K,
@@ -582,7 +625,7 @@ hipError_t gather_go(const void *x, int64_t T, const uint32_t *codes, const uint
   const int64_t blocks = (N + 16 * R - 1) / (16 * R);
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks, (unsigned)E), block(64 * W);
-  const size_t lds = (size_t)2 * 16 * R * (K / G) * 2;
+  const size_t lds = gather_lds_bytes(R, K, G);
   switch (G) {
     case 32: hipLaunchKernelGGL((gather_qmvm_kernel<XT, BITS, W, 0, R>), grid, block, lds, s, (const uint16_t *)x, T, codes, scales, biases, E, N, K, ids, topk, kw, (uint16_t *)y); break;
     case 64: hipLaunchKernelGGL((gather_qmvm_kernel<XT, BITS, W, 1, R>), grid, block, lds, s, (const uint16_t *)x, T, codes, scales, biases, E, N, K, ids, topk, kw, (uint16_t *)y); break;
@@ -652,8 +695,6 @@ hipError_t launch_qmvm(const void *x, int x_dtype, int M, const uint32_t *codes,
   return hipErrorInvalidValue;
 }
 
-// staged scales and biases of a gather workgroup of R blocks
-inline size_t gather_lds_bytes(int R, int64_t K, int G) { return (size_t)2 * 16 * R * (K / G) * 2; }
 
 bool gather_qmvm_supported(int bits, int64_t K, int G) {
   return (bits == 4 || bits == 8) && K >= 32 && gather_lds_bytes(1, K, G) <= kMaxStagedLds;
