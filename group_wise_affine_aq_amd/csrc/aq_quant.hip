@@ -74,11 +74,20 @@ __device__ __forceinline__ uint16_t f16_scale_up(double b, double top, int L) {
 }
 
 // nearest grid index, ties to even.  mid(j) = b + (j + 1/2) s separates j, j+1.
+// The binary32 estimate t = (w - b) * rcp(s) of the real (w - b) / s has a
+// relative error below 2^-22 (one rounding in the subtraction, at most one
+// unit in the last place in v_rcp_f32, one in the product), so below 2^-14
+// absolutely for t <= 255: when t is farther than 2^-10 from every
+// half-integer, rint(t) clamped to [0, L] is already the answer; only the
+// rest take the exact binary64 tests.
 __device__ __forceinline__ uint32_t nearest_code(float w, double b, double s, float bf, float rs,
                                                  int L) {
   if (s == 0.0) return 0;
-  int q = (int)__builtin_rintf((w - bf) * rs);  // candidate, within one of the answer
+  const float t = (w - bf) * rs;
+  const float r = __builtin_rintf(t);
+  int q = (int)r;  // candidate, within one of the answer (saturating conversion)
   q = q < 0 ? 0 : (q > L ? L : q);
+  if (__builtin_fabsf(t - r) <= 0.5f - 0x1p-10f) return (uint32_t)q;
   const double wd = (double)w;
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
