@@ -257,6 +257,22 @@ __global__ __launch_bounds__(256) void quantize_mse_kernel(const void *__restric
   for (int j = 0; j < BITS; ++j) dst[j] = (uint8_t)(best_packed >> (8 * j));
 }
 
+// two binary32 values rounded to nearest even into fp16 or bf16 and packed
+// (v_cvt_pk_bf16_f32 for bf16; the values here are finite, where it agrees
+// bit for bit with the integer rounding used elsewhere)
+template <int ODT>
+__device__ __forceinline__ uint32_t pack_rne(float lo, float hi) {
+  if constexpr (ODT == X_BF16) {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    const b2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  } else {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+}
+
 // One thread per 32-code chunk of an output row.  With GATHER (quantized
 // embedding, "Tutorial 10: Quantization", s.6) output row t is table row
 // ids[t] (N table rows, T output rows); an id outside [0, N) gives a zero row.
@@ -269,8 +285,17 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint32_t *__restr
                                                          void *__restrict__ out) {
   const int64_t cpr = K >> 5;  // chunks per row
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (GATHER ? T : N) * cpr) return;
-  const int64_t t = idx / cpr, c = idx - t * cpr;
+  const int64_t total = (GATHER ? T : N) * cpr;
+  if (idx >= total) return;
+  int64_t t, c;
+  if (total <= 0xFFFFFFFFll) {  // uniform: 32-bit division when the index fits
+    const uint32_t t32 = (uint32_t)idx / (uint32_t)cpr;
+    t = t32;
+    c = (int64_t)((uint32_t)idx - t32 * (uint32_t)cpr);
+  } else {
+    t = idx / cpr;
+    c = idx - t * cpr;
+  }
   int64_t n = t;
   bool zero = false;
   if constexpr (GATHER) {
@@ -298,11 +323,7 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint32_t *__restr
   } else {
     uint32_t p[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint32_t lo = ODT == X_F16 ? f32_to_f16_rne(r[2 * j]) : f32_to_bf16_rne(r[2 * j]);
-      const uint32_t hi = ODT == X_F16 ? f32_to_f16_rne(r[2 * j + 1]) : f32_to_bf16_rne(r[2 * j + 1]);
-      p[j] = lo | (hi << 16);
-    }
+    for (int j = 0; j < 16; ++j) p[j] = pack_rne<ODT>(r[2 * j], r[2 * j + 1]);
     uint4 *o = reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out) + e);
 #pragma unroll
     for (int j = 0; j < 4; ++j) o[j] = make_uint4(p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]);
