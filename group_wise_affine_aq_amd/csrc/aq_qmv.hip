@@ -610,39 +610,51 @@ __global__ __launch_bounds__(64 * W) void qmv1_kernel(const uint16_t *__restrict
   uint16_t *obuf = reinterpret_cast<uint16_t *>(smem + (size_t)CP * kChunkLdsBytes) +
                    (size_t)wave * kStreamRound;
 
+  // x loads first, then the first round of weight loads, then the wait for
+  // x: the two round trips overlap.  The first fill is unconditional (a wave
+  // without rows re-reads row N - 1 and stores nothing), so the wait for x
+  // leaves the weight loads in flight on every path; the scheduling
+  // barriers keep that order.
   XStage<XS> xst;
   stage_x_load<BITS, 1, XT, 64 * W, XS>(xr, 1, (int)(K >> 5), CP, xst);
+  __builtin_amdgcn_sched_barrier(0);
   PassData<BITS, 1> buf[D];
+  {
+    const int nu = nunits < kStreamRound ? nunits : kStreamRound;
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int i = d / CPL < nu ? d / CPL : (nu > 0 ? nu - 1 : 0);
+      const int64_t row = gw + (int64_t)i * TW;
+      core.load_pass(buf[d], row < N ? row : N - 1, (d % CPL) * 64 + lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
   uint32_t xv[CPL][16];
   float2 xs[CPL];
+  stage_x_store<BITS, 1, XT, 64 * W, XS>(1, CP, xst, xlds, xsum);
+  __syncthreads();
+  if (nunits == 0) return;
+#pragma unroll
+  for (int p = 0; p < CPL; ++p) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(xlds + ((size_t)j * CP + p * 64 + lane) * 16);
+      xv[p][4 * j] = v.x; xv[p][4 * j + 1] = v.y; xv[p][4 * j + 2] = v.z; xv[p][4 * j + 3] = v.w;
+    }
+    xs[p] = reinterpret_cast<const float2 *>(xsum)[p * 64 + lane];
+  }
   const uint32_t magic = vgpr_const(pairing<BITS, XT>::magic);
-  bool staged = false;
-  for (int u0 = 0; u0 < nunits || !staged; u0 += kStreamRound) {
+  for (int u0 = 0; u0 < nunits; u0 += kStreamRound) {
     const int nu = nunits - u0 < kStreamRound ? nunits - u0 : kStreamRound;
     auto row_of = [&](int i) -> int64_t {
       i = i < nu ? i : nu - 1;  // past the end: harmless re-read of the last row
       return gw + (int64_t)(u0 + i) * TW;
     };
-    if (nu > 0) {
+    if (u0 > 0) {  // the first round was filled above
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         core.load_pass(buf[d], row_of(d / CPL), (d % CPL) * 64 + lane);
         __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    if (!staged) {
-      stage_x_store<BITS, 1, XT, 64 * W, XS>(1, CP, xst, xlds, xsum);
-      __syncthreads();
-      staged = true;
-      if (nunits == 0) return;
-#pragma unroll
-      for (int p = 0; p < CPL; ++p) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint4 v = *reinterpret_cast<const uint4 *>(xlds + ((size_t)j * CP + p * 64 + lane) * 16);
-          xv[p][4 * j] = v.x; xv[p][4 * j + 1] = v.y; xv[p][4 * j + 2] = v.z; xv[p][4 * j + 3] = v.w;
-        }
-        xs[p] = reinterpret_cast<const float2 *>(xsum)[p * 64 + lane];
       }
     }
     float acc = 0.f;
