@@ -36,14 +36,21 @@
 //  * x is read straight from global memory (it stays in L2), one 16-byte load
 //    per lane carrying two chunks (M <= 8) or four (M <= 4) in the lanes of
 //    A-operand rows that only feed discarded output rows, moved into place by
-//    a DPP row rotation; its pairs are permuted to the order the unpack
-//    produces (code e with code e+4);
+//    a DPP row rotation; for 4-bit codes its pairs are permuted once per load
+//    to the order the unpack produces (code e with code e+4);
 //  * the workgroup's scales and biases (16 R whole rows, one contiguous range
-//    each) are staged in LDS once with 16-byte loads: per-group 2-byte
-//    loads from every lane cost more than all the rest of the kernel;
-//  * a workgroup of W waves covers 16 R rows; its waves split K and add their
-//    partial sums through LDS at the end (W chosen per shape so that the
-//    grid fills the chip with waves that each keep loads in flight).
+//    each) are staged in LDS once, by loads that write LDS directly, issued
+//    ahead of the first steps' loads: per-group 2-byte loads from every lane
+//    cost more than all the rest of the kernel;
+//  * a workgroup of W waves covers R blocks of 16 rows, every wave all R of
+//    them (each x load and Sum-x MFMA serves R blocks); its waves split K and
+//    add their partial sums through LDS at the end (R and W chosen per shape,
+//    see qmvm_shape);
+//  * step offsets are scalar, steps past a wave's range read outside every
+//    buffer resource (zeros, no memory access) so every load is issued
+//    unconditionally, and the steady-state loop is branch-free with its
+//    refills pinned in place (the in-order load counter then waits only for
+//    the step being computed).
 #include "aq_device.hpp"
 #include "aq_internal.hpp"
 
@@ -190,8 +197,8 @@ struct MStep {
   uint4 xl[4 / NXL];   // x loads of the step, NXL MFMA slots each (natural pair order)
 };
 
-// lane l of a row of 16 receives the value of lane (l + 16 - k) % 16 ... i.e. a
-// rotation of each 16-lane row by k (DPP row_ror)
+// DPP row_ror: lane l of each row of 16 lanes receives the value of lane
+// (l + 16 - K16) % 16 of the same row
 template <int K16>
 __device__ __forceinline__ uint4 row_ror(uint4 v) {
   if constexpr (K16 == 0) return v;
