@@ -30,7 +30,8 @@ first part).  The JSON line also carries:
 Per decode shape the line also carries the time of a plain streaming read of
 the same bytes (same cold rotation and timing), a measured second denominator.
   specdec, moe  the M = 2..8 matrix-vector kernels (bf16 x, [14336, 4096] and
-                [4096, 14336] at 4/64 and 8/128) and the MoE gather kernel
+                [4096, 14336] at 4/64 and 8/128; also M = 16 and 64, sliced
+                few-row kernel) and the MoE gather kernel
                 (32 tokens, top-6 of 64 experts), % of HBM per launch on cold
                 weights; plus the matrix-core gather on the same experts at
                 prefill size (2048 tokens, top-6), TFLOP/s;
@@ -421,12 +422,14 @@ def _graph_us(torch, stream, launches, reps=5):
 
 
 def _specdec(aq, inputs, dev, stream):
-    """Matrix-vector kernels for M = 2..8 rows (bf16), each launch on a cold
-    copy of the weights (>= 1 GiB rotated), per-launch time in a graph."""
+    """Matrix-vector kernels for M = 2..8 rows (bf16), and the same matrices
+    at 16 and 64 rows, each launch on a cold copy of the weights (>= 1 GiB
+    rotated), per-launch time in a graph."""
     import torch
     cfg = inputs.WORKLOADS["specdec"]
     wid = inputs.WORKLOAD_ID["specdec"]
-    out = {"workload": "spec-decode QMV, x bf16 [M, K], M in {2,3,4,6,8}, cold weights"}
+    out = {"workload": "spec-decode QMV, x bf16 [M, K], M in {2,3,4,6,8}; batched decode "
+                       "M in {16, 64}; cold weights"}
     for (N, K) in cfg["shapes"]:
         w = inputs.weights_device(N, K, device=dev, seed=0, key=(wid,))
         for bits, g in zip(cfg["bits"], cfg["group_size"]):
@@ -436,7 +439,7 @@ def _specdec(aq, inputs, dev, stream):
             sets = [packed] + [tuple(t.clone() for t in packed) for _ in range(copies - 1)]
             ceil_us = _read_ceiling_us(aq, torch, wbytes, stream)
             rows = {}
-            for M in cfg["M"]:
+            for M in cfg["M"] + cfg["M_batch"]:
                 x = inputs.activations_device(M, K, "bf16", device=dev, seed=0, key=(wid, N, M))
                 y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
                 fs = [lambda c=c, s_=s_, b=b: aq.aq_quantized_matmul(x, c, s_, b, g, bits, y=y)

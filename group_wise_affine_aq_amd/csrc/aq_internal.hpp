@@ -36,8 +36,12 @@ hipError_t launch_qmv(const void *x, int x_dtype, int M, const uint32_t *codes,
                       int bits, void *y, hipStream_t s);
 
 // y[M, N] = x[M, K] @ W^T for a few rows on the matrix cores (4-bit and
-// 8-bit codes); qmvm_supported says which shapes it takes
+// 8-bit codes; more than 16 rows run as slices of 16); qmvm_supported says
+// which shapes it takes, qmvm_preferred whether it beats the tiled matmul
+// kernel at M > 8
+constexpr int kQmvmMaxRows = 256;
 bool qmvm_supported(int M, int bits, int64_t N, int64_t K, int G);
+bool qmvm_preferred(int64_t M, int bits, int64_t N, int64_t K, int G);
 // launch shapes the kernels use (also reported by aq_qmv_describe)
 void qmvm_shape(int M, int bits, int64_t N, int64_t K, int G, int &R, int &W, int &XR);
 void qmv1_shape(int64_t N, int64_t K, int &cpl, int &ud, int &w);

@@ -458,45 +458,61 @@ struct MBlock {
 
 // LDS of a workgroup: the staged scales and biases, and afterwards (behind a
 // barrier) the waves' partial sums in the same space
-inline size_t qmvm_lds_bytes(int W, int R, int64_t K, int G) {
-  const size_t sb = (size_t)2 * sb_entries(16 * R, K / G) * 2, part = (size_t)W * 16 * R * 8 * 4;
+inline size_t qmvm_lds_bytes(int W, int R, int64_t K, int G, int MR = 8) {
+  const size_t sb = (size_t)2 * sb_entries(16 * R, K / G) * 2, part = (size_t)W * 16 * R * MR * 4;
   return sb > part ? sb : part;
 }
 
 // sum the W waves' partial sums (lanes h < 2 hold output rows 0..7) through
 // LDS (part: [W][16 R][8] floats, free for this use); out(n, m, v) receives
 // row n of the 16 R, x row m < 8, value v
-template <int W, int R, typename F>
+// MR: x rows kept (8, or 16 when every lane's 4 rows count)
+template <int W, int R, int MR, typename F>
 __device__ __forceinline__ void reduce_out(float *part, int wave, int lane,
                                            const f32x4v (&acc)[R], F out) {
   const int n16 = lane & 15, h = lane >> 4;
-  if (h < 2) {
+  if (h < MR / 4) {
 #pragma unroll
     for (int b = 0; b < R; ++b)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) part[(wave * 16 * R + 16 * b + n16) * 8 + 4 * h + e] = acc[b][e];
+      for (int e = 0; e < 4; ++e) part[(wave * 16 * R + 16 * b + n16) * MR + 4 * h + e] = acc[b][e];
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < 16 * R * 8; i += 64 * W) {
+  for (int i = threadIdx.x; i < 16 * R * MR; i += 64 * W) {
     float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < W; ++w) v += part[w * 16 * R * 8 + i];
-    out(i >> 3, i & 7, v);
+    for (int w = 0; w < W; ++w) v += part[w * 16 * R * MR + i];
+    out(i / MR, i % MR, v);
   }
 }
 
+// S > 1 (XR = 16): x has up to 16 S rows, run as S slices of 16 rows; the
+// S slices of one block of W rows are consecutive workgroups of one XCD
+// (block b runs on XCD b % 8), so that block is read from HBM once and the
+// other slices find it in that XCD's L2.
 template <typename XT, int BITS, int W, int GS, int XR, int R>
 __global__ __launch_bounds__(64 * W) void qmvm_kernel(const uint16_t *__restrict__ x, int M,
                                                       const uint32_t *__restrict__ codes,
                                                       const uint16_t *__restrict__ scales,
                                                       const uint16_t *__restrict__ biases,
                                                       int64_t N, int64_t K, int kw,
-                                                      uint16_t *__restrict__ y) {
+                                                      uint16_t *__restrict__ y, int S) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // [2][16 R][gpr]; then partials
   typedef MBlock<XT, BITS, W, GS, XR, R> Blk;
+  constexpr int MR = XR == 16 ? 16 : 8;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t row0 = (int64_t)blockIdx.x * Blk::ROWS;
+  int64_t rb = blockIdx.x;
+  if (S > 1) {
+    const int64_t k = blockIdx.x >> 3;
+    const int sl = (int)(k % S);
+    rb = (k / S) * 8 + (blockIdx.x & 7);
+    x += (int64_t)sl * 16 * K;
+    y += (int64_t)sl * 16 * N;
+    M = M - 16 * sl < 16 ? M - 16 * sl : 16;
+  }
+  const int64_t row0 = rb * Blk::ROWS;
+  if (row0 >= N) return;  // padding of the slice mapping (uniform, before any barrier)
   const int64_t nrows = N - row0 < Blk::ROWS ? N - row0 : Blk::ROWS;
   const int64_t gpr = (K >> 5) >> GS;
   Blk blk;
@@ -515,7 +531,7 @@ __global__ __launch_bounds__(64 * W) void qmvm_kernel(const uint16_t *__restrict
   f32x4v acc[R];
   blk.template finish<D>(st, acc);
   __syncthreads();  // every wave is done with the staged scales
-  reduce_out<W, R>(reinterpret_cast<float *>(lds), wave, lane, acc, [&](int nn, int m, float v) {
+  reduce_out<W, R, MR>(reinterpret_cast<float *>(lds), wave, lane, acc, [&](int nn, int m, float v) {
     if (m < M && row0 + nn < N) y[(int64_t)m * N + row0 + nn] = xtraits<XT>::from_f32(v);
   });
 }
@@ -590,7 +606,7 @@ __global__ __launch_bounds__(64 * W) void gather_qmvm_kernel(
       blk.template prologue<D>(xro, st);
       f32x4v acc[R];
       blk.template finish<D>(st, acc);
-      reduce_out<W, R>(part, wave, lane, acc, [&](int nn, int mm, float v) {
+      reduce_out<W, R, 8>(part, wave, lane, acc, [&](int nn, int mm, float v) {
         if (b0 + mm < n && row0 + nn < N)
           y[(t0 + list[b0 + mm]) * N + row0 + nn] = xtraits<XT>::from_f32(v);
       });
@@ -605,13 +621,15 @@ hipError_t qmvm_go(const void *x, int M, const uint32_t *codes, const uint16_t *
   const int64_t steps = (K + kStepK - 1) / kStepK;
   const int kw = (int)((steps + W - 1) / W) * kStepK;  // k per wave, whole steps
   const int64_t blocks = (N + 16 * R - 1) / (16 * R);
-  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)blocks), block(64 * W);
-  const size_t lds = qmvm_lds_bytes(W, R, K, G);
+  const int S = XR == 16 ? (M + 15) / 16 : 1;  // slices of 16 x rows
+  const int64_t grid_blocks = S > 1 ? (blocks + 7) / 8 * 8 * S : blocks;
+  if (grid_blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)grid_blocks), block(64 * W);
+  const size_t lds = qmvm_lds_bytes(W, R, K, G, XR == 16 ? 16 : 8);
   switch (G) {
-    case 32: hipLaunchKernelGGL((qmvm_kernel<XT, BITS, W, 0, XR, R>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y); break;
-    case 64: hipLaunchKernelGGL((qmvm_kernel<XT, BITS, W, 1, XR, R>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y); break;
-    case 128: hipLaunchKernelGGL((qmvm_kernel<XT, BITS, W, 2, XR, R>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y); break;
+    case 32: hipLaunchKernelGGL((qmvm_kernel<XT, BITS, W, 0, XR, R>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y, S); break;
+    case 64: hipLaunchKernelGGL((qmvm_kernel<XT, BITS, W, 1, XR, R>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y, S); break;
+    case 128: hipLaunchKernelGGL((qmvm_kernel<XT, BITS, W, 2, XR, R>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y, S); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -648,11 +666,36 @@ constexpr size_t kMaxStagedLds = 64 * 1024;
 }  // namespace
 
 bool qmvm_supported(int M, int bits, int64_t N, int64_t K, int G) {
-  return M >= 2 && M <= 8 && (bits == 4 || bits == 8) && N >= 1 && K >= 32 &&
-         16 * K * 2 <= 0x7FFFFFFF && qmvm_lds_bytes(16, 1, K, G) <= kMaxStagedLds;
+  return M >= 2 && M <= kQmvmMaxRows && (bits == 4 || bits == 8) && N >= 1 && K >= 32 &&
+         16 * K * 2 <= 0x7FFFFFFF && qmvm_lds_bytes(16, 1, K, G, 16) <= kMaxStagedLds;
+}
+
+bool qmvm_preferred(int64_t M, int bits, int64_t N, int64_t K, int G) {
+  // Past 8 rows each slice of 16 x rows costs about one few-row pass over W
+  // (11-14 us at 14336 x 4096 or 4096 x 14336, 4-bit and 8-bit, on the
+  // MI355X), while the tiled kernel computes whole 256 x 224 tiles: at most
+  // 256 rows it runs ceil(N / 224) workgroups for the time of one tile
+  // (115 us at K = 4096, 345 us at K = 14336, the chip a quarter full or
+  // less).  Measured crossover: 128 < M < 192 at N = 14336; with fewer
+  // workgroups than a quarter of the compute units the slices win to 256.
+  if (M > kQmvmMaxRows || !qmvm_supported((int)M, bits, N, K, G)) return false;
+  const int64_t qmm_wgs = (M + 255) / 256 * ((N + 223) / 224);
+  return M <= 128 || qmm_wgs * 4 < device_cus();
 }
 
 void qmvm_shape(int M, int bits, int64_t N, int64_t K, int G, int &R, int &W, int &XR) {
+  XR = M <= 4 ? 4 : M <= 8 ? 8 : 16;
+  const int64_t S = (M + 15) / 16;  // slices of 16 x rows (XR = 16)
+  if (XR == 16) {
+    // 16 rows per slot: two blocks of 16 rows over 4 waves whenever that
+    // still gives a workgroup per compute unit (measured best at
+    // 14336 x 4096 from M = 9 and at 4096 x 14336 from M = 17, both widths)
+    if ((N + 31) / 32 * S >= device_cus() && qmvm_lds_bytes(4, 2, K, G, 16) <= kMaxStagedLds) {
+      R = 2;
+      W = 4;
+      return;
+    }
+  }
   // Tall matrices: 2 blocks of 16 rows per workgroup (half the x loads per
   // weight byte) with K split over 8 waves.  Otherwise one block, K split
   // over W waves so that the grid has about four waves per SIMD (each wave
@@ -661,14 +704,14 @@ void qmvm_shape(int M, int bits, int64_t N, int64_t K, int G, int &R, int &W, in
   // waves, deeper load pipelines gain nothing; 8-bit steps carry twice the
   // bytes and run best with half the waves.
   const int64_t target = 4 * 4 * (int64_t)device_cus();
-  R = N >= 8192 && qmvm_lds_bytes(8, 2, K, G) <= kMaxStagedLds ? 2 : 1;
-  const int64_t rowblocks = (N + 16 * R - 1) / (16 * R);
+  R = XR < 16 && N >= 8192 && qmvm_lds_bytes(8, 2, K, G) <= kMaxStagedLds ? 2 : 1;
+  // workgroups: row blocks, times the slices
+  const int64_t rowblocks = (N + 16 * R - 1) / (16 * R) * S;
   W = R == 2 ? 8
              : rowblocks * 2 >= target ? 2
              : rowblocks * 4 >= target ? 4
              : rowblocks * 8 >= target ? 8 : 16;
   if (bits == 8 && W > 2) W /= 2;
-  XR = M <= 4 ? 4 : 8;
 }
 
 hipError_t launch_qmvm(const void *x, int x_dtype, int M, const uint32_t *codes,
@@ -690,9 +733,11 @@ hipError_t launch_qmvm(const void *x, int x_dtype, int M, const uint32_t *codes,
   } else { AQ_QMVM_W(T, B, XR, 1) }
 #define AQ_QMVM(T) \
   if (bits == 4) { \
-    if (XR == 4) { AQ_QMVM_R(T, 4, 4) } else { AQ_QMVM_R(T, 4, 8) } \
+    if (XR == 4) { AQ_QMVM_R(T, 4, 4) } else if (XR == 8) { AQ_QMVM_R(T, 4, 8) } \
+    else { AQ_QMVM_R(T, 4, 16) } \
   } else { \
-    if (XR == 4) { AQ_QMVM_R(T, 8, 4) } else { AQ_QMVM_R(T, 8, 8) } \
+    if (XR == 4) { AQ_QMVM_R(T, 8, 4) } else if (XR == 8) { AQ_QMVM_R(T, 8, 8) } \
+    else { AQ_QMVM_R(T, 8, 16) } \
   }
   if (x_dtype == X_BF16) { AQ_QMVM(bf16_t) }
   if (x_dtype == X_F16) { AQ_QMVM(f16_t) }

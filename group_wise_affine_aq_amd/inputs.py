@@ -17,7 +17,8 @@ the 70B MLP up-projection, an MoE expert stack):
             N(0, 0.02) with round(0.001*N*K) distinct entries scaled by 20;
             4-bit G=64; x fp16 [1, K] ~ N(0, 1)
   specdec   x bf16 [M, K], M in {2,3,4,6,8}; W [14336,4096] and [4096,14336]
-            ~ N(0, 0.02); 4-bit G=64 and 8-bit G=128
+            ~ N(0, 0.02); 4-bit G=64 and 8-bit G=128; also M in {16, 64}
+            (a batch of decoding sequences)
   prefill   X bf16 [2048, 8192] ~ N(0, 1); W [28672, 8192] ~ N(0, 0.02) at
             4-bit G=64, 3-bit G=64 and 2-bit G=32
   moe       64 experts W_e [1408, 2048] ~ N(0, 0.02) 4-bit G=64; x fp16
@@ -39,7 +40,7 @@ WORKLOADS = {
     "decode": dict(shapes=[(4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336)], bits=[4],
                    group_size=[64], M=[1], x_dtype="f16", outliers=True),
     "specdec": dict(shapes=[(14336, 4096), (4096, 14336)], bits=[4, 8], group_size=[64, 128],
-                    M=[2, 3, 4, 6, 8], x_dtype="bf16", outliers=False),
+                    M=[2, 3, 4, 6, 8], M_batch=[16, 64], x_dtype="bf16", outliers=False),
     "prefill": dict(shapes=[(28672, 8192)], bits=[4, 3, 2], group_size=[64, 64, 32], M=[2048],
                     x_dtype="bf16", outliers=False),
     "moe": dict(shapes=[(1408, 2048)], experts=64, tokens=32, topk=6, bits=[4], group_size=[64],

@@ -200,9 +200,13 @@ def test_qmv_parity(aq, bits, M, xdt):
     _assert_close(y, y_ref, A, f"qmv b{bits} M{M} {xdt}")
 
 
-@pytest.mark.parametrize("xdt", ["f16", "bf16"])
-@pytest.mark.parametrize("N,K,G", [(1, 32, 32), (1, 64, 64), (3, 128, 128), (200, 96, 32),
-                                   (129, 2048, 64), (5, 32768, 64)])
+_QMV_SHAPES = [(1, 32, 32), (1, 64, 64), (3, 128, 128), (200, 96, 32), (129, 2048, 64),
+               (5, 32768, 64)]
+
+
+# bf16 only at K >= 2048, where the bound covers a bf16 result's own rounding
+@pytest.mark.parametrize("xdt,N,K,G", [("f16",) + t for t in _QMV_SHAPES] +
+                         [("bf16",) + t for t in _QMV_SHAPES if t[1] >= 2048])
 def test_qmv_shapes(aq, xdt, N, K, G):
     bits = 4
     _, (c, s, b) = _quantized(N, K, G, bits, seed=5)
@@ -213,12 +217,14 @@ def test_qmv_shapes(aq, xdt, N, K, G):
         _assert_close(y, y_ref, A, f"qmv N{N} K{K} M{M}")
 
 
-@pytest.mark.parametrize("xdt", ["f16", "bf16"])
 @pytest.mark.parametrize("bits", [4, 8])
-@pytest.mark.parametrize("G,K", [(32, 2144), (64, 2112), (128, 2176), (32, 96), (64, 64)])
+@pytest.mark.parametrize("xdt,G,K", [(xdt, G, K) for G, K in ((32, 2144), (64, 2112), (128, 2176))
+                                     for xdt in ("f16", "bf16")] + [("f16", 32, 96), ("f16", 64, 64)])
 def test_qmv_few_rows_groups(aq, xdt, bits, G, K):
     """2..8 rows (the matrix-core path) at every group size, K ragged against
-    the 128-code step and the per-wave K split, N ragged against 16-row tiles."""
+    the 128-code step and the per-wave K split, N ragged against 16-row tiles
+    (bf16 only at K >= 2048, where the bound covers a bf16 result's own
+    rounding)."""
     N = 45
     _, (c, s, b) = _quantized(N, K, G, bits, seed=14)
     for M in (2, 4, 6, 8):
@@ -234,10 +240,40 @@ def test_qmv_few_rows_tall(aq, bits, G):
     N, K = 8200, 256
     _, (c, s, b) = _quantized(N, K, G, bits, seed=16)
     for M in (3, 8):
-        xb = inputs.activations(M, K, "bf16", seed=16, key=(bits, G, M))
-        y_ref, A = oracle.matmul(inputs.from_bits(xb, "bf16"), c, s, b, K, G, bits)
-        y = aq.aq_qmv(bits_to_dev(xb, "bf16"), *packed_to_dev(c, s, b), G, bits)
+        xb = inputs.activations(M, K, "f16", seed=16, key=(bits, G, M))
+        y_ref, A = oracle.matmul(inputs.from_bits(xb, "f16"), c, s, b, K, G, bits)
+        y = aq.aq_qmv(bits_to_dev(xb, "f16"), *packed_to_dev(c, s, b), G, bits)
         _assert_close(y, y_ref, A, f"qmv tall b{bits} G{G} M{M}")
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("xdt,G,K", [("f16", 32, 2144), ("bf16", 32, 2144), ("bf16", 64, 2112),
+                                     ("f16", 128, 384), ("f16", 64, 64)])
+def test_matmul_few_rows_sliced(aq, xdt, bits, G, K):
+    """9..64 rows through the dispatcher: the matrix-core few-row kernel with
+    16 rows of x per slot, slices of 16 rows past 16 (a partial last slice),
+    row blocks (14) not a multiple of the 8-block slice mapping, K ragged.
+    bf16 only at K >= 2048, where the bound covers a bf16 result's own
+    rounding (fp16 holds it at any K)."""
+    N = 213
+    _, (c, s, b) = _quantized(N, K, G, bits, seed=21)
+    for M in (9, 12, 16, 17, 31, 40, 64):
+        xb = inputs.activations(M, K, xdt, seed=21, key=(G, K, M, bits))
+        y_ref, A = oracle.matmul(inputs.from_bits(xb, xdt), c, s, b, K, G, bits)
+        y = aq.aq_quantized_matmul(bits_to_dev(xb, xdt), *packed_to_dev(c, s, b), G, bits)
+        _assert_close(y, y_ref, A, f"sliced b{bits} G{G} K{K} M{M} {xdt}")
+
+
+@pytest.mark.parametrize("bits,G", [(4, 64), (8, 128)])
+def test_matmul_few_rows_sliced_tall(aq, bits, G):
+    """Tall matrices (two 16-row blocks per workgroup) at 16..64 rows."""
+    N, K = 8200, 256
+    _, (c, s, b) = _quantized(N, K, G, bits, seed=22)
+    for M in (16, 24, 64):
+        xb = inputs.activations(M, K, "f16", seed=22, key=(bits, G, M))
+        y_ref, A = oracle.matmul(inputs.from_bits(xb, "f16"), c, s, b, K, G, bits)
+        y = aq.aq_quantized_matmul(bits_to_dev(xb, "f16"), *packed_to_dev(c, s, b), G, bits)
+        _assert_close(y, y_ref, A, f"sliced tall b{bits} G{G} M{M}")
 
 
 def test_qmv_unit_vectors(aq):
@@ -308,7 +344,7 @@ def test_qmm_equals_gemm_of_dequantized(aq):
 
 
 # ---- dispatch ----------------------------------------------------------------------------------
-@pytest.mark.parametrize("M", [1, 3, 8, 9, 40])
+@pytest.mark.parametrize("M", [1, 3, 8, 9, 40, 64, 65, 200, 300])
 def test_quantized_matmul_dispatch(aq, M):
     G, bits, N, K, xdt = 64, 4, 100, 640, "f16"
     _, (c, s, b) = _quantized(N, K, G, bits, seed=10)
@@ -330,7 +366,8 @@ def _experts(E, N, K, G, bits, seed):
 @pytest.mark.parametrize("xdt", ["f16", "bf16"])
 def test_gather_parity(aq, bits, xdt):
     G = GROUP_FOR_BITS[bits]
-    E, N, K, T, topk = 8, 100, 4 * G, 9, 3
+    # bf16 at K >= 2048, where the bound covers a bf16 result's own rounding
+    E, N, K, T, topk = 8, 100, 4 * G if xdt == "f16" else 2048 + 4 * G, 9, 3
     c, s, b = _experts(E, N, K, G, bits, seed=11)
     ids = inputs.expert_ids(T, E, topk, seed=11)
     xb = inputs.activations(T, K, xdt, seed=11)
@@ -345,9 +382,9 @@ def test_gather_groups(aq, bits, G):
     E, N, K, T, topk = 5, 37, 5 * G if G == 32 else 3 * G, 11, 2
     c, s, b = _experts(E, N, K, G, bits, seed=15)
     ids = inputs.expert_ids(T, E, topk, seed=15)
-    xb = inputs.activations(T, K, "bf16", seed=15)
-    y_ref, A = oracle.gather_matmul(inputs.from_bits(xb, "bf16"), c, s, b, ids, K, G, bits)
-    y = aq.aq_gather_qmv(bits_to_dev(xb, "bf16"), *packed_to_dev(c, s, b), to_dev(ids), G, bits)
+    xb = inputs.activations(T, K, "f16", seed=15)
+    y_ref, A = oracle.gather_matmul(inputs.from_bits(xb, "f16"), c, s, b, ids, K, G, bits)
+    y = aq.aq_gather_qmv(bits_to_dev(xb, "f16"), *packed_to_dev(c, s, b), to_dev(ids), G, bits)
     _assert_close(y, y_ref, A, f"gather b{bits} G{G}")
 
 

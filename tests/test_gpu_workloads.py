@@ -1,12 +1,13 @@
 """Parity at the full workload sizes, through the entry points the benchmark
-times (shape dispatch for M <= 8, the matrix-core kernel for prefill, the
+times (shape dispatch for few rows, the matrix-core kernel for prefill, the
 gather kernel for the experts).
 
   tiny     W [512, 512] 4-bit G=64, x fp16 [1, 512]
   decode   W [4096,4096], [1024,4096], [14336,4096], [4096,14336], 0.1% outliers
            x20, 4-bit G=64, x fp16 [1, K]
   specdec  W [14336,4096], [4096,14336] at 4-bit G=64 and 8-bit G=128,
-           x bf16 [M, K], M in {2,3,4,6,8}
+           x bf16 [M, K], M in {2,3,4,6,8}; also M in {12,16,40,64} (sampled
+           columns)
   prefill  X bf16 [2048, 8192], W [28672, 8192] at 4-bit G=64, 3-bit G=64,
            2-bit G=32 (outputs compared on a seeded sample of rows x columns)
   moe      64 experts [1408, 2048] 4-bit G=64, x fp16 [32, 2048], ids [32, 6];
@@ -85,6 +86,24 @@ def test_specdec(aq, N, K, bits, G):
         y_ref, A = oracle.matmul(inputs.from_bits(xb, "bf16"), c, s, b, K, G, bits)
         y = aq.aq_quantized_matmul(bits_to_dev(xb, "bf16"), *dev, G, bits)
         _close(out_to_f64(y), y_ref, A, f"specdec {N}x{K} b{bits} M{M}")
+
+
+@pytest.mark.parametrize("bits,G", [(4, 64), (8, 128)])
+@pytest.mark.parametrize("N,K", inputs.WORKLOADS["specdec"]["shapes"])
+def test_specdec_more_rows(aq, N, K, bits, G):
+    """The same matrices at 12..64 rows of x (a batch of decoding sequences):
+    the few-row kernel with 16 x rows per slot and slices of 16; every row,
+    512 sampled output columns plus the first and last."""
+    w = inputs.weights(N, K, seed=0, key=(WID["specdec"],))
+    c, s, b = oracle.quantize(w, G, bits)
+    dev = packed_to_dev(c, s, b)
+    rng = np.random.default_rng(N + bits)
+    cols = np.unique(np.concatenate([rng.choice(N, 512, replace=False), [0, N - 1]]))
+    for M in sorted({12, 40, *inputs.WORKLOADS["specdec"]["M_batch"]}):
+        xb = inputs.activations(M, K, "bf16", seed=0, key=(WID["specdec"], N, M))
+        y_ref, A = oracle.matmul(inputs.from_bits(xb, "bf16"), c, s, b, K, G, bits, cols=cols)
+        y = aq.aq_quantized_matmul(bits_to_dev(xb, "bf16"), *dev, G, bits)
+        _close(out_to_f64(y)[:, cols], y_ref, A, f"specdec {N}x{K} b{bits} M{M}")
 
 
 @pytest.fixture(scope="module")
