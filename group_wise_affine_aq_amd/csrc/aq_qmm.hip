@@ -533,6 +533,328 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const uint16_t *__restric
   }
 }
 
+// ---------------------------------------------------------------------------
+// The prefill product with weights dequantized straight into matrix-core
+// operands.  One 256-thread workgroup computes a 256 x 256 tile of Y; wave w
+// owns the 64 columns 64w .. 64w+63 and all 256 rows: 8 x 2 blocks of
+// v_mfma_f32_32x32x16 (256 accumulators per lane, in the accumulation
+// registers one wave per SIMD can hold).  Each lane loads, for each of its two
+// 32-column blocks, one whole 32-code chunk of its column's W row per K step
+// of 64 and dequantizes it (q*s + b in binary32, rounded to nearest even into
+// the activation type, the value aq_dequantize returns) directly into the B
+// operand: no weight ever passes through LDS, and no other wave needs it.
+// Only the X tile is shared: each step's 256 x 64 tile is copied to LDS by
+// direct global-to-LDS loads into one of four stages, three steps ahead of
+// its use, as are the W chunks (register sets), so one barrier per step
+// suffices and HBM latency stays hidden behind three steps of matrix work.
+// K order inside a step: the B operand of lane l (column l % 32, half
+// h = l / 32) for 16-k slice ks holds codes 8 ks .. 8 ks + 7 of chunk h, i.e.
+// k = 32 h + 8 ks + 0..7; the A fragments are read from LDS in that same
+// order (a permutation of k applied to both operands leaves the dot products
+// unchanged).
+constexpr int WBN = 256;                     // tile columns
+constexpr int WFM = BM / 32, WFN = 2;        // 32x32 blocks per wave: 8 x 2
+constexpr int kWStages = 4;                  // X stages in LDS (32 KB each)
+
+// per-step loads of one thread: the X copy, then the two W chunks
+template <int BITS>
+constexpr int kWrStepLoads = kXDma + 2 * kChunkLoads<BITS>;
+
+// s_waitcnt immediate: at most n vector-memory operations outstanding, and
+// no LDS operation (lgkmcnt 0)
+constexpr int vm_lgkm0_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4); }
+
+// Workgroup barrier for the X stages: this wave's outstanding loads are
+// first cut to `n` (its copies of the stage read next have landed) and its
+// LDS reads drained (no copy issued after the barrier can overtake them).
+// __syncthreads() would add a release fence, which also waits for every
+// global-to-LDS copy still in flight, the later stages' included.  The empty
+// asm statements keep the compiler from moving memory accesses across.
+template <int n>
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(n));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// one thread's W chunks (one per 32-column block) of one K step
+template <int BITS>
+struct WrRegs {
+  uint32_t w[WFN][BITS];
+  uint32_t s[WFN], b[WFN];
+};
+
+// Scheduling hint for one 16-k slice: 16 MFMAs, NR LDS reads and NG global
+// loads among the first slots, NV vector ALU instructions after each MFMA.
+template <int NR, int NV, int NG>
+__device__ __forceinline__ void sched_kslice() {
+#pragma unroll
+  for (int i = 0; i < WFM * WFN; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (i < NG) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    if (NV > 0) __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
+  }
+}
+
+template <int BITS, typename XT>
+__global__ __launch_bounds__(kThreads) void qmm_wr_kernel(const uint16_t *__restrict__ x,
+                                                          int64_t M,
+                                                          const uint32_t *__restrict__ codes,
+                                                          const uint16_t *__restrict__ scales,
+                                                          const uint16_t *__restrict__ biases,
+                                                          int64_t N, int64_t K, int G,
+                                                          uint16_t *__restrict__ y) {
+  // four distinct LDS objects, one per X stage
+  __shared__ __attribute__((aligned(16))) char xs0[kXStage], xs1[kXStage], xs2[kXStage],
+      xs3[kXStage];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;
+
+  const int nch = (int)(K >> 5), gshift = __builtin_ctz((unsigned)G) - 5;
+  const int64_t wpr = (int64_t)nch * BITS, gpr = nch >> gshift;
+  const int ksteps = (int)((K + BK - 1) / BK);
+
+  // Grid x: column tiles, y: row tiles.  Blocks are dealt to the 8 XCDs
+  // round-robin in x-fastest order, so the blocks resident on one XCD hold
+  // every eighth column tile of the same one or two row tiles and share
+  // those X rows in its L2.  (No division: the tile coordinates stay scalar,
+  // and with them the operand resources.)
+  const int64_t tile_m = (int64_t)blockIdx.y * BM;
+  const int64_t tile_n = (int64_t)blockIdx.x * WBN;
+
+  // operand tiles as buffer resources: rows past M or N read as zero
+  const int64_t mrows = M - tile_m < BM ? M - tile_m : BM;
+  const int64_t nrows = N - tile_n < WBN ? N - tile_n : WBN;
+  const int xbytes = (int)(mrows * K * 2);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + tile_m * K, xbytes);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(codes + tile_n * wpr, nrows * wpr * 4);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(scales + tile_n * gpr, nrows * gpr * 2);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(biases + tile_n * gpr, nrows * gpr * 2);
+
+  // K steps: when K % 64 == 32 the lone last chunk is step 0 (its upper half
+  // reads zeros), so every later step is full
+  const bool ktail = (K % BK) != 0;
+  const int koff = ktail ? BK : 0;
+  auto kbase = [&](int st) -> int { return ktail && st == 0 ? (int)K - 32 : st * BK - koff; };
+  auto kclamp = [&](int st) -> int { return kbase(st < ksteps ? st : ksteps - 1); };
+
+  // X copy: load i of wave w fills rows 8 (8w + i) .. +7; LDS row r holds
+  // the row's 16-byte unit u at slot u ^ ((r >> 1) & 7)
+  uint32_t xvoff[kXDma], xvoff_tail[kXDma];
+#pragma unroll
+  for (int i = 0; i < kXDma; ++i) {
+    const int row = 8 * (wave * kXDma + i) + (lane >> 3);
+    const int u = (lane & 7) ^ ((row >> 1) & 7);
+    xvoff[i] = (uint32_t)(row * K * 2) + (uint32_t)u * 16u;
+    xvoff_tail[i] = u < 4 ? xvoff[i] : (uint32_t)xbytes;  // k past K: out of range, reads zero
+  }
+  // loads i0 .. i1-1 of a step's X copy
+  auto dma_x = [&](int k0, char *dst, const uint32_t (&vo)[kXDma], int i0 = 0, int i1 = kXDma) {
+    const uint32_t so = (uint32_t)k0 * 2u;
+#pragma unroll
+    for (int i = 0; i < kXDma; ++i)
+      if (i >= i0 && i < i1)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rx, (lds_void *)(dst + (wave * kXDma + i) * 1024), 16, (int)vo[i], (int)so, 0, 0);
+  };
+
+  // W: block cb of lane l is tile column 64 w + 32 cb + l % 32; the lane
+  // reads chunk h of the step (step 0 of a K tail: only h = 0 is inside K)
+  uint32_t wvoff[WFN], svoff[WFN], wvoff0[WFN], svoff0[WFN];
+#pragma unroll
+  for (int cb = 0; cb < WFN; ++cb) {
+    const int n = 64 * wave + 32 * cb + (lane & 31);
+    wvoff[cb] = (uint32_t)(n * wpr + h * BITS) * 4u;
+    svoff[cb] = (uint32_t)(n * gpr + (gshift == 0 ? h : 0)) * 2u;
+    wvoff0[cb] = ktail && h ? 0x80000000u : wvoff[cb];  // past every resource: zeros
+    svoff0[cb] = ktail && h ? 0x80000000u : svoff[cb];
+  }
+  // the W chunk of blocks cb0 .. cb1-1 (codes, scale, bias)
+  auto load_w = [&](int k0, WrRegs<BITS> &r, const uint32_t (&wv)[WFN], const uint32_t (&sv)[WFN],
+                    int cb0 = 0, int cb1 = WFN) {
+    const int c0 = k0 >> 5;
+#pragma unroll
+    for (int cb = 0; cb < WFN; ++cb) {
+      if (cb < cb0 || cb >= cb1) continue;
+      bload_chunk<BITS>(rw, wv[cb], (uint32_t)(c0 * BITS) * 4u, r.w[cb]);
+      const uint32_t so = (uint32_t)(c0 >> gshift) * 2u;
+      r.s[cb] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)sv[cb], (int)so, 0);
+      r.b[cb] = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)sv[cb], (int)so, 0);
+    }
+  };
+  const uint32_t nmask = opaque(0x0F0F0F0Fu);
+  auto dequant = [&](const WrRegs<BITS> &r, auto kscon, uint4 (&bq)[WFN]) {
+    constexpr int ks = decltype(kscon)::value;
+#pragma unroll
+    for (int cb = 0; cb < WFN; ++cb)
+      bq[cb] = dequant8<BITS, XT, ks>(r.w[cb], f16_to_f32((uint16_t)r.s[cb]),
+                                      f16_to_f32((uint16_t)r.b[cb]), nmask);
+  };
+
+  // A fragments: lane l supplies row (l % 32) of a 32-row block and unit
+  // 4 h + ks of the step
+  uint32_t xfo[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    xfo[ks] = (uint32_t)((lane & 31) * 128 + (((4 * h + ks) ^ (((lane & 31) >> 1) & 7)) * 16));
+  auto frag = [&](const char *st_base, int ks, uint4 (&a)[WFM]) {
+    const char *p = st_base + xfo[ks];
+#pragma unroll
+    for (int i = 0; i < WFM; ++i) a[i] = *reinterpret_cast<const uint4 *>(p + i * 32 * 128);
+  };
+
+  f32x16v acc[WFM][WFN];
+#pragma unroll
+  for (int i = 0; i < WFM; ++i)
+#pragma unroll
+    for (int j = 0; j < WFN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  auto mfma_ks = [&](const uint4 (&a)[WFM], const uint4 (&b)[WFN]) {
+#pragma unroll
+    for (int j = 0; j < WFN; ++j)
+#pragma unroll
+      for (int i = 0; i < WFM; ++i) acc[i][j] = mfma32<XT>(a[i], b[j], acc[i][j]);
+  };
+
+  // The pipeline takes the four stages as restrict pointers: every LDS access
+  // in it then carries alias scopes, from which the compiler's wait placement
+  // can tell a copy into one stage from reads of another (without them it
+  // makes each fragment read wait for the latest copy into any stage).
+  auto run = [&](char *__restrict__ q0, char *__restrict__ q1, char *__restrict__ q2,
+                 char *__restrict__ q3) {
+  auto stage = [&](auto jcon) -> char * {
+    constexpr int j = decltype(jcon)::value;
+    return j == 0 ? q0 : j == 1 ? q1 : j == 2 ? q2 : q3;
+  };
+  WrRegs<BITS> wr[kWStages];  // W of step s in wr[s % 4]
+  uint4 fa[2][WFM], fb[2][WFN];
+  using K0 = std::integral_constant<int, 0>;
+  using K1 = std::integral_constant<int, 1>;
+  using K2 = std::integral_constant<int, 2>;
+  using K3 = std::integral_constant<int, 3>;
+  constexpr int kNV = 3;  // vector instructions between consecutive MFMAs
+
+  // Step st from stage / register set j = st % 4.  On entry fa[0], fb[0]
+  // hold slice 0.  Each slice's MFMAs run while the next slice's fragments
+  // are read and its weights dequantized; before the last slice the wave
+  // waits for step st + 1's data, meets the others at the barrier (every
+  // wave is then done with stage j), and starts step st + 4's X copy into
+  // stage j.  A step's loads are spread over four slices (X copy: half after
+  // the barrier of step s - 4, half in slice 0 of step s - 3; W: one block in
+  // each of slices 1 and 2 of step s - 3): issued in a burst they queue at
+  // the memory pipeline and stall the wave's matrix-core issue.  Either way
+  // exactly 28 (4-bit) loads follow a step's last one before the barrier
+  // that waits for it.
+  // The wait counts the loads issued after step st + 1's; in the steps after
+  // the main loop (FIN) the compiler drops loads whose registers are never
+  // read again, so there the wave waits for all of its loads.
+  auto step = [&](auto jcon, auto fincon, int st) {
+    constexpr int j = decltype(jcon)::value;
+    constexpr bool FIN = decltype(fincon)::value;
+    constexpr int jn = (j + 1) & 3;
+    using JN = std::integral_constant<int, jn>;
+    constexpr int j3 = (j + 3) & 3;  // stage / register set of step st + 3
+    using J3 = std::integral_constant<int, j3>;
+    char *sb = stage(jcon);
+    const int k3 = kclamp(st + 3);
+    frag(sb, 1, fa[1]);
+    dequant(wr[j], K1{}, fb[1]);
+    dma_x(k3, stage(J3{}), xvoff, kXDma / 2, kXDma);
+    mfma_ks(fa[0], fb[0]);
+    sched_kslice<WFM, kNV, kXDma / 2>();
+    __builtin_amdgcn_sched_barrier(0);
+    frag(sb, 2, fa[0]);
+    dequant(wr[j], K2{}, fb[0]);
+    load_w(k3, wr[j3], wvoff, svoff, 0, 1);
+    mfma_ks(fa[1], fb[1]);
+    sched_kslice<WFM, kNV, kChunkLoads<BITS>>();
+    __builtin_amdgcn_sched_barrier(0);
+    frag(sb, 3, fa[1]);
+    dequant(wr[j], K3{}, fb[1]);
+    load_w(k3, wr[j3], wvoff, svoff, 1, 2);
+    mfma_ks(fa[0], fb[0]);
+    sched_kslice<WFM, kNV, kChunkLoads<BITS>>();
+    __builtin_amdgcn_sched_barrier(0);
+    // step st + 1's X and W have landed (steps st + 2, st + 3 stay in flight)
+    constexpr int kAhead = FIN ? 0 : (2 * kWrStepLoads<BITS> < 63 ? 2 * kWrStepLoads<BITS> : 63);
+    stage_barrier<kAhead>();
+    dma_x(kclamp(st + 4), sb, xvoff, 0, kXDma / 2);
+    frag(stage(JN{}), 0, fa[0]);
+    dequant(wr[jn], K0{}, fb[0]);
+    mfma_ks(fa[1], fb[1]);
+    sched_kslice<WFM, kNV, kXDma / 2>();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // prologue: steps 0 .. 2 and the first half of step 3's X copy in flight
+  // (step 0 masked past K when it is the tail chunk), then slice 0 of step 0
+  // (fenced: the counter wait below relies on this issue order)
+  dma_x(kbase(0), q0, ktail ? xvoff_tail : xvoff);
+  load_w(kbase(0), wr[0], wvoff0, svoff0);
+  __builtin_amdgcn_sched_barrier(0);
+  dma_x(kclamp(1), q1, xvoff);
+  load_w(kclamp(1), wr[1], wvoff, svoff);
+  __builtin_amdgcn_sched_barrier(0);
+  dma_x(kclamp(2), q2, xvoff);
+  load_w(kclamp(2), wr[2], wvoff, svoff);
+  __builtin_amdgcn_sched_barrier(0);
+  dma_x(kclamp(3), q3, xvoff, 0, kXDma / 2);
+  __builtin_amdgcn_sched_barrier(0);
+  stage_barrier<(2 * kWrStepLoads<BITS> + kXDma / 2 < 63 ? 2 * kWrStepLoads<BITS> + kXDma / 2
+                                                          : 63)>();
+  frag(q0, 0, fa[0]);
+  dequant(wr[0], K0{}, fb[0]);
+
+  using LOOP = std::false_type;
+  using FIN = std::true_type;
+  int st = 0;
+  for (; st + 4 <= ksteps; st += 4) {
+    step(K0{}, LOOP{}, st);
+    step(K1{}, LOOP{}, st + 1);
+    step(K2{}, LOOP{}, st + 2);
+    step(K3{}, LOOP{}, st + 3);
+  }
+  if (st < ksteps) step(K0{}, FIN{}, st);
+  if (st + 1 < ksteps) step(K1{}, FIN{}, st + 1);
+  if (st + 2 < ksteps) step(K2{}, FIN{}, st + 2);
+  // the loads issued past the last step (clamped, in range) finish here
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  };
+  run(xs0, xs1, xs2, xs3);
+
+  // epilogue: accumulator r of lane l in a 32x32 block is row
+  // 8*(r/4) + 4*(l/32) + r%4, column l % 32
+#pragma unroll
+  for (int i = 0; i < WFM; ++i)
+#pragma unroll
+    for (int j = 0; j < WFN; ++j) {
+      const int64_t n = tile_n + 64 * wave + 32 * j + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = tile_m + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (m < M && n < N) y[m * N + n] = xtraits<XT>::from_f32(acc[i][j][r]);
+      }
+    }
+}
+
+template <int BITS, typename XT>
+hipError_t qmm_wr_launch(const void *x, int64_t M, const uint32_t *codes, const uint16_t *scales,
+                         const uint16_t *biases, int64_t N, int64_t K, int G, void *y,
+                         hipStream_t s) {
+  const int64_t mt = (M + BM - 1) / BM, nt = (N + WBN - 1) / WBN;
+  if (nt > 0x7FFFFFFF || mt > 65535) return hipErrorInvalidValue;  // grid limits
+  if ((int64_t)BM * K * 2 > 0x7FFFFFFF) return hipErrorInvalidValue;  // 32-bit tile offsets
+  hipLaunchKernelGGL((qmm_wr_kernel<BITS, XT>), dim3((unsigned)nt, (unsigned)mt), dim3(kThreads),
+                     0, s, (const uint16_t *)x, M, codes, scales, biases, N, K, G,
+                     (uint16_t *)y);
+  return hipGetLastError();
+}
+
 template <int BITS, typename XT>
 hipError_t qmm_launch(const void *x, int64_t M, const uint32_t *codes, const uint16_t *scales,
                       const uint16_t *biases, int64_t N, int64_t K, int G, void *y,
@@ -578,15 +900,21 @@ template <typename XT>
 hipError_t qmm_bits(const void *x, int64_t M, const uint32_t *codes, const uint16_t *scales,
                     const uint16_t *biases, int64_t N, int64_t K, int G, int bits, void *y,
                     hipStream_t s) {
+#ifdef AQ_QMM_OLD
+#define AQ_QL qmm_launch
+#else
+#define AQ_QL qmm_wr_launch
+#endif
   switch (bits) {
-    case 2: return qmm_launch<2, XT>(x, M, codes, scales, biases, N, K, G, y, s);
-    case 3: return qmm_launch<3, XT>(x, M, codes, scales, biases, N, K, G, y, s);
-    case 4: return qmm_launch<4, XT>(x, M, codes, scales, biases, N, K, G, y, s);
-    case 5: return qmm_launch<5, XT>(x, M, codes, scales, biases, N, K, G, y, s);
-    case 6: return qmm_launch<6, XT>(x, M, codes, scales, biases, N, K, G, y, s);
-    case 7: return qmm_launch<7, XT>(x, M, codes, scales, biases, N, K, G, y, s);
-    case 8: return qmm_launch<8, XT>(x, M, codes, scales, biases, N, K, G, y, s);
+    case 2: return AQ_QL<2, XT>(x, M, codes, scales, biases, N, K, G, y, s);
+    case 3: return AQ_QL<3, XT>(x, M, codes, scales, biases, N, K, G, y, s);
+    case 4: return AQ_QL<4, XT>(x, M, codes, scales, biases, N, K, G, y, s);
+    case 5: return AQ_QL<5, XT>(x, M, codes, scales, biases, N, K, G, y, s);
+    case 6: return AQ_QL<6, XT>(x, M, codes, scales, biases, N, K, G, y, s);
+    case 7: return AQ_QL<7, XT>(x, M, codes, scales, biases, N, K, G, y, s);
+    case 8: return AQ_QL<8, XT>(x, M, codes, scales, biases, N, K, G, y, s);
   }
+#undef AQ_QL
   return hipErrorInvalidValue;
 }
 
