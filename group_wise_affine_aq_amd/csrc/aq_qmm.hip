@@ -553,12 +553,12 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(const uint16_t *__restric
 // order (a permutation of k applied to both operands leaves the dot products
 // unchanged).
 constexpr int WBN = 256;                     // tile columns
-constexpr int WFM = BM / 32, WFN = 2;        // 32x32 blocks per wave: 8 x 2
+constexpr int WFN = 2;                       // 32-column blocks per wave
 constexpr int kWStages = 4;                  // X stages in LDS (32 KB each)
 
-// per-step loads of one thread: the X copy, then the two W chunks
-template <int BITS>
-constexpr int kWrStepLoads = kXDma + 2 * kChunkLoads<BITS>;
+// a tile of 32 FM rows: 16-byte X units per thread per step
+template <int FM>
+constexpr int kWrXDma = 32 * FM * BK / 8 / kThreads;
 
 // s_waitcnt immediate: at most n vector-memory operations outstanding, and
 // no LDS operation (lgkmcnt 0)
@@ -586,12 +586,12 @@ struct WrRegs {
   uint32_t s[WFN], b[WFN];
 };
 
-// Scheduling hint for one 16-k slice: 16 MFMAs, NR LDS reads and NG global
+// Scheduling hint for one 16-k slice: 2 FM MFMAs, NR LDS reads and NG global
 // loads among the first slots, NV vector ALU instructions after each MFMA.
-template <int NR, int NV, int NG>
+template <int FM, int NR, int NV, int NG>
 __device__ __forceinline__ void sched_kslice() {
 #pragma unroll
-  for (int i = 0; i < WFM * WFN; ++i) {
+  for (int i = 0; i < FM * WFN; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     if (i < NG) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
@@ -599,17 +599,25 @@ __device__ __forceinline__ void sched_kslice() {
   }
 }
 
-template <int BITS, typename XT>
+// FM: 32-row blocks per tile (8: 256 x 256 tiles; 4: 128 x 256, for a last
+// partial round of tiles).  G1: one group per 32-code chunk (G = 32).  y rows
+// are ldy elements apart.
+template <int BITS, typename XT, int FM, bool G1>
 __global__ __launch_bounds__(kThreads) void qmm_wr_kernel(const uint16_t *__restrict__ x,
                                                           int64_t M,
                                                           const uint32_t *__restrict__ codes,
                                                           const uint16_t *__restrict__ scales,
                                                           const uint16_t *__restrict__ biases,
                                                           int64_t N, int64_t K, int G,
-                                                          uint16_t *__restrict__ y) {
+                                                          uint16_t *__restrict__ y, int64_t ldy) {
+  constexpr int TBM = 32 * FM, kXSt = TBM * BK * 2, kXD = kWrXDma<FM>;
+  // a thread's loads per step: the X copy, the codes of its two W chunks,
+  // their scales and biases (G > 32: one scale and one bias per lane, for
+  // the block of its half, exchanged between the halves afterwards)
+  constexpr int kCode = kChunkLoads<BITS> - 2;
+  constexpr int kStepLoads = kXD + 2 * kCode + (G1 ? 4 : 2);
   // four distinct LDS objects, one per X stage
-  __shared__ __attribute__((aligned(16))) char xs0[kXStage], xs1[kXStage], xs2[kXStage],
-      xs3[kXStage];
+  __shared__ __attribute__((aligned(16))) char xs0[kXSt], xs1[kXSt], xs2[kXSt], xs3[kXSt];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5;
@@ -623,11 +631,11 @@ __global__ __launch_bounds__(kThreads) void qmm_wr_kernel(const uint16_t *__rest
   // every eighth column tile of the same one or two row tiles and share
   // those X rows in its L2.  (No division: the tile coordinates stay scalar,
   // and with them the operand resources.)
-  const int64_t tile_m = (int64_t)blockIdx.y * BM;
+  const int64_t tile_m = (int64_t)blockIdx.y * TBM;
   const int64_t tile_n = (int64_t)blockIdx.x * WBN;
 
   // operand tiles as buffer resources: rows past M or N read as zero
-  const int64_t mrows = M - tile_m < BM ? M - tile_m : BM;
+  const int64_t mrows = M - tile_m < TBM ? M - tile_m : TBM;
   const int64_t nrows = N - tile_n < WBN ? N - tile_n : WBN;
   const int xbytes = (int)(mrows * K * 2);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + tile_m * K, xbytes);
@@ -644,46 +652,64 @@ __global__ __launch_bounds__(kThreads) void qmm_wr_kernel(const uint16_t *__rest
 
   // X copy: load i of wave w fills rows 8 (8w + i) .. +7; LDS row r holds
   // the row's 16-byte unit u at slot u ^ ((r >> 1) & 7)
-  uint32_t xvoff[kXDma], xvoff_tail[kXDma];
+  uint32_t xvoff[kXD], xvoff_tail[kXD];
 #pragma unroll
-  for (int i = 0; i < kXDma; ++i) {
-    const int row = 8 * (wave * kXDma + i) + (lane >> 3);
+  for (int i = 0; i < kXD; ++i) {
+    const int row = 8 * (wave * kXD + i) + (lane >> 3);
     const int u = (lane & 7) ^ ((row >> 1) & 7);
     xvoff[i] = (uint32_t)(row * K * 2) + (uint32_t)u * 16u;
     xvoff_tail[i] = u < 4 ? xvoff[i] : (uint32_t)xbytes;  // k past K: out of range, reads zero
   }
   // loads i0 .. i1-1 of a step's X copy
-  auto dma_x = [&](int k0, char *dst, const uint32_t (&vo)[kXDma], int i0 = 0, int i1 = kXDma) {
+  auto dma_x = [&](int k0, char *dst, const uint32_t (&vo)[kXD], int i0 = 0, int i1 = kWrXDma<FM>) {
     const uint32_t so = (uint32_t)k0 * 2u;
 #pragma unroll
-    for (int i = 0; i < kXDma; ++i)
+    for (int i = 0; i < kXD; ++i)
       if (i >= i0 && i < i1)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rx, (lds_void *)(dst + (wave * kXDma + i) * 1024), 16, (int)vo[i], (int)so, 0, 0);
+            rx, (lds_void *)(dst + (wave * kXD + i) * 1024), 16, (int)vo[i], (int)so, 0, 0);
   };
 
   // W: block cb of lane l is tile column 64 w + 32 cb + l % 32; the lane
-  // reads chunk h of the step (step 0 of a K tail: only h = 0 is inside K)
+  // reads chunk h of the step (step 0 of a K tail: only h = 0 is inside K).
+  // G = 32: the lane reads the scale and bias of its chunk for both blocks;
+  // G > 32 (both chunks in one group): only those of block h, which one
+  // v_permlane32_swap then gives to both halves.
   uint32_t wvoff[WFN], svoff[WFN], wvoff0[WFN], svoff0[WFN];
 #pragma unroll
   for (int cb = 0; cb < WFN; ++cb) {
-    const int n = 64 * wave + 32 * cb + (lane & 31);
-    wvoff[cb] = (uint32_t)(n * wpr + h * BITS) * 4u;
-    svoff[cb] = (uint32_t)(n * gpr + (gshift == 0 ? h : 0)) * 2u;
+    const int n = 64 * wave + 32 * (G1 ? cb : h) + (lane & 31);
+    wvoff[cb] = (uint32_t)((64 * wave + 32 * cb + (lane & 31)) * wpr + h * BITS) * 4u;
+    svoff[cb] = (uint32_t)(n * gpr + (G1 ? h : 0)) * 2u;
     wvoff0[cb] = ktail && h ? 0x80000000u : wvoff[cb];  // past every resource: zeros
-    svoff0[cb] = ktail && h ? 0x80000000u : svoff[cb];
+    svoff0[cb] = G1 && ktail && h ? 0x80000000u : svoff[cb];
   }
-  // the W chunk of blocks cb0 .. cb1-1 (codes, scale, bias)
+  // part p of a step's W loads: the codes of block p, then (G = 32) the
+  // scale and bias of block p, or (G > 32) the scale (p = 0) or the bias
   auto load_w = [&](int k0, WrRegs<BITS> &r, const uint32_t (&wv)[WFN], const uint32_t (&sv)[WFN],
-                    int cb0 = 0, int cb1 = WFN) {
+                    int part) {
     const int c0 = k0 >> 5;
-#pragma unroll
-    for (int cb = 0; cb < WFN; ++cb) {
-      if (cb < cb0 || cb >= cb1) continue;
-      bload_chunk<BITS>(rw, wv[cb], (uint32_t)(c0 * BITS) * 4u, r.w[cb]);
-      const uint32_t so = (uint32_t)(c0 >> gshift) * 2u;
-      r.s[cb] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)sv[cb], (int)so, 0);
-      r.b[cb] = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)sv[cb], (int)so, 0);
+    bload_chunk<BITS>(rw, wv[part], (uint32_t)(c0 * BITS) * 4u, r.w[part]);
+    const uint32_t so = (uint32_t)(c0 >> gshift) * 2u;
+    if constexpr (G1) {
+      r.s[part] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)sv[part], (int)so, 0);
+      r.b[part] = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)sv[part], (int)so, 0);
+    } else if (part == 0) {
+      r.s[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)sv[0], (int)so, 0);
+    } else {
+      r.b[0] = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)sv[0], (int)so, 0);
+    }
+  };
+  // before the first use of a register set (G > 32): lanes l and l + 32 hold
+  // the scale (bias) of blocks 0 and 1; afterwards every lane holds both
+  auto share_sb = [&](WrRegs<BITS> &r) {
+    if constexpr (!G1) {
+      const auto sp = __builtin_amdgcn_permlane32_swap(r.s[0], r.s[0], false, false);
+      const auto bp = __builtin_amdgcn_permlane32_swap(r.b[0], r.b[0], false, false);
+      r.s[0] = sp[0];
+      r.s[1] = sp[1];
+      r.b[0] = bp[0];
+      r.b[1] = bp[1];
     }
   };
   const uint32_t nmask = opaque(0x0F0F0F0Fu);
@@ -701,24 +727,24 @@ __global__ __launch_bounds__(kThreads) void qmm_wr_kernel(const uint16_t *__rest
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
     xfo[ks] = (uint32_t)((lane & 31) * 128 + (((4 * h + ks) ^ (((lane & 31) >> 1) & 7)) * 16));
-  auto frag = [&](const char *st_base, int ks, uint4 (&a)[WFM]) {
+  auto frag = [&](const char *st_base, int ks, uint4 (&a)[FM]) {
     const char *p = st_base + xfo[ks];
 #pragma unroll
-    for (int i = 0; i < WFM; ++i) a[i] = *reinterpret_cast<const uint4 *>(p + i * 32 * 128);
+    for (int i = 0; i < FM; ++i) a[i] = *reinterpret_cast<const uint4 *>(p + i * 32 * 128);
   };
 
-  f32x16v acc[WFM][WFN];
+  f32x16v acc[FM][WFN];
 #pragma unroll
-  for (int i = 0; i < WFM; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < WFN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  auto mfma_ks = [&](const uint4 (&a)[WFM], const uint4 (&b)[WFN]) {
+  auto mfma_ks = [&](const uint4 (&a)[FM], const uint4 (&b)[WFN]) {
 #pragma unroll
     for (int j = 0; j < WFN; ++j)
 #pragma unroll
-      for (int i = 0; i < WFM; ++i) acc[i][j] = mfma32<XT>(a[i], b[j], acc[i][j]);
+      for (int i = 0; i < FM; ++i) acc[i][j] = mfma32<XT>(a[i], b[j], acc[i][j]);
   };
 
   // The pipeline takes the four stages as restrict pointers: every LDS access
@@ -732,7 +758,7 @@ __global__ __launch_bounds__(kThreads) void qmm_wr_kernel(const uint16_t *__rest
     return j == 0 ? q0 : j == 1 ? q1 : j == 2 ? q2 : q3;
   };
   WrRegs<BITS> wr[kWStages];  // W of step s in wr[s % 4]
-  uint4 fa[2][WFM], fb[2][WFN];
+  uint4 fa[2][FM], fb[2][WFN];
   using K0 = std::integral_constant<int, 0>;
   using K1 = std::integral_constant<int, 1>;
   using K2 = std::integral_constant<int, 2>;
@@ -764,30 +790,31 @@ __global__ __launch_bounds__(kThreads) void qmm_wr_kernel(const uint16_t *__rest
     const int k3 = kclamp(st + 3);
     frag(sb, 1, fa[1]);
     dequant(wr[j], K1{}, fb[1]);
-    dma_x(k3, stage(J3{}), xvoff, kXDma / 2, kXDma);
+    dma_x(k3, stage(J3{}), xvoff, kXD / 2, kXD);
     mfma_ks(fa[0], fb[0]);
-    sched_kslice<WFM, kNV, kXDma / 2>();
+    sched_kslice<FM, FM, kNV, kXD / 2>();
     __builtin_amdgcn_sched_barrier(0);
     frag(sb, 2, fa[0]);
     dequant(wr[j], K2{}, fb[0]);
-    load_w(k3, wr[j3], wvoff, svoff, 0, 1);
+    load_w(k3, wr[j3], wvoff, svoff, 0);
     mfma_ks(fa[1], fb[1]);
-    sched_kslice<WFM, kNV, kChunkLoads<BITS>>();
+    sched_kslice<FM, FM, kNV, kChunkLoads<BITS>>();
     __builtin_amdgcn_sched_barrier(0);
     frag(sb, 3, fa[1]);
     dequant(wr[j], K3{}, fb[1]);
-    load_w(k3, wr[j3], wvoff, svoff, 1, 2);
+    load_w(k3, wr[j3], wvoff, svoff, 1);
     mfma_ks(fa[0], fb[0]);
-    sched_kslice<WFM, kNV, kChunkLoads<BITS>>();
+    sched_kslice<FM, FM, kNV, kChunkLoads<BITS>>();
     __builtin_amdgcn_sched_barrier(0);
     // step st + 1's X and W have landed (steps st + 2, st + 3 stay in flight)
-    constexpr int kAhead = FIN ? 0 : (2 * kWrStepLoads<BITS> < 63 ? 2 * kWrStepLoads<BITS> : 63);
+    constexpr int kAhead = FIN ? 0 : (2 * kStepLoads < 63 ? 2 * kStepLoads : 63);
     stage_barrier<kAhead>();
-    dma_x(kclamp(st + 4), sb, xvoff, 0, kXDma / 2);
+    dma_x(kclamp(st + 4), sb, xvoff, 0, kXD / 2);
     frag(stage(JN{}), 0, fa[0]);
+    share_sb(wr[jn]);
     dequant(wr[jn], K0{}, fb[0]);
     mfma_ks(fa[1], fb[1]);
-    sched_kslice<WFM, kNV, kXDma / 2>();
+    sched_kslice<FM, FM, kNV, kXD / 2>();
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -795,19 +822,27 @@ __global__ __launch_bounds__(kThreads) void qmm_wr_kernel(const uint16_t *__rest
   // (step 0 masked past K when it is the tail chunk), then slice 0 of step 0
   // (fenced: the counter wait below relies on this issue order)
   dma_x(kbase(0), q0, ktail ? xvoff_tail : xvoff);
-  load_w(kbase(0), wr[0], wvoff0, svoff0);
+  load_w(kbase(0), wr[0], wvoff0, svoff0, 0);
+  load_w(kbase(0), wr[0], wvoff0, svoff0, 1);
   __builtin_amdgcn_sched_barrier(0);
   dma_x(kclamp(1), q1, xvoff);
-  load_w(kclamp(1), wr[1], wvoff, svoff);
+  load_w(kclamp(1), wr[1], wvoff, svoff, 0);
+  load_w(kclamp(1), wr[1], wvoff, svoff, 1);
   __builtin_amdgcn_sched_barrier(0);
   dma_x(kclamp(2), q2, xvoff);
-  load_w(kclamp(2), wr[2], wvoff, svoff);
+  load_w(kclamp(2), wr[2], wvoff, svoff, 0);
+  load_w(kclamp(2), wr[2], wvoff, svoff, 1);
   __builtin_amdgcn_sched_barrier(0);
-  dma_x(kclamp(3), q3, xvoff, 0, kXDma / 2);
+  dma_x(kclamp(3), q3, xvoff, 0, kXD / 2);
   __builtin_amdgcn_sched_barrier(0);
-  stage_barrier<(2 * kWrStepLoads<BITS> + kXDma / 2 < 63 ? 2 * kWrStepLoads<BITS> + kXDma / 2
+  stage_barrier<(2 * kStepLoads + kXD / 2 < 63 ? 2 * kStepLoads + kXD / 2
                                                           : 63)>();
   frag(q0, 0, fa[0]);
+  share_sb(wr[0]);
+  if (!G1 && ktail && h) {  // step 0 is the K tail: chunk 1 lies past K, its weights read 0
+    wr[0].s[0] = wr[0].s[1] = 0;
+    wr[0].b[0] = wr[0].b[1] = 0;
+  }
   dequant(wr[0], K0{}, fb[0]);
 
   using LOOP = std::false_type;
@@ -830,14 +865,14 @@ __global__ __launch_bounds__(kThreads) void qmm_wr_kernel(const uint16_t *__rest
   // epilogue: accumulator r of lane l in a 32x32 block is row
   // 8*(r/4) + 4*(l/32) + r%4, column l % 32
 #pragma unroll
-  for (int i = 0; i < WFM; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < WFN; ++j) {
       const int64_t n = tile_n + 64 * wave + 32 * j + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t m = tile_m + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (m < M && n < N) y[m * N + n] = xtraits<XT>::from_f32(acc[i][j][r]);
+        if (m < M && n < N) y[m * ldy + n] = xtraits<XT>::from_f32(acc[i][j][r]);
       }
     }
 }
@@ -847,11 +882,41 @@ hipError_t qmm_wr_launch(const void *x, int64_t M, const uint32_t *codes, const 
                          const uint16_t *biases, int64_t N, int64_t K, int G, void *y,
                          hipStream_t s) {
   const int64_t mt = (M + BM - 1) / BM, nt = (N + WBN - 1) / WBN;
-  if (nt > 0x7FFFFFFF || mt > 65535) return hipErrorInvalidValue;  // grid limits
+  if (nt > 0x7FFFFFFF || 2 * mt > 65535) return hipErrorInvalidValue;  // grid limits
   if ((int64_t)BM * K * 2 > 0x7FFFFFFF) return hipErrorInvalidValue;  // 32-bit tile offsets
-  hipLaunchKernelGGL((qmm_wr_kernel<BITS, XT>), dim3((unsigned)nt, (unsigned)mt), dim3(kThreads),
-                     0, s, (const uint16_t *)x, M, codes, scales, biases, N, K, G,
-                     (uint16_t *)y);
+  // One block per compute unit at a time: when the tiles leave a last round
+  // at most half full, and that remainder is a whole number of column tiles,
+  // those columns run as 128-row tiles in a second launch (twice the blocks,
+  // half the work each), which fills the chip for that round.  At 2048 x
+  // 28672: 896 tiles = 768 (three rounds) + 16 columns of 8, run as 256
+  // half tiles.
+  const int64_t cus = device_cus(), rem = (mt * nt) % cus;
+  const int64_t ntail = rem > 0 && 2 * rem <= cus && rem % mt == 0 ? rem / mt : 0;
+  const int64_t nmain = nt - ntail, n0 = nmain * WBN;
+  const int64_t wpr = (K >> 5) * BITS, gpr = (K >> 5) / (G >> 5);
+  uint16_t *yo = (uint16_t *)y;
+  auto go = [&](auto fm, auto g1) {
+    constexpr int FM = decltype(fm)::value;
+    constexpr bool G1 = decltype(g1)::value;
+    if (FM == 8)
+      hipLaunchKernelGGL((qmm_wr_kernel<BITS, XT, 8, G1>), dim3((unsigned)nmain, (unsigned)mt),
+                         dim3(kThreads), 0, s, (const uint16_t *)x, M, codes, scales, biases,
+                         n0 < N ? n0 : N, K, G, yo, N);
+    else
+      hipLaunchKernelGGL((qmm_wr_kernel<BITS, XT, 4, G1>), dim3((unsigned)ntail, (unsigned)(2 * mt)),
+                         dim3(kThreads), 0, s, (const uint16_t *)x, M, codes + n0 * wpr,
+                         scales + n0 * gpr, biases + n0 * gpr, N - n0, K, G, yo + n0, N);
+  };
+  using F8 = std::integral_constant<int, 8>;
+  using F4 = std::integral_constant<int, 4>;
+  if (nmain > 0) {
+    if (G == 32) go(F8{}, std::true_type{});
+    else go(F8{}, std::false_type{});
+  }
+  if (ntail > 0) {
+    if (G == 32) go(F4{}, std::true_type{});
+    else go(F4{}, std::false_type{});
+  }
   return hipGetLastError();
 }
 

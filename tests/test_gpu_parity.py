@@ -328,6 +328,19 @@ def test_qmm_shapes_bf16(aq, M, N, K, G):
     _assert_close(y, y_ref, A, f"qmm {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K,G", [(300, 33029, 96, 32), (64, 51200, 160, 32)])
+def test_qmm_tile_rounds(aq, M, N, K, G):
+    """Shapes that fill the chip in rounds of 256-row tiles: 260 tiles (the
+    last, partial round as 128-row tiles in a second launch; ragged rows,
+    columns and K tail) and 200 tiles (one launch of full tiles)."""
+    bits, xdt = 4, "f16"
+    _, (c, s, b) = _quantized(N, K, G, bits, seed=23)
+    xb = inputs.activations(M, K, xdt, seed=23, key=(M, N, K))
+    y_ref, A = oracle.matmul(inputs.from_bits(xb, xdt), c, s, b, K, G, bits)
+    y = aq.aq_qmm(bits_to_dev(xb, xdt), *packed_to_dev(c, s, b), G, bits)
+    _assert_close(y, y_ref, A, f"qmm {M}x{N}x{K}")
+
+
 def test_qmm_equals_gemm_of_dequantized(aq):
     """The matrix-core path multiplies exactly the bf16 weights that
     aq_dequantize produces (accumulation order aside)."""
