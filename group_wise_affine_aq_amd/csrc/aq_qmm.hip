@@ -2,31 +2,34 @@
 // cores.
 //
 // The operation is Y = X @ W^T with W in packed form ("Quantization",
-// metalworking MLX notes, QMM: dequantize weight tiles into on-chip memory,
-// then a tiled GEMM against them).  On MI355X:
-//  * one 256-thread workgroup computes a 256 x 224 tile of Y (2048 x 28672
-//    is exactly 1024 tiles, four full rounds of the 256 CUs); its 4 waves are
-//    stacked along M, each owning a 64 x 224 sub-tile made of 2 x 7 blocks of
-//    v_mfma_f32_32x32x16_{bf16,f16} with binary32 accumulation (on gfx950
-//    the 32x32x16 form sustains about 1.7x the rate of 16x16x32);
-//  * per K step of 64 the X tile is copied to LDS and the W tile is read as
-//    packed codes, dequantized in registers (q*s + b in binary32, rounded to
-//    nearest even into the activation type -- exactly what aq_dequantize
-//    returns) and written to LDS, so each weight is dequantized once per 256
-//    rows of X; both LDS tiles use a 144-byte row pitch so the 16-byte
-//    fragment reads of 16 lanes fall into disjoint banks;
-//  * the LDS tiles are double-buffered: the global loads for step k+1 are in
-//    flight while the matrix cores work on step k;
-//  * tiles are ordered so that the workgroups resident on one XCD (blocks
-//    are dealt to the 8 XCDs round-robin) share one row-tile of X in that
-//    XCD's L2.
+// metalworking MLX notes, QMM: dequantize weight tiles on chip, then a tiled
+// GEMM against them).  Two tile engines, both built on
+// v_mfma_f32_32x32x16_{bf16,f16} with binary32 accumulation (on gfx950 the
+// 32x32x16 form sustains about 1.7x the rate of 16x16x32) and on weights
+// dequantized exactly as aq_dequantize returns them (q*s + b in binary32,
+// rounded to nearest even into the activation type):
 //
-// The gather variant ("Quantization", metalworking: gather variants of the
-// kernels for MoE experts, here at prefill size) computes y[t, j, :] =
-// x[t] @ W_{ids[t, j]}^T with the same tile engine: one workgroup per
-// (224-column tile, expert) scans the routing ids on the device, lists the
-// (token, slot) pairs routed to its expert in id order, and runs 256-row
-// tiles over that list, loading X rows by token and storing Y rows by pair.
+// qmm_wr_kernel (the prefill product, aq_qmm): one 256-thread workgroup per
+// 256 x 256 tile of Y, one wave per SIMD.  Wave w owns the 64 columns
+// 64w .. 64w+63 for all 256 rows (8 x 2 blocks, 256 accumulation registers)
+// and dequantizes its own W chunks straight into the B operand, so no
+// weight passes through LDS.  Only the X tile is shared: each K step's
+// 256 x 64 slice is copied to LDS by direct global-to-LDS loads into one of
+// four stages, three steps ahead, as are the W chunks into register sets.
+// A step's loads are spread over its four 16-k slices, and the one barrier
+// per step waits only for the stage it needs.  When the tiles leave a last
+// round at most half full, those columns run as 128 x 256 tiles in a second
+// launch.
+//
+// qmm_kernel (the MoE gather at prefill size, "Quantization", metalworking:
+// gather variants of the kernels for MoE experts): y[t, j, :] =
+// x[t] @ W_{ids[t, j]}^T.  One workgroup per (224-column tile, expert) scans
+// the routing ids on the device, lists the (token, slot) pairs routed to its
+// expert in id order, and runs 256 x 224 tiles over that list: X rows loaded
+// by token (direct to LDS), the W tile dequantized once per tile into LDS
+// (both tiles double-buffered, 144-byte W rows so the fragment reads are
+// free of bank conflicts), four waves stacked along M with 2 x 7 blocks
+// each, Y rows stored by pair.
 #include "aq_device.hpp"
 #include "aq_internal.hpp"
 
