@@ -189,12 +189,12 @@ __device__ __forceinline__ uint4 permute_x(uint4 v) {
 }
 
 // one step (4 chunks) of one wave's K range, as loaded
-template <int NXL, int BITS, int R>
+template <int NXL, int BITS, int R, int XS>
 struct MStep {
   // per block of 16 rows.  4-bit: quarter h holds chunk c0 + h of row n16.
   // 8-bit: words 4r .. 4r+3 hold words 4 (h & 1) .. +3 of chunk c0 + 2r + (h >> 1)
   uint32_t cw[R][BITS];
-  uint4 xl[4 / NXL];   // x loads of the step, NXL MFMA slots each (natural pair order)
+  uint4 xl[XS][4 / NXL];  // x loads of the step per x set, NXL MFMA slots each (natural pair order)
 };
 
 // DPP row_ror: lane l of each row of 16 lanes receives the value of lane
@@ -218,17 +218,21 @@ __device__ __forceinline__ uint4 row_ror(uint4 v) {
 // chunk slot of an x load -- output rows >= XR are discarded, so A-operand
 // rows XR.. may hold anything, and one 16-byte load per lane carries
 // NXL = 16 / XR chunks (lanes XR s .. XR s + XR - 1 of a row of 16 hold chunk
-// slot s); a row rotation moves a slot to lanes 0.. .
+// slot s); a row rotation moves a slot to lanes 0.. .  XR = 32: two sets of
+// 16 x rows (the second 16 rows below the first), each weight chunk loaded
+// and unpacked once for both.
 template <typename XT, int BITS, int W, int GS, int XR, int R>
 struct MBlock {
   static constexpr int CPG = 1 << GS;  // chunks per group (G = 32 CPG)
   static constexpr int NG = 4 / CPG;   // groups per step
-  static constexpr int NXL = 16 / XR;
+  static constexpr int XS = XR == 32 ? 2 : 1;     // sets of x rows
+  static constexpr int XRS = XR == 32 ? 16 : XR;  // x rows per slot of one set
+  static constexpr int NXL = 16 / XRS;
   static constexpr int ROWS = 16 * R;
   // 8-bit with a group inside each 32-code chunk: a lane-half swap per
   // register pair keeps every MFMA inside one chunk (one group)
   static constexpr bool kSwap = BITS == 8 && GS == 0;
-  typedef MStep<NXL, BITS, R> Step;
+  typedef MStep<NXL, BITS, R, XS> Step;
 
   // first chunk of the codes behind MFMA slot j of the step at chunk c0 (the
   // slot is past K iff this chunk is), and quarter h's offset into its x row
@@ -246,6 +250,7 @@ struct MBlock {
   const uint16_t *sbl;  // LDS: scales [16 R][gpr], then at sbo the biases
   int64_t K, wpr, gpr;
   int nch, n16, h, c_beg, c_end, sbo;
+  uint32_t xset;  // bytes from one x set to the next (16 rows)
   // per-lane parts of the load offsets (the step's part is a scalar offset):
   // codes of block b; x of load t, and the chunk of its slot past c0
   uint32_t wv[R], xb[4 / NXL];
@@ -263,6 +268,7 @@ struct MBlock {
     rx = rx_;
     sbl = sbl_;
     sbo = sb_entries(ROWS, gpr);
+    xset = (uint32_t)(16 * K * 2);
     // this wave's K range, whole steps of 4 chunks (each a whole number of groups)
     c_beg = wave * (kw >> 5);
     c_end = c_beg + (kw >> 5) < nch ? c_beg + (kw >> 5) : nch;
@@ -271,7 +277,7 @@ struct MBlock {
 #pragma unroll
     for (int b = 0; b < R; ++b) wv[b] = (uint32_t)((int64_t)(16 * b + n16) * wpr * 4 + 16 * h);
 #pragma unroll
-    for (int t = 0; t < 4 / NXL; ++t) xj[t] = slot_chunk(0, t * NXL + n16 / XR);
+    for (int t = 0; t < 4 / NXL; ++t) xj[t] = slot_chunk(0, t * NXL + n16 / XRS);
   }
 
   // x rows for the next run: xro is the byte offset of the x row that chunk
@@ -279,7 +285,7 @@ struct MBlock {
   __device__ void set_x(uint32_t xro) {
 #pragma unroll
     for (int t = 0; t < 4 / NXL; ++t) {
-      const int j = t * NXL + n16 / XR;  // MFMA slot this lane's load carries
+      const int j = t * NXL + n16 / XRS;  // MFMA slot this lane's load carries
       xb[t] = xro + (uint32_t)slot_xoff(slot_chunk(0, j), j, h) * 2u;
     }
   }
@@ -336,17 +342,20 @@ struct MBlock {
       }
     const int lim = c_end - c0;
 #pragma unroll
-    for (int t = 0; t < 4 / NXL; ++t) {
-      const uint32_t xo = xj[t] < lim ? xb[t] : kOutside;
-      const u32x4v u = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)xo, (int)((uint32_t)c0 * 64u), 0);
-      st.xl[t] = make_uint4(u[0], u[1], u[2], u[3]);
-    }
+    for (int xs = 0; xs < XS; ++xs)
+#pragma unroll
+      for (int t = 0; t < 4 / NXL; ++t) {
+        const uint32_t xo = xj[t] < lim ? xb[t] + (uint32_t)xs * xset : kOutside;
+        const u32x4v u =
+            __builtin_amdgcn_raw_buffer_load_b128(rx, (int)xo, (int)((uint32_t)c0 * 64u), 0);
+        st.xl[xs][t] = make_uint4(u[0], u[1], u[2], u[3]);
+      }
   }
 
   // FULL: the step lies inside K (no group past its end to skip)
   template <bool FULL>
-  __device__ void compute(int c0, Step &st, f32x4v (&acc)[R], uint32_t vmask, uint32_t vmagic,
-                          uint4 ones) const {
+  __device__ void compute(int c0, Step &st, f32x4v (&acc)[XS][R], uint32_t vmask,
+                          uint32_t vmagic, uint4 ones) const {
     const float off = mm_traits<XT, BITS>::off;
 #pragma unroll
     for (int b = 0; b < R; ++b) {
@@ -365,32 +374,44 @@ struct MBlock {
           }
       }
     }
-    uint4 xp[4 / NXL];  // x loads in the k order of the B operand
+    uint4 xp[XS][4 / NXL];  // x loads in the k order of the B operand
 #pragma unroll
-    for (int t = 0; t < 4 / NXL; ++t) xp[t] = BITS == 4 ? permute_x(st.xl[t]) : st.xl[t];
+    for (int xs = 0; xs < XS; ++xs)
+#pragma unroll
+      for (int t = 0; t < 4 / NXL; ++t)
+        xp[xs][t] = BITS == 4 ? permute_x(st.xl[xs][t]) : st.xl[xs][t];
 #pragma unroll
     for (int q = 0; q < NG; ++q) {
       if (!FULL && c0 + q * CPG >= c_end) break;  // past K (uniform)
-      f32x4v xg = (f32x4v){0.f, 0.f, 0.f, 0.f}, pg[R];
+      f32x4v xg[XS], pg[XS][R];
 #pragma unroll
-      for (int b = 0; b < R; ++b) pg[b] = (f32x4v){0.f, 0.f, 0.f, 0.f};
+      for (int xs = 0; xs < XS; ++xs) {
+        xg[xs] = (f32x4v){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < R; ++b) pg[xs][b] = (f32x4v){0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
       for (int jj = 0; jj < CPG; ++jj) {
         const int j = q * CPG + jj;
-        uint4 xa = xp[j / NXL];
-        if constexpr (NXL == 2) {
-          if (j % 2 == 1) xa = row_ror<8>(xa);
-        } else if constexpr (NXL == 4) {
-          if (j % 4 == 1) xa = row_ror<12>(xa);
-          if (j % 4 == 2) xa = row_ror<8>(xa);
-          if (j % 4 == 3) xa = row_ror<4>(xa);
+        uint4 xa[XS];
+#pragma unroll
+        for (int xs = 0; xs < XS; ++xs) {
+          xa[xs] = xp[xs][j / NXL];
+          if constexpr (NXL == 2) {
+            if (j % 2 == 1) xa[xs] = row_ror<8>(xa[xs]);
+          } else if constexpr (NXL == 4) {
+            if (j % 4 == 1) xa[xs] = row_ror<12>(xa[xs]);
+            if (j % 4 == 2) xa[xs] = row_ror<8>(xa[xs]);
+            if (j % 4 == 3) xa[xs] = row_ror<4>(xa[xs]);
+          }
+          xg[xs] = mfma16<XT>(xa[xs], ones, xg[xs]);
         }
-        xg = mfma16<XT>(xa, ones, xg);
 #pragma unroll
         for (int b = 0; b < R; ++b) {
           const uint4 wb = BITS == 4 ? unpack_word(st.cw[b][j], vmask, vmagic)
                                      : unpack_bytes<XT>(st.cw[b][2 * j], st.cw[b][2 * j + 1], vmagic);
-          pg[b] = mfma16<XT>(xa, wb, pg[b]);
+#pragma unroll
+          for (int xs = 0; xs < XS; ++xs) pg[xs][b] = mfma16<XT>(xa[xs], wb, pg[xs][b]);
         }
       }
 #pragma unroll
@@ -399,8 +420,11 @@ struct MBlock {
         const float sc = f16_to_f32(sbl[li]), bi = f16_to_f32(sbl[sbo + li]);
         const float bo = __builtin_fmaf(-off, sc, bi);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc[b][e] = __builtin_fmaf(bo, xg[e], __builtin_fmaf(sc, pg[b][e], acc[b][e]));
+        for (int xs = 0; xs < XS; ++xs)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[xs][b][e] =
+                __builtin_fmaf(bo, xg[xs][e], __builtin_fmaf(sc, pg[xs][b][e], acc[xs][b][e]));
       }
     }
   }
@@ -413,7 +437,7 @@ struct MBlock {
   // past the wave's range the offset lies outside the resource, so the load
   // returns zeros and touches no memory.
   // loads one prologue issues per thread
-  static constexpr int kStepLoads = R * (BITS / 4) + 4 / NXL;
+  static constexpr int kStepLoads = R * (BITS / 4) + XS * 4 / NXL;
 
   template <int D>
   __device__ void prologue(uint32_t xro, Step (&st)[D]) {
@@ -425,15 +449,17 @@ struct MBlock {
     }
   }
 
-  // partial sums of this wave's K range; lane (n16, h) gets in acc[b] output
-  // rows m = 4 h + e of x against W row 16 b + n16
+  // partial sums of this wave's K range; lane (n16, h) gets in acc[xs][b]
+  // output rows m = 16 xs + 4 h + e of x against W row 16 b + n16
   template <int D>
-  __device__ void finish(Step (&st)[D], f32x4v (&acc)[R]) const {
+  __device__ void finish(Step (&st)[D], f32x4v (&acc)[XS][R]) const {
     const uint32_t vmask = opaque(0x000F000Fu), vmagic = opaque(mm_traits<XT, BITS>::magic);
     const uint32_t vones = opaque(mm_traits<XT, BITS>::ones);
     const uint4 ones = make_uint4(vones, vones, vones, vones);
 #pragma unroll
-    for (int b = 0; b < R; ++b) acc[b] = (f32x4v){0.f, 0.f, 0.f, 0.f};
+    for (int xs = 0; xs < XS; ++xs)
+#pragma unroll
+      for (int b = 0; b < R; ++b) acc[xs][b] = (f32x4v){0.f, 0.f, 0.f, 0.f};
     // steady state: all D buffered steps are whole steps inside the range, so
     // the body has no branch (a branch around a step makes the compiler's
     // load-counter bookkeeping wait for later steps' loads as well)
@@ -466,16 +492,20 @@ inline size_t qmvm_lds_bytes(int W, int R, int64_t K, int G, int MR = 8) {
 // sum the W waves' partial sums (lanes h < 2 hold output rows 0..7) through
 // LDS (part: [W][16 R][8] floats, free for this use); out(n, m, v) receives
 // row n of the 16 R, x row m < 8, value v
-// MR: x rows kept (8, or 16 when every lane's 4 rows count)
-template <int W, int R, int MR, typename F>
+// MR: x rows kept (8, 16 when every lane's 4 rows count, 32 with two x sets
+// of 16: XS = 2)
+template <int W, int R, int MR, int XS, typename F>
 __device__ __forceinline__ void reduce_out(float *part, int wave, int lane,
-                                           const f32x4v (&acc)[R], F out) {
+                                           const f32x4v (&acc)[XS][R], F out) {
   const int n16 = lane & 15, h = lane >> 4;
-  if (h < MR / 4) {
+  if (h < MR / XS / 4) {
 #pragma unroll
-    for (int b = 0; b < R; ++b)
+    for (int xs = 0; xs < XS; ++xs)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) part[(wave * 16 * R + 16 * b + n16) * MR + 4 * h + e] = acc[b][e];
+      for (int b = 0; b < R; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          part[(wave * 16 * R + 16 * b + n16) * MR + 16 * xs + 4 * h + e] = acc[xs][b][e];
   }
   __syncthreads();
   for (int i = threadIdx.x; i < 16 * R * MR; i += 64 * W) {
@@ -486,8 +516,8 @@ __device__ __forceinline__ void reduce_out(float *part, int wave, int lane,
   }
 }
 
-// S > 1 (XR = 16): x has up to 16 S rows, run as S slices of 16 rows; the
-// S slices of one block of W rows are consecutive workgroups of one XCD
+// S > 1 (XR = 16 or 32): x has up to XR S rows, run as S slices of XR rows;
+// the S slices of one block of W rows are consecutive workgroups of one XCD
 // (block b runs on XCD b % 8), so that block is read from HBM once and the
 // other slices find it in that XCD's L2.
 template <typename XT, int BITS, int W, int GS, int XR, int R>
@@ -499,7 +529,7 @@ __global__ __launch_bounds__(64 * W) void qmvm_kernel(const uint16_t *__restrict
                                                       uint16_t *__restrict__ y, int S) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // [2][16 R][gpr]; then partials
   typedef MBlock<XT, BITS, W, GS, XR, R> Blk;
-  constexpr int MR = XR == 16 ? 16 : 8;
+  constexpr int MR = XR >= 16 ? XR : 8;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int64_t rb = blockIdx.x;
@@ -507,9 +537,9 @@ __global__ __launch_bounds__(64 * W) void qmvm_kernel(const uint16_t *__restrict
     const int64_t k = blockIdx.x >> 3;
     const int sl = (int)(k % S);
     rb = (k / S) * 8 + (blockIdx.x & 7);
-    x += (int64_t)sl * 16 * K;
-    y += (int64_t)sl * 16 * N;
-    M = M - 16 * sl < 16 ? M - 16 * sl : 16;
+    x += (int64_t)sl * XR * K;
+    y += (int64_t)sl * XR * N;
+    M = M - XR * sl < XR ? M - XR * sl : XR;
   }
   const int64_t row0 = rb * Blk::ROWS;
   if (row0 >= N) return;  // padding of the slice mapping (uniform, before any barrier)
@@ -518,7 +548,7 @@ __global__ __launch_bounds__(64 * W) void qmvm_kernel(const uint16_t *__restrict
   Blk blk;
   blk.setup(codes + row0 * (K >> 5) * BITS, nrows, K, kw, wave, lane, lds,
             mk_rsrc(x, (int64_t)M * K * 2));  // rows of x past M read as zero
-  const uint32_t xro = (uint32_t)((int64_t)((lane & 15) % XR) * K * 2);
+  const uint32_t xro = (uint32_t)((int64_t)((lane & 15) % Blk::XRS) * K * 2);
   constexpr int D = kDepth<BITS>;
   typename Blk::Step st[D];
   // staging first, then the first steps' loads: one round trip covers both
@@ -528,10 +558,10 @@ __global__ __launch_bounds__(64 * W) void qmvm_kernel(const uint16_t *__restrict
   Blk::template stage_sb_wait<D * Blk::kStepLoads>(scales + row0 * gpr, biases + row0 * gpr,
                                                    nrows, gpr, lds);
   __syncthreads();
-  f32x4v acc[R];
+  f32x4v acc[Blk::XS][R];
   blk.template finish<D>(st, acc);
   __syncthreads();  // every wave is done with the staged scales
-  reduce_out<W, R, MR>(reinterpret_cast<float *>(lds), wave, lane, acc, [&](int nn, int m, float v) {
+  reduce_out<W, R, MR, Blk::XS>(reinterpret_cast<float *>(lds), wave, lane, acc, [&](int nn, int m, float v) {
     if (m < M && row0 + nn < N) y[(int64_t)m * N + row0 + nn] = xtraits<XT>::from_f32(v);
   });
 }
@@ -604,9 +634,9 @@ __global__ __launch_bounds__(64 * W) void gather_qmvm_kernel(
                                       : (uint32_t)(T * K * 2);
       typename Blk::Step st[D];
       blk.template prologue<D>(xro, st);
-      f32x4v acc[R];
+      f32x4v acc[1][R];
       blk.template finish<D>(st, acc);
-      reduce_out<W, R, 8>(part, wave, lane, acc, [&](int nn, int mm, float v) {
+      reduce_out<W, R, 8, 1>(part, wave, lane, acc, [&](int nn, int mm, float v) {
         if (b0 + mm < n && row0 + nn < N)
           y[(t0 + list[b0 + mm]) * N + row0 + nn] = xtraits<XT>::from_f32(v);
       });
@@ -621,11 +651,11 @@ hipError_t qmvm_go(const void *x, int M, const uint32_t *codes, const uint16_t *
   const int64_t steps = (K + kStepK - 1) / kStepK;
   const int kw = (int)((steps + W - 1) / W) * kStepK;  // k per wave, whole steps
   const int64_t blocks = (N + 16 * R - 1) / (16 * R);
-  const int S = XR == 16 ? (M + 15) / 16 : 1;  // slices of 16 x rows
+  const int S = XR >= 16 ? (M + XR - 1) / XR : 1;  // slices of XR x rows
   const int64_t grid_blocks = S > 1 ? (blocks + 7) / 8 * 8 * S : blocks;
   if (grid_blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)grid_blocks), block(64 * W);
-  const size_t lds = qmvm_lds_bytes(W, R, K, G, XR == 16 ? 16 : 8);
+  const size_t lds = qmvm_lds_bytes(W, R, K, G, XR >= 16 ? XR : 8);
   switch (G) {
     case 32: hipLaunchKernelGGL((qmvm_kernel<XT, BITS, W, 0, XR, R>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y, S); break;
     case 64: hipLaunchKernelGGL((qmvm_kernel<XT, BITS, W, 1, XR, R>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y, S); break;
@@ -667,30 +697,37 @@ constexpr size_t kMaxStagedLds = 64 * 1024;
 
 bool qmvm_supported(int M, int bits, int64_t N, int64_t K, int G) {
   return M >= 2 && M <= kQmvmMaxRows && (bits == 4 || bits == 8) && N >= 1 && K >= 32 &&
-         16 * K * 2 <= 0x7FFFFFFF && qmvm_lds_bytes(16, 1, K, G, 16) <= kMaxStagedLds;
+         32 * K * 2 <= 0x7FFFFFFF && qmvm_lds_bytes(16, 1, K, G, 32) <= kMaxStagedLds;
 }
 
 bool qmvm_preferred(int64_t M, int bits, int64_t N, int64_t K, int G) {
-  // Past 8 rows each slice of 16 x rows costs about one few-row pass over W
-  // (11-14 us at 14336 x 4096 or 4096 x 14336, 4-bit and 8-bit, on the
-  // MI355X), while the tiled kernel computes whole 256 x 224 tiles: at most
-  // 256 rows it runs ceil(N / 224) workgroups for the time of one tile
-  // (115 us at K = 4096, 345 us at K = 14336, the chip a quarter full or
-  // less).  Measured crossover: 128 < M < 192 at N = 14336; with fewer
-  // workgroups than a quarter of the compute units the slices win to 256.
+  // Past 8 rows each slice of x rows costs about one pass over W (11-14 us at
+  // 14336 x 4096 and 4096 x 14336, 4-bit and 8-bit, on the MI355X), while the
+  // prefill kernel computes whole 256 x 256 tiles, ceil(N / 256) of them per
+  // 256 rows: at most 256 rows it takes 62-68 us at 14336 x 4096 and about
+  // 200 us at 4096 x 14336 (16 tiles).  Measured crossover: M = 96 .. 128 at
+  // N = 14336; with fewer tiles than an eighth of the compute units the
+  // slices win up to 256 rows.
   if (M > kQmvmMaxRows || !qmvm_supported((int)M, bits, N, K, G)) return false;
-  const int64_t qmm_wgs = (M + 255) / 256 * ((N + 223) / 224);
-  return M <= 128 || qmm_wgs * 4 < device_cus();
+  const int64_t qmm_tiles = (M + 255) / 256 * ((N + 255) / 256);
+  return M <= 64 || qmm_tiles * 8 < device_cus();
 }
 
 void qmvm_shape(int M, int bits, int64_t N, int64_t K, int G, int &R, int &W, int &XR) {
-  XR = M <= 4 ? 4 : M <= 8 ? 8 : 16;
-  const int64_t S = (M + 15) / 16;  // slices of 16 x rows (XR = 16)
-  if (XR == 16) {
-    // 16 rows per slot: two blocks of 16 rows over 4 waves whenever that
-    // still gives a workgroup per compute unit (measured best at
+  // Past 16 rows, two sets of 16 x rows per wave (each weight chunk loaded
+  // and unpacked once for 32 rows of x) when the slices of 32 still fill the
+  // chip with two row blocks per workgroup; else slices of 16.  Measured at
+  // 14336 x 4096, 4-bit: M = 17 / 32 / 128 take 19.8 / 24.6 / 72.6 us in
+  // slices of 32, 27.1 / 28.0 / 83.9 us in slices of 16; at 4096 x 14336,
+  // M = 17 .. 32, slices of 16 are faster (23.6 .. 24.4 against 24.9 .. 33.6).
+  XR = M <= 4 ? 4 : M <= 8 ? 8 : M <= 16 ? 16
+       : (N + 31) / 32 * ((M + 31) / 32) >= device_cus() ? 32 : 16;
+  const int64_t S = XR >= 16 ? (M + XR - 1) / XR : 1;  // slices of XR x rows
+  if (XR >= 16) {
+    // 16 or 32 rows per slot: two blocks of 16 rows over 4 waves whenever
+    // that still gives a workgroup per compute unit (measured best at
     // 14336 x 4096 from M = 9 and at 4096 x 14336 from M = 17, both widths)
-    if ((N + 31) / 32 * S >= device_cus() && qmvm_lds_bytes(4, 2, K, G, 16) <= kMaxStagedLds) {
+    if ((N + 31) / 32 * S >= device_cus() && qmvm_lds_bytes(4, 2, K, G, XR) <= kMaxStagedLds) {
       R = 2;
       W = 4;
       return;
@@ -734,10 +771,10 @@ hipError_t launch_qmvm(const void *x, int x_dtype, int M, const uint32_t *codes,
 #define AQ_QMVM(T) \
   if (bits == 4) { \
     if (XR == 4) { AQ_QMVM_R(T, 4, 4) } else if (XR == 8) { AQ_QMVM_R(T, 4, 8) } \
-    else { AQ_QMVM_R(T, 4, 16) } \
+    else if (XR == 16) { AQ_QMVM_R(T, 4, 16) } else { AQ_QMVM_R(T, 4, 32) } \
   } else { \
     if (XR == 4) { AQ_QMVM_R(T, 8, 4) } else if (XR == 8) { AQ_QMVM_R(T, 8, 8) } \
-    else { AQ_QMVM_R(T, 8, 16) } \
+    else if (XR == 16) { AQ_QMVM_R(T, 8, 16) } else { AQ_QMVM_R(T, 8, 32) } \
   }
   if (x_dtype == X_BF16) { AQ_QMVM(bf16_t) }
   if (x_dtype == X_F16) { AQ_QMVM(f16_t) }

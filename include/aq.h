@@ -169,10 +169,10 @@ aq_status aq_qmm(const void *x, aq_dtype x_dtype, int64_t M, const uint32_t *cod
 /* Shape dispatch for y = x @ W^T ("Quantization", metalworking: host-side
  * dispatch picks the kernel per shape): M <= 8 goes to the matrix-vector
  * kernels of aq_qmv.  For 9 <= M <= 256 with 4-bit or 8-bit codes, while
- * aq_qmm's 256 x 224 output tiles would leave most of the chip idle (M <= 128,
- * or fewer tiles than a quarter of the compute units), the few-row
- * matrix-core kernel of aq_qmv runs on slices of 16 rows of x (binary32
- * accumulation, the same bound).  Otherwise aq_qmm.  Same arguments as aq_qmv
+ * aq_qmm's 256 x 256 output tiles would be mostly empty or too few for the
+ * chip (M <= 64, or fewer tiles than an eighth of the compute units), the
+ * few-row matrix-core kernel of aq_qmv runs on slices of 16 or 32 rows of x
+ * (binary32 accumulation, the same bound).  Otherwise aq_qmm.  Same arguments as aq_qmv
  * with any M >= 1; may query the current device's compute-unit count. */
 aq_status aq_quantized_matmul(const void *x, aq_dtype x_dtype, int64_t M, const uint32_t *codes,
                               const uint16_t *scales, const uint16_t *biases, int64_t N,

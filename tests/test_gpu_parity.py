@@ -266,10 +266,12 @@ def test_matmul_few_rows_sliced(aq, xdt, bits, G, K):
 
 @pytest.mark.parametrize("bits,G", [(4, 64), (8, 128)])
 def test_matmul_few_rows_sliced_tall(aq, bits, G):
-    """Tall matrices (two 16-row blocks per workgroup) at 16..64 rows."""
+    """Tall matrices (two 16-row blocks per workgroup) at 16..64 rows: past 16
+    rows two sets of 16 x rows per wave (slices of 32; 40 rows leave the
+    second slice's second set empty)."""
     N, K = 8200, 256
     _, (c, s, b) = _quantized(N, K, G, bits, seed=22)
-    for M in (16, 24, 64):
+    for M in (16, 24, 40, 64):
         xb = inputs.activations(M, K, "f16", seed=22, key=(bits, G, M))
         y_ref, A = oracle.matmul(inputs.from_bits(xb, "f16"), c, s, b, K, G, bits)
         y = aq.aq_quantized_matmul(bits_to_dev(xb, "f16"), *packed_to_dev(c, s, b), G, bits)
