@@ -3,33 +3,28 @@
 //
 // The operation is Y = X @ W^T with W in packed form ("Quantization",
 // metalworking MLX notes, QMM: dequantize weight tiles on chip, then a tiled
-// GEMM against them).  Two tile engines, both built on
-// v_mfma_f32_32x32x16_{bf16,f16} with binary32 accumulation (on gfx950 the
-// 32x32x16 form sustains about 1.7x the rate of 16x16x32) and on weights
-// dequantized exactly as aq_dequantize returns them (q*s + b in binary32,
-// rounded to nearest even into the activation type):
+// GEMM against them), built on v_mfma_f32_32x32x16_{bf16,f16} with binary32
+// accumulation (on gfx950 the 32x32x16 form sustains about 1.7x the rate of
+// 16x16x32) and on weights dequantized exactly as aq_dequantize returns them
+// (q*s + b in binary32, rounded to nearest even into the activation type).
 //
-// qmm_wr_kernel (the prefill product, aq_qmm): one 256-thread workgroup per
-// 256 x 256 tile of Y, one wave per SIMD.  Wave w owns the 64 columns
-// 64w .. 64w+63 for all 256 rows (8 x 2 blocks, 256 accumulation registers)
-// and dequantizes its own W chunks straight into the B operand, so no
-// weight passes through LDS.  Only the X tile is shared: each K step's
-// 256 x 64 slice is copied to LDS by direct global-to-LDS loads into one of
-// four stages, three steps ahead, as are the W chunks into register sets.
-// A step's loads are spread over its four 16-k slices, and the one barrier
-// per step waits only for the stage it needs.  When the tiles leave a last
-// round at most half full, those columns run as 128 x 256 tiles in a second
-// launch.
+// qmm_wr_kernel: one 256-thread workgroup per 256 x 256 tile of Y, one wave
+// per SIMD.  Wave w owns the 64 columns 64w .. 64w+63 for all 256 rows
+// (8 x 2 blocks, 256 accumulation registers) and dequantizes its own W
+// chunks straight into the B operand, so no weight passes through LDS.
+// Only the X tile is shared: each K step's 256 x 64 slice is copied to LDS
+// by direct global-to-LDS loads into one of four stages, three steps ahead,
+// as are the W chunks into register sets.  A step's loads are spread over
+// its four 16-k slices, and the one barrier per step waits only for the
+// stage it needs.  When the tiles leave a last round at most half full,
+// those columns run as 128 x 256 tiles in a second launch.
 //
-// qmm_kernel (the MoE gather at prefill size, "Quantization", metalworking:
-// gather variants of the kernels for MoE experts): y[t, j, :] =
-// x[t] @ W_{ids[t, j]}^T.  One workgroup per (224-column tile, expert) scans
-// the routing ids on the device, lists the (token, slot) pairs routed to its
-// expert in id order, and runs 256 x 224 tiles over that list: X rows loaded
-// by token (direct to LDS), the W tile dequantized once per tile into LDS
-// (both tiles double-buffered, 144-byte W rows so the fragment reads are
-// free of bank conflicts), four waves stacked along M with 2 x 7 blocks
-// each, Y rows stored by pair.
+// The gather variant ("Quantization", metalworking: gather variants of the
+// kernels for MoE experts, here at prefill size) computes y[t, j, :] =
+// x[t] @ W_{ids[t, j]}^T on the same engine: one workgroup per (256-column
+// tile, expert) scans the routing ids on the device, lists the (token, slot)
+// pairs routed to its expert in id order, and runs 256-row tiles over that
+// list, loading X rows by token and storing Y rows by pair.
 #include "aq_device.hpp"
 #include "aq_internal.hpp"
 
@@ -40,18 +35,8 @@ typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8v __attribute__((ext_vector_type(8)));
 typedef float f32x16v __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 256, BN = 224, BK = 64;
-constexpr int WM = 64, WN = 224;            // wave sub-tile
-constexpr int FM = WM / 32, FN = WN / 32;   // 32x32 blocks per wave: 2 x 7
+constexpr int BM = 256, BK = 64;  // tile rows (full tiles), K step
 constexpr int kThreads = 256;
-// LDS: [X stage 0][X stage 1][W stage 0][W stage 1]
-constexpr int kXStage = BM * BK * 2;            // 32 KB: 128-byte rows, 16-byte units swizzled
-constexpr int kWPitch = (BK + 8) * 2;           // 144-byte W rows
-constexpr int kWRows = 256;                     // rows >= BN are written, never read
-constexpr int kWStage = kWRows * kWPitch;       // 36 KB
-static_assert(2 * (kXStage + kWStage) <= 160 * 1024, "LDS");
-constexpr int kXDma = BM * BK / 8 / kThreads;   // 16-byte X units per thread per step: 8
-constexpr int kWChunks = 2;                     // 32-code W chunks per thread per step
 
 // loads issued for one W chunk (codes, scale, bias)
 template <int BITS>
@@ -155,31 +140,6 @@ __device__ __forceinline__ void bload_chunk(__amdgpu_buffer_rsrc_t r, uint32_t v
   }
 }
 
-// one thread's W chunks of one K step, as loaded
-template <int BITS>
-struct WRegs {
-  uint32_t w[kWChunks][BITS];
-  uint32_t s[kWChunks], b[kWChunks];
-};
-
-// Scheduling hint for one segment of 14 MFMAs: NR LDS reads and NG global
-// loads among the first slots, NV vector ALU instructions after each MFMA,
-// NW LDS writes among the last slots.
-template <int NR, int NV, int NW, int NG>
-__device__ __forceinline__ void sched_segment() {
-#pragma unroll
-  for (int i = 0; i < FM * FN; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    if (i < NG) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    if (NV > 0) __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
-    if (i >= FM * FN - NW) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-  }
-}
-// vector instructions to dequantize 8 codes (approximate)
-template <int BITS>
-constexpr int kDequant8Valu = BITS == 4 ? 24 : (BITS == 8 ? 22 : 30);
-
 // routing of the gather variant: ids [T, topk] flattened, experts [0, E)
 struct Routing {
   const int32_t *ids;
@@ -209,331 +169,6 @@ __device__ __forceinline__ int block_exclusive_sum(int v, int *wsum, int *total)
   }
   *total = all;
   return before + incl - v;
-}
-
-template <int BITS, typename XT, bool GATHER>
-__global__ __launch_bounds__(kThreads) void qmm_kernel(const uint16_t *__restrict__ x, int64_t M,
-                                                       const uint32_t *__restrict__ codes,
-                                                       const uint16_t *__restrict__ scales,
-                                                       const uint16_t *__restrict__ biases,
-                                                       int64_t N, int64_t K, int G,
-                                                       uint16_t *__restrict__ y, int mtiles,
-                                                       int ntiles, Routing route) {
-  // four distinct LDS objects, so the compiler can tell the DMA target of a
-  // step from the buffers read and written beside it
-  __shared__ __attribute__((aligned(16))) char xs0[kXStage], xs1[kXStage];
-  __shared__ __attribute__((aligned(16))) char ws0[kWStage], ws1[kWStage];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave;
-
-  const int nch = (int)(K >> 5), gshift = __builtin_ctz((unsigned)G) - 5;
-  const int64_t wpr = (int64_t)nch * BITS, gpr = nch >> gshift;
-  const int ksteps = (int)((K + BK - 1) / BK);
-
-  int64_t tile_m = 0, tile_n;
-  int expert = 0;
-  if constexpr (!GATHER) {
-    // XCD-aware tile order: block b runs on XCD b % 8; consecutive blocks of
-    // one XCD take consecutive tiles of a row-major (m, n) order, so they
-    // share m (the X row tile stays in that XCD's L2).
-    const int tiles = mtiles * ntiles;
-    int t = blockIdx.x;
-    if ((tiles & 7) == 0) t = (t & 7) * (tiles >> 3) + (t >> 3);
-    tile_m = (int64_t)(t / ntiles) * BM;
-    tile_n = (int64_t)(t % ntiles) * BN;
-  } else {
-    tile_n = (int64_t)blockIdx.x * BN;
-    expert = blockIdx.y;
-    codes += expert * N * wpr;
-    scales += expert * N * gpr;
-    biases += expert * N * gpr;
-  }
-
-  // operand tiles as buffer resources: rows past M or N read as zero (the
-  // gather variant addresses all of x by token)
-  const int64_t mrows = M - tile_m < BM ? M - tile_m : BM;
-  const int64_t nrows = N - tile_n < BN ? N - tile_n : BN;
-  const int xbytes = (int)((GATHER ? M : mrows) * K * 2);
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + tile_m * K, xbytes);
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(codes + tile_n * wpr, nrows * wpr * 4);
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(scales + tile_n * gpr, nrows * gpr * 2);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(biases + tile_n * gpr, nrows * gpr * 2);
-
-  // K steps: when K % 64 == 32 the lone last chunk is processed first (step
-  // 0, masked in the prologue), so every later step is full.
-  const bool ktail = (K % BK) != 0;
-  const int koff = ktail ? BK : 0;
-  auto kbase = [&](int st) -> int {  // first k of step st
-    return ktail && st == 0 ? (int)K - 32 : st * BK - koff;
-  };
-  auto kfull = [&](int st) -> int { return st * BK - koff; };  // st >= 1, branch-free
-
-  // X: each step's 256 x 64 tile goes straight to LDS (16 bytes per lane per
-  // load, landing at consecutive 16-byte slots).  LDS row r holds the row's
-  // unit u at slot u ^ ((r >> 1) & 7), so the fragment reads below are free
-  // of bank conflicts; load i of wave w fills rows 8 (8w + i) .. +7.
-  uint32_t xvoff[kXDma], xvoff_tail[kXDma];
-  __shared__ int glist[GATHER ? kGList : 1];  // pairs of the expert in this pass
-  // row r of the tile at list position r0 is x row r (plain) or the token of
-  // pair glist[r0 + r] (gather); rows >= rows read as zero
-  auto set_rows = [&](int r0, int rows) {
-#pragma unroll
-    for (int i = 0; i < kXDma; ++i) {
-      const int row = 8 * (wave * kXDma + i) + (lane >> 3);
-      const int u = (lane & 7) ^ ((row >> 1) & 7);
-      uint32_t ro;
-      if constexpr (GATHER)
-        ro = row < rows ? (uint32_t)((int64_t)(glist[r0 + row] / route.topk) * K * 2)
-                        : (uint32_t)xbytes;
-      else
-        ro = (uint32_t)(row * K * 2);
-      xvoff[i] = ro + (uint32_t)u * 16u;
-      xvoff_tail[i] = u < 4 ? xvoff[i] : (uint32_t)xbytes;  // k past K: out of range, reads zero
-    }
-  };
-  auto dma_x = [&](int k0, int buf, const uint32_t (&vo)[kXDma]) {
-    const uint32_t so = (uint32_t)k0 * 2u;
-#pragma unroll
-    for (int i = 0; i < kXDma; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rx, (lds_void *)((buf ? xs1 : xs0) + (wave * kXDma + i) * 1024), 16, (int)vo[i], (int)so,
-          0, 0);
-  };
-
-  // W: thread chunk c (0, 1) is LDS row (tid + 256 c) / 2, half (tid & 1)
-  uint32_t wvoff[kWChunks], svoff[kWChunks];
-#pragma unroll
-  for (int c = 0; c < kWChunks; ++c) {
-    const int ch = tid + kThreads * c, row = ch >> 1, half = ch & 1;
-    wvoff[c] = (uint32_t)(row * wpr + half * BITS) * 4u;
-    svoff[c] = (uint32_t)(row * gpr + (gshift == 0 ? half : 0)) * 2u;
-  }
-  auto load_w_chunk = [&](int k0, int c, WRegs<BITS> &r) {
-    const int c0 = k0 >> 5;
-    bload_chunk<BITS>(rw, wvoff[c], (uint32_t)(c0 * BITS) * 4u, r.w[c]);
-    const uint32_t so = (uint32_t)(c0 >> gshift) * 2u;
-    r.s[c] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)svoff[c], (int)so, 0);
-    r.b[c] = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)svoff[c], (int)so, 0);
-  };
-  // dequantize codes 8u .. 8u+7 of chunk c into W stage `buf`
-  const uint32_t nmask = opaque(0x0F0F0F0Fu);
-  auto store_w8 = [&](const WRegs<BITS> &r, int c, auto ucon, int buf, bool zero) {
-    constexpr int U = decltype(ucon)::value;
-    const int ch = tid + kThreads * c, row = ch >> 1, half = ch & 1;
-    const uint4 v = dequant8<BITS, XT, U>(r.w[c], f16_to_f32((uint16_t)r.s[c]),
-                                          f16_to_f32((uint16_t)r.b[c]), nmask);
-    *reinterpret_cast<uint4 *>((buf ? ws1 : ws0) + row * kWPitch + half * 64 + U * 16) =
-        zero ? make_uint4(0, 0, 0, 0) : v;
-  };
-  using U0 = std::integral_constant<int, 0>;
-  using U1 = std::integral_constant<int, 1>;
-  using U2 = std::integral_constant<int, 2>;
-  using U3 = std::integral_constant<int, 3>;
-
-  // one 256 x 224 tile: rows from list position r0 (gather) or x row tile_m
-  auto tile = [&](int r0, int rows) {
-  set_rows(r0, rows);
-  f32x16v acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  // fragments: lane l supplies row (l % 32) of a 32-row block and k units
-  // (l / 32) + 2 kk of the step (8 k each)
-  const int xrow = wm * WM + (lane & 31);
-  uint32_t xfo[4];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-    xfo[kk] = (uint32_t)(xrow * 128 + ((((lane >> 5) + 2 * kk) ^ ((lane >> 1) & 7)) * 16));
-  const uint32_t wfo = (uint32_t)((lane & 31) * kWPitch + (lane >> 5) * 16);
-  auto frag = [&](int buf, int kk, uint4(&a)[FM], uint4(&b)[FN]) {
-    const char *lx = (buf ? xs1 : xs0) + xfo[kk];
-    const char *lw = (buf ? ws1 : ws0) + wfo + kk * 32;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) a[i] = *reinterpret_cast<const uint4 *>(lx + i * 32 * 128);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) b[j] = *reinterpret_cast<const uint4 *>(lw + j * 32 * kWPitch);
-  };
-  auto mfma_kk = [&](const uint4(&a)[FM], const uint4(&b)[FN]) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int i = 0; i < FM; ++i) acc[i][j] = mfma32<XT>(a[i], b[j], acc[i][j]);
-  };
-
-  WRegs<BITS> wr[2];  // W of step s lives in wr[s & 1]
-  auto last = [&](int st) { return st < ksteps ? st : ksteps - 1; };
-
-  // One K step st from LDS stage cb.  With one wave per SIMD, matrix-core and
-  // vector work overlap only through this wave's own instruction order, so
-  // the step is cut into four fenced segments, one per 16-k slice: each issues
-  // the fragment reads of the next slice, then its 14 MFMAs with a quarter of
-  // the next step's work between them.  With `more`, step st + 1 is prepared
-  // in stage cb ^ 1: its X by DMA at the start, its W (loaded a step ago)
-  // dequantized 8 codes at a time; the W registers are then reloaded for
-  // step st + 3.  The DMA is waited for before the step ends (the barrier
-  // after it publishes stage cb ^ 1); the W loads stay in flight.
-  auto step = [&](auto cbcon, bool more, int st) {
-    constexpr int cb = decltype(cbcon)::value;
-    WRegs<BITS> &wn = wr[(cb + 1) & 1];  // st has the parity of cb
-    uint4 fa[2][FM], fb[2][FN];
-    frag(cb, 0, fa[0], fb[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    frag(cb, 1, fa[1], fb[1]);
-    if (more) dma_x(kfull(st + 1), cb ^ 1, xvoff);
-    mfma_kk(fa[0], fb[0]);
-    if (more) {
-      store_w8(wn, 0, U0{}, cb ^ 1, false);
-      store_w8(wn, 0, U1{}, cb ^ 1, false);
-    }
-    sched_segment<FM + FN, 2 * kDequant8Valu<BITS> / (FM * FN), 2, kXDma>();
-    __builtin_amdgcn_sched_barrier(0);
-    frag(cb, 2, fa[0], fb[0]);
-    mfma_kk(fa[1], fb[1]);
-    if (more) {
-      store_w8(wn, 0, U2{}, cb ^ 1, false);
-      store_w8(wn, 0, U3{}, cb ^ 1, false);
-      load_w_chunk(kfull(last(st + 3)), 0, wn);
-    }
-    sched_segment<FM + FN, 2 * kDequant8Valu<BITS> / (FM * FN), 2, 0>();
-    __builtin_amdgcn_sched_barrier(0);
-    frag(cb, 3, fa[1], fb[1]);
-    mfma_kk(fa[0], fb[0]);
-    if (more) {
-      store_w8(wn, 1, U0{}, cb ^ 1, false);
-      store_w8(wn, 1, U1{}, cb ^ 1, false);
-    }
-    sched_segment<FM + FN, 2 * kDequant8Valu<BITS> / (FM * FN), 2, 0>();
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_kk(fa[1], fb[1]);
-    if (more) {
-      store_w8(wn, 1, U2{}, cb ^ 1, false);
-      store_w8(wn, 1, U3{}, cb ^ 1, false);
-      load_w_chunk(kfull(last(st + 3)), 1, wn);
-    }
-    sched_segment<0, 2 * kDequant8Valu<BITS> / (FM * FN), 2, 0>();
-    __builtin_amdgcn_sched_barrier(0);
-    if (more) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kWChunks * kChunkLoads<BITS>));
-  };
-
-  // prologue: step 0 into stage 0 (masked past K when it is the tail chunk),
-  // W of steps 1 and 2 in flight
-  dma_x(kbase(0), 0, ktail ? xvoff_tail : xvoff);
-  load_w_chunk(kbase(0), 0, wr[0]);
-  load_w_chunk(kbase(0), 1, wr[0]);
-  load_w_chunk(kbase(last(1)), 0, wr[1]);
-  load_w_chunk(kbase(last(1)), 1, wr[1]);
-  const bool zhalf = ktail && (tid & 1);  // both chunks of a thread are in the same half
-  store_w8(wr[0], 0, U0{}, 0, zhalf);
-  store_w8(wr[0], 0, U1{}, 0, zhalf);
-  store_w8(wr[0], 0, U2{}, 0, zhalf);
-  store_w8(wr[0], 0, U3{}, 0, zhalf);
-  store_w8(wr[0], 1, U0{}, 0, zhalf);
-  store_w8(wr[0], 1, U1{}, 0, zhalf);
-  store_w8(wr[0], 1, U2{}, 0, zhalf);
-  store_w8(wr[0], 1, U3{}, 0, zhalf);
-  load_w_chunk(kbase(last(2)), 0, wr[0]);
-  load_w_chunk(kbase(last(2)), 1, wr[0]);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kWChunks * kChunkLoads<BITS>));
-  __syncthreads();
-
-  using C0 = std::integral_constant<int, 0>;
-  using C1 = std::integral_constant<int, 1>;
-  int st = 0;
-  for (; st + 2 < ksteps; st += 2) {
-    step(C0{}, true, st);
-    __syncthreads();
-    step(C1{}, true, st + 1);
-    __syncthreads();
-  }
-  if (st + 1 < ksteps) {
-    step(C0{}, true, st);
-    __syncthreads();
-    step(C1{}, false, st + 1);
-  } else {
-    step(C0{}, false, st);
-  }
-
-  // epilogue: accumulator r of lane l in a 32x32 block is row
-  // 8*(r/4) + 4*(l/32) + r%4, column l % 32 (2-byte stores; staging the tile
-  // through LDS for 16-byte stores measured slower)
-  if constexpr (!GATHER) {
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int64_t n = tile_n + j * 32 + (lane & 31);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t m = tile_m + wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (m < M && n < N) y[m * N + n] = xtraits<XT>::from_f32(acc[i][j][r]);
-      }
-    }
-  } else {
-    // row lr of the tile is pair glist[r0 + lr]: y row of that (token, slot)
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int lr = wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (lr < rows) {
-          uint16_t *yr = y + (int64_t)glist[r0 + lr] * N;
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int64_t n = tile_n + j * 32 + (lane & 31);
-            if (n < N) yr[n] = xtraits<XT>::from_f32(acc[i][j][r]);
-          }
-        }
-      }
-  }
-  };
-
-  if constexpr (!GATHER) {
-    tile(0, (int)mrows);
-  } else {
-    __shared__ int gsum[kThreads / 64 + 2];
-    const int64_t total = route.pairs;
-    // pairs whose id is outside [0, E): zero rows (written by expert 0)
-    if (expert == 0)
-      for (int64_t p = tid; p < total; p += kThreads) {
-        const int32_t id = route.ids[p];
-        if (id < 0 || id >= route.E)
-          for (int nn = 0; nn < nrows; ++nn) y[p * N + tile_n + nn] = 0;
-      }
-    // passes over the ids: each lists, in id order, the next kGList pairs
-    // routed to this expert (thread t scans a contiguous segment; a block
-    // prefix sum of the segment counts gives every match its rank)
-    int64_t pos = 0;
-    while (pos < total) {
-      const int64_t seg = (total - pos + kThreads - 1) / kThreads;
-      const int64_t a = pos + tid * seg, b = a + seg < total ? a + seg : total;
-      int cnt = 0;
-#pragma unroll 8
-      for (int64_t p = a; p < b; ++p) cnt += route.ids[p] == expert;
-      int found;
-      int rank = block_exclusive_sum(cnt, gsum, &found);
-      if (tid == 0) gsum[kThreads / 64] = -1;
-      __syncthreads();
-      if (cnt > 0)
-        for (int64_t p = a; p < b; ++p)
-          if (route.ids[p] == expert) {
-            if (rank < kGList) glist[rank] = (int)p;
-            else if (rank == kGList) gsum[kThreads / 64] = (int)p;  // first pair left over
-            ++rank;
-          }
-      __syncthreads();
-      const int listed = found < kGList ? found : kGList;
-      pos = found > kGList ? (int64_t)gsum[kThreads / 64] : total;
-      for (int r0 = 0; r0 < listed; r0 += BM) {
-        tile(r0, listed - r0 < BM ? listed - r0 : BM);
-        __syncthreads();  // LDS stages and the list are reused
-      }
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -604,15 +239,19 @@ __device__ __forceinline__ void sched_kslice() {
 
 // FM: 32-row blocks per tile (8: 256 x 256 tiles; 4: 128 x 256, for a last
 // partial round of tiles).  G1: one group per 32-code chunk (G = 32).  y rows
-// are ldy elements apart.
-template <int BITS, typename XT, int FM, bool G1>
+// are ldy elements apart.  GATHER (MoE prefill, FM = 8): grid y is the
+// expert; the workgroup lists the (token, slot) pairs routed to its expert
+// (route) and runs 256-row tiles over that list, X rows loaded by token and
+// Y rows stored by pair.
+template <int BITS, typename XT, int FM, bool G1, bool GATHER>
 __global__ __launch_bounds__(kThreads) void qmm_wr_kernel(const uint16_t *__restrict__ x,
                                                           int64_t M,
                                                           const uint32_t *__restrict__ codes,
                                                           const uint16_t *__restrict__ scales,
                                                           const uint16_t *__restrict__ biases,
                                                           int64_t N, int64_t K, int G,
-                                                          uint16_t *__restrict__ y, int64_t ldy) {
+                                                          uint16_t *__restrict__ y, int64_t ldy,
+                                                          Routing route) {
   constexpr int TBM = 32 * FM, kXSt = TBM * BK * 2, kXD = kWrXDma<FM>;
   // a thread's loads per step: the X copy, the codes of its two W chunks,
   // their scales and biases (G > 32: one scale and one bias per lane, for
@@ -634,13 +273,23 @@ __global__ __launch_bounds__(kThreads) void qmm_wr_kernel(const uint16_t *__rest
   // every eighth column tile of the same one or two row tiles and share
   // those X rows in its L2.  (No division: the tile coordinates stay scalar,
   // and with them the operand resources.)
-  const int64_t tile_m = (int64_t)blockIdx.y * TBM;
+  int64_t tile_m = 0;
   const int64_t tile_n = (int64_t)blockIdx.x * WBN;
+  int expert = 0;
+  if constexpr (GATHER) {
+    expert = blockIdx.y;
+    codes += (int64_t)expert * N * wpr;
+    scales += (int64_t)expert * N * gpr;
+    biases += (int64_t)expert * N * gpr;
+  } else {
+    tile_m = (int64_t)blockIdx.y * TBM;
+  }
 
-  // operand tiles as buffer resources: rows past M or N read as zero
+  // operand tiles as buffer resources: rows past M or N read as zero (the
+  // gather addresses all of x by token)
   const int64_t mrows = M - tile_m < TBM ? M - tile_m : TBM;
   const int64_t nrows = N - tile_n < WBN ? N - tile_n : WBN;
-  const int xbytes = (int)(mrows * K * 2);
+  const int xbytes = (int)((GATHER ? M : mrows) * K * 2);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + tile_m * K, xbytes);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(codes + tile_n * wpr, nrows * wpr * 4);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(scales + tile_n * gpr, nrows * gpr * 2);
@@ -654,15 +303,26 @@ __global__ __launch_bounds__(kThreads) void qmm_wr_kernel(const uint16_t *__rest
   auto kclamp = [&](int st) -> int { return kbase(st < ksteps ? st : ksteps - 1); };
 
   // X copy: load i of wave w fills rows 8 (8w + i) .. +7; LDS row r holds
-  // the row's 16-byte unit u at slot u ^ ((r >> 1) & 7)
+  // the row's 16-byte unit u at slot u ^ ((r >> 1) & 7).  Row r of the tile
+  // at list position r0 is x row r (plain) or the token of pair
+  // glist[r0 + r] (gather; rows >= rows read as zero).
   uint32_t xvoff[kXD], xvoff_tail[kXD];
+  __shared__ int glist[GATHER ? kGList : 1];  // pairs of the expert in this pass
+  auto set_rows = [&](int r0, int rows) {
 #pragma unroll
-  for (int i = 0; i < kXD; ++i) {
-    const int row = 8 * (wave * kXD + i) + (lane >> 3);
-    const int u = (lane & 7) ^ ((row >> 1) & 7);
-    xvoff[i] = (uint32_t)(row * K * 2) + (uint32_t)u * 16u;
-    xvoff_tail[i] = u < 4 ? xvoff[i] : (uint32_t)xbytes;  // k past K: out of range, reads zero
-  }
+    for (int i = 0; i < kXD; ++i) {
+      const int row = 8 * (wave * kXD + i) + (lane >> 3);
+      const int u = (lane & 7) ^ ((row >> 1) & 7);
+      uint32_t ro;
+      if constexpr (GATHER)
+        ro = row < rows ? (uint32_t)((int64_t)(glist[r0 + row] / route.topk) * K * 2)
+                        : (uint32_t)xbytes;
+      else
+        ro = (uint32_t)(row * K * 2);
+      xvoff[i] = ro + (uint32_t)u * 16u;
+      xvoff_tail[i] = u < 4 ? xvoff[i] : (uint32_t)xbytes;  // k past K: out of range, reads zero
+    }
+  };
   // loads i0 .. i1-1 of a step's X copy
   auto dma_x = [&](int k0, char *dst, const uint32_t (&vo)[kXD], int i0 = 0, int i1 = kWrXDma<FM>) {
     const uint32_t so = (uint32_t)k0 * 2u;
@@ -737,12 +397,6 @@ __global__ __launch_bounds__(kThreads) void qmm_wr_kernel(const uint16_t *__rest
   };
 
   f32x16v acc[FM][WFN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < WFN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   auto mfma_ks = [&](const uint4 (&a)[FM], const uint4 (&b)[WFN]) {
 #pragma unroll
     for (int j = 0; j < WFN; ++j)
@@ -760,6 +414,12 @@ __global__ __launch_bounds__(kThreads) void qmm_wr_kernel(const uint16_t *__rest
     constexpr int j = decltype(jcon)::value;
     return j == 0 ? q0 : j == 1 ? q1 : j == 2 ? q2 : q3;
   };
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < WFN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   WrRegs<BITS> wr[kWStages];  // W of step s in wr[s % 4]
   uint4 fa[2][FM], fb[2][WFN];
   using K0 = std::integral_constant<int, 0>;
@@ -863,21 +523,80 @@ __global__ __launch_bounds__(kThreads) void qmm_wr_kernel(const uint16_t *__rest
   // the loads issued past the last step (clamped, in range) finish here
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   };
-  run(xs0, xs1, xs2, xs3);
-
-  // epilogue: accumulator r of lane l in a 32x32 block is row
-  // 8*(r/4) + 4*(l/32) + r%4, column l % 32
+  if constexpr (!GATHER) {
+    set_rows(0, TBM);
+    run(xs0, xs1, xs2, xs3);
+    // epilogue: accumulator r of lane l in a 32x32 block is row
+    // 8*(r/4) + 4*(l/32) + r%4, column l % 32
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < WFN; ++j) {
-      const int64_t n = tile_n + 64 * wave + 32 * j + (lane & 31);
+      for (int j = 0; j < WFN; ++j) {
+        const int64_t n = tile_n + 64 * wave + 32 * j + (lane & 31);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t m = tile_m + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (m < M && n < N) y[m * ldy + n] = xtraits<XT>::from_f32(acc[i][j][r]);
+        for (int r = 0; r < 16; ++r) {
+          const int64_t m = tile_m + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (m < M && n < N) y[m * ldy + n] = xtraits<XT>::from_f32(acc[i][j][r]);
+        }
       }
+  } else {
+    // one 256-row tile of the list from position r0; row lr of the tile is
+    // pair glist[r0 + lr], stored to that (token, slot)'s y row
+    auto tile = [&](int r0, int rows) {
+      set_rows(r0, rows);
+      run(xs0, xs1, xs2, xs3);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int lr = i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (lr < rows) {
+            uint16_t *yr = y + (int64_t)glist[r0 + lr] * ldy;
+#pragma unroll
+            for (int j = 0; j < WFN; ++j) {
+              const int64_t n = tile_n + 64 * wave + 32 * j + (lane & 31);
+              if (n < N) yr[n] = xtraits<XT>::from_f32(acc[i][j][r]);
+            }
+          }
+        }
+      __syncthreads();  // the stages and the list are reused
+    };
+    __shared__ int gsum[kThreads / 64 + 2];
+    const int64_t total = route.pairs;
+    // pairs whose id is outside [0, E): zero rows (written by expert 0)
+    if (expert == 0)
+      for (int64_t p = tid; p < total; p += kThreads) {
+        const int32_t id = route.ids[p];
+        if (id < 0 || id >= route.E)
+          for (int nn = 0; nn < nrows; ++nn) y[p * ldy + tile_n + nn] = 0;
+      }
+    // passes over the ids: each lists, in id order, the next kGList pairs
+    // routed to this expert (thread t scans a contiguous segment; a block
+    // prefix sum of the segment counts gives every match its rank)
+    int64_t pos = 0;
+    while (pos < total) {
+      const int64_t seg = (total - pos + kThreads - 1) / kThreads;
+      const int64_t a = pos + tid * seg, b = a + seg < total ? a + seg : total;
+      int cnt = 0;
+#pragma unroll 8
+      for (int64_t p = a; p < b; ++p) cnt += route.ids[p] == expert;
+      int found;
+      int rank = block_exclusive_sum(cnt, gsum, &found);
+      if (tid == 0) gsum[kThreads / 64] = -1;
+      __syncthreads();
+      if (cnt > 0)
+        for (int64_t p = a; p < b; ++p)
+          if (route.ids[p] == expert) {
+            if (rank < kGList) glist[rank] = (int)p;
+            else if (rank == kGList) gsum[kThreads / 64] = (int)p;  // first pair left over
+            ++rank;
+          }
+      __syncthreads();
+      const int listed = found < kGList ? found : kGList;
+      pos = found > kGList ? (int64_t)gsum[kThreads / 64] : total;
+      for (int r0 = 0; r0 < listed; r0 += TBM) tile(r0, listed - r0 < TBM ? listed - r0 : TBM);
     }
+  }
 }
 
 template <int BITS, typename XT>
@@ -902,13 +621,15 @@ hipError_t qmm_wr_launch(const void *x, int64_t M, const uint32_t *codes, const 
     constexpr int FM = decltype(fm)::value;
     constexpr bool G1 = decltype(g1)::value;
     if (FM == 8)
-      hipLaunchKernelGGL((qmm_wr_kernel<BITS, XT, 8, G1>), dim3((unsigned)nmain, (unsigned)mt),
-                         dim3(kThreads), 0, s, (const uint16_t *)x, M, codes, scales, biases,
-                         n0 < N ? n0 : N, K, G, yo, N);
+      hipLaunchKernelGGL((qmm_wr_kernel<BITS, XT, 8, G1, false>),
+                         dim3((unsigned)nmain, (unsigned)mt), dim3(kThreads), 0, s,
+                         (const uint16_t *)x, M, codes, scales, biases, n0 < N ? n0 : N, K, G, yo,
+                         N, Routing{});
     else
-      hipLaunchKernelGGL((qmm_wr_kernel<BITS, XT, 4, G1>), dim3((unsigned)ntail, (unsigned)(2 * mt)),
-                         dim3(kThreads), 0, s, (const uint16_t *)x, M, codes + n0 * wpr,
-                         scales + n0 * gpr, biases + n0 * gpr, N - n0, K, G, yo + n0, N);
+      hipLaunchKernelGGL((qmm_wr_kernel<BITS, XT, 4, G1, false>),
+                         dim3((unsigned)ntail, (unsigned)(2 * mt)), dim3(kThreads), 0, s,
+                         (const uint16_t *)x, M, codes + n0 * wpr, scales + n0 * gpr,
+                         biases + n0 * gpr, N - n0, K, G, yo + n0, N, Routing{});
   };
   using F8 = std::integral_constant<int, 8>;
   using F4 = std::integral_constant<int, 4>;
@@ -924,31 +645,23 @@ hipError_t qmm_wr_launch(const void *x, int64_t M, const uint32_t *codes, const 
 }
 
 template <int BITS, typename XT>
-hipError_t qmm_launch(const void *x, int64_t M, const uint32_t *codes, const uint16_t *scales,
-                      const uint16_t *biases, int64_t N, int64_t K, int G, void *y,
-                      hipStream_t s) {
-  auto kern = qmm_kernel<BITS, XT, false>;
-  const int64_t mt = (M + BM - 1) / BM, nt = (N + BN - 1) / BN;
-  if (mt * nt > 0x7FFFFFFF || mt > 0x7FFFFFFF || nt > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if ((int64_t)BM * K * 2 > 0x7FFFFFFF) return hipErrorInvalidValue;  // 32-bit tile offsets
-  hipLaunchKernelGGL(kern, dim3((unsigned)(mt * nt)), dim3(kThreads), 0, s, (const uint16_t *)x, M,
-                     codes, scales, biases, N, K, G, (uint16_t *)y, (int)mt, (int)nt, Routing{});
-  return hipGetLastError();
-}
-
-template <int BITS, typename XT>
 hipError_t gather_qmm_launch(const void *x, int64_t T, const uint32_t *codes,
                              const uint16_t *scales, const uint16_t *biases, int64_t E, int64_t N,
                              int64_t K, const int32_t *ids, int topk, int G, void *y,
                              hipStream_t s) {
-  auto kern = qmm_kernel<BITS, XT, true>;
-  const int64_t nt = (N + BN - 1) / BN;
+  const int64_t nt = (N + WBN - 1) / WBN;
   // all of x is addressed with 32-bit byte offsets; pairs are listed as int
   if (T * K * 2 > 0x7FFFFFFF || T * topk > 0x7FFFFFFF || nt > 0x7FFFFFFF || E > 65535)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(kern, dim3((unsigned)nt, (unsigned)E), dim3(kThreads), 0, s,
-                     (const uint16_t *)x, T, codes, scales, biases, N, K, G, (uint16_t *)y, 0,
-                     (int)nt, Routing{ids, T * topk, topk, E});
+  const Routing route{ids, T * topk, topk, E};
+  if (G == 32)
+    hipLaunchKernelGGL((qmm_wr_kernel<BITS, XT, 8, true, true>), dim3((unsigned)nt, (unsigned)E),
+                       dim3(kThreads), 0, s, (const uint16_t *)x, T, codes, scales, biases, N, K,
+                       G, (uint16_t *)y, N, route);
+  else
+    hipLaunchKernelGGL((qmm_wr_kernel<BITS, XT, 8, false, true>), dim3((unsigned)nt, (unsigned)E),
+                       dim3(kThreads), 0, s, (const uint16_t *)x, T, codes, scales, biases, N, K,
+                       G, (uint16_t *)y, N, route);
   return hipGetLastError();
 }
 
@@ -968,11 +681,7 @@ template <typename XT>
 hipError_t qmm_bits(const void *x, int64_t M, const uint32_t *codes, const uint16_t *scales,
                     const uint16_t *biases, int64_t N, int64_t K, int G, int bits, void *y,
                     hipStream_t s) {
-#ifdef AQ_QMM_OLD
-#define AQ_QL qmm_launch
-#else
 #define AQ_QL qmm_wr_launch
-#endif
   switch (bits) {
     case 2: return AQ_QL<2, XT>(x, M, codes, scales, biases, N, K, G, y, s);
     case 3: return AQ_QL<3, XT>(x, M, codes, scales, biases, N, K, G, y, s);

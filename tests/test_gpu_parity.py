@@ -264,7 +264,7 @@ def test_matmul_few_rows_sliced(aq, xdt, bits, G, K):
         _assert_close(y, y_ref, A, f"sliced b{bits} G{G} K{K} M{M} {xdt}")
 
 
-@pytest.mark.parametrize("bits,G", [(4, 64), (8, 128)])
+@pytest.mark.parametrize("bits,G", [(4, 64), (8, 128), (8, 32), (4, 32)])
 def test_matmul_few_rows_sliced_tall(aq, bits, G):
     """Tall matrices (two 16-row blocks per workgroup) at 16..64 rows: past 16
     rows two sets of 16 x rows per wave (slices of 32; 40 rows leave the
