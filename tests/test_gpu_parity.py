@@ -419,7 +419,7 @@ def test_gather_long_rows(aq, K):
 @pytest.mark.parametrize("bits", ALL_BITS)
 @pytest.mark.parametrize("xdt,K", [("f16", 544), ("bf16", 2048)])
 def test_gather_qmm_parity(aq, bits, xdt, K):
-    """Several experts with ~180 routed rows each, N ragged against 224-column
+    """Several experts with ~180 routed rows each, N ragged against 256-column
     tiles, K with a 32-code tail (fp16) or at bf16 depth."""
     G = 32 if K % 64 else GROUP_FOR_BITS[bits]
     E, N, T, topk = 5, 300, 300, 3
