@@ -784,11 +784,13 @@ template <> struct stream_shape<8> { static constexpr int R = 4, D = 2; };
 // wave, W waves per workgroup.  Measured on the MI355X (cold weights): at
 // K = 4096, 8-wave workgroups for N > 2048 and one row in flight per wave past
 // N = 8192 (the waves then outnumber a CU's rows enough to keep its loads in
-// flight); at K = 14336, 8-wave workgroups.
+// flight); at K = 14336 (4096 rows), 4-wave workgroups (9.22 us against
+// 9.32 .. 9.46 with 8 waves and 10.1 with 2; two rows in flight per wave,
+// 9.6 .. 12.0).
 void qmv1_shape(int64_t N, int64_t K, int &cpl, int &ud, int &w) {
   cpl = (int)((K / 32 + 63) / 64);
   ud = cpl == 1 ? 4 : (cpl == 2 ? (N > 8192 ? 1 : 2) : 1);
-  w = (cpl == 2 && N > 2048) || cpl == 7 ? 8 : 4;
+  w = cpl == 2 && N > 2048 ? 8 : 4;
 }
 
 namespace {
@@ -830,7 +832,7 @@ hipError_t qmv1_dispatch(const void *x, const Weights &wt, int64_t N, int64_t K,
     case 4: return qmv1_launch<BITS, XT, 4, 1>(x, wt, N, K, G, y, s);
     case 5: return qmv1_launch<BITS, XT, 5, 1>(x, wt, N, K, G, y, s);
     case 6: return qmv1_launch<BITS, XT, 6, 1>(x, wt, N, K, G, y, s);
-    case 7: return qmv1_launch<BITS, XT, 7, 1, 8>(x, wt, N, K, G, y, s);
+    case 7: return qmv1_launch<BITS, XT, 7, 1>(x, wt, N, K, G, y, s);
     case 8: return qmv1_launch<BITS, XT, 8, 1>(x, wt, N, K, G, y, s);
   }
   return hipErrorInvalidValue;
