@@ -330,11 +330,13 @@ def test_qmm_shapes_bf16(aq, M, N, K, G):
     _assert_close(y, y_ref, A, f"qmm {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K,G", [(300, 33029, 96, 32), (64, 51200, 160, 32)])
+@pytest.mark.parametrize("M,N,K,G", [(300, 33029, 96, 32), (64, 51200, 160, 32),
+                                     (300, 33029, 128, 64), (64, 51200, 256, 128)])
 def test_qmm_tile_rounds(aq, M, N, K, G):
     """Shapes that fill the chip in rounds of 256-row tiles: 260 tiles (the
     last, partial round as 128-row tiles in a second launch; ragged rows,
-    columns and K tail) and 200 tiles (one launch of full tiles)."""
+    columns, K tail at G = 32) and 200 tiles (one launch of full tiles), with
+    one group per chunk (G = 32) and with groups spanning chunks."""
     bits, xdt = 4, "f16"
     _, (c, s, b) = _quantized(N, K, G, bits, seed=23)
     xb = inputs.activations(M, K, xdt, seed=23, key=(M, N, K))
