@@ -194,7 +194,7 @@ aq_status aq_gather_qmv(const void *x, aq_dtype x_dtype, int64_t T, const uint32
 /* The gather product at prefill size, on the matrix cores (the QMM engine
  * of aq_qmm): same operation, arguments and layouts as aq_gather_qmv, for
  * many tokens per expert.  The routing is resolved on the device: one
- * workgroup per (224 columns, expert) lists the (token, slot) pairs routed
+ * workgroup per (256 columns, expert) lists the (token, slot) pairs routed
  * to its expert and runs 256-row tiles of them, so each expert's weights are
  * read once per 256 routed rows.  Weight tiles are rounded to x_dtype as in
  * aq_qmm.  AQ_ERR_UNSUPPORTED if T*K*2 > 2^31-1 (x addressed with 32-bit
