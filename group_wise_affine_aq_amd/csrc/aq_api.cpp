@@ -207,12 +207,14 @@ aq_status aq_quantized_matmul(const void *x, aq_dtype x_dtype, int64_t M, const 
   if (M >= 1 && M <= kMaxQmvRows)
     return aq_qmv(x, x_dtype, M, codes, scales, biases, N, K, group_size, bits, y, stream);
   // a few rows more: the tiled kernel's 256-row tiles would be mostly empty
-  // and too few to fill the chip
-  if (M > kMaxQmvRows && aq::qmvm_preferred(M, bits, N, K, group_size)) {
+  // and too few to fill the chip (arguments validated before the shape
+  // heuristics look at them)
+  if (M > kMaxQmvRows) {
     aq_status st = check_matmul(x, x_dtype, M, codes, scales, biases, N, K, group_size, bits, y);
     if (st != AQ_OK) return st;
-    return from_hip(aq::launch_qmvm(x, (int)x_dtype, (int)M, codes, scales, biases, N, K,
-                                    group_size, bits, y, static_cast<hipStream_t>(stream)));
+    if (aq::qmvm_preferred(M, bits, N, K, group_size))
+      return from_hip(aq::launch_qmvm(x, (int)x_dtype, (int)M, codes, scales, biases, N, K,
+                                      group_size, bits, y, static_cast<hipStream_t>(stream)));
   }
   return aq_qmm(x, x_dtype, M, codes, scales, biases, N, K, group_size, bits, y, stream);
 }

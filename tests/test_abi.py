@@ -65,25 +65,41 @@ def qmv(lib, fn="aq_qmv", x=P, xdt=F16, M=1, codes=P, scales=P, biases=P, N=64, 
 
 @pytest.mark.parametrize("fn", ["aq_qmv", "aq_qmm", "aq_quantized_matmul"])
 def test_matmul_argument_errors(lib, fn):
-    assert qmv(lib, fn, bits=1) == INVALID
-    assert qmv(lib, fn, bits=9) == INVALID
-    assert qmv(lib, fn, G=16) == INVALID
-    assert qmv(lib, fn, G=48) == INVALID
-    assert qmv(lib, fn, K=96, G=64) == INVALID   # K % G != 0
-    assert qmv(lib, fn, N=0) == INVALID
-    assert qmv(lib, fn, K=0) == INVALID
-    assert qmv(lib, fn, M=0) == INVALID
-    assert qmv(lib, fn, xdt=F32) == INVALID
-    assert qmv(lib, fn, xdt=7) == INVALID
-    assert qmv(lib, fn, x=None) == INVALID
-    assert qmv(lib, fn, y=None) == INVALID
-    assert qmv(lib, fn, codes=None) == INVALID
-    assert qmv(lib, fn, scales=None) == INVALID
-    assert qmv(lib, fn, biases=None) == INVALID
-    assert qmv(lib, fn, x=MIS) == ALIGN
-    assert qmv(lib, fn, y=MIS) == ALIGN
-    assert qmv(lib, fn, codes=MIS) == ALIGN
-    assert qmv(lib, fn, scales=MIS) == ALIGN
+    _matmul_argument_errors(lib, fn, 1)
+
+
+@pytest.mark.parametrize("M", [16, 100, 300])
+def test_dispatch_argument_errors_past_eight_rows(lib, M):
+    """The shape dispatch validates before its shape heuristics run (a group
+    size of 0 must come back as an error, not reach a division)."""
+    assert qmv(lib, "aq_quantized_matmul", M=M, G=0) == INVALID
+    _matmul_argument_errors(lib, "aq_quantized_matmul", M)
+
+
+def _matmul_argument_errors(lib, fn, M):
+    def call(**k):
+        k.setdefault("M", M)
+        return qmv(lib, fn, **k)
+
+    assert call(bits=1) == INVALID
+    assert call(bits=9) == INVALID
+    assert call(G=16) == INVALID
+    assert call(G=48) == INVALID
+    assert call(K=96, G=64) == INVALID   # K % G != 0
+    assert call(N=0) == INVALID
+    assert call(K=0) == INVALID
+    assert call(M=0) == INVALID
+    assert call(xdt=F32) == INVALID
+    assert call(xdt=7) == INVALID
+    assert call(x=None) == INVALID
+    assert call(y=None) == INVALID
+    assert call(codes=None) == INVALID
+    assert call(scales=None) == INVALID
+    assert call(biases=None) == INVALID
+    assert call(x=MIS) == ALIGN
+    assert call(y=MIS) == ALIGN
+    assert call(codes=MIS) == ALIGN
+    assert call(scales=MIS) == ALIGN
 
 
 def test_qmv_rows_limit(lib):
