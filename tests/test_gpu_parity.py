@@ -371,6 +371,20 @@ def test_quantized_matmul_dispatch(aq, M):
     _assert_close(y, y_ref, A, f"dispatch M{M}")
 
 
+@pytest.mark.parametrize("bits", [2, 3, 5, 6, 7])
+def test_quantized_matmul_dispatch_other_widths(aq, bits):
+    """9..256 rows with code widths the few-row kernel does not take: the
+    dispatcher falls through to the prefill kernel."""
+    G = GROUP_FOR_BITS[bits]
+    N, K, xdt = 100, 640 if G != 128 else 768, "f16"
+    _, (c, s, b) = _quantized(N, K, G, bits, seed=24)
+    for M in (9, 40, 256):
+        xb = inputs.activations(M, K, xdt, seed=24, key=(M, bits))
+        y_ref, A = oracle.matmul(inputs.from_bits(xb, xdt), c, s, b, K, G, bits)
+        y = aq.aq_quantized_matmul(bits_to_dev(xb, xdt), *packed_to_dev(c, s, b), G, bits)
+        _assert_close(y, y_ref, A, f"dispatch b{bits} M{M}")
+
+
 # ---- gather (MoE) ---------------------------------------------------------------------------------
 def _experts(E, N, K, G, bits, seed):
     q = [oracle.quantize(inputs.weights(N, K, seed=seed, key=(e, G, bits)), G, bits)
