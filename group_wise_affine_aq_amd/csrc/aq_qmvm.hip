@@ -670,11 +670,10 @@ inline size_t gather_lds_bytes(int R, int64_t K, int G) {
   return (size_t)2 * sb_entries(16 * R, K / G) * 2;
 }
 
-template <typename XT, int BITS, int R>
+template <typename XT, int BITS, int R, int W>
 hipError_t gather_go(const void *x, int64_t T, const uint32_t *codes, const uint16_t *scales,
                      const uint16_t *biases, int64_t E, int64_t N, int64_t K,
                      const int32_t *ids, int topk, int G, void *y, hipStream_t s) {
-  constexpr int W = 2;  // the grid has (rows / 16 R) x E workgroups: split K in two
   const int64_t steps = (K + kStepK - 1) / kStepK;
   const int kw = (int)((steps + W - 1) / W) * kStepK;
   const int64_t blocks = (N + 16 * R - 1) / (16 * R);
@@ -793,13 +792,19 @@ hipError_t launch_gather_qmvm(const void *x, int x_dtype, int64_t T, const uint3
                               const uint16_t *scales, const uint16_t *biases, int64_t E, int64_t N,
                               int64_t K, const int32_t *ids, int topk, int G, int bits,
                               void *y, hipStream_t s) {
-  // 4 blocks of 16 rows per workgroup (the x rows of a batch are loaded once
-  // per 64 rows; the grid is (rows / 64) x experts), fewer if the staged
-  // scales would not fit
+  // 4 blocks of 16 rows per workgroup, K split over 2 waves (the x rows of a
+  // batch are loaded once per 64 rows; the grid is (rows / 64) x experts),
+  // fewer blocks if the staged scales would not fit.  With at most one pair
+  // per expert on average (decode of a few tokens) each workgroup has a
+  // single batch and the launch is latency-bound: 2 blocks over 4 waves give
+  // the touched experts four times the waves (measured 15-36% faster at 1-8
+  // tokens of 64 experts, top-6; slower from about 3 pairs per expert on).
+  const bool few = T * topk <= E;
 #define AQ_GATHER_B(XT, B) \
-  if (gather_lds_bytes(4, K, G) <= kMaxStagedLds) return gather_go<XT, B, 4>(x, T, codes, scales, biases, E, N, K, ids, topk, G, y, s); \
-  if (gather_lds_bytes(2, K, G) <= kMaxStagedLds) return gather_go<XT, B, 2>(x, T, codes, scales, biases, E, N, K, ids, topk, G, y, s); \
-  return gather_go<XT, B, 1>(x, T, codes, scales, biases, E, N, K, ids, topk, G, y, s);
+  if (few && gather_lds_bytes(2, K, G) <= kMaxStagedLds) return gather_go<XT, B, 2, 4>(x, T, codes, scales, biases, E, N, K, ids, topk, G, y, s); \
+  if (gather_lds_bytes(4, K, G) <= kMaxStagedLds) return gather_go<XT, B, 4, 2>(x, T, codes, scales, biases, E, N, K, ids, topk, G, y, s); \
+  if (gather_lds_bytes(2, K, G) <= kMaxStagedLds) return gather_go<XT, B, 2, 2>(x, T, codes, scales, biases, E, N, K, ids, topk, G, y, s); \
+  return gather_go<XT, B, 1, 2>(x, T, codes, scales, biases, E, N, K, ids, topk, G, y, s);
 #define AQ_GATHER(XT) \
   if (bits == 4) { AQ_GATHER_B(XT, 4) } else { AQ_GATHER_B(XT, 8) }
   if (x_dtype == X_BF16) { AQ_GATHER(bf16_t) }

@@ -419,6 +419,20 @@ def test_gather_groups(aq, bits, G):
     _assert_close(y, y_ref, A, f"gather b{bits} G{G}")
 
 
+@pytest.mark.parametrize("bits,G", [(4, 32), (4, 64), (8, 128), (8, 32)])
+@pytest.mark.parametrize("T,xdt,K", [(1, "f16", 384), (3, "f16", 9600), (4, "bf16", 2304)])
+def test_gather_few_tokens(aq, bits, G, T, xdt, K):
+    """At most one (token, slot) pair per expert on average: the launch with
+    more waves per row (a ragged last block of rows, K split four ways)."""
+    E, N, topk = 16, 100, 4
+    c, s, b = _experts(E, N, K, G, bits, seed=19)
+    ids = inputs.expert_ids(T, E, topk, seed=19, key=(T,))
+    xb = inputs.activations(T, K, xdt, seed=19)
+    y_ref, A = oracle.gather_matmul(inputs.from_bits(xb, xdt), c, s, b, ids, K, G, bits)
+    y = aq.aq_gather_qmv(bits_to_dev(xb, xdt), *packed_to_dev(c, s, b), to_dev(ids), G, bits)
+    _assert_close(y, y_ref, A, f"gather few T{T} b{bits} G{G} {xdt} K{K}")
+
+
 @pytest.mark.parametrize("K", [9600, 19200])
 def test_gather_long_rows(aq, K):
     """Rows long enough that fewer 16-row blocks per workgroup fit the staged scales."""
