@@ -569,22 +569,24 @@ __global__ __launch_bounds__(64 * W) void qmvm_kernel(const uint16_t *__restrict
 // Mixture-of-experts gather ("Quantization", metalworking, gather variants
 // for MoE experts): y[t, j, :] = x[t] @ W_{ids[t, j]}^T.  One workgroup per
 // (16 R rows, expert e) collects the (token, slot) pairs routed to e and runs
-// them in batches of up to 8 x rows through the matrix cores, so each
-// expert's rows are read once per batch of tokens that chose it (experts no
-// token chose are never read).  Pairs whose id is outside [0, E) get zero
+// them in batches through the matrix cores (with WIDE, 16 x rows while more
+// than 8 pairs are left; else 8, the lighter form with two K chunks per MFMA
+// slot), so each expert's rows are read once per batch of tokens that chose
+// it (experts no token chose are never read).  Pairs whose id is outside [0, E) get zero
 // rows, written by the workgroups of expert 0.
 constexpr int kGTile = 256;  // ids scanned per round
 
-template <typename XT, int BITS, int W, int GS, int R>
+template <typename XT, int BITS, int W, int GS, int R, bool WIDE>
 __global__ __launch_bounds__(64 * W) void gather_qmvm_kernel(
     const uint16_t *__restrict__ x, int64_t T, const uint32_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ biases, int64_t E, int64_t N,
     int64_t K, const int32_t *__restrict__ ids, int topk, int kw, uint16_t *__restrict__ y) {
   __shared__ int list[kGTile];
   __shared__ int count;
-  __shared__ __attribute__((aligned(16))) float part[W * 16 * R * 8];
+  __shared__ __attribute__((aligned(16))) float part[W * 16 * R * (WIDE ? 16 : 8)];
   extern __shared__ __attribute__((aligned(16))) uint16_t sbl[];  // [2][16 R][gpr]
   typedef MBlock<XT, BITS, W, GS, 8, R> Blk;
+  typedef MBlock<XT, BITS, W, GS, 16, R> Blk16;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int e = blockIdx.y;
@@ -608,9 +610,10 @@ __global__ __launch_bounds__(64 * W) void gather_qmvm_kernel(
   __syncthreads();
   if (count == 0) return;
 
+  const uint32_t *wrows = codes + e * wpe + row0 * (K >> 5) * BITS;
+  const __amdgpu_buffer_rsrc_t rx = mk_rsrc(x, T * K * 2);
   Blk blk;
-  blk.setup(codes + e * wpe + row0 * (K >> 5) * BITS, nrows, K, kw, wave, lane, sbl,
-            mk_rsrc(x, T * K * 2));
+  blk.setup(wrows, nrows, K, kw, wave, lane, sbl, rx);
   Blk::stage_sb(scales + (e * N + row0) * gpr, biases + (e * N + row0) * gpr, nrows, gpr, sbl,
                 wave, lane);
   Blk::template stage_sb_wait<0>(scales + (e * N + row0) * gpr, biases + (e * N + row0) * gpr,
@@ -626,21 +629,35 @@ __global__ __launch_bounds__(64 * W) void gather_qmvm_kernel(
     }
     __syncthreads();
     const int n = count;
-    for (int b0 = 0; b0 < n; b0 += 8) {
-      // slot row m = n16 % 8 carries pair list[b0 + m]; missing pairs read
-      // past the x resource (zeros)
-      const int m = lane & 7;
-      const uint32_t xro = b0 + m < n ? (uint32_t)(((t0 + list[b0 + m]) / topk) * K * 2)
-                                      : (uint32_t)(T * K * 2);
-      typename Blk::Step st[D];
-      blk.template prologue<D>(xro, st);
-      f32x4v acc[1][R];
-      blk.template finish<D>(st, acc);
-      reduce_out<W, R, 8, 1>(part, wave, lane, acc, [&](int nn, int mm, float v) {
+    for (int b0 = 0; b0 < n;) {
+      // slot row m = n16 % (batch rows) carries pair list[b0 + m]; missing
+      // pairs read past the x resource (zeros)
+      const auto xrow = [&](int m) {
+        return b0 + m < n ? (uint32_t)(((t0 + list[b0 + m]) / topk) * K * 2)
+                          : (uint32_t)(T * K * 2);
+      };
+      const auto store = [&](int nn, int mm, float v) {
         if (b0 + mm < n && row0 + nn < N)
           y[(t0 + list[b0 + mm]) * N + row0 + nn] = xtraits<XT>::from_f32(v);
-      });
-      __syncthreads();  // part and list reused
+      };
+      f32x4v acc[1][R];
+      if (WIDE && n - b0 > 8) {  // uniform
+        Blk16 wide;
+        wide.setup(wrows, nrows, K, kw, wave, lane, sbl, rx);
+        typename Blk16::Step st[D];
+        wide.template prologue<D>(xrow(lane & 15), st);
+        wide.template finish<D>(st, acc);
+        reduce_out<W, R, 16, 1>(part, wave, lane, acc, store);
+        __syncthreads();  // part and list reused
+        b0 += 16;
+      } else {
+        typename Blk::Step st[D];
+        blk.template prologue<D>(xrow(lane & 7), st);
+        blk.template finish<D>(st, acc);
+        reduce_out<W, R, 8, 1>(part, wave, lane, acc, store);
+        __syncthreads();
+        b0 += 8;
+      }
     }
   }
 }
@@ -670,7 +687,7 @@ inline size_t gather_lds_bytes(int R, int64_t K, int G) {
   return (size_t)2 * sb_entries(16 * R, K / G) * 2;
 }
 
-template <typename XT, int BITS, int R, int W>
+template <typename XT, int BITS, int R, int W, bool WIDE = true>
 hipError_t gather_go(const void *x, int64_t T, const uint32_t *codes, const uint16_t *scales,
                      const uint16_t *biases, int64_t E, int64_t N, int64_t K,
                      const int32_t *ids, int topk, int G, void *y, hipStream_t s) {
@@ -681,9 +698,9 @@ hipError_t gather_go(const void *x, int64_t T, const uint32_t *codes, const uint
   const dim3 grid((unsigned)blocks, (unsigned)E), block(64 * W);
   const size_t lds = gather_lds_bytes(R, K, G);
   switch (G) {
-    case 32: hipLaunchKernelGGL((gather_qmvm_kernel<XT, BITS, W, 0, R>), grid, block, lds, s, (const uint16_t *)x, T, codes, scales, biases, E, N, K, ids, topk, kw, (uint16_t *)y); break;
-    case 64: hipLaunchKernelGGL((gather_qmvm_kernel<XT, BITS, W, 1, R>), grid, block, lds, s, (const uint16_t *)x, T, codes, scales, biases, E, N, K, ids, topk, kw, (uint16_t *)y); break;
-    case 128: hipLaunchKernelGGL((gather_qmvm_kernel<XT, BITS, W, 2, R>), grid, block, lds, s, (const uint16_t *)x, T, codes, scales, biases, E, N, K, ids, topk, kw, (uint16_t *)y); break;
+    case 32: hipLaunchKernelGGL((gather_qmvm_kernel<XT, BITS, W, 0, R, WIDE>), grid, block, lds, s, (const uint16_t *)x, T, codes, scales, biases, E, N, K, ids, topk, kw, (uint16_t *)y); break;
+    case 64: hipLaunchKernelGGL((gather_qmvm_kernel<XT, BITS, W, 1, R, WIDE>), grid, block, lds, s, (const uint16_t *)x, T, codes, scales, biases, E, N, K, ids, topk, kw, (uint16_t *)y); break;
+    case 128: hipLaunchKernelGGL((gather_qmvm_kernel<XT, BITS, W, 2, R, WIDE>), grid, block, lds, s, (const uint16_t *)x, T, codes, scales, biases, E, N, K, ids, topk, kw, (uint16_t *)y); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -799,9 +816,11 @@ hipError_t launch_gather_qmvm(const void *x, int x_dtype, int64_t T, const uint3
   // single batch and the launch is latency-bound: 2 blocks over 4 waves give
   // the touched experts four times the waves (measured 15-36% faster at 1-8
   // tokens of 64 experts, top-6; slower from about 3 pairs per expert on).
+  // That launch leaves out the 16-row batches: they serve experts with more
+  // than 8 pairs, and their registers cost it about 1 us.
   const bool few = T * topk <= E;
 #define AQ_GATHER_B(XT, B) \
-  if (few && gather_lds_bytes(2, K, G) <= kMaxStagedLds) return gather_go<XT, B, 2, 4>(x, T, codes, scales, biases, E, N, K, ids, topk, G, y, s); \
+  if (few && gather_lds_bytes(2, K, G) <= kMaxStagedLds) return gather_go<XT, B, 2, 4, false>(x, T, codes, scales, biases, E, N, K, ids, topk, G, y, s); \
   if (gather_lds_bytes(4, K, G) <= kMaxStagedLds) return gather_go<XT, B, 4, 2>(x, T, codes, scales, biases, E, N, K, ids, topk, G, y, s); \
   if (gather_lds_bytes(2, K, G) <= kMaxStagedLds) return gather_go<XT, B, 2, 2>(x, T, codes, scales, biases, E, N, K, ids, topk, G, y, s); \
   return gather_go<XT, B, 1, 2>(x, T, codes, scales, biases, E, N, K, ids, topk, G, y, s);

@@ -433,6 +433,23 @@ def test_gather_few_tokens(aq, bits, G, T, xdt, K):
     _assert_close(y, y_ref, A, f"gather few T{T} b{bits} G{G} {xdt} K{K}")
 
 
+@pytest.mark.parametrize("bits,G", [(4, 64), (8, 32), (8, 128)])
+@pytest.mark.parametrize("E,T,topk,xdt", [(2, 21, 1, "f16"), (4, 40, 2, "f16"), (3, 150, 3, "f16"),
+                                          (4, 37, 3, "bf16")])
+def test_gather_crowded_experts(aq, bits, G, E, T, topk, xdt):
+    """Experts with more than 8 routed pairs: batches of 16 x rows (a partial
+    one included), a trailing batch of 8, and, past 256 pairs, several rounds
+    of the id scan."""
+    N, K = 100, 4 * G if xdt == "f16" else 2048 + 4 * G
+    c, s, b = _experts(E, N, K, G, bits, seed=23)
+    ids = inputs.expert_ids(T, E, topk, seed=23, key=(E, T))
+    assert np.bincount(ids.ravel(), minlength=E).max() > 8
+    xb = inputs.activations(T, K, xdt, seed=23)
+    y_ref, A = oracle.gather_matmul(inputs.from_bits(xb, xdt), c, s, b, ids, K, G, bits)
+    y = aq.aq_gather_qmv(bits_to_dev(xb, xdt), *packed_to_dev(c, s, b), to_dev(ids), G, bits)
+    _assert_close(y, y_ref, A, f"gather crowded E{E} T{T} top{topk} b{bits} G{G} {xdt}")
+
+
 @pytest.mark.parametrize("K", [9600, 19200])
 def test_gather_long_rows(aq, K):
     """Rows long enough that fewer 16-row blocks per workgroup fit the staged scales."""
