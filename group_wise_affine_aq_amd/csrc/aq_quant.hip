@@ -283,11 +283,18 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint32_t *__restr
                                                          int64_t N, int64_t K, int G,
                                                          const int32_t *__restrict__ ids, int64_t T,
                                                          void *__restrict__ out) {
+  // Output chunk idx is elements [32 idx, 32 idx + 32) (row t of the output
+  // is row t of the table, or the t-th looked-up row), so a wave's output is
+  // one contiguous span: each lane's chunk goes through LDS, and the wave
+  // stores the span with consecutive 16-byte units per lane (8 cache lines
+  // per store instruction instead of 32 at one chunk per lane).
+  constexpr int NQ = ODT == X_F32 ? 8 : 4;  // 16-byte units per chunk
+  __shared__ __attribute__((aligned(16))) uint4 stage[256 * NQ];
   const int64_t cpr = K >> 5;  // chunks per row
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = (GATHER ? T : N) * cpr;
-  if (idx >= total) return;
-  int64_t t, c;
+  const bool live = idx < total;
+  int64_t t = 0, c = 0;
   if (total <= 0xFFFFFFFFll) {  // uniform: 32-bit division when the index fits
     const uint32_t t32 = (uint32_t)idx / (uint32_t)cpr;
     t = t32;
@@ -297,11 +304,13 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint32_t *__restr
     c = idx - t * cpr;
   }
   int64_t n = t;
-  bool zero = false;
+  bool zero = !live;
   if constexpr (GATHER) {
-    const int32_t id = ids[t];
-    zero = id < 0 || (int64_t)id >= N;
-    n = zero ? 0 : id;
+    if (live) {
+      const int32_t id = ids[t];
+      zero = id < 0 || (int64_t)id >= N;
+      n = zero ? 0 : id;
+    }
   }
   float r[32];
   if (zero) {
@@ -315,18 +324,29 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint32_t *__restr
 #pragma unroll
     for (int i = 0; i < 32; ++i) r[i] = __builtin_fmaf((float)chunk_code<BITS>(wv, i), s, b);
   }
-  const int64_t e = t * K + c * 32;
+  uint4 q[NQ];
   if constexpr (ODT == X_F32) {
-    float4 *o = reinterpret_cast<float4 *>(reinterpret_cast<float *>(out) + e);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) o[j] = make_float4(r[4 * j], r[4 * j + 1], r[4 * j + 2], r[4 * j + 3]);
+    for (int j = 0; j < 8; ++j)
+      q[j] = make_uint4(__float_as_uint(r[4 * j]), __float_as_uint(r[4 * j + 1]),
+                        __float_as_uint(r[4 * j + 2]), __float_as_uint(r[4 * j + 3]));
   } else {
-    uint32_t p[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) p[j] = pack_rne<ODT>(r[2 * j], r[2 * j + 1]);
-    uint4 *o = reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out) + e);
+    for (int j = 0; j < 4; ++j)
+      q[j] = make_uint4(pack_rne<ODT>(r[8 * j], r[8 * j + 1]), pack_rne<ODT>(r[8 * j + 2], r[8 * j + 3]),
+                        pack_rne<ODT>(r[8 * j + 4], r[8 * j + 5]), pack_rne<ODT>(r[8 * j + 6], r[8 * j + 7]));
+  }
+  const int lane = threadIdx.x & 63;
+  uint4 *ws = stage + (threadIdx.x >> 6) * 64 * NQ;  // this wave's span
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = make_uint4(p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]);
+  for (int j = 0; j < NQ; ++j) ws[lane * NQ + j] = q[j];
+  __syncthreads();
+  const int64_t w0 = idx - lane;  // the wave's first chunk
+  uint4 *o = reinterpret_cast<uint4 *>(out) + w0 * NQ;
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    const int u = j * 64 + lane;  // unit u of the span: chunk w0 + u / NQ
+    if (w0 + u / NQ < total) o[u] = ws[u];
   }
 }
 

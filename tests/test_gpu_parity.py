@@ -158,6 +158,32 @@ def test_dequantize_bitexact(aq, bits, out):
     assert np.array_equal(out_bits(got), ref_bits)
 
 
+@pytest.mark.parametrize("bits,out", [(4, "bf16"), (3, "f32"), (8, "f16")])
+@pytest.mark.parametrize("lookup", [False, True])
+def test_dequantize_stays_in_output(aq, bits, out, lookup):
+    """The last wave's store span ends inside the output: elements past it are
+    never written (a ragged tail of chunks inside one wave and one workgroup)."""
+    import torch
+    G = GROUP_FOR_BITS[bits]
+    R, K = 37, 5 * G
+    _, (c, s, b) = _quantized(R, K, G, bits, seed=21)
+    code = {"f32": oracle.F32, "f16": oracle.F16, "bf16": oracle.BF16}[out]
+    ids = np.random.default_rng(21).integers(-1, R + 1, size=29).astype(np.int32)
+    rows = len(ids) if lookup else R
+    slack = 4096
+    buf = torch.full((rows * K + slack,), 3.0, dtype=torch_dtype(out), device="cuda")
+    dst = buf[:rows * K].view(rows, K)
+    if lookup:
+        aq.aq_embedding(to_dev(ids), *packed_to_dev(c, s, b), G, bits, out=dst)
+        ref = oracle.embedding(c, s, b, ids, K, G, bits, code)
+    else:
+        aq.aq_dequantize(*packed_to_dev(c, s, b), G, bits, out=dst)
+        ref = oracle.dequantize(c, s, b, K, G, bits, code)
+    assert torch.equal(buf[rows * K:].cpu(), torch.full((slack,), 3.0, dtype=torch_dtype(out)))
+    ref_bits = ref.view(np.uint32) if out == "f32" else ref
+    assert np.array_equal(out_bits(dst), ref_bits)
+
+
 # ---- quantized embedding ---------------------------------------------------------------------
 @pytest.mark.parametrize("bits", ALL_BITS)
 @pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
