@@ -27,7 +27,8 @@
 // codes fill exactly `bits` bytes at byte offset 8k/8*bits of the row, so
 // every thread stores whole bytes and no two threads share a byte.  A group
 // is G/8 adjacent lanes, reduced with lane shuffles.  Dequantize: one thread
-// per 32-code chunk (`bits` words).
+// per 32-code chunk (`bits` words); a wave's 64 output chunks are one
+// contiguous span, stored through LDS in lane-contiguous 16-byte units.
 #include "aq_device.hpp"
 #include "aq_internal.hpp"
 
