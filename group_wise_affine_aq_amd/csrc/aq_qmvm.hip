@@ -582,7 +582,8 @@ __global__ __launch_bounds__(64 * W) void gather_qmvm_kernel(
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ biases, int64_t E, int64_t N,
     int64_t K, const int32_t *__restrict__ ids, int topk, int kw, uint16_t *__restrict__ y) {
   __shared__ int list[kGTile];
-  __shared__ int count;
+  __shared__ int count;  // pairs of the current round in list
+  __shared__ int later;  // set if this expert has pairs past the first round
   __shared__ __attribute__((aligned(16))) float part[W * 16 * R * (WIDE ? 16 : 8)];
   extern __shared__ __attribute__((aligned(16))) uint16_t sbl[];  // [2][16 R][gpr]
   typedef MBlock<XT, BITS, W, GS, 8, R> Blk;
@@ -602,13 +603,20 @@ __global__ __launch_bounds__(64 * W) void gather_qmvm_kernel(
       if (id < 0 || id >= E)
         for (int nn = 0; nn < nrows; ++nn) y[p * N + row0 + nn] = 0;
     }
-  // does any pair choose this expert?  (if not, nothing of it is read)
-  if (threadIdx.x == 0) count = 0;
+  // does any pair choose this expert?  (if not, nothing of it is read)  The
+  // same scan lists the first round's pairs.
+  if (threadIdx.x == 0) {
+    count = 0;
+    later = 0;
+  }
   __syncthreads();
   for (int64_t p = threadIdx.x; p < total; p += 64 * W)
-    if (ids[p] == e) atomicAdd(&count, 1);
+    if (ids[p] == e) {
+      if (p < kGTile) list[atomicAdd(&count, 1)] = (int)p;
+      else later = 1;
+    }
   __syncthreads();
-  if (count == 0) return;
+  if (count == 0 && later == 0) return;
 
   const uint32_t *wrows = codes + e * wpe + row0 * (K >> 5) * BITS;
   const __amdgpu_buffer_rsrc_t rx = mk_rsrc(x, T * K * 2);
@@ -620,14 +628,15 @@ __global__ __launch_bounds__(64 * W) void gather_qmvm_kernel(
                                  nrows, gpr, sbl);
   constexpr int D = kDepth<BITS>;
   for (int64_t t0 = 0; t0 < total; t0 += kGTile) {
-    __syncthreads();  // also publishes the staged scales before the first batch
-    if (threadIdx.x == 0) count = 0;
-    __syncthreads();
-    for (int i = threadIdx.x; i < kGTile; i += 64 * W) {
-      const int64_t p = t0 + i;
-      if (p < total && ids[p] == e) list[atomicAdd(&count, 1)] = (int)i;
+    if (t0 > 0) {  // uniform; the first round's list is already built
+      if (threadIdx.x == 0) count = 0;
+      __syncthreads();
+      for (int i = threadIdx.x; i < kGTile; i += 64 * W) {
+        const int64_t p = t0 + i;
+        if (p < total && ids[p] == e) list[atomicAdd(&count, 1)] = (int)i;
+      }
     }
-    __syncthreads();
+    __syncthreads();  // publishes the list (and, first, the staged scales)
     const int n = count;
     for (int b0 = 0; b0 < n;) {
       // slot row m = n16 % (batch rows) carries pair list[b0 + m]; missing

@@ -476,6 +476,21 @@ def test_gather_crowded_experts(aq, bits, G, E, T, topk, xdt):
     _assert_close(y, y_ref, A, f"gather crowded E{E} T{T} top{topk} b{bits} G{G} {xdt}")
 
 
+def test_gather_expert_only_past_first_round(aq):
+    """Experts whose pairs all lie past the first 256 (token, slot) pairs are
+    still run (the first id scan lists only the first 256)."""
+    G, bits, E, N, K, T, topk = 64, 4, 3, 70, 256, 100, 3
+    c, s, b = _experts(E, N, K, G, bits, seed=25)
+    ids = np.zeros((T, topk), dtype=np.int32)
+    ids[90:, 1] = 1  # pairs 271.. only
+    ids[95:, 2] = 2
+    assert (ids.ravel()[:256] == 0).all()
+    xb = inputs.activations(T, K, "f16", seed=25)
+    y_ref, A = oracle.gather_matmul(inputs.from_bits(xb, "f16"), c, s, b, ids, K, G, bits)
+    y = aq.aq_gather_qmv(bits_to_dev(xb, "f16"), *packed_to_dev(c, s, b), to_dev(ids), G, bits)
+    _assert_close(y, y_ref, A, "gather expert only past the first round")
+
+
 @pytest.mark.parametrize("K", [9600, 19200])
 def test_gather_long_rows(aq, K):
     """Rows long enough that fewer 16-row blocks per workgroup fit the staged scales."""
