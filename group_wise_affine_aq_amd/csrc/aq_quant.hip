@@ -12,12 +12,14 @@
 // binary32 weights are exact in binary64.  Approximate binary32 arithmetic
 // only proposes candidates that the exact tests then correct by one step.
 //
-// Range search ("mlx-gptq", "How it works": the --mse grid search narrows a
-// group's min-max range where clipping the extremes costs less than the
-// coarser step costs the rest of the group): candidates i < steps shrink the
-// range to [p min, p max], p = (100 - i) / 100 (binary64), each quantized by
-// the rules above; the least binary64 sum of squared errors wins, an equal
-// one keeping the wider candidate.
+// Range search ("mlx-gptq", "How it works", the --mse option: a group may be
+// quantized over a range narrower than its min-max span, trading error on its
+// outermost members for a finer step on the others): candidate i < steps
+// moves both ends of [min, max] inwards by d = (max - min) * (i / 200)
+// (binary64, no contraction), keeping the centred fraction (100 - i) / 100
+// of the width, so every candidate lies inside [min, max]; each is quantized
+// by the rules above and the least binary64 sum of squared errors wins, an
+// equal one keeping the wider candidate.
 //
 // Dequantize ("Tutorial 10: Quantization", s.3/s.7): q*s + b in binary32
 // (one rounding, the product is exact), then round-to-nearest-even to the
@@ -218,11 +220,18 @@ __global__ __launch_bounds__(256) void quantize_mse_kernel(const void *__restric
   double best = __builtin_inf();
   uint16_t best_b = 0, best_s = 0;
   uint64_t best_packed = 0;
+  const double width = (double)hi - (double)lo;
   for (int i = 0; i < steps; ++i) {
-    const double pr = (double)(100 - i) / 100.0;
-    const uint16_t b16 = f16_round_down_d(pr * (double)lo);
+    double clo, chi;
+    {
+#pragma clang fp contract(off)
+      const double d = width * ((double)i / 200.0);
+      clo = (double)lo + d;
+      chi = (double)hi - d;
+    }
+    const uint16_t b16 = f16_round_down_d(clo);
     const double b = h2d(b16);
-    const uint16_t s16 = f16_scale_up(b, pr * (double)hi, L);
+    const uint16_t s16 = f16_scale_up(b, chi, L);
     const double s = h2d(s16);
     const float bf = (float)b;
     const float rs = s16 ? __builtin_amdgcn_rcpf((float)s) : 0.f;

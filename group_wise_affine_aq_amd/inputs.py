@@ -67,6 +67,21 @@ def weights(N: int, K: int, *, seed: int = 0, key=(0,), std: float = 0.02,
     return w.astype(np.float32)
 
 
+def same_sign_weights(N: int, K: int, G: int, *, seed: int = 0, key=(0,),
+                      std: float = 0.02) -> np.ndarray:
+    """float32 [N, K] whose groups of G along a row each share one sign:
+    |N(0, std)| + std/2, negated in every other group, and in every third
+    group one member (at a seeded position) multiplied by 8."""
+    r = _rng(seed, ROLE_W, N, K, G, *key)
+    w = np.abs(r.standard_normal((N, K))) * std + std / 2
+    grp = w.reshape(N, K // G, G)
+    grp[:, 1::2, :] *= -1.0
+    far = r.integers(0, G, size=(N, K // G))
+    rows, gs = np.nonzero(np.broadcast_to(np.arange(K // G) % 3 == 0, (N, K // G)))
+    grp[rows, gs, far[rows, gs]] *= 8.0
+    return w.astype(np.float32)
+
+
 def activations(M: int, K: int, dtype: str, *, seed: int = 0, key=(0,)) -> np.ndarray:
     """uint16 bit patterns [M, K] of fp16 or bf16 values ~ N(0, 1)."""
     x = _rng(seed, ROLE_X, M, K, *key).standard_normal((M, K))

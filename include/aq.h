@@ -100,15 +100,17 @@ aq_status aq_quantize(const void *w, aq_dtype w_dtype, int64_t N, int64_t K, int
                       int bits, uint32_t *codes, uint16_t *scales, uint16_t *biases,
                       void *stream);
 
-/* Range-search quantize ("mlx-gptq", "How it works": the --mse grid search
- * narrows a group's min-max range where clipping the extremes costs less
- * than the coarser step costs the rest of the group).  Same arguments,
- * outputs, format and preconditions as aq_quantize, plus steps in [1, 50]:
- * candidate i < steps narrows the group's range to [p*min, p*max] with
- * p = (100 - i)/100 (binary64), takes bias, scale and codes from it by the
- * rules of aq_quantize (members outside the narrowed range clip to code 0
- * or 2^bits-1) and scores sum (w - (q*s + b))^2 in binary64; the least
- * score wins, an equal score keeping the wider candidate.  steps = 1 gives
+/* Range-search quantize ("mlx-gptq", "How it works", the --mse option: a
+ * group may be quantized over a range narrower than its min-max span,
+ * trading error on its outermost members for a finer step on the others).
+ * Same arguments, outputs, format and preconditions as aq_quantize, plus
+ * steps in [1, 50]: candidate i < steps moves both ends of the group's range
+ * inwards by d = (max - min) * (i / 200) (binary64, left to right), i.e.
+ * keeps the centred fraction (100 - i)/100 of the width, so every candidate
+ * lies inside [min, max]; it takes bias, scale and codes from that range by
+ * the rules of aq_quantize (members outside it clip to code 0 or 2^bits-1)
+ * and scores sum (w - (q*s + b))^2 in binary64; the least score wins, an
+ * equal score keeping the wider candidate.  steps = 1 gives
  * exactly aq_quantize.  (The pages fix neither the grid nor the measure;
  * these are this library's choices.)  Scores that differ only in the last
  * bits of their binary64 sums may pick either candidate.

@@ -155,9 +155,10 @@ def quantize(w: np.ndarray, group_size: int, bits: int):
 
 def quantize_mse(w: np.ndarray, group_size: int, bits: int, steps: int, only: int = -1,
                  details: bool = False):
-    """Range-search quantizer (reading R14): candidates p_i = (100 - i)/100,
-    i < steps, shrink [min, max] to [p min, p max]; least binary64 squared error
-    wins.  only >= 0 evaluates that candidate alone.
+    """Range-search quantizer (reading R14): candidate i < steps moves both ends
+    of [min, max] inwards by d_i = (max - min) * (i / 200), keeping the centred
+    fraction (100 - i)/100 of the width; least binary64 squared error wins.
+    only >= 0 evaluates that candidate alone.
     -> (codes, scales, biases), plus (chosen int32 [N, K/G], errs float64
     [N, K/G, steps]) when details."""
     w = np.ascontiguousarray(w, dtype=np.float32)

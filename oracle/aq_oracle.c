@@ -53,16 +53,21 @@
  *      (token, slot), no routing-weight combine.
  *  R13 embedding ([T10] s.6): out[t,:] is row ids[t] dequantized as in R4;
  *      an id outside the table gives a zero row.
- *  R14 range search ([GPTQ] "How it works", the --mse grid search: a
- *      group's min-max range is narrowed where clipping its extremes costs
- *      less than the coarser step costs the other members).  The pages give
- *      no grid and no error measure; taken here: candidates i = 0..steps-1
- *      with p_i = (100 - i) / 100 (binary64 division), range
- *      [p_i * min, p_i * max] (binary64 products), bias and scale from that
- *      range by R1, codes by R2 against them (members outside the range
- *      clip to 0 or 2^b-1), error = sum over the group, in member order,
- *      of (w - (q*s + b))^2 in binary64.  The least error wins; an equal
- *      error keeps the earlier (wider) candidate.  steps = 1 is R1/R2.
+ *  R14 range search ([GPTQ] "How it works", the --mse option: a group may
+ *      be quantized over a range narrower than its min-max span, trading
+ *      error on its outermost members for a finer step on the others).
+ *      The pages give no grid and no error measure; taken here: candidate
+ *      i = 0..steps-1 keeps the fraction p_i = (100 - i)/100 of the width,
+ *      centred, i.e. both ends move inwards by the same amount
+ *        d_i = (max - min) * (i / 200)            (binary64, left to right)
+ *        range_i = [min + d_i, max - d_i]         (binary64)
+ *      so every candidate lies inside [min, max] whatever the signs of the
+ *      members (candidate 0 is [min, max] itself).  Bias and scale come
+ *      from range_i by R1, codes by R2 against them (members outside the
+ *      range clip to 0 or 2^b-1), error = sum over the group, in member
+ *      order, of (w - (q*s + b))^2 in binary64.  The least error wins; an
+ *      equal error keeps the earlier (wider) candidate.  steps = 1 is
+ *      R1/R2.
  *
  * Exactness of the binary64 comparisons used below.  Every finite fp16
  * value is an integer multiple of 2^-24 of magnitude < 2^16; q*s with
@@ -383,12 +388,15 @@ int oracle_quantize_mse(const float *w, int64_t N, int64_t K, int G, int bits, i
       double best = INFINITY;
       int best_i = -1;
       uint16_t best_b = 0, best_s = 0;
+      const double width = hi - lo;
       for (int i = (only >= 0 ? only : 0); i < (only >= 0 ? only + 1 : steps); ++i) {
-        const double p = (double)(100 - i) / 100.0;
+        /* both ends move inwards by d; the range keeps (100 - i)% of its width */
+        const double d = width * ((double)i / 200.0);
+        const double clo = lo + d, chi = hi - d;
         uint16_t b16 = 0, s16 = 0;
-        half_round_down(p * lo, &b16);
+        half_round_down(clo, &b16);
         const double b = oracle_half_to_double(b16);
-        group_scale(b, p * hi, L, &s16);
+        group_scale(b, chi, L, &s16);
         const double s = oracle_half_to_double(s16);
         double e = 0.0;
         for (int k = 0; k < G; ++k) {

@@ -88,6 +88,22 @@ def test_quantize_mse(aq, bits, G):
     assert _check_mse(w, G, bits, steps, got) <= N * K // G // 50
 
 
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("G", [32, 128])
+def test_quantize_mse_same_sign_groups(aq, bits, G):
+    """Groups whose members all share a sign (alternating positive and
+    negative, some with one far member): the device follows the reference,
+    and its grids never reach below the min-max grid's bias nor use a larger
+    scale (every candidate range lies inside [min, max])."""
+    N, K, steps = 21, 6 * G, 50
+    w = inputs.same_sign_weights(N, K, G, seed=22, key=(bits,))
+    got = packed_from_dev(*aq.aq_quantize_mse(to_dev(w), G, bits, steps))
+    _check_mse(w, G, bits, steps, got)
+    _, s0, b0 = oracle.quantize(w, G, bits)
+    f16 = lambda a: a.view(np.float16).astype(np.float64)
+    assert (f16(got[2]) >= f16(b0)).all() and (f16(got[1]) <= f16(s0)).all()
+
+
 def test_quantize_mse_one_step_and_half_inputs(aq):
     G, bits, N, K = 64, 4, 29, 512
     w = inputs.weights(N, K, seed=19, outliers=True)
@@ -230,7 +246,8 @@ _QMV_SHAPES = [(1, 32, 32), (1, 64, 64), (3, 128, 128), (200, 96, 32), (129, 204
                (5, 32768, 64)]
 
 
-# bf16 only at K >= 2048, where the bound covers a bf16 result's own rounding
+# bf16 only at K >= 512 (test_bf16_small_k), where the bound covers a bf16
+# result's own rounding
 @pytest.mark.parametrize("xdt,N,K,G", [("f16",) + t for t in _QMV_SHAPES] +
                          [("bf16",) + t for t in _QMV_SHAPES if t[1] >= 2048])
 def test_qmv_shapes(aq, xdt, N, K, G):
@@ -345,9 +362,10 @@ def test_qmm_shapes_f16(aq, M, N, K, G):
 @pytest.mark.parametrize("M,N,K,G", [(1, 1, 2048, 32), (7, 33, 2080, 32), (257, 129, 2112, 64),
                                      (33, 300, 4096, 128)])
 def test_qmm_shapes_bf16(aq, M, N, K, G):
-    """bf16 at the workloads' depth (K >= 2048).  A bf16 output alone may be
-    off by 2^-8*|y|, which the bound 2^-9*A covers only while |y| <= A/2 -- true
-    for such K (|y|/A ~ 1/sqrt(K)), not for tiny K, for any kernel."""
+    """bf16 at the workloads' depth (K >= 2048; 512..1408 in test_bf16_small_k).
+    A bf16 output alone may be off by 2^-8*|y|, which the bound 2^-9*A covers
+    only while |y| <= A/2 (|y|/A ~ 1/sqrt(K)); the kernel's rounding of the
+    weights to bf16 adds to that, so below K ~ 512 it can leave the bound."""
     bits, xdt = 4, "bf16"
     _, (c, s, b) = _quantized(N, K, G, bits, seed=8)
     xb = inputs.activations(M, K, xdt, seed=8, key=(M, N, K))
@@ -384,6 +402,41 @@ def test_qmm_equals_gemm_of_dequantized(aq):
     ref = (x.float() @ wq.float().T).double().cpu().numpy()
     y = out_to_f64(aq.aq_qmm(x, *dev, G, bits))
     assert np.max(np.abs(y - ref) / (np.abs(ref) + 1e-3)) < 2 ** -7
+
+
+# ---- bf16 below the workloads' depth --------------------------------------------------------
+@pytest.mark.parametrize("bits", [3, 4, 8])
+@pytest.mark.parametrize("K,G", [(512, 64), (1024, 128), (1408, 64)])
+def test_bf16_small_k(aq, bits, K, G):
+    """bf16 activations at K = 512, 1024 and 1408 (an MoE down-projection
+    width) through every matmul entry point: aq_qmv at 1, 3 and 8 rows,
+    aq_qmm, aq_gather_qmv and aq_gather_qmm.  From K = 512 the bound covers a
+    bf16 result's own rounding and the prefill kernel's rounding of the
+    weights to bf16 (tests/test_oracle_matmul.py pins where it stops)."""
+    xdt = "bf16"
+    N = 100
+    _, (c, s, b) = _quantized(N, K, G, bits, seed=25)
+    dev = packed_to_dev(c, s, b)
+    for M in (1, 3, 8):
+        xb = inputs.activations(M, K, xdt, seed=25, key=(K, M, bits))
+        y_ref, A = oracle.matmul(inputs.from_bits(xb, xdt), c, s, b, K, G, bits)
+        _assert_close(aq.aq_qmv(bits_to_dev(xb, xdt), *dev, G, bits), y_ref, A,
+                      f"qmv bf16 K{K} M{M} b{bits}")
+    M = 130
+    xb = inputs.activations(M, K, xdt, seed=25, key=(K, M, bits))
+    y_ref, A = oracle.matmul(inputs.from_bits(xb, xdt), c, s, b, K, G, bits)
+    _assert_close(aq.aq_qmm(bits_to_dev(xb, xdt), *dev, G, bits), y_ref, A,
+                  f"qmm bf16 K{K} b{bits}")
+    E, T, topk = 6, 40, 3
+    ce, se, be = _experts(E, N, K, G, bits, seed=25)
+    ids = inputs.expert_ids(T, E, topk, seed=25)
+    xb = inputs.activations(T, K, xdt, seed=25, key=(K, bits))
+    y_ref, A = oracle.gather_matmul(inputs.from_bits(xb, xdt), ce, se, be, ids, K, G, bits)
+    deve = packed_to_dev(ce, se, be)
+    _assert_close(aq.aq_gather_qmv(bits_to_dev(xb, xdt), *deve, to_dev(ids), G, bits), y_ref, A,
+                  f"gather_qmv bf16 K{K} b{bits}")
+    _assert_close(aq.aq_gather_qmm(bits_to_dev(xb, xdt), *deve, to_dev(ids), G, bits), y_ref, A,
+                  f"gather_qmm bf16 K{K} b{bits}")
 
 
 # ---- dispatch ----------------------------------------------------------------------------------

@@ -120,25 +120,41 @@ def test_expert_ids_distinct():
     assert ids.min() >= 0 and ids.max() < 64
 
 
-def test_bf16_output_rounding_alone_can_exceed_bound_at_tiny_k():
-    """A bf16 result can be off by 2^-8*|y| from its own rounding, which the
-    bound 2^-9*A covers only while |y| <= A/2.  At K = 64 even the exactly
-    rounded bf16 value of the reference result comes close to or leaves the
-    bound, so bf16 matmul parity is checked at the workloads' depth (K >= 2048)."""
-    G, bits, M, N, K = 64, 4, 64, 128, 64
-    w = inputs.weights(N, K, seed=8, key=(G, bits, 17), outliers=True)
+def _bf16_ratios(M, N, K, G, seed=8, bits=4):
+    """Worst error/bound of (a) the reference result rounded once to bf16 (the
+    best any bf16 output can do) and (b) a model of the prefill kernel's
+    arithmetic: weights rounded to bf16 first (the reference's own bf16
+    dequantize), products summed in binary32, the sum rounded to bf16."""
+    w = inputs.weights(N, K, seed=seed, key=(G, bits, 17), outliers=True)
     codes, scales, biases = oracle.quantize(w, G, bits)
-    xb = inputs.activations(M, K, "bf16", seed=8, key=(M, N, K))
-    y_ref, A = oracle.matmul(inputs.from_bits(xb, "bf16"), codes, scales, biases, K, G, bits)
-    y_rounded = inputs.from_bits(inputs.to_bits(y_ref.astype(np.float32), "bf16"), "bf16")
-    _, ratio = oracle.within_tolerance(y_rounded, y_ref, A)
-    assert ratio > 0.5
-    # at K = 4096 the same rounding uses a small part of the bound
-    K = 4096
-    w = inputs.weights(N, K, seed=8, key=(G, bits, 18), outliers=True)
-    codes, scales, biases = oracle.quantize(w, G, bits)
-    xb = inputs.activations(M, K, "bf16", seed=8, key=(M, N, K))
-    y_ref, A = oracle.matmul(inputs.from_bits(xb, "bf16"), codes, scales, biases, K, G, bits)
-    y_rounded = inputs.from_bits(inputs.to_bits(y_ref.astype(np.float32), "bf16"), "bf16")
-    _, ratio = oracle.within_tolerance(y_rounded, y_ref, A)
-    assert ratio < 0.25
+    xb = inputs.activations(M, K, "bf16", seed=seed, key=(M, N, K))
+    x = inputs.from_bits(xb, "bf16")
+    y_ref, A = oracle.matmul(x, codes, scales, biases, K, G, bits)
+    best = inputs.from_bits(inputs.to_bits(y_ref.astype(np.float32), "bf16"), "bf16")
+    w_bf16 = inputs.from_bits(oracle.dequantize(codes, scales, biases, K, G, bits, oracle.BF16),
+                              "bf16")
+    model = x.astype(np.float32) @ w_bf16.astype(np.float32).T
+    model = inputs.from_bits(inputs.to_bits(model, "bf16"), "bf16")
+    return oracle.within_tolerance(best, y_ref, A)[1], oracle.within_tolerance(model, y_ref, A)[1]
+
+
+def test_bf16_bound_threshold_in_k():
+    """Where the 2^-9*A bound fails for bf16 results, and why.  A bf16 result
+    carries its own rounding, up to 2^-8*|y|, which the bound covers only
+    while |y| <= A/2 (|y|/A shrinks like 1/sqrt(K) on random data):
+      * K = 64: even the correctly rounded reference leaves the bound, so no
+        bf16 output can meet it there;
+      * K = 96 and 160: the correctly rounded reference stays inside, but
+        rounding the weights to bf16 before the product (the prefill kernel's
+        arithmetic) adds up to 2^-8 relative per term and leaves it;
+      * K >= 512: both stay well inside (under 0.6 of the bound), which is where
+        the bf16 parity tests start."""
+    best, model = _bf16_ratios(64, 128, 64, 64)
+    assert best > 1.0
+    for M, N, K, G in ((7, 33, 96, 32), (257, 129, 160, 32)):
+        best, model = _bf16_ratios(M, N, K, G)
+        assert best < 1.0 < model, (K, best, model)
+    for M, N, K, G in ((64, 128, 512, 64), (37, 100, 1024, 64), (64, 128, 1408, 64),
+                       (64, 128, 4096, 64)):
+        best, model = _bf16_ratios(M, N, K, G)
+        assert best < 0.6 and model < 0.6, (K, best, model)

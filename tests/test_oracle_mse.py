@@ -1,14 +1,22 @@
 """Pins of the CPU reference range-search quantizer (reading R14).
 
-"mlx-gptq", "How it works": the --mse grid search narrows a group's min-max
-range where clipping the extremes costs less than the coarser step costs the
-rest of the group.  Reading R14 fixes the grid (p_i = (100 - i)/100, range
-[p_i min, p_i max]) and the measure (sum of squared errors).  Pinned here by
+"mlx-gptq", "How it works" (the --mse option): a group may be quantized over a
+range narrower than its min-max span, trading error on its outermost members
+for a finer step on all the others.  Reading R14 fixes the family of
+narrowed ranges (candidate i keeps the centred fraction p_i = (100 - i)/100
+of the width: both ends move inwards by d_i = (max - min) * i/200) and the
+measure (sum of squared errors).  Pinned here by
   * an exact brute force over the candidates with rational arithmetic
     (bias, scale, codes and error of every candidate derived independently,
-    the winner taken over exact errors),
+    the winner taken over exact errors), on mixed-sign groups and on groups
+    whose members all share a sign,
+  * exact containment: every candidate range lies inside [min, max] and keeps
+    p_i of the width up to two binary64 roundings, so its bias never falls
+    below the min-max grid's bias and its scale never exceeds that grid's,
   * the special case steps = 1, which is the plain quantizer,
-  * "never worse than the min-max grid" per group, exactly,
+  * "never worse than the min-max grid" per group, exactly, and strictly
+    better on a same-sign group with one far value (the page's case: clipping
+    the extreme pays),
   * the clipping invariants of the chosen grid.
 """
 import bisect
@@ -28,6 +36,10 @@ def _h(v):
     return int(np.float16(v).view(np.uint16))
 
 
+def _f16(h):
+    return float(np.uint16(h).view(np.float16))
+
+
 def candidate(ws, bits, lo, hi):
     """Bias, scale and codes of the grid spanning [lo, hi], by enumeration."""
     L = (1 << bits) - 1
@@ -44,20 +56,26 @@ def candidate(ws, bits, lo, hi):
     return b, s, qs, err
 
 
+def candidate_range(lo, hi, i):
+    """Range i of the search, in binary64 as the reading states (Python floats
+    are binary64): both ends move inwards by (max - min) * (i / 200)."""
+    d = (hi - lo) * (i / 200)
+    return lo + d, hi - d
+
+
 def brute_force_search(ws, bits, steps):
     lo, hi = min(ws), max(ws)
-    cands = []
-    for i in range(steps):
-        p = (100 - i) / 100.0          # binary64, as the reading states
-        cands.append(candidate(ws, bits, Fraction(p * lo), Fraction(p * hi)))
-    return cands
+    return [candidate(ws, bits, *map(Fraction, candidate_range(lo, hi, i)))
+            for i in range(steps)]
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4])
-@pytest.mark.parametrize("G", [32, 64])
-def test_brute_force_search(bits, G):
-    steps = 21
-    w = inputs.weights(2, 2 * G, seed=3, key=(bits, G, 14), outliers=True)
+def _same_sign_rows(G, n, seed):
+    """Rows of two groups each, every group of one sign (alternating), some
+    with one member far out."""
+    return inputs.same_sign_weights(n, 2 * G, G, seed=seed, key=(14,))
+
+
+def _check_against_brute_force(w, G, bits, steps):
     codes, scales, biases, chosen, errs = oracle.quantize_mse(w, G, bits, steps, details=True)
     q = oracle.unpack(codes, w.shape[1], bits)
     narrowed = 0
@@ -78,8 +96,62 @@ def test_brute_force_search(bits, G):
             assert biases[n, g] == _h(float(b)) and scales[n, g] == _h(float(s)), (n, g)
             assert list(q[n, g * G:(g + 1) * G]) == qs, (n, g)
             narrowed += i > 0
+    return narrowed
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("G", [32, 64])
+def test_brute_force_search(bits, G):
+    w = inputs.weights(2, 2 * G, seed=3, key=(bits, G, 14), outliers=True)
+    narrowed = _check_against_brute_force(w, G, bits, 21)
     if bits <= 3:
         assert narrowed > 0  # low bit widths do narrow on Gaussian groups
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("G", [32, 64])
+def test_brute_force_search_same_sign_groups(bits, G):
+    w = _same_sign_rows(G, 2, seed=bits * 100 + G)
+    narrowed = _check_against_brute_force(w, G, bits, 21)
+    assert narrowed > 0  # the far values get clipped on one side or the other
+
+
+def test_candidate_ranges_lie_inside_the_group_range():
+    """Exactly: lo <= lo_i <= hi_i <= hi, and hi_i - lo_i = p_i (hi - lo) up to
+    the two binary64 roundings of the ends, for mixed-sign, all-positive and
+    all-negative groups (including a constant group and a one-binade span)."""
+    rng = np.random.default_rng(7)
+    groups = [rng.standard_normal(64) * 0.02,
+              np.abs(rng.standard_normal(64)) * 0.02 + 1e-3,
+              -np.abs(rng.standard_normal(64)) * 0.02 - 1e-3,
+              np.full(64, 0.37), np.linspace(1.0, 1.9, 64), np.linspace(-3e4, -1e-4, 64)]
+    for grp in groups:
+        g32 = [float(np.float32(v)) for v in grp]
+        lo, hi = min(g32), max(g32)
+        for i in range(50):
+            a, b = candidate_range(lo, hi, i)
+            A, B, Lo, Hi = map(Fraction, (a, b, lo, hi))
+            assert Lo <= A <= B <= Hi, i
+            keep = Fraction(100 - i, 100) * (Hi - Lo)
+            ulp = Fraction(max(abs(lo), abs(hi))) * Fraction(1, 2**51)
+            assert abs((B - A) - keep) <= 2 * ulp + (Hi - Lo) * Fraction(1, 2**50), i
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_candidates_never_widen_the_min_max_grid(bits):
+    """Each candidate's grid, as the reference builds it (only = j), has a bias
+    >= the min-max grid's bias and a scale <= its scale: the search only ever
+    narrows, on same-sign groups too (with the range [p min, p max] an
+    all-positive group's lower end would fall below its minimum)."""
+    G, steps = 32, 50
+    w = np.concatenate([_same_sign_rows(G, 2, seed=bits),
+                        inputs.weights(2, 2 * G, seed=8, key=(bits,), outliers=True)])
+    _, s0, b0 = oracle.quantize(w, G, bits)
+    b0v, s0v = np.vectorize(_f16)(b0), np.vectorize(_f16)(s0)
+    for j in range(steps):
+        _, sj, bj = oracle.quantize_mse(w, G, bits, steps, only=j)
+        assert (np.vectorize(_f16)(bj) >= b0v).all(), j
+        assert (np.vectorize(_f16)(sj) <= s0v).all(), j
 
 
 @pytest.mark.parametrize("bits", range(2, 9))
@@ -103,16 +175,36 @@ def _group_errors(w, c, s, b, G, bits):
 @pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_never_worse_than_min_max(bits):
     G, steps = 32, 50
-    w = inputs.weights(6, 4 * G, seed=5, key=(bits,), outliers=True)
+    w = np.concatenate([inputs.weights(6, 4 * G, seed=5, key=(bits,), outliers=True),
+                        np.tile(_same_sign_rows(G, 2, seed=50 + bits), 2)])
     e_mse = _group_errors(w, *oracle.quantize_mse(w, G, bits, steps), G, bits)
     e_rtn = _group_errors(w, *oracle.quantize(w, G, bits), G, bits)
     assert all(a <= b for a, b in zip(e_mse.ravel(), e_rtn.ravel()))
 
 
+def test_clipping_a_far_value_of_a_positive_group_pays():
+    """An all-positive group: 31 members spread evenly over [1, 1.125] and one
+    at 2.  At 2 bits the min-max grid puts one level near the far value and
+    leaves three for the rest; the search clips the far value and must come
+    out strictly better, its bias still no lower than the group minimum."""
+    G, bits = 32, 2
+    grp = np.concatenate([np.linspace(1.0, 1.125, G - 1), [2.0]]).astype(np.float32)
+    w = grp[None, :]
+    e_rtn = _group_errors(w, *oracle.quantize(w, G, bits), G, bits)[0, 0]
+    c, s, b, chosen, _ = oracle.quantize_mse(w, G, bits, 50, details=True)
+    e_mse = _group_errors(w, c, s, b, G, bits)[0, 0]
+    assert chosen[0, 0] > 0 and e_mse < e_rtn
+    # the low end never falls below the minimum (with [p min, p max] it would
+    # drop to p * 1.0 < 1.0 and waste part of the grid below every member)
+    assert _f16(b[0, 0]) >= 1.0
+    assert _f16(b[0, 0]) + 3 * _f16(s[0, 0]) < 2.0  # the far value is clipped
+
+
 def test_clipping_invariants():
     G, bits, steps = 64, 3, 30
     L = (1 << bits) - 1
-    w = inputs.weights(8, 4 * G, seed=6, key=(15,), outliers=True)
+    w = np.concatenate([inputs.weights(8, 4 * G, seed=6, key=(15,), outliers=True),
+                        np.tile(_same_sign_rows(G, 2, seed=9), 2)])
     c, s, b = oracle.quantize_mse(w, G, bits, steps)
     q = oracle.unpack(c, w.shape[1], bits)
     sv = s.view(np.float16).astype(np.float64)
