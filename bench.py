@@ -178,7 +178,7 @@ def main():
     ms_per_step = ms_total / args.steps
     value = step_wbytes * args.steps / (ms_total * 1e-3) / 1e9
     print(f"# timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step (device), "
-          f"host wall {wall * 1e3 / args.steps:.2f} us/step", file=sys.stderr, flush=True)
+          f"host wall {wall * 1e6 / args.steps:.2f} us/step", file=sys.stderr, flush=True)
 
     # ---- per-launch durations (HIP events on the launch stream) ---------------------------
     # For each shape: one graph of `reps` back-to-back launches over the cold

@@ -16,6 +16,9 @@ namespace {
 
 constexpr int64_t kMaxQmvRows = 8;
 constexpr int64_t kMaxQmmK = 0x7FFFFFFF / (256 * 2);  // 4194303
+// the prefill grid: 256-column tiles in x, 256-row tiles (or twice as many
+// 128-row halves for a split last round) in y, at most 65535
+constexpr int64_t kMaxQmmM = 65535 / 2 * 256;  // 8388352
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -195,8 +198,7 @@ aq_status aq_qmm(const void *x, aq_dtype x_dtype, int64_t M, const uint32_t *cod
   aq_status st = check_matmul(x, x_dtype, M, codes, scales, biases, N, K, group_size, bits, y);
   if (st != AQ_OK) return st;
   // the kernel addresses a 256-row tile of x with 32-bit byte offsets
-  if (K > kMaxQmmK || ((M + 255) / 256) * ((N + 223) / 224) > 0x7FFFFFFF)
-    return AQ_ERR_UNSUPPORTED;
+  if (K > kMaxQmmK || M > kMaxQmmM || (N + 255) / 256 > 0x7FFFFFFF) return AQ_ERR_UNSUPPORTED;
   return from_hip(aq::launch_qmm(x, (int)x_dtype, M, codes, scales, biases, N, K, group_size,
                                  bits, y, static_cast<hipStream_t>(stream)));
 }

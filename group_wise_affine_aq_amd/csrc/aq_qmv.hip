@@ -194,12 +194,8 @@ struct QmvCore {
       gchar *rc = uniform_ptr(wt.codes + n * ((int64_t)nch * BITS));
       const int64_t so = n * (int64_t)(nch >> gshift);
       load_chunk_g<BITS>(rc, coff, d.w[r]);
-#ifndef NO_SB
       d.s[r] = gload<uint16_t>(uniform_ptr(wt.scales + so), goff);
       d.b[r] = gload<uint16_t>(uniform_ptr(wt.biases + so), goff);
-#else
-      (void)so; (void)goff;
-#endif
     }
   }
 
@@ -754,26 +750,13 @@ hipError_t allow_lds(KernelT kernel, size_t bytes) {
 }
 
 constexpr int kRows = 2;  // rows per wave, sliced kernel and gather
-#ifndef AQ_STREAM_WAVES
-#define AQ_STREAM_WAVES 16
-#endif
-constexpr int kStreamWaves = AQ_STREAM_WAVES;  // one 16-wave workgroup per CU shares one x copy
+constexpr int kStreamWaves = 16;  // one 16-wave workgroup per CU shares one x copy
 constexpr int kStreamLdsMax = 96 * 1024;
 
 
-#ifndef AQ_STREAM_M1_DEPTH
-#define AQ_STREAM_M1_DEPTH 4
-#endif
-#ifndef AQ_STREAM_CTAS_PER_CU
-#define AQ_STREAM_CTAS_PER_CU 1
-#endif
+constexpr int kStreamCtasPerCu = 1;
 template <int MB> struct stream_shape;
-#ifndef AQ_STREAM_M1_ROWS
-#define AQ_STREAM_M1_ROWS 1
-#endif
-template <> struct stream_shape<1> {
-  static constexpr int R = AQ_STREAM_M1_ROWS, D = AQ_STREAM_M1_DEPTH;
-};
+template <> struct stream_shape<1> { static constexpr int R = 1, D = 4; };
 template <> struct stream_shape<2> { static constexpr int R = 2, D = 4; };
 template <> struct stream_shape<4> { static constexpr int R = 4, D = 2; };
 template <> struct stream_shape<8> { static constexpr int R = 4, D = 2; };
@@ -853,7 +836,7 @@ hipError_t qmv_launch(const void *x, int M, const Weights &wt, int64_t N, int64_
     if (e != hipSuccess) return e;
     const int64_t units = (N + R - 1) / R;
     const int64_t want = (units + W - 1) / W;
-    const int64_t cap = (int64_t)device_cus() * AQ_STREAM_CTAS_PER_CU;
+    const int64_t cap = (int64_t)device_cus() * kStreamCtasPerCu;
     const dim3 grid((unsigned)(want < cap ? want : cap));
     hipLaunchKernelGGL(kern, grid, dim3(64 * W), stream_lds, s, (const uint16_t *)x, M, wt, N,
                        K, G, (uint16_t *)y, (int)need);

@@ -71,8 +71,11 @@ const char *aq_status_string(aq_status status);
 /* Library version string. */
 const char *aq_version(void);
 
-/* uint32 words per packed row: K*bits/32.  -1 if K*bits is not a multiple
- * of 32 or an argument is out of range. */
+/* uint32 words per packed row: K*bits/32 (one least-significant-bit-first
+ * bitstream per row, several codes to a 32-bit word: "Quantizing a Model for
+ * MLX", "What MLX quantization stores"; "Tutorial 10: Quantization", s.3 and
+ * s.4, packed weight shape [out, in*bits/32]).  -1 if K*bits is not a
+ * multiple of 32 or an argument is out of range. */
 int64_t aq_codes_words(int64_t K, int bits);
 
 /* Bytes of one quantized matrix: N*K*bits/8 codes + 2 bytes of scale and
@@ -163,7 +166,8 @@ int aq_qmv_describe(int64_t M, int64_t N, int64_t K, int group_size, int bits, a
  * tiles are dequantized to x_dtype (rounded to nearest even, the value
  * aq_dequantize returns for that type) and multiplied on the matrix cores
  * with binary32 accumulation.  AQ_ERR_UNSUPPORTED for K > 4194303 (a
- * 256-row tile of x is addressed with 32-bit byte offsets). */
+ * 256-row tile of x is addressed with 32-bit byte offsets) or M > 8388352
+ * (the launch grid holds at most 65535 row tiles of 128). */
 aq_status aq_qmm(const void *x, aq_dtype x_dtype, int64_t M, const uint32_t *codes,
                  const uint16_t *scales, const uint16_t *biases, int64_t N, int64_t K,
                  int group_size, int bits, void *y, void *stream);
@@ -185,9 +189,12 @@ aq_status aq_quantized_matmul(const void *x, aq_dtype x_dtype, int64_t M, const 
  *   y[t, j, :] = x[t, :] @ W_e^T   with e = ids[t, j].
  * x: device [T, K] (AQ_F16 or AQ_BF16); codes: device [E, N, K*bits/32];
  * scales, biases: device [E, N, K/G]; ids: device int32 [T, topk];
- * y: device [T, topk, N] in x_dtype.  No routing weights are applied.  Each
- * expert's weights are read once per call however many tokens chose it.
- * An id outside [0, E) is not read from; its output row is set to zero. */
+ * y: device [T, topk, N] in x_dtype.  No routing weights are applied.  The
+ * routing is resolved on the device: each expert's weights are read once
+ * for every batch of up to 16 (token, slot) pairs routed to it (8 on the
+ * vector path for 2-, 3-, 5-, 6- and 7-bit codes), and experts no token
+ * chose are never read.  An id outside [0, E) is not read from; its output
+ * row is set to zero. */
 aq_status aq_gather_qmv(const void *x, aq_dtype x_dtype, int64_t T, const uint32_t *codes,
                         const uint16_t *scales, const uint16_t *biases, int64_t E, int64_t N,
                         int64_t K, const int32_t *ids, int topk, int group_size, int bits,

@@ -141,6 +141,12 @@ def test_qmm_depth_limit(lib):
     assert qmv(lib, "aq_quantized_matmul", M=16, K=4194304) == UNSUPPORTED
 
 
+def test_qmm_row_limit(lib):
+    """The prefill grid holds at most 65535 row tiles of 128 rows."""
+    assert qmv(lib, "aq_qmm", M=8388353) == UNSUPPORTED
+    assert qmv(lib, "aq_quantized_matmul", M=8388353) == UNSUPPORTED
+
+
 def test_quantize_dequantize_argument_errors(lib):
     q = lambda **k: lib.aq_quantize(k.get("w", P), k.get("dt", F32), k.get("N", 4), k.get("K", 64),
                                     k.get("G", 64), k.get("bits", 4), k.get("codes", P),
