@@ -65,6 +65,7 @@ def _load():
             "oracle_unpack": ([vp, i64, i64, i32, vp], i32),
             "oracle_quantize": ([vp, i64, i64, i32, i32, vp, vp, vp], i32),
             "oracle_quantize_mse": ([vp, i64, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp], i32),
+            "oracle_quantize_zp": ([vp, i64, i64, i32, i32, vp, vp, vp, vp], i32),
             "oracle_dequantize_exact": ([vp, vp, vp, i64, i64, i32, i32, vp], i32),
             "oracle_dequantize": ([vp, vp, vp, i64, i64, i32, i32, i32, vp], i32),
             "oracle_embedding": ([vp, vp, vp, i64, i64, i32, i32, vp, i64, i32, vp], i32),
@@ -178,6 +179,27 @@ def quantize_mse(w: np.ndarray, group_size: int, bits: int, steps: int, only: in
     if details:
         return codes, scales, biases, chosen, errs
     return codes, scales, biases
+
+
+def quantize_zp(w: np.ndarray, group_size: int, bits: int):
+    """Integer-zero-point quantizer (reading R15): the smallest fp16 scale s
+    admitting an integer zero point z in [0, 2^bits - 1] whose grid -z*s + q*s
+    spans the group with -z*s an exact fp16 value; bias = -z*s.
+    -> (codes, scales, biases, zeros uint8 [N, K/G])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    if K % group_size:
+        raise OracleError(ERR_ARG, "quantize_zp")
+    ng = K // group_size
+    codes = np.zeros((N, K * bits // 32), dtype=np.uint32)
+    scales = np.zeros((N, ng), dtype=np.uint16)
+    biases = np.zeros((N, ng), dtype=np.uint16)
+    zeros = np.zeros((N, ng), dtype=np.uint8)
+    st = _load().oracle_quantize_zp(_p(w), N, K, group_size, bits, _p(codes), _p(scales),
+                                    _p(biases), _p(zeros))
+    if st:
+        raise OracleError(st, "quantize_zp")
+    return codes, scales, biases, zeros
 
 
 def dequantize_exact(codes, scales, biases, K: int, group_size: int, bits: int) -> np.ndarray:

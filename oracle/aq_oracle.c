@@ -68,6 +68,18 @@
  *      order, of (w - (q*s + b))^2 in binary64.  The least error wins; an
  *      equal error keeps the earlier (wider) candidate.  steps = 1 is
  *      R1/R2.
+ *  R15 integer zero point ([GPTQ] "On NVIDIA: the same recipe in AWQ
+ *      format", --zero-point int: every group's offset is a whole number of
+ *      steps, so the grid converts to a layout with integer zero points
+ *      without loss).  The zero point z is an integer in [0, 2^b-1] (it is
+ *      stored as a b-bit unsigned integer in such a layout), so every grid
+ *      -z*s + q*s, q = 0..2^b-1, contains 0.  Taken here: the scale is the
+ *      smallest fp16 s >= 0 for which some integer z in [0, 2^b-1] gives
+ *      -z*s <= min, (2^b-1-z)*s >= max and -z*s exactly an fp16 value;
+ *      z is the smallest such integer for that s; bias = -z*s (exact, +0
+ *      when z = 0); codes by R2 against that bias and scale.  Hence every
+ *      member lies on the grid's span and |w - w^| <= s/2, and w^ =
+ *      (q - z)*s exactly.
  *
  * Exactness of the binary64 comparisons used below.  Every finite fp16
  * value is an integer multiple of 2^-24 of magnitude < 2^16; q*s with
@@ -411,6 +423,75 @@ int oracle_quantize_mse(const float *w, int64_t N, int64_t K, int G, int bits, i
       scales[n * ng + g] = best_s;
       biases[n * ng + g] = best_b;
       if (chosen) chosen[n * ng + g] = best_i;
+      for (int i = 0; i < G; ++i)
+        put_code(row, g * G + i, bits, group_code((double)grp[i], b, s, L));
+    }
+  }
+  return err;
+}
+
+/* Integer zero point (R15).  For one group with members in [lo, hi]:
+ * the smallest fp16 scale s admitting an integer z in [0, L] with
+ * -z*s <= lo, (L - z)*s >= hi and -z*s exactly an fp16 value, and the
+ * smallest such z.  Scales are tried in increasing order from the smallest
+ * one whose L steps span [min(lo, 0), max(hi, 0)] (no smaller scale can
+ * cover a grid that contains 0); for each, every z in [0, L] is checked with
+ * exact binary64 comparisons (z*s has at most 19 significant bits).
+ * Returns OR_ERR_RANGE when no fp16 scale admits one. */
+static int group_zero_point(double lo, double hi, int L, uint16_t *s_out, int *z_out) {
+  const double lo0 = lo < 0.0 ? lo : 0.0, hi0 = hi > 0.0 ? hi : 0.0;
+  uint16_t s0 = 0;
+  if (group_scale(lo0, hi0, L, &s0) != OR_OK) return OR_ERR_RANGE;
+  for (uint32_t p = s0; p <= HALF_MAX_FINITE_MAG; ++p) {
+    const double sv = oracle_half_to_double((uint16_t)p);
+    for (int z = 0; z <= L; ++z) {
+      const double bottom = -(double)z * sv, top = (double)(L - z) * sv;
+      if (bottom > lo || top < hi) continue;
+      if (oracle_half_to_double(oracle_double_to_half_rne(bottom)) != bottom) continue;
+      *s_out = (uint16_t)p;
+      *z_out = z;
+      return OR_OK;
+    }
+  }
+  return OR_ERR_RANGE;
+}
+
+/* Quantize with integer zero points (R15): same outputs as oracle_quantize
+ * plus zeros [N, K/G] (the integer z of each group; may be NULL). */
+int oracle_quantize_zp(const float *w, int64_t N, int64_t K, int G, int bits, uint32_t *codes,
+                       uint16_t *scales, uint16_t *biases, uint8_t *zeros) {
+  int st = check_shape(N, K, G, bits);
+  if (st) return st;
+  const int L = (1 << bits) - 1;
+  const int64_t wpr = K * bits / 32, ng = K / G;
+  int err = OR_OK;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    uint32_t *row = codes + n * wpr;
+    memset(row, 0, (size_t)wpr * sizeof(uint32_t));
+    for (int64_t g = 0; g < ng; ++g) {
+      const float *grp = w + n * K + g * G;
+      double lo = INFINITY, hi = -INFINITY;
+      int bad = 0;
+      for (int i = 0; i < G; ++i) {
+        double v = (double)grp[i];
+        if (!isfinite(v)) bad = 1;
+        if (v < lo) lo = v;
+        if (v > hi) hi = v;
+      }
+      uint16_t s16 = 0;
+      int z = 0;
+      if (bad || group_zero_point(lo, hi, L, &s16, &z) != OR_OK) {
+#pragma omp critical
+        err = OR_ERR_RANGE;
+        continue;
+      }
+      const double s = oracle_half_to_double(s16);
+      const double b = -(double)z * s;
+      const uint16_t b16 = z == 0 ? (uint16_t)0 : oracle_double_to_half_rne(b);
+      scales[n * ng + g] = s16;
+      biases[n * ng + g] = b16;
+      if (zeros) zeros[n * ng + g] = (uint8_t)z;
       for (int i = 0; i < G; ++i)
         put_code(row, g * G + i, bits, group_code((double)grp[i], b, s, L));
     }
