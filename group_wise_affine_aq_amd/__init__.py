@@ -9,7 +9,8 @@ library has not been built, or a call fails, an exception is raised.
 
 Packed weights use the layout of the pages' container ("Tutorial 10:
 Quantization", s.4): codes uint32 [N, K*bits/32] (stored in torch as int32),
-scales and biases fp16 [N, K/group_size].
+scales and biases fp16 [N, K/group_size].  Consumers accept biases=None
+(every bias +0).
 """
 from __future__ import annotations
 
@@ -18,7 +19,8 @@ import os
 
 __all__ = [
     "AQError", "lib_path", "load_library", "aq_status_string", "aq_version", "aq_codes_words",
-    "aq_qweight_bytes", "aq_quantize", "aq_quantize_mse", "aq_dequantize", "aq_qmv", "aq_qmm",
+    "aq_qweight_bytes", "aq_quantize", "aq_quantize_mse", "aq_quantize_zp", "aq_dequantize",
+    "aq_embedding", "aq_qmv", "aq_qmm",
     "aq_quantized_matmul", "aq_gather_qmv", "aq_gather_qmm", "aq_gather_quantized_matmul",
 ]
 
@@ -60,6 +62,7 @@ def load_library():
         "aq_qweight_bytes": ([i64, i64, i32, i32], i64),
         "aq_quantize": ([vp, i32, i64, i64, i32, i32, vp, vp, vp, vp], i32),
         "aq_quantize_mse": ([vp, i32, i64, i64, i32, i32, i32, vp, vp, vp, vp], i32),
+        "aq_quantize_zp": ([vp, i32, i64, i64, i32, i32, vp, vp, vp, vp, vp], i32),
         "aq_qmv_describe": ([i64, i64, i64, i32, i32, i32, ctypes.c_char_p, i32], i32),
         "aq_dequantize": ([vp, vp, vp, i64, i64, i32, i32, vp, i32, vp], i32),
         "aq_embedding": ([vp, vp, vp, i64, i64, i32, i32, vp, i64, vp, i32, vp], i32),
@@ -187,6 +190,28 @@ def aq_quantize_mse(w, group_size: int, bits: int, steps: int, codes=None, scale
                              _stream(stream))
     _check(st, "aq_quantize_mse")
     return codes, scales, biases
+
+
+def aq_quantize_zp(w, group_size: int, bits: int, codes=None, scales=None, biases=None,
+                   zeros=None, stream=None):
+    """Integer-zero-point quantize W [N, K] -> (codes, scales, biases, zeros),
+    zeros uint8 [N, K/group_size] with bias = -zero * scale exactly."""
+    torch = _torch()
+    lib = load_library()
+    N, K = w.shape
+    if codes is None:
+        codes = torch.empty((N, K * bits // 32), dtype=torch.int32, device=w.device)
+    if scales is None:
+        scales = torch.empty((N, K // group_size), dtype=torch.float16, device=w.device)
+    if biases is None:
+        biases = torch.empty((N, K // group_size), dtype=torch.float16, device=w.device)
+    if zeros is None:
+        zeros = torch.empty((N, K // group_size), dtype=torch.uint8, device=w.device)
+    st = lib.aq_quantize_zp(_dev(w, "w"), _dtype_code(w), N, K, group_size, bits,
+                            _dev(codes, "codes"), _dev(scales, "scales"), _dev(biases, "biases"),
+                            _dev(zeros, "zeros"), _stream(stream))
+    _check(st, "aq_quantize_zp")
+    return codes, scales, biases, zeros
 
 
 def aq_dequantize(codes, scales, biases, group_size: int, bits: int, out_dtype=None, out=None,

@@ -34,9 +34,18 @@ bool valid_act_dtype(int d) { return d == AQ_F16 || d == AQ_BF16; }
 
 aq_status from_hip(hipError_t e) { return e == hipSuccess ? AQ_OK : AQ_ERR_HIP; }
 
+// outputs of the quantizers: all three arrays required
 aq_status check_weights(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases) {
   if (!codes || !scales || !biases) return AQ_ERR_INVALID_ARG;
   if (!aligned16(codes) || !aligned16(scales) || !aligned16(biases)) return AQ_ERR_ALIGNMENT;
+  return AQ_OK;
+}
+
+// inputs of the consumers: a null bias array means every bias is +0
+aq_status check_packed(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases) {
+  if (!codes || !scales) return AQ_ERR_INVALID_ARG;
+  if (!aligned16(codes) || !aligned16(scales) || (biases && !aligned16(biases)))
+    return AQ_ERR_ALIGNMENT;
   return AQ_OK;
 }
 
@@ -46,7 +55,7 @@ aq_status check_matmul(const void *x, int x_dtype, int64_t M, const uint32_t *co
   if (!valid_format(N, K, G, bits) || M < 1 || !valid_act_dtype(x_dtype))
     return AQ_ERR_INVALID_ARG;
   if (!x || !y) return AQ_ERR_INVALID_ARG;
-  aq_status st = check_weights(codes, scales, biases);
+  aq_status st = check_packed(codes, scales, biases);
   if (st != AQ_OK) return st;
   if (!aligned16(x) || !aligned16(y)) return AQ_ERR_ALIGNMENT;
   return AQ_OK;
@@ -129,13 +138,27 @@ aq_status aq_quantize_mse(const void *w, aq_dtype w_dtype, int64_t N, int64_t K,
                                           scales, biases, static_cast<hipStream_t>(stream)));
 }
 
+aq_status aq_quantize_zp(const void *w, aq_dtype w_dtype, int64_t N, int64_t K, int group_size,
+                         int bits, uint32_t *codes, uint16_t *scales, uint16_t *biases,
+                         uint8_t *zeros, void *stream) {
+  if (!valid_format(N, K, group_size, bits)) return AQ_ERR_INVALID_ARG;
+  if (w_dtype != AQ_F32 && w_dtype != AQ_F16 && w_dtype != AQ_BF16) return AQ_ERR_INVALID_ARG;
+  if (!w) return AQ_ERR_INVALID_ARG;
+  aq_status st = check_weights(codes, scales, biases);
+  if (st != AQ_OK) return st;
+  if (!aligned16(w) || (zeros && !aligned16(zeros))) return AQ_ERR_ALIGNMENT;
+  if (N * (K / 8) > (int64_t)0x7FFFFFFF * 256) return AQ_ERR_UNSUPPORTED;
+  return from_hip(aq::launch_quantize_zp(w, (int)w_dtype, N, K, group_size, bits, codes, scales,
+                                         biases, zeros, static_cast<hipStream_t>(stream)));
+}
+
 aq_status aq_dequantize(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
                         int64_t N, int64_t K, int group_size, int bits, void *out,
                         aq_dtype out_dtype, void *stream) {
   if (!valid_format(N, K, group_size, bits)) return AQ_ERR_INVALID_ARG;
   if (out_dtype != AQ_F32 && out_dtype != AQ_F16 && out_dtype != AQ_BF16) return AQ_ERR_INVALID_ARG;
   if (!out) return AQ_ERR_INVALID_ARG;
-  aq_status st = check_weights(codes, scales, biases);
+  aq_status st = check_packed(codes, scales, biases);
   if (st != AQ_OK) return st;
   if (!aligned16(out)) return AQ_ERR_ALIGNMENT;
   if (N * (K / 32) > (int64_t)0x7FFFFFFF * 256) return AQ_ERR_UNSUPPORTED;
@@ -149,7 +172,7 @@ aq_status aq_embedding(const uint32_t *codes, const uint16_t *scales, const uint
   if (!valid_format(V, K, group_size, bits) || T < 1) return AQ_ERR_INVALID_ARG;
   if (out_dtype != AQ_F32 && out_dtype != AQ_F16 && out_dtype != AQ_BF16) return AQ_ERR_INVALID_ARG;
   if (!out || !ids) return AQ_ERR_INVALID_ARG;
-  aq_status st = check_weights(codes, scales, biases);
+  aq_status st = check_packed(codes, scales, biases);
   if (st != AQ_OK) return st;
   if (!aligned16(out) || !aligned16(ids)) return AQ_ERR_ALIGNMENT;
   if (T * (K / 32) > (int64_t)0x7FFFFFFF * 256) return AQ_ERR_UNSUPPORTED;
@@ -229,7 +252,7 @@ static aq_status check_gather(const void *x, aq_dtype x_dtype, int64_t T, const 
       !valid_act_dtype(x_dtype))
     return AQ_ERR_INVALID_ARG;
   if (!x || !y || !ids) return AQ_ERR_INVALID_ARG;
-  aq_status st = check_weights(codes, scales, biases);
+  aq_status st = check_packed(codes, scales, biases);
   if (st != AQ_OK) return st;
   if (!aligned16(x) || !aligned16(y) || !aligned16(ids)) return AQ_ERR_ALIGNMENT;
   if (E > 65535 || T * topk > 0x7FFFFFFF) return AQ_ERR_UNSUPPORTED;

@@ -20,6 +20,11 @@ hipError_t launch_quantize_mse(const void *w, int w_dtype, int64_t N, int64_t K,
                                int steps, uint32_t *codes, uint16_t *scales, uint16_t *biases,
                                hipStream_t s);
 
+// integer zero points: bias = -z*s exactly, z in [0, 2^bits - 1]; zeros may be null
+hipError_t launch_quantize_zp(const void *w, int w_dtype, int64_t N, int64_t K, int G, int bits,
+                              uint32_t *codes, uint16_t *scales, uint16_t *biases, uint8_t *zeros,
+                              hipStream_t s);
+
 hipError_t launch_dequantize(const uint32_t *codes, const uint16_t *scales,
                              const uint16_t *biases, int64_t N, int64_t K, int G, int bits,
                              void *out, int out_dtype, hipStream_t s);

@@ -280,7 +280,7 @@ __global__ __launch_bounds__(kThreads) void qmm_wr_kernel(const uint16_t *__rest
     expert = blockIdx.y;
     codes += (int64_t)expert * N * wpr;
     scales += (int64_t)expert * N * gpr;
-    biases += (int64_t)expert * N * gpr;
+    if (biases) biases += (int64_t)expert * N * gpr;
   } else {
     tile_m = (int64_t)blockIdx.y * TBM;
   }
@@ -293,7 +293,9 @@ __global__ __launch_bounds__(kThreads) void qmm_wr_kernel(const uint16_t *__rest
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + tile_m * K, xbytes);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(codes + tile_n * wpr, nrows * wpr * 4);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(scales + tile_n * gpr, nrows * gpr * 2);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(biases + tile_n * gpr, nrows * gpr * 2);
+  // without a bias array (null) a resource of size 0: its loads return +0
+  const __amdgpu_buffer_rsrc_t rb = biases ? make_rsrc(biases + tile_n * gpr, nrows * gpr * 2)
+                                           : make_rsrc(scales, 0);
 
   // K steps: when K % 64 == 32 the lone last chunk is step 0 (its upper half
   // reads zeros), so every later step is full
@@ -629,7 +631,8 @@ hipError_t qmm_wr_launch(const void *x, int64_t M, const uint32_t *codes, const 
       hipLaunchKernelGGL((qmm_wr_kernel<BITS, XT, 4, G1, false>),
                          dim3((unsigned)ntail, (unsigned)(2 * mt)), dim3(kThreads), 0, s,
                          (const uint16_t *)x, M, codes + n0 * wpr, scales + n0 * gpr,
-                         biases + n0 * gpr, N - n0, K, G, yo + n0, N, Routing{});
+                         biases ? biases + n0 * gpr : nullptr, N - n0, K, G, yo + n0, N,
+                         Routing{});
   };
   using F8 = std::integral_constant<int, 8>;
   using F4 = std::integral_constant<int, 4>;

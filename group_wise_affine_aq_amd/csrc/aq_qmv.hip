@@ -165,8 +165,24 @@ struct PassData {
 struct Weights {
   const uint32_t *codes;
   const uint16_t *scales;
-  const uint16_t *biases;
+  const uint16_t *biases;  // null: every bias is +0
 };
+
+// The fp16 bias at byte offset goff of a row's biases, read through a buffer
+// resource whose base is uniform (scalar registers).  Without a bias array
+// the resource has size 0, so the load returns 0 (+0.0) without touching
+// memory and the kernels need no second code path.
+__device__ __forceinline__ uint32_t load_bias(const Weights &wt, int64_t so, int64_t ng,
+                                              uint32_t goff) {
+  const uint16_t *base = wt.biases ? wt.biases + so : wt.scales;
+  const int bytes = wt.biases ? (int)(ng * 2) : 0;
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<void *>(((uint64_t)hi << 32) | lo), 0, bytes, 0x00020000);
+  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)goff, 0, 0);
+}
 
 template <int BITS, int MB, typename XT, int R>
 struct QmvCore {
@@ -195,7 +211,7 @@ struct QmvCore {
       const int64_t so = n * (int64_t)(nch >> gshift);
       load_chunk_g<BITS>(rc, coff, d.w[r]);
       d.s[r] = gload<uint16_t>(uniform_ptr(wt.scales + so), goff);
-      d.b[r] = gload<uint16_t>(uniform_ptr(wt.biases + so), goff);
+      d.b[r] = load_bias(wt, so, nch >> gshift, goff);
     }
   }
 
@@ -694,7 +710,8 @@ __global__ __launch_bounds__(kThreads) void gather_qmv_kernel(
   const int e = blockIdx.y;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t wpe = N * ((K >> 5) * BITS), spe = N * (K / G);
-  const Weights we{wt.codes + e * wpe, wt.scales + e * spe, wt.biases + e * spe};
+  const Weights we{wt.codes + e * wpe, wt.scales + e * spe,
+                   wt.biases ? wt.biases + e * spe : nullptr};
   const int64_t total = T * topk;
 
   for (int64_t t0 = 0; t0 < total; t0 += kGatherTile) {

@@ -127,6 +127,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t mk_rsrc(const void *base, int6
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, 0x00020000);
 }
 
+// biases of a range of rows; without a bias array (null) a resource of size 0,
+// whose loads return 0 (+0.0) without touching memory
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bias_rsrc(const uint16_t *scales_rows,
+                                                          const uint16_t *biases_rows,
+                                                          int64_t bytes) {
+  return biases_rows ? mk_rsrc(biases_rows, bytes) : mk_rsrc(scales_rows, 0);
+}
+
 __device__ __forceinline__ uint32_t opaque(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xE4, 0xF, 0xF, false);
 }
@@ -299,7 +307,7 @@ struct MBlock {
   static __device__ void stage_sb(const uint16_t *scales_rows, const uint16_t *biases_rows,
                                   int64_t nrows, int64_t gpr_, uint16_t *sb, int wave, int lane) {
     const __amdgpu_buffer_rsrc_t rs = mk_rsrc(scales_rows, nrows * gpr_ * 2);
-    const __amdgpu_buffer_rsrc_t rb = mk_rsrc(biases_rows, nrows * gpr_ * 2);
+    const __amdgpu_buffer_rsrc_t rb = bias_rsrc(scales_rows, biases_rows, nrows * gpr_ * 2);
     const int pad = sb_entries(ROWS, gpr_);
     for (int blk = wave; blk < (pad >> 9); blk += W) {
       const int off = (blk * 64 + lane) * 16;
@@ -320,7 +328,7 @@ struct MBlock {
     const int valid = (int)(nrows * gpr_);
     if (valid & 7) {  // uniform: only a workgroup with a partial block of rows
       const __amdgpu_buffer_rsrc_t rs = mk_rsrc(scales_rows, nrows * gpr_ * 2);
-      const __amdgpu_buffer_rsrc_t rb = mk_rsrc(biases_rows, nrows * gpr_ * 2);
+      const __amdgpu_buffer_rsrc_t rb = bias_rsrc(scales_rows, biases_rows, nrows * gpr_ * 2);
       const int pad = sb_entries(ROWS, gpr_);
       const int e = (valid & ~7) + (int)threadIdx.x;
       if (threadIdx.x < 8 && e < valid) {
@@ -552,10 +560,10 @@ __global__ __launch_bounds__(64 * W) void qmvm_kernel(const uint16_t *__restrict
   constexpr int D = kDepth<BITS>;
   typename Blk::Step st[D];
   // staging first, then the first steps' loads: one round trip covers both
-  Blk::stage_sb(scales + row0 * gpr, biases + row0 * gpr, nrows, gpr, lds, wave, lane);
+  Blk::stage_sb(scales + row0 * gpr, biases ? biases + row0 * gpr : nullptr, nrows, gpr, lds, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
   blk.template prologue<D>(xro, st);
-  Blk::template stage_sb_wait<D * Blk::kStepLoads>(scales + row0 * gpr, biases + row0 * gpr,
+  Blk::template stage_sb_wait<D * Blk::kStepLoads>(scales + row0 * gpr, biases ? biases + row0 * gpr : nullptr,
                                                    nrows, gpr, lds);
   __syncthreads();
   f32x4v acc[Blk::XS][R];
@@ -622,9 +630,9 @@ __global__ __launch_bounds__(64 * W) void gather_qmvm_kernel(
   const __amdgpu_buffer_rsrc_t rx = mk_rsrc(x, T * K * 2);
   Blk blk;
   blk.setup(wrows, nrows, K, kw, wave, lane, sbl, rx);
-  Blk::stage_sb(scales + (e * N + row0) * gpr, biases + (e * N + row0) * gpr, nrows, gpr, sbl,
+  Blk::stage_sb(scales + (e * N + row0) * gpr, biases ? biases + (e * N + row0) * gpr : nullptr, nrows, gpr, sbl,
                 wave, lane);
-  Blk::template stage_sb_wait<0>(scales + (e * N + row0) * gpr, biases + (e * N + row0) * gpr,
+  Blk::template stage_sb_wait<0>(scales + (e * N + row0) * gpr, biases ? biases + (e * N + row0) * gpr : nullptr,
                                  nrows, gpr, sbl);
   constexpr int D = kDepth<BITS>;
   for (int64_t t0 = 0; t0 < total; t0 += kGTile) {

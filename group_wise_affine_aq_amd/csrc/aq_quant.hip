@@ -21,6 +21,15 @@
 // by the rules above and the least binary64 sum of squared errors wins, an
 // equal one keeping the wider candidate.
 //
+// Integer zero point ("mlx-gptq", "On NVIDIA: the same recipe in AWQ format",
+// --zero-point int: every group's offset is a whole number of steps, for a
+// lossless conversion to a layout that stores integer zero points): the zero
+// point z is an integer in [0, 2^bits - 1], so every grid -z*s + q*s holds 0;
+// s is the smallest fp16 for which some such z has -z*s <= min,
+// (2^bits - 1 - z)*s >= max and -z*s exactly an fp16 value, z the smallest
+// one for that s, bias = -z*s, codes as above.  Every test is exact: z*s has
+// at most 19 significant bits.
+//
 // Dequantize ("Tutorial 10: Quantization", s.3/s.7): q*s + b in binary32
 // (one rounding, the product is exact), then round-to-nearest-even to the
 // output type.
@@ -267,6 +276,90 @@ __global__ __launch_bounds__(256) void quantize_mse_kernel(const void *__restric
   for (int j = 0; j < BITS; ++j) dst[j] = (uint8_t)(best_packed >> (8 * j));
 }
 
+// smallest integer u in [0, cap + 1] with u*s >= t (t >= 0, s > 0 an fp16
+// value): the binary64 quotient proposes it, exact products correct it
+__device__ __forceinline__ int ceil_steps(double t, double s, int cap) {
+  const double qd = t / s;
+  if (!(qd <= (double)cap)) return cap + 1;
+  int u = (int)__builtin_ceil(qd);
+  while (u > 0 && (double)(u - 1) * s >= t) --u;
+  while (u <= cap && (double)u * s < t) ++u;
+  return u;
+}
+
+// The zero-point search for one group with members in [lo, hi]: scale
+// pattern and zero point.  Scales start at the smallest one whose L steps
+// span [min(lo, 0), max(hi, 0)] (a grid holding 0 cannot be narrower).
+__device__ __forceinline__ uint16_t zero_point_scale(float lo, float hi, int L, int &z) {
+  const double lo0 = lo < 0.f ? (double)lo : 0.0, hi0 = hi > 0.f ? (double)hi : 0.0;
+  z = 0;
+  for (uint16_t p = f16_scale_up(lo0, hi0, L); p <= 0x7BFFu; ++p) {
+    const double sv = h2d(p);
+    if (sv == 0.0) return p;  // only an all-zero group: z = 0, s = 0
+    const int zmin = ceil_steps(-lo0, sv, L);
+    const int zmax = L - ceil_steps(hi0, sv, L);
+    for (int zz = zmin; zz <= zmax; ++zz) {
+      const float bottom = (float)zz * (float)sv;  // exact in binary32
+      if (f16_to_f32(f32_to_f16_rne(bottom)) == bottom) {
+        z = zz;
+        return p;
+      }
+    }
+  }
+  return 0x7BFFu;  // outside the documented precondition
+}
+
+// Integer-zero-point quantize: the thread mapping of quantize_kernel; every
+// lane of a group runs the same search.
+template <int WDT, int BITS>
+__global__ __launch_bounds__(256) void quantize_zp_kernel(const void *__restrict__ w, int64_t N,
+                                                          int64_t K, int G,
+                                                          uint32_t *__restrict__ codes,
+                                                          uint16_t *__restrict__ scales,
+                                                          uint16_t *__restrict__ biases,
+                                                          uint8_t *__restrict__ zeros) {
+  const int64_t opr = K >> 3;
+  const int64_t total = N * opr;
+  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool active = idx < total;
+  if (!active) idx = total - 1;
+  const int64_t n = idx / opr, o = idx - n * opr;
+
+  float v[8];
+  load8<WDT>(w, n * K + o * 8, v);
+  float lo = v[0], hi = v[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) { lo = fminf(lo, v[i]); hi = fmaxf(hi, v[i]); }
+  const int lanes = G >> 3;
+  for (int d = 1; d < lanes; d <<= 1) {
+    lo = fminf(lo, __shfl_xor(lo, d));
+    hi = fmaxf(hi, __shfl_xor(hi, d));
+  }
+  constexpr int L = (1 << BITS) - 1;
+  int z = 0;
+  const uint16_t s16 = zero_point_scale(lo, hi, L, z);
+  const double s = h2d(s16);
+  const uint16_t b16 = z == 0 ? (uint16_t)0 : f32_to_f16_rne(-((float)z * (float)s));
+  const double b = h2d(b16);
+  const float bf = (float)b;
+  const float rs = s16 ? __builtin_amdgcn_rcpf((float)s) : 0.f;
+  uint64_t packed = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    packed |= (uint64_t)nearest_code(v[i], b, s, bf, rs, L) << (BITS * i);
+
+  if (!active) return;
+  if ((o & (lanes - 1)) == 0) {
+    const int64_t gi = n * (K / G) + (o * 8) / G;
+    scales[gi] = s16;
+    biases[gi] = b16;
+    if (zeros) zeros[gi] = (uint8_t)z;
+  }
+  uint8_t *dst = reinterpret_cast<uint8_t *>(codes + n * (K * BITS / 32)) + o * BITS;
+#pragma unroll
+  for (int j = 0; j < BITS; ++j) dst[j] = (uint8_t)(packed >> (8 * j));
+}
+
 // two binary32 values rounded to nearest even into fp16 or bf16 and packed
 // (v_cvt_pk_bf16_f32 for bf16; the values here are finite, where it agrees
 // bit for bit with the integer rounding used elsewhere)
@@ -330,7 +423,8 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint32_t *__restr
     uint32_t wv[BITS];
     load_chunk<BITS>(codes + n * (K * BITS / 32) + c * BITS, wv);
     const int64_t gi = n * (K / G) + (c * 32) / G;
-    const float s = f16_to_f32(scales[gi]), b = f16_to_f32(biases[gi]);
+    // a null bias array means every bias is +0: q*s + 0 is q*s exactly
+    const float s = f16_to_f32(scales[gi]), b = biases ? f16_to_f32(biases[gi]) : 0.f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) r[i] = __builtin_fmaf((float)chunk_code<BITS>(wv, i), s, b);
   }
@@ -388,6 +482,20 @@ hipError_t quantize_mse_w(const void *w, int64_t N, int64_t K, int G, int bits, 
   return hipGetLastError();
 }
 
+template <int WDT>
+hipError_t quantize_zp_w(const void *w, int64_t N, int64_t K, int G, int bits, uint32_t *codes,
+                         uint16_t *scales, uint16_t *biases, uint8_t *zeros, hipStream_t s) {
+  const int64_t total = N * (K / 8);
+  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+#define AQ_Q(B) case B: hipLaunchKernelGGL((quantize_zp_kernel<WDT, B>), grid, block, 0, s, w, N, K, G, codes, scales, biases, zeros); break;
+  switch (bits) {
+    AQ_Q(2) AQ_Q(3) AQ_Q(4) AQ_Q(5) AQ_Q(6) AQ_Q(7) AQ_Q(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef AQ_Q
+  return hipGetLastError();
+}
+
 template <int ODT, bool GATHER>
 hipError_t dequantize_o(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
                         int64_t N, int64_t K, int G, int bits, const int32_t *ids, int64_t T,
@@ -434,6 +542,17 @@ hipError_t launch_quantize_mse(const void *w, int w_dtype, int64_t N, int64_t K,
     case X_F32: return quantize_mse_w<X_F32>(w, N, K, G, bits, steps, codes, scales, biases, s);
     case X_F16: return quantize_mse_w<X_F16>(w, N, K, G, bits, steps, codes, scales, biases, s);
     case X_BF16: return quantize_mse_w<X_BF16>(w, N, K, G, bits, steps, codes, scales, biases, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_quantize_zp(const void *w, int w_dtype, int64_t N, int64_t K, int G, int bits,
+                              uint32_t *codes, uint16_t *scales, uint16_t *biases, uint8_t *zeros,
+                              hipStream_t s) {
+  switch (w_dtype) {
+    case X_F32: return quantize_zp_w<X_F32>(w, N, K, G, bits, codes, scales, biases, zeros, s);
+    case X_F16: return quantize_zp_w<X_F16>(w, N, K, G, bits, codes, scales, biases, zeros, s);
+    case X_BF16: return quantize_zp_w<X_BF16>(w, N, K, G, bits, codes, scales, biases, zeros, s);
   }
   return hipErrorInvalidValue;
 }

@@ -31,6 +31,11 @@
  *  - Arguments are checked on the host before anything is enqueued; a bad
  *    argument returns an error and enqueues nothing.  Launch failures return
  *    AQ_ERR_HIP.  Nothing aborts and no exception crosses the ABI.
+ *  - Biases are optional for every consumer (dequantize, embedding and the
+ *    matmuls): a NULL biases pointer means every bias is +0, i.e. w = q*s
+ *    ("Tutorial 10: Quantization", s.4: biases "Optional ... or None").
+ *    The results are then bit for bit those of an all-zero bias array, and
+ *    no bias bytes are read.  The quantizers always write biases.
  *  - group_size in {32, 64, 128}; bits in [2, 8]; K % group_size == 0
  *    (a layer whose width is not a multiple of the group size is left
  *    unquantized: "Quantizing a Model for MLX", "What MLX quantization
@@ -121,6 +126,24 @@ aq_status aq_quantize(const void *w, aq_dtype w_dtype, int64_t N, int64_t K, int
 aq_status aq_quantize_mse(const void *w, aq_dtype w_dtype, int64_t N, int64_t K, int group_size,
                           int bits, int steps, uint32_t *codes, uint16_t *scales, uint16_t *biases,
                           void *stream);
+
+/* Quantize with integer zero points ("mlx-gptq", "On NVIDIA: the same recipe
+ * in AWQ format", --zero-point int: every group's offset is a whole number of
+ * steps, so the result converts without loss to a layout that stores an
+ * integer zero point z per group and decodes (q - z)*s).  Same arguments,
+ * outputs, format and preconditions as aq_quantize, plus zeros: device uint8
+ * [N, K/G] receiving each group's z, or NULL.  Per group:
+ *   z is an integer in [0, 2^bits - 1], so the grid -z*s + q*s contains 0;
+ *   s = the smallest fp16 >= 0 for which some such z has -z*s <= the group
+ *       minimum, (2^bits-1-z)*s >= the group maximum and -z*s exactly an
+ *       fp16 value; z = the smallest such integer for that s;
+ *   b = -z*s (exact; +0 when z = 0), q as in aq_quantize;
+ * hence q*s + b = (q - z)*s exactly and |w - (q*s + b)| <= s/2.  The output
+ * is an ordinary (codes, scales, biases) container: every consumer below
+ * takes it unchanged. */
+aq_status aq_quantize_zp(const void *w, aq_dtype w_dtype, int64_t N, int64_t K, int group_size,
+                         int bits, uint32_t *codes, uint16_t *scales, uint16_t *biases,
+                         uint8_t *zeros, void *stream);
 
 /* Dequantize ("Tutorial 10: Quantization", s.3 and s.7): out[n, k] =
  * q*s + b evaluated in binary32 (q*s is exact, the add rounds to nearest

@@ -95,7 +95,7 @@ def _matmul_argument_errors(lib, fn, M):
     assert call(y=None) == INVALID
     assert call(codes=None) == INVALID
     assert call(scales=None) == INVALID
-    assert call(biases=None) == INVALID
+    # biases=None is valid (every bias +0): test_consumers_take_null_biases
     assert call(x=MIS) == ALIGN
     assert call(y=MIS) == ALIGN
     assert call(codes=MIS) == ALIGN
@@ -192,6 +192,40 @@ def test_quantize_mse_argument_errors(lib):
     assert q(K=96) == INVALID
     assert q(biases=None) == INVALID
     assert q(w=MIS) == ALIGN
+
+
+def test_quantize_zp_argument_errors(lib):
+    q = lambda **k: lib.aq_quantize_zp(k.get("w", P), k.get("dt", F32), 4, k.get("K", 64), 64,
+                                       k.get("bits", 4), k.get("codes", P), P,
+                                       k.get("biases", P), k.get("zeros", None), None)
+    assert q(bits=1) == INVALID
+    assert q(bits=9) == INVALID
+    assert q(K=96) == INVALID
+    assert q(dt=7) == INVALID
+    assert q(w=None) == INVALID
+    assert q(codes=None) == INVALID
+    assert q(biases=None) == INVALID       # the quantizers always write biases
+    assert q(w=MIS) == ALIGN
+    assert q(zeros=MIS) == ALIGN           # zeros optional, aligned when given
+
+
+def test_consumers_take_null_biases(lib):
+    """A null bias array is accepted by every consumer (every bias +0); the
+    other checks still run: a misaligned scale array is still refused, and a
+    misaligned bias array too when one is given."""
+    for fn in ("aq_qmv", "aq_qmm", "aq_quantized_matmul"):
+        assert qmv(lib, fn, biases=None, scales=MIS) == ALIGN
+        assert qmv(lib, fn, biases=None, bits=1) == INVALID
+        assert qmv(lib, fn, biases=MIS) == ALIGN
+        assert qmv(lib, fn, biases=None, codes=None) == INVALID
+    assert lib.aq_dequantize(P, MIS, None, 4, 64, 64, 4, P, F16, None) == ALIGN
+    assert lib.aq_dequantize(P, P, None, 4, 64, 64, 9, P, F16, None) == INVALID
+    assert lib.aq_embedding(P, MIS, None, 4, 64, 64, 4, P, 2, P, F16, None) == ALIGN
+    for name in ("aq_gather_qmv", "aq_gather_qmm", "aq_gather_quantized_matmul"):
+        assert getattr(lib, name)(P, F16, 4, P, MIS, None, 8, 64, 128, P, 2, 64, 4, P,
+                                  None) == ALIGN
+        assert getattr(lib, name)(P, F16, 4, P, P, None, 8, 64, 128, P, 0, 64, 4, P,
+                                  None) == INVALID
 
 
 def test_gather_argument_errors(lib):

@@ -160,6 +160,128 @@ def test_quantize_edge_groups(aq, bits):
     _check_mse(w, G, bits, 50, packed_from_dev(*aq.aq_quantize_mse(to_dev(w), G, bits, 50)))
 
 
+# ---- integer zero point -----------------------------------------------------------------
+def _zp_from_dev(got):
+    c, s, b = packed_from_dev(*got[:3])
+    return c, s, b, got[3].cpu().numpy()
+
+
+@pytest.mark.parametrize("bits", ALL_BITS)
+@pytest.mark.parametrize("G", [32, 64, 128])
+def test_quantize_zp_bitexact(aq, bits, G):
+    """Codes, scales, biases and zero points bit-exact with the reference, on
+    Gaussian rows with outliers and on groups whose members share a sign."""
+    N, K = 37, 6 * G
+    w = np.concatenate([inputs.weights(N - 8, K, seed=40, key=(G, bits), outliers=True),
+                        inputs.same_sign_weights(8, K, G, seed=41, key=(G, bits))])
+    ref = oracle.quantize_zp(w, G, bits)
+    got = _zp_from_dev(aq.aq_quantize_zp(to_dev(w), G, bits))
+    for a, r, name in zip(got, ref, ("codes", "scales", "biases", "zeros")):
+        assert np.array_equal(a, r), name
+
+
+@pytest.mark.parametrize("wdt", ["f16", "bf16"])
+def test_quantize_zp_half_inputs_and_edge_groups(aq, wdt):
+    G, bits = 32, 4
+    L = (1 << bits) - 1
+    rng = np.random.default_rng(42)
+    rows = [np.zeros(G), -np.zeros(G), np.full(G, 0.123), np.full(G, -7.5),
+            rng.standard_normal(G) * 1e-6, np.linspace(-600.0, 500.0, G),
+            np.linspace(0.25, 1.5, G), -np.linspace(0.25, 1.5, G)]
+    s0, z0 = 2.0 ** -8, 5
+    q = rng.integers(0, L + 1, G)
+    q[0], q[1] = 0, L
+    rows.append((q - z0) * s0)                                # exact grid points
+    w32 = inputs.from_bits(inputs.to_bits(np.array(rows), wdt), wdt).astype(np.float32)
+    ref = oracle.quantize_zp(w32, G, bits)
+    got = _zp_from_dev(aq.aq_quantize_zp(bits_to_dev(inputs.to_bits(w32, wdt), wdt), G, bits))
+    for a, r, name in zip(got, ref, ("codes", "scales", "biases", "zeros")):
+        assert np.array_equal(a, r), name
+
+
+def test_quantize_zp_without_zeros_output(aq):
+    import torch
+    import ctypes
+    G, bits, N, K = 64, 4, 9, 256
+    w = inputs.weights(N, K, seed=43, outliers=True)
+    wd = to_dev(w)
+    codes = torch.empty((N, K * bits // 32), dtype=torch.int32, device="cuda")
+    scales = torch.empty((N, K // G), dtype=torch.float16, device="cuda")
+    biases = torch.empty((N, K // G), dtype=torch.float16, device="cuda")
+    lib = aq.load_library()
+    st = lib.aq_quantize_zp(ctypes.c_void_p(wd.data_ptr()), 0, N, K, G, bits,
+                            ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
+                            ctypes.c_void_p(biases.data_ptr()), None,
+                            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0
+    torch.cuda.synchronize()
+    ref = oracle.quantize_zp(w, G, bits)
+    for a, r in zip(packed_from_dev(codes, scales, biases), ref[:3]):
+        assert np.array_equal(a, r)
+
+
+# ---- null biases (every bias +0) -----------------------------------------------------------
+@pytest.mark.parametrize("bits,G", [(4, 64), (8, 128), (3, 64), (2, 32)])
+def test_null_bias_consumers(aq, bits, G):
+    """Every consumer with biases=None gives exactly the result of an all-zero
+    bias array (the same kernels read +0), and that result matches the
+    reference with zero biases: bit-exact for dequantize and the embedding,
+    within the bound for the matmuls (1, 3, 8, 40 and 130 rows, and the
+    gathers)."""
+    import torch
+    N, K = 70, 8 * G
+    w = inputs.weights(N, K, seed=44, key=(bits, G))
+    c, s, _ = oracle.quantize(w, G, bits)
+    zb = np.zeros_like(s)                                   # fp16 +0 biases
+    dc, ds, dz = packed_to_dev(c, s, zb)
+    for out in ("f32", "bf16"):
+        code = {"f32": oracle.F32, "bf16": oracle.BF16}[out]
+        ref = oracle.dequantize(c, s, zb, K, G, bits, code)
+        a = out_bits(aq.aq_dequantize(dc, ds, None, G, bits, out_dtype=torch_dtype(out)))
+        b = out_bits(aq.aq_dequantize(dc, ds, dz, G, bits, out_dtype=torch_dtype(out)))
+        assert np.array_equal(a, b)
+        assert np.array_equal(a, ref.view(np.uint32) if out == "f32" else ref)
+    ids = np.array([3, 0, 69, -1, 70, 12], dtype=np.int32)
+    a = out_bits(aq.aq_embedding(to_dev(ids), dc, ds, None, G, bits, out_dtype=torch.bfloat16))
+    b = out_bits(aq.aq_embedding(to_dev(ids), dc, ds, dz, G, bits, out_dtype=torch.bfloat16))
+    assert np.array_equal(a, b)
+    for M in (1, 3, 8, 40, 130):
+        xb = inputs.activations(M, K, "f16", seed=44, key=(M, bits))
+        x = bits_to_dev(xb, "f16")
+        y_ref, A = oracle.matmul(inputs.from_bits(xb, "f16"), c, s, zb, K, G, bits)
+        fns = [aq.aq_quantized_matmul, aq.aq_qmm] + ([aq.aq_qmv] if M <= 8 else [])
+        for fn in fns:
+            y0, y1 = fn(x, dc, ds, None, G, bits), fn(x, dc, ds, dz, G, bits)
+            assert np.array_equal(out_bits(y0), out_bits(y1)), (fn.__name__, M)
+            _assert_close(y0, y_ref, A, f"null-bias {fn.__name__} M{M} b{bits}")
+    E, T, topk = 5, 24, 3
+    ce, se, _ = _experts(E, N, K, G, bits, seed=45)
+    zbe = np.zeros_like(se)
+    ide = inputs.expert_ids(T, E, topk, seed=45)
+    xb = inputs.activations(T, K, "f16", seed=45)
+    y_ref, A = oracle.gather_matmul(inputs.from_bits(xb, "f16"), ce, se, zbe, ide, K, G, bits)
+    dce, dse, dze = packed_to_dev(ce, se, zbe)
+    for fn in (aq.aq_gather_qmv, aq.aq_gather_qmm, aq.aq_gather_quantized_matmul):
+        y0 = fn(bits_to_dev(xb, "f16"), dce, dse, None, to_dev(ide), G, bits)
+        y1 = fn(bits_to_dev(xb, "f16"), dce, dse, dze, to_dev(ide), G, bits)
+        assert np.array_equal(out_bits(y0), out_bits(y1)), fn.__name__
+        _assert_close(y0, y_ref, A, f"null-bias {fn.__name__} b{bits}")
+
+
+def test_zero_point_output_through_every_consumer(aq):
+    """The zero-point quantizer's container feeds the consumers unchanged: the
+    4-bit G=64 result through the decode, few-row and prefill kernels."""
+    G, bits, N, K = 64, 4, 300, 4096
+    w = inputs.weights(N, K, seed=46, outliers=True)
+    c, s, b, _ = oracle.quantize_zp(w, G, bits)
+    dev = packed_to_dev(c, s, b)
+    for M in (1, 4, 24, 300):
+        xb = inputs.activations(M, K, "bf16", seed=46, key=(M,))
+        y_ref, A = oracle.matmul(inputs.from_bits(xb, "bf16"), c, s, b, K, G, bits)
+        _assert_close(aq.aq_quantized_matmul(bits_to_dev(xb, "bf16"), *dev, G, bits), y_ref, A,
+                      f"zero-point container M{M}")
+
+
 # ---- dequantize -------------------------------------------------------------------------
 @pytest.mark.parametrize("bits", ALL_BITS)
 @pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
