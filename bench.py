@@ -21,7 +21,12 @@ first part).  The JSON line also carries:
                 back-to-back launches) vs 8 TB/s, and its HBM traffic per
                 launch from the committed counter summary when it matches the
                 current kernel source;
-  cpu_baseline  the CPU reference computing the same step on the host cores;
+  cpu_baseline  the CPU reference computing the same decode step on the host
+                cores (value), with "legs" timing it beside every other
+                section on bounded samples of the same inputs: spec-decode
+                (M = 4), MoE gather, quantize, prefill (a few rows of X
+                against the whole W) and the tiny 512 x 512 case on one
+                thread; nproc, OpenMP threads and the CPU model are stated;
   qmm           the metric's second part: prefill Y = X @ W^T with X bf16
                 [2048, 8192] and W [28672, 8192] at 4-bit G=64 (plus 3-bit
                 G=64 and 2-bit G=32), TFLOP/s vs the 2.5 PFLOP/s dense bf16 peak
@@ -262,17 +267,19 @@ def main():
         torch.cuda.synchronize()
 
     # ---- CPU baseline: the CPU reference on the same step -----------------------------------
+    legs = None
     if not args.no_cpu:
         result["cpu_baseline"] = _cpu_baseline(mats, args.cpu_seconds)
+        legs = result["cpu_baseline"]["legs"]
 
     # ---- spec-decode (M = 2..8) and MoE gather: % of HBM per launch ------------------------
     if not args.no_extra:
-        result["specdec"] = _specdec(aq, inputs, dev, stream)
-        result["moe"] = _moe(aq, inputs, dev, stream)
+        result["specdec"] = _specdec(aq, inputs, dev, stream, legs)
+        result["moe"] = _moe(aq, inputs, dev, stream, legs)
 
     # ---- quantize and dequantize (offline conversion, standalone decode) -------------------
     if not args.no_extra:
-        result["quantize_dequantize"] = _quant_dequant(aq, inputs, dev, stream)
+        result["quantize_dequantize"] = _quant_dequant(aq, inputs, dev, stream, legs)
 
     # ---- quantized embedding ---------------------------------------------------------------
     if not args.no_embedding:
@@ -285,7 +292,7 @@ def main():
         if args.no_embedding:
             del round_graph, step_graphs, sets
         torch.cuda.synchronize()
-        result["qmm"] = _qmm(aq, inputs, dev, args.qmm_iters)
+        result["qmm"] = _qmm(aq, inputs, dev, args.qmm_iters, legs)
 
     print(json.dumps(result), flush=True)
 
@@ -359,42 +366,81 @@ def _traffic(kname, group):
         return None
 
 
-def _cpu_baseline(mats, seconds):
+def _host_packed(c, s, b):
+    """Device packed weights -> the reference's numpy arrays."""
     import numpy as np
     import torch
+    return (c.cpu().numpy().view(np.uint32), s.view(torch.int16).cpu().numpy().view(np.uint16),
+            b.view(torch.int16).cpu().numpy().view(np.uint16))
 
-    import oracle
+
+def _host_x(x, dtype):
+    """Device fp16/bf16 activations -> exact float64 values."""
+    import numpy as np
+    import torch
     from group_wise_affine_aq_amd import inputs as _inp
+    return _inp.from_bits(x.view(torch.int16).cpu().numpy().view(np.uint16), dtype)
 
-    host = []
-    for m in mats:
-        c, s, b = m["packed"]
-        host.append((_inp.from_bits(m["x"].view(torch.int16).cpu().numpy().view(np.uint16), "f16"),
-                     c.cpu().numpy().view(np.uint32),
-                     s.view(torch.int16).cpu().numpy().view(np.uint16),
-                     b.view(torch.int16).cpu().numpy().view(np.uint16), m["K"]))
-    reps, t_start = 0, time.perf_counter()
+
+def _cpu_timed(fn, seconds):
+    """Run fn until at least `seconds` of wall time have passed (at least once);
+    returns (runs, elapsed seconds)."""
+    runs, t0 = 0, time.perf_counter()
     while True:
-        for x, c, s, b, K in host:
-            oracle.matmul(x, c, s, b, K, G, BITS)
-        reps += 1
-        el = time.perf_counter() - t_start
+        fn()
+        runs += 1
+        el = time.perf_counter() - t0
         if el >= seconds:
-            break
-    step_bytes = sum(m["wbytes"] for m in mats)
-    cpu_gbs = step_bytes * reps / el / 1e9
-    model = "?"
+            return runs, el
+
+
+def _cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
             if line.startswith("model name"):
-                model = line.split(":", 1)[1].strip()
-                break
+                return line.split(":", 1)[1].strip()
     except OSError:
         pass
-    return {"value": round(cpu_gbs, 3), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+    return "?"
+
+
+def _cpu_baseline(mats, seconds):
+    """The reference on the decode step (all host threads OpenMP gives it), and
+    the single-thread tiny case; the other sections add their legs."""
+    import oracle
+    from group_wise_affine_aq_amd import inputs as _inp
+
+    host = [(_host_x(m["x"], "f16"), *_host_packed(*m["packed"]), m["K"]) for m in mats]
+
+    def step():
+        for x, c, s, b, K in host:
+            oracle.matmul(x, c, s, b, K, G, BITS)
+
+    reps, el = _cpu_timed(step, seconds)
+    step_bytes = sum(m["wbytes"] for m in mats)
+    cpu_gbs = step_bytes * reps / el / 1e9
+    model, threads = _cpu_model(), oracle.num_threads()
+    # the tiny workload (W [512, 512] 4-bit G=64, x fp16 [1, 512]) on one thread
+    w = _inp.weights(512, 512, seed=0)
+    c, s, b = oracle.quantize(w, G, BITS)
+    x = _inp.from_bits(_inp.activations(1, 512, "f16", seed=0), "f16")
+    oracle.set_num_threads(1)
+    try:
+        runs, t1 = _cpu_timed(lambda: oracle.matmul(x, c, s, b, 512, G, BITS), 1.0)
+    finally:
+        oracle.set_num_threads(threads)
+    tiny_bytes = oracle.qweight_bytes(512, 512, G, BITS)
+    legs = {"tiny_single_thread": {
+        "workload": "W [512,512] 4-bit G=64, x fp16 [1,512]", "threads": 1,
+        "us_per_call": round(t1 / runs * 1e6, 1), "gbs": round(tiny_bytes * runs / t1 / 1e9, 3),
+        "sample": f"{runs} calls in {t1:.1f} s"}}
+    print(f"# CPU reference: decode {cpu_gbs:.3f} GB/s on {threads} threads; tiny case "
+          f"{legs['tiny_single_thread']['us_per_call']} us on one thread", file=sys.stderr,
+          flush=True)
+    return {"value": round(cpu_gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{reps} full decode step(s) (4 matrices, {step_bytes} packed weight bytes, "
-                      f"fp64 accumulation), {el:.1f} s on {model}"}
+                      f"fp64 accumulation), {el:.1f} s on {model}",
+            "nproc": os.cpu_count(), "omp_threads": threads, "cpu_model": model, "legs": legs}
 
 
 def _graph_us(torch, stream, launches, reps=5):
@@ -421,7 +467,7 @@ def _graph_us(torch, stream, launches, reps=5):
     return sum(durs) / len(durs)
 
 
-def _specdec(aq, inputs, dev, stream):
+def _specdec(aq, inputs, dev, stream, legs=None):
     """Matrix-vector kernels for M = 2..8 rows (bf16), and the same matrices
     at 16 and 64 rows, each launch on a cold copy of the weights (>= 1 GiB
     rotated), per-launch time in a graph."""
@@ -453,13 +499,25 @@ def _specdec(aq, inputs, dev, stream):
                       file=sys.stderr, flush=True)
             out[f"{N}x{K}_b{bits}_g{g}"] = dict(weight_bytes=wbytes,
                                                 read_ceiling_us=round(ceil_us, 3), **rows)
+            if legs is not None and "specdec" not in legs:
+                # the reference on the first matrix, M = 4 rows of the same x
+                import oracle
+                M = 4
+                x = inputs.activations_device(M, K, "bf16", device=dev, seed=0, key=(wid, N, M))
+                hx, hp = _host_x(x, "bf16"), _host_packed(*packed)
+                runs, el = _cpu_timed(lambda: oracle.matmul(hx, *hp, K, g, bits), 1.5)
+                legs["specdec"] = {"workload": f"W [{N},{K}] {bits}-bit G={g}, x bf16 [{M},{K}]",
+                                   "threads": oracle.num_threads(),
+                                   "gbs": round(wbytes * runs / el / 1e9, 3),
+                                   "gpu_gbs": rows[f"M{M}"]["weight_gbs"],
+                                   "sample": f"{runs} call(s) in {el:.1f} s"}
             del sets, packed
             torch.cuda.synchronize()
         del w
     return out
 
 
-def _moe(aq, inputs, dev, stream):
+def _moe(aq, inputs, dev, stream, legs=None):
     """Gather matrix-vector kernel: 32 tokens x top-6 of 64 experts [1408, 2048]
     4-bit G=64; cold copies of the expert stack rotated (>= 1 GiB)."""
     import numpy as np
@@ -491,6 +549,14 @@ def _moe(aq, inputs, dev, stream):
                        f"ids [{T},{topk}], cold weights",
            "experts_used": used, "algo_bytes": algo, "avg_us": round(us, 3),
            "gbs": round(gbs, 1), "pct_hbm": round(100 * gbs / HBM_PEAK_GBS, 1)}
+    if legs is not None:
+        import oracle
+        hx, hp = _host_x(x, "f16"), _host_packed(*packed)
+        runs, el = _cpu_timed(lambda: oracle.gather_matmul(hx, *hp, ids_np, K, g, bits), 1.5)
+        legs["moe"] = {"workload": res["workload"].replace(", cold weights", ""),
+                       "threads": oracle.num_threads(),
+                       "gbs": round(algo * runs / el / 1e9, 3), "gpu_gbs": round(gbs, 1),
+                       "sample": f"{runs} call(s) in {el:.1f} s"}
     # the same expert stack at prefill size on the matrix cores
     Tp = cfg["prefill_tokens"]
     ids_p = torch.from_numpy(inputs.expert_ids(Tp, E, topk, seed=0, key=(wid, 1))).to(dev)
@@ -511,7 +577,7 @@ def _moe(aq, inputs, dev, stream):
     return res
 
 
-def _quant_dequant(aq, inputs, dev, stream):
+def _quant_dequant(aq, inputs, dev, stream, legs=None):
     """aq_quantize on W [28672, 8192] fp32 (4-bit G=64) and aq_dequantize of the
     result to bf16: each one pass over HBM, timed in graphs of back-to-back
     launches."""
@@ -539,6 +605,18 @@ def _quant_dequant(aq, inputs, dev, stream):
     res["quantize_mse"] = {"steps": steps, "avg_us": round(us, 2), "bytes": nb,
                            "gbs": round(nb / (us * 1e-6) / 1e9, 1),
                            "weights_per_s": round(N * K / (us * 1e-6), 1)}
+    if legs is not None:
+        # the reference quantizer on the first 1024 rows of the same W
+        import oracle
+        rows = 1024
+        hw = w[:rows].cpu().numpy()
+        runs, el = _cpu_timed(lambda: oracle.quantize(hw, g, bits), 1.5)
+        nbs = 4 * rows * K + aq.aq_qweight_bytes(rows, K, g, bits)
+        legs["quantize"] = {"workload": f"W [{rows} of {N} rows, {K}] fp32 -> 4-bit G=64",
+                            "threads": oracle.num_threads(),
+                            "gbs": round(nbs * runs / el / 1e9, 3),
+                            "gpu_gbs": res["quantize"]["gbs"],
+                            "sample": f"{runs} call(s) in {el:.1f} s"}
     print(f"# quantize {res['quantize']['avg_us']:.1f} us ({res['quantize']['gbs']} GB/s), "
           f"dequantize {res['dequantize_bf16']['avg_us']:.1f} us ({res['dequantize_bf16']['gbs']} GB/s), "
           f"range-search quantize ({steps} ranges) {res['quantize_mse']['avg_us']:.1f} us",
@@ -595,7 +673,7 @@ def _embedding(aq, inputs, dev, stream):
     return out
 
 
-def _qmm(aq, inputs, dev, iters):
+def _qmm(aq, inputs, dev, iters, legs=None):
     import torch
     M, N, K = PREFILL["M"], PREFILL["N"], PREFILL["K"]
     x = inputs.activations_device(M, K, "bf16", device=dev, seed=0, key=(3,))
@@ -625,6 +703,18 @@ def _qmm(aq, inputs, dev, iters):
                                 "pct_mfma_peak": round(100 * tf / MFMA_BF16_PEAK_TFLOPS, 1)}
         print(f"# QMM {bits}-bit G={g}: {avg:.3f} ms (median {med:.3f}), {tf:.1f} TFLOP/s",
               file=sys.stderr, flush=True)
+        if legs is not None and "qmm" not in legs:
+            # the reference on the first 4 rows of X against all of W
+            import oracle
+            Ms = 4
+            hx, hp = _host_x(x[:Ms], "bf16"), _host_packed(c, s, b)
+            runs, el = _cpu_timed(lambda: oracle.matmul(hx, *hp, K, g, bits), 1.0)
+            legs["qmm"] = {"workload": f"X bf16 [{Ms} of {M} rows, {K}] x W [{N},{K}] "
+                                       f"{bits}-bit G={g}",
+                           "threads": oracle.num_threads(),
+                           "gflops": round(2 * Ms * N * K * runs / el / 1e9, 3),
+                           "gpu_gflops": round(tf * 1e3, 1),
+                           "sample": f"{runs} call(s) in {el:.1f} s"}
         del c, s, b
     # dense bf16 GEMM on the library GEMM (hipBLASLt) at the same shape, for context
     wd = w.to(torch.bfloat16)

@@ -31,7 +31,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 def lib_path() -> str:
-    return os.path.join(_HERE, "libaq.so")
+    """The in-tree library, or the file AQ_LIB names (the sanitizer build)."""
+    return os.environ.get("AQ_LIB") or os.path.join(_HERE, "libaq.so")
 
 
 class AQError(RuntimeError):

@@ -92,6 +92,7 @@ const char *aq_status_string(aq_status status) {
     case AQ_ERR_HIP: return "AQ_ERR_HIP: HIP runtime error at launch";
     case AQ_ERR_RANGE: return "AQ_ERR_RANGE: value out of range";
     case AQ_ERR_INDEX: return "AQ_ERR_INDEX: index out of range";
+    default: break;
   }
   return "unknown aq_status";
 }

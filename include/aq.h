@@ -59,13 +59,21 @@ typedef enum aq_status {
   AQ_ERR_ALIGNMENT = -3,   /* a pointer is not 16-byte aligned */
   AQ_ERR_HIP = -4,         /* the HIP runtime reported an error at launch */
   AQ_ERR_RANGE = -5,       /* reserved: value out of the representable range */
-  AQ_ERR_INDEX = -6        /* reserved: index out of range */
+  AQ_ERR_INDEX = -6,       /* reserved: index out of range */
+  /* range markers, never returned: they make every 32-bit integer a value of
+   * the type, so any int a caller passes is well defined in C and C++ */
+  AQ_STATUS_RANGE_MIN_ = -0x7FFFFFFF - 1,
+  AQ_STATUS_RANGE_MAX_ = 0x7FFFFFFF
 } aq_status;
 
 typedef enum aq_dtype {
   AQ_F32 = 0,  /* IEEE binary32 */
   AQ_F16 = 1,  /* IEEE binary16 */
-  AQ_BF16 = 2  /* bfloat16 */
+  AQ_BF16 = 2, /* bfloat16 */
+  /* range markers, never valid arguments (AQ_ERR_INVALID_ARG): every 32-bit
+   * integer is a value of the type, so validating one is well defined */
+  AQ_DTYPE_RANGE_MIN_ = -0x7FFFFFFF - 1,
+  AQ_DTYPE_RANGE_MAX_ = 0x7FFFFFFF
 } aq_dtype;
 
 /* ---- host helpers (no GPU involved) ------------------------------------ */

@@ -50,11 +50,15 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        build()
-        lib = ctypes.CDLL(_LIB)
+        path = os.environ.get("AQ_ORACLE_LIB")  # the sanitizer build, if named
+        if not path:
+            build()
+            path = _LIB
+        lib = ctypes.CDLL(path)
         i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
         sig = {
             "oracle_num_threads": ([], i32),
+            "oracle_set_num_threads": ([i32], None),
             "oracle_half_to_double": ([ctypes.c_uint16], ctypes.c_double),
             "oracle_bf16_to_double": ([ctypes.c_uint16], ctypes.c_double),
             "oracle_double_to_half_rne": ([ctypes.c_double], ctypes.c_uint16),
@@ -92,6 +96,11 @@ def num_threads() -> int:
 
 
 # --- scalar number-format helpers -------------------------------------------
+def set_num_threads(n: int) -> None:
+    """Threads used by the reference's parallel loops from now on."""
+    _load().oracle_set_num_threads(int(n))
+
+
 def half_to_double(h: int) -> float:
     return _load().oracle_half_to_double(int(h))
 

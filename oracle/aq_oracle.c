@@ -118,6 +118,15 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* threads of the parallel loops from now on (the single-thread timing) */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* ---------------------------------------------------------------------
  * IEEE-754 binary16 and bfloat16, from their definitions.
  * ------------------------------------------------------------------- */

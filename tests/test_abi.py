@@ -51,6 +51,7 @@ def test_host_helpers(lib):
     assert aq.aq_qweight_bytes(1, 70553706496, 64, 4) == 39686459904
     assert aq.aq_qweight_bytes(10, 100, 64, 4) == -1
     assert "INVALID" in aq.aq_status_string(INVALID)
+    assert aq.aq_status_string(12345) == "unknown aq_status"
     assert aq.aq_version().startswith("libaq")
 
 
@@ -91,6 +92,7 @@ def _matmul_argument_errors(lib, fn, M):
     assert call(M=0) == INVALID
     assert call(xdt=F32) == INVALID
     assert call(xdt=7) == INVALID
+    assert call(xdt=-3) == INVALID
     assert call(x=None) == INVALID
     assert call(y=None) == INVALID
     assert call(codes=None) == INVALID
