@@ -299,7 +299,11 @@ def main():
 
 def _read_ceiling_us(aq, torch, nbytes, stream):
     """Per-launch time of a plain streaming read of nbytes cold bytes (graph of
-    back-to-back launches over >= 1 GiB of rotating buffers, HIP events)."""
+    back-to-back launches over >= 1 GiB of rotating buffers, HIP events): the
+    best of grid-stride reads at four launch shapes and one-shot reads (all of
+    a thread's loads in flight at once, a contiguous block per workgroup) at
+    three, the fastest forms a sweep of 3 block sizes x 3 depths x 4 grid
+    sizes found on the MI355X."""
     copies = max(2, math.ceil(COLD_BYTES / nbytes))
     bufs = [torch.empty(nbytes // 4, dtype=torch.int32, device=stream.device) for _ in range(copies)]
     for b in bufs:
@@ -307,12 +311,17 @@ def _read_ceiling_us(aq, torch, nbytes, stream):
     sink = torch.zeros(4, dtype=torch.int32, device=stream.device)
     best = float("inf")
     gs = torch.cuda.Stream()
-    for blocks, unroll in ((512, 4), (1024, 4), (2048, 1), (512, 8)):
+    shapes = [("stride", 512, 4), ("stride", 1024, 4), ("stride", 2048, 1), ("stride", 512, 8),
+              ("oneshot", 256, 8), ("oneshot", 512, 4), ("oneshot", 256, 4)]
+    for kind, a, unroll in shapes:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(gs):
             with torch.cuda.graph(g, stream=gs):
                 for i in range(copies):
-                    aq.aq_bench_stream_read(bufs[i], blocks, unroll, sink=sink)
+                    if kind == "stride":
+                        aq.aq_bench_stream_read(bufs[i], a, unroll, sink=sink)
+                    else:
+                        aq.aq_bench_read_oneshot(bufs[i], a, unroll, sink=sink)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()

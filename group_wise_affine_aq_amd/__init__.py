@@ -77,6 +77,7 @@ def load_library():
         "aq_gather_quantized_matmul": (
             [vp, i32, i64, vp, vp, vp, i64, i64, i64, vp, i32, i32, i32, vp, vp], i32),
         "aq_bench_stream_read": ([vp, i64, i32, i32, vp, vp], i32),
+        "aq_bench_read_oneshot": ([vp, i64, i32, i32, vp, vp], i32),
         "aq_bench_mfma_clock": ([i32, i32, vp, vp], i32),
     }
     for name, (args, res) in sigs.items():
@@ -323,6 +324,19 @@ def aq_bench_stream_read(buf, blocks: int = 512, unroll: int = 4, sink=None, str
     st = load_library().aq_bench_stream_read(_dev(buf, "buf"), nbytes, blocks, unroll,
                                              _dev(sink, "sink"), _stream(stream))
     _check(st, "aq_bench_stream_read")
+    return sink
+
+
+def aq_bench_read_oneshot(buf, threads: int = 256, unroll: int = 8, sink=None, stream=None):
+    """Read all of the device tensor `buf` once, every thread's loads issued up
+    front, one contiguous block per workgroup."""
+    torch = _torch()
+    if sink is None:
+        sink = torch.zeros(4, dtype=torch.int32, device=buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    st = load_library().aq_bench_read_oneshot(_dev(buf, "buf"), nbytes, threads, unroll,
+                                              _dev(sink, "sink"), _stream(stream))
+    _check(st, "aq_bench_read_oneshot")
     return sink
 
 

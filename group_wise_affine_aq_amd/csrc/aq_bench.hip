@@ -27,6 +27,25 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4 *__restric
   if (acc == 0x9E3779B9u) sink[0] = acc;  // practically never; keeps the loads alive
 }
 
+// one-shot streaming read: workgroup b reads the contiguous block of
+// blockDim * U 16-byte units at b * blockDim * U; every thread issues its U
+// loads before using any of them
+template <int U>
+__global__ __launch_bounds__(1024) void read_oneshot_kernel(const uint4 *__restrict__ p, int64_t n16,
+                                                            uint32_t *sink) {
+  const int64_t base = (int64_t)blockIdx.x * blockDim.x * U + threadIdx.x;
+  uint4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t j = base + (int64_t)u * blockDim.x;
+    v[u] = j < n16 ? p[j] : make_uint4(0, 0, 0, 0);
+  }
+  uint32_t acc = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  if (acc == 0x9E3779B9u) sink[0] = acc;  // practically never; keeps the loads alive
+}
+
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
 typedef float f32x16v __attribute__((ext_vector_type(16)));
 
@@ -76,6 +95,26 @@ aq_status aq_bench_stream_read(const void *buf, int64_t bytes, int blocks, int u
     case 1: hipLaunchKernelGGL(stream_read_kernel<1>, dim3(blocks), dim3(256), 0, s, p, n16, sink); break;
     case 4: hipLaunchKernelGGL(stream_read_kernel<4>, dim3(blocks), dim3(256), 0, s, p, n16, sink); break;
     default: hipLaunchKernelGGL(stream_read_kernel<8>, dim3(blocks), dim3(256), 0, s, p, n16, sink); break;
+  }
+  return hipGetLastError() == hipSuccess ? AQ_OK : AQ_ERR_HIP;
+}
+
+aq_status aq_bench_read_oneshot(const void *buf, int64_t bytes, int threads, int unroll,
+                                uint32_t *sink, void *stream) {
+  if (!buf || !sink || bytes < 16 || bytes % 16 != 0) return AQ_ERR_INVALID_ARG;
+  if (threads != 256 && threads != 512 && threads != 1024) return AQ_ERR_INVALID_ARG;
+  if (unroll != 4 && unroll != 8 && unroll != 16) return AQ_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(buf) & 15u) != 0) return AQ_ERR_ALIGNMENT;
+  const int64_t n16 = bytes / 16, per = (int64_t)threads * unroll;
+  const int64_t blocks = (n16 + per - 1) / per;
+  if (blocks > 0x7FFFFFFF) return AQ_ERR_UNSUPPORTED;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint4 *p = static_cast<const uint4 *>(buf);
+  const dim3 grid((unsigned)blocks), block((unsigned)threads);
+  switch (unroll) {
+    case 4: hipLaunchKernelGGL(read_oneshot_kernel<4>, grid, block, 0, s, p, n16, sink); break;
+    case 8: hipLaunchKernelGGL(read_oneshot_kernel<8>, grid, block, 0, s, p, n16, sink); break;
+    default: hipLaunchKernelGGL(read_oneshot_kernel<16>, grid, block, 0, s, p, n16, sink); break;
   }
   return hipGetLastError() == hipSuccess ? AQ_OK : AQ_ERR_HIP;
 }

@@ -26,6 +26,15 @@ extern "C" {
 aq_status aq_bench_stream_read(const void *buf, int64_t bytes, int blocks, int unroll,
                                uint32_t *sink, void *stream);
 
+/* Read `bytes` bytes at `buf` once, in one-shot form: workgroups of `threads`
+ * (256, 512 or 1024) threads, each thread issuing all of its `unroll` (4, 8
+ * or 16) 16-byte loads before using any; workgroup b reads the contiguous
+ * block of threads * unroll * 16 bytes at b times that size.  Same sink,
+ * alignment and error conventions as aq_bench_stream_read (AQ_ERR_UNSUPPORTED
+ * past 2^31 - 1 workgroups). */
+aq_status aq_bench_read_oneshot(const void *buf, int64_t bytes, int threads, int unroll,
+                                uint32_t *sink, void *stream);
+
 /* Run `iters` rounds of 14 independent v_mfma_f32_32x32x16_bf16 per wave on
  * `blocks` workgroups of 4 waves (one per SIMD when blocks <= the CU count)
  * and record, per wave, the shader-clock cycles (s_memtime) and the 100 MHz

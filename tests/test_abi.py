@@ -134,6 +134,11 @@ def test_bench_helper_argument_errors(lib):
     assert lib.aq_bench_stream_read(MIS, 1024, 512, 4, P, None) == ALIGN
     assert lib.aq_bench_mfma_clock(0, 10, P, None) == INVALID
     assert lib.aq_bench_mfma_clock(4, 0, P, None) == INVALID
+    assert lib.aq_bench_read_oneshot(P, 1024, 128, 8, P, None) == INVALID
+    assert lib.aq_bench_read_oneshot(P, 1024, 256, 2, P, None) == INVALID
+    assert lib.aq_bench_read_oneshot(P, 1000, 256, 8, P, None) == INVALID
+    assert lib.aq_bench_read_oneshot(MIS, 1024, 256, 8, P, None) == ALIGN
+    assert lib.aq_bench_read_oneshot(P, 1024, 256, 8, None, None) == INVALID
     assert lib.aq_bench_mfma_clock(4, 10, None, None) == INVALID
 
 
