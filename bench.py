@@ -41,8 +41,9 @@ the same bytes (same cold rotation and timing), a measured second denominator.
                 weights; plus the matrix-core gather on the same experts at
                 prefill size (2048 tokens, top-6), TFLOP/s;
   quantize_dequantize  aq_quantize of the prefill-size matrix (fp32 in),
-                aq_dequantize of it to bf16 (% of HBM), and the range-search
-                aq_quantize_mse over 21 narrowed ranges;
+                aq_dequantize of it to bf16 (% of HBM), the integer-zero-point
+                aq_quantize_zp and the range-search aq_quantize_mse over 21
+                narrowed ranges;
   embedding     quantized embedding lookups (rows of a [128256, 4096] 8-bit
                 table dequantized to bf16) for 1 and 2048 tokens.
 
@@ -606,7 +607,16 @@ def _quant_dequant(aq, inputs, dev, stream, legs=None):
     res["dequantize_bf16"] = {"avg_us": round(us, 2), "bytes": nb,
                               "gbs": round(nb / (us * 1e-6) / 1e9, 1),
                               "pct_hbm": round(100 * nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
-    # range search over 21 narrowed ranges (p = 1.00 .. 0.80), same matrix
+    # integer zero points, same matrix (zeros written too)
+    zeros = torch.empty((N, K // g), dtype=torch.uint8, device=dev)
+    us = _graph_us(torch, stream, [lambda: aq.aq_quantize_zp(w, g, bits, codes=c, scales=s_,
+                                                             biases=b, zeros=zeros)] * 4)
+    nb = 4 * N * K + packed + N * (K // g)
+    res["quantize_zp"] = {"avg_us": round(us, 2), "bytes": nb,
+                          "gbs": round(nb / (us * 1e-6) / 1e9, 1),
+                          "pct_hbm": round(100 * nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
+    # range search over 21 narrowed ranges (both ends moved inwards, keeping
+    # 100 % .. 80 % of the width), same matrix
     steps = 21
     us = _graph_us(torch, stream,
                    [lambda: aq.aq_quantize_mse(w, g, bits, steps, codes=c, scales=s_, biases=b)] * 2)
@@ -626,6 +636,8 @@ def _quant_dequant(aq, inputs, dev, stream, legs=None):
                             "gbs": round(nbs * runs / el / 1e9, 3),
                             "gpu_gbs": res["quantize"]["gbs"],
                             "sample": f"{runs} call(s) in {el:.1f} s"}
+    print(f"# zero-point quantize {res['quantize_zp']['avg_us']:.1f} us "
+          f"({res['quantize_zp']['gbs']} GB/s)", file=sys.stderr, flush=True)
     print(f"# quantize {res['quantize']['avg_us']:.1f} us ({res['quantize']['gbs']} GB/s), "
           f"dequantize {res['dequantize_bf16']['avg_us']:.1f} us ({res['dequantize_bf16']['gbs']} GB/s), "
           f"range-search quantize ({steps} ranges) {res['quantize_mse']['avg_us']:.1f} us",
