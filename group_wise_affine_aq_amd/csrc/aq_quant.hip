@@ -276,41 +276,62 @@ __global__ __launch_bounds__(256) void quantize_mse_kernel(const void *__restric
   for (int j = 0; j < BITS; ++j) dst[j] = (uint8_t)(best_packed >> (8 * j));
 }
 
-// smallest integer u in [0, cap + 1] with u*s >= t (t >= 0, s > 0 an fp16
-// value): the binary64 quotient proposes it, exact products correct it
-__device__ __forceinline__ int ceil_steps(double t, double s, int cap) {
-  const double qd = t / s;
-  if (!(qd <= (double)cap)) return cap + 1;
-  int u = (int)__builtin_ceil(qd);
-  while (u > 0 && (double)(u - 1) * s >= t) --u;
-  while (u <= cap && (double)u * s < t) ++u;
+// Smallest u in [0, cap] with u s >= t (t >= 0, s > 0), or cap + 1 when
+// cap s < t.  u <= 255 and s an fp16 value make every product u s exact in
+// binary32, so each comparison is exact; the reciprocal only seeds the walk.
+__device__ __forceinline__ int ceil_steps(float t, float s, int cap) {
+  if ((float)cap * s < t) return cap + 1;
+  int u = (int)__builtin_ceilf(t * __builtin_amdgcn_rcpf(s));
+  u = u < 0 ? 0 : (u > cap ? cap : u);
+  while (u > 0 && (float)(u - 1) * s >= t) --u;
+  while ((float)u * s < t) ++u;
   return u;
 }
 
-// The zero-point search for one group with members in [lo, hi]: scale
-// pattern and zero point.  Scales start at the smallest one whose L steps
-// span [min(lo, 0), max(hi, 0)] (a grid holding 0 cannot be narrower).
-__device__ __forceinline__ uint16_t zero_point_scale(float lo, float hi, int L, int &z) {
-  const double lo0 = lo < 0.f ? (double)lo : 0.0, hi0 = hi > 0.f ? (double)hi : 0.0;
+// The smallest zero point admitted by the nonzero scale pattern p for a group
+// in [-nlo, hi0] (nlo, hi0 >= 0): the least integer z with z s >= nlo,
+// (L - z) s >= hi0 and z s an fp16 value (exact in binary32: z <= 255), or -1.
+__device__ __forceinline__ int zero_point_at(uint16_t p, float nlo, float hi0, int L) {
+  const float sv = f16_to_f32(p);
+  const int zmin = ceil_steps(nlo, sv, L);
+  const int zmax = L - ceil_steps(hi0, sv, L);
+  for (int zz = zmin; zz <= zmax; ++zz) {
+    const float bottom = (float)zz * sv;
+    if (f16_to_f32(f32_to_f16_rne(bottom)) == bottom) return zz;
+  }
+  return -1;
+}
+
+// The zero-point search for one group with members in [lo, hi]: the smallest
+// scale pattern admitting a zero point, and that zero point.  Scales start at
+// the smallest one whose L steps span [min(lo, 0), max(hi, 0)] (a grid holding
+// 0 cannot be narrower) and go up one pattern at a time; the `lanes` lanes of
+// the group test consecutive patterns side by side (lane li tests base + li)
+// and the least lane offset with an answer wins.
+__device__ __forceinline__ uint16_t zero_point_scale(float lo, float hi, int L, int lanes, int li,
+                                                     int &z) {
+  const float nlo = lo < 0.f ? -lo : 0.f, hi0 = hi > 0.f ? hi : 0.f;
+  const uint16_t p0 = f16_scale_up(lo < 0.f ? (double)lo : 0.0, (double)hi0, L);
   z = 0;
-  for (uint16_t p = f16_scale_up(lo0, hi0, L); p <= 0x7BFFu; ++p) {
-    const double sv = h2d(p);
-    if (sv == 0.0) return p;  // only an all-zero group: z = 0, s = 0
-    const int zmin = ceil_steps(-lo0, sv, L);
-    const int zmax = L - ceil_steps(hi0, sv, L);
-    for (int zz = zmin; zz <= zmax; ++zz) {
-      const float bottom = (float)zz * (float)sv;  // exact in binary32
-      if (f16_to_f32(f32_to_f16_rne(bottom)) == bottom) {
-        z = zz;
-        return p;
-      }
+  if (p0 == 0) return 0;  // only an all-zero group: z = 0, s = 0
+  for (uint32_t base = p0; base <= 0x7BFFu; base += (uint32_t)lanes) {
+    const uint32_t p = base + (uint32_t)li;
+    const int zz = p <= 0x7BFFu ? zero_point_at((uint16_t)p, nlo, hi0, L) : -1;
+    uint32_t key = zz >= 0 ? ((uint32_t)li << 8) | (uint32_t)zz : 0xFFFFFFFFu;
+    for (int d = 1; d < lanes; d <<= 1) {
+      const uint32_t other = (uint32_t)__shfl_xor((int)key, d);
+      key = other < key ? other : key;
+    }
+    if (key != 0xFFFFFFFFu) {
+      z = (int)(key & 0xFFu);
+      return (uint16_t)(base + (key >> 8));
     }
   }
   return 0x7BFFu;  // outside the documented precondition
 }
 
-// Integer-zero-point quantize: the thread mapping of quantize_kernel; every
-// lane of a group runs the same search.
+// Integer-zero-point quantize: the thread mapping of quantize_kernel; the
+// lanes of a group share its scale search.
 template <int WDT, int BITS>
 __global__ __launch_bounds__(256) void quantize_zp_kernel(const void *__restrict__ w, int64_t N,
                                                           int64_t K, int G,
@@ -337,7 +358,7 @@ __global__ __launch_bounds__(256) void quantize_zp_kernel(const void *__restrict
   }
   constexpr int L = (1 << BITS) - 1;
   int z = 0;
-  const uint16_t s16 = zero_point_scale(lo, hi, L, z);
+  const uint16_t s16 = zero_point_scale(lo, hi, L, lanes, (int)threadIdx.x & (lanes - 1), z);
   const double s = h2d(s16);
   const uint16_t b16 = z == 0 ? (uint16_t)0 : f32_to_f16_rne(-((float)z * (float)s));
   const double b = h2d(b16);
