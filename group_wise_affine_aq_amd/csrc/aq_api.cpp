@@ -202,10 +202,10 @@ int aq_qmv_describe(int64_t M, int64_t N, int64_t K, int group_size, int bits, a
     return -1;
   const char *xt = x_dtype == AQ_F16 ? "f16" : "bf16";
   if (M == 1 && K <= 8 * 2048) {
-    int cpl, ud, w;
-    aq::qmv1_shape(N, K, cpl, ud, w);
-    return snprintf(buf, (size_t)len, "qmv1_kernel<BITS=%d, %s, CPL=%d, UD=%d, W=%d>", bits, xt,
-                    cpl, ud, w);
+    int cpl, ud, w, sl;
+    aq::qmv1_shape(N, K, group_size, cpl, ud, w, sl);
+    return snprintf(buf, (size_t)len, "qmv1_kernel<BITS=%d, %s, CPL=%d, UD=%d, W=%d, SL=%d>", bits,
+                    xt, cpl, ud, w, sl);
   }
   if (aq::qmvm_supported((int)M, bits, N, K, group_size)) {
     int R, W, XR;

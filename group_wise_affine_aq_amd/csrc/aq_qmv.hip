@@ -168,19 +168,24 @@ struct Weights {
   const uint16_t *biases;  // null: every bias is +0
 };
 
-// The fp16 bias at byte offset goff of a row's biases, read through a buffer
-// resource whose base is uniform (scalar registers).  Without a bias array
+// A buffer resource over `bytes` bytes at a base that is the same in every
+// lane (moved to scalar registers).  Loads at offsets past `bytes` return 0
+// without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void *base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(((uint64_t)hi << 32) | lo), 0,
+                                           bytes, 0x00020000);
+}
+
+// The fp16 bias at byte offset goff of a row's biases.  Without a bias array
 // the resource has size 0, so the load returns 0 (+0.0) without touching
 // memory and the kernels need no second code path.
 __device__ __forceinline__ uint32_t load_bias(const Weights &wt, int64_t so, int64_t ng,
                                               uint32_t goff) {
-  const uint16_t *base = wt.biases ? wt.biases + so : wt.scales;
-  const int bytes = wt.biases ? (int)(ng * 2) : 0;
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-      reinterpret_cast<void *>(((uint64_t)hi << 32) | lo), 0, bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t r =
+      uniform_rsrc(wt.biases ? wt.biases + so : wt.scales, wt.biases ? (int)(ng * 2) : 0);
   return __builtin_amdgcn_raw_buffer_load_b16(r, (int)goff, 0, 0);
 }
 
@@ -600,11 +605,21 @@ __global__ __launch_bounds__(64 * W) void qmv_stream_kernel(const uint16_t *__re
 // chunks (the chunks l, l + 64, ... it multiplies in every row) in
 // registers, copied once from the workgroup's LDS copy of x.  The ring of
 // D = CPL * UD load buffers holds whole rows, so the pass of every ring slot
-// is a compile-time constant and the streaming loop touches no LDS at all.
-// Rows are dealt to waves round-robin (row gw, gw + TW, ...), D steps of
-// loads stay in flight across row boundaries, finished rows are parked in
-// LDS and written after the loop (as in the M <= 8 streaming kernel).
-template <int BITS, typename XT, int CPL, int UD, int W>
+// is a compile-time constant.  Rows are dealt to waves round-robin (row gw,
+// gw + TW, ...), D steps of loads stay in flight across row boundaries,
+// finished rows are parked in LDS and written after the loop (as in the
+// M <= 8 streaming kernel).
+// A row's scales and biases arrive with SL 4-byte loads of each per lane
+// (SL * 128 groups), issued just ahead of the row's first code load; when
+// that chunk is consumed the wave writes them into its LDS table as one
+// dword per group (scale | bias << 16), from which every chunk of the row
+// reads its group.  That replaces two 2-byte loads per chunk (3 vector
+// memory instructions per 1 KB of codes become 1 + 2 SL / CPL).  With an
+// odd number of groups per row, every other row starts 2 bytes into a
+// dword: its loads start at the dword boundary below, so dword j holds
+// groups 2 j - 1 and 2 j, and the table entries move down by one (the
+// table keeps two spare entries in front for that).
+template <int BITS, typename XT, int CPL, int UD, int W, int SL>
 __global__ __launch_bounds__(64 * W) void qmv1_kernel(const uint16_t *__restrict__ x, Weights wt,
                                                       int64_t N, int64_t K, int G,
                                                       uint16_t *__restrict__ y) {
@@ -616,11 +631,52 @@ __global__ __launch_bounds__(64 * W) void qmv1_kernel(const uint16_t *__restrict
   const QmvCore<BITS, 1, XT, 1> core(wt, N, K, G);
   const int64_t TW = (int64_t)gridDim.x * W, gw = (int64_t)blockIdx.x * W + wave;
   const int nunits = gw < N ? (int)((N - 1 - gw) / TW + 1) : 0;
+  const int ng = core.nch >> core.gshift;  // groups per row, at most SL * 128
 
   uint8_t *xlds = smem;
   float *xsum = reinterpret_cast<float *>(smem + (size_t)CP * 64);
   uint16_t *obuf = reinterpret_cast<uint16_t *>(smem + (size_t)CP * kChunkLdsBytes) +
                    (size_t)wave * kStreamRound;
+  uint32_t *sbt = reinterpret_cast<uint32_t *>(smem + (size_t)CP * kChunkLdsBytes +
+                                               (size_t)W * kStreamRound * 2) +
+                  (size_t)wave * (SL * 128 + 2);  // group g at entry 2 + g
+
+  // codes of one chunk of a row (chunk clamped to the last: padding lanes
+  // re-read it and multiply zeros)
+  auto load_codes = [&](PassData<BITS, 1> &d, int64_t row, int chunk) {
+    const uint32_t c = (uint32_t)(chunk < core.nch - 1 ? chunk : core.nch - 1);
+    load_chunk_g<BITS>(uniform_ptr(wt.codes + row * ((int64_t)core.nch * BITS)),
+                       c * (uint32_t)(BITS * 4), d.w[0]);
+  };
+  // lane l, load r: groups 2 j - odd and 2 j - odd + 1 of the row, j = l + 64 r,
+  // odd = 1 when the row starts 2 bytes into a dword (the scale and bias
+  // arrays are 16-byte aligned, so both rows start alike); returns odd.  The
+  // range is whole dwords, so a row ending mid-dword still reads its last
+  // group (the other half, past the row, lies in the same aligned dword as
+  // the array's own bytes and is never used).
+  auto stage_load = [&](int64_t row, uint32_t (&ss)[SL], uint32_t (&bb)[SL]) -> int {
+    const int64_t so = row * ng;
+    const int odd = (int)(so & 1);
+    const int bytes = ((ng + odd) * 2 + 3) & ~3;
+    const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(wt.scales + so - odd, bytes);
+    const __amdgpu_buffer_rsrc_t rb = uniform_rsrc(wt.biases ? wt.biases + so - odd : wt.scales,
+                                                   wt.biases ? bytes : 0);
+#pragma unroll
+    for (int r = 0; r < SL; ++r) {
+      ss[r] = __builtin_amdgcn_raw_buffer_load_b32(rs, (lane + 64 * r) * 4, 0, 0);
+      bb[r] = __builtin_amdgcn_raw_buffer_load_b32(rb, (lane + 64 * r) * 4, 0, 0);
+    }
+    return odd;
+  };
+  auto stage_store = [&](const uint32_t (&ss)[SL], const uint32_t (&bb)[SL], int odd) {
+    uint32_t *t = sbt + 2 - odd;
+#pragma unroll
+    for (int r = 0; r < SL; ++r) {
+      const int j = lane + 64 * r;
+      t[2 * j] = __builtin_amdgcn_perm(bb[r], ss[r], 0x05040100u);      // low halves
+      t[2 * j + 1] = __builtin_amdgcn_perm(bb[r], ss[r], 0x07060302u);  // high halves
+    }
+  };
 
   // x loads first, then the first round of weight loads, then the wait for
   // x: the two round trips overlap.  The first fill is unconditional (a wave
@@ -631,13 +687,17 @@ __global__ __launch_bounds__(64 * W) void qmv1_kernel(const uint16_t *__restrict
   stage_x_load<BITS, 1, XT, 64 * W, XS>(xr, 1, (int)(K >> 5), CP, xst);
   __builtin_amdgcn_sched_barrier(0);
   PassData<BITS, 1> buf[D];
+  uint32_t stg_s[UD][SL], stg_b[UD][SL];  // staged scale / bias dwords of the rows in flight
+  int stg_odd[UD];
   {
     const int nu = nunits < kStreamRound ? nunits : kStreamRound;
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const int i = d / CPL < nu ? d / CPL : (nu > 0 ? nu - 1 : 0);
-      const int64_t row = gw + (int64_t)i * TW;
-      core.load_pass(buf[d], row < N ? row : N - 1, (d % CPL) * 64 + lane);
+      int64_t row = gw + (int64_t)i * TW;
+      row = row < N ? row : N - 1;
+      if (d % CPL == 0) stg_odd[d / CPL] = stage_load(row, stg_s[d / CPL], stg_b[d / CPL]);
+      load_codes(buf[d], row, (d % CPL) * 64 + lane);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -665,13 +725,17 @@ __global__ __launch_bounds__(64 * W) void qmv1_kernel(const uint16_t *__restrict
     if (u0 > 0) {  // the first round was filled above
 #pragma unroll
       for (int d = 0; d < D; ++d) {
-        core.load_pass(buf[d], row_of(d / CPL), (d % CPL) * 64 + lane);
+        if (d % CPL == 0)
+          stg_odd[d / CPL] = stage_load(row_of(d / CPL), stg_s[d / CPL], stg_b[d / CPL]);
+        load_codes(buf[d], row_of(d / CPL), (d % CPL) * 64 + lane);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
     float acc = 0.f;
     auto consume = [&](const PassData<BITS, 1> &bb, int p, int unit) {
-      acc = chunk_dot<BITS, XT>(bb.w[0], bb.s[0], bb.b[0], xv[p], xs[p], acc, magic);
+      const int c = p * 64 + lane < core.nch - 1 ? p * 64 + lane : core.nch - 1;
+      const uint32_t sb = sbt[2 + (c >> core.gshift)];
+      acc = chunk_dot<BITS, XT>(bb.w[0], sb & 0xFFFFu, sb >> 16, xv[p], xs[p], acc, magic);
       if (p == CPL - 1) {
         const float v = wave_sum(acc);
         if (lane == 0) obuf[unit] = xtraits<XT>::from_f32(v);
@@ -682,13 +746,19 @@ __global__ __launch_bounds__(64 * W) void qmv1_kernel(const uint16_t *__restrict
     for (; i + UD <= nu; i += UD) {  // whole rings of UD rows
 #pragma unroll
       for (int d = 0; d < D; ++d) {
+        if (d % CPL == 0) stage_store(stg_s[d / CPL], stg_b[d / CPL], stg_odd[d / CPL]);
         consume(buf[d], d % CPL, i + d / CPL);
-        core.load_pass(buf[d], row_of(i + UD + d / CPL), (d % CPL) * 64 + lane);
+        if (d % CPL == 0)
+          stg_odd[d / CPL] = stage_load(row_of(i + UD + d / CPL), stg_s[d / CPL], stg_b[d / CPL]);
+        load_codes(buf[d], row_of(i + UD + d / CPL), (d % CPL) * 64 + lane);
       }
     }
 #pragma unroll
     for (int d = 0; d < D; ++d)  // the last < UD rows: already loaded
-      if (i + d / CPL < nu) consume(buf[d], d % CPL, i + d / CPL);
+      if (i + d / CPL < nu) {
+        if (d % CPL == 0) stage_store(stg_s[d / CPL], stg_b[d / CPL], stg_odd[d / CPL]);
+        consume(buf[d], d % CPL, i + d / CPL);
+      }
     __builtin_amdgcn_wave_barrier();
     for (int e = lane; e < nu; e += 64) y[gw + (int64_t)(u0 + e) * TW] = obuf[e];
     __builtin_amdgcn_wave_barrier();
@@ -781,25 +851,32 @@ template <> struct stream_shape<8> { static constexpr int R = 4, D = 2; };
 }  // namespace
 
 // M = 1 kernel shape: CPL 64-chunk passes per row, UD rows in flight per
-// wave, W waves per workgroup.  Measured on the MI355X (cold weights): at
-// K = 4096, 8-wave workgroups for N > 2048 and one row in flight per wave past
-// N = 8192 (the waves then outnumber a CU's rows enough to keep its loads in
-// flight); at K = 14336 (4096 rows), 4-wave workgroups (9.22 us against
-// 9.32 .. 9.46 with 8 waves and 10.1 with 2; two rows in flight per wave,
-// 9.6 .. 12.0).
-void qmv1_shape(int64_t N, int64_t K, int &cpl, int &ud, int &w) {
+// wave, W waves per workgroup, SL staging loads of scales (and of biases) per
+// lane and row.  Measured on the MI355X (cold weights): at K = 4096, 8-wave
+// workgroups for N > 2048 and one row in flight per wave past N = 8192 (the
+// waves then outnumber a CU's rows enough to keep its loads in flight); at
+// K = 14336 (4096 rows, 2 waves per SIMD), 8-wave workgroups 8.59 .. 8.75 us
+// against 8.59 .. 8.95 with 4 waves (two rows in flight per wave 10.4 .. 10.6),
+// and SL = 2 at G = 64 about 0.05 .. 0.1 us ahead of SL = 4.
+void qmv1_shape(int64_t N, int64_t K, int G, int &cpl, int &ud, int &w, int &sl) {
   cpl = (int)((K / 32 + 63) / 64);
   ud = cpl == 1 ? 4 : (cpl == 2 ? (N > 8192 ? 1 : 2) : 1);
-  w = cpl == 2 && N > 2048 ? 8 : 4;
+  // from 5 chunks per lane on, x in registers leaves room for 2 waves per
+  // SIMD: one workgroup of 8 waves per CU stages x once for all of them
+  w = (cpl == 2 && N > 2048) || cpl >= 5 ? 8 : 4;
+  // 4-byte staging loads per lane: 128 groups each, in powers of two
+  const int groups = (64 * cpl * 32) / G;
+  sl = groups <= 128 ? 1 : (groups <= 256 ? 2 : 4);
 }
 
 namespace {
 
-template <int BITS, typename XT, int CPL, int UD, int W = 4>
+template <int BITS, typename XT, int CPL, int UD, int W, int SL>
 hipError_t qmv1_launch(const void *x, const Weights &wt, int64_t N, int64_t K, int G, void *y,
                        hipStream_t s) {
-  auto kern = qmv1_kernel<BITS, XT, CPL, UD, W>;
-  const size_t lds = (size_t)64 * CPL * kChunkLdsBytes + (size_t)W * kStreamRound * 2;
+  auto kern = qmv1_kernel<BITS, XT, CPL, UD, W, SL>;
+  const size_t lds = (size_t)64 * CPL * kChunkLdsBytes + (size_t)W * kStreamRound * 2 +
+                     (size_t)W * (SL * 128 + 2) * 4;
   static int per_cu = 0;  // resident workgroups per CU for this instantiation
   if (per_cu == 0) {
     int v = 0;
@@ -816,24 +893,34 @@ hipError_t qmv1_launch(const void *x, const Weights &wt, int64_t N, int64_t K, i
   return hipGetLastError();
 }
 
+// CPL chunks per lane with the launch shape qmv1_shape picks
+template <int BITS, typename XT, int CPL, int UD, int W>
+hipError_t qmv1_launch_sl(int sl, const void *x, const Weights &wt, int64_t N, int64_t K, int G,
+                          void *y, hipStream_t s) {
+  constexpr int SLMAX = CPL <= 2 ? 1 : (CPL <= 4 ? 2 : 4);
+  if (sl == 1) return qmv1_launch<BITS, XT, CPL, UD, W, 1>(x, wt, N, K, G, y, s);
+  if (SLMAX >= 2 && sl == 2) return qmv1_launch<BITS, XT, CPL, UD, W, (SLMAX >= 2 ? 2 : 1)>(x, wt, N, K, G, y, s);
+  return qmv1_launch<BITS, XT, CPL, UD, W, SLMAX>(x, wt, N, K, G, y, s);
+}
+
 template <int BITS, typename XT>
 hipError_t qmv1_dispatch(const void *x, const Weights &wt, int64_t N, int64_t K, int G, void *y,
                          hipStream_t s) {
-  int cpl, ud, w;
-  qmv1_shape(N, K, cpl, ud, w);
+  int cpl, ud, w, sl;
+  qmv1_shape(N, K, G, cpl, ud, w, sl);
   switch (cpl) {
-    case 1: return qmv1_launch<BITS, XT, 1, 4>(x, wt, N, K, G, y, s);
+    case 1: return qmv1_launch_sl<BITS, XT, 1, 4, 4>(sl, x, wt, N, K, G, y, s);
     case 2:
       if (w == 8)
-        return ud == 1 ? qmv1_launch<BITS, XT, 2, 1, 8>(x, wt, N, K, G, y, s)
-                       : qmv1_launch<BITS, XT, 2, 2, 8>(x, wt, N, K, G, y, s);
-      return qmv1_launch<BITS, XT, 2, 2>(x, wt, N, K, G, y, s);
-    case 3: return qmv1_launch<BITS, XT, 3, 1>(x, wt, N, K, G, y, s);
-    case 4: return qmv1_launch<BITS, XT, 4, 1>(x, wt, N, K, G, y, s);
-    case 5: return qmv1_launch<BITS, XT, 5, 1>(x, wt, N, K, G, y, s);
-    case 6: return qmv1_launch<BITS, XT, 6, 1>(x, wt, N, K, G, y, s);
-    case 7: return qmv1_launch<BITS, XT, 7, 1>(x, wt, N, K, G, y, s);
-    case 8: return qmv1_launch<BITS, XT, 8, 1>(x, wt, N, K, G, y, s);
+        return ud == 1 ? qmv1_launch_sl<BITS, XT, 2, 1, 8>(sl, x, wt, N, K, G, y, s)
+                       : qmv1_launch_sl<BITS, XT, 2, 2, 8>(sl, x, wt, N, K, G, y, s);
+      return qmv1_launch_sl<BITS, XT, 2, 2, 4>(sl, x, wt, N, K, G, y, s);
+    case 3: return qmv1_launch_sl<BITS, XT, 3, 1, 4>(sl, x, wt, N, K, G, y, s);
+    case 4: return qmv1_launch_sl<BITS, XT, 4, 1, 4>(sl, x, wt, N, K, G, y, s);
+    case 5: return qmv1_launch_sl<BITS, XT, 5, 1, 8>(sl, x, wt, N, K, G, y, s);
+    case 6: return qmv1_launch_sl<BITS, XT, 6, 1, 8>(sl, x, wt, N, K, G, y, s);
+    case 7: return qmv1_launch_sl<BITS, XT, 7, 1, 8>(sl, x, wt, N, K, G, y, s);
+    case 8: return qmv1_launch_sl<BITS, XT, 8, 1, 8>(sl, x, wt, N, K, G, y, s);
   }
   return hipErrorInvalidValue;
 }

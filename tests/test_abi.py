@@ -179,6 +179,9 @@ def test_qmv_describe(lib):
     assert d(1, 4096, 4096, 64, 4).startswith("qmv1_kernel<BITS=4, f16, CPL=2")
     assert d(1, 14336, 4096, 64, 4) != d(1, 1024, 4096, 64, 4)
     assert "CPL=7" in d(1, 4096, 14336, 64, 4, "bf16")
+    assert d(1, 4096, 14336, 64, 4).endswith("W=8, SL=2>")
+    assert d(1, 4096, 14336, 32, 4).endswith("SL=4>")
+    assert d(1, 4096, 14336, 128, 8).endswith("SL=1>")
     assert d(4, 14336, 4096, 64, 4, "bf16").startswith("qmvm_kernel<bf16, BITS=4")
     assert d(3, 100, 256, 64, 3).startswith("qmv vector kernel")
     buf = ctypes.create_string_buffer(8)

@@ -382,6 +382,37 @@ def test_qmv_shapes(aq, xdt, N, K, G):
         _assert_close(y, y_ref, A, f"qmv N{N} K{K} M{M}")
 
 
+@pytest.mark.parametrize("bits", [3, 4, 8])
+@pytest.mark.parametrize("G", [32, 64, 128])
+@pytest.mark.parametrize("K", [9600, 14336, 16384])
+def test_qmv_decode_long_rows(aq, bits, G, K):
+    """M = 1 at 5..8 chunks per lane: 1, 2 and 4 staging loads of scales and
+    biases per lane and row (128 groups each), a ragged last pass (K = 9600:
+    300 chunks), and biases=None (a size-0 staging resource reads +0)."""
+    N = 45
+    _, (c, s, b) = _quantized(N, K, G, bits, seed=23)
+    zb = np.zeros_like(b)
+    xb = inputs.activations(1, K, "f16", seed=23, key=(bits, G, K))
+    x = bits_to_dev(xb, "f16")
+    y_ref, A = oracle.matmul(inputs.from_bits(xb, "f16"), c, s, b, K, G, bits)
+    dc, ds, db = packed_to_dev(c, s, b)
+    _assert_close(aq.aq_qmv(x, dc, ds, db, G, bits), y_ref, A, f"qmv1 b{bits} G{G} K{K}")
+    y_ref, A = oracle.matmul(inputs.from_bits(xb, "f16"), c, s, zb, K, G, bits)
+    _assert_close(aq.aq_qmv(x, dc, ds, None, G, bits), y_ref, A,
+                  f"qmv1 b{bits} G{G} K{K} no bias")
+
+
+def test_qmv_decode_many_rows_per_wave(aq):
+    """M = 1 with more rows per wave than one output round (32 rows): each
+    later round refills the ring, staged scales and biases included."""
+    N, K, G, bits = 300000, 64, 32, 4
+    _, (c, s, b) = _quantized(N, K, G, bits, seed=24)
+    xb = inputs.activations(1, K, "f16", seed=24)
+    y_ref, A = oracle.matmul(inputs.from_bits(xb, "f16"), c, s, b, K, G, bits)
+    y = aq.aq_qmv(bits_to_dev(xb, "f16"), *packed_to_dev(c, s, b), G, bits)
+    _assert_close(y, y_ref, A, "qmv1 many rows")
+
+
 @pytest.mark.parametrize("bits", [4, 8])
 @pytest.mark.parametrize("xdt,G,K", [(xdt, G, K) for G, K in ((32, 2144), (64, 2112), (128, 2176))
                                      for xdt in ("f16", "bf16")] + [("f16", 32, 96), ("f16", 64, 64)])
