@@ -527,14 +527,16 @@ __device__ __forceinline__ void reduce_out(float *part, int wave, int lane,
 // S > 1 (XR = 16 or 32): x has up to XR S rows, run as S slices of XR rows;
 // the S slices of one block of W rows are consecutive workgroups of one XCD
 // (block b runs on XCD b % 8), so that block is read from HBM once and the
-// other slices find it in that XCD's L2.
+// other slices find it in that XCD's L2.  Workgroup b covers rows
+// [b * stride, b * stride + stride), stride <= 16 R (rows past the stride or
+// past N read as zero and are not stored).
 template <typename XT, int BITS, int W, int GS, int XR, int R>
 __global__ __launch_bounds__(64 * W) void qmvm_kernel(const uint16_t *__restrict__ x, int M,
                                                       const uint32_t *__restrict__ codes,
                                                       const uint16_t *__restrict__ scales,
                                                       const uint16_t *__restrict__ biases,
                                                       int64_t N, int64_t K, int kw,
-                                                      uint16_t *__restrict__ y, int S) {
+                                                      uint16_t *__restrict__ y, int S, int stride) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // [2][16 R][gpr]; then partials
   typedef MBlock<XT, BITS, W, GS, XR, R> Blk;
   constexpr int MR = XR >= 16 ? XR : 8;
@@ -549,9 +551,9 @@ __global__ __launch_bounds__(64 * W) void qmvm_kernel(const uint16_t *__restrict
     y += (int64_t)sl * XR * N;
     M = M - XR * sl < XR ? M - XR * sl : XR;
   }
-  const int64_t row0 = rb * Blk::ROWS;
+  const int64_t row0 = rb * stride;
   if (row0 >= N) return;  // padding of the slice mapping (uniform, before any barrier)
-  const int64_t nrows = N - row0 < Blk::ROWS ? N - row0 : Blk::ROWS;
+  const int64_t nrows = N - row0 < stride ? N - row0 : stride;
   const int64_t gpr = (K >> 5) >> GS;
   Blk blk;
   blk.setup(codes + row0 * (K >> 5) * BITS, nrows, K, kw, wave, lane, lds,
@@ -570,7 +572,7 @@ __global__ __launch_bounds__(64 * W) void qmvm_kernel(const uint16_t *__restrict
   blk.template finish<D>(st, acc);
   __syncthreads();  // every wave is done with the staged scales
   reduce_out<W, R, MR, Blk::XS>(reinterpret_cast<float *>(lds), wave, lane, acc, [&](int nn, int m, float v) {
-    if (m < M && row0 + nn < N) y[(int64_t)m * N + row0 + nn] = xtraits<XT>::from_f32(v);
+    if (m < M && nn < nrows) y[(int64_t)m * N + row0 + nn] = xtraits<XT>::from_f32(v);
   });
 }
 
@@ -684,16 +686,27 @@ hipError_t qmvm_go(const void *x, int M, const uint32_t *codes, const uint16_t *
                    const uint16_t *biases, int64_t N, int64_t K, int G, void *y, hipStream_t s) {
   const int64_t steps = (K + kStepK - 1) / kStepK;
   const int kw = (int)((steps + W - 1) / W) * kStepK;  // k per wave, whole steps
-  const int64_t blocks = (N + 16 * R - 1) / (16 * R);
   const int S = XR >= 16 ? (M + XR - 1) / XR : 1;  // slices of XR x rows
+  // rows per workgroup: 16 R, except for tall matrices with one slice, where
+  // the rows are dealt evenly over a whole number of workgroups per compute
+  // unit (14336 rows: 512 workgroups of 28 rather than 448 of 32, which left
+  // 192 compute units two workgroups and 64 one; each compute unit's
+  // second workgroup cost about 4.5 us)
+  int stride = 16 * R;
+  if (S == 1 && R == 2) {
+    const int64_t cus = device_cus();
+    const int64_t per_cu = (N + 32 * cus - 1) / (32 * cus);
+    stride = (int)((N + per_cu * cus - 1) / (per_cu * cus));
+  }
+  const int64_t blocks = (N + stride - 1) / stride;
   const int64_t grid_blocks = S > 1 ? (blocks + 7) / 8 * 8 * S : blocks;
   if (grid_blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid((unsigned)grid_blocks), block(64 * W);
   const size_t lds = qmvm_lds_bytes(W, R, K, G, XR >= 16 ? XR : 8);
   switch (G) {
-    case 32: hipLaunchKernelGGL((qmvm_kernel<XT, BITS, W, 0, XR, R>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y, S); break;
-    case 64: hipLaunchKernelGGL((qmvm_kernel<XT, BITS, W, 1, XR, R>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y, S); break;
-    case 128: hipLaunchKernelGGL((qmvm_kernel<XT, BITS, W, 2, XR, R>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y, S); break;
+    case 32: hipLaunchKernelGGL((qmvm_kernel<XT, BITS, W, 0, XR, R>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y, S, stride); break;
+    case 64: hipLaunchKernelGGL((qmvm_kernel<XT, BITS, W, 1, XR, R>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y, S, stride); break;
+    case 128: hipLaunchKernelGGL((qmvm_kernel<XT, BITS, W, 2, XR, R>), grid, block, lds, s, (const uint16_t *)x, M, codes, scales, biases, N, K, kw, (uint16_t *)y, S, stride); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -766,21 +779,27 @@ void qmvm_shape(int M, int bits, int64_t N, int64_t K, int G, int &R, int &W, in
       return;
     }
   }
-  // Tall matrices: 2 blocks of 16 rows per workgroup (half the x loads per
-  // weight byte) with K split over 8 waves.  Otherwise one block, K split
-  // over W waves so that the grid has about four waves per SIMD (each wave
-  // then runs a few steps).  Measured on the MI355X at N x K = 14336 x 4096
-  // and 4096 x 14336, M = 2..8: more blocks per workgroup leave too few
-  // waves, deeper load pipelines gain nothing; 8-bit steps carry twice the
-  // bytes and run best with half the waves.
+  // Tall matrices: up to 2 blocks of 16 rows per workgroup (half the x loads
+  // per weight byte), rows dealt evenly (qmvm_go), K split over 4 waves
+  // (measured at 14336 x 4096, M = 2 / 8: 4-bit 12.0 / 12.1 us against
+  // 12.8 / 13.7 with 8 waves and 32-row workgroups; 8-bit 13.7 / 14.9 against
+  // 14.1 / 16.0).  Otherwise one block, K split over W waves so that the grid
+  // has about four waves per SIMD (each wave then runs a few steps).
+  // Measured on the MI355X at N x K = 14336 x 4096 and 4096 x 14336,
+  // M = 2..8: more blocks per workgroup leave too few waves, deeper load
+  // pipelines gain nothing; 8-bit steps carry twice the bytes and run best
+  // with half the waves.
   const int64_t target = 4 * 4 * (int64_t)device_cus();
-  R = XR < 16 && N >= 8192 && qmvm_lds_bytes(8, 2, K, G) <= kMaxStagedLds ? 2 : 1;
+  R = XR < 16 && N >= 8192 && qmvm_lds_bytes(4, 2, K, G) <= kMaxStagedLds ? 2 : 1;
+  if (R == 2) {
+    W = 4;
+    return;
+  }
   // workgroups: row blocks, times the slices
-  const int64_t rowblocks = (N + 16 * R - 1) / (16 * R) * S;
-  W = R == 2 ? 8
-             : rowblocks * 2 >= target ? 2
-             : rowblocks * 4 >= target ? 4
-             : rowblocks * 8 >= target ? 8 : 16;
+  const int64_t rowblocks = (N + 15) / 16 * S;
+  W = rowblocks * 2 >= target ? 2
+      : rowblocks * 4 >= target ? 4
+      : rowblocks * 8 >= target ? 8 : 16;
   if (bits == 8 && W > 2) W /= 2;
 }
 
@@ -798,7 +817,6 @@ hipError_t launch_qmvm(const void *x, int x_dtype, int M, const uint32_t *codes,
   }
 #define AQ_QMVM_R(T, B, XR) \
   if (R == 2) { \
-    if (W == 8) return qmvm_go<T, B, 8, XR, 2>(x, M, codes, scales, biases, N, K, G, y, s); \
     return qmvm_go<T, B, 4, XR, 2>(x, M, codes, scales, biases, N, K, G, y, s); \
   } else { AQ_QMVM_W(T, B, XR, 1) }
 #define AQ_QMVM(T) \
