@@ -355,24 +355,29 @@ def _mfma_clock(aq, torch, cus):
 
 def _traffic(kname, group):
     """HBM bytes per launch of the roofline kernel from the committed counter
-    summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size),
-    or None when no summary for the current kernel source exists."""
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size;
+    one line per decode instantiation), or None when the summary was taken
+    on another kernel source or does not cover this kernel."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "qmv_decode_m1_traffic.txt")
     src = os.path.join(ROOT, "group_wise_affine_aq_amd", "csrc", "aq_qmv.hip")
     if not os.path.exists(path):
         return None
-    kv = {}
+    sha, per_kernel = None, {}
     for line in open(path):
-        if ":" in line and not line.startswith("#"):
-            k, v = line.split(":", 1)
-            kv[k.strip()] = v.strip()
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if kv.get("source_sha256_16") != sha or kv.get("kernel") != kname:
+        if line.startswith("#") or ":" not in line:
+            continue
+        k, v = line.rsplit(":", 1)
+        k, v = k.strip(), v.strip()
+        if k == "source_sha256_16":
+            sha = v
+        elif k.startswith("hbm_bytes_per_launch "):
+            per_kernel[k[len("hbm_bytes_per_launch "):]] = v
+    if sha != hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] or kname not in per_kernel:
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
+        return float(per_kernel[kname])
+    except ValueError:
         return None
 
 
