@@ -202,8 +202,8 @@ int aq_qmv_describe(int64_t M, int64_t N, int64_t K, int group_size, int bits, a
     return -1;
   const char *xt = x_dtype == AQ_F16 ? "f16" : "bf16";
   if (M == 1 && K <= 8 * 2048) {
-    int cpl, ud, w, sl;
-    aq::qmv1_shape(N, K, group_size, cpl, ud, w, sl);
+    int cpl, ud, w, sl, wpc;
+    aq::qmv1_shape(N, K, group_size, cpl, ud, w, sl, wpc);
     return snprintf(buf, (size_t)len, "qmv1_kernel<BITS=%d, %s, CPL=%d, UD=%d, W=%d, SL=%d>", bits,
                     xt, cpl, ud, w, sl);
   }

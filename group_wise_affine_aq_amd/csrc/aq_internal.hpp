@@ -49,7 +49,7 @@ bool qmvm_supported(int M, int bits, int64_t N, int64_t K, int G);
 bool qmvm_preferred(int64_t M, int bits, int64_t N, int64_t K, int G);
 // launch shapes the kernels use (also reported by aq_qmv_describe)
 void qmvm_shape(int M, int bits, int64_t N, int64_t K, int G, int &R, int &W, int &XR);
-void qmv1_shape(int64_t N, int64_t K, int G, int &cpl, int &ud, int &w, int &sl);
+void qmv1_shape(int64_t N, int64_t K, int G, int &cpl, int &ud, int &w, int &sl, int &wpc);
 hipError_t launch_qmvm(const void *x, int x_dtype, int M, const uint32_t *codes,
                        const uint16_t *scales, const uint16_t *biases, int64_t N, int64_t K, int G,
                        int bits, void *y, hipStream_t s);

@@ -852,18 +852,33 @@ template <> struct stream_shape<8> { static constexpr int R = 4, D = 2; };
 
 // M = 1 kernel shape: CPL 64-chunk passes per row, UD rows in flight per
 // wave, W waves per workgroup, SL staging loads of scales (and of biases) per
-// lane and row.  Measured on the MI355X (cold weights): at K = 4096, 8-wave
-// workgroups for N > 2048 and one row in flight per wave past N = 8192 (the
-// waves then outnumber a CU's rows enough to keep its loads in flight); at
-// K = 14336 (4096 rows, 2 waves per SIMD), 8-wave workgroups 8.59 .. 8.75 us
-// against 8.59 .. 8.95 with 4 waves (two rows in flight per wave 10.4 .. 10.6),
-// and SL = 2 at G = 64 about 0.05 .. 0.1 us ahead of SL = 4.
-void qmv1_shape(int64_t N, int64_t K, int G, int &cpl, int &ud, int &w, int &sl) {
+// lane and row, and at most WPC workgroups per CU (0: as many as fit).
+// Measured on the MI355X (4-bit, cold weights; µs): at K = 4096 fewer waves
+// than fit run faster -- 14336 rows: 4-wave workgroups, 3 per CU (3072
+// waves) 7.88 .. 8.07, against 8.31 .. 8.42 with 6144 waves (8-wave
+// workgroups, all that fit) and 8.05 .. 8.21 with 4096; 4096 rows: one
+// 16-wave workgroup per CU, a row per wave, 4.08 .. 4.12, against
+// 4.38 .. 4.51 with 2 rows in flight per wave on 8-wave workgroups;
+// 1024 rows: one or two rows in flight per wave, 3.14 .. 3.20 either way.
+// At K = 14336 (4096 rows, 2 waves per SIMD), 8-wave workgroups
+// 8.59 .. 8.75 us against 8.59 .. 8.95 with 4 waves (two rows in flight per
+// wave 10.4 .. 10.6), and SL = 2 at G = 64 about 0.05 .. 0.1 us ahead of
+// SL = 4.
+void qmv1_shape(int64_t N, int64_t K, int G, int &cpl, int &ud, int &w, int &sl, int &wpc) {
   cpl = (int)((K / 32 + 63) / 64);
-  ud = cpl == 1 ? 4 : (cpl == 2 ? (N > 8192 ? 1 : 2) : 1);
-  // from 5 chunks per lane on, x in registers leaves room for 2 waves per
-  // SIMD: one workgroup of 8 waves per CU stages x once for all of them
-  w = (cpl == 2 && N > 2048) || cpl >= 5 ? 8 : 4;
+  ud = cpl == 1 ? 4 : (cpl == 2 && N <= 2048 ? 2 : 1);  // (1 and 2 measured alike at 1024 rows)
+  wpc = 0;
+  if (cpl == 2 && N > 8192) {
+    w = 4;
+    wpc = 3;
+  } else if (cpl == 2 && N > 2048) {
+    w = 16;
+    wpc = 1;
+  } else {
+    // from 5 chunks per lane on, x in registers leaves room for 2 waves per
+    // SIMD: one workgroup of 8 waves per CU stages x once for all of them
+    w = cpl >= 5 ? 8 : 4;
+  }
   // 4-byte staging loads per lane: 128 groups each, in powers of two
   const int groups = (64 * cpl * 32) / G;
   sl = groups <= 128 ? 1 : (groups <= 256 ? 2 : 4);
@@ -873,7 +888,7 @@ namespace {
 
 template <int BITS, typename XT, int CPL, int UD, int W, int SL>
 hipError_t qmv1_launch(const void *x, const Weights &wt, int64_t N, int64_t K, int G, void *y,
-                       hipStream_t s) {
+                       int wpc, hipStream_t s) {
   auto kern = qmv1_kernel<BITS, XT, CPL, UD, W, SL>;
   const size_t lds = (size_t)64 * CPL * kChunkLdsBytes + (size_t)W * kStreamRound * 2 +
                      (size_t)W * (SL * 128 + 2) * 4;
@@ -886,7 +901,7 @@ hipError_t qmv1_launch(const void *x, const Weights &wt, int64_t N, int64_t K, i
     per_cu = v;
   }
   const int64_t want = (N + W - 1) / W;
-  const int64_t cap = (int64_t)device_cus() * per_cu;
+  const int64_t cap = (int64_t)device_cus() * (wpc > 0 && wpc < per_cu ? wpc : per_cu);
   const dim3 grid((unsigned)(want < cap ? want : cap));
   hipLaunchKernelGGL(kern, grid, dim3(64 * W), lds, s, (const uint16_t *)x, wt, N, K, G,
                      (uint16_t *)y);
@@ -895,33 +910,35 @@ hipError_t qmv1_launch(const void *x, const Weights &wt, int64_t N, int64_t K, i
 
 // CPL chunks per lane with the launch shape qmv1_shape picks
 template <int BITS, typename XT, int CPL, int UD, int W>
-hipError_t qmv1_launch_sl(int sl, const void *x, const Weights &wt, int64_t N, int64_t K, int G,
-                          void *y, hipStream_t s) {
+hipError_t qmv1_launch_sl(int sl, int wpc, const void *x, const Weights &wt, int64_t N, int64_t K,
+                          int G, void *y, hipStream_t s) {
   constexpr int SLMAX = CPL <= 2 ? 1 : (CPL <= 4 ? 2 : 4);
-  if (sl == 1) return qmv1_launch<BITS, XT, CPL, UD, W, 1>(x, wt, N, K, G, y, s);
-  if (SLMAX >= 2 && sl == 2) return qmv1_launch<BITS, XT, CPL, UD, W, (SLMAX >= 2 ? 2 : 1)>(x, wt, N, K, G, y, s);
-  return qmv1_launch<BITS, XT, CPL, UD, W, SLMAX>(x, wt, N, K, G, y, s);
+  if (sl == 1) return qmv1_launch<BITS, XT, CPL, UD, W, 1>(x, wt, N, K, G, y, wpc, s);
+  if (SLMAX >= 2 && sl == 2)
+    return qmv1_launch<BITS, XT, CPL, UD, W, (SLMAX >= 2 ? 2 : 1)>(x, wt, N, K, G, y, wpc, s);
+  return qmv1_launch<BITS, XT, CPL, UD, W, SLMAX>(x, wt, N, K, G, y, wpc, s);
 }
 
 template <int BITS, typename XT>
 hipError_t qmv1_dispatch(const void *x, const Weights &wt, int64_t N, int64_t K, int G, void *y,
                          hipStream_t s) {
-  int cpl, ud, w, sl;
-  qmv1_shape(N, K, G, cpl, ud, w, sl);
+  int cpl, ud, w, sl, wpc;
+  qmv1_shape(N, K, G, cpl, ud, w, sl, wpc);
+#define AQ_QMV1(C, U, WW) return qmv1_launch_sl<BITS, XT, C, U, WW>(sl, wpc, x, wt, N, K, G, y, s)
   switch (cpl) {
-    case 1: return qmv1_launch_sl<BITS, XT, 1, 4, 4>(sl, x, wt, N, K, G, y, s);
+    case 1: AQ_QMV1(1, 4, 4);
     case 2:
-      if (w == 8)
-        return ud == 1 ? qmv1_launch_sl<BITS, XT, 2, 1, 8>(sl, x, wt, N, K, G, y, s)
-                       : qmv1_launch_sl<BITS, XT, 2, 2, 8>(sl, x, wt, N, K, G, y, s);
-      return qmv1_launch_sl<BITS, XT, 2, 2, 4>(sl, x, wt, N, K, G, y, s);
-    case 3: return qmv1_launch_sl<BITS, XT, 3, 1, 4>(sl, x, wt, N, K, G, y, s);
-    case 4: return qmv1_launch_sl<BITS, XT, 4, 1, 4>(sl, x, wt, N, K, G, y, s);
-    case 5: return qmv1_launch_sl<BITS, XT, 5, 1, 8>(sl, x, wt, N, K, G, y, s);
-    case 6: return qmv1_launch_sl<BITS, XT, 6, 1, 8>(sl, x, wt, N, K, G, y, s);
-    case 7: return qmv1_launch_sl<BITS, XT, 7, 1, 8>(sl, x, wt, N, K, G, y, s);
-    case 8: return qmv1_launch_sl<BITS, XT, 8, 1, 8>(sl, x, wt, N, K, G, y, s);
+      if (w == 16) AQ_QMV1(2, 1, 16);
+      if (ud == 1) AQ_QMV1(2, 1, 4);
+      AQ_QMV1(2, 2, 4);
+    case 3: AQ_QMV1(3, 1, 4);
+    case 4: AQ_QMV1(4, 1, 4);
+    case 5: AQ_QMV1(5, 1, 8);
+    case 6: AQ_QMV1(6, 1, 8);
+    case 7: AQ_QMV1(7, 1, 8);
+    case 8: AQ_QMV1(8, 1, 8);
   }
+#undef AQ_QMV1
   return hipErrorInvalidValue;
 }
 
