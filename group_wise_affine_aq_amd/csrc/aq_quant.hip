@@ -226,19 +226,20 @@ __global__ __launch_bounds__(256) void quantize_mse_kernel(const void *__restric
                                                            uint32_t *__restrict__ codes,
                                                            uint16_t *__restrict__ scales,
                                                            uint16_t *__restrict__ biases) {
-  const int64_t opr = K >> 3;
-  const int64_t total = N * opr;
+  // the thread mapping of quantize_kernel: one 32-weight chunk per thread
+  const int64_t cpr = K >> 5;
+  const int64_t total = N * cpr;
   int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const bool active = idx < total;
   if (!active) idx = total - 1;
-  const int64_t n = idx / opr, o = idx - n * opr;
+  const int64_t n = idx / cpr, o = idx - n * cpr;
 
-  float v[8];
-  load8<WDT>(w, n * K + o * 8, v);
+  float v[32];
+  load32<WDT>(w, n * K + o * 32, v);
   float lo = v[0], hi = v[0];
 #pragma unroll
-  for (int i = 1; i < 8; ++i) { lo = fminf(lo, v[i]); hi = fmaxf(hi, v[i]); }
-  const int lanes = G >> 3;
+  for (int i = 1; i < 32; ++i) { lo = fminf(lo, v[i]); hi = fmaxf(hi, v[i]); }
+  const int lanes = G >> 5;
   for (int d = 1; d < lanes; d <<= 1) {
     lo = fminf(lo, __shfl_xor(lo, d));
     hi = fmaxf(hi, __shfl_xor(hi, d));
@@ -246,7 +247,9 @@ __global__ __launch_bounds__(256) void quantize_mse_kernel(const void *__restric
   constexpr int L = (1 << BITS) - 1;
   double best = __builtin_inf();
   uint16_t best_b = 0, best_s = 0;
-  uint64_t best_packed = 0;
+  uint32_t best_w[BITS];
+#pragma unroll
+  for (int j = 0; j < BITS; ++j) best_w[j] = 0;
   const double width = (double)hi - (double)lo;
   for (int i = 0; i < steps; ++i) {
     double clo, chi;
@@ -262,14 +265,18 @@ __global__ __launch_bounds__(256) void quantize_mse_kernel(const void *__restric
     const double s = h2d(s16);
     const float bf = (float)b;
     const float rs = s16 ? __builtin_amdgcn_rcpf((float)s) : 0.f;
-    uint64_t packed = 0;
+    uint32_t words[BITS];
+#pragma unroll
+    for (int j = 0; j < BITS; ++j) words[j] = 0;
     double e = 0.0;
     {
 #pragma clang fp contract(off)
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
+      for (int k = 0; k < 32; ++k) {
         const uint32_t q = nearest_code(v[k], b, s, bf, rs, L);
-        packed |= (uint64_t)q << (BITS * k);
+        const int bit = k * BITS, wi = bit >> 5, sh = bit & 31;
+        words[wi] |= q << sh;
+        if (sh + BITS > 32) words[wi + 1] |= q >> (32 - sh);
         const double dv = (double)v[k] - (b + (double)q * s);
         e = e + dv * dv;
       }
@@ -279,19 +286,20 @@ __global__ __launch_bounds__(256) void quantize_mse_kernel(const void *__restric
       best = e;
       best_b = b16;
       best_s = s16;
-      best_packed = packed;
+#pragma unroll
+      for (int j = 0; j < BITS; ++j) best_w[j] = words[j];
     }
   }
 
   if (!active) return;
   if ((o & (lanes - 1)) == 0) {
-    const int64_t gi = n * (K / G) + (o * 8) / G;
+    const int64_t gi = n * (K / G) + (o * 32) / G;
     scales[gi] = best_s;
     biases[gi] = best_b;
   }
-  uint8_t *dst = reinterpret_cast<uint8_t *>(codes + n * (K * BITS / 32)) + o * BITS;
+  uint32_t *dst = codes + n * (K * BITS / 32) + o * BITS;
 #pragma unroll
-  for (int j = 0; j < BITS; ++j) dst[j] = (uint8_t)(best_packed >> (8 * j));
+  for (int j = 0; j < BITS; ++j) dst[j] = best_w[j];
 }
 
 // Smallest u in [0, cap] with u s >= t (t >= 0, s > 0), or cap + 1 when
@@ -510,7 +518,7 @@ hipError_t quantize_w(const void *w, int64_t N, int64_t K, int G, int bits, uint
 template <int WDT>
 hipError_t quantize_mse_w(const void *w, int64_t N, int64_t K, int G, int bits, int steps,
                           uint32_t *codes, uint16_t *scales, uint16_t *biases, hipStream_t s) {
-  const int64_t total = N * (K / 8);
+  const int64_t total = N * (K / 32);
   const dim3 grid((unsigned)((total + 255) / 256)), block(256);
 #define AQ_Q(B) case B: hipLaunchKernelGGL((quantize_mse_kernel<WDT, B>), grid, block, 0, s, w, N, K, G, steps, codes, scales, biases); break;
   switch (bits) {
