@@ -21,7 +21,7 @@ first part).  The JSON line also carries:
                 back-to-back launches) vs 8 TB/s, and its HBM traffic per
                 launch from the committed counter summary when it matches the
                 current kernel source;
-  cpu_baseline  the CPU reference computing the same decode step on the host
+  cpu_baseline  the CPU oracle computing the same decode step on the host
                 cores (value), with "legs" timing it beside every other
                 section on bounded samples of the same inputs: spec-decode
                 (M = 4), MoE gather, quantize, prefill (a few rows of X
@@ -267,7 +267,7 @@ def main():
             bb.copy_(a)
         torch.cuda.synchronize()
 
-    # ---- CPU baseline: the CPU reference on the same step -----------------------------------
+    # ---- CPU baseline: the CPU oracle on the same step -----------------------------------
     legs = None
     if not args.no_cpu:
         result["cpu_baseline"] = _cpu_baseline(mats, args.cpu_seconds)
@@ -382,7 +382,7 @@ def _traffic(kname, group):
 
 
 def _host_packed(c, s, b):
-    """Device packed weights -> the reference's numpy arrays."""
+    """Device packed weights -> the oracle's numpy arrays."""
     import numpy as np
     import torch
     return (c.cpu().numpy().view(np.uint32), s.view(torch.int16).cpu().numpy().view(np.uint16),
@@ -420,7 +420,7 @@ def _cpu_model():
 
 
 def _cpu_baseline(mats, seconds):
-    """The reference on the decode step (all host threads OpenMP gives it), and
+    """The oracle on the decode step (all host threads OpenMP gives it), and
     the single-thread tiny case; the other sections add their legs."""
     import oracle
     from group_wise_affine_aq_amd import inputs as _inp
@@ -449,7 +449,7 @@ def _cpu_baseline(mats, seconds):
         "workload": "W [512,512] 4-bit G=64, x fp16 [1,512]", "threads": 1,
         "us_per_call": round(t1 / runs * 1e6, 1), "gbs": round(tiny_bytes * runs / t1 / 1e9, 3),
         "sample": f"{runs} calls in {t1:.1f} s"}}
-    print(f"# CPU reference: decode {cpu_gbs:.3f} GB/s on {threads} threads; tiny case "
+    print(f"# CPU oracle: decode {cpu_gbs:.3f} GB/s on {threads} threads; tiny case "
           f"{legs['tiny_single_thread']['us_per_call']} us on one thread", file=sys.stderr,
           flush=True)
     return {"value": round(cpu_gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
@@ -515,7 +515,7 @@ def _specdec(aq, inputs, dev, stream, legs=None):
             out[f"{N}x{K}_b{bits}_g{g}"] = dict(weight_bytes=wbytes,
                                                 read_ceiling_us=round(ceil_us, 3), **rows)
             if legs is not None and "specdec" not in legs:
-                # the reference on the first matrix, M = 4 rows of the same x
+                # the oracle on the first matrix, M = 4 rows of the same x
                 import oracle
                 M = 4
                 x = inputs.activations_device(M, K, "bf16", device=dev, seed=0, key=(wid, N, M))
@@ -630,7 +630,7 @@ def _quant_dequant(aq, inputs, dev, stream, legs=None):
                            "gbs": round(nb / (us * 1e-6) / 1e9, 1),
                            "weights_per_s": round(N * K / (us * 1e-6), 1)}
     if legs is not None:
-        # the reference quantizer on the first 1024 rows of the same W
+        # the oracle quantizer on the first 1024 rows of the same W
         import oracle
         rows = 1024
         hw = w[:rows].cpu().numpy()
@@ -730,7 +730,7 @@ def _qmm(aq, inputs, dev, iters, legs=None):
         print(f"# QMM {bits}-bit G={g}: {avg:.3f} ms (median {med:.3f}), {tf:.1f} TFLOP/s",
               file=sys.stderr, flush=True)
         if legs is not None and "qmm" not in legs:
-            # the reference on the first 4 rows of X against all of W
+            # the oracle on the first 4 rows of X against all of W
             import oracle
             Ms = 4
             hx, hp = _host_x(x[:Ms], "bf16"), _host_packed(c, s, b)

@@ -2,7 +2,7 @@
 
 This module only draws random numbers and converts between number formats;
 it holds none of the quantization arithmetic.  Both the HIP path and the CPU
-reference consume exactly the arrays made here.
+oracle consume exactly the arrays made here.
 
 Generator: numpy ``PCG64`` seeded through ``SeedSequence(seed, spawn_key=...)``
 so that every (workload, tensor role, shape) draws from its own substream.

@@ -1,4 +1,4 @@
-"""CPU reference ("oracle") for group-wise affine quantization.
+"""CPU oracle for group-wise affine quantization.
 
 TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by ``__graft_entry__.smoke()``
 and by the CPU-baseline leg of ``bench.py``.  The product library never
@@ -97,7 +97,7 @@ def num_threads() -> int:
 
 # --- scalar number-format helpers -------------------------------------------
 def set_num_threads(n: int) -> None:
-    """Threads used by the reference's parallel loops from now on."""
+    """Threads used by the oracle's parallel loops from now on."""
     _load().oracle_set_num_threads(int(n))
 
 
@@ -272,7 +272,7 @@ def matmul(x: np.ndarray, codes, scales, biases, K: int, group_size: int, bits: 
 
 def gather_matmul(x: np.ndarray, codes, scales, biases, ids: np.ndarray, K: int, group_size: int,
                   bits: int):
-    """MoE reference: y[t, j, :] = x[t] @ W_{ids[t, j]}^T; returns (y, A) [T, topk, N]."""
+    """MoE oracle: y[t, j, :] = x[t] @ W_{ids[t, j]}^T; returns (y, A) [T, topk, N]."""
     x = np.ascontiguousarray(x, dtype=np.float64)
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     T, topk = ids.shape

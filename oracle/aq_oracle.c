@@ -1,5 +1,5 @@
 /*
- * aq_oracle.c -- CPU reference ("oracle") for group-wise affine weight-only
+ * aq_oracle.c -- CPU oracle for group-wise affine weight-only
  * quantization and the matmul that consumes the packed form.
  *
  * TEST INFRASTRUCTURE ONLY.  This file is used by the test-suite, by the
@@ -46,7 +46,7 @@
  *  R4  dequantize follows [T10] s.3 operation order: q*scale + bias
  *      evaluated in binary32 (q*scale is exact, so only the add rounds),
  *      then a round-to-nearest-even cast to the output type.
- *  R5  matmul reference: y[m,n] = sum_k x[m,k] * w^[n,k] with w^ the exact
+ *  R5  matmul oracle: y[m,n] = sum_k x[m,k] * w^[n,k] with w^ the exact
  *      value q*scale + bias, products and sums in binary64; the companion
  *      A[m,n] = sum_k |x[m,k] * w^[n,k]| scales the tolerance.
  *  R6  gather (MoE): y[t,j,:] = x[t,:] @ W_{ids[t,j]}^T, one output per
@@ -589,7 +589,7 @@ int oracle_embedding(const uint32_t *codes, const uint16_t *scales, const uint16
 }
 
 /* ---------------------------------------------------------------------
- * Matmul reference ([T10] s.5 Approach 1: dequantize then multiply;
+ * Matmul oracle ([T10] s.5 Approach 1: dequantize then multiply;
  * reading R5).  x holds the exact activation values as binary64.
  * Only the output columns listed in `cols` (nc of them) are computed, so
  * large shapes can be checked on a sample; y and A are [M, nc].

@@ -10,4 +10,4 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
-    config.addinivalue_line("markers", "slow: large CPU-side reference work")
+    config.addinivalue_line("markers", "slow: large CPU-side oracle work")

@@ -1,11 +1,11 @@
 """Host-code sanitizer run: AddressSanitizer + UndefinedBehaviorSanitizer
-builds of the CPU reference (gcc) and of libaq's host code (hipcc, the flags
+builds of the CPU oracle (gcc) and of libaq's host code (hipcc, the flags
 given to the host pass only), then the CPU tests against them.
 
     python tests/run_sanitizers.py
 
 The two libraries use different sanitizer runtimes (gcc's and clang's), so
-the reference's tests and the C-ABI tests run in two pytest processes, each
+the oracle's tests and the C-ABI tests run in two pytest processes, each
 with its runtime preloaded into the (uninstrumented) Python interpreter.
 Device code is built as usual; sanitizers are not available for it.  Exit
 status: 0 when both runs pass.
@@ -77,7 +77,7 @@ def main() -> int:
                              "LD_PRELOAD": f"{gcc_asan}:{gcc_ubsan}"})
     rc2 = run([os.path.join(ROOT, "tests", "test_abi.py")],
               {"AQ_LIB": aq_lib, "LD_PRELOAD": clang_rt[-1]})
-    print(f"sanitized runs: reference tests rc={rc1}, C-ABI tests rc={rc2}")
+    print(f"sanitized runs: oracle tests rc={rc1}, C-ABI tests rc={rc2}")
     return 0 if rc1 == 0 and rc2 == 0 else 1
 
 

@@ -1,10 +1,10 @@
-"""GPU parity of every libaq entry point against the CPU reference, on seeded
-inputs at sizes the reference finishes in seconds, spanning several tiles,
+"""GPU parity of every libaq entry point against the CPU oracle, on seeded
+inputs at sizes the oracle finishes in seconds, spanning several tiles,
 slices and ragged tails, across all bit widths, group sizes and dtypes.
 
 Bar: quantize and dequantize bit-exact; matmuls |y - y_ref| <= 2^-9*A + 1e-6
-per element with A = sum_k |x_k * w^_k| (w^ the reference's dequantized
-weight).  Inputs come only from the seeded generator and the reference."""
+per element with A = sum_k |x_k * w^_k| (w^ the oracle's dequantized
+weight).  Inputs come only from the seeded generator and the oracle."""
 import numpy as np
 import pytest
 
@@ -52,10 +52,10 @@ def test_quantize_bitexact_f32(aq, bits, G):
 
 
 def _check_mse(w, G, bits, steps, got):
-    """Range search: bit-exact with the reference wherever both pick the same
+    """Range search: bit-exact with the oracle wherever both pick the same
     candidate; elsewhere the device's candidate must tie the least error up to
     the rounding of the binary64 sums (the two add in different orders), and
-    its scale, bias and codes must be exactly the reference's for it."""
+    its scale, bias and codes must be exactly the oracle's for it."""
     c, s, b, chosen, errs = oracle.quantize_mse(w, G, bits, steps, details=True)
     gc, gs, gb = got
     K = w.shape[1]
@@ -92,7 +92,7 @@ def test_quantize_mse(aq, bits, G):
 @pytest.mark.parametrize("G", [32, 128])
 def test_quantize_mse_same_sign_groups(aq, bits, G):
     """Groups whose members all share a sign (alternating positive and
-    negative, some with one far member): the device follows the reference,
+    negative, some with one far member): the device follows the oracle,
     and its grids never reach below the min-max grid's bias nor use a larger
     scale (every candidate range lies inside [min, max])."""
     N, K, steps = 21, 6 * G, 50
@@ -169,7 +169,7 @@ def _zp_from_dev(got):
 @pytest.mark.parametrize("bits", ALL_BITS)
 @pytest.mark.parametrize("G", [32, 64, 128])
 def test_quantize_zp_bitexact(aq, bits, G):
-    """Codes, scales, biases and zero points bit-exact with the reference, on
+    """Codes, scales, biases and zero points bit-exact with the oracle, on
     Gaussian rows with outliers and on groups whose members share a sign."""
     N, K = 37, 6 * G
     w = np.concatenate([inputs.weights(N - 8, K, seed=40, key=(G, bits), outliers=True),
@@ -225,7 +225,7 @@ def test_quantize_zp_without_zeros_output(aq):
 def test_null_bias_consumers(aq, bits, G):
     """Every consumer with biases=None gives exactly the result of an all-zero
     bias array (the same kernels read +0), and that result matches the
-    reference with zero biases: bit-exact for dequantize and the embedding,
+    oracle with zero biases: bit-exact for dequantize and the embedding,
     within the bound for the matmuls (1, 3, 8, 40 and 130 rows, and the
     gathers)."""
     import torch
@@ -762,7 +762,7 @@ def test_gather_qmm_more_pairs_than_one_list(aq):
 @pytest.mark.parametrize("T", [4, 200])
 def test_gather_dispatch(aq, T):
     """Few rows per expert go to the matrix-vector gather, many to the
-    matrix-core gather; both agree with the reference."""
+    matrix-core gather; both agree with the oracle."""
     G, bits, E, N, K, topk = 64, 4, 8, 70, 256, 2
     c, s, b = _experts(E, N, K, G, bits, seed=23)
     ids = inputs.expert_ids(T, E, topk, seed=23)
@@ -808,7 +808,7 @@ def test_gather_all_same_expert_is_qmv(aq):
     yq = out_to_f64(aq.aq_qmv(bits_to_dev(xb, "f16"), dev[0][2].contiguous(),
                               dev[1][2].contiguous(), dev[2][2].contiguous(), G, bits))
     # the two kernels sum in different orders (M = 8 runs on the matrix cores),
-    # so they agree through the reference, each within the bound
+    # so they agree through the oracle, each within the bound
     y_ref, A = oracle.matmul(inputs.from_bits(xb, "f16"), c[2], s[2], b[2], K, G, bits)
     for got, what in ((yg[:, 0, :], "gather"), (yq, "qmv")):
         ok, ratio = oracle.within_tolerance(got, y_ref, A)

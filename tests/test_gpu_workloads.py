@@ -41,7 +41,7 @@ def aq():
 
 
 def _check_quantize(aq, w, G, bits):
-    """GPU quantize of W equals the reference bit for bit; returns the packing."""
+    """GPU quantize of W equals the oracle bit for bit; returns the packing."""
     ref = oracle.quantize(w, G, bits)
     got = packed_from_dev(*aq.aq_quantize(to_dev(w), G, bits))
     for name, a, b in zip(("codes", "scales", "biases"), got, ref):
@@ -150,7 +150,7 @@ def test_moe(aq):
 def test_moe_prefill(aq):
     """The same expert stack at prefill size through the matrix-core gather:
     2048 tokens top-6; 128 sampled (token, slot) rows checked against the
-    reference, all rows finite."""
+    oracle, all rows finite."""
     cfg = inputs.WORKLOADS["moe"]
     (N, K), E, T, topk = cfg["shapes"][0], cfg["experts"], cfg["prefill_tokens"], cfg["topk"]
     packs = [oracle.quantize(inputs.weights(N, K, seed=0, key=(WID["moe"], e)), 64, 4)
@@ -179,7 +179,7 @@ def test_embedding(aq):
     for T in cfg["tokens"]:
         ids = inputs.token_ids(T, V, seed=0, key=(WID["embedding"],))
         out = aq.aq_embedding(to_dev(ids), c, s, b, G, bits, out_dtype=torch.bfloat16)
-        # the rows the tokens refer to, quantized again by the reference
+        # the rows the tokens refer to, quantized again by the oracle
         rows = np.unique(ids)
         ri = torch.from_numpy(rows.astype(np.int64)).cuda()
         cr, sr, br = oracle.quantize(w[ri].cpu().numpy(), G, bits)

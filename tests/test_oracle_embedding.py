@@ -1,6 +1,6 @@
 """Pins for the oracle's quantized embedding ("Tutorial 10: Quantization",
 s.6 "Quantized Embeddings": the packed rows, scales and biases of the looked-up
-token ids are selected, then dequantized).  The reference here selects rows
+token ids are selected, then dequantized).  The oracle here selects rows
 with numpy indexing exactly as that section writes it and decodes them with
 the independent shift-and-mask decoder written from s.3; it shares nothing
 with the oracle's C code."""

@@ -1,4 +1,4 @@
-"""Pins of the CPU reference's format arithmetic and bit layout against what
+"""Pins of the CPU oracle's format arithmetic and bit layout against what
 the pages print (tests/golden/*.json) and against an independent decoder.
 
 Not GPU tests: they run on the host only."""

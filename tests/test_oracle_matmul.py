@@ -1,6 +1,6 @@
-"""Pins of the CPU reference matmul and gather.
+"""Pins of the CPU oracle matmul and gather.
 
-The reference follows "Tutorial 10: Quantization", section 5, Approach 1
+The oracle follows "Tutorial 10: Quantization", section 5, Approach 1
 (dequantize, then multiply, y = x @ W^T), accumulating in binary64.  Pinned
 by: a dense numpy product on an independently decoded W (tiny shapes, every
 bit width and group size), the unit-vector special case (y = w^[:, k]), the
@@ -121,9 +121,9 @@ def test_expert_ids_distinct():
 
 
 def _bf16_ratios(M, N, K, G, seed=8, bits=4):
-    """Worst error/bound of (a) the reference result rounded once to bf16 (the
+    """Worst error/bound of (a) the oracle result rounded once to bf16 (the
     best any bf16 output can do) and (b) a model of the prefill kernel's
-    arithmetic: weights rounded to bf16 first (the reference's own bf16
+    arithmetic: weights rounded to bf16 first (the oracle's own bf16
     dequantize), products summed in binary32, the sum rounded to bf16."""
     w = inputs.weights(N, K, seed=seed, key=(G, bits, 17), outliers=True)
     codes, scales, biases = oracle.quantize(w, G, bits)
@@ -142,9 +142,9 @@ def test_bf16_bound_threshold_in_k():
     """Where the 2^-9*A bound fails for bf16 results, and why.  A bf16 result
     carries its own rounding, up to 2^-8*|y|, which the bound covers only
     while |y| <= A/2 (|y|/A shrinks like 1/sqrt(K) on random data):
-      * K = 64: even the correctly rounded reference leaves the bound, so no
+      * K = 64: even the correctly rounded result leaves the bound, so no
         bf16 output can meet it there;
-      * K = 96 and 160: the correctly rounded reference stays inside, but
+      * K = 96 and 160: the correctly rounded result stays inside, but
         rounding the weights to bf16 before the product (the prefill kernel's
         arithmetic) adds up to 2^-8 relative per term and leaves it;
       * K >= 512: both stay well inside (under 0.6 of the bound), which is where

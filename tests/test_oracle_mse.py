@@ -1,4 +1,4 @@
-"""Pins of the CPU reference range-search quantizer (reading R14).
+"""Pins of the CPU oracle range-search quantizer (reading R14).
 
 "mlx-gptq", "How it works" (the --mse option): a group may be quantized over a
 range narrower than its min-max span, trading error on its outermost members
@@ -86,7 +86,7 @@ def _check_against_brute_force(w, G, bits, steps):
             exact = [c[3] for c in cands]
             best = min(exact)
             i = int(chosen[n, g])
-            # the reference's winner has the least exact error, up to the
+            # the oracle's winner has the least exact error, up to the
             # rounding of its binary64 sums
             assert exact[i] <= best * (1 + Fraction(1, 10**12)), (n, g, i)
             # and its error sums agree with the exact ones
@@ -139,7 +139,7 @@ def test_candidate_ranges_lie_inside_the_group_range():
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_candidates_never_widen_the_min_max_grid(bits):
-    """Each candidate's grid, as the reference builds it (only = j), has a bias
+    """Each candidate's grid, as the oracle builds it (only = j), has a bias
     >= the min-max grid's bias and a scale <= its scale: the search only ever
     narrows, on same-sign groups too (with the range [p min, p max] an
     all-positive group's lower end would fall below its minimum)."""

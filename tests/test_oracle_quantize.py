@@ -1,6 +1,6 @@
-"""Pins of the CPU reference quantizer.
+"""Pins of the CPU oracle quantizer.
 
-The quantizer is an encoding (readings R1, R2 in the reference's header):
+The quantizer is an encoding (readings R1, R2 in the oracle's header):
 per group of G weights along a row, bias = the group minimum rounded down to
 fp16, scale = the smallest fp16 whose top grid point reaches the group
 maximum, code = nearest grid index with ties to even.  These tests pin it by
@@ -31,7 +31,7 @@ def _h(v):
 
 
 def brute_force_group(ws, bits):
-    """Exact reference for one group, by enumeration with rationals."""
+    """Exact answer for one group, by enumeration with rationals."""
     L = (1 << bits) - 1
     lo, hi = Fraction(min(ws)), Fraction(max(ws))
     # bias: the largest fp16 value <= lo

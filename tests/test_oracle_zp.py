@@ -1,4 +1,4 @@
-"""Pins of the CPU reference integer-zero-point quantizer (reading R15).
+"""Pins of the CPU oracle integer-zero-point quantizer (reading R15).
 
 "mlx-gptq", "On NVIDIA: the same recipe in AWQ format" (--zero-point int):
 each group's offset is a whole number of steps, so the grid converts without
@@ -10,7 +10,7 @@ integer; bias = -z*s; codes are the nearest grid points (ties to even).
 Pinned here by
   * a brute force that scans every non-negative fp16 scale in increasing
     order and every z, with exact rational arithmetic (it shares nothing with
-    the reference's search),
+    the oracle's search),
   * exact invariants: z integer in [0, L], bias == -z*s exactly, every member
     on the grid's span, |w - w^| <= s/2, code z decodes to exactly 0,
   * minimality: the next smaller fp16 scale admits no zero point,
