@@ -77,6 +77,9 @@ def _load():
             "oracle_matmul": ([vp, i64, vp, vp, vp, i64, i64, i32, i32, vp, vp], i32),
             "oracle_gather_matmul": ([vp, i64, vp, vp, vp, i64, i64, i64, vp, i64, i32, i32, vp, vp],
                                      i32),
+            "oracle_e2m1_to_double": ([i32], ctypes.c_double),
+            "oracle_quantize_mxfp4": ([vp, i64, i64, vp, vp], i32),
+            "oracle_dequantize_mxfp4_exact": ([vp, vp, i64, i64, vp], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(lib, name)
@@ -285,6 +288,57 @@ def gather_matmul(x: np.ndarray, codes, scales, biases, ids: np.ndarray, K: int,
     if st:
         raise OracleError(st, "gather_matmul")
     return y, A
+
+
+# --- mxfp4 (reading R16) ----------------------------------------------------------
+def e2m1_to_double(code: int) -> float:
+    """Value of a 4-bit E2M1 code (bit 3 sign, bits 2..1 exponent, bit 0 mantissa)."""
+    return _load().oracle_e2m1_to_double(int(code))
+
+
+def quantize_mxfp4(w: np.ndarray):
+    """w float32 [N, K] (K % 32 == 0) -> (codes uint32 [N, K/8], scales uint8
+    [N, K/32] holding X + 127): per group of 32, 2^X with X = floor(log2 max|w|)
+    - 2 clamped to [-127, 127], codes the nearest E2M1 values of w / 2^X."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    codes = np.zeros((N, K // 8), dtype=np.uint32)
+    scales = np.zeros((N, K // 32), dtype=np.uint8)
+    st = _load().oracle_quantize_mxfp4(_p(w), N, K, _p(codes), _p(scales))
+    if st:
+        raise OracleError(st, "quantize_mxfp4")
+    return codes, scales
+
+
+def dequantize_mxfp4_exact(codes, scales, K: int) -> np.ndarray:
+    """Exact code value * 2^X as float64 [N, K]."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint32)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    N = codes.shape[0]
+    out = np.zeros((N, K), dtype=np.float64)
+    st = _load().oracle_dequantize_mxfp4_exact(_p(codes), _p(scales), N, K, _p(out))
+    if st:
+        raise OracleError(st, "dequantize_mxfp4_exact")
+    return out
+
+
+def dequantize_mxfp4(codes, scales, K: int, out_dtype: int):
+    """Dequantize to F32 (float32) or F16/BF16 (uint16 bit patterns), each the
+    exact value rounded to nearest even (binary32 holds every value whose
+    exponent fits it)."""
+    exact = dequantize_mxfp4_exact(codes, scales, K)
+    if out_dtype == F32:
+        with np.errstate(over="ignore"):
+            return exact.astype(np.float32)
+    rnd = double_to_half_rne if out_dtype == F16 else (lambda v: float_to_bf16_rne(np.float32(v)))
+    return np.vectorize(rnd, otypes=[np.uint16])(exact).astype(np.uint16)
+
+
+def matmul_dense(x: np.ndarray, w: np.ndarray):
+    """y = x @ w^T and A = |x| @ |w|^T in float64 for an exact dequantized w."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    return x @ w.T, np.abs(x) @ np.abs(w).T
 
 
 def within_tolerance(y, y_ref, A):

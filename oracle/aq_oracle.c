@@ -80,6 +80,20 @@
  *      when z = 0); codes by R2 against that bias and scale.  Hence every
  *      member lies on the grid's span and |w - w^| <= s/2, and w^ =
  *      (q - z)*s exactly.
+ *  R16 mxfp4 ([MLXQ] newer-modes paragraph and [QMLX] "Modes, bits and
+ *      mixed recipes": a block-scaled float mode with groups of 32 and
+ *      4-bit codes that keeps one exponent per group instead of a scale and
+ *      a bias).  The pages give no bit layout; taken here, the microscaling
+ *      (MX) definition of that name: a code is an E2M1 float -- bit 3 the
+ *      sign, bits 2..1 an exponent e with bias 1, bit 0 a mantissa m; value
+ *      (1 + m/2) * 2^(e-1) for e > 0 and m/2 for e = 0, so the magnitudes
+ *      of codes 0..7 are 0, 0.5, 1, 1.5, 2, 3, 4, 6 -- and the group's
+ *      scale is 2^X, stored as the byte X + 127.  X = floor(log2(max|w|))
+ *      - 2 (2 = the exponent of E2M1's largest value), clamped to
+ *      [-127, 127], and -127 for an all-zero group.  A member's code is
+ *      its sign bit with the magnitude code nearest to |w| / 2^X (ties to
+ *      the even mantissa; above 6 that is 6); codes are packed as in R3
+ *      with b = 4.  Dequantized value: code value * 2^X.
  *
  * Exactness of the binary64 comparisons used below.  Every finite fp16
  * value is an integer multiple of 2^-24 of magnitude < 2^16; q*s with
@@ -666,6 +680,84 @@ int oracle_gather_matmul(const double *x, int64_t T, const uint32_t *codes, cons
       st = oracle_matmul(x + t * K, 1, codes + e * wpe, scales + e * spe, biases + e * spe, N, K,
                          G, bits, y + (t * topk + j) * N, A + (t * topk + j) * N);
       if (st) return st;
+    }
+  return OR_OK;
+}
+
+/* ---------------------------------------------------------------------
+ * mxfp4 (reading R16).  codes [N, K/8] words (R3 with b = 4), scales
+ * [N, K/32] bytes holding X + 127; K a multiple of 32.
+ * ------------------------------------------------------------------- */
+/* magnitude of E2M1 code c (0..7): m/2 for e = 0, (1 + m/2) 2^(e-1) else */
+static double e2m1_magnitude(int c) {
+  const int e = (c >> 1) & 3, m = c & 1;
+  return e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+}
+
+double oracle_e2m1_to_double(int code) {
+  const double v = e2m1_magnitude(code & 7);
+  return (code & 8) ? -v : v;
+}
+
+/* the magnitude code nearest to t >= 0 (ties to the even mantissa) */
+static int e2m1_nearest(double t) {
+  int best = 0;
+  for (int c = 1; c < 8; ++c) {
+    const double d = fabs(t - e2m1_magnitude(c)), db = fabs(t - e2m1_magnitude(best));
+    if (d < db || (d == db && (c & 1) == 0 && (best & 1) == 1)) best = c;
+  }
+  return best;
+}
+
+/* the group's scale exponent X (R16) */
+static int mx_exponent(const float *g, int n) {
+  double amax = 0.0;
+  for (int i = 0; i < n; ++i) {
+    const double a = fabs((double)g[i]);
+    if (a > amax) amax = a;
+  }
+  if (amax == 0.0) return -127;
+  int ex;
+  frexp(amax, &ex);  /* amax = f * 2^ex, f in [0.5, 1): floor(log2(amax)) = ex - 1 */
+  int X = ex - 1 - 2;
+  return X < -127 ? -127 : (X > 127 ? 127 : X);
+}
+
+int oracle_quantize_mxfp4(const float *w, int64_t N, int64_t K, uint32_t *codes,
+                          uint8_t *scales) {
+  if (N < 0 || K < 0 || K % 32) return OR_ERR_ARG;
+  for (int64_t i = 0; i < N * K; ++i)
+    if (!isfinite(w[i])) return OR_ERR_RANGE;
+  const int64_t wpr = K / 8, ng = K / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    uint32_t *row = codes + n * wpr;
+    memset(row, 0, (size_t)wpr * sizeof(uint32_t));
+    for (int64_t g = 0; g < ng; ++g) {
+      const float *grp = w + n * K + g * 32;
+      const int X = mx_exponent(grp, 32);
+      scales[n * ng + g] = (uint8_t)(X + 127);
+      for (int i = 0; i < 32; ++i) {
+        const double t = ldexp(fabs((double)grp[i]), -X);  /* exact: a power-of-two scaling */
+        const int code = (signbit(grp[i]) ? 8 : 0) | e2m1_nearest(t);
+        const int64_t k = g * 32 + i;
+        row[k / 8] |= (uint32_t)code << (4 * (k % 8));
+      }
+    }
+  }
+  return OR_OK;
+}
+
+/* exact dequantized values (binary64 holds every code value times 2^X) */
+int oracle_dequantize_mxfp4_exact(const uint32_t *codes, const uint8_t *scales, int64_t N,
+                                  int64_t K, double *out) {
+  if (N < 0 || K < 0 || K % 32) return OR_ERR_ARG;
+  const int64_t wpr = K / 8, ng = K / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) {
+      const int code = (int)((codes[n * wpr + k / 8] >> (4 * (k % 8))) & 15u);
+      out[n * K + k] = ldexp(oracle_e2m1_to_double(code), (int)scales[n * ng + k / 32] - 127);
     }
   return OR_OK;
 }
