@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "aq_internal.hpp"
+
 namespace aq {
 
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
@@ -113,6 +115,38 @@ __device__ __forceinline__ void load_chunk(const uint32_t *__restrict__ p, uint3
 #pragma unroll
     for (int j = 0; j < BITS; ++j) w[j] = p[j];
   }
+}
+
+// ---- weight loads for the quantizers ------------------------------------------------
+
+template <int WDT>
+__device__ __forceinline__ void load8(const void *__restrict__ base, int64_t e, float *v) {
+  if constexpr (WDT == X_F32) {
+    const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(base) + e);
+    float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    uint4 a = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(base) + e);
+    uint32_t u[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (WDT == X_F16) {
+        v[2 * i] = f16_to_f32((uint16_t)(u[i] & 0xFFFFu));
+        v[2 * i + 1] = f16_to_f32((uint16_t)(u[i] >> 16));
+      } else {
+        v[2 * i] = bf16_to_f32((uint16_t)(u[i] & 0xFFFFu));
+        v[2 * i + 1] = bf16_to_f32((uint16_t)(u[i] >> 16));
+      }
+    }
+  }
+}
+
+// 32 weights (one 32-code chunk, BITS whole words of codes) of the row
+// starting at element e, widened exactly to binary32
+template <int WDT>
+__device__ __forceinline__ void load32(const void *__restrict__ base, int64_t e, float *v) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) load8<WDT>(base, e + 8 * j, v + 8 * j);
 }
 
 }  // namespace aq

@@ -118,36 +118,6 @@ __device__ __forceinline__ uint32_t nearest_code(float w, double b, double s, fl
   return (uint32_t)q;
 }
 
-template <int WDT>
-__device__ __forceinline__ void load8(const void *__restrict__ base, int64_t e, float *v) {
-  if constexpr (WDT == X_F32) {
-    const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(base) + e);
-    float4 a = p[0], b = p[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  } else {
-    uint4 a = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(base) + e);
-    uint32_t u[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (WDT == X_F16) {
-        v[2 * i] = f16_to_f32((uint16_t)(u[i] & 0xFFFFu));
-        v[2 * i + 1] = f16_to_f32((uint16_t)(u[i] >> 16));
-      } else {
-        v[2 * i] = bf16_to_f32((uint16_t)(u[i] & 0xFFFFu));
-        v[2 * i + 1] = bf16_to_f32((uint16_t)(u[i] >> 16));
-      }
-    }
-  }
-}
-
-// 32 weights (one 32-code chunk, BITS whole words of codes) of the row
-// starting at element e, widened exactly to binary32
-template <int WDT>
-__device__ __forceinline__ void load32(const void *__restrict__ base, int64_t e, float *v) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) load8<WDT>(base, e + 8 * j, v + 8 * j);
-}
-
 // One thread per 32-weight chunk: a group is G/32 adjacent lanes (1, 2 or
 // 4), reduced by lane shuffles; the thread writes its chunk's BITS words of
 // codes whole.  (With 8 weights per thread, the group search and the

@@ -252,6 +252,59 @@ aq_status aq_gather_quantized_matmul(const void *x, aq_dtype x_dtype, int64_t T,
                                      const int32_t *ids, int topk, int group_size, int bits,
                                      void *y, void *stream);
 
+/* ---- mxfp4: block-scaled 4-bit floats ------------------------------------ */
+
+/* The block-scaled float mode mxfp4 ("Quantization", metalworking MLX notes,
+ * the paragraph on the newer modes; "Quantizing a Model for MLX", "Modes,
+ * bits and mixed recipes": groups of 32 weights, 4-bit codes, one exponent
+ * per group in place of a scale and a bias).  The pages give no bit layout;
+ * this library takes the microscaling (MX) definition of that name:
+ *
+ *   codes   uint32 [N, K/8]   E2M1 codes: bit 3 the sign, bits 2..1 an
+ *                             exponent e with bias 1, bit 0 a mantissa m;
+ *                             value (1 + m/2)*2^(e-1) for e > 0, m/2 for
+ *                             e = 0 (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6);
+ *                             packed as the 4-bit bitstream above (code k of
+ *                             a row at bits [4k, 4k+4))
+ *   scales  uint8  [N, K/32]  X + 127 for the group scale 2^X (E8M0)
+ *
+ * The group is fixed at 32 and there are no biases.  N >= 1, K >= 32 and a
+ * multiple of 32.  The conventions above (device pointers 16-byte aligned,
+ * caller-owned buffers, host-side checks, asynchronous on `stream`) hold. */
+
+/* Quantize W [N, K] (device; AQ_F32, AQ_F16 or AQ_BF16, widened exactly to
+ * binary32) into mxfp4 codes and scales (device).  Per group of 32:
+ *   X = floor(log2 max|w|) - 2 (2 = the exponent of 6, the largest code
+ *       value), clamped to [-127, 127]; -127 for a group of zeros;
+ *   each weight's code is its own sign bit (so -0 gives code 8) with the
+ *       magnitude code nearest to |w| / 2^X, ties to the even mantissa, and
+ *       6 for anything above.
+ * Precondition (not checked on the device): weights finite; otherwise the
+ * outputs for that group are unspecified. */
+aq_status aq_quantize_mxfp4(const void *w, aq_dtype w_dtype, int64_t N, int64_t K,
+                            uint32_t *codes, uint8_t *scales, void *stream);
+
+/* Dequantize mxfp4: out[n, k] = code value * 2^X, exact in binary32 (2 or
+ * fewer significant bits; +-inf beyond the binary32 range, which only scale
+ * bytes 254 and 255 reach, and which aq_quantize_mxfp4 never writes), then
+ * rounded to nearest even into out_dtype (AQ_F32, AQ_F16 or AQ_BF16).  out
+ * is device memory [N, K]. */
+aq_status aq_dequantize_mxfp4(const uint32_t *codes, const uint8_t *scales, int64_t N, int64_t K,
+                              void *out, aq_dtype out_dtype, void *stream);
+
+/* Decode matrix-vector product with mxfp4 weights ("Quantization",
+ * metalworking, QMV bullet: the weights are dequantized in registers on
+ * every use): y[n] = sum_k x[k] * w^[n, k] for one row x.  x: device [K] in
+ * x_dtype (AQ_F16 or AQ_BF16); y: device [N] in x_dtype.  Each group's
+ * products are summed in binary32 and scaled by 2^X; y is rounded to nearest
+ * even.  AQ_ERR_UNSUPPORTED for K > 49152 (x is held on chip). */
+aq_status aq_qmv_mxfp4(const void *x, aq_dtype x_dtype, const uint32_t *codes,
+                       const uint8_t *scales, int64_t N, int64_t K, void *y, void *stream);
+
+/* Which kernel aq_qmv_mxfp4 launches for this shape, as text (as
+ * aq_qmv_describe does); -1 for arguments aq_qmv_mxfp4 would reject. */
+int aq_qmv_mxfp4_describe(int64_t N, int64_t K, aq_dtype x_dtype, char *buf, int len);
+
 #ifdef __cplusplus
 }
 #endif
