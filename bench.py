@@ -44,6 +44,10 @@ the same bytes (same cold rotation and timing), a measured second denominator.
                 aq_dequantize of it to bf16 (% of HBM), the integer-zero-point
                 aq_quantize_zp and the range-search aq_quantize_mse over 21
                 narrowed ranges;
+  mxfp4         the decode product with mxfp4 weights (E2M1 codes, one
+                exponent byte per 32 weights) on the four decode matrices,
+                with the plain read of the same bytes, and mxfp4 quantize /
+                dequantize of the prefill-size matrix;
   embedding     quantized embedding lookups (rows of a [128256, 4096] 8-bit
                 table dequantized to bf16) for 1 and 2048 tokens.
 
@@ -81,6 +85,7 @@ def parse():
     p.add_argument("--no-embedding", action="store_true", help="skip the embedding section")
     p.add_argument("--no-extra", action="store_true",
                    help="skip the spec-decode (M = 2..8) and MoE gather sections")
+    p.add_argument("--no-mxfp4", action="store_true", help="skip the mxfp4 section")
     p.add_argument("--qmm-iters", type=int, default=20)
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain 512 MiB device copy (counter calibration)")
@@ -281,6 +286,10 @@ def main():
     # ---- quantize and dequantize (offline conversion, standalone decode) -------------------
     if not args.no_extra:
         result["quantize_dequantize"] = _quant_dequant(aq, inputs, dev, stream, legs)
+
+    # ---- mxfp4: block-scaled 4-bit floats ----------------------------------------------------
+    if not args.no_mxfp4:
+        result["mxfp4"] = _mxfp4(aq, inputs, dev, stream, legs)
 
     # ---- quantized embedding ---------------------------------------------------------------
     if not args.no_embedding:
@@ -650,6 +659,84 @@ def _quant_dequant(aq, inputs, dev, stream, legs=None):
     del w, c, s_, b, out
     torch.cuda.synchronize()
     return res
+
+
+def _mxfp4(aq, inputs, dev, stream, legs=None):
+    """mxfp4 (E2M1 codes, one exponent byte per 32 weights, 4.25 bits per
+    weight): the decode product on the four decode matrices (the headline
+    weights quantized by aq_quantize_mxfp4, x fp16), each launch on a cold
+    copy (>= 1 GiB rotated), per-launch time in a graph, with the plain read
+    of the same bytes beside it; and aq_quantize_mxfp4 / aq_dequantize_mxfp4
+    (bf16 out) on the prefill-size matrix."""
+    import torch
+    out = {"workload": "mxfp4 decode M=1, W [4096,4096] [1024,4096] [14336,4096] [4096,14336], "
+                       "fp16 x, cold weights"}
+    rows = {}
+    total_us = total_bytes = 0
+    for i, (N, K) in enumerate(DECODE_SHAPES):
+        w = inputs.weights_device(N, K, device=dev, seed=0, key=(1, i), outliers=True)
+        packed = aq.aq_quantize_mxfp4(w)
+        del w
+        wbytes = N * K // 2 + N * K // 32
+        copies = max(2, math.ceil(COLD_BYTES / wbytes))
+        sets = [packed] + [tuple(t.clone() for t in packed) for _ in range(copies - 1)]
+        x = inputs.activations_device(1, K, "f16", device=dev, seed=0, key=(1, i))
+        y = torch.empty((1, N), dtype=torch.float16, device=dev)
+        fs = [lambda c=c, s_=s_: aq.aq_qmv_mxfp4(x, c, s_, y=y) for (c, s_) in sets] * 2
+        us = _graph_us(torch, stream, fs)
+        ceil_us = _read_ceiling_us(aq, torch, wbytes, stream)
+        gbs = wbytes / (us * 1e-6) / 1e9
+        rows[f"{N}x{K}"] = {"kernel": aq.aq_qmv_mxfp4_describe(N, K), "weight_bytes": wbytes,
+                            "avg_us": round(us, 3), "weight_gbs": round(gbs, 1),
+                            "pct_hbm": round(100 * gbs / HBM_PEAK_GBS, 1),
+                            "read_ceiling_us": round(ceil_us, 3),
+                            "frac_of_read_ceiling": round(ceil_us / us, 3)}
+        total_us += us
+        total_bytes += wbytes
+        print(f"# mxfp4 QMV {N}x{K}: {us:.2f} us, {gbs:.0f} GB/s weights, "
+              f"{ceil_us / us:.2f} of the plain read", file=sys.stderr, flush=True)
+        if legs is not None and "mxfp4_decode" not in legs:
+            # the oracle on the first matrix: exact dequantize, then the product
+            import oracle
+            hx = _host_x(x, "f16")
+            hc = packed[0].cpu().numpy().view("uint32")
+            hs = packed[1].cpu().numpy()
+            runs, el = _cpu_timed(
+                lambda: oracle.matmul_dense(hx, oracle.dequantize_mxfp4_exact(hc, hs, K)), 1.5)
+            legs["mxfp4_decode"] = {"workload": f"mxfp4 W [{N},{K}], x fp16 [1,{K}]",
+                                    "threads": oracle.num_threads(),
+                                    "gbs": round(wbytes * runs / el / 1e9, 3),
+                                    "gpu_gbs": round(gbs, 1),
+                                    "sample": f"{runs} call(s) in {el:.1f} s"}
+        del sets, packed
+        torch.cuda.synchronize()
+    out["per_shape"] = rows
+    out["step_us"] = round(total_us, 3)
+    out["step_weight_bytes"] = total_bytes
+    out["step_weight_gbs"] = round(total_bytes / (total_us * 1e-6) / 1e9, 1)
+    # quantize (fp32 in) and dequantize (bf16 out) of the prefill-size matrix
+    N, K = PREFILL["N"], PREFILL["K"]
+    w = inputs.weights_device(N, K, device=dev, seed=0, key=(inputs.WORKLOAD_ID["prefill"],))
+    c, s_ = aq.aq_quantize_mxfp4(w)
+    deq = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    packed = N * K // 2 + N * K // 32
+    us = _graph_us(torch, stream, [lambda: aq.aq_quantize_mxfp4(w, codes=c, scales=s_)] * 4)
+    nb = 4 * N * K + packed
+    out["quantize"] = {"workload": f"W [{N},{K}] fp32", "avg_us": round(us, 2), "bytes": nb,
+                       "gbs": round(nb / (us * 1e-6) / 1e9, 1),
+                       "pct_hbm": round(100 * nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
+    us = _graph_us(torch, stream, [lambda: aq.aq_dequantize_mxfp4(c, s_, K, out=deq)] * 4)
+    nb = packed + 2 * N * K
+    out["dequantize_bf16"] = {"avg_us": round(us, 2), "bytes": nb,
+                              "gbs": round(nb / (us * 1e-6) / 1e9, 1),
+                              "pct_hbm": round(100 * nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
+    print(f"# mxfp4 step {total_us:.2f} us ({out['step_weight_gbs']} GB/s); quantize "
+          f"{out['quantize']['avg_us']:.1f} us ({out['quantize']['gbs']} GB/s), dequantize "
+          f"{out['dequantize_bf16']['avg_us']:.1f} us ({out['dequantize_bf16']['gbs']} GB/s)",
+          file=sys.stderr, flush=True)
+    del w, c, s_, deq
+    torch.cuda.synchronize()
+    return out
 
 
 def _embedding(aq, inputs, dev, stream):

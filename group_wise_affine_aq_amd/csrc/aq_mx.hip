@@ -21,9 +21,11 @@
 // (subnormals included) order as their patterns do, and the thresholds
 // between neighbouring code values, times 2^X, are exact binary32 values
 // built from their exponent and mantissa fields, so no rounding mode or
-// denormal setting enters.  Dequantized values are built the same way (a
-// code value times 2^X has at most two significant bits, exact in binary32
-// down to 2^-128), then rounded to nearest even into the output type.
+// denormal setting enters.  A dequantized value (a code value times 2^X:
+// at most two significant bits, exact in bf16 and binary32 down to 2^-128)
+// comes from the gfx950 scaled convert, or for the one exponent binary32
+// cannot scale by (X = 128) from the same bit construction, then is rounded
+// to nearest even into the output type.
 //
 // The product (decode, M = 1): the E2M1 pairs go through the gfx950
 // scaled-convert instruction (v_cvt_scalef32_pk_f16_fp4 / _bf16_fp4, scale
@@ -67,87 +69,146 @@ __device__ __forceinline__ uint32_t e2m1_code(uint32_t a, const uint32_t (&t)[7]
 }
 
 // binary32 pattern of code c (sign in bit 3) times 2^X, X in [-127, 128];
-// +-inf where that exceeds the binary32 range (X = 128, or 127 with |c| > 1.5)
+// +-inf where that exceeds the binary32 range (X = 128, or 127 with |c| > 1.5).
+// Written with selects only: every lane takes the same path.
 __device__ __forceinline__ uint32_t e2m1_value_bits(uint32_t c, int X) {
   const uint32_t sign = (c & 8u) << 28, m = c & 7u;
-  if (m == 0) return sign;
-  const int e = m == 1 ? -1 : (int)(m >> 1) - 1;  // value (1 + mb/2) 2^e
-  const uint32_t mb = m == 1 ? 0u : (m & 1u) << 22;
-  const int E = e + X + 127;                      // in [-1, 257]
-  if (E >= 255) return sign | 0x7F800000u;
-  if (E >= 1) return sign | ((uint32_t)E << 23) | mb;
-  return sign | ((0x800000u | mb) >> (1 - E));
+  // m >= 1: value (1 + mb/2) 2^e with e = (m >> 1) - 1 and mb = m & 1 from
+  // m = 2 on (code 1 is 0.5 = 2^-1)
+  const uint32_t mb = m >= 2u ? (m & 1u) << 22 : 0u;
+  const int E = (int)(m >> 1) - 1 + X + 127;  // biased exponent, in [-1, 257]
+  const uint32_t normal = ((uint32_t)E << 23) | mb;
+  const uint32_t sub = (0x800000u | mb) >> ((uint32_t)(1 - E) & 31u);  // used for E in {-1, 0}
+  uint32_t r = E >= 255 ? 0x7F800000u : (E >= 1 ? normal : sub);
+  r = m == 0u ? 0u : r;
+  return sign | r;
 }
 
-// ---- quantize: one thread per 32-weight group ----------------------------------------
+// ---- quantize and dequantize: one thread per word (8 codes) ----------------------------
+// A workgroup takes kMxUnroll * 256 consecutive words per pass, word
+// base + u * 256 + thread, so every load and store instruction of a wave
+// covers one contiguous span and each thread has kMxUnroll words in flight.
+// Four consecutive words are one group: the four lanes of a DPP quad.
+constexpr int kMxUnroll = 4;
+
+__device__ __forceinline__ uint32_t quad_max(uint32_t a) {
+  uint32_t b = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+  a = a > b ? a : b;
+  b = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x4E, 0xF, 0xF, false);           // [2,3,0,1]
+  return a > b ? a : b;
+}
 
 template <int WDT>
 __global__ __launch_bounds__(256) void quantize_mx_kernel(const void *__restrict__ w,
-                                                          int64_t groups,
+                                                          int64_t words,
                                                           uint32_t *__restrict__ codes,
                                                           uint8_t *__restrict__ scales) {
   // midpoints as (mantissa field, exponent)
   constexpr uint32_t kMant[7] = {0u, 0x400000u, 0x200000u, 0x600000u, 0x200000u, 0x600000u,
                                  0x200000u};
   constexpr int kExp[7] = {-2, -1, 0, 0, 1, 1, 2};
-  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < groups;
-       g += (int64_t)gridDim.x * blockDim.x) {
-    float v[32];
-    load32<WDT>(w, g * 32, v);
-    uint32_t amax = 0;
+  const int64_t pass = (int64_t)gridDim.x * (256 * kMxUnroll);
+  for (int64_t base = (int64_t)blockIdx.x * (256 * kMxUnroll); base < words; base += pass) {
+    float v[kMxUnroll][8];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const uint32_t a = __builtin_bit_cast(uint32_t, v[i]) & 0x7FFFFFFFu;
-      amax = a > amax ? a : amax;
+    for (int u = 0; u < kMxUnroll; ++u) {
+      const int64_t t = base + u * 256 + threadIdx.x;
+      if (t < words) load8<WDT>(w, t * 8, v[u]);
     }
-    // floor(log2 max) = biased exponent - 127 for a normal maximum; a zero
-    // or subnormal maximum (biased exponent 0) and the exponent 1 both clamp
-    const int eb = (int)(amax >> 23);
-    const int X = (eb < 2 ? 2 : eb) - 129;
-    uint32_t t[7];
 #pragma unroll
-    for (int k = 0; k < 7; ++k) t[k] = pow2_bits(kMant[k], kExp[k] + X);
-    uint32_t q[4] = {0u, 0u, 0u, 0u};
+    for (int u = 0; u < kMxUnroll; ++u) {
+      const int64_t t = base + u * 256 + threadIdx.x;
+      if (t >= words) break;  // words is a multiple of 4: quads leave together
+      uint32_t amax = 0;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const uint32_t u = __builtin_bit_cast(uint32_t, v[i]);
-      const uint32_t c = e2m1_code(u & 0x7FFFFFFFu, t) | ((u >> 31) << 3);
-      q[i >> 3] |= c << (4 * (i & 7));
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t a = __builtin_bit_cast(uint32_t, v[u][i]) & 0x7FFFFFFFu;
+        amax = a > amax ? a : amax;
+      }
+      amax = quad_max(amax);
+      // floor(log2 max) = biased exponent - 127 for a normal maximum; a zero
+      // or subnormal maximum (biased exponent 0) and the exponent 1 both clamp
+      const int eb = (int)(amax >> 23);
+      const int X = (eb < 2 ? 2 : eb) - 129;
+      uint32_t th[7];
+#pragma unroll
+      for (int k = 0; k < 7; ++k) th[k] = pow2_bits(kMant[k], kExp[k] + X);
+      uint32_t q = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t b = __builtin_bit_cast(uint32_t, v[u][i]);
+        q |= (e2m1_code(b & 0x7FFFFFFFu, th) | ((b >> 31) << 3)) << (4 * i);
+      }
+      codes[t] = q;
+      if ((threadIdx.x & 3) == 0) scales[t >> 2] = (uint8_t)(X + 127);
     }
-    reinterpret_cast<uint4 *>(codes)[g] = make_uint4(q[0], q[1], q[2], q[3]);
-    scales[g] = (uint8_t)(X + 127);
   }
 }
-
-// ---- dequantize: one thread per word (8 codes) ---------------------------------------
 
 template <int OUT>
 __global__ __launch_bounds__(256) void dequantize_mx_kernel(const uint32_t *__restrict__ codes,
                                                             const uint8_t *__restrict__ scales,
                                                             int64_t words, void *__restrict__ out) {
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < words;
-       t += (int64_t)gridDim.x * blockDim.x) {
-    const uint32_t wd = codes[t];
-    const int X = (int)scales[t >> 2] - 127;
-    uint32_t f[8];
+  const int64_t pass = (int64_t)gridDim.x * (256 * kMxUnroll);
+  for (int64_t base = (int64_t)blockIdx.x * (256 * kMxUnroll); base < words; base += pass) {
+    uint32_t wd[kMxUnroll], sc[kMxUnroll];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) f[j] = e2m1_value_bits((wd >> (4 * j)) & 15u, X);
-    if constexpr (OUT == X_F32) {
-      uint4 *o = reinterpret_cast<uint4 *>(out) + 2 * t;
-      o[0] = make_uint4(f[0], f[1], f[2], f[3]);
-      o[1] = make_uint4(f[4], f[5], f[6], f[7]);
-    } else {
-      uint32_t h[4];
+    for (int u = 0; u < kMxUnroll; ++u) {
+      const int64_t t = base + u * 256 + threadIdx.x;
+      if (t < words) {
+        wd[u] = codes[t];
+        sc[u] = scales[t >> 2];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kMxUnroll; ++u) {
+      const int64_t t = base + u * 256 + threadIdx.x;
+      if (t >= words) break;
+      const int X = (int)sc[u] - 127;
+      // Every code value times 2^X has at most two significant bits, so it
+      // is exact in bf16 (subnormals down to 2^-128 included) and binary32
+      // is its upper half.  The scaled convert (code pair * 2^X, the scale
+      // 2^X given as a binary32) returns exactly that pair, +-inf past the
+      // range, for X up to 127, checked on the MI355X for every code pair
+      // and exponent.  X = 128 (scale byte 255) has no binary32 scale: those
+      // groups take the bit construction.
+      const float scale = __builtin_bit_cast(float, (uint32_t)(X + 127) << 23);
+      uint32_t pr[4];
+      pr[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[u], scale, 0));
+      pr[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[u], scale, 1));
+      pr[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[u], scale, 2));
+      pr[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[u], scale, 3));
+      uint32_t f[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float a = __builtin_bit_cast(float, f[2 * j]);
-        const float b = __builtin_bit_cast(float, f[2 * j + 1]);
-        if constexpr (OUT == X_F16)
-          h[j] = (uint32_t)f32_to_f16_rne(a) | ((uint32_t)f32_to_f16_rne(b) << 16);
-        else
-          h[j] = (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
+        f[2 * j] = pr[j] << 16;
+        f[2 * j + 1] = pr[j] & 0xFFFF0000u;
       }
-      reinterpret_cast<uint4 *>(out)[t] = make_uint4(h[0], h[1], h[2], h[3]);
+      const bool edge = X > 127;
+      if (edge) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f[j] = e2m1_value_bits((wd[u] >> (4 * j)) & 15u, X);
+      }
+      if constexpr (OUT == X_F32) {
+        uint4 *o = reinterpret_cast<uint4 *>(out) + 2 * t;
+        o[0] = make_uint4(f[0], f[1], f[2], f[3]);
+        o[1] = make_uint4(f[4], f[5], f[6], f[7]);
+      } else if constexpr (OUT == X_F16) {
+        uint32_t h[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          h[j] = (uint32_t)f32_to_f16_rne(__builtin_bit_cast(float, f[2 * j])) |
+                 ((uint32_t)f32_to_f16_rne(__builtin_bit_cast(float, f[2 * j + 1])) << 16);
+        reinterpret_cast<uint4 *>(out)[t] = make_uint4(h[0], h[1], h[2], h[3]);
+      } else {
+        if (edge) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            pr[j] = (uint32_t)f32_to_bf16_rne(__builtin_bit_cast(float, f[2 * j])) |
+                    ((uint32_t)f32_to_bf16_rne(__builtin_bit_cast(float, f[2 * j + 1])) << 16);
+        }
+        reinterpret_cast<uint4 *>(out)[t] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+      }
     }
   }
 }
@@ -419,10 +480,10 @@ hipError_t qmv_mx_dispatch(const void *x, const uint32_t *codes, const uint8_t *
   return hipErrorInvalidValue;
 }
 
-// grid for the flat quantize / dequantize loops: one thread per item, at
-// most 2^22 workgroups (each thread then takes several items)
-dim3 flat_grid(int64_t items) {
-  const int64_t b = (items + 255) / 256;
+// grid for the quantize / dequantize loops over words: kMxUnroll words per
+// thread and pass, at most 2^22 workgroups (then several passes)
+dim3 word_grid(int64_t words) {
+  const int64_t b = (words + 256 * kMxUnroll - 1) / (256 * kMxUnroll);
   return dim3((unsigned)(b < (1 << 22) ? b : (1 << 22)));
 }
 
@@ -446,17 +507,17 @@ void qmv1_mx_shape(int64_t N, int64_t K, int &cpl, int &ud, int &w, int &wpc) {
 
 hipError_t launch_quantize_mx(const void *w, int w_dtype, int64_t N, int64_t K, uint32_t *codes,
                               uint8_t *scales, hipStream_t s) {
-  const int64_t groups = N * (K / 32);
-  const dim3 grid = flat_grid(groups);
+  const int64_t words = N * (K / 8);
+  const dim3 grid = word_grid(words);
   switch (w_dtype) {
     case X_F32:
-      hipLaunchKernelGGL(quantize_mx_kernel<X_F32>, grid, dim3(256), 0, s, w, groups, codes, scales);
+      hipLaunchKernelGGL(quantize_mx_kernel<X_F32>, grid, dim3(256), 0, s, w, words, codes, scales);
       break;
     case X_F16:
-      hipLaunchKernelGGL(quantize_mx_kernel<X_F16>, grid, dim3(256), 0, s, w, groups, codes, scales);
+      hipLaunchKernelGGL(quantize_mx_kernel<X_F16>, grid, dim3(256), 0, s, w, words, codes, scales);
       break;
     case X_BF16:
-      hipLaunchKernelGGL(quantize_mx_kernel<X_BF16>, grid, dim3(256), 0, s, w, groups, codes,
+      hipLaunchKernelGGL(quantize_mx_kernel<X_BF16>, grid, dim3(256), 0, s, w, words, codes,
                          scales);
       break;
     default: return hipErrorInvalidValue;
@@ -467,7 +528,7 @@ hipError_t launch_quantize_mx(const void *w, int w_dtype, int64_t N, int64_t K, 
 hipError_t launch_dequantize_mx(const uint32_t *codes, const uint8_t *scales, int64_t N, int64_t K,
                                 void *out, int out_dtype, hipStream_t s) {
   const int64_t words = N * (K / 8);
-  const dim3 grid = flat_grid(words);
+  const dim3 grid = word_grid(words);
   switch (out_dtype) {
     case X_F32:
       hipLaunchKernelGGL(dequantize_mx_kernel<X_F32>, grid, dim3(256), 0, s, codes, scales, words,
