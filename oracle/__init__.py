@@ -80,6 +80,11 @@ def _load():
             "oracle_e2m1_to_double": ([i32], ctypes.c_double),
             "oracle_quantize_mxfp4": ([vp, i64, i64, vp, vp], i32),
             "oracle_dequantize_mxfp4_exact": ([vp, vp, i64, i64, vp], i32),
+            "oracle_e4m3_to_double": ([i32], ctypes.c_double),
+            "oracle_quantize_mxfp8": ([vp, i64, i64, vp, vp], i32),
+            "oracle_dequantize_mxfp8_exact": ([vp, vp, i64, i64, vp], i32),
+            "oracle_quantize_nvfp4": ([vp, i64, i64, i32, vp, vp], i32),
+            "oracle_dequantize_nvfp4_exact": ([vp, vp, i64, i64, i32, vp], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(lib, name)
@@ -332,6 +337,90 @@ def dequantize_mxfp4(codes, scales, K: int, out_dtype: int):
             return exact.astype(np.float32)
     rnd = double_to_half_rne if out_dtype == F16 else (lambda v: float_to_bf16_rne(np.float32(v)))
     return np.vectorize(rnd, otypes=[np.uint16])(exact).astype(np.uint16)
+
+
+def _round_exact(exact, out_dtype: int):
+    if out_dtype == F32:
+        with np.errstate(over="ignore", invalid="ignore"):
+            return exact.astype(np.float32)
+
+    def bf(v):
+        with np.errstate(over="ignore", invalid="ignore"):
+            return float_to_bf16_rne(np.float32(v))
+    rnd = double_to_half_rne if out_dtype == F16 else bf
+    return np.vectorize(rnd, otypes=[np.uint16])(exact).astype(np.uint16)
+
+
+# --- mxfp8 (reading R17) and nvfp4 (reading R18) ---------------------------------------
+def e4m3_to_double(code: int) -> float:
+    """Value of an 8-bit E4M3 code (bit 7 sign, bits 6..3 exponent, bits 2..0
+    mantissa; magnitude pattern 0x7F is NaN)."""
+    return _load().oracle_e4m3_to_double(int(code))
+
+
+def quantize_mxfp8(w: np.ndarray):
+    """w float32 [N, K] (K % 32 == 0) -> (codes uint32 [N, K/4] (bytes in row
+    order), scales uint8 [N, K/32] holding X + 127): per group of 32, 2^X with
+    X = floor(log2 max|w|) - 8 clamped to [-127, 127], codes the nearest E4M3
+    values of w / 2^X."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    codes = np.zeros((N, K // 4), dtype=np.uint32)
+    scales = np.zeros((N, K // 32), dtype=np.uint8)
+    st = _load().oracle_quantize_mxfp8(_p(w), N, K, _p(codes), _p(scales))
+    if st:
+        raise OracleError(st, "quantize_mxfp8")
+    return codes, scales
+
+
+def dequantize_mxfp8_exact(codes, scales, K: int) -> np.ndarray:
+    """Exact code value * 2^X as float64 [N, K] (NaN for the NaN patterns)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint32)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    N = codes.shape[0]
+    out = np.zeros((N, K), dtype=np.float64)
+    st = _load().oracle_dequantize_mxfp8_exact(_p(codes), _p(scales), N, K, _p(out))
+    if st:
+        raise OracleError(st, "dequantize_mxfp8_exact")
+    return out
+
+
+def dequantize_mxfp8(codes, scales, K: int, out_dtype: int):
+    """The exact values rounded to nearest even: float32 for F32, uint16 bit
+    patterns for F16 / BF16."""
+    return _round_exact(dequantize_mxfp8_exact(codes, scales, K), out_dtype)
+
+
+def quantize_nvfp4(w: np.ndarray, T: int = 0):
+    """w float32 [N, K] (K % 16 == 0) -> (codes uint32 [N, K/8], scales uint8
+    [N, K/16] E4M3 patterns): with the tensor scale 2^T, per group of 16
+    s = the E4M3 value nearest to max|w| / (6 * 2^T), codes the nearest E2M1
+    values of w / (s * 2^T)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    codes = np.zeros((N, K // 8), dtype=np.uint32)
+    scales = np.zeros((N, K // 16), dtype=np.uint8)
+    st = _load().oracle_quantize_nvfp4(_p(w), N, K, int(T), _p(codes), _p(scales))
+    if st:
+        raise OracleError(st, "quantize_nvfp4")
+    return codes, scales
+
+
+def dequantize_nvfp4_exact(codes, scales, K: int, T: int = 0) -> np.ndarray:
+    """Exact code value * s * 2^T as float64 [N, K] (NaN where s is a NaN pattern)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint32)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    N = codes.shape[0]
+    out = np.zeros((N, K), dtype=np.float64)
+    st = _load().oracle_dequantize_nvfp4_exact(_p(codes), _p(scales), N, K, int(T), _p(out))
+    if st:
+        raise OracleError(st, "dequantize_nvfp4_exact")
+    return out
+
+
+def dequantize_nvfp4(codes, scales, K: int, out_dtype: int, T: int = 0):
+    """The exact values rounded to nearest even (as dequantize_mxfp8)."""
+    return _round_exact(dequantize_nvfp4_exact(codes, scales, K, T), out_dtype)
 
 
 def matmul_dense(x: np.ndarray, w: np.ndarray):

@@ -94,6 +94,36 @@
  *      its sign bit with the magnitude code nearest to |w| / 2^X (ties to
  *      the even mantissa; above 6 that is 6); codes are packed as in R3
  *      with b = 4.  Dequantized value: code value * 2^X.
+ *  R17 mxfp8 (the same passages: a block-scaled float mode with groups of
+ *      32 and 8-bit codes).  Taken, again from the microscaling definition:
+ *      a code is an E4M3 float -- bit 7 the sign, bits 6..3 an exponent e
+ *      with bias 7, bits 2..0 a mantissa m; value (1 + m/8) * 2^(e-7) for
+ *      e > 0 and (m/8) * 2^-6 for e = 0; the pattern e = 15, m = 7 is not a
+ *      number, so the largest finite magnitude is 448 = 1.75 * 2^8.  The
+ *      group scale is 2^X, byte X + 127, with X = floor(log2(max|w|)) - 8
+ *      (8 = the exponent of 448), clamped to [-127, 127], -127 for an
+ *      all-zero group.  A member's code is its sign bit with the finite
+ *      magnitude code nearest to |w| / 2^X (ties to the even code, i.e. the
+ *      even mantissa; above 448 that is 448); codes are bytes in row order
+ *      (R3 with b = 8).  Dequantized value: code value * 2^X.
+ *  R18 nvfp4 ([ET] "NVIDIA FP4 weight-only quantization", group size 16;
+ *      the same MLX passages: groups of 16, 4-bit codes).  Taken from the
+ *      NVFP4 format of that name: codes are E2M1 as in R16, packed as in
+ *      R16; each group of 16 stores one scale s, an E4M3 value (as in R17,
+ *      sign bit 0) written as its byte; the whole matrix shares a second
+ *      scale, here a power of two 2^T with T an integer in [-100, 100]
+ *      chosen by the caller (0: no second scale), which lets the group
+ *      scales use E4M3's normal range whatever the weights' magnitude.
+ *      s = the E4M3 magnitude nearest to max|w| / (6 * 2^T) (6 = the
+ *      largest E2M1 value; ties to the even code, above 448 that is 448),
+ *      and a member's code is its sign bit with the magnitude code nearest
+ *      to |w| / (s * 2^T) (ties to the even mantissa, above 6 that is 6),
+ *      or magnitude 0 when s = 0.  Dequantized value: code value * s * 2^T.
+ *      Exactness: an E4M3 value has at most 4 significant bits and an E2M1
+ *      one at most 2, so every midpoint of either grid times 6, times a
+ *      power of two or times s has at most 8 significant bits; the
+ *      nearest-value decisions below compare a weight with such products,
+ *      which binary64 holds exactly.
  *
  * Exactness of the binary64 comparisons used below.  Every finite fp16
  * value is an integer multiple of 2^-24 of magnitude < 2^16; q*s with
@@ -758,6 +788,147 @@ int oracle_dequantize_mxfp4_exact(const uint32_t *codes, const uint8_t *scales, 
     for (int64_t k = 0; k < K; ++k) {
       const int code = (int)((codes[n * wpr + k / 8] >> (4 * (k % 8))) & 15u);
       out[n * K + k] = ldexp(oracle_e2m1_to_double(code), (int)scales[n * ng + k / 32] - 127);
+    }
+  return OR_OK;
+}
+
+/* ---------------------------------------------------------------------
+ * E4M3 (readings R17, R18).
+ * ------------------------------------------------------------------- */
+/* magnitude of E4M3 code c (0..126): (m/8) 2^-6 for e = 0, (1 + m/8) 2^(e-7) else */
+static double e4m3_magnitude(int c) {
+  const int e = (c >> 3) & 15, m = c & 7;
+  return e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+}
+
+double oracle_e4m3_to_double(int code) {
+  if ((code & 0x7F) == 0x7F) return NAN;
+  const double v = e4m3_magnitude(code & 0x7F);
+  return (code & 0x80) ? -v : v;
+}
+
+/* the finite E4M3 magnitude code (0..126) nearest to a / d (a >= 0, d > 0),
+ * ties to the even code.  t > m  <=>  a > m * d, and m * d is exact (R18),
+ * so every decision is exact.  The magnitudes grow with the code: the
+ * candidate is the largest code whose magnitude is <= t, then the midpoint
+ * to the next code decides. */
+static int e4m3_nearest(double a, double d) {
+  int lo = 0, hi = 126;
+  while (lo < hi) { /* largest c with magnitude(c) * d <= a */
+    const int mid = (lo + hi + 1) / 2;
+    if (e4m3_magnitude(mid) * d <= a) lo = mid; else hi = mid - 1;
+  }
+  if (lo == 126) return 126;
+  const double m = 0.5 * (e4m3_magnitude(lo) + e4m3_magnitude(lo + 1)) * d;
+  if (a > m) return lo + 1;
+  if (a == m) return (lo & 1) ? lo + 1 : lo;
+  return lo;
+}
+
+/* the E2M1 magnitude code (0..7) nearest to a / s (a >= 0, s > 0), ties to
+ * the even mantissa, by the same exact midpoint comparisons */
+static int e2m1_nearest_scaled(double a, double s) {
+  int c = 0;
+  while (c < 7 && e2m1_magnitude(c + 1) * s <= a) ++c;
+  if (c == 7) return 7;
+  const double m = 0.5 * (e2m1_magnitude(c) + e2m1_magnitude(c + 1)) * s;
+  if (a > m) return c + 1;
+  if (a == m) return (c & 1) ? c + 1 : c;
+  return c;
+}
+
+/* ---------------------------------------------------------------------
+ * mxfp8 (reading R17).  codes [N, K/4] words (bytes in row order), scales
+ * [N, K/32] bytes holding X + 127; K a multiple of 32.
+ * ------------------------------------------------------------------- */
+int oracle_quantize_mxfp8(const float *w, int64_t N, int64_t K, uint32_t *codes,
+                          uint8_t *scales) {
+  if (N < 0 || K < 0 || K % 32) return OR_ERR_ARG;
+  for (int64_t i = 0; i < N * K; ++i)
+    if (!isfinite(w[i])) return OR_ERR_RANGE;
+  const int64_t wpr = K / 4, ng = K / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    uint32_t *row = codes + n * wpr;
+    memset(row, 0, (size_t)wpr * sizeof(uint32_t));
+    for (int64_t g = 0; g < ng; ++g) {
+      const float *grp = w + n * K + g * 32;
+      double amax = 0.0;
+      for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs((double)grp[i]));
+      int X = -127;
+      if (amax > 0.0) {
+        int ex;
+        frexp(amax, &ex); /* floor(log2(amax)) = ex - 1 */
+        X = ex - 1 - 8;
+        X = X < -127 ? -127 : (X > 127 ? 127 : X);
+      }
+      scales[n * ng + g] = (uint8_t)(X + 127);
+      const double d = ldexp(1.0, X);
+      for (int i = 0; i < 32; ++i) {
+        const int code = (signbit(grp[i]) ? 0x80 : 0) | e4m3_nearest(fabs((double)grp[i]), d);
+        const int64_t k = g * 32 + i;
+        row[k / 4] |= (uint32_t)code << (8 * (k % 4));
+      }
+    }
+  }
+  return OR_OK;
+}
+
+int oracle_dequantize_mxfp8_exact(const uint32_t *codes, const uint8_t *scales, int64_t N,
+                                  int64_t K, double *out) {
+  if (N < 0 || K < 0 || K % 32) return OR_ERR_ARG;
+  const int64_t wpr = K / 4, ng = K / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) {
+      const int code = (int)((codes[n * wpr + k / 4] >> (8 * (k % 4))) & 0xFFu);
+      out[n * K + k] = ldexp(oracle_e4m3_to_double(code), (int)scales[n * ng + k / 32] - 127);
+    }
+  return OR_OK;
+}
+
+/* ---------------------------------------------------------------------
+ * nvfp4 (reading R18).  codes [N, K/8] words (as mxfp4), scales [N, K/16]
+ * E4M3 bytes, tensor scale 2^T; K a multiple of 16.
+ * ------------------------------------------------------------------- */
+int oracle_quantize_nvfp4(const float *w, int64_t N, int64_t K, int T, uint32_t *codes,
+                          uint8_t *scales) {
+  if (N < 0 || K < 0 || K % 16 || T < -100 || T > 100) return OR_ERR_ARG;
+  for (int64_t i = 0; i < N * K; ++i)
+    if (!isfinite(w[i])) return OR_ERR_RANGE;
+  const int64_t wpr = K / 8, ng = K / 16;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    uint32_t *row = codes + n * wpr;
+    memset(row, 0, (size_t)wpr * sizeof(uint32_t));
+    for (int64_t g = 0; g < ng; ++g) {
+      const float *grp = w + n * K + g * 16;
+      double amax = 0.0;
+      for (int i = 0; i < 16; ++i) amax = fmax(amax, fabs((double)grp[i]));
+      const int sc = e4m3_nearest(amax, ldexp(6.0, T)); /* nearest to amax / (6 * 2^T) */
+      scales[n * ng + g] = (uint8_t)sc;
+      const double s = ldexp(e4m3_magnitude(sc), T);    /* the group's step, s * 2^T */
+      for (int i = 0; i < 16; ++i) {
+        const int mag = s > 0.0 ? e2m1_nearest_scaled(fabs((double)grp[i]), s) : 0;
+        const int code = (signbit(grp[i]) ? 8 : 0) | mag;
+        const int64_t k = g * 16 + i;
+        row[k / 8] |= (uint32_t)code << (4 * (k % 8));
+      }
+    }
+  }
+  return OR_OK;
+}
+
+int oracle_dequantize_nvfp4_exact(const uint32_t *codes, const uint8_t *scales, int64_t N,
+                                  int64_t K, int T, double *out) {
+  if (N < 0 || K < 0 || K % 16 || T < -100 || T > 100) return OR_ERR_ARG;
+  const int64_t wpr = K / 8, ng = K / 16;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) {
+      const int code = (int)((codes[n * wpr + k / 8] >> (4 * (k % 8))) & 15u);
+      out[n * K + k] =
+          ldexp(oracle_e2m1_to_double(code) * oracle_e4m3_to_double(scales[n * ng + k / 16]), T);
     }
   return OR_OK;
 }
