@@ -230,6 +230,7 @@ static int half_round_down(double x, uint16_t *out) {
 /* Round-to-nearest-even of a finite double to binary16 (overflow to inf
  * at and above 65520, the midpoint past the largest finite value). */
 uint16_t oracle_double_to_half_rne(double x) {
+  if (isnan(x)) return (uint16_t)(signbit(x) ? 0xFE00u : 0x7E00u); /* a quiet NaN stays NaN */
   uint16_t sign = (x < 0 || (x == 0 && signbit(x))) ? 0x8000u : 0;
   double mag = fabs(x);
   if (mag >= 65520.0) return sign | 0x7C00u;

@@ -154,6 +154,11 @@ def test_half_rne_matches_numpy():
     with np.errstate(over="ignore"):  # 65520 and above round to inf, as they should
         for x in xs:
             assert oracle.double_to_half_rne(float(x)) == int(np.float16(x).view(np.uint16)), x
+    # infinities stay infinite and NaN stays NaN (numpy agrees on the class)
+    for x in (np.inf, -np.inf, np.nan, -np.nan):
+        got = np.uint16(oracle.double_to_half_rne(float(x))).view(np.float16)
+        want = np.float16(x)
+        assert (np.isnan(got) and np.isnan(want)) or (got == want and np.signbit(got) == np.signbit(want))
 
 
 def test_bf16_rne_matches_torch():
