@@ -22,7 +22,7 @@ __all__ = [
     "aq_qweight_bytes", "aq_quantize", "aq_quantize_mse", "aq_quantize_zp", "aq_dequantize",
     "aq_embedding", "aq_qmv", "aq_qmm",
     "aq_quantized_matmul", "aq_gather_qmv", "aq_gather_qmm", "aq_gather_quantized_matmul",
-    "aq_quantize_mxfp4", "aq_dequantize_mxfp4", "aq_qmv_mxfp4", "aq_qmv_mxfp4_describe",
+    "aq_quantize_fp", "aq_dequantize_fp", "aq_qmv_fp", "aq_qmv_fp_describe", "FP_MODES",
 ]
 
 AQ_OK = 0
@@ -77,10 +77,10 @@ def load_library():
                           i32),
         "aq_gather_quantized_matmul": (
             [vp, i32, i64, vp, vp, vp, i64, i64, i64, vp, i32, i32, i32, vp, vp], i32),
-        "aq_quantize_mxfp4": ([vp, i32, i64, i64, vp, vp, vp], i32),
-        "aq_dequantize_mxfp4": ([vp, vp, i64, i64, vp, i32, vp], i32),
-        "aq_qmv_mxfp4": ([vp, i32, vp, vp, i64, i64, vp, vp], i32),
-        "aq_qmv_mxfp4_describe": ([i64, i64, i32, ctypes.c_char_p, i32], i32),
+        "aq_quantize_fp": ([vp, i32, i64, i64, i32, i32, vp, vp, vp], i32),
+        "aq_dequantize_fp": ([vp, vp, i64, i64, i32, i32, vp, i32, vp], i32),
+        "aq_qmv_fp": ([vp, i32, vp, vp, i64, i64, i32, i32, vp, vp], i32),
+        "aq_qmv_fp_describe": ([i64, i64, i32, i32, ctypes.c_char_p, i32], i32),
         "aq_bench_stream_read": ([vp, i64, i32, i32, vp, vp], i32),
         "aq_bench_read_oneshot": ([vp, i64, i32, i32, vp, vp], i32),
         "aq_bench_mfma_clock": ([i32, i32, vp, vp], i32),
@@ -355,59 +355,67 @@ def aq_bench_mfma_clock(blocks: int, iters: int, out=None, stream=None):
     return out
 
 
-# ---- mxfp4 ------------------------------------------------------------------------------
-# codes uint32 [N, K/8] (int32 in torch): E2M1 codes, 8 to a word; scales uint8
-# [N, K/32]: X + 127 for the group scale 2^X.
-def aq_quantize_mxfp4(w, codes=None, scales=None, stream=None):
-    """Quantize W [N, K] (fp32/fp16/bf16, device) to mxfp4 -> (codes, scales)."""
+# ---- block-scaled float modes ---------------------------------------------------------
+# mode -> (enum value, group size, code bits).  codes uint32 [N, K*bits/32]
+# (int32 in torch); scales uint8 [N, K/group]: X + 127 for the mx modes, an
+# E4M3 value for nvfp4 (with the tensor scale 2^tensor_exp).
+FP_MODES = {"mxfp4": (0, 32, 4), "nvfp4": (1, 16, 4), "mxfp8": (2, 32, 8)}
+
+
+def aq_quantize_fp(w, mode: str, tensor_exp: int = 0, codes=None, scales=None, stream=None):
+    """Quantize W [N, K] (fp32/fp16/bf16, device) in a block-scaled float mode
+    -> (codes, scales)."""
     torch = _torch()
     lib = load_library()
+    m, g, bits = FP_MODES[mode]
     N, K = w.shape
     if codes is None:
-        codes = torch.empty((N, K // 8), dtype=torch.int32, device=w.device)
+        codes = torch.empty((N, K * bits // 32), dtype=torch.int32, device=w.device)
     if scales is None:
-        scales = torch.empty((N, K // 32), dtype=torch.uint8, device=w.device)
-    st = lib.aq_quantize_mxfp4(_dev(w, "w"), _dtype_code(w), N, K, _dev(codes, "codes"),
-                               _dev(scales, "scales"), _stream(stream))
-    _check(st, "aq_quantize_mxfp4")
+        scales = torch.empty((N, K // g), dtype=torch.uint8, device=w.device)
+    st = lib.aq_quantize_fp(_dev(w, "w"), _dtype_code(w), N, K, m, tensor_exp,
+                            _dev(codes, "codes"), _dev(scales, "scales"), _stream(stream))
+    _check(st, "aq_quantize_fp")
     return codes, scales
 
 
-def aq_dequantize_mxfp4(codes, scales, K: int, out_dtype=None, out=None, stream=None):
-    """mxfp4 codes/scales -> W^ [N, K] in out_dtype (default fp32)."""
+def aq_dequantize_fp(codes, scales, K: int, mode: str, tensor_exp: int = 0, out_dtype=None,
+                     out=None, stream=None):
+    """Block-scaled codes/scales -> W^ [N, K] in out_dtype (default fp32)."""
     torch = _torch()
     lib = load_library()
     N = codes.shape[0]
     if out is None:
         out = torch.empty((N, K), dtype=out_dtype or torch.float32, device=codes.device)
-    st = lib.aq_dequantize_mxfp4(_dev(codes, "codes"), _dev(scales, "scales"), N, K,
-                                 _dev(out, "out"), _dtype_code(out), _stream(stream))
-    _check(st, "aq_dequantize_mxfp4")
+    st = lib.aq_dequantize_fp(_dev(codes, "codes"), _dev(scales, "scales"), N, K,
+                              FP_MODES[mode][0], tensor_exp, _dev(out, "out"), _dtype_code(out),
+                              _stream(stream))
+    _check(st, "aq_dequantize_fp")
     return out
 
 
-def aq_qmv_mxfp4(x, codes, scales, y=None, stream=None):
-    """y = x @ W^T for one row x [K] (or [1, K]) in fp16/bf16 and mxfp4 W [N, K]."""
+def aq_qmv_fp(x, codes, scales, mode: str, tensor_exp: int = 0, y=None, stream=None):
+    """y = x @ W^T for one row x [K] (or [1, K]) in fp16/bf16 and block-scaled W [N, K]."""
     torch = _torch()
     lib = load_library()
     K = x.shape[-1]
     if x.numel() != K:
-        raise ValueError("aq_qmv_mxfp4 takes one row of x")
+        raise ValueError("aq_qmv_fp takes one row of x")
     N = codes.shape[0]
     if y is None:
         y = torch.empty(tuple(x.shape[:-1]) + (N,), dtype=x.dtype, device=x.device)
-    st = lib.aq_qmv_mxfp4(_dev(x, "x"), _dtype_code(x), _dev(codes, "codes"),
-                          _dev(scales, "scales"), N, K, _dev(y, "y"), _stream(stream))
-    _check(st, "aq_qmv_mxfp4")
+    st = lib.aq_qmv_fp(_dev(x, "x"), _dtype_code(x), _dev(codes, "codes"), _dev(scales, "scales"),
+                       N, K, FP_MODES[mode][0], tensor_exp, _dev(y, "y"), _stream(stream))
+    _check(st, "aq_qmv_fp")
     return y
 
 
-def aq_qmv_mxfp4_describe(N: int, K: int, x_dtype="f16") -> str:
-    """Name and compile-time shape of the kernel aq_qmv_mxfp4 launches."""
+def aq_qmv_fp_describe(N: int, K: int, mode: str, x_dtype="f16") -> str:
+    """Name and compile-time shape of the kernel aq_qmv_fp launches."""
     lib = load_library()
     code = {"f16": AQ_F16, "bf16": AQ_BF16}[x_dtype]
     buf = ctypes.create_string_buffer(160)
-    n = lib.aq_qmv_mxfp4_describe(N, K, code, buf, len(buf))
+    n = lib.aq_qmv_fp_describe(N, K, FP_MODES[mode][0], code, buf, len(buf))
     if n < 0:
-        raise AQError(-1, "aq_qmv_mxfp4_describe")
+        raise AQError(-1, "aq_qmv_fp_describe")
     return buf.value.decode()

@@ -302,49 +302,66 @@ aq_status aq_gather_qmv(const void *x, aq_dtype x_dtype, int64_t T, const uint32
                                         static_cast<hipStream_t>(stream)));
 }
 
-// ---- mxfp4 ----------------------------------------------------------------------
+// ---- block-scaled float modes ---------------------------------------------------------
 
-static bool valid_mx(int64_t N, int64_t K) { return N >= 1 && K >= 32 && K % 32 == 0; }
+// group size of a mode; 0 for an unknown mode
+static int fp_group(int mode) {
+  return mode == AQ_MXFP4 || mode == AQ_MXFP8 ? 32 : (mode == AQ_NVFP4 ? 16 : 0);
+}
 
-aq_status aq_quantize_mxfp4(const void *w, aq_dtype w_dtype, int64_t N, int64_t K,
-                            uint32_t *codes, uint8_t *scales, void *stream) {
-  if (!valid_mx(N, K)) return AQ_ERR_INVALID_ARG;
+// shape, mode and tensor exponent (2^T only for nvfp4, |T| <= 100)
+static bool valid_fp(int64_t N, int64_t K, int mode, int T) {
+  const int g = fp_group(mode);
+  if (g == 0 || N < 1 || K < g || K % g != 0) return false;
+  return mode == AQ_NVFP4 ? (T >= -100 && T <= 100) : T == 0;
+}
+
+aq_status aq_quantize_fp(const void *w, aq_dtype w_dtype, int64_t N, int64_t K, aq_fp_mode mode,
+                         int tensor_exp, uint32_t *codes, uint8_t *scales, void *stream) {
+  if (!valid_fp(N, K, (int)mode, tensor_exp)) return AQ_ERR_INVALID_ARG;
   if (w_dtype != AQ_F32 && w_dtype != AQ_F16 && w_dtype != AQ_BF16) return AQ_ERR_INVALID_ARG;
   if (!w || !codes || !scales) return AQ_ERR_INVALID_ARG;
   if (!aligned16(w) || !aligned16(codes) || !aligned16(scales)) return AQ_ERR_ALIGNMENT;
-  return from_hip(aq::launch_quantize_mx(w, (int)w_dtype, N, K, codes, scales,
-                                         static_cast<hipStream_t>(stream)));
+  return from_hip(aq::launch_quantize_fp(w, (int)w_dtype, N, K, (int)mode, tensor_exp, codes,
+                                         scales, static_cast<hipStream_t>(stream)));
 }
 
-aq_status aq_dequantize_mxfp4(const uint32_t *codes, const uint8_t *scales, int64_t N, int64_t K,
-                              void *out, aq_dtype out_dtype, void *stream) {
-  if (!valid_mx(N, K)) return AQ_ERR_INVALID_ARG;
+aq_status aq_dequantize_fp(const uint32_t *codes, const uint8_t *scales, int64_t N, int64_t K,
+                           aq_fp_mode mode, int tensor_exp, void *out, aq_dtype out_dtype,
+                           void *stream) {
+  if (!valid_fp(N, K, (int)mode, tensor_exp)) return AQ_ERR_INVALID_ARG;
   if (out_dtype != AQ_F32 && out_dtype != AQ_F16 && out_dtype != AQ_BF16) return AQ_ERR_INVALID_ARG;
   if (!codes || !scales || !out) return AQ_ERR_INVALID_ARG;
   if (!aligned16(codes) || !aligned16(scales) || !aligned16(out)) return AQ_ERR_ALIGNMENT;
-  return from_hip(aq::launch_dequantize_mx(codes, scales, N, K, out, (int)out_dtype,
-                                           static_cast<hipStream_t>(stream)));
+  return from_hip(aq::launch_dequantize_fp(codes, scales, N, K, (int)mode, tensor_exp, out,
+                                           (int)out_dtype, static_cast<hipStream_t>(stream)));
 }
 
-aq_status aq_qmv_mxfp4(const void *x, aq_dtype x_dtype, const uint32_t *codes,
-                       const uint8_t *scales, int64_t N, int64_t K, void *y, void *stream) {
-  if (!valid_mx(N, K) || !valid_act_dtype(x_dtype)) return AQ_ERR_INVALID_ARG;
+aq_status aq_qmv_fp(const void *x, aq_dtype x_dtype, const uint32_t *codes,
+                    const uint8_t *scales, int64_t N, int64_t K, aq_fp_mode mode, int tensor_exp,
+                    void *y, void *stream) {
+  if (!valid_fp(N, K, (int)mode, tensor_exp) || !valid_act_dtype(x_dtype))
+    return AQ_ERR_INVALID_ARG;
   if (!x || !codes || !scales || !y) return AQ_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !aligned16(y))
     return AQ_ERR_ALIGNMENT;
-  if (K > aq::kMxMaxK) return AQ_ERR_UNSUPPORTED;
-  return from_hip(aq::launch_qmv_mx(x, (int)x_dtype, codes, scales, N, K, y,
-                                    static_cast<hipStream_t>(stream)));
+  // the kernels walk rows in 32-code chunks and hold x on chip
+  if (K % 32 != 0 || K > aq::kFpMaxK) return AQ_ERR_UNSUPPORTED;
+  return from_hip(aq::launch_qmv_fp(x, (int)x_dtype, codes, scales, N, K, (int)mode, tensor_exp,
+                                    y, static_cast<hipStream_t>(stream)));
 }
 
-int aq_qmv_mxfp4_describe(int64_t N, int64_t K, aq_dtype x_dtype, char *buf, int len) {
-  if (!valid_mx(N, K) || K > aq::kMxMaxK || !valid_act_dtype(x_dtype) || !buf || len < 1)
-    return -1;
+int aq_qmv_fp_describe(int64_t N, int64_t K, aq_fp_mode mode, aq_dtype x_dtype, char *buf,
+                       int len) {
+  if (!valid_fp(N, K, (int)mode, 0)) return -1;
+  if (K % 32 != 0 || K > aq::kFpMaxK || !valid_act_dtype(x_dtype) || !buf || len < 1) return -1;
   const char *xt = x_dtype == AQ_F16 ? "f16" : "bf16";
+  const char *mt = mode == AQ_MXFP4 ? "mxfp4" : (mode == AQ_NVFP4 ? "nvfp4" : "mxfp8");
   int cpl, ud, w, wpc;
-  aq::qmv1_mx_shape(N, K, cpl, ud, w, wpc);
-  if (cpl == 0) return snprintf(buf, (size_t)len, "qmv1_mx_lds_kernel<%s, W=%d>", xt, w);
-  return snprintf(buf, (size_t)len, "qmv1_mx_kernel<%s, CPL=%d, UD=%d, W=%d>", xt, cpl, ud, w);
+  aq::qmv1_fp_shape(N, K, (int)mode, cpl, ud, w, wpc);
+  if (cpl == 0) return snprintf(buf, (size_t)len, "qmv1_fp_lds_kernel<%s, %s, W=%d>", mt, xt, w);
+  return snprintf(buf, (size_t)len, "qmv1_fp_kernel<%s, %s, CPL=%d, UD=%d, W=%d>", mt, xt, cpl, ud,
+                  w);
 }
 
 }  // extern "C"

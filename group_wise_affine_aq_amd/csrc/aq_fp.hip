@@ -1,53 +1,56 @@
-// aq_mx.hip -- mxfp4: block-scaled 4-bit float codes, for gfx950.  Quantize,
-// dequantize and the M = 1 matrix-vector product.
+// aq_fp.hip -- the block-scaled float modes mxfp4, nvfp4 and mxfp8, for
+// gfx950: quantize, dequantize and the M = 1 matrix-vector product.
 //
-// Format (MLX "Quantization", the paragraph on the newer modes; "Quantizing a
-// Model for MLX", "Modes, bits and mixed recipes": groups of 32 weights with
-// 4-bit codes and one exponent per group in place of a scale and a bias; the
-// pages give no bit layout, so the microscaling (MX) definition of that name
-// is taken):
-//   a code is an E2M1 float: bit 3 the sign, bits 2..1 an exponent e with
-//   bias 1, bit 0 a mantissa m; its value is (1 + m/2) 2^(e-1) for e > 0 and
-//   m/2 for e = 0, so codes 0..7 are 0, 0.5, 1, 1.5, 2, 3, 4, 6;
-//   codes sit eight to a uint32 word, least significant nibble first (the
-//   bitstream of the affine format with 4-bit codes): a group is 4 words;
-//   the group's scale is 2^X, stored as the byte X + 127.
-// Quantize: X = floor(log2 max|w|) - 2 (2 being the exponent of 6, the
-// largest code value), clamped to [-127, 127], and -127 for a group of
-// zeros; each weight takes its own sign bit and the magnitude code nearest
-// to |w| / 2^X, ties to the even mantissa, saturating at 6.
+// The modes (MLX "Quantization", the paragraph on the newer modes;
+// "Quantizing a Model for MLX", "Modes, bits and mixed recipes": groups of
+// 32 / 16 / 32 weights with 4 / 4 / 8-bit float codes and a per-group scale
+// in place of an affine scale and bias; ExecuTorch "Quantization": nvfp4 is
+// NVIDIA's FP4 weight-only format at group size 16).  The pages give no bit
+// layout; the definitions of those names are taken:
+//   E2M1 code (4 bits): bit 3 sign, bits 2..1 exponent e (bias 1), bit 0
+//     mantissa m; (1 + m/2) 2^(e-1), or m/2 for e = 0: 0, 0.5, 1, 1.5, 2, 3,
+//     4, 6.  Eight to a uint32 word, least significant nibble first.
+//   E4M3 code (8 bits): bit 7 sign, bits 6..3 exponent e (bias 7), bits 2..0
+//     mantissa m; (1 + m/8) 2^(e-7), or (m/8) 2^-6 for e = 0; magnitude
+//     pattern 0x7F is not a number; largest 448.  Four to a word, in order.
+//   mxfp4: E2M1 codes, scale 2^X per 32 (byte X + 127),
+//     X = floor(log2 max|w|) - 2 clamped to [-127, 127] (-127 for zeros).
+//   mxfp8: E4M3 codes, scale 2^X per 32, X = floor(log2 max|w|) - 8.
+//   nvfp4: E2M1 codes, an E4M3 scale s per 16 (its byte), under a tensor
+//     scale 2^T: s = the E4M3 value nearest to max|w| / (6 * 2^T), value =
+//     code * s * 2^T.
+//   Codes are the nearest grid values of w / scale, ties to the even code,
+//   saturating at the largest finite magnitude; an nvfp4 group whose s is 0
+//   keeps only signs.
 //
-// Every decision is taken on binary32 bit patterns: non-negative floats
-// (subnormals included) order as their patterns do, and the thresholds
-// between neighbouring code values, times 2^X, are exact binary32 values
-// built from their exponent and mantissa fields, so no rounding mode or
-// denormal setting enters.  A dequantized value (a code value times 2^X:
-// at most two significant bits, exact in bf16 and binary32 down to 2^-128)
-// comes from the gfx950 scaled convert, or for the one exponent binary32
-// cannot scale by (X = 128) from the same bit construction, then is rounded
-// to nearest even into the output type.
+// Quantize decisions are exact: the E2M1 midpoints times 2^X or times
+// s * 2^T, and the E4M3 midpoints times 6 * 2^T, have at most 8 significant
+// bits, so they are exact binary32 values, and non-negative binary32 numbers
+// (subnormals included) order as their bit patterns, which is how they are
+// compared; mxfp8 rounds w / 2^X (a power-of-two scaling, exact) to E4M3 by
+// integer rounding of the binary32 pattern.
 //
-// The product (decode, M = 1): the E2M1 pairs go through the gfx950
-// scaled-convert instruction (v_cvt_scalef32_pk_f16_fp4 / _bf16_fp4, scale
-// 1.0: every code value is exact in fp16 and bf16) straight into v_dot2
-// against x; each 32-weight chunk's binary32 sum is scaled once by 2^X
-// (v_ldexp_f32).  Structure as in the affine decode kernel: x resident in
-// registers, a ring of CPL chunk loads per wave that crosses row
-// boundaries, finished rows parked in LDS and written in batches.
+// Dequantize and the product decode codes with the gfx950 scaled converts
+// (v_cvt_scalef32_pk_{f16,bf16}_{fp4,fp8}); with scale 1.0 every E2M1 and
+// E4M3 value is exact in fp16 and bf16.  The product (M = 1) has the layout
+// of the affine decode kernel: x resident in registers, a ring of chunk
+// loads per wave across row boundaries, rows parked in LDS; a chunk (32
+// codes) is dotted with x by v_dot2 in binary32 and scaled once per group.
 #include "aq_device.hpp"
 #include "aq_internal.hpp"
 
 namespace aq {
 namespace {
 
-typedef _Float16 fp4h2v __attribute__((ext_vector_type(2)));
-typedef __bf16 fp4b2v __attribute__((ext_vector_type(2)));
+typedef _Float16 fp_h2 __attribute__((ext_vector_type(2)));
+typedef __bf16 fp_b2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(1))) const uint8_t gbyte;
-typedef uint32_t mxu4 __attribute__((ext_vector_type(4)));
+typedef uint32_t fp_u4 __attribute__((ext_vector_type(4)));
 
-constexpr int kMxRound = 32;  // rows per wave between output flushes
+constexpr int kFpRound = 32;  // rows per wave between output flushes
+constexpr int kFpUnroll = 4;  // 8-weight units per thread and pass (quantize, dequantize)
 
-// ---- E2M1 arithmetic on binary32 bit patterns ----------------------------------------
+// ---- number formats on binary32 bit patterns ------------------------------------------
 
 // (1 + mant / 2^23) * 2^e as a binary32 pattern; exact for -129 <= e <= 127
 // with mant holding at most two leading bits (the subnormal shift drops
@@ -58,186 +61,371 @@ __device__ __forceinline__ uint32_t pow2_bits(uint32_t mant, int e) {
   return (0x800000u | mant) >> (1 - E);
 }
 
+// E2M1 midpoints 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 as (mantissa field, exponent)
+__device__ constexpr uint32_t kMidMant[7] = {0u, 0x400000u, 0x200000u, 0x600000u,
+                                             0x200000u, 0x600000u, 0x200000u};
+__device__ constexpr int kMidExp[7] = {-2, -1, 0, 0, 1, 1, 2};
+
 // the magnitude code (0..7) of a weight whose |w| has pattern a, given the
-// patterns of the seven midpoints 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 times
-// 2^X: a tie goes to the even mantissa, i.e. up across the midpoints into
-// codes 2, 4, 6 and down across the others
+// patterns of the seven midpoints times the scale: a tie goes to the even
+// mantissa, i.e. up across the midpoints into codes 2, 4, 6 and down across
+// the others
 __device__ __forceinline__ uint32_t e2m1_code(uint32_t a, const uint32_t (&t)[7]) {
   return (uint32_t)(a > t[0]) + (uint32_t)(a >= t[1]) + (uint32_t)(a > t[2]) +
          (uint32_t)(a >= t[3]) + (uint32_t)(a > t[4]) + (uint32_t)(a >= t[5]) +
          (uint32_t)(a > t[6]);
 }
 
-// binary32 pattern of code c (sign in bit 3) times 2^X, X in [-127, 128];
-// +-inf where that exceeds the binary32 range (X = 128, or 127 with |c| > 1.5).
-// Written with selects only: every lane takes the same path.
+// binary32 pattern of E2M1 code c (sign in bit 3) times 2^X, X in [-127, 128];
+// +-inf past the binary32 range.  Selects only: every lane takes one path.
 __device__ __forceinline__ uint32_t e2m1_value_bits(uint32_t c, int X) {
   const uint32_t sign = (c & 8u) << 28, m = c & 7u;
-  // m >= 1: value (1 + mb/2) 2^e with e = (m >> 1) - 1 and mb = m & 1 from
-  // m = 2 on (code 1 is 0.5 = 2^-1)
+  // m >= 1: (1 + mb/2) 2^e with e = (m >> 1) - 1, mb = m & 1 from m = 2 on
   const uint32_t mb = m >= 2u ? (m & 1u) << 22 : 0u;
   const int E = (int)(m >> 1) - 1 + X + 127;  // biased exponent, in [-1, 257]
   const uint32_t normal = ((uint32_t)E << 23) | mb;
-  const uint32_t sub = (0x800000u | mb) >> ((uint32_t)(1 - E) & 31u);  // used for E in {-1, 0}
+  const uint32_t sub = (0x800000u | mb) >> ((uint32_t)(1 - E) & 31u);  // for E in {-1, 0}
   uint32_t r = E >= 255 ? 0x7F800000u : (E >= 1 ? normal : sub);
   r = m == 0u ? 0u : r;
   return sign | r;
 }
 
-// ---- quantize and dequantize: one thread per word (8 codes) ----------------------------
-// A workgroup takes kMxUnroll * 256 consecutive words per pass, word
-// base + u * 256 + thread, so every load and store instruction of a wave
-// covers one contiguous span and each thread has kMxUnroll words in flight.
-// Four consecutive words are one group: the four lanes of a DPP quad.
-constexpr int kMxUnroll = 4;
-
-__device__ __forceinline__ uint32_t quad_max(uint32_t a) {
-  uint32_t b = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
-  a = a > b ? a : b;
-  b = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x4E, 0xF, 0xF, false);           // [2,3,0,1]
-  return a > b ? a : b;
+// value of an E4M3 magnitude code c (0..127) as a binary32 (exact; NaN for 0x7F)
+__device__ __forceinline__ float e4m3_mag(uint32_t c) {
+  const int e = (int)(c >> 3), m = (int)(c & 7u);
+  const float v = e ? __builtin_ldexpf((float)(8 + m), e - 10) : __builtin_ldexpf((float)m, -9);
+  return c == 0x7Fu ? __builtin_nanf("") : v;
 }
 
-template <int WDT>
-__global__ __launch_bounds__(256) void quantize_mx_kernel(const void *__restrict__ w,
-                                                          int64_t words,
+// the finite E4M3 magnitude code nearest to t (t >= 0 exact, t < 2^10),
+// ties to the even code, saturating at 448 (code 126)
+__device__ __forceinline__ uint32_t e4m3_round(float t) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, t);
+  if (b >= 0x3C800000u) {  // t >= 2^-6: normal; round the mantissa to 3 bits
+    const uint32_t r = (b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20;
+    const int c = (int)r - (120 << 3);  // exponent bias 127 -> 7
+    return c > 126 ? 126u : (uint32_t)c;
+  }
+  return (uint32_t)__builtin_rintf(t * 512.0f);  // steps of 2^-9: 0..8
+}
+
+// maximum over the lanes of a DPP quad / of a lane pair
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t pair_max(uint32_t a) {
+  return umax(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t quad_max(uint32_t a) {
+  a = pair_max(a);
+  return umax(a, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x4E, 0xF, 0xF, false));
+}
+
+// ---- quantize: one thread per 8 weights ------------------------------------------------
+// A workgroup takes kFpUnroll * 256 consecutive units per pass, unit
+// base + u * 256 + thread, so every load and store instruction of a wave
+// covers one contiguous span.  A group is the 4 (mxfp4, mxfp8) or 2 (nvfp4)
+// lanes of a DPP quad or pair; the unit count is a multiple of that, so a
+// group's lanes leave the loop together.
+template <int MODE, int WDT>
+__global__ __launch_bounds__(256) void quantize_fp_kernel(const void *__restrict__ w,
+                                                          int64_t units, int T,
                                                           uint32_t *__restrict__ codes,
                                                           uint8_t *__restrict__ scales) {
-  // midpoints as (mantissa field, exponent)
-  constexpr uint32_t kMant[7] = {0u, 0x400000u, 0x200000u, 0x600000u, 0x200000u, 0x600000u,
-                                 0x200000u};
-  constexpr int kExp[7] = {-2, -1, 0, 0, 1, 1, 2};
-  const int64_t pass = (int64_t)gridDim.x * (256 * kMxUnroll);
-  for (int64_t base = (int64_t)blockIdx.x * (256 * kMxUnroll); base < words; base += pass) {
-    float v[kMxUnroll][8];
+  const int64_t pass = (int64_t)gridDim.x * (256 * kFpUnroll);
+  for (int64_t base = (int64_t)blockIdx.x * (256 * kFpUnroll); base < units; base += pass) {
+    float v[kFpUnroll][8];
 #pragma unroll
-    for (int u = 0; u < kMxUnroll; ++u) {
+    for (int u = 0; u < kFpUnroll; ++u) {
       const int64_t t = base + u * 256 + threadIdx.x;
-      if (t < words) load8<WDT>(w, t * 8, v[u]);
+      if (t < units) load8<WDT>(w, t * 8, v[u]);
     }
 #pragma unroll
-    for (int u = 0; u < kMxUnroll; ++u) {
+    for (int u = 0; u < kFpUnroll; ++u) {
       const int64_t t = base + u * 256 + threadIdx.x;
-      if (t >= words) break;  // words is a multiple of 4: quads leave together
-      uint32_t amax = 0;
+      if (t >= units) break;
+      uint32_t a[8], amax = 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const uint32_t a = __builtin_bit_cast(uint32_t, v[u][i]) & 0x7FFFFFFFu;
-        amax = a > amax ? a : amax;
+        a[i] = __builtin_bit_cast(uint32_t, v[u][i]) & 0x7FFFFFFFu;
+        amax = umax(amax, a[i]);
       }
-      amax = quad_max(amax);
-      // floor(log2 max) = biased exponent - 127 for a normal maximum; a zero
-      // or subnormal maximum (biased exponent 0) and the exponent 1 both clamp
-      const int eb = (int)(amax >> 23);
-      const int X = (eb < 2 ? 2 : eb) - 129;
-      uint32_t th[7];
+      if constexpr (MODE == FP_NVFP4) {
+        amax = pair_max(amax);
+        // s: the E4M3 code nearest to amax / (6 * 2^T).  The binary32
+        // quotient is within a few ulps, so its rounding is at most one code
+        // off; the exact tests against the midpoints between neighbouring
+        // codes, times 6 * 2^T, settle it (a tie keeps the even code).
+        const float amaxf = __builtin_bit_cast(float, amax);
+        uint32_t sc = e4m3_round(__builtin_ldexpf(amaxf * (1.0f / 6.0f), -T));
+        auto bound = [&](uint32_t c) {  // pattern of 6 * 2^T * (v(c) + v(c + 1)) / 2
+          return __builtin_bit_cast(
+              uint32_t, __builtin_ldexpf(3.0f * (e4m3_mag(c) + e4m3_mag(c + 1)), T));
+        };
+        if (sc > 0) {
+          const uint32_t lo = bound(sc - 1);
+          if (amax < lo || (amax == lo && (sc & 1u))) --sc;
+        }
+        if (sc < 126) {
+          const uint32_t hi = bound(sc);
+          if (amax > hi || (amax == hi && (sc & 1u))) ++sc;
+        }
+        const float step = __builtin_ldexpf(e4m3_mag(sc), T);  // s * 2^T, exact
+        uint32_t th[7];
 #pragma unroll
-      for (int k = 0; k < 7; ++k) th[k] = pow2_bits(kMant[k], kExp[k] + X);
-      uint32_t q = 0;
+        for (int k = 0; k < 7; ++k)
+          th[k] = __builtin_bit_cast(
+              uint32_t, __builtin_bit_cast(float, pow2_bits(kMidMant[k], kMidExp[k])) * step);
+        uint32_t q = 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t b = __builtin_bit_cast(uint32_t, v[u][i]);
-        q |= (e2m1_code(b & 0x7FFFFFFFu, th) | ((b >> 31) << 3)) << (4 * i);
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t mag = sc == 0 ? 0u : e2m1_code(a[i], th);
+          q |= (mag | ((__builtin_bit_cast(uint32_t, v[u][i]) >> 31) << 3)) << (4 * i);
+        }
+        codes[t] = q;
+        if ((threadIdx.x & 1) == 0) scales[t >> 1] = (uint8_t)sc;
+      } else {
+        amax = quad_max(amax);
+        // floor(log2 max) = biased exponent - 127 for a normal maximum; a
+        // zero or subnormal maximum has biased exponent 0 and clamps
+        constexpr int EMAX = MODE == FP_MXFP4 ? 2 : 8;  // exponent of the largest code value
+        const int eb = (int)(amax >> 23);
+        int X = eb - 127 - EMAX;
+        X = X < -127 ? -127 : X;
+        if constexpr (MODE == FP_MXFP4) {
+          uint32_t th[7];
+#pragma unroll
+          for (int k = 0; k < 7; ++k) th[k] = pow2_bits(kMidMant[k], kMidExp[k] + X);
+          uint32_t q = 0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            q |= (e2m1_code(a[i], th) | ((__builtin_bit_cast(uint32_t, v[u][i]) >> 31) << 3))
+                 << (4 * i);
+          codes[t] = q;
+        } else {
+          // |w| / 2^X < 512 exactly (a power-of-two scaling of a normal |w|;
+          // a subnormal |w| is its integer mantissa times 2^-149), then
+          // rounded to E4M3; a result below 2^-126 rounds to code 0 anyway
+          uint32_t q[2] = {0u, 0u};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float tq = (a[i] >> 23) ? __builtin_ldexpf(__builtin_bit_cast(float, a[i]), -X)
+                                          : __builtin_ldexpf((float)a[i], -149 - X);
+            const uint32_t c = e4m3_round(tq) | ((__builtin_bit_cast(uint32_t, v[u][i]) >> 31) << 7);
+            q[i >> 2] |= c << (8 * (i & 3));
+          }
+          reinterpret_cast<uint2 *>(codes)[t] = make_uint2(q[0], q[1]);
+        }
+        if ((threadIdx.x & 3) == 0) scales[t >> 2] = (uint8_t)(X + 127);
       }
-      codes[t] = q;
-      if ((threadIdx.x & 3) == 0) scales[t >> 2] = (uint8_t)(X + 127);
     }
   }
 }
 
+// ---- dequantize: one thread per 8 weights ----------------------------------------------
+
+// eight binary32 patterns -> out[8 t .. 8 t + 7] in OUT
 template <int OUT>
-__global__ __launch_bounds__(256) void dequantize_mx_kernel(const uint32_t *__restrict__ codes,
-                                                            const uint8_t *__restrict__ scales,
-                                                            int64_t words, void *__restrict__ out) {
-  const int64_t pass = (int64_t)gridDim.x * (256 * kMxUnroll);
-  for (int64_t base = (int64_t)blockIdx.x * (256 * kMxUnroll); base < words; base += pass) {
-    uint32_t wd[kMxUnroll], sc[kMxUnroll];
+__device__ __forceinline__ void store8(void *out, int64_t t, const uint32_t (&f)[8]) {
+  if constexpr (OUT == X_F32) {
+    uint4 *o = reinterpret_cast<uint4 *>(out) + 2 * t;
+    o[0] = make_uint4(f[0], f[1], f[2], f[3]);
+    o[1] = make_uint4(f[4], f[5], f[6], f[7]);
+  } else {
+    uint32_t h[4];
 #pragma unroll
-    for (int u = 0; u < kMxUnroll; ++u) {
+    for (int j = 0; j < 4; ++j) {
+      const float a = __builtin_bit_cast(float, f[2 * j]);
+      const float b = __builtin_bit_cast(float, f[2 * j + 1]);
+      if constexpr (OUT == X_F16)
+        h[j] = (uint32_t)f32_to_f16_rne(a) | ((uint32_t)f32_to_f16_rne(b) << 16);
+      else
+        h[j] = (uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16);
+    }
+    reinterpret_cast<uint4 *>(out)[t] = make_uint4(h[0], h[1], h[2], h[3]);
+  }
+}
+
+// the two fp16 values of a convert's result as binary32 patterns
+__device__ __forceinline__ void h2_to_f32(fp_h2 h, uint32_t &lo, uint32_t &hi) {
+  lo = __builtin_bit_cast(uint32_t, (float)h[0]);
+  hi = __builtin_bit_cast(uint32_t, (float)h[1]);
+}
+
+template <int MODE, int OUT>
+__global__ __launch_bounds__(256) void dequantize_fp_kernel(const uint32_t *__restrict__ codes,
+                                                            const uint8_t *__restrict__ scales,
+                                                            int64_t units, int T,
+                                                            void *__restrict__ out) {
+  constexpr int WPU = MODE == FP_MXFP8 ? 2 : 1;  // code words per unit of 8 weights
+  const int64_t pass = (int64_t)gridDim.x * (256 * kFpUnroll);
+  for (int64_t base = (int64_t)blockIdx.x * (256 * kFpUnroll); base < units; base += pass) {
+    uint32_t wd[kFpUnroll][WPU], sc[kFpUnroll];
+#pragma unroll
+    for (int u = 0; u < kFpUnroll; ++u) {
       const int64_t t = base + u * 256 + threadIdx.x;
-      if (t < words) {
-        wd[u] = codes[t];
-        sc[u] = scales[t >> 2];
+      if (t < units) {
+        if constexpr (WPU == 2) {
+          const uint2 p = reinterpret_cast<const uint2 *>(codes)[t];
+          wd[u][0] = p.x;
+          wd[u][1] = p.y;
+        } else {
+          wd[u][0] = codes[t];
+        }
+        sc[u] = scales[MODE == FP_NVFP4 ? t >> 1 : t >> 2];
       }
     }
 #pragma unroll
-    for (int u = 0; u < kMxUnroll; ++u) {
+    for (int u = 0; u < kFpUnroll; ++u) {
       const int64_t t = base + u * 256 + threadIdx.x;
-      if (t >= words) break;
-      const int X = (int)sc[u] - 127;
-      // Every code value times 2^X has at most two significant bits, so it
-      // is exact in bf16 (subnormals down to 2^-128 included) and binary32
-      // is its upper half.  The scaled convert (code pair * 2^X, the scale
-      // 2^X given as a binary32) returns exactly that pair, +-inf past the
-      // range, for X up to 127, checked on the MI355X for every code pair
-      // and exponent.  X = 128 (scale byte 255) has no binary32 scale: those
-      // groups take the bit construction.
-      const float scale = __builtin_bit_cast(float, (uint32_t)(X + 127) << 23);
-      uint32_t pr[4];
-      pr[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[u], scale, 0));
-      pr[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[u], scale, 1));
-      pr[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[u], scale, 2));
-      pr[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[u], scale, 3));
+      if (t >= units) break;
       uint32_t f[8];
+      if constexpr (MODE == FP_MXFP4) {
+        const int X = (int)sc[u] - 127;
+        // A code value times 2^X has at most two significant bits: exact in
+        // bf16 (subnormals down to 2^-128 included), and binary32 is its
+        // upper half.  The scaled convert (code pair * 2^X, the scale given
+        // as a binary32) returns exactly that pair, +-inf past the range,
+        // for X up to 127 (checked on the MI355X for every code pair and
+        // exponent); X = 128 (byte 255) has no binary32 scale and takes the
+        // bit construction.
+        const float scale = __builtin_bit_cast(float, (uint32_t)(X + 127) << 23);
+        uint32_t pr[4];
+        pr[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[u][0], scale, 0));
+        pr[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[u][0], scale, 1));
+        pr[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[u][0], scale, 2));
+        pr[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd[u][0], scale, 3));
+        const bool edge = X > 127;
+        if constexpr (OUT == X_BF16) {
+          if (!edge) {
+            reinterpret_cast<uint4 *>(out)[t] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+            continue;
+          }
+        }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f[2 * j] = pr[j] << 16;
-        f[2 * j + 1] = pr[j] & 0xFFFF0000u;
-      }
-      const bool edge = X > 127;
-      if (edge) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) f[j] = e2m1_value_bits((wd[u] >> (4 * j)) & 15u, X);
-      }
-      if constexpr (OUT == X_F32) {
-        uint4 *o = reinterpret_cast<uint4 *>(out) + 2 * t;
-        o[0] = make_uint4(f[0], f[1], f[2], f[3]);
-        o[1] = make_uint4(f[4], f[5], f[6], f[7]);
-      } else if constexpr (OUT == X_F16) {
-        uint32_t h[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          h[j] = (uint32_t)f32_to_f16_rne(__builtin_bit_cast(float, f[2 * j])) |
-                 ((uint32_t)f32_to_f16_rne(__builtin_bit_cast(float, f[2 * j + 1])) << 16);
-        reinterpret_cast<uint4 *>(out)[t] = make_uint4(h[0], h[1], h[2], h[3]);
-      } else {
+        for (int j = 0; j < 4; ++j) {
+          f[2 * j] = pr[j] << 16;
+          f[2 * j + 1] = pr[j] & 0xFFFF0000u;
+        }
         if (edge) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            pr[j] = (uint32_t)f32_to_bf16_rne(__builtin_bit_cast(float, f[2 * j])) |
-                    ((uint32_t)f32_to_bf16_rne(__builtin_bit_cast(float, f[2 * j + 1])) << 16);
+          for (int j = 0; j < 8; ++j) f[j] = e2m1_value_bits((wd[u][0] >> (4 * j)) & 15u, X);
         }
-        reinterpret_cast<uint4 *>(out)[t] = make_uint4(pr[0], pr[1], pr[2], pr[3]);
+      } else if constexpr (MODE == FP_NVFP4) {
+        // |code value| (exact in fp16) times |s| * 2^T: at most six
+        // significant bits and a normal binary32 (|T| <= 100), so the
+        // product is exact; the signs of code and scale are applied to the
+        // bits afterwards.  (Multiplying signed values, the compiler fuses
+        // product and fp16 conversion into one mixed-precision FMA with a +0
+        // addend, which turns a -0 product into +0.)
+        const float step = __builtin_ldexpf(e4m3_mag(sc[u] & 0x7Fu), T);
+        const uint32_t ssign = (sc[u] & 0x80u) << 24;
+        const uint32_t mags = wd[u][0] & 0x77777777u;
+        const fp_h2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(mags, 1.0f, 0);
+        const fp_h2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(mags, 1.0f, 1);
+        const fp_h2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(mags, 1.0f, 2);
+        const fp_h2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(mags, 1.0f, 3);
+        const fp_h2 ps[4] = {p0, p1, p2, p3};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f[2 * j] = __builtin_bit_cast(uint32_t, (float)ps[j][0] * step) ^ ssign ^
+                     (((wd[u][0] >> (8 * j + 3)) & 1u) << 31);
+          f[2 * j + 1] = __builtin_bit_cast(uint32_t, (float)ps[j][1] * step) ^ ssign ^
+                         (((wd[u][0] >> (8 * j + 7)) & 1u) << 31);
+        }
+      } else {
+        // E4M3 value (exact in fp16) times 2^X: ldexp rounds only where the
+        // result leaves the binary32 range (to +-inf); binary32 subnormals
+        // down to 2^-136 hold every such value exactly
+        const int X = (int)sc[u] - 127;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const fp_h2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wd[u][h], 1.0f, false);
+          const fp_h2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wd[u][h], 1.0f, true);
+          f[4 * h] = __builtin_bit_cast(uint32_t, __builtin_ldexpf((float)lo[0], X));
+          f[4 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_ldexpf((float)lo[1], X));
+          f[4 * h + 2] = __builtin_bit_cast(uint32_t, __builtin_ldexpf((float)hi[0], X));
+          f[4 * h + 3] = __builtin_bit_cast(uint32_t, __builtin_ldexpf((float)hi[1], X));
+        }
       }
+      store8<OUT>(out, t, f);
     }
   }
 }
 
 // ---- the M = 1 product -------------------------------------------------------------
 
-// sum over the 8 codes of word w of x * code value, x given as 4 packed pairs
-// in natural order (the convert's byte select b yields codes 2b and 2b + 1)
+// sum over the 8 E2M1 codes of word w of x * code value, x as 4 packed pairs
+// in natural order (byte select b yields codes 2b and 2b + 1)
 __device__ __forceinline__ float fp4_word_dot(f16_t, uint32_t w, const uint32_t *xp, float acc) {
   acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0),
-                               __builtin_bit_cast(fp4h2v, xp[0]), acc, false);
+                               __builtin_bit_cast(fp_h2, xp[0]), acc, false);
   acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1),
-                               __builtin_bit_cast(fp4h2v, xp[1]), acc, false);
+                               __builtin_bit_cast(fp_h2, xp[1]), acc, false);
   acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2),
-                               __builtin_bit_cast(fp4h2v, xp[2]), acc, false);
+                               __builtin_bit_cast(fp_h2, xp[2]), acc, false);
   acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3),
-                               __builtin_bit_cast(fp4h2v, xp[3]), acc, false);
+                               __builtin_bit_cast(fp_h2, xp[3]), acc, false);
   return acc;
 }
 __device__ __forceinline__ float fp4_word_dot(bf16_t, uint32_t w, const uint32_t *xp, float acc) {
   acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0),
-                                        __builtin_bit_cast(fp4b2v, xp[0]), acc, false);
+                                        __builtin_bit_cast(fp_b2, xp[0]), acc, false);
   acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1),
-                                        __builtin_bit_cast(fp4b2v, xp[1]), acc, false);
+                                        __builtin_bit_cast(fp_b2, xp[1]), acc, false);
   acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2),
-                                        __builtin_bit_cast(fp4b2v, xp[2]), acc, false);
+                                        __builtin_bit_cast(fp_b2, xp[2]), acc, false);
   acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3),
-                                        __builtin_bit_cast(fp4b2v, xp[3]), acc, false);
+                                        __builtin_bit_cast(fp_b2, xp[3]), acc, false);
   return acc;
+}
+// the same for the 4 E4M3 codes of word w (x as 2 packed pairs)
+__device__ __forceinline__ float fp8_word_dot(f16_t, uint32_t w, const uint32_t *xp, float acc) {
+  acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false),
+                               __builtin_bit_cast(fp_h2, xp[0]), acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true),
+                               __builtin_bit_cast(fp_h2, xp[1]), acc, false);
+  return acc;
+}
+__device__ __forceinline__ float fp8_word_dot(bf16_t, uint32_t w, const uint32_t *xp, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false),
+                                        __builtin_bit_cast(fp_b2, xp[0]), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true),
+                                        __builtin_bit_cast(fp_b2, xp[1]), acc, false);
+  return acc;
+}
+
+// per-mode chunk layout: a chunk is 32 codes (VW 16-byte vectors) and its
+// scale bytes (one exponent, or two E4M3 scales for nvfp4's two groups)
+template <int MODE> struct chunk_fmt {
+  static constexpr int VW = MODE == FP_MXFP8 ? 2 : 1;
+  static constexpr int SB = MODE == FP_NVFP4 ? 2 : 1;
+};
+
+// x * w^ over one chunk, the chunk's scale applied
+template <int MODE, typename XT>
+__device__ __forceinline__ float chunk_sum(const fp_u4 (&cw)[chunk_fmt<MODE>::VW], uint32_t sb,
+                                           const uint32_t *xv) {
+  if constexpr (MODE == FP_MXFP4) {
+    float s = 0.f;
+    s = fp4_word_dot(XT{}, cw[0][0], xv, s);
+    s = fp4_word_dot(XT{}, cw[0][1], xv + 4, s);
+    s = fp4_word_dot(XT{}, cw[0][2], xv + 8, s);
+    s = fp4_word_dot(XT{}, cw[0][3], xv + 12, s);
+    return __builtin_ldexpf(s, (int)sb - 127);
+  } else if constexpr (MODE == FP_NVFP4) {
+    float s0 = 0.f, s1 = 0.f;
+    s0 = fp4_word_dot(XT{}, cw[0][0], xv, s0);
+    s0 = fp4_word_dot(XT{}, cw[0][1], xv + 4, s0);
+    s1 = fp4_word_dot(XT{}, cw[0][2], xv + 8, s1);
+    s1 = fp4_word_dot(XT{}, cw[0][3], xv + 12, s1);
+    return s0 * e4m3_mag(sb & 0xFFu) + s1 * e4m3_mag(sb >> 8);
+  } else {
+    float s = 0.f;
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s = fp8_word_dot(XT{}, cw[v][j], xv + 8 * v + 2 * j, s);
+    return __builtin_ldexpf(s, (int)sb - 127);
+  }
 }
 
 // a wave-uniform global pointer (its address goes to scalar registers)
@@ -248,40 +436,56 @@ __device__ __forceinline__ gbyte *wave_ptr(const void *p) {
   return reinterpret_cast<gbyte *>(((uint64_t)hi << 32) | lo);
 }
 
+// code bytes and scale bytes per row
+template <int MODE>
+__device__ __forceinline__ void row_bytes(int64_t K, int64_t &cb, int64_t &sbb) {
+  cb = MODE == FP_MXFP8 ? K : K / 2;
+  sbb = MODE == FP_NVFP4 ? K / 16 : K / 32;
+}
+
 // The decode kernel for K <= 64 * 32 * CPL.  Lane l owns chunks l, l + 64,
-// ... of every row (a chunk = 32 codes = 16 bytes, so each load instruction
-// of a wave reads 1 KB of one row) and keeps the matching x chunks in
-// registers.  Rows are dealt to waves round-robin (row gw, gw + TW, ...);
-// the ring holds the D = CPL * UD chunk loads of UD rows and each slot is
-// reloaded with the next rows' chunk as soon as it is consumed.
-template <typename XT, int CPL, int UD, int W>
-__global__ __launch_bounds__(64 * W) void qmv1_mx_kernel(const uint16_t *__restrict__ x,
+// ... of every row (each load instruction of a wave reads 64 consecutive
+// 16-byte pieces of one row) and keeps the matching x chunks in registers.
+// Rows are dealt to waves round-robin (row gw, gw + TW, ...); the ring holds
+// the D = CPL * UD chunk loads of UD rows and each slot is reloaded with the
+// next rows' chunk as soon as it is consumed.
+template <int MODE, typename XT, int CPL, int UD, int W>
+__global__ __launch_bounds__(64 * W) void qmv1_fp_kernel(const uint16_t *__restrict__ x,
                                                          const uint32_t *__restrict__ codes,
                                                          const uint8_t *__restrict__ scales,
-                                                         int64_t N, int64_t K,
+                                                         int64_t N, int64_t K, int T,
                                                          uint16_t *__restrict__ y) {
+  using CF = chunk_fmt<MODE>;
   constexpr int D = CPL * UD, CP = 64 * CPL;
   constexpr int XS = (4 * CP + 64 * W - 1) / (64 * W);  // x loads per thread
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int nch = (int)(K >> 5);
+  int64_t rcb, rsb;
+  row_bytes<MODE>(K, rcb, rsb);
   const int64_t TW = (int64_t)gridDim.x * W, gw = (int64_t)blockIdx.x * W + wave;
   const int nunits = gw < N ? (int)((N - 1 - gw) / TW + 1) : 0;
   // x as 16-byte quarters of chunks, quarter-major (quarter j of chunk c at
   // j * CP + c: 64 lanes reading one quarter hit consecutive addresses);
   // chunks past the row are zero
   uint4 *xl = reinterpret_cast<uint4 *>(smem);
-  uint16_t *obuf = reinterpret_cast<uint16_t *>(smem + (size_t)CP * 64) + (size_t)wave * kMxRound;
+  uint16_t *obuf = reinterpret_cast<uint16_t *>(smem + (size_t)CP * 64) + (size_t)wave * kFpRound;
 
-  mxu4 cb[D];
+  fp_u4 cb[D][CF::VW];
   uint32_t sb[D];
   auto load = [&](int d, int64_t row) {
     const int c0 = (d % CPL) * 64 + lane;
     const uint32_t c = (uint32_t)(c0 < nch ? c0 : nch - 1);  // padding lanes re-read the last
-    gbyte *rc = wave_ptr(codes + row * (K >> 3));
-    gbyte *rs = wave_ptr(scales + row * (int64_t)nch);
-    cb[d] = *reinterpret_cast<__attribute__((address_space(1))) const mxu4 *>(rc + c * 16u);
-    sb[d] = rs[c];
+    gbyte *rc = wave_ptr(reinterpret_cast<const uint8_t *>(codes) + row * rcb);
+    gbyte *rs = wave_ptr(scales + row * rsb);
+#pragma unroll
+    for (int v = 0; v < CF::VW; ++v)
+      cb[d][v] = *reinterpret_cast<__attribute__((address_space(1))) const fp_u4 *>(
+          rc + (c * CF::VW + v) * 16u);
+    if constexpr (CF::SB == 2)
+      sb[d] = *reinterpret_cast<__attribute__((address_space(1))) const uint16_t *>(rs + c * 2u);
+    else
+      sb[d] = rs[c];
   };
 
   // x loads, then the first ring fill, then x into LDS: the weight loads
@@ -296,7 +500,7 @@ __global__ __launch_bounds__(64 * W) void qmv1_mx_kernel(const uint16_t *__restr
   }
   __builtin_amdgcn_sched_barrier(0);
   {
-    const int nu = nunits < kMxRound ? nunits : kMxRound;
+    const int nu = nunits < kFpRound ? nunits : kFpRound;
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       const int i = d / CPL < nu ? d / CPL : (nu > 0 ? nu - 1 : 0);
@@ -321,8 +525,8 @@ __global__ __launch_bounds__(64 * W) void qmv1_mx_kernel(const uint16_t *__restr
       xv[p][4 * j] = v.x; xv[p][4 * j + 1] = v.y; xv[p][4 * j + 2] = v.z; xv[p][4 * j + 3] = v.w;
     }
 
-  for (int u0 = 0; u0 < nunits; u0 += kMxRound) {
-    const int nu = nunits - u0 < kMxRound ? nunits - u0 : kMxRound;
+  for (int u0 = 0; u0 < nunits; u0 += kFpRound) {
+    const int nu = nunits - u0 < kFpRound ? nunits - u0 : kFpRound;
     auto row_of = [&](int i) -> int64_t {
       i = i < nu ? i : nu - 1;  // past the end: harmless re-read of the last row
       return gw + (int64_t)(u0 + i) * TW;
@@ -337,14 +541,10 @@ __global__ __launch_bounds__(64 * W) void qmv1_mx_kernel(const uint16_t *__restr
     float acc = 0.f;
     auto consume = [&](int d, int unit) {
       const int p = d % CPL;
-      float s = 0.f;
-      s = fp4_word_dot(XT{}, cb[d][0], &xv[p][0], s);
-      s = fp4_word_dot(XT{}, cb[d][1], &xv[p][4], s);
-      s = fp4_word_dot(XT{}, cb[d][2], &xv[p][8], s);
-      s = fp4_word_dot(XT{}, cb[d][3], &xv[p][12], s);
-      acc += __builtin_ldexpf(s, (int)sb[d] - 127);
+      acc += chunk_sum<MODE, XT>(cb[d], sb[d], xv[p]);
       if (p == CPL - 1) {
-        const float v = wave_sum(acc);
+        float v = wave_sum(acc);
+        if constexpr (MODE == FP_NVFP4) v = __builtin_ldexpf(v, T);
         if (lane == 0) obuf[unit] = xtraits<XT>::from_f32(v);
         acc = 0.f;
       }
@@ -369,43 +569,50 @@ __global__ __launch_bounds__(64 * W) void qmv1_mx_kernel(const uint16_t *__restr
 
 // The decode kernel for longer rows: x stays in LDS (K * 2 bytes) and every
 // lane walks its chunks l, l + 64, ... reading x from there.
-template <typename XT, int W>
-__global__ __launch_bounds__(64 * W) void qmv1_mx_lds_kernel(const uint16_t *__restrict__ x,
+template <int MODE, typename XT, int W>
+__global__ __launch_bounds__(64 * W) void qmv1_fp_lds_kernel(const uint16_t *__restrict__ x,
                                                              const uint32_t *__restrict__ codes,
                                                              const uint8_t *__restrict__ scales,
-                                                             int64_t N, int64_t K,
+                                                             int64_t N, int64_t K, int T,
                                                              uint16_t *__restrict__ y) {
+  using CF = chunk_fmt<MODE>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int nch = (int)(K >> 5);
+  int64_t rcb, rsb;
+  row_bytes<MODE>(K, rcb, rsb);
   uint4 *xl = reinterpret_cast<uint4 *>(smem);  // chunk c at xl[4 c .. 4 c + 3]
   const uint4 *xg = reinterpret_cast<const uint4 *>(x);
   for (int e = (int)threadIdx.x; e < 4 * nch; e += 64 * W) xl[e] = xg[e];
   __syncthreads();
   const int64_t TW = (int64_t)gridDim.x * W;
   for (int64_t row = (int64_t)blockIdx.x * W + wave; row < N; row += TW) {
-    gbyte *rc = wave_ptr(codes + row * (K >> 3));
-    gbyte *rs = wave_ptr(scales + row * (int64_t)nch);
+    gbyte *rc = wave_ptr(reinterpret_cast<const uint8_t *>(codes) + row * rcb);
+    gbyte *rs = wave_ptr(scales + row * rsb);
     float acc = 0.f;
 #pragma unroll 4
     for (int c = lane; c < nch; c += 64) {
-      const mxu4 w = *reinterpret_cast<__attribute__((address_space(1))) const mxu4 *>(
-          rc + (uint32_t)c * 16u);
-      const int X = (int)rs[c] - 127;
+      fp_u4 cw[CF::VW];
+#pragma unroll
+      for (int v = 0; v < CF::VW; ++v)
+        cw[v] = *reinterpret_cast<__attribute__((address_space(1))) const fp_u4 *>(
+            rc + ((uint32_t)c * CF::VW + v) * 16u);
+      uint32_t sbv;
+      if constexpr (CF::SB == 2)
+        sbv = *reinterpret_cast<__attribute__((address_space(1))) const uint16_t *>(
+            rs + (uint32_t)c * 2u);
+      else
+        sbv = rs[c];
       uint32_t xp[16];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint4 v = xl[4 * c + j];
         xp[4 * j] = v.x; xp[4 * j + 1] = v.y; xp[4 * j + 2] = v.z; xp[4 * j + 3] = v.w;
       }
-      float s = 0.f;
-      s = fp4_word_dot(XT{}, w[0], &xp[0], s);
-      s = fp4_word_dot(XT{}, w[1], &xp[4], s);
-      s = fp4_word_dot(XT{}, w[2], &xp[8], s);
-      s = fp4_word_dot(XT{}, w[3], &xp[12], s);
-      acc += __builtin_ldexpf(s, X);
+      acc += chunk_sum<MODE, XT>(cw, sbv, xp);
     }
-    const float v = wave_sum(acc);
+    float v = wave_sum(acc);
+    if constexpr (MODE == FP_NVFP4) v = __builtin_ldexpf(v, T);
     if (lane == 0) y[row] = xtraits<XT>::from_f32(v);
   }
 }
@@ -420,26 +627,26 @@ int resident_blocks(KernelT kern, int threads, size_t lds) {
   return v;
 }
 
-template <typename XT, int CPL, int UD, int W>
-hipError_t qmv1_mx_launch(const void *x, const uint32_t *codes, const uint8_t *scales, int64_t N,
-                          int64_t K, void *y, int wpc, hipStream_t s) {
-  auto kern = qmv1_mx_kernel<XT, CPL, UD, W>;
-  const size_t lds = (size_t)64 * CPL * 64 + (size_t)W * kMxRound * 2;
+template <int MODE, typename XT, int CPL, int UD, int W>
+hipError_t qmv1_fp_launch(const void *x, const uint32_t *codes, const uint8_t *scales, int64_t N,
+                          int64_t K, int T, void *y, int wpc, hipStream_t s) {
+  auto kern = qmv1_fp_kernel<MODE, XT, CPL, UD, W>;
+  const size_t lds = (size_t)64 * CPL * 64 + (size_t)W * kFpRound * 2;
   static int per_cu = 0;  // resident workgroups per CU for this instantiation
   if (per_cu == 0) per_cu = resident_blocks(kern, 64 * W, lds);
   const int64_t want = (N + W - 1) / W;
   const int64_t cap = (int64_t)device_cus() * (wpc > 0 && wpc < per_cu ? wpc : per_cu);
   const dim3 grid((unsigned)(want < cap ? want : cap));
-  hipLaunchKernelGGL(kern, grid, dim3(64 * W), lds, s, (const uint16_t *)x, codes, scales, N, K,
+  hipLaunchKernelGGL(kern, grid, dim3(64 * W), lds, s, (const uint16_t *)x, codes, scales, N, K, T,
                      (uint16_t *)y);
   return hipGetLastError();
 }
 
-template <typename XT>
-hipError_t qmv1_mx_lds_launch(const void *x, const uint32_t *codes, const uint8_t *scales,
-                              int64_t N, int64_t K, void *y, hipStream_t s) {
+template <int MODE, typename XT>
+hipError_t qmv1_fp_lds_launch(const void *x, const uint32_t *codes, const uint8_t *scales,
+                              int64_t N, int64_t K, int T, void *y, hipStream_t s) {
   constexpr int W = 8;
-  auto kern = qmv1_mx_lds_kernel<XT, W>;
+  auto kern = qmv1_fp_lds_kernel<MODE, XT, W>;
   const size_t lds = (size_t)K * 2;
   if (lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
@@ -451,51 +658,104 @@ hipError_t qmv1_mx_lds_launch(const void *x, const uint32_t *codes, const uint8_
   const int64_t want = (N + W - 1) / W;
   const int64_t cap = (int64_t)device_cus() * per_cu;
   const dim3 grid((unsigned)(want < cap ? want : cap));
-  hipLaunchKernelGGL(kern, grid, dim3(64 * W), lds, s, (const uint16_t *)x, codes, scales, N, K,
+  hipLaunchKernelGGL(kern, grid, dim3(64 * W), lds, s, (const uint16_t *)x, codes, scales, N, K, T,
                      (uint16_t *)y);
   return hipGetLastError();
 }
 
-template <typename XT>
-hipError_t qmv_mx_dispatch(const void *x, const uint32_t *codes, const uint8_t *scales, int64_t N,
-                           int64_t K, void *y, hipStream_t s) {
+template <int MODE, typename XT>
+hipError_t qmv_fp_dispatch(const void *x, const uint32_t *codes, const uint8_t *scales, int64_t N,
+                           int64_t K, int T, void *y, hipStream_t s) {
   int cpl, ud, w, wpc;
-  qmv1_mx_shape(N, K, cpl, ud, w, wpc);
-#define AQ_MX1(C, U, WW) return qmv1_mx_launch<XT, C, U, WW>(x, codes, scales, N, K, y, wpc, s)
+  qmv1_fp_shape(N, K, MODE, cpl, ud, w, wpc);
+#define AQ_FP1(C, U, WW) \
+  return qmv1_fp_launch<MODE, XT, C, U, WW>(x, codes, scales, N, K, T, y, wpc, s)
   switch (cpl) {
-    case 0: return qmv1_mx_lds_launch<XT>(x, codes, scales, N, K, y, s);
-    case 1: AQ_MX1(1, 4, 4);
+    case 0: return qmv1_fp_lds_launch<MODE, XT>(x, codes, scales, N, K, T, y, s);
+    case 1: AQ_FP1(1, 4, 4);
     case 2:
-      if (w == 16) AQ_MX1(2, 1, 16);
-      if (ud == 1) AQ_MX1(2, 1, 4);
-      AQ_MX1(2, 2, 4);
-    case 3: AQ_MX1(3, 1, 4);
-    case 4: AQ_MX1(4, 1, 4);
-    case 5: AQ_MX1(5, 1, 8);
-    case 6: AQ_MX1(6, 1, 8);
-    case 7: AQ_MX1(7, 1, 8);
-    case 8: AQ_MX1(8, 1, 8);
+      if (w == 16) AQ_FP1(2, 1, 16);
+      if (ud == 1) AQ_FP1(2, 1, 4);
+      AQ_FP1(2, 2, 4);
+    case 3: AQ_FP1(3, 1, 4);
+    case 4: AQ_FP1(4, 1, 4);
+    case 5: AQ_FP1(5, 1, 8);
+    case 6: AQ_FP1(6, 1, 8);
+    case 7: AQ_FP1(7, 1, 8);
+    case 8: AQ_FP1(8, 1, 8);
   }
-#undef AQ_MX1
+#undef AQ_FP1
   return hipErrorInvalidValue;
 }
 
-// grid for the quantize / dequantize loops over words: kMxUnroll words per
-// thread and pass, at most 2^22 workgroups (then several passes)
-dim3 word_grid(int64_t words) {
-  const int64_t b = (words + 256 * kMxUnroll - 1) / (256 * kMxUnroll);
+template <int MODE>
+hipError_t qmv_fp_mode(const void *x, int x_dtype, const uint32_t *codes, const uint8_t *scales,
+                       int64_t N, int64_t K, int T, void *y, hipStream_t s) {
+  if (x_dtype == X_F16) return qmv_fp_dispatch<MODE, f16_t>(x, codes, scales, N, K, T, y, s);
+  if (x_dtype == X_BF16) return qmv_fp_dispatch<MODE, bf16_t>(x, codes, scales, N, K, T, y, s);
+  return hipErrorInvalidValue;
+}
+
+// grid for the quantize / dequantize loops: kFpUnroll units per thread and
+// pass, at most 2^22 workgroups (then several passes)
+dim3 unit_grid(int64_t units) {
+  const int64_t b = (units + 256 * kFpUnroll - 1) / (256 * kFpUnroll);
   return dim3((unsigned)(b < (1 << 22) ? b : (1 << 22)));
+}
+
+template <int MODE>
+hipError_t quantize_fp_mode(const void *w, int w_dtype, int64_t units, int T, uint32_t *codes,
+                            uint8_t *scales, hipStream_t s) {
+  const dim3 grid = unit_grid(units);
+  switch (w_dtype) {
+    case X_F32:
+      hipLaunchKernelGGL((quantize_fp_kernel<MODE, X_F32>), grid, dim3(256), 0, s, w, units, T,
+                         codes, scales);
+      break;
+    case X_F16:
+      hipLaunchKernelGGL((quantize_fp_kernel<MODE, X_F16>), grid, dim3(256), 0, s, w, units, T,
+                         codes, scales);
+      break;
+    case X_BF16:
+      hipLaunchKernelGGL((quantize_fp_kernel<MODE, X_BF16>), grid, dim3(256), 0, s, w, units, T,
+                         codes, scales);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t dequantize_fp_mode(const uint32_t *codes, const uint8_t *scales, int64_t units, int T,
+                              void *out, int out_dtype, hipStream_t s) {
+  const dim3 grid = unit_grid(units);
+  switch (out_dtype) {
+    case X_F32:
+      hipLaunchKernelGGL((dequantize_fp_kernel<MODE, X_F32>), grid, dim3(256), 0, s, codes, scales,
+                         units, T, out);
+      break;
+    case X_F16:
+      hipLaunchKernelGGL((dequantize_fp_kernel<MODE, X_F16>), grid, dim3(256), 0, s, codes, scales,
+                         units, T, out);
+      break;
+    case X_BF16:
+      hipLaunchKernelGGL((dequantize_fp_kernel<MODE, X_BF16>), grid, dim3(256), 0, s, codes,
+                         scales, units, T, out);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
 
 // M = 1 launch shape: the affine decode kernel's (x chunks per lane, rows in
-// flight, waves per workgroup, workgroups per CU), the mxfp4 rows being
-// slightly shorter than affine 4-bit rows at G = 64 (4.25 against 4.5 bits
-// per weight); cpl = 0 selects the LDS kernel for K > 16384.
-void qmv1_mx_shape(int64_t N, int64_t K, int &cpl, int &ud, int &w, int &wpc) {
+// flight, waves per workgroup, workgroups per CU); cpl = 0 selects the LDS
+// kernel: for K > 16384, and for nvfp4 at 8 chunks per lane (its two scales
+// per chunk would push the register kernel past 256 registers).
+void qmv1_fp_shape(int64_t N, int64_t K, int mode, int &cpl, int &ud, int &w, int &wpc) {
   int sl;
-  if (K > 8 * 2048) {
+  if (K > 8 * 2048 || (mode == FP_NVFP4 && K > 7 * 2048)) {
     cpl = 0;
     ud = 1;
     w = 8;
@@ -505,52 +765,35 @@ void qmv1_mx_shape(int64_t N, int64_t K, int &cpl, int &ud, int &w, int &wpc) {
   qmv1_shape(N, K, 32, cpl, ud, w, sl, wpc);
 }
 
-hipError_t launch_quantize_mx(const void *w, int w_dtype, int64_t N, int64_t K, uint32_t *codes,
-                              uint8_t *scales, hipStream_t s) {
-  const int64_t words = N * (K / 8);
-  const dim3 grid = word_grid(words);
-  switch (w_dtype) {
-    case X_F32:
-      hipLaunchKernelGGL(quantize_mx_kernel<X_F32>, grid, dim3(256), 0, s, w, words, codes, scales);
-      break;
-    case X_F16:
-      hipLaunchKernelGGL(quantize_mx_kernel<X_F16>, grid, dim3(256), 0, s, w, words, codes, scales);
-      break;
-    case X_BF16:
-      hipLaunchKernelGGL(quantize_mx_kernel<X_BF16>, grid, dim3(256), 0, s, w, words, codes,
-                         scales);
-      break;
-    default: return hipErrorInvalidValue;
+hipError_t launch_quantize_fp(const void *w, int w_dtype, int64_t N, int64_t K, int mode, int T,
+                              uint32_t *codes, uint8_t *scales, hipStream_t s) {
+  const int64_t units = N * (K / 8);
+  switch (mode) {
+    case FP_MXFP4: return quantize_fp_mode<FP_MXFP4>(w, w_dtype, units, T, codes, scales, s);
+    case FP_NVFP4: return quantize_fp_mode<FP_NVFP4>(w, w_dtype, units, T, codes, scales, s);
+    case FP_MXFP8: return quantize_fp_mode<FP_MXFP8>(w, w_dtype, units, T, codes, scales, s);
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
-hipError_t launch_dequantize_mx(const uint32_t *codes, const uint8_t *scales, int64_t N, int64_t K,
-                                void *out, int out_dtype, hipStream_t s) {
-  const int64_t words = N * (K / 8);
-  const dim3 grid = word_grid(words);
-  switch (out_dtype) {
-    case X_F32:
-      hipLaunchKernelGGL(dequantize_mx_kernel<X_F32>, grid, dim3(256), 0, s, codes, scales, words,
-                         out);
-      break;
-    case X_F16:
-      hipLaunchKernelGGL(dequantize_mx_kernel<X_F16>, grid, dim3(256), 0, s, codes, scales, words,
-                         out);
-      break;
-    case X_BF16:
-      hipLaunchKernelGGL(dequantize_mx_kernel<X_BF16>, grid, dim3(256), 0, s, codes, scales, words,
-                         out);
-      break;
-    default: return hipErrorInvalidValue;
+hipError_t launch_dequantize_fp(const uint32_t *codes, const uint8_t *scales, int64_t N, int64_t K,
+                                int mode, int T, void *out, int out_dtype, hipStream_t s) {
+  const int64_t units = N * (K / 8);
+  switch (mode) {
+    case FP_MXFP4: return dequantize_fp_mode<FP_MXFP4>(codes, scales, units, T, out, out_dtype, s);
+    case FP_NVFP4: return dequantize_fp_mode<FP_NVFP4>(codes, scales, units, T, out, out_dtype, s);
+    case FP_MXFP8: return dequantize_fp_mode<FP_MXFP8>(codes, scales, units, T, out, out_dtype, s);
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
-hipError_t launch_qmv_mx(const void *x, int x_dtype, const uint32_t *codes, const uint8_t *scales,
-                         int64_t N, int64_t K, void *y, hipStream_t s) {
-  if (x_dtype == X_F16) return qmv_mx_dispatch<f16_t>(x, codes, scales, N, K, y, s);
-  if (x_dtype == X_BF16) return qmv_mx_dispatch<bf16_t>(x, codes, scales, N, K, y, s);
+hipError_t launch_qmv_fp(const void *x, int x_dtype, const uint32_t *codes, const uint8_t *scales,
+                         int64_t N, int64_t K, int mode, int T, void *y, hipStream_t s) {
+  switch (mode) {
+    case FP_MXFP4: return qmv_fp_mode<FP_MXFP4>(x, x_dtype, codes, scales, N, K, T, y, s);
+    case FP_NVFP4: return qmv_fp_mode<FP_NVFP4>(x, x_dtype, codes, scales, N, K, T, y, s);
+    case FP_MXFP8: return qmv_fp_mode<FP_MXFP8>(x, x_dtype, codes, scales, N, K, T, y, s);
+  }
   return hipErrorInvalidValue;
 }
 

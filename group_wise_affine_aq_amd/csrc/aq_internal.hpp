@@ -80,15 +80,18 @@ hipError_t launch_gather_qmm(const void *x, int x_dtype, int64_t T, const uint32
                              int64_t K, const int32_t *ids, int topk, int G, int bits, void *y,
                              hipStream_t s);
 
-// mxfp4 (E2M1 codes, 8 to a word; one E8M0 exponent byte per 32 weights)
-constexpr int64_t kMxMaxK = 49152;  // the decode kernel keeps x (K * 2 bytes) in LDS
-hipError_t launch_quantize_mx(const void *w, int w_dtype, int64_t N, int64_t K, uint32_t *codes,
-                              uint8_t *scales, hipStream_t s);
-hipError_t launch_dequantize_mx(const uint32_t *codes, const uint8_t *scales, int64_t N, int64_t K,
-                                void *out, int out_dtype, hipStream_t s);
+// block-scaled float modes: mxfp4 (E2M1 codes, exponent byte per 32), nvfp4
+// (E2M1 codes, E4M3 scale per 16, tensor scale 2^T), mxfp8 (E4M3 codes,
+// exponent byte per 32)
+enum FpMode { FP_MXFP4 = 0, FP_NVFP4 = 1, FP_MXFP8 = 2 };
+constexpr int64_t kFpMaxK = 49152;  // the decode kernel keeps x (K * 2 bytes) in LDS
+hipError_t launch_quantize_fp(const void *w, int w_dtype, int64_t N, int64_t K, int mode, int T,
+                              uint32_t *codes, uint8_t *scales, hipStream_t s);
+hipError_t launch_dequantize_fp(const uint32_t *codes, const uint8_t *scales, int64_t N, int64_t K,
+                                int mode, int T, void *out, int out_dtype, hipStream_t s);
 // y[N] = x[K] @ W^T; cpl = 0 is the LDS kernel for K > 16384
-void qmv1_mx_shape(int64_t N, int64_t K, int &cpl, int &ud, int &w, int &wpc);
-hipError_t launch_qmv_mx(const void *x, int x_dtype, const uint32_t *codes, const uint8_t *scales,
-                         int64_t N, int64_t K, void *y, hipStream_t s);
+void qmv1_fp_shape(int64_t N, int64_t K, int mode, int &cpl, int &ud, int &w, int &wpc);
+hipError_t launch_qmv_fp(const void *x, int x_dtype, const uint32_t *codes, const uint8_t *scales,
+                         int64_t N, int64_t K, int mode, int T, void *y, hipStream_t s);
 
 }  // namespace aq

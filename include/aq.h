@@ -252,58 +252,86 @@ aq_status aq_gather_quantized_matmul(const void *x, aq_dtype x_dtype, int64_t T,
                                      const int32_t *ids, int topk, int group_size, int bits,
                                      void *y, void *stream);
 
-/* ---- mxfp4: block-scaled 4-bit floats ------------------------------------ */
+/* ---- block-scaled float modes ------------------------------------------- */
 
-/* The block-scaled float mode mxfp4 ("Quantization", metalworking MLX notes,
- * the paragraph on the newer modes; "Quantizing a Model for MLX", "Modes,
- * bits and mixed recipes": groups of 32 weights, 4-bit codes, one exponent
- * per group in place of a scale and a bias).  The pages give no bit layout;
- * this library takes the microscaling (MX) definition of that name:
+/* The block-scaled float modes ("Quantization", metalworking MLX notes, the
+ * paragraph on the newer modes; "Quantizing a Model for MLX", "Modes, bits
+ * and mixed recipes": mxfp4, nvfp4 and mxfp8 with groups of 32, 16 and 32
+ * weights and 4, 4 and 8-bit codes, a per-group scale in place of a scale
+ * and a bias; ExecuTorch "Quantization": nvfp4 is NVIDIA's FP4 weight-only
+ * format at group size 16).  The pages give no bit layout; this library
+ * takes the definitions of those names (microscaling for mxfp4 and mxfp8,
+ * NVFP4 for nvfp4):
  *
- *   codes   uint32 [N, K/8]   E2M1 codes: bit 3 the sign, bits 2..1 an
- *                             exponent e with bias 1, bit 0 a mantissa m;
- *                             value (1 + m/2)*2^(e-1) for e > 0, m/2 for
- *                             e = 0 (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6);
- *                             packed as the 4-bit bitstream above (code k of
- *                             a row at bits [4k, 4k+4))
- *   scales  uint8  [N, K/32]  X + 127 for the group scale 2^X (E8M0)
+ *   E2M1 code (4 bits): bit 3 sign, bits 2..1 exponent e (bias 1), bit 0
+ *     mantissa m; (1 + m/2)*2^(e-1), or m/2 for e = 0 (magnitudes 0, 0.5,
+ *     1, 1.5, 2, 3, 4, 6).
+ *   E4M3 code (8 bits): bit 7 sign, bits 6..3 exponent e (bias 7), bits
+ *     2..0 mantissa m; (1 + m/8)*2^(e-7), or (m/8)*2^-6 for e = 0;
+ *     magnitude pattern 0x7F is NaN; largest finite magnitude 448.
  *
- * The group is fixed at 32 and there are no biases.  N >= 1, K >= 32 and a
- * multiple of 32.  The conventions above (device pointers 16-byte aligned,
- * caller-owned buffers, host-side checks, asynchronous on `stream`) hold. */
+ *   mode      group  codes                         scales
+ *   AQ_MXFP4   32    uint32 [N, K/8]  E2M1         uint8 [N, K/32]  X + 127 for 2^X
+ *   AQ_NVFP4   16    uint32 [N, K/8]  E2M1         uint8 [N, K/16]  E4M3 value s
+ *   AQ_MXFP8   32    uint32 [N, K/4]  E4M3         uint8 [N, K/32]  X + 127 for 2^X
+ *
+ * Codes are packed least significant first into the row's words (code k of
+ * a row at bits [b*k, b*k + b) of its bitstream, as above).  A weight's
+ * value is code * 2^X (mx modes) or code * s * 2^T (nvfp4, where the whole
+ * matrix shares the tensor scale 2^T, the argument tensor_exp = T in
+ * [-100, 100]; 0 means no tensor scale; for the mx modes tensor_exp must
+ * be 0).  N >= 1, K >= the group size and a multiple of it.  The
+ * conventions above (device pointers 16-byte aligned, caller-owned buffers,
+ * host-side checks, asynchronous on `stream`) hold. */
+typedef enum aq_fp_mode {
+  AQ_MXFP4 = 0,
+  AQ_NVFP4 = 1,
+  AQ_MXFP8 = 2,
+  /* range markers, never valid arguments (AQ_ERR_INVALID_ARG) */
+  AQ_FP_MODE_RANGE_MIN_ = -0x7FFFFFFF - 1,
+  AQ_FP_MODE_RANGE_MAX_ = 0x7FFFFFFF
+} aq_fp_mode;
 
 /* Quantize W [N, K] (device; AQ_F32, AQ_F16 or AQ_BF16, widened exactly to
- * binary32) into mxfp4 codes and scales (device).  Per group of 32:
- *   X = floor(log2 max|w|) - 2 (2 = the exponent of 6, the largest code
- *       value), clamped to [-127, 127]; -127 for a group of zeros;
- *   each weight's code is its own sign bit (so -0 gives code 8) with the
- *       magnitude code nearest to |w| / 2^X, ties to the even mantissa, and
- *       6 for anything above.
+ * binary32) into codes and scales (device) of the given mode.  Per group:
+ *   mxfp4, mxfp8: X = floor(log2 max|w|) - E, E the exponent of the
+ *     largest code value (2 for E2M1's 6, 8 for E4M3's 448), clamped to
+ *     [-127, 127]; -127 for a group of zeros.  The step is 2^X.
+ *   nvfp4: s = the E4M3 value nearest to max|w| / (6 * 2^T), ties to the
+ *     even code, 448 above it.  The step is s * 2^T.
+ *   each weight's code is its own sign bit (so -0 keeps it) with the
+ *   magnitude code nearest to |w| / step, ties to the even code, the
+ *   largest finite magnitude above it; magnitude 0 when s = 0.
+ * A tensor exponent that puts the largest group scale near the top of
+ * E4M3's range is T = ceil(log2(max|W| / 2688)) (2688 = 6 * 448).
  * Precondition (not checked on the device): weights finite; otherwise the
  * outputs for that group are unspecified. */
-aq_status aq_quantize_mxfp4(const void *w, aq_dtype w_dtype, int64_t N, int64_t K,
-                            uint32_t *codes, uint8_t *scales, void *stream);
+aq_status aq_quantize_fp(const void *w, aq_dtype w_dtype, int64_t N, int64_t K, aq_fp_mode mode,
+                         int tensor_exp, uint32_t *codes, uint8_t *scales, void *stream);
 
-/* Dequantize mxfp4: out[n, k] = code value * 2^X, exact in binary32 (2 or
- * fewer significant bits; +-inf beyond the binary32 range, which only scale
- * bytes 254 and 255 reach, and which aq_quantize_mxfp4 never writes), then
- * rounded to nearest even into out_dtype (AQ_F32, AQ_F16 or AQ_BF16).  out
- * is device memory [N, K]. */
-aq_status aq_dequantize_mxfp4(const uint32_t *codes, const uint8_t *scales, int64_t N, int64_t K,
-                              void *out, aq_dtype out_dtype, void *stream);
+/* Dequantize: out[n, k] = the exact value code * step (NaN for NaN code or
+ * scale patterns; steps from any scale byte, not only those the quantizer
+ * writes), rounded to nearest even into out_dtype (AQ_F32, AQ_F16 or
+ * AQ_BF16), +-inf past its range.  out is device memory [N, K]. */
+aq_status aq_dequantize_fp(const uint32_t *codes, const uint8_t *scales, int64_t N, int64_t K,
+                           aq_fp_mode mode, int tensor_exp, void *out, aq_dtype out_dtype,
+                           void *stream);
 
-/* Decode matrix-vector product with mxfp4 weights ("Quantization",
- * metalworking, QMV bullet: the weights are dequantized in registers on
- * every use): y[n] = sum_k x[k] * w^[n, k] for one row x.  x: device [K] in
- * x_dtype (AQ_F16 or AQ_BF16); y: device [N] in x_dtype.  Each group's
- * products are summed in binary32 and scaled by 2^X; y is rounded to nearest
- * even.  AQ_ERR_UNSUPPORTED for K > 49152 (x is held on chip). */
-aq_status aq_qmv_mxfp4(const void *x, aq_dtype x_dtype, const uint32_t *codes,
-                       const uint8_t *scales, int64_t N, int64_t K, void *y, void *stream);
+/* Decode matrix-vector product ("Quantization", metalworking, QMV bullet:
+ * the weights are dequantized in registers on every use): y[n] =
+ * sum_k x[k] * w^[n, k] for one row x.  x: device [K] in x_dtype (AQ_F16 or
+ * AQ_BF16); y: device [N] in x_dtype.  Products are summed in binary32 per
+ * group and scaled once per group; y is rounded to nearest even.
+ * AQ_ERR_UNSUPPORTED for K not a multiple of 32 (nvfp4) or K > 49152 (x is
+ * held on chip). */
+aq_status aq_qmv_fp(const void *x, aq_dtype x_dtype, const uint32_t *codes,
+                    const uint8_t *scales, int64_t N, int64_t K, aq_fp_mode mode, int tensor_exp,
+                    void *y, void *stream);
 
-/* Which kernel aq_qmv_mxfp4 launches for this shape, as text (as
- * aq_qmv_describe does); -1 for arguments aq_qmv_mxfp4 would reject. */
-int aq_qmv_mxfp4_describe(int64_t N, int64_t K, aq_dtype x_dtype, char *buf, int len);
+/* Which kernel aq_qmv_fp launches for this shape and mode, as text (as
+ * aq_qmv_describe does); -1 for arguments aq_qmv_fp would reject. */
+int aq_qmv_fp_describe(int64_t N, int64_t K, aq_fp_mode mode, aq_dtype x_dtype, char *buf,
+                       int len);
 
 #ifdef __cplusplus
 }

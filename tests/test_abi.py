@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("aq_quantize", "aq_quantize_mse", "aq_dequantize", "aq_qmv", "aq_qmm", "aq_gather_qmv",
               "aq_quantized_matmul", "aq_codes_words", "aq_qweight_bytes", "aq_status_string",
-              "aq_quantize_mxfp4", "aq_dequantize_mxfp4", "aq_qmv_mxfp4"):
+              "aq_quantize_fp", "aq_dequantize_fp", "aq_qmv_fp"):
         assert n in names
 
 
@@ -220,46 +220,62 @@ def test_quantize_zp_argument_errors(lib):
     assert q(zeros=MIS) == ALIGN           # zeros optional, aligned when given
 
 
-def test_mxfp4_argument_errors(lib):
-    """mxfp4: K a multiple of 32 (the fixed group), no bias array, every
-    pointer required and 16-byte aligned; the decode product holds x on chip
-    up to K = 49152."""
-    q = lambda **k: lib.aq_quantize_mxfp4(k.get("w", P), k.get("dt", F32), k.get("N", 4),
-                                          k.get("K", 64), k.get("codes", P), k.get("scales", P),
-                                          None)
+def test_fp_mode_argument_errors(lib):
+    """Block-scaled float modes: K a multiple of the mode's group (32, 16,
+    32), a tensor exponent only for nvfp4 (|T| <= 100), every pointer
+    required and 16-byte aligned; the decode product takes K a multiple of
+    32 up to 49152."""
+    MX4, NV4, MX8 = 0, 1, 2
+    q = lambda **k: lib.aq_quantize_fp(k.get("w", P), k.get("dt", F32), k.get("N", 4),
+                                       k.get("K", 64), k.get("mode", MX4), k.get("T", 0),
+                                       k.get("codes", P), k.get("scales", P), None)
     assert q(K=48) == INVALID
+    assert q(K=40, mode=NV4) == INVALID
     assert q(K=0) == INVALID
     assert q(N=0) == INVALID
+    assert q(mode=3) == INVALID
+    assert q(mode=-1) == INVALID
+    assert q(T=1) == INVALID              # the mx modes take no tensor scale
+    assert q(mode=MX8, T=-2) == INVALID
+    assert q(mode=NV4, T=101) == INVALID
+    assert q(mode=NV4, T=-101) == INVALID
     assert q(dt=3) == INVALID
     assert q(w=None) == INVALID
     assert q(scales=None) == INVALID
     assert q(w=MIS) == ALIGN
-    assert q(scales=MIS) == ALIGN
-    d = lambda **k: lib.aq_dequantize_mxfp4(k.get("codes", P), k.get("scales", P), 4,
-                                            k.get("K", 64), k.get("out", P), k.get("dt", F16),
-                                            None)
+    assert q(mode=NV4, T=-100, scales=MIS) == ALIGN
+    d = lambda **k: lib.aq_dequantize_fp(k.get("codes", P), k.get("scales", P), 4,
+                                         k.get("K", 64), k.get("mode", MX8), k.get("T", 0),
+                                         k.get("out", P), k.get("dt", F16), None)
     assert d(K=40) == INVALID
+    assert d(mode=5) == INVALID
     assert d(dt=4) == INVALID
     assert d(out=None) == INVALID
     assert d(scales=None) == INVALID
     assert d(codes=MIS) == ALIGN
-    assert d(out=MIS) == ALIGN
-    m = lambda **k: lib.aq_qmv_mxfp4(k.get("x", P), k.get("dt", F16), k.get("codes", P),
-                                     k.get("scales", P), k.get("N", 4), k.get("K", 64),
-                                     k.get("y", P), None)
-    assert m(dt=F32) == INVALID            # activations are fp16 or bf16
+    assert d(mode=NV4, T=7, out=MIS) == ALIGN
+    m = lambda **k: lib.aq_qmv_fp(k.get("x", P), k.get("dt", F16), k.get("codes", P),
+                                  k.get("scales", P), k.get("N", 4), k.get("K", 64),
+                                  k.get("mode", MX4), k.get("T", 0), k.get("y", P), None)
+    assert m(dt=F32) == INVALID           # activations are fp16 or bf16
     assert m(K=33) == INVALID
     assert m(N=0) == INVALID
     assert m(y=None) == INVALID
+    assert m(mode=MX8, T=3) == INVALID
     assert m(scales=MIS) == ALIGN
     assert m(x=MIS) == ALIGN
     assert m(K=49152 + 32) == UNSUPPORTED
+    assert m(mode=NV4, K=48) == UNSUPPORTED  # a whole group, not a whole 32-code chunk
     buf = ctypes.create_string_buffer(96)
-    assert lib.aq_qmv_mxfp4_describe(4096, 49152 + 32, F16, buf, 96) == -1
-    assert lib.aq_qmv_mxfp4_describe(4096, 100, F16, buf, 96) == -1
-    assert aq.aq_qmv_mxfp4_describe(14336, 4096) == "qmv1_mx_kernel<f16, CPL=2, UD=1, W=4>"
-    assert aq.aq_qmv_mxfp4_describe(4096, 14336, "bf16") == "qmv1_mx_kernel<bf16, CPL=7, UD=1, W=8>"
-    assert aq.aq_qmv_mxfp4_describe(4096, 28672).startswith("qmv1_mx_lds_kernel<f16")
+    assert lib.aq_qmv_fp_describe(4096, 49152 + 32, MX4, F16, buf, 96) == -1
+    assert lib.aq_qmv_fp_describe(4096, 100, MX4, F16, buf, 96) == -1
+    assert lib.aq_qmv_fp_describe(4096, 4096, 9, F16, buf, 96) == -1
+    d = aq.aq_qmv_fp_describe
+    assert d(14336, 4096, "mxfp4") == "qmv1_fp_kernel<mxfp4, f16, CPL=2, UD=1, W=4>"
+    assert d(4096, 14336, "mxfp8", "bf16") == "qmv1_fp_kernel<mxfp8, bf16, CPL=7, UD=1, W=8>"
+    assert d(4096, 14336, "nvfp4") == "qmv1_fp_kernel<nvfp4, f16, CPL=7, UD=1, W=8>"
+    assert d(4096, 16384, "nvfp4").startswith("qmv1_fp_lds_kernel<nvfp4")
+    assert d(4096, 28672, "mxfp4").startswith("qmv1_fp_lds_kernel<mxfp4, f16")
 
 
 def test_consumers_take_null_biases(lib):

@@ -1,10 +1,13 @@
-"""GPU parity of the mxfp4 entry points (block-scaled E2M1 codes, one E8M0
-exponent per 32 weights) against the CPU oracle.
+"""GPU parity of the block-scaled float modes (mxfp4, nvfp4, mxfp8: E2M1 or
+E4M3 codes with a per-group scale) against the CPU oracle.
 
-Bar: quantize and dequantize bit-exact; the decode product within
-2^-9 * A + 1e-6 per element, A = sum_k |x_k * w^_k| with w^ the oracle's
-exact dequantized weight.  Codes and scales fed to the consumers come from
-the oracle's quantizer or from the seeded generator, never from the device."""
+Bar: quantize and dequantize bit-exact (NaN where the oracle has NaN); the
+decode product within 2^-9 * A + 1e-6 per element, A = sum_k |x_k * w^_k|
+with w^ the oracle's exact dequantized weight.  Codes and scales fed to the
+consumers come from the oracle's quantizer or from the seeded generator,
+never from the device."""
+import math
+
 import numpy as np
 import pytest
 
@@ -13,6 +16,10 @@ from group_wise_affine_aq_amd import inputs
 from gpu_util import bits_to_dev, out_bits, out_to_f64, to_dev, torch_dtype
 
 pytestmark = pytest.mark.gpu
+
+MODES = ["mxfp4", "nvfp4", "mxfp8"]
+GROUP = {"mxfp4": 32, "nvfp4": 16, "mxfp8": 32}
+BITS = {"mxfp4": 4, "nvfp4": 4, "mxfp8": 8}
 
 
 @pytest.fixture(scope="module")
@@ -25,22 +32,70 @@ def aq():
     return mod
 
 
-def _mx_to_dev(codes, scales):
+def _tensor_exp(w, mode):
+    """nvfp4's tensor exponent: the largest group scale near the top of E4M3
+    (T = ceil(log2(max|W| / 2688))); 0 for the mx modes."""
+    if mode != "nvfp4":
+        return 0
+    amax = float(np.abs(w).max())
+    return 0 if amax == 0 else max(-100, min(100, math.ceil(math.log2(amax / 2688))))
+
+
+def _oracle_quantize(w, mode, T):
+    if mode == "mxfp4":
+        return oracle.quantize_mxfp4(w)
+    if mode == "mxfp8":
+        return oracle.quantize_mxfp8(w)
+    return oracle.quantize_nvfp4(w, T)
+
+
+def _oracle_exact(c, s, K, mode, T):
+    if mode == "mxfp4":
+        return oracle.dequantize_mxfp4_exact(c, s, K)
+    if mode == "mxfp8":
+        return oracle.dequantize_mxfp8_exact(c, s, K)
+    return oracle.dequantize_nvfp4_exact(c, s, K, T)
+
+
+def _oracle_dequantize(c, s, K, mode, T, code):
+    if mode == "mxfp4":
+        return oracle.dequantize_mxfp4(c, s, K, code)
+    if mode == "mxfp8":
+        return oracle.dequantize_mxfp8(c, s, K, code)
+    return oracle.dequantize_nvfp4(c, s, K, code, T)
+
+
+def _to_dev(codes, scales):
     import torch
     c = torch.from_numpy(np.ascontiguousarray(codes).view(np.int32)).cuda()
     s = torch.from_numpy(np.ascontiguousarray(scales, dtype=np.uint8)).cuda()
     return c, s
 
 
-def _mx_from_dev(codes, scales):
+def _from_dev(codes, scales):
     return codes.cpu().numpy().view(np.uint32), scales.cpu().numpy()
 
 
+def _isnan_bits(b, out):
+    if out == "f32":
+        return np.isnan(b.view(np.float32))
+    if out == "f16":
+        return ((b & 0x7C00) == 0x7C00) & ((b & 0x03FF) != 0)
+    return ((b & 0x7F80) == 0x7F80) & ((b & 0x007F) != 0)
+
+
+def _assert_same_bits(got, ref_bits, out):
+    """Bit-exact, except that any NaN pattern matches any NaN pattern."""
+    gn, rn = _isnan_bits(got, out), _isnan_bits(ref_bits, out)
+    assert np.array_equal(gn, rn)
+    assert np.array_equal(got[~gn], ref_bits[~rn])
+
+
 def _special_rows():
-    """Rows of 32-weight groups at the format's edges: zeros and -0, subnormal
-    maxima (X clamped to -127), the smallest unclamped exponents, every
-    midpoint of the E2M1 grid at several scales (ties), members above 6 * 2^X
-    (saturation), the binary32 top (X = 125), mixed signs."""
+    """Rows of 32 weights at the formats' edges: zeros and -0, subnormal
+    maxima (exponents clamped), every E2M1 midpoint at several scales
+    (ties), members past the largest code value (saturation), the binary32
+    top, mixed signs, one large member among tiny ones."""
     mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.5, 7.0, 7.5, 0.5, 1.0, 3.0, 6.0, 0.1,
                      4.0], dtype=np.float64)
     rows = []
@@ -54,12 +109,14 @@ def _special_rows():
     rows.append(np.ldexp(np.linspace(-1.0, 1.0, 32), -126))           # max|w| = 2^-126
     rows.append(np.full(32, 3.4e38) * np.where(np.arange(32) % 2, 1, -1))
     rows.append(np.where(np.arange(32) == 7, 1.0, 1e-30))             # one large member
+    rows.append(np.linspace(-500.0, 500.0, 32))                       # E4M3 ties and saturation
     return np.stack(rows).astype(np.float32)
 
 
 # ---- quantize -------------------------------------------------------------------------
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("wdt", ["f32", "f16", "bf16"])
-def test_quantize_mxfp4_bitexact(aq, wdt):
+def test_quantize_fp_bitexact(aq, mode, wdt):
     N, K = 37, 13 * 32
     w = inputs.weights(N, K, seed=60, key=(1,), outliers=True)
     if wdt != "f32":
@@ -68,103 +125,119 @@ def test_quantize_mxfp4_bitexact(aq, wdt):
         wd = bits_to_dev(wb, wdt)
     else:
         wd = to_dev(w)
-    c, s = oracle.quantize_mxfp4(w)
-    gc, gs = _mx_from_dev(*aq.aq_quantize_mxfp4(wd))
+    T = _tensor_exp(w, mode)
+    c, s = _oracle_quantize(w, mode, T)
+    gc, gs = _from_dev(*aq.aq_quantize_fp(wd, mode, T))
     assert np.array_equal(gs, s)
     assert np.array_equal(gc, c)
 
 
-def test_quantize_mxfp4_special_groups(aq):
+@pytest.mark.parametrize("mode", MODES)
+def test_quantize_fp_special_groups(aq, mode):
     w = _special_rows()
-    # the same groups side by side in one row as well (several groups per row)
-    w2 = np.ascontiguousarray(w.reshape(1, -1))
+    w2 = np.ascontiguousarray(w.reshape(1, -1))  # the same groups side by side in one row
     for m in (w, w2):
-        c, s = oracle.quantize_mxfp4(m)
-        gc, gs = _mx_from_dev(*aq.aq_quantize_mxfp4(to_dev(m)))
-        assert np.array_equal(gs, s)
-        assert np.array_equal(gc, c)
+        for T in ((0, -14, 60, -100) if mode == "nvfp4" else (0,)):
+            c, s = _oracle_quantize(m, mode, T)
+            gc, gs = _from_dev(*aq.aq_quantize_fp(to_dev(m), mode, T))
+            assert np.array_equal(gs, s), T
+            assert np.array_equal(gc, c), T
 
 
-@pytest.mark.parametrize("N,K", [(1, 32), (3, 64), (1000, 4096), (33, 14336 + 32)])
-def test_quantize_mxfp4_shapes(aq, N, K):
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("N,K", [(1, 32), (3, 64), (5, 48), (1000, 4096), (33, 14336 + 32)])
+def test_quantize_fp_shapes(aq, mode, N, K):
+    if K % GROUP[mode]:
+        pytest.skip("K not a multiple of the group")
     w = inputs.weights(N, K, seed=61, key=(N, K), outliers=True)
-    c, s = oracle.quantize_mxfp4(w)
-    gc, gs = _mx_from_dev(*aq.aq_quantize_mxfp4(to_dev(w)))
+    T = _tensor_exp(w, mode)
+    c, s = _oracle_quantize(w, mode, T)
+    gc, gs = _from_dev(*aq.aq_quantize_fp(to_dev(w), mode, T))
     assert np.array_equal(gs, s) and np.array_equal(gc, c)
 
 
 # ---- dequantize -----------------------------------------------------------------------
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
-def test_dequantize_mxfp4_bitexact(aq, out):
-    """Oracle-quantized weights plus arbitrary words and scale bytes over the
-    whole byte range (254 and 255 overflow binary32 to +-inf for the larger
-    codes)."""
+def test_dequantize_fp_bitexact(aq, mode, out):
+    """Oracle-quantized weights, plus arbitrary code words and every scale
+    byte (NaN patterns and binary32 overflow included)."""
     N, K = 29, 9 * 32
     w = inputs.weights(N, K, seed=62, outliers=True)
-    c, s = oracle.quantize_mxfp4(w)
+    T = _tensor_exp(w, mode)
+    c, s = _oracle_quantize(w, mode, T)
     rng = np.random.default_rng(62)
-    rc = rng.integers(0, 2 ** 32, size=(N, K // 8), dtype=np.uint64).astype(np.uint32)
-    rs = np.arange(N * K // 32, dtype=np.int64).reshape(N, K // 32) % 256
-    rs = rs.astype(np.uint8)
+    rc = rng.integers(0, 2 ** 32, size=c.shape, dtype=np.uint64).astype(np.uint32)
+    rs = (np.arange(s.size, dtype=np.int64).reshape(s.shape) % 256).astype(np.uint8)
     code = {"f32": oracle.F32, "f16": oracle.F16, "bf16": oracle.BF16}[out]
-    for cc, ss in ((c, s), (rc, rs)):
-        ref = oracle.dequantize_mxfp4(cc, ss, K, code)
-        got = aq.aq_dequantize_mxfp4(*_mx_to_dev(cc, ss), K, out_dtype=torch_dtype(out))
+    for cc, ss, TT in ((c, s, T), (rc, rs, T), (rc, rs, 0)):
+        ref = _oracle_dequantize(cc, ss, K, mode, TT, code)
+        got = aq.aq_dequantize_fp(*_to_dev(cc, ss), K, mode, TT, out_dtype=torch_dtype(out))
         ref_bits = ref.view(np.uint32) if out == "f32" else ref
-        assert np.array_equal(out_bits(got), ref_bits)
+        _assert_same_bits(out_bits(got), ref_bits, out)
 
 
-def test_dequantize_mxfp4_large(aq):
+@pytest.mark.parametrize("mode", MODES)
+def test_dequantize_fp_large(aq, mode):
     N, K = 4096, 4096
     w = inputs.weights(N, K, seed=63)
-    c, s = oracle.quantize_mxfp4(w)
-    got = aq.aq_dequantize_mxfp4(*_mx_to_dev(c, s), K)
-    assert np.array_equal(out_bits(got), oracle.dequantize_mxfp4(c, s, K, oracle.F32).view(np.uint32))
+    T = _tensor_exp(w, mode)
+    c, s = _oracle_quantize(w, mode, T)
+    got = aq.aq_dequantize_fp(*_to_dev(c, s), K, mode, T)
+    ref = _oracle_dequantize(c, s, K, mode, T, oracle.F32)
+    assert np.array_equal(out_bits(got), ref.view(np.uint32))
 
 
 # ---- the decode product ---------------------------------------------------------------
-def _qmv_check(aq, N, K, xdt, seed, w=None):
+def _qmv_check(aq, mode, N, K, xdt, seed, w=None, T=None):
     if w is None:
         w = inputs.weights(N, K, seed=seed, key=(N, K), outliers=True)
-    c, s = oracle.quantize_mxfp4(w)
+    if T is None:
+        T = _tensor_exp(w, mode)
+    c, s = _oracle_quantize(w, mode, T)
     xb = inputs.activations(1, K, xdt, seed=seed, key=(N, K))
-    y_ref, A = oracle.matmul_dense(inputs.from_bits(xb, xdt), oracle.dequantize_mxfp4_exact(c, s, K))
-    y = aq.aq_qmv_mxfp4(bits_to_dev(xb, xdt), *_mx_to_dev(c, s))
+    y_ref, A = oracle.matmul_dense(inputs.from_bits(xb, xdt), _oracle_exact(c, s, K, mode, T))
+    y = aq.aq_qmv_fp(bits_to_dev(xb, xdt), *_to_dev(c, s), mode, T)
     ok, ratio = oracle.within_tolerance(out_to_f64(y), y_ref, A)
-    assert ok, f"qmv_mxfp4 N{N} K{K} {xdt}: worst error/bound = {ratio:.3f}"
+    assert ok, f"qmv_fp {mode} N{N} K{K} {xdt} T{T}: worst error/bound = {ratio:.3f}"
 
 
 # K: one chunk; 1..8 chunks per lane (ragged last passes: 4160 = 130 chunks,
 # 9600 = 300); past 16384 the kernel that keeps x in LDS, up to its limit
-_MX_K = [32, 96, 2048, 4160, 6176, 8192, 9600, 12288, 14336, 16384, 16416, 28672, 49152]
+_FP_K = [32, 96, 2048, 4160, 6176, 8192, 9600, 12288, 14336, 16384, 16416, 28672, 49152]
 
 
-@pytest.mark.parametrize("K", _MX_K)
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("K", _FP_K)
 @pytest.mark.parametrize("xdt", ["f16", "bf16"])
-def test_qmv_mxfp4_parity(aq, xdt, K):
+def test_qmv_fp_parity(aq, mode, xdt, K):
     if xdt == "bf16" and K < 512:
         pytest.skip("bf16: the bound covers the result's own rounding from K = 512 on")
-    _qmv_check(aq, 67, K, xdt, seed=64)
+    _qmv_check(aq, mode, 67, K, xdt, seed=64)
 
 
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("N,K", [(1, 4096), (1024, 4096), (4096, 4096), (14336, 4096),
                                  (4096, 14336), (9000, 2048)])
-def test_qmv_mxfp4_launch_shapes(aq, N, K):
+def test_qmv_fp_launch_shapes(aq, mode, N, K):
     """The shapes that select each launch configuration (rows in flight,
     waves per workgroup, workgroups per CU)."""
-    _qmv_check(aq, N, K, "f16", seed=65)
+    _qmv_check(aq, mode, N, K, "f16", seed=65)
 
 
-def test_qmv_mxfp4_many_rows_per_wave(aq):
+@pytest.mark.parametrize("mode", MODES)
+def test_qmv_fp_many_rows_per_wave(aq, mode):
     """More rows per wave than one output round: the ring refills."""
-    _qmv_check(aq, 300000, 64, "f16", seed=66)
+    _qmv_check(aq, mode, 300000, 64, "f16", seed=66)
 
 
-def test_qmv_mxfp4_special_groups(aq):
+@pytest.mark.parametrize("mode", MODES)
+def test_qmv_fp_special_groups(aq, mode):
     """Groups of zeros, subnormal and clamped exponents, ties and saturated
     members (the groups near the binary32 top left out: their products
-    overflow)."""
+    overflow); nvfp4 also without a tensor scale."""
     w = _special_rows()
     w = w[np.abs(w).max(axis=1) < 1e4]
     w = np.ascontiguousarray(np.tile(w.reshape(1, -1), (5, 3)))
-    _qmv_check(aq, w.shape[0], w.shape[1], "f16", seed=67, w=w)
+    for T in ((None, 0) if mode == "nvfp4" else (None,)):
+        _qmv_check(aq, mode, w.shape[0], w.shape[1], "f16", seed=67, w=w, T=T)
