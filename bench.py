@@ -44,10 +44,10 @@ the same bytes (same cold rotation and timing), a measured second denominator.
                 aq_dequantize of it to bf16 (% of HBM), the integer-zero-point
                 aq_quantize_zp and the range-search aq_quantize_mse over 21
                 narrowed ranges;
-  mxfp4         the decode product with mxfp4 weights (E2M1 codes, one
-                exponent byte per 32 weights) on the four decode matrices,
-                with the plain read of the same bytes, and mxfp4 quantize /
-                dequantize of the prefill-size matrix;
+  fp_modes      the block-scaled float modes mxfp4, nvfp4 and mxfp8: the
+                decode product on the four decode matrices, with the plain
+                read of the same bytes, and quantize / dequantize of the
+                prefill-size matrix, per mode;
   embedding     quantized embedding lookups (rows of a [128256, 4096] 8-bit
                 table dequantized to bf16) for 1 and 2048 tokens.
 
@@ -85,7 +85,8 @@ def parse():
     p.add_argument("--no-embedding", action="store_true", help="skip the embedding section")
     p.add_argument("--no-extra", action="store_true",
                    help="skip the spec-decode (M = 2..8) and MoE gather sections")
-    p.add_argument("--no-mxfp4", action="store_true", help="skip the mxfp4 section")
+    p.add_argument("--no-fp-modes", action="store_true",
+                   help="skip the block-scaled float modes section (mxfp4, nvfp4, mxfp8)")
     p.add_argument("--qmm-iters", type=int, default=20)
     p.add_argument("--copy-probe", action="store_true",
                    help="also run a plain 512 MiB device copy (counter calibration)")
@@ -287,9 +288,9 @@ def main():
     if not args.no_extra:
         result["quantize_dequantize"] = _quant_dequant(aq, inputs, dev, stream, legs)
 
-    # ---- mxfp4: block-scaled 4-bit floats ----------------------------------------------------
-    if not args.no_mxfp4:
-        result["mxfp4"] = _mxfp4(aq, inputs, dev, stream, legs)
+    # ---- block-scaled float modes ---------------------------------------------------------
+    if not args.no_fp_modes:
+        result["fp_modes"] = _fp_modes(aq, inputs, dev, stream, legs)
 
     # ---- quantized embedding ---------------------------------------------------------------
     if not args.no_embedding:
@@ -661,81 +662,100 @@ def _quant_dequant(aq, inputs, dev, stream, legs=None):
     return res
 
 
-def _mxfp4(aq, inputs, dev, stream, legs=None):
-    """mxfp4 (E2M1 codes, one exponent byte per 32 weights, 4.25 bits per
-    weight): the decode product on the four decode matrices (the headline
-    weights quantized by aq_quantize_mxfp4, x fp16), each launch on a cold
-    copy (>= 1 GiB rotated), per-launch time in a graph, with the plain read
-    of the same bytes beside it; and aq_quantize_mxfp4 / aq_dequantize_mxfp4
-    (bf16 out) on the prefill-size matrix."""
+def _fp_tensor_exp(w, mode):
+    """nvfp4's tensor exponent T = ceil(log2(max|W| / 2688)) (the largest group
+    scale near the top of E4M3's range); 0 for the mx modes."""
+    if mode != "nvfp4":
+        return 0
+    amax = float(w.abs().max())
+    return 0 if amax == 0 else max(-100, min(100, math.ceil(math.log2(amax / 2688))))
+
+
+def _fp_modes(aq, inputs, dev, stream, legs=None):
+    """Block-scaled float modes (mxfp4: E2M1 codes + exponent byte per 32,
+    4.25 bits/weight; nvfp4: E2M1 codes + E4M3 scale per 16, 4.5 bits;
+    mxfp8: E4M3 codes + exponent byte per 32, 8.25 bits): the decode product
+    on the four decode matrices (the headline weights quantized by
+    aq_quantize_fp, x fp16), each launch on a cold copy (>= 1 GiB rotated),
+    per-launch time in a graph, with the plain read of the same bytes beside
+    it; and aq_quantize_fp / aq_dequantize_fp (bf16) on the prefill-size
+    matrix."""
     import torch
-    out = {"workload": "mxfp4 decode M=1, W [4096,4096] [1024,4096] [14336,4096] [4096,14336], "
-                       "fp16 x, cold weights"}
-    rows = {}
-    total_us = total_bytes = 0
-    for i, (N, K) in enumerate(DECODE_SHAPES):
-        w = inputs.weights_device(N, K, device=dev, seed=0, key=(1, i), outliers=True)
-        packed = aq.aq_quantize_mxfp4(w)
-        del w
-        wbytes = N * K // 2 + N * K // 32
-        copies = max(2, math.ceil(COLD_BYTES / wbytes))
-        sets = [packed] + [tuple(t.clone() for t in packed) for _ in range(copies - 1)]
-        x = inputs.activations_device(1, K, "f16", device=dev, seed=0, key=(1, i))
-        y = torch.empty((1, N), dtype=torch.float16, device=dev)
-        fs = [lambda c=c, s_=s_: aq.aq_qmv_mxfp4(x, c, s_, y=y) for (c, s_) in sets] * 2
-        us = _graph_us(torch, stream, fs)
-        ceil_us = _read_ceiling_us(aq, torch, wbytes, stream)
-        gbs = wbytes / (us * 1e-6) / 1e9
-        rows[f"{N}x{K}"] = {"kernel": aq.aq_qmv_mxfp4_describe(N, K), "weight_bytes": wbytes,
-                            "avg_us": round(us, 3), "weight_gbs": round(gbs, 1),
-                            "pct_hbm": round(100 * gbs / HBM_PEAK_GBS, 1),
-                            "read_ceiling_us": round(ceil_us, 3),
-                            "frac_of_read_ceiling": round(ceil_us / us, 3)}
-        total_us += us
-        total_bytes += wbytes
-        print(f"# mxfp4 QMV {N}x{K}: {us:.2f} us, {gbs:.0f} GB/s weights, "
-              f"{ceil_us / us:.2f} of the plain read", file=sys.stderr, flush=True)
-        if legs is not None and "mxfp4_decode" not in legs:
-            # the oracle on the first matrix: exact dequantize, then the product
-            import oracle
-            hx = _host_x(x, "f16")
-            hc = packed[0].cpu().numpy().view("uint32")
-            hs = packed[1].cpu().numpy()
-            runs, el = _cpu_timed(
-                lambda: oracle.matmul_dense(hx, oracle.dequantize_mxfp4_exact(hc, hs, K)), 1.5)
-            legs["mxfp4_decode"] = {"workload": f"mxfp4 W [{N},{K}], x fp16 [1,{K}]",
-                                    "threads": oracle.num_threads(),
-                                    "gbs": round(wbytes * runs / el / 1e9, 3),
-                                    "gpu_gbs": round(gbs, 1),
-                                    "sample": f"{runs} call(s) in {el:.1f} s"}
-        del sets, packed
+    out = {"workload": "decode M=1, W [4096,4096] [1024,4096] [14336,4096] [4096,14336], "
+                       "fp16 x, cold weights; quantize / dequantize W [28672,8192] fp32 <-> bf16"}
+    ceilings = {}
+    for mode, (_, grp, bits) in aq.FP_MODES.items():
+        rows = {}
+        total_us = total_bytes = 0
+        for i, (N, K) in enumerate(DECODE_SHAPES):
+            w = inputs.weights_device(N, K, device=dev, seed=0, key=(1, i), outliers=True)
+            T = _fp_tensor_exp(w, mode)
+            packed = aq.aq_quantize_fp(w, mode, T)
+            del w
+            wbytes = N * K * bits // 8 + N * K // grp
+            copies = max(2, math.ceil(COLD_BYTES / wbytes))
+            sets = [packed] + [tuple(t.clone() for t in packed) for _ in range(copies - 1)]
+            x = inputs.activations_device(1, K, "f16", device=dev, seed=0, key=(1, i))
+            y = torch.empty((1, N), dtype=torch.float16, device=dev)
+            fs = [lambda c=c, s_=s_: aq.aq_qmv_fp(x, c, s_, mode, T, y=y) for (c, s_) in sets] * 2
+            us = _graph_us(torch, stream, fs)
+            if wbytes not in ceilings:
+                ceilings[wbytes] = _read_ceiling_us(aq, torch, wbytes, stream)
+            ceil_us = ceilings[wbytes]
+            gbs = wbytes / (us * 1e-6) / 1e9
+            rows[f"{N}x{K}"] = {"kernel": aq.aq_qmv_fp_describe(N, K, mode), "weight_bytes": wbytes,
+                                "tensor_exp": T, "avg_us": round(us, 3),
+                                "weight_gbs": round(gbs, 1),
+                                "pct_hbm": round(100 * gbs / HBM_PEAK_GBS, 1),
+                                "read_ceiling_us": round(ceil_us, 3),
+                                "frac_of_read_ceiling": round(ceil_us / us, 3)}
+            total_us += us
+            total_bytes += wbytes
+            print(f"# {mode} QMV {N}x{K}: {us:.2f} us, {gbs:.0f} GB/s weights, "
+                  f"{ceil_us / us:.2f} of the plain read", file=sys.stderr, flush=True)
+            if legs is not None and f"{mode}_decode" not in legs:
+                # the oracle on the first matrix: exact dequantize, then the product
+                import oracle
+                hx = _host_x(x, "f16")
+                hc = packed[0].cpu().numpy().view("uint32")
+                hs = packed[1].cpu().numpy()
+                deq = {"mxfp4": lambda: oracle.dequantize_mxfp4_exact(hc, hs, K),
+                       "mxfp8": lambda: oracle.dequantize_mxfp8_exact(hc, hs, K),
+                       "nvfp4": lambda: oracle.dequantize_nvfp4_exact(hc, hs, K, T)}[mode]
+                runs, el = _cpu_timed(lambda: oracle.matmul_dense(hx, deq()), 1.0)
+                legs[f"{mode}_decode"] = {"workload": f"{mode} W [{N},{K}], x fp16 [1,{K}]",
+                                          "threads": oracle.num_threads(),
+                                          "gbs": round(wbytes * runs / el / 1e9, 3),
+                                          "gpu_gbs": round(gbs, 1),
+                                          "sample": f"{runs} call(s) in {el:.1f} s"}
+            del sets, packed
+            torch.cuda.synchronize()
+        res = {"per_shape": rows, "step_us": round(total_us, 3), "step_weight_bytes": total_bytes,
+               "step_weight_gbs": round(total_bytes / (total_us * 1e-6) / 1e9, 1)}
+        # quantize (fp32 in) and dequantize (bf16 out) of the prefill-size matrix
+        N, K = PREFILL["N"], PREFILL["K"]
+        w = inputs.weights_device(N, K, device=dev, seed=0, key=(inputs.WORKLOAD_ID["prefill"],))
+        T = _fp_tensor_exp(w, mode)
+        c, s_ = aq.aq_quantize_fp(w, mode, T)
+        deq = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+        packed = N * K * bits // 8 + N * K // grp
+        us = _graph_us(torch, stream, [lambda: aq.aq_quantize_fp(w, mode, T, codes=c, scales=s_)] * 4)
+        nb = 4 * N * K + packed
+        res["quantize"] = {"avg_us": round(us, 2), "bytes": nb,
+                           "gbs": round(nb / (us * 1e-6) / 1e9, 1),
+                           "pct_hbm": round(100 * nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
+        us = _graph_us(torch, stream, [lambda: aq.aq_dequantize_fp(c, s_, K, mode, T, out=deq)] * 4)
+        nb = packed + 2 * N * K
+        res["dequantize_bf16"] = {"avg_us": round(us, 2), "bytes": nb,
+                                  "gbs": round(nb / (us * 1e-6) / 1e9, 1),
+                                  "pct_hbm": round(100 * nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
+        print(f"# {mode} step {total_us:.2f} us ({res['step_weight_gbs']} GB/s); quantize "
+              f"{res['quantize']['avg_us']:.1f} us ({res['quantize']['gbs']} GB/s), dequantize "
+              f"{res['dequantize_bf16']['avg_us']:.1f} us ({res['dequantize_bf16']['gbs']} GB/s)",
+              file=sys.stderr, flush=True)
+        out[mode] = res
+        del w, c, s_, deq
         torch.cuda.synchronize()
-    out["per_shape"] = rows
-    out["step_us"] = round(total_us, 3)
-    out["step_weight_bytes"] = total_bytes
-    out["step_weight_gbs"] = round(total_bytes / (total_us * 1e-6) / 1e9, 1)
-    # quantize (fp32 in) and dequantize (bf16 out) of the prefill-size matrix
-    N, K = PREFILL["N"], PREFILL["K"]
-    w = inputs.weights_device(N, K, device=dev, seed=0, key=(inputs.WORKLOAD_ID["prefill"],))
-    c, s_ = aq.aq_quantize_mxfp4(w)
-    deq = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
-    packed = N * K // 2 + N * K // 32
-    us = _graph_us(torch, stream, [lambda: aq.aq_quantize_mxfp4(w, codes=c, scales=s_)] * 4)
-    nb = 4 * N * K + packed
-    out["quantize"] = {"workload": f"W [{N},{K}] fp32", "avg_us": round(us, 2), "bytes": nb,
-                       "gbs": round(nb / (us * 1e-6) / 1e9, 1),
-                       "pct_hbm": round(100 * nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
-    us = _graph_us(torch, stream, [lambda: aq.aq_dequantize_mxfp4(c, s_, K, out=deq)] * 4)
-    nb = packed + 2 * N * K
-    out["dequantize_bf16"] = {"avg_us": round(us, 2), "bytes": nb,
-                              "gbs": round(nb / (us * 1e-6) / 1e9, 1),
-                              "pct_hbm": round(100 * nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
-    print(f"# mxfp4 step {total_us:.2f} us ({out['step_weight_gbs']} GB/s); quantize "
-          f"{out['quantize']['avg_us']:.1f} us ({out['quantize']['gbs']} GB/s), dequantize "
-          f"{out['dequantize_bf16']['avg_us']:.1f} us ({out['dequantize_bf16']['gbs']} GB/s)",
-          file=sys.stderr, flush=True)
-    del w, c, s_, deq
-    torch.cuda.synchronize()
     return out
 
 
