@@ -417,7 +417,9 @@ __device__ __forceinline__ float chunk_sum(const fp_u4 (&cw)[chunk_fmt<MODE>::VW
     s0 = fp4_word_dot(XT{}, cw[0][1], xv + 4, s0);
     s1 = fp4_word_dot(XT{}, cw[0][2], xv + 8, s1);
     s1 = fp4_word_dot(XT{}, cw[0][3], xv + 12, s1);
-    return s0 * e4m3_mag(sb & 0xFFu) + s1 * e4m3_mag(sb >> 8);
+    // the two E4M3 scales through one convert (exact in fp16)
+    const fp_h2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false);
+    return s0 * (float)sc[0] + s1 * (float)sc[1];
   } else {
     float s = 0.f;
 #pragma unroll
