@@ -106,8 +106,9 @@
  *      magnitude code nearest to |w| / 2^X (ties to the even code, i.e. the
  *      even mantissa; above 448 that is 448); codes are bytes in row order
  *      (R3 with b = 8).  Dequantized value: code value * 2^X.
- *  R18 nvfp4 ([ET] "NVIDIA FP4 weight-only quantization", group size 16;
- *      the same MLX passages: groups of 16, 4-bit codes).  Taken from the
+ *  R18 nvfp4 ([ET] configuration table and CLI options: NVIDIA's FP4
+ *      format for weights, group size 16; the same MLX passages: groups of
+ *      16, 4-bit codes).  Taken from the
  *      NVFP4 format of that name: codes are E2M1 as in R16, packed as in
  *      R16; each group of 16 stores one scale s, an E4M3 value (as in R17,
  *      sign bit 0) written as its byte; the whole matrix shares a second

@@ -241,3 +241,31 @@ def test_qmv_fp_special_groups(aq, mode):
     w = np.ascontiguousarray(np.tile(w.reshape(1, -1), (5, 3)))
     for T in ((None, 0) if mode == "nvfp4" else (None,)):
         _qmv_check(aq, mode, w.shape[0], w.shape[1], "f16", seed=67, w=w, T=T)
+
+
+# ---- the prefill-size matrix ----------------------------------------------------------
+@pytest.fixture(scope="module")
+def prefill_weights():
+    N, K = inputs.WORKLOADS["prefill"]["shapes"][0]
+    return inputs.weights(N, K, seed=0, key=(inputs.WORKLOAD_ID["prefill"],))
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_fp_prefill_size(aq, prefill_weights, mode):
+    """The benchmark's 28672 x 8192 matrix: quantize bit-exact on every
+    element; dequantize to bf16 bit-exact on sampled rows."""
+    import torch
+    w = prefill_weights
+    N, K = w.shape
+    T = _tensor_exp(w, mode)
+    wd = to_dev(w)
+    gc, gs = aq.aq_quantize_fp(wd, mode, T)
+    del wd
+    c, s = _oracle_quantize(w, mode, T)
+    assert np.array_equal(gs.cpu().numpy(), s)
+    assert np.array_equal(gc.cpu().numpy().view(np.uint32), c)
+    out = aq.aq_dequantize_fp(gc, gs, K, mode, T, out_dtype=torch.bfloat16)
+    rows = np.unique(np.concatenate([np.random.default_rng(5).choice(N, 64, replace=False),
+                                     [0, N - 1]]))
+    ref = _oracle_dequantize(c[rows], s[rows], K, mode, T, oracle.BF16)
+    _assert_same_bits(out_bits(out)[rows], ref, "bf16")

@@ -3,7 +3,7 @@
 "Quantization" (metalworking, newer-modes paragraph) and "Quantizing a Model
 for MLX" ("Modes, bits and mixed recipes") name mxfp8 (groups of 32, 8-bit
 codes) and nvfp4 (groups of 16, 4-bit codes) as block-scaled float modes; the
-ExecuTorch page calls nvfp4 NVIDIA FP4 weight-only quantization with group
+ExecuTorch page lists nvfp4 as NVIDIA's FP4 format for weights, with group
 size 16.  The bit layouts are taken from the microscaling (E4M3 codes, a
 power-of-two scale) and NVFP4 (E2M1 codes, an E4M3 scale per 16, a tensor
 scale) definitions.  Pinned here by
