@@ -17,7 +17,8 @@
 // as are the W chunks into register sets.  A step's loads are spread over
 // its four 16-k slices, and the one barrier per step waits only for the
 // stage it needs.  When the tiles leave a last round at most half full,
-// those columns run as 128 x 256 tiles in a second launch.
+// those columns run as 256 x 128 tiles (one 32-column block per wave) in a
+// second launch.
 //
 // The gather variant ("Quantization", metalworking: gather variants of the
 // kernels for MoE experts, here at prefill size) computes y[t, j, :] =
@@ -176,8 +177,9 @@ __device__ __forceinline__ int block_exclusive_sum(int v, int *wsum, int *total)
 // operands.  One 256-thread workgroup computes a 256 x 256 tile of Y; wave w
 // owns the 64 columns 64w .. 64w+63 and all 256 rows: 8 x 2 blocks of
 // v_mfma_f32_32x32x16 (256 accumulators per lane, in the accumulation
-// registers one wave per SIMD can hold).  Each lane loads, for each of its two
-// 32-column blocks, one whole 32-code chunk of its column's W row per K step
+// registers one wave per SIMD can hold; with NB = 1, a 256 x 128 tile, wave w
+// owns the 32 columns 32w .. 32w+31, 8 x 1 blocks).  Each lane loads, for each
+// of its NB 32-column blocks, one whole 32-code chunk of its column's W row per K step
 // of 64 and dequantizes it (q*s + b in binary32, rounded to nearest even into
 // the activation type, the value aq_dequantize returns) directly into the B
 // operand: no weight ever passes through LDS, and no other wave needs it.
@@ -190,8 +192,7 @@ __device__ __forceinline__ int block_exclusive_sum(int v, int *wsum, int *total)
 // k = 32 h + 8 ks + 0..7; the A fragments are read from LDS in that same
 // order (a permutation of k applied to both operands leaves the dot products
 // unchanged).
-constexpr int WBN = 256;                     // tile columns
-constexpr int WFN = 2;                       // 32-column blocks per wave
+constexpr int WBN = 256;                     // tile columns (two 32-column blocks per wave)
 constexpr int kWStages = 4;                  // X stages in LDS (32 KB each)
 
 // a tile of 32 FM rows: 16-byte X units per thread per step
@@ -218,18 +219,18 @@ __device__ __forceinline__ void stage_barrier() {
 }
 
 // one thread's W chunks (one per 32-column block) of one K step
-template <int BITS>
+template <int BITS, int NB>
 struct WrRegs {
-  uint32_t w[WFN][BITS];
-  uint32_t s[WFN], b[WFN];
+  uint32_t w[NB][BITS];
+  uint32_t s[NB], b[NB];
 };
 
 // Scheduling hint for one 16-k slice: 2 FM MFMAs, NR LDS reads and NG global
 // loads among the first slots, NV vector ALU instructions after each MFMA.
-template <int FM, int NR, int NV, int NG>
+template <int FM, int NB, int NR, int NV, int NG>
 __device__ __forceinline__ void sched_kslice() {
 #pragma unroll
-  for (int i = 0; i < FM * WFN; ++i) {
+  for (int i = 0; i < FM * NB; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     if (i < NG) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
@@ -237,13 +238,13 @@ __device__ __forceinline__ void sched_kslice() {
   }
 }
 
-// FM: 32-row blocks per tile (8: 256 x 256 tiles; 4: 128 x 256, for a last
-// partial round of tiles).  G1: one group per 32-code chunk (G = 32).  y rows
-// are ldy elements apart.  GATHER (MoE prefill, FM = 8): grid y is the
+// FM: 32-row blocks per tile.  NB: 32-column blocks per wave (2: 256 x 256
+// tiles; 1: 256 x 128, for a last partial round of tiles).  G1: one group
+// per 32-code chunk (G = 32).  y rows are ldy elements apart.  GATHER (MoE prefill, FM = 8): grid y is the
 // expert; the workgroup lists the (token, slot) pairs routed to its expert
 // (route) and runs 256-row tiles over that list, X rows loaded by token and
 // Y rows stored by pair.
-template <int BITS, typename XT, int FM, bool G1, bool GATHER>
+template <int BITS, typename XT, int FM, int NB, bool G1, bool GATHER>
 __global__ __launch_bounds__(kThreads) void qmm_wr_kernel(const uint16_t *__restrict__ x,
                                                           int64_t M,
                                                           const uint32_t *__restrict__ codes,
@@ -252,12 +253,13 @@ __global__ __launch_bounds__(kThreads) void qmm_wr_kernel(const uint16_t *__rest
                                                           int64_t N, int64_t K, int G,
                                                           uint16_t *__restrict__ y, int64_t ldy,
                                                           Routing route) {
-  constexpr int TBM = 32 * FM, kXSt = TBM * BK * 2, kXD = kWrXDma<FM>;
-  // a thread's loads per step: the X copy, the codes of its two W chunks,
+  constexpr int TBM = 32 * FM, TBN = 128 * NB, kXSt = TBM * BK * 2, kXD = kWrXDma<FM>;
+  // a thread's loads per step: the X copy, the codes of its NB W chunks,
   // their scales and biases (G > 32: one scale and one bias per lane, for
-  // the block of its half, exchanged between the halves afterwards)
+  // the block of its half, exchanged between the halves afterwards when
+  // NB = 2)
   constexpr int kCode = kChunkLoads<BITS> - 2;
-  constexpr int kStepLoads = kXD + 2 * kCode + (G1 ? 4 : 2);
+  constexpr int kStepLoads = kXD + NB * kCode + (G1 ? 2 * NB : 2);
   // four distinct LDS objects, one per X stage
   __shared__ __attribute__((aligned(16))) char xs0[kXSt], xs1[kXSt], xs2[kXSt], xs3[kXSt];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -274,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void qmm_wr_kernel(const uint16_t *__rest
   // those X rows in its L2.  (No division: the tile coordinates stay scalar,
   // and with them the operand resources.)
   int64_t tile_m = 0;
-  const int64_t tile_n = (int64_t)blockIdx.x * WBN;
+  const int64_t tile_n = (int64_t)blockIdx.x * TBN;
   int expert = 0;
   if constexpr (GATHER) {
     expert = blockIdx.y;
@@ -288,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void qmm_wr_kernel(const uint16_t *__rest
   // operand tiles as buffer resources: rows past M or N read as zero (the
   // gather addresses all of x by token)
   const int64_t mrows = M - tile_m < TBM ? M - tile_m : TBM;
-  const int64_t nrows = N - tile_n < WBN ? N - tile_n : WBN;
+  const int64_t nrows = N - tile_n < TBN ? N - tile_n : TBN;
   const int xbytes = (int)((GATHER ? M : mrows) * K * 2);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + tile_m * K, xbytes);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(codes + tile_n * wpr, nrows * wpr * 4);
@@ -340,35 +342,38 @@ __global__ __launch_bounds__(kThreads) void qmm_wr_kernel(const uint16_t *__rest
   // G = 32: the lane reads the scale and bias of its chunk for both blocks;
   // G > 32 (both chunks in one group): only those of block h, which one
   // v_permlane32_swap then gives to both halves.
-  uint32_t wvoff[WFN], svoff[WFN], wvoff0[WFN], svoff0[WFN];
+  uint32_t wvoff[NB], svoff[NB], wvoff0[NB], svoff0[NB];
 #pragma unroll
-  for (int cb = 0; cb < WFN; ++cb) {
-    const int n = 64 * wave + 32 * (G1 ? cb : h) + (lane & 31);
-    wvoff[cb] = (uint32_t)((64 * wave + 32 * cb + (lane & 31)) * wpr + h * BITS) * 4u;
+  for (int cb = 0; cb < NB; ++cb) {
+    const int n = 32 * NB * wave + 32 * (G1 ? cb : (NB == 2 ? h : 0)) + (lane & 31);
+    wvoff[cb] = (uint32_t)((32 * NB * wave + 32 * cb + (lane & 31)) * wpr + h * BITS) * 4u;
     svoff[cb] = (uint32_t)(n * gpr + (G1 ? h : 0)) * 2u;
     wvoff0[cb] = ktail && h ? 0x80000000u : wvoff[cb];  // past every resource: zeros
     svoff0[cb] = G1 && ktail && h ? 0x80000000u : svoff[cb];
   }
-  // part p of a step's W loads: the codes of block p, then (G = 32) the
-  // scale and bias of block p, or (G > 32) the scale (p = 0) or the bias
-  auto load_w = [&](int k0, WrRegs<BITS> &r, const uint32_t (&wv)[WFN], const uint32_t (&sv)[WFN],
+  // part p of a step's W loads: the codes of block p (if any), then (G = 32)
+  // the scale and bias of block p, or (G > 32) the scale (p = 0) or the bias
+  auto load_w = [&](int k0, WrRegs<BITS, NB> &r, const uint32_t (&wv)[NB], const uint32_t (&sv)[NB],
                     int part) {
     const int c0 = k0 >> 5;
-    bload_chunk<BITS>(rw, wv[part], (uint32_t)(c0 * BITS) * 4u, r.w[part]);
+    if (part < NB) bload_chunk<BITS>(rw, wv[part], (uint32_t)(c0 * BITS) * 4u, r.w[part]);
     const uint32_t so = (uint32_t)(c0 >> gshift) * 2u;
     if constexpr (G1) {
-      r.s[part] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)sv[part], (int)so, 0);
-      r.b[part] = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)sv[part], (int)so, 0);
+      if (part < NB) {
+        r.s[part] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)sv[part], (int)so, 0);
+        r.b[part] = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)sv[part], (int)so, 0);
+      }
     } else if (part == 0) {
       r.s[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)sv[0], (int)so, 0);
     } else {
       r.b[0] = __builtin_amdgcn_raw_buffer_load_b16(rb, (int)sv[0], (int)so, 0);
     }
   };
-  // before the first use of a register set (G > 32): lanes l and l + 32 hold
-  // the scale (bias) of blocks 0 and 1; afterwards every lane holds both
-  auto share_sb = [&](WrRegs<BITS> &r) {
-    if constexpr (!G1) {
+  // before the first use of a register set (G > 32, NB = 2): lanes l and
+  // l + 32 hold the scale (bias) of blocks 0 and 1; afterwards every lane
+  // holds both (NB = 1: both halves loaded those of their own column)
+  auto share_sb = [&](WrRegs<BITS, NB> &r) {
+    if constexpr (!G1 && NB == 2) {
       const auto sp = __builtin_amdgcn_permlane32_swap(r.s[0], r.s[0], false, false);
       const auto bp = __builtin_amdgcn_permlane32_swap(r.b[0], r.b[0], false, false);
       r.s[0] = sp[0];
@@ -378,10 +383,10 @@ __global__ __launch_bounds__(kThreads) void qmm_wr_kernel(const uint16_t *__rest
     }
   };
   const uint32_t nmask = opaque(0x0F0F0F0Fu);
-  auto dequant = [&](const WrRegs<BITS> &r, auto kscon, uint4 (&bq)[WFN]) {
+  auto dequant = [&](const WrRegs<BITS, NB> &r, auto kscon, uint4 (&bq)[NB]) {
     constexpr int ks = decltype(kscon)::value;
 #pragma unroll
-    for (int cb = 0; cb < WFN; ++cb)
+    for (int cb = 0; cb < NB; ++cb)
       bq[cb] = dequant8<BITS, XT, ks>(r.w[cb], f16_to_f32((uint16_t)r.s[cb]),
                                       f16_to_f32((uint16_t)r.b[cb]), nmask);
   };
@@ -398,10 +403,10 @@ __global__ __launch_bounds__(kThreads) void qmm_wr_kernel(const uint16_t *__rest
     for (int i = 0; i < FM; ++i) a[i] = *reinterpret_cast<const uint4 *>(p + i * 32 * 128);
   };
 
-  f32x16v acc[FM][WFN];
-  auto mfma_ks = [&](const uint4 (&a)[FM], const uint4 (&b)[WFN]) {
+  f32x16v acc[FM][NB];
+  auto mfma_ks = [&](const uint4 (&a)[FM], const uint4 (&b)[NB]) {
 #pragma unroll
-    for (int j = 0; j < WFN; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int i = 0; i < FM; ++i) acc[i][j] = mfma32<XT>(a[i], b[j], acc[i][j]);
   };
@@ -419,11 +424,11 @@ __global__ __launch_bounds__(kThreads) void qmm_wr_kernel(const uint16_t *__rest
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < WFN; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  WrRegs<BITS> wr[kWStages];  // W of step s in wr[s % 4]
-  uint4 fa[2][FM], fb[2][WFN];
+  WrRegs<BITS, NB> wr[kWStages];  // W of step s in wr[s % 4]
+  uint4 fa[2][FM], fb[2][NB];
   using K0 = std::integral_constant<int, 0>;
   using K1 = std::integral_constant<int, 1>;
   using K2 = std::integral_constant<int, 2>;
@@ -457,19 +462,19 @@ __global__ __launch_bounds__(kThreads) void qmm_wr_kernel(const uint16_t *__rest
     dequant(wr[j], K1{}, fb[1]);
     dma_x(k3, stage(J3{}), xvoff, kXD / 2, kXD);
     mfma_ks(fa[0], fb[0]);
-    sched_kslice<FM, FM, kNV, kXD / 2>();
+    sched_kslice<FM, NB, FM, kNV, kXD / 2>();
     __builtin_amdgcn_sched_barrier(0);
     frag(sb, 2, fa[0]);
     dequant(wr[j], K2{}, fb[0]);
     load_w(k3, wr[j3], wvoff, svoff, 0);
     mfma_ks(fa[1], fb[1]);
-    sched_kslice<FM, FM, kNV, kChunkLoads<BITS>>();
+    sched_kslice<FM, NB, FM, kNV, kChunkLoads<BITS>>();
     __builtin_amdgcn_sched_barrier(0);
     frag(sb, 3, fa[1]);
     dequant(wr[j], K3{}, fb[1]);
     load_w(k3, wr[j3], wvoff, svoff, 1);
     mfma_ks(fa[0], fb[0]);
-    sched_kslice<FM, FM, kNV, kChunkLoads<BITS>>();
+    sched_kslice<FM, NB, FM, kNV, kChunkLoads<BITS>>();
     __builtin_amdgcn_sched_barrier(0);
     // step st + 1's X and W have landed (steps st + 2, st + 3 stay in flight)
     constexpr int kAhead = FIN ? 0 : (2 * kStepLoads < 63 ? 2 * kStepLoads : 63);
@@ -479,7 +484,7 @@ __global__ __launch_bounds__(kThreads) void qmm_wr_kernel(const uint16_t *__rest
     share_sb(wr[jn]);
     dequant(wr[jn], K0{}, fb[0]);
     mfma_ks(fa[1], fb[1]);
-    sched_kslice<FM, FM, kNV, kXD / 2>();
+    sched_kslice<FM, NB, FM, kNV, kXD / 2>();
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -505,8 +510,8 @@ __global__ __launch_bounds__(kThreads) void qmm_wr_kernel(const uint16_t *__rest
   frag(q0, 0, fa[0]);
   share_sb(wr[0]);
   if (!G1 && ktail && h) {  // step 0 is the K tail: chunk 1 lies past K, its weights read 0
-    wr[0].s[0] = wr[0].s[1] = 0;
-    wr[0].b[0] = wr[0].b[1] = 0;
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) wr[0].s[cb] = wr[0].b[cb] = 0;
   }
   dequant(wr[0], K0{}, fb[0]);
 
@@ -533,8 +538,8 @@ __global__ __launch_bounds__(kThreads) void qmm_wr_kernel(const uint16_t *__rest
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < WFN; ++j) {
-        const int64_t n = tile_n + 64 * wave + 32 * j + (lane & 31);
+      for (int j = 0; j < NB; ++j) {
+        const int64_t n = tile_n + 32 * NB * wave + 32 * j + (lane & 31);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t m = tile_m + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -555,8 +560,8 @@ __global__ __launch_bounds__(kThreads) void qmm_wr_kernel(const uint16_t *__rest
           if (lr < rows) {
             uint16_t *yr = y + (int64_t)glist[r0 + lr] * ldy;
 #pragma unroll
-            for (int j = 0; j < WFN; ++j) {
-              const int64_t n = tile_n + 64 * wave + 32 * j + (lane & 31);
+            for (int j = 0; j < NB; ++j) {
+              const int64_t n = tile_n + 32 * NB * wave + 32 * j + (lane & 31);
               if (n < N) yr[n] = xtraits<XT>::from_f32(acc[i][j][r]);
             }
           }
@@ -610,39 +615,41 @@ hipError_t qmm_wr_launch(const void *x, int64_t M, const uint32_t *codes, const 
   if ((int64_t)BM * K * 2 > 0x7FFFFFFF) return hipErrorInvalidValue;  // 32-bit tile offsets
   // One block per compute unit at a time: when the tiles leave a last round
   // at most half full, and that remainder is a whole number of column tiles,
-  // those columns run as 128-row tiles in a second launch (twice the blocks,
-  // half the work each), which fills the chip for that round.  At 2048 x
-  // 28672: 896 tiles = 768 (three rounds) + 16 columns of 8, run as 256
-  // half tiles.
+  // those columns run as 128-column tiles in a second launch (twice the
+  // blocks, half the work each), which fills the chip for that round.  At
+  // 2048 x 28672: 896 tiles = 768 (three rounds) + 16 columns of 8, run as
+  // 256 half tiles.  Halving the columns rather than the rows keeps each
+  // dequantized weight fragment serving 8 row blocks (measured on the MI355X,
+  // 4-bit: the tail took 169-193 us as 128 x 256 tiles).
   const int64_t cus = device_cus(), rem = (mt * nt) % cus;
   const int64_t ntail = rem > 0 && 2 * rem <= cus && rem % mt == 0 ? rem / mt : 0;
   const int64_t nmain = nt - ntail, n0 = nmain * WBN;
   const int64_t wpr = (K >> 5) * BITS, gpr = (K >> 5) / (G >> 5);
   uint16_t *yo = (uint16_t *)y;
-  auto go = [&](auto fm, auto g1) {
-    constexpr int FM = decltype(fm)::value;
+  auto go = [&](auto nb, auto g1) {
+    constexpr int NB = decltype(nb)::value;
     constexpr bool G1 = decltype(g1)::value;
-    if (FM == 8)
-      hipLaunchKernelGGL((qmm_wr_kernel<BITS, XT, 8, G1, false>),
+    if (NB == 2)
+      hipLaunchKernelGGL((qmm_wr_kernel<BITS, XT, 8, 2, G1, false>),
                          dim3((unsigned)nmain, (unsigned)mt), dim3(kThreads), 0, s,
                          (const uint16_t *)x, M, codes, scales, biases, n0 < N ? n0 : N, K, G, yo,
                          N, Routing{});
     else
-      hipLaunchKernelGGL((qmm_wr_kernel<BITS, XT, 4, G1, false>),
-                         dim3((unsigned)ntail, (unsigned)(2 * mt)), dim3(kThreads), 0, s,
-                         (const uint16_t *)x, M, codes + n0 * wpr, scales + n0 * gpr,
+      hipLaunchKernelGGL((qmm_wr_kernel<BITS, XT, 8, 1, G1, false>),
+                         dim3((unsigned)((N - n0 + 127) / 128), (unsigned)mt), dim3(kThreads), 0,
+                         s, (const uint16_t *)x, M, codes + n0 * wpr, scales + n0 * gpr,
                          biases ? biases + n0 * gpr : nullptr, N - n0, K, G, yo + n0, N,
                          Routing{});
   };
-  using F8 = std::integral_constant<int, 8>;
-  using F4 = std::integral_constant<int, 4>;
+  using B2 = std::integral_constant<int, 2>;
+  using B1 = std::integral_constant<int, 1>;
   if (nmain > 0) {
-    if (G == 32) go(F8{}, std::true_type{});
-    else go(F8{}, std::false_type{});
+    if (G == 32) go(B2{}, std::true_type{});
+    else go(B2{}, std::false_type{});
   }
   if (ntail > 0) {
-    if (G == 32) go(F4{}, std::true_type{});
-    else go(F4{}, std::false_type{});
+    if (G == 32) go(B1{}, std::true_type{});
+    else go(B1{}, std::false_type{});
   }
   return hipGetLastError();
 }
@@ -658,11 +665,11 @@ hipError_t gather_qmm_launch(const void *x, int64_t T, const uint32_t *codes,
     return hipErrorInvalidValue;
   const Routing route{ids, T * topk, topk, E};
   if (G == 32)
-    hipLaunchKernelGGL((qmm_wr_kernel<BITS, XT, 8, true, true>), dim3((unsigned)nt, (unsigned)E),
+    hipLaunchKernelGGL((qmm_wr_kernel<BITS, XT, 8, 2, true, true>), dim3((unsigned)nt, (unsigned)E),
                        dim3(kThreads), 0, s, (const uint16_t *)x, T, codes, scales, biases, N, K,
                        G, (uint16_t *)y, N, route);
   else
-    hipLaunchKernelGGL((qmm_wr_kernel<BITS, XT, 8, false, true>), dim3((unsigned)nt, (unsigned)E),
+    hipLaunchKernelGGL((qmm_wr_kernel<BITS, XT, 8, 2, false, true>), dim3((unsigned)nt, (unsigned)E),
                        dim3(kThreads), 0, s, (const uint16_t *)x, T, codes, scales, biases, N, K,
                        G, (uint16_t *)y, N, route);
   return hipGetLastError();
