@@ -682,7 +682,8 @@ def _fp_modes(aq, inputs, dev, stream, legs=None):
     matrix."""
     import torch
     out = {"workload": "decode M=1, W [4096,4096] [1024,4096] [14336,4096] [4096,14336], "
-                       "fp16 x, cold weights; quantize / dequantize W [28672,8192] fp32 <-> bf16"}
+                       "fp16 x, cold weights; M=4, 8 bf16 x on the two 33 MB matrices; "
+                       "quantize / dequantize W [28672,8192] fp32 <-> bf16"}
     ceilings = {}
     for mode, (_, grp, bits) in aq.FP_MODES.items():
         rows = {}
@@ -713,6 +714,21 @@ def _fp_modes(aq, inputs, dev, stream, legs=None):
             total_bytes += wbytes
             print(f"# {mode} QMV {N}x{K}: {us:.2f} us, {gbs:.0f} GB/s weights, "
                   f"{ceil_us / us:.2f} of the plain read", file=sys.stderr, flush=True)
+            if N * K >= 4096 * 14336:
+                # speculative-decoding widths on the matrix cores, bf16 x
+                for M in (4, 8):
+                    xm = inputs.activations_device(M, K, "bf16", device=dev, seed=0, key=(2, i))
+                    ym = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+                    fm = [lambda c=c, s_=s_: aq.aq_matmul_fp(xm, c, s_, mode, T, y=ym)
+                          for (c, s_) in sets] * 2
+                    usm = _graph_us(torch, stream, fm)
+                    gm = wbytes / (usm * 1e-6) / 1e9
+                    rows[f"{N}x{K}"][f"rows_M{M}"] = {
+                        "avg_us": round(usm, 3), "weight_gbs": round(gm, 1),
+                        "pct_hbm": round(100 * gm / HBM_PEAK_GBS, 1),
+                        "frac_of_read_ceiling": round(ceil_us / usm, 3)}
+                    print(f"# {mode} M={M} bf16 {N}x{K}: {usm:.2f} us, {gm:.0f} GB/s weights, "
+                          f"{ceil_us / usm:.2f} of the plain read", file=sys.stderr, flush=True)
             if legs is not None and f"{mode}_decode" not in legs:
                 # the oracle on the first matrix: exact dequantize, then the product
                 import oracle

@@ -22,7 +22,7 @@ __all__ = [
     "aq_qweight_bytes", "aq_quantize", "aq_quantize_mse", "aq_quantize_zp", "aq_dequantize",
     "aq_embedding", "aq_qmv", "aq_qmm",
     "aq_quantized_matmul", "aq_gather_qmv", "aq_gather_qmm", "aq_gather_quantized_matmul",
-    "aq_quantize_fp", "aq_dequantize_fp", "aq_qmv_fp", "aq_qmv_fp_describe", "FP_MODES",
+    "aq_quantize_fp", "aq_dequantize_fp", "aq_qmv_fp", "aq_matmul_fp", "aq_qmv_fp_describe", "FP_MODES",
 ]
 
 AQ_OK = 0
@@ -80,6 +80,7 @@ def load_library():
         "aq_quantize_fp": ([vp, i32, i64, i64, i32, i32, vp, vp, vp], i32),
         "aq_dequantize_fp": ([vp, vp, i64, i64, i32, i32, vp, i32, vp], i32),
         "aq_qmv_fp": ([vp, i32, vp, vp, i64, i64, i32, i32, vp, vp], i32),
+        "aq_matmul_fp": ([vp, i32, i64, vp, vp, i64, i64, i32, i32, vp, vp], i32),
         "aq_qmv_fp_describe": ([i64, i64, i32, i32, ctypes.c_char_p, i32], i32),
         "aq_bench_stream_read": ([vp, i64, i32, i32, vp, vp], i32),
         "aq_bench_read_oneshot": ([vp, i64, i32, i32, vp, vp], i32),
@@ -407,6 +408,23 @@ def aq_qmv_fp(x, codes, scales, mode: str, tensor_exp: int = 0, y=None, stream=N
     st = lib.aq_qmv_fp(_dev(x, "x"), _dtype_code(x), _dev(codes, "codes"), _dev(scales, "scales"),
                        N, K, FP_MODES[mode][0], tensor_exp, _dev(y, "y"), _stream(stream))
     _check(st, "aq_qmv_fp")
+    return y
+
+
+def aq_matmul_fp(x, codes, scales, mode: str, tensor_exp: int = 0, y=None, stream=None):
+    """y = x @ W^T for x [M, K] (fp16/bf16, device) and block-scaled W [N, K]."""
+    torch = _torch()
+    lib = load_library()
+    M, K = (1, x.shape[-1]) if x.dim() == 1 else (x.shape[0], x.shape[1])
+    if x.dim() > 2:
+        raise ValueError("aq_matmul_fp takes x as [K] or [M, K]")
+    N = codes.shape[0]
+    if y is None:
+        y = torch.empty(tuple(x.shape[:-1]) + (N,), dtype=x.dtype, device=x.device)
+    st = lib.aq_matmul_fp(_dev(x, "x"), _dtype_code(x), M, _dev(codes, "codes"),
+                          _dev(scales, "scales"), N, K, FP_MODES[mode][0], tensor_exp,
+                          _dev(y, "y"), _stream(stream))
+    _check(st, "aq_matmul_fp")
     return y
 
 

@@ -351,6 +351,24 @@ aq_status aq_qmv_fp(const void *x, aq_dtype x_dtype, const uint32_t *codes,
                                     y, static_cast<hipStream_t>(stream)));
 }
 
+aq_status aq_matmul_fp(const void *x, aq_dtype x_dtype, int64_t M, const uint32_t *codes,
+                       const uint8_t *scales, int64_t N, int64_t K, aq_fp_mode mode,
+                       int tensor_exp, void *y, void *stream) {
+  if (M < 1) return AQ_ERR_INVALID_ARG;
+  if (M == 1) return aq_qmv_fp(x, x_dtype, codes, scales, N, K, mode, tensor_exp, y, stream);
+  if (!valid_fp(N, K, (int)mode, tensor_exp) || !valid_act_dtype(x_dtype))
+    return AQ_ERR_INVALID_ARG;
+  if (!x || !codes || !scales || !y) return AQ_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !aligned16(y))
+    return AQ_ERR_ALIGNMENT;
+  // 32-code chunks; 16 rows of x per grid slice (at most 65535 slices); the
+  // scale array addressed with 32-bit byte offsets
+  if (K % 32 != 0 || K > aq::kFpMaxK || M > 16 * 65535) return AQ_ERR_UNSUPPORTED;
+  if (N * (K / (mode == AQ_NVFP4 ? 16 : 32)) > 0x7FFFFFF0) return AQ_ERR_UNSUPPORTED;
+  return from_hip(aq::launch_mm_fp_rows(x, (int)x_dtype, M, codes, scales, N, K, (int)mode,
+                                        tensor_exp, y, static_cast<hipStream_t>(stream)));
+}
+
 int aq_qmv_fp_describe(int64_t N, int64_t K, aq_fp_mode mode, aq_dtype x_dtype, char *buf,
                        int len) {
   if (!valid_fp(N, K, (int)mode, 0)) return -1;

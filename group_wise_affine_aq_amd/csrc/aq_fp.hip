@@ -619,6 +619,236 @@ __global__ __launch_bounds__(64 * W) void qmv1_fp_lds_kernel(const uint16_t *__r
   }
 }
 
+// ---- products for 2 and more rows of x, on the matrix cores ---------------------------
+//
+// y[m, n] = sum_k x[m, k] * w^[n, k] for slices of up to 16 rows of x (the
+// QMV of "Quantization", metalworking MLX notes, at the widths of its
+// dispatch section: several rows of x per pass over W, as in speculative
+// decoding).  v_mfma_f32_16x16x32_{f16,bf16}: A = 16 rows of x (rows past M
+// read as zero), B = 16 rows of W over one 32-code chunk, its codes
+// converted with scale 1 (E2M1 and E4M3 values are exact in fp16 and
+// bf16).  An mx group is one chunk, so each MFMA's result is the group's
+// sum, scaled once by its 2^X into the binary32 accumulators; nvfp4's chunk
+// holds two 16-code groups, so it takes two MFMAs against x masked to each
+// group's half of the chunk, and the matrix's 2^T is applied to the sums.
+//  * Loads: lane (n16 = l % 16, quarter h = l / 16) of block b reads chunk
+//    c0 + h of W row 16 b + n16 (16 bytes; fp8 32), and a 4x4 transpose of
+//    (quarter, word) gives quarter h word h of every chunk of the step (fp8:
+//    words 2h and 2h + 1): codes 8h .. 8h + 7 of chunk c0 + j, the B operand
+//    of MFMA j.  x comes straight from global memory (it stays in L2), one
+//    16-byte load per lane and chunk (codes 8h .. 8h + 7 of x row n16, the A
+//    operand), shared by the R blocks; scales, two dword loads (nvfp4:
+//    three) per row and step from the dword boundary below the step's first
+//    scale byte.
+//  * Workgroup: R blocks of 16 rows of W, K split over W waves in steps of
+//    4 chunks, D steps of loads in flight per wave; chunks past K read as
+//    zero through out-of-range buffer offsets; the waves' partial sums meet
+//    in LDS.
+constexpr uint32_t kFpOutside = 0x80000000u;  // a buffer offset past every resource
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t fp_rsrc(const void *base, int64_t bytes) {
+  const int n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (bytes < 0 ? 0 : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, n, 0x00020000);
+}
+
+typedef float fp_f4 __attribute__((ext_vector_type(4)));
+typedef _Float16 fp_h8 __attribute__((ext_vector_type(8)));
+typedef __bf16 fp_b8 __attribute__((ext_vector_type(8)));
+
+template <typename XT>
+__device__ __forceinline__ fp_f4 mfma_x16(fp_u4 a, fp_u4 b) {
+  const fp_f4 z = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (std::is_same<XT, bf16_t>::value)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(fp_b8, a),
+                                                   __builtin_bit_cast(fp_b8, b), z, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(fp_h8, a),
+                                                  __builtin_bit_cast(fp_h8, b), z, 0, 0, 0);
+}
+
+// 4x4 transpose of (lane quarter, word): afterwards quarter h holds in r[j]
+// what quarter j held in r[h]
+__device__ __forceinline__ void quarter_transpose(uint32_t (&r)[4]) {
+  auto a = __builtin_amdgcn_permlane32_swap(r[0], r[2], false, false);
+  r[0] = a[0]; r[2] = a[1];
+  auto b = __builtin_amdgcn_permlane32_swap(r[1], r[3], false, false);
+  r[1] = b[0]; r[3] = b[1];
+  auto c = __builtin_amdgcn_permlane16_swap(r[0], r[1], false, false);
+  r[0] = c[0]; r[1] = c[1];
+  auto d = __builtin_amdgcn_permlane16_swap(r[2], r[3], false, false);
+  r[2] = d[0]; r[3] = d[1];
+}
+
+// 8 consecutive codes (fp4: one word; fp8: two) -> their exact values as 4
+// packed pairs in the activation type, natural order
+template <int MODE, typename XT>
+__device__ __forceinline__ fp_u4 codes_to_b(uint32_t w0, uint32_t w1) {
+  fp_u4 b;
+  if constexpr (MODE == FP_MXFP8) {
+    if constexpr (std::is_same<XT, bf16_t>::value) {
+      b[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+      b[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+      b[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+      b[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+    } else {
+      b[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false));
+      b[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true));
+      b[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false));
+      b[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true));
+    }
+  } else {
+    (void)w1;
+    if constexpr (std::is_same<XT, bf16_t>::value) {
+      b[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w0, 1.0f, 0));
+      b[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w0, 1.0f, 1));
+      b[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w0, 1.0f, 2));
+      b[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w0, 1.0f, 3));
+    } else {
+      b[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 0));
+      b[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 1));
+      b[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 2));
+      b[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w0, 1.0f, 3));
+    }
+  }
+  return b;
+}
+
+template <int MODE, typename XT, int W, int R, int D>
+__global__ __launch_bounds__(64 * W) void mm_fp_rows_kernel(const uint16_t *__restrict__ x,
+                                                            int64_t M,
+                                                            const uint32_t *__restrict__ codes,
+                                                            const uint8_t *__restrict__ scales,
+                                                            int64_t N, int64_t K, int T,
+                                                            uint16_t *__restrict__ y) {
+  using CF = chunk_fmt<MODE>;
+  constexpr int CB = 16 * CF::VW;      // code bytes per chunk and row
+  constexpr int NSW = CF::SB + 1;      // scale dwords loaded per row and step
+  __shared__ __attribute__((aligned(16))) float part[W][R][16][16];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n16 = lane & 15, h = lane >> 4;
+  const int nch = (int)(K >> 5);
+  const int nsteps = (nch + 3) >> 2;
+  const int spw = (nsteps + W - 1) / W;
+  const int s0 = wave * spw, s1 = s0 + spw < nsteps ? s0 + spw : nsteps;
+  const int64_t row0 = (int64_t)blockIdx.x * 16 * R;
+  const int64_t rows = N - row0 < 16 * R ? N - row0 : 16 * R;
+  const int64_t m0 = (int64_t)blockIdx.y * 16;
+  const int64_t mrows = M - m0 < 16 ? M - m0 : 16;
+  int64_t rcb, rsb;
+  row_bytes<MODE>(K, rcb, rsb);
+  const __amdgpu_buffer_rsrc_t rc =
+      fp_rsrc(reinterpret_cast<const uint8_t *>(codes) + row0 * rcb, rows * rcb);
+  // scales: the whole array, in whole dwords (it starts 16-byte aligned, so
+  // the dword holding its last byte lies inside its allocation)
+  const __amdgpu_buffer_rsrc_t rs = fp_rsrc(scales, (N * rsb + 3) & ~(int64_t)3);
+  const __amdgpu_buffer_rsrc_t rx = fp_rsrc(x + m0 * K, mrows * K * 2);
+
+  struct Step {
+    uint32_t cw[R][4 * CF::VW];  // chunk c0 + h of row 16 b + n16, as loaded
+    uint32_t sc[R][NSW];         // dwords holding the row's scale bytes of the step
+    fp_u4 xl[4];                 // codes 8h .. 8h + 7 of chunk c0 + j of x row n16
+  };
+  auto load = [&](Step &st, int s) {
+    const bool in = s < s1;  // uniform; past the range every offset lies outside
+    const int c0 = 4 * s;
+#pragma unroll
+    for (int b = 0; b < R; ++b) {
+      const int r = 16 * b + n16, c = c0 + h;
+      const uint32_t off = in && c < nch ? (uint32_t)(r * rcb + (int64_t)c * CB) : kFpOutside;
+#pragma unroll
+      for (int v = 0; v < CF::VW; ++v) {
+        const fp_u4 t = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(off + 16u * v), 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.cw[b][4 * v + i] = t[i];
+      }
+      const uint32_t so = (uint32_t)((row0 + r) * rsb + (int64_t)c0 * CF::SB);
+      const uint32_t sa = in ? (so & ~3u) : kFpOutside;
+#pragma unroll
+      for (int i = 0; i < NSW; ++i)
+        st.sc[b][i] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(sa + 4u * i), 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = c0 + j;
+      const uint32_t off =
+          in && c < nch ? (uint32_t)(n16 * K * 2 + ((int64_t)c * 32 + 8 * h) * 2) : kFpOutside;
+      st.xl[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0);
+    }
+  };
+
+  fp_f4 acc[R];
+#pragma unroll
+  for (int b = 0; b < R; ++b) acc[b] = fp_f4{0.f, 0.f, 0.f, 0.f};
+  const fp_u4 zero4 = {0u, 0u, 0u, 0u};
+  auto compute = [&](const Step &st, int s) {
+    const int c0 = 4 * s;
+#pragma unroll
+    for (int b = 0; b < R; ++b) {
+      uint32_t e[4], o[4];  // fp4: word h of each chunk; fp8: words 2h and 2h + 1
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        e[i] = st.cw[b][CF::VW * i];
+        o[i] = CF::VW == 2 ? st.cw[b][2 * i + 1] : 0u;
+      }
+      quarter_transpose(e);
+      if constexpr (CF::VW == 2) quarter_transpose(o);
+      // the row's scale bytes of chunks c0 .. c0 + 3 (SB each), from the
+      // dwords loaded at the dword boundary below them
+      const uint32_t sh = (uint32_t)((row0 + 16 * b + n16) * rsb) & 3u;
+      const uint32_t sl = __builtin_amdgcn_alignbyte(st.sc[b][1], st.sc[b][0], sh);
+      const uint32_t sh2 = CF::SB == 2 ? __builtin_amdgcn_alignbyte(st.sc[b][NSW - 1], st.sc[b][1], sh)
+                                       : 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool live = c0 + j < nch;  // uniform: chunks past K contribute nothing
+        const fp_u4 bw = codes_to_b<MODE, XT>(e[j], o[j]);
+        if constexpr (MODE == FP_NVFP4) {
+          // the two E4M3 scales of the chunk (its groups 0 and 1) through one
+          // convert (exact in fp16); x masked to each group's 16 codes
+          const uint32_t sw = j < 2 ? sl : sh2;
+          const fp_h2 g = (j & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, true)
+                                  : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
+          const fp_u4 xa = h < 2 ? st.xl[j] : zero4, xb = h < 2 ? zero4 : st.xl[j];
+          const fp_f4 t0 = mfma_x16<XT>(xa, bw), t1 = mfma_x16<XT>(xb, bw);
+          const float g0 = live ? (float)g[0] : 0.f, g1 = live ? (float)g[1] : 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[b][i] = __builtin_fmaf(t1[i], g1, __builtin_fmaf(t0[i], g0, acc[b][i]));
+        } else {
+          const float g = live ? __builtin_ldexpf(1.0f, (int)((sl >> (8 * j)) & 0xFFu) - 127) : 0.f;
+          const fp_f4 t = mfma_x16<XT>(st.xl[j], bw);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[b][i] = __builtin_fmaf(t[i], g, acc[b][i]);
+        }
+      }
+    }
+  };
+
+  Step st[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) load(st[d], s0 + d);
+  for (int s = s0; s < s1; s += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (s + d < s1) compute(st[d], s + d);
+      load(st[d], s + d + D);
+    }
+  }
+  // lane (n16, h) holds x rows 4h .. 4h + 3 of W row 16 b + n16
+#pragma unroll
+  for (int b = 0; b < R; ++b)
+    *reinterpret_cast<fp_f4 *>(&part[wave][b][n16][4 * h]) = acc[b];
+  __syncthreads();
+  for (int t = threadIdx.x; t < R * 256; t += 64 * W) {
+    const int b = t >> 8, m = (t >> 4) & 15, nn = t & 15;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) v += part[w][b][nn][m];
+    if constexpr (MODE == FP_NVFP4) v = __builtin_ldexpf(v, T);
+    const int64_t n = row0 + 16 * b + nn;
+    if (m < mrows && n < N) y[(m0 + m) * N + n] = xtraits<XT>::from_f32(v);
+  }
+}
+
 template <typename KernelT>
 int resident_blocks(KernelT kern, int threads, size_t lds) {
   int v = 0;
@@ -695,6 +925,55 @@ hipError_t qmv_fp_mode(const void *x, int x_dtype, const uint32_t *codes, const 
                        int64_t N, int64_t K, int T, void *y, hipStream_t s) {
   if (x_dtype == X_F16) return qmv_fp_dispatch<MODE, f16_t>(x, codes, scales, N, K, T, y, s);
   if (x_dtype == X_BF16) return qmv_fp_dispatch<MODE, bf16_t>(x, codes, scales, N, K, T, y, s);
+  return hipErrorInvalidValue;
+}
+
+// 2+ rows of x: workgroups of R blocks of 16 rows of W per slice of 16 x
+// rows (R = 2, or 1 when that leaves compute units without a workgroup),
+// and the steps of 4 chunks split over 2, 4 or 8 waves so that the launch
+// holds about four waves per SIMD, each wave with at least 4 steps (16-wave
+// workgroups would cap a wave at 128 registers: nvfp4 then spills); D steps
+// of loads in flight per wave
+template <int MODE> constexpr int kFewDepth = 2;
+
+template <int MODE, typename XT, int R>
+hipError_t mm_fp_rows_r(const void *x, int64_t M, const uint32_t *codes, const uint8_t *scales,
+                        int64_t N, int64_t K, int T, void *y, hipStream_t s) {
+  constexpr int D = kFewDepth<MODE>;
+  const int64_t blocks = (N + 16 * R - 1) / (16 * R), slices = (M + 15) / 16;
+  if (blocks > 0x7FFFFFFF || slices > 65535) return hipErrorInvalidValue;
+  const int64_t steps = (K / 32 + 3) / 4, wgs = blocks * slices;
+  const int64_t target = 4 * 4 * (int64_t)device_cus();
+  int w = wgs * 2 >= target ? 2 : wgs * 4 >= target ? 4 : 8;
+  while (w > 2 && steps < 4 * w) w /= 2;
+  const dim3 grid((unsigned)blocks, (unsigned)slices);
+#define AQ_MMFP(WW)                                                                           \
+  hipLaunchKernelGGL((mm_fp_rows_kernel<MODE, XT, WW, R, D>), grid, dim3(64 * WW), 0, s,      \
+                     (const uint16_t *)x, M, codes, scales, N, K, T, (uint16_t *)y);          \
+  break;
+  switch (w) {
+    case 2: AQ_MMFP(2)
+    case 4: AQ_MMFP(4)
+    default: AQ_MMFP(8)
+  }
+#undef AQ_MMFP
+  return hipGetLastError();
+}
+
+template <int MODE, typename XT>
+hipError_t mm_fp_rows_mode(const void *x, int64_t M, const uint32_t *codes, const uint8_t *scales,
+                           int64_t N, int64_t K, int T, void *y, hipStream_t s) {
+  if ((N + 31) / 32 * ((M + 15) / 16) >= device_cus())
+    return mm_fp_rows_r<MODE, XT, 2>(x, M, codes, scales, N, K, T, y, s);
+  return mm_fp_rows_r<MODE, XT, 1>(x, M, codes, scales, N, K, T, y, s);
+}
+
+template <int MODE>
+hipError_t mm_fp_rows_dtype(const void *x, int x_dtype, int64_t M, const uint32_t *codes,
+                            const uint8_t *scales, int64_t N, int64_t K, int T, void *y,
+                            hipStream_t s) {
+  if (x_dtype == X_F16) return mm_fp_rows_mode<MODE, f16_t>(x, M, codes, scales, N, K, T, y, s);
+  if (x_dtype == X_BF16) return mm_fp_rows_mode<MODE, bf16_t>(x, M, codes, scales, N, K, T, y, s);
   return hipErrorInvalidValue;
 }
 
@@ -795,6 +1074,17 @@ hipError_t launch_qmv_fp(const void *x, int x_dtype, const uint32_t *codes, cons
     case FP_MXFP4: return qmv_fp_mode<FP_MXFP4>(x, x_dtype, codes, scales, N, K, T, y, s);
     case FP_NVFP4: return qmv_fp_mode<FP_NVFP4>(x, x_dtype, codes, scales, N, K, T, y, s);
     case FP_MXFP8: return qmv_fp_mode<FP_MXFP8>(x, x_dtype, codes, scales, N, K, T, y, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_mm_fp_rows(const void *x, int x_dtype, int64_t M, const uint32_t *codes,
+                             const uint8_t *scales, int64_t N, int64_t K, int mode, int T, void *y,
+                             hipStream_t s) {
+  switch (mode) {
+    case FP_MXFP4: return mm_fp_rows_dtype<FP_MXFP4>(x, x_dtype, M, codes, scales, N, K, T, y, s);
+    case FP_NVFP4: return mm_fp_rows_dtype<FP_NVFP4>(x, x_dtype, M, codes, scales, N, K, T, y, s);
+    case FP_MXFP8: return mm_fp_rows_dtype<FP_MXFP8>(x, x_dtype, M, codes, scales, N, K, T, y, s);
   }
   return hipErrorInvalidValue;
 }

@@ -93,5 +93,9 @@ hipError_t launch_dequantize_fp(const uint32_t *codes, const uint8_t *scales, in
 void qmv1_fp_shape(int64_t N, int64_t K, int mode, int &cpl, int &ud, int &w, int &wpc);
 hipError_t launch_qmv_fp(const void *x, int x_dtype, const uint32_t *codes, const uint8_t *scales,
                          int64_t N, int64_t K, int mode, int T, void *y, hipStream_t s);
+// y = x @ W^T for M >= 2 rows of x (slices of 16) and block-scaled W
+hipError_t launch_mm_fp_rows(const void *x, int x_dtype, int64_t M, const uint32_t *codes,
+                             const uint8_t *scales, int64_t N, int64_t K, int mode, int T, void *y,
+                             hipStream_t s);
 
 }  // namespace aq

@@ -328,6 +328,21 @@ aq_status aq_qmv_fp(const void *x, aq_dtype x_dtype, const uint32_t *codes,
                     const uint8_t *scales, int64_t N, int64_t K, aq_fp_mode mode, int tensor_exp,
                     void *y, void *stream);
 
+/* The product for M rows of x ("Quantization", metalworking, QMV bullet and
+ * its dispatch section on several rows of x per pass over W, as in
+ * speculative decoding): y[m, n] = sum_k x[m, k] * w^[n, k].  x: device
+ * [M, K] row-major in x_dtype (AQ_F16 or AQ_BF16); y: device [M, N] in
+ * x_dtype.  M = 1 is aq_qmv_fp.  M >= 2 runs on the matrix cores in slices
+ * of 16 rows of x, each slice one pass over W: per 32-code chunk the exact
+ * code values times x, summed in binary32 per group and scaled once per
+ * group (nvfp4: 2^T applied to the sums); y is rounded to nearest even.
+ * Arguments as aq_qmv_fp (the same K limits; AQ_ERR_INVALID_ARG for
+ * M < 1, AQ_ERR_UNSUPPORTED past M = 16 * 65535 or past 2^31 - 16 scale
+ * bytes). */
+aq_status aq_matmul_fp(const void *x, aq_dtype x_dtype, int64_t M, const uint32_t *codes,
+                       const uint8_t *scales, int64_t N, int64_t K, aq_fp_mode mode,
+                       int tensor_exp, void *y, void *stream);
+
 /* Which kernel aq_qmv_fp launches for this shape and mode, as text (as
  * aq_qmv_describe does); -1 for arguments aq_qmv_fp would reject. */
 int aq_qmv_fp_describe(int64_t N, int64_t K, aq_fp_mode mode, aq_dtype x_dtype, char *buf,

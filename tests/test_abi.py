@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("aq_quantize", "aq_quantize_mse", "aq_dequantize", "aq_qmv", "aq_qmm", "aq_gather_qmv",
               "aq_quantized_matmul", "aq_codes_words", "aq_qweight_bytes", "aq_status_string",
-              "aq_quantize_fp", "aq_dequantize_fp", "aq_qmv_fp"):
+              "aq_quantize_fp", "aq_dequantize_fp", "aq_qmv_fp", "aq_matmul_fp"):
         assert n in names
 
 
@@ -266,6 +266,24 @@ def test_fp_mode_argument_errors(lib):
     assert m(x=MIS) == ALIGN
     assert m(K=49152 + 32) == UNSUPPORTED
     assert m(mode=NV4, K=48) == UNSUPPORTED  # a whole group, not a whole 32-code chunk
+    mm = lambda **k: lib.aq_matmul_fp(k.get("x", P), k.get("dt", F16), k.get("M", 4),
+                                      k.get("codes", P), k.get("scales", P), k.get("N", 4),
+                                      k.get("K", 64), k.get("mode", MX4), k.get("T", 0),
+                                      k.get("y", P), None)
+    assert mm(M=0) == INVALID
+    assert mm(M=-3) == INVALID
+    assert mm(dt=F32) == INVALID
+    assert mm(K=33) == INVALID
+    assert mm(N=0) == INVALID
+    assert mm(y=None) == INVALID
+    assert mm(codes=None) == INVALID
+    assert mm(mode=MX4, T=2) == INVALID
+    assert mm(scales=MIS) == ALIGN
+    assert mm(x=MIS) == ALIGN
+    assert mm(K=49152 + 32) == UNSUPPORTED
+    assert mm(mode=NV4, K=48) == UNSUPPORTED
+    assert mm(M=16 * 65535 + 1) == UNSUPPORTED
+    assert mm(M=1, K=33) == INVALID       # one row: the decode product's checks
     buf = ctypes.create_string_buffer(96)
     assert lib.aq_qmv_fp_describe(4096, 49152 + 32, MX4, F16, buf, 96) == -1
     assert lib.aq_qmv_fp_describe(4096, 100, MX4, F16, buf, 96) == -1

@@ -243,6 +243,73 @@ def test_qmv_fp_special_groups(aq, mode):
         _qmv_check(aq, mode, w.shape[0], w.shape[1], "f16", seed=67, w=w, T=T)
 
 
+# ---- products for 2 and more rows of x (matrix cores) --------------------------------
+def _mm_check(aq, mode, M, N, K, xdt, seed, w=None, T=None):
+    if w is None:
+        w = inputs.weights(N, K, seed=seed, key=(N, K), outliers=True)
+    if T is None:
+        T = _tensor_exp(w, mode)
+    c, s = _oracle_quantize(w, mode, T)
+    xb = inputs.activations(M, K, xdt, seed=seed, key=(M, N, K))
+    y_ref, A = oracle.matmul_dense(inputs.from_bits(xb, xdt), _oracle_exact(c, s, K, mode, T))
+    y = aq.aq_matmul_fp(bits_to_dev(xb, xdt), *_to_dev(c, s), mode, T)
+    assert tuple(y.shape) == (M, N)
+    ok, ratio = oracle.within_tolerance(out_to_f64(y), y_ref, A)
+    assert ok, f"matmul_fp {mode} M{M} N{N} K{K} {xdt} T{T}: worst error/bound = {ratio:.3f}"
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("M", [2, 3, 8, 16, 17, 40])
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+def test_matmul_fp_rows(aq, mode, M, xdt):
+    """M rows of x in slices of 16 (17 and 40: a partial last slice); N not a
+    multiple of the 32-row workgroup; K = 2080: 65 chunks, a partial last
+    step of 4 chunks."""
+    _mm_check(aq, mode, M, 100, 2080, xdt, seed=70)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("N,K", [(1, 32), (5, 96), (33, 160), (64, 4096), (257, 12288),
+                                 (70, 49152)])
+def test_matmul_fp_shapes(aq, mode, N, K):
+    """One chunk, fewer chunks than a step, a row per workgroup block, the
+    wave counts of the launch (2..8 waves splitting K) and the largest K."""
+    _mm_check(aq, mode, 4, N, K, "f16", seed=71)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("N,K,M", [(14336, 4096, 4), (4096, 14336, 8)])
+def test_matmul_fp_decode_shapes(aq, mode, N, K, M):
+    """The speculative-decoding widths on the decode matrices."""
+    _mm_check(aq, mode, M, N, K, "bf16", seed=72)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_matmul_fp_special_groups(aq, mode):
+    """Groups of zeros, subnormal and clamped exponents, ties and saturated
+    members (as for M = 1); nvfp4 also without a tensor scale."""
+    w = _special_rows()
+    w = w[np.abs(w).max(axis=1) < 1e4]
+    w = np.ascontiguousarray(np.tile(w.reshape(1, -1), (5, 3)))
+    for T in ((None, 0) if mode == "nvfp4" else (None,)):
+        _mm_check(aq, mode, 5, w.shape[0], w.shape[1], "f16", seed=73, w=w, T=T)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_matmul_fp_one_row_is_qmv(aq, mode):
+    """M = 1 goes to the decode product: the same bits as aq_qmv_fp."""
+    import torch
+    N, K = 300, 4096
+    w = inputs.weights(N, K, seed=74, key=(N, K))
+    T = _tensor_exp(w, mode)
+    c, s = _oracle_quantize(w, mode, T)
+    x = bits_to_dev(inputs.activations(1, K, "f16", seed=74, key=(N, K)), "f16")
+    a = aq.aq_matmul_fp(x, *_to_dev(c, s), mode, T)
+    b = aq.aq_qmv_fp(x, *_to_dev(c, s), mode, T)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
 # ---- the prefill-size matrix ----------------------------------------------------------
 @pytest.fixture(scope="module")
 def prefill_weights():
