@@ -682,7 +682,8 @@ def _fp_modes(aq, inputs, dev, stream, legs=None):
     matrix."""
     import torch
     out = {"workload": "decode M=1, W [4096,4096] [1024,4096] [14336,4096] [4096,14336], "
-                       "fp16 x, cold weights; M=4, 8 bf16 x on the two 33 MB matrices; "
+                       "fp16 x, cold weights; M=4, 8 bf16 x on the two 33 MB matrices; the MoE "
+                       "gather workload with block-scaled experts; "
                        "quantize / dequantize W [28672,8192] fp32 <-> bf16"}
     ceilings = {}
     for mode, (_, grp, bits) in aq.FP_MODES.items():
@@ -765,6 +766,7 @@ def _fp_modes(aq, inputs, dev, stream, legs=None):
         res["dequantize_bf16"] = {"avg_us": round(us, 2), "bytes": nb,
                                   "gbs": round(nb / (us * 1e-6) / 1e9, 1),
                                   "pct_hbm": round(100 * nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
+        res["moe"] = _fp_moe(aq, inputs, dev, stream, mode, grp, bits)
         print(f"# {mode} step {total_us:.2f} us ({res['step_weight_gbs']} GB/s); quantize "
               f"{res['quantize']['avg_us']:.1f} us ({res['quantize']['gbs']} GB/s), dequantize "
               f"{res['dequantize_bf16']['avg_us']:.1f} us ({res['dequantize_bf16']['gbs']} GB/s)",
@@ -773,6 +775,45 @@ def _fp_modes(aq, inputs, dev, stream, legs=None):
         del w, c, s_, deq
         torch.cuda.synchronize()
     return out
+
+
+def _fp_moe(aq, inputs, dev, stream, mode, grp, bits):
+    """The MoE decode workload (32 tokens x top-6 of 64 experts [1408, 2048],
+    the same seeded weights and ids as the affine gather) with the experts in a
+    block-scaled mode: aq_gather_matmul_fp, cold copies of the expert stack."""
+    import numpy as np
+    import torch
+    cfg = inputs.WORKLOADS["moe"]
+    wid = inputs.WORKLOAD_ID["moe"]
+    (N, K), E, T, topk = cfg["shapes"][0], cfg["experts"], cfg["tokens"], cfg["topk"]
+    amax = max(float(inputs.weights_device(N, K, device=dev, seed=0, key=(wid, e)).abs().max())
+               for e in range(E))
+    Te = 0 if mode != "nvfp4" or amax == 0 else max(-100, min(100, math.ceil(math.log2(amax / 2688))))
+    parts = [aq.aq_quantize_fp(inputs.weights_device(N, K, device=dev, seed=0, key=(wid, e)),
+                               mode, Te) for e in range(E)]
+    packed = tuple(torch.stack([p[i] for p in parts]) for i in range(2))
+    del parts
+    ids_np = inputs.expert_ids(T, E, topk, seed=0, key=(wid,))
+    ids = torch.from_numpy(ids_np).to(dev)
+    x = inputs.activations_device(T, K, "f16", device=dev, seed=0, key=(wid,))
+    y = torch.empty((T, topk, N), dtype=torch.float16, device=dev)
+    ebytes = N * K * bits // 8 + N * K // grp
+    copies = max(2, math.ceil(COLD_BYTES / (E * ebytes)))
+    sets = [packed] + [tuple(t.clone() for t in packed) for _ in range(copies - 1)]
+    fs = [lambda c=c, s_=s_: aq.aq_gather_matmul_fp(x, c, s_, ids, mode, Te, y=y)
+          for (c, s_) in sets]
+    us = _graph_us(torch, stream, fs)
+    used = len(np.unique(ids_np))
+    algo = used * ebytes + T * K * 2 + T * topk * N * 2 + T * topk * 4
+    gbs = algo / (us * 1e-6) / 1e9
+    print(f"# {mode} MoE gather ({used} of {E} experts used): {us:.2f} us, {gbs:.0f} GB/s "
+          "algorithmic", file=sys.stderr, flush=True)
+    del sets, packed
+    torch.cuda.synchronize()
+    return {"workload": f"{E} experts [{N},{K}] {mode}, x fp16 [{T},{K}], ids [{T},{topk}], "
+                        "cold weights",
+            "experts_used": used, "algo_bytes": algo, "avg_us": round(us, 3),
+            "gbs": round(gbs, 1), "pct_hbm": round(100 * gbs / HBM_PEAK_GBS, 1)}
 
 
 def _embedding(aq, inputs, dev, stream):

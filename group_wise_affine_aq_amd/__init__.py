@@ -22,7 +22,8 @@ __all__ = [
     "aq_qweight_bytes", "aq_quantize", "aq_quantize_mse", "aq_quantize_zp", "aq_dequantize",
     "aq_embedding", "aq_qmv", "aq_qmm",
     "aq_quantized_matmul", "aq_gather_qmv", "aq_gather_qmm", "aq_gather_quantized_matmul",
-    "aq_quantize_fp", "aq_dequantize_fp", "aq_qmv_fp", "aq_matmul_fp", "aq_qmv_fp_describe", "FP_MODES",
+    "aq_quantize_fp", "aq_dequantize_fp", "aq_qmv_fp", "aq_matmul_fp", "aq_gather_matmul_fp", "aq_qmv_fp_describe",
+    "FP_MODES",
 ]
 
 AQ_OK = 0
@@ -81,6 +82,8 @@ def load_library():
         "aq_dequantize_fp": ([vp, vp, i64, i64, i32, i32, vp, i32, vp], i32),
         "aq_qmv_fp": ([vp, i32, vp, vp, i64, i64, i32, i32, vp, vp], i32),
         "aq_matmul_fp": ([vp, i32, i64, vp, vp, i64, i64, i32, i32, vp, vp], i32),
+        "aq_gather_matmul_fp": ([vp, i32, i64, vp, vp, i64, i64, i64, vp, i32, i32, i32, vp, vp],
+                                i32),
         "aq_qmv_fp_describe": ([i64, i64, i32, i32, ctypes.c_char_p, i32], i32),
         "aq_bench_stream_read": ([vp, i64, i32, i32, vp, vp], i32),
         "aq_bench_read_oneshot": ([vp, i64, i32, i32, vp, vp], i32),
@@ -425,6 +428,25 @@ def aq_matmul_fp(x, codes, scales, mode: str, tensor_exp: int = 0, y=None, strea
                           _dev(scales, "scales"), N, K, FP_MODES[mode][0], tensor_exp,
                           _dev(y, "y"), _stream(stream))
     _check(st, "aq_matmul_fp")
+    return y
+
+
+def aq_gather_matmul_fp(x, codes, scales, ids, mode: str, tensor_exp: int = 0, y=None,
+                        stream=None):
+    """y[t, j] = x[t] @ W_{ids[t, j]}^T: x [T, K] fp16/bf16, block-scaled experts
+    codes [E, N, K*bits/32] (int32), scales [E, N, K/group] (uint8), ids [T, topk]
+    (int32), all on the device; y [T, topk, N] in x's dtype."""
+    torch = _torch()
+    lib = load_library()
+    T, K = x.shape
+    E, N = codes.shape[0], codes.shape[1]
+    topk = ids.shape[1]
+    if y is None:
+        y = torch.empty((T, topk, N), dtype=x.dtype, device=x.device)
+    st = lib.aq_gather_matmul_fp(_dev(x, "x"), _dtype_code(x), T, _dev(codes, "codes"),
+                                 _dev(scales, "scales"), E, N, K, _dev(ids, "ids"), topk,
+                                 FP_MODES[mode][0], tensor_exp, _dev(y, "y"), _stream(stream))
+    _check(st, "aq_gather_matmul_fp")
     return y
 
 

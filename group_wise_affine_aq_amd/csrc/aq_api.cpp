@@ -369,6 +369,26 @@ aq_status aq_matmul_fp(const void *x, aq_dtype x_dtype, int64_t M, const uint32_
                                         tensor_exp, y, static_cast<hipStream_t>(stream)));
 }
 
+aq_status aq_gather_matmul_fp(const void *x, aq_dtype x_dtype, int64_t T, const uint32_t *codes,
+                              const uint8_t *scales, int64_t E, int64_t N, int64_t K,
+                              const int32_t *ids, int topk, aq_fp_mode mode, int tensor_exp,
+                              void *y, void *stream) {
+  if (!valid_fp(N, K, (int)mode, tensor_exp) || !valid_act_dtype(x_dtype) || T < 1 || E < 1 ||
+      topk < 1)
+    return AQ_ERR_INVALID_ARG;
+  if (!x || !codes || !scales || !ids || !y) return AQ_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || !aligned16(ids) ||
+      !aligned16(y))
+    return AQ_ERR_ALIGNMENT;
+  // 32-code chunks; x and the scale array addressed with 32-bit byte offsets
+  if (K % 32 != 0 || K > aq::kFpMaxK || E > 65535 || T * topk > 0x7FFFFFFF ||
+      T * K * 2 > 0x7FFFFFFF || E * N * (K / (mode == AQ_NVFP4 ? 16 : 32)) > 0x7FFFFFF0)
+    return AQ_ERR_UNSUPPORTED;
+  return from_hip(aq::launch_gather_mm_fp(x, (int)x_dtype, T, codes, scales, E, N, K, ids, topk,
+                                          (int)mode, tensor_exp, y,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 int aq_qmv_fp_describe(int64_t N, int64_t K, aq_fp_mode mode, aq_dtype x_dtype, char *buf,
                        int len) {
   if (!valid_fp(N, K, (int)mode, 0)) return -1;

@@ -713,35 +713,28 @@ __device__ __forceinline__ fp_u4 codes_to_b(uint32_t w0, uint32_t w1) {
   return b;
 }
 
+// One pass of a workgroup over its R blocks of 16 rows of W against 16 rows
+// of x: lane (n16, h) gets the byte offset xro of x row n16 in rx
+// (kFpOutside for a missing row: it reads as zero); srow0 is the block's
+// first row in the scale array rs.  Leaves the x rows x W rows sums of the
+// wave's K range in part[wave] (entry [b][n][m] for W row 16 b + n, x row m)
+// and meets the other waves at a barrier; the caller adds the W partial sums.
 template <int MODE, typename XT, int W, int R, int D>
-__global__ __launch_bounds__(64 * W) void mm_fp_rows_kernel(const uint16_t *__restrict__ x,
-                                                            int64_t M,
-                                                            const uint32_t *__restrict__ codes,
-                                                            const uint8_t *__restrict__ scales,
-                                                            int64_t N, int64_t K, int T,
-                                                            uint16_t *__restrict__ y) {
+__device__ __forceinline__ void fp_rows_pass(__amdgpu_buffer_rsrc_t rx, uint32_t xro,
+                                             __amdgpu_buffer_rsrc_t rc,
+                                             __amdgpu_buffer_rsrc_t rs, int64_t srow0,
+                                             int64_t K, float (*part)[R][16][16]) {
   using CF = chunk_fmt<MODE>;
   constexpr int CB = 16 * CF::VW;      // code bytes per chunk and row
   constexpr int NSW = CF::SB + 1;      // scale dwords loaded per row and step
-  __shared__ __attribute__((aligned(16))) float part[W][R][16][16];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n16 = lane & 15, h = lane >> 4;
   const int nch = (int)(K >> 5);
   const int nsteps = (nch + 3) >> 2;
   const int spw = (nsteps + W - 1) / W;
   const int s0 = wave * spw, s1 = s0 + spw < nsteps ? s0 + spw : nsteps;
-  const int64_t row0 = (int64_t)blockIdx.x * 16 * R;
-  const int64_t rows = N - row0 < 16 * R ? N - row0 : 16 * R;
-  const int64_t m0 = (int64_t)blockIdx.y * 16;
-  const int64_t mrows = M - m0 < 16 ? M - m0 : 16;
   int64_t rcb, rsb;
   row_bytes<MODE>(K, rcb, rsb);
-  const __amdgpu_buffer_rsrc_t rc =
-      fp_rsrc(reinterpret_cast<const uint8_t *>(codes) + row0 * rcb, rows * rcb);
-  // scales: the whole array, in whole dwords (it starts 16-byte aligned, so
-  // the dword holding its last byte lies inside its allocation)
-  const __amdgpu_buffer_rsrc_t rs = fp_rsrc(scales, (N * rsb + 3) & ~(int64_t)3);
-  const __amdgpu_buffer_rsrc_t rx = fp_rsrc(x + m0 * K, mrows * K * 2);
 
   struct Step {
     uint32_t cw[R][4 * CF::VW];  // chunk c0 + h of row 16 b + n16, as loaded
@@ -761,7 +754,7 @@ __global__ __launch_bounds__(64 * W) void mm_fp_rows_kernel(const uint16_t *__re
 #pragma unroll
         for (int i = 0; i < 4; ++i) st.cw[b][4 * v + i] = t[i];
       }
-      const uint32_t so = (uint32_t)((row0 + r) * rsb + (int64_t)c0 * CF::SB);
+      const uint32_t so = (uint32_t)((srow0 + r) * rsb + (int64_t)c0 * CF::SB);
       const uint32_t sa = in ? (so & ~3u) : kFpOutside;
 #pragma unroll
       for (int i = 0; i < NSW; ++i)
@@ -771,7 +764,7 @@ __global__ __launch_bounds__(64 * W) void mm_fp_rows_kernel(const uint16_t *__re
     for (int j = 0; j < 4; ++j) {
       const int c = c0 + j;
       const uint32_t off =
-          in && c < nch ? (uint32_t)(n16 * K * 2 + ((int64_t)c * 32 + 8 * h) * 2) : kFpOutside;
+          in && c < nch ? (uint32_t)(xro + ((int64_t)c * 32 + 8 * h) * 2) : kFpOutside;
       st.xl[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0);
     }
   };
@@ -794,7 +787,7 @@ __global__ __launch_bounds__(64 * W) void mm_fp_rows_kernel(const uint16_t *__re
       if constexpr (CF::VW == 2) quarter_transpose(o);
       // the row's scale bytes of chunks c0 .. c0 + 3 (SB each), from the
       // dwords loaded at the dword boundary below them
-      const uint32_t sh = (uint32_t)((row0 + 16 * b + n16) * rsb) & 3u;
+      const uint32_t sh = (uint32_t)((srow0 + 16 * b + n16) * rsb) & 3u;
       const uint32_t sl = __builtin_amdgcn_alignbyte(st.sc[b][1], st.sc[b][0], sh);
       const uint32_t sh2 = CF::SB == 2 ? __builtin_amdgcn_alignbyte(st.sc[b][NSW - 1], st.sc[b][1], sh)
                                        : 0u;
@@ -838,6 +831,31 @@ __global__ __launch_bounds__(64 * W) void mm_fp_rows_kernel(const uint16_t *__re
   for (int b = 0; b < R; ++b)
     *reinterpret_cast<fp_f4 *>(&part[wave][b][n16][4 * h]) = acc[b];
   __syncthreads();
+}
+
+template <int MODE, typename XT, int W, int R, int D>
+__global__ __launch_bounds__(64 * W) void mm_fp_rows_kernel(const uint16_t *__restrict__ x,
+                                                            int64_t M,
+                                                            const uint32_t *__restrict__ codes,
+                                                            const uint8_t *__restrict__ scales,
+                                                            int64_t N, int64_t K, int T,
+                                                            uint16_t *__restrict__ y) {
+  __shared__ __attribute__((aligned(16))) float part[W][R][16][16];
+  const int n16 = threadIdx.x & 15;
+  const int64_t row0 = (int64_t)blockIdx.x * 16 * R;
+  const int64_t rows = N - row0 < 16 * R ? N - row0 : 16 * R;
+  const int64_t m0 = (int64_t)blockIdx.y * 16;
+  const int64_t mrows = M - m0 < 16 ? M - m0 : 16;
+  int64_t rcb, rsb;
+  row_bytes<MODE>(K, rcb, rsb);
+  const __amdgpu_buffer_rsrc_t rc =
+      fp_rsrc(reinterpret_cast<const uint8_t *>(codes) + row0 * rcb, rows * rcb);
+  // scales: the whole array, in whole dwords (it starts 16-byte aligned, so
+  // the dword holding its last byte lies inside its allocation)
+  const __amdgpu_buffer_rsrc_t rs = fp_rsrc(scales, (N * rsb + 3) & ~(int64_t)3);
+  const __amdgpu_buffer_rsrc_t rx = fp_rsrc(x + m0 * K, mrows * K * 2);
+  fp_rows_pass<MODE, XT, W, R, D>(rx, n16 < mrows ? (uint32_t)(n16 * K * 2) : kFpOutside, rc, rs,
+                                  row0, K, part);
   for (int t = threadIdx.x; t < R * 256; t += 64 * W) {
     const int b = t >> 8, m = (t >> 4) & 15, nn = t & 15;
     float v = 0.f;
@@ -846,6 +864,68 @@ __global__ __launch_bounds__(64 * W) void mm_fp_rows_kernel(const uint16_t *__re
     if constexpr (MODE == FP_NVFP4) v = __builtin_ldexpf(v, T);
     const int64_t n = row0 + 16 * b + nn;
     if (m < mrows && n < N) y[(m0 + m) * N + n] = xtraits<XT>::from_f32(v);
+  }
+}
+
+// Mixture-of-experts gather of the block-scaled product ("Quantization",
+// metalworking: gather variants of the kernels for MoE experts):
+// y[t, j, :] = x[t] @ W_{ids[t, j]}^T.  One workgroup per (32 rows, expert
+// e) lists the (token, slot) pairs routed to e, 256 ids at a time, and runs
+// them through fp_rows_pass in batches of 16 (x rows by token, y rows by
+// pair), so each expert's rows are read once per batch of 16 pairs that
+// chose it and experts no pair chose are never read.  Pairs whose id lies
+// outside [0, E) get zero rows, written by the workgroups of expert 0.
+template <int MODE, typename XT, int W, int R, int D>
+__global__ __launch_bounds__(64 * W) void gather_fp_rows_kernel(
+    const uint16_t *__restrict__ x, int64_t Tk, const uint32_t *__restrict__ codes,
+    const uint8_t *__restrict__ scales, int64_t E, int64_t N, int64_t K,
+    const int32_t *__restrict__ ids, int topk, int T, uint16_t *__restrict__ y) {
+  __shared__ __attribute__((aligned(16))) float part[W][R][16][16];
+  __shared__ int list[256];
+  __shared__ int count;
+  const int n16 = threadIdx.x & 15;
+  const int64_t e = blockIdx.y;
+  const int64_t row0 = (int64_t)blockIdx.x * 16 * R;
+  const int64_t rows = N - row0 < 16 * R ? N - row0 : 16 * R;
+  const int64_t total = Tk * topk;
+  int64_t rcb, rsb;
+  row_bytes<MODE>(K, rcb, rsb);
+  if (e == 0)
+    for (int64_t p = threadIdx.x; p < total; p += 64 * W) {
+      const int32_t id = ids[p];
+      if (id < 0 || id >= E)
+        for (int nn = 0; nn < rows; ++nn) y[p * N + row0 + nn] = 0;
+    }
+  const __amdgpu_buffer_rsrc_t rc = fp_rsrc(
+      reinterpret_cast<const uint8_t *>(codes) + (e * N + row0) * rcb, rows * rcb);
+  const __amdgpu_buffer_rsrc_t rs = fp_rsrc(scales, (E * N * rsb + 3) & ~(int64_t)3);
+  const __amdgpu_buffer_rsrc_t rx = fp_rsrc(x, Tk * K * 2);
+  for (int64_t t0 = 0; t0 < total; t0 += 256) {
+    __syncthreads();  // every thread has read the last round's count
+    if (threadIdx.x == 0) count = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < 256; i += 64 * W) {
+      const int64_t p = t0 + i;
+      if (p < total && ids[p] == e) list[atomicAdd(&count, 1)] = i;
+    }
+    __syncthreads();
+    const int n = count;
+    for (int b0 = 0; b0 < n; b0 += 16) {  // uniform
+      const int nb = n - b0 < 16 ? n - b0 : 16;
+      const uint32_t xro = n16 < nb ? (uint32_t)(((t0 + list[b0 + n16]) / topk) * K * 2)
+                                    : kFpOutside;
+      fp_rows_pass<MODE, XT, W, R, D>(rx, xro, rc, rs, e * N + row0, K, part);
+      for (int t = threadIdx.x; t < R * 256; t += 64 * W) {
+        const int b = t >> 8, m = (t >> 4) & 15, nn = t & 15;
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) v += part[w][b][nn][m];
+        if constexpr (MODE == FP_NVFP4) v = __builtin_ldexpf(v, T);
+        const int64_t nr = row0 + 16 * b + nn;
+        if (m < nb && nr < N) y[(t0 + list[b0 + m]) * N + nr] = xtraits<XT>::from_f32(v);
+      }
+      __syncthreads();  // part and list reused
+    }
   }
 }
 
@@ -968,6 +1048,48 @@ hipError_t mm_fp_rows_mode(const void *x, int64_t M, const uint32_t *codes, cons
   return mm_fp_rows_r<MODE, XT, 1>(x, M, codes, scales, N, K, T, y, s);
 }
 
+// gather: workgroups of 32 rows of one expert (16 when that leaves compute
+// units idle), steps split over 2, 4 or 8 waves as above
+template <int MODE, typename XT, int R>
+hipError_t gather_fp_rows_r(const void *x, int64_t Tk, const uint32_t *codes,
+                            const uint8_t *scales, int64_t E, int64_t N, int64_t K,
+                            const int32_t *ids, int topk, int T, void *y, hipStream_t s) {
+  constexpr int D = kFewDepth<MODE>;
+  const int64_t blocks = (N + 16 * R - 1) / (16 * R);
+  if (blocks > 0x7FFFFFFF || E > 65535) return hipErrorInvalidValue;
+  const int64_t steps = (K / 32 + 3) / 4, wgs = blocks * E;
+  const int64_t target = 4 * 4 * (int64_t)device_cus();
+  int w = wgs * 2 >= target ? 2 : wgs * 4 >= target ? 4 : 8;
+  while (w > 2 && steps < 4 * w) w /= 2;
+  const dim3 grid((unsigned)blocks, (unsigned)E);
+#define AQ_GFP(WW)                                                                              \
+  hipLaunchKernelGGL((gather_fp_rows_kernel<MODE, XT, WW, R, D>), grid, dim3(64 * WW), 0, s,    \
+                     (const uint16_t *)x, Tk, codes, scales, E, N, K, ids, topk, T,             \
+                     (uint16_t *)y);                                                            \
+  break;
+  switch (w) {
+    case 2: AQ_GFP(2)
+    case 4: AQ_GFP(4)
+    default: AQ_GFP(8)
+  }
+#undef AQ_GFP
+  return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t gather_fp_rows_dtype(const void *x, int x_dtype, int64_t Tk, const uint32_t *codes,
+                                const uint8_t *scales, int64_t E, int64_t N, int64_t K,
+                                const int32_t *ids, int topk, int T, void *y, hipStream_t s) {
+  const bool two = (N + 31) / 32 * E >= device_cus();
+  if (x_dtype == X_F16)
+    return two ? gather_fp_rows_r<MODE, f16_t, 2>(x, Tk, codes, scales, E, N, K, ids, topk, T, y, s)
+               : gather_fp_rows_r<MODE, f16_t, 1>(x, Tk, codes, scales, E, N, K, ids, topk, T, y, s);
+  if (x_dtype == X_BF16)
+    return two ? gather_fp_rows_r<MODE, bf16_t, 2>(x, Tk, codes, scales, E, N, K, ids, topk, T, y, s)
+               : gather_fp_rows_r<MODE, bf16_t, 1>(x, Tk, codes, scales, E, N, K, ids, topk, T, y, s);
+  return hipErrorInvalidValue;
+}
+
 template <int MODE>
 hipError_t mm_fp_rows_dtype(const void *x, int x_dtype, int64_t M, const uint32_t *codes,
                             const uint8_t *scales, int64_t N, int64_t K, int T, void *y,
@@ -1085,6 +1207,21 @@ hipError_t launch_mm_fp_rows(const void *x, int x_dtype, int64_t M, const uint32
     case FP_MXFP4: return mm_fp_rows_dtype<FP_MXFP4>(x, x_dtype, M, codes, scales, N, K, T, y, s);
     case FP_NVFP4: return mm_fp_rows_dtype<FP_NVFP4>(x, x_dtype, M, codes, scales, N, K, T, y, s);
     case FP_MXFP8: return mm_fp_rows_dtype<FP_MXFP8>(x, x_dtype, M, codes, scales, N, K, T, y, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gather_mm_fp(const void *x, int x_dtype, int64_t Tk, const uint32_t *codes,
+                               const uint8_t *scales, int64_t E, int64_t N, int64_t K,
+                               const int32_t *ids, int topk, int mode, int T, void *y,
+                               hipStream_t s) {
+  switch (mode) {
+    case FP_MXFP4:
+      return gather_fp_rows_dtype<FP_MXFP4>(x, x_dtype, Tk, codes, scales, E, N, K, ids, topk, T, y, s);
+    case FP_NVFP4:
+      return gather_fp_rows_dtype<FP_NVFP4>(x, x_dtype, Tk, codes, scales, E, N, K, ids, topk, T, y, s);
+    case FP_MXFP8:
+      return gather_fp_rows_dtype<FP_MXFP8>(x, x_dtype, Tk, codes, scales, E, N, K, ids, topk, T, y, s);
   }
   return hipErrorInvalidValue;
 }

@@ -97,5 +97,10 @@ hipError_t launch_qmv_fp(const void *x, int x_dtype, const uint32_t *codes, cons
 hipError_t launch_mm_fp_rows(const void *x, int x_dtype, int64_t M, const uint32_t *codes,
                              const uint8_t *scales, int64_t N, int64_t K, int mode, int T, void *y,
                              hipStream_t s);
+// y[t, j, :] = x[t] @ W_{ids[t, j]}^T, block-scaled experts W [E, N, K]
+hipError_t launch_gather_mm_fp(const void *x, int x_dtype, int64_t Tk, const uint32_t *codes,
+                               const uint8_t *scales, int64_t E, int64_t N, int64_t K,
+                               const int32_t *ids, int topk, int mode, int T, void *y,
+                               hipStream_t s);
 
 }  // namespace aq

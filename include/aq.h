@@ -343,6 +343,25 @@ aq_status aq_matmul_fp(const void *x, aq_dtype x_dtype, int64_t M, const uint32_
                        const uint8_t *scales, int64_t N, int64_t K, aq_fp_mode mode,
                        int tensor_exp, void *y, void *stream);
 
+/* Mixture-of-experts gather of the block-scaled product ("Quantization",
+ * metalworking: gather variants of the kernels for MoE experts):
+ * y[t, j, :] = x[t] @ W_{ids[t, j]}^T for every token t < T and slot
+ * j < topk, one output row per (token, slot), no routing weights.  x: device
+ * [T, K] in x_dtype (AQ_F16 or AQ_BF16); codes and scales: device, E
+ * experts' arrays of aq_quantize_fp back to back ([E, N, ...]); ids: device
+ * int32 [T, topk]; y: device [T, topk, N] in x_dtype.  An id outside
+ * [0, E) gives a zero row and reads no weights; experts no pair chose are
+ * never read.  Each expert's rows are read once per batch of 16 (token,
+ * slot) pairs routed to it, on the matrix cores as in aq_matmul_fp (the
+ * same sums, the same rounding).  AQ_ERR_INVALID_ARG for T, E or topk
+ * below 1 or a bad mode, tensor exponent or pointer; AQ_ERR_UNSUPPORTED for
+ * K not a multiple of 32 or past 49152, E > 65535, or x or the scale array
+ * past 2^31 bytes. */
+aq_status aq_gather_matmul_fp(const void *x, aq_dtype x_dtype, int64_t T, const uint32_t *codes,
+                              const uint8_t *scales, int64_t E, int64_t N, int64_t K,
+                              const int32_t *ids, int topk, aq_fp_mode mode, int tensor_exp,
+                              void *y, void *stream);
+
 /* Which kernel aq_qmv_fp launches for this shape and mode, as text (as
  * aq_qmv_describe does); -1 for arguments aq_qmv_fp would reject. */
 int aq_qmv_fp_describe(int64_t N, int64_t K, aq_fp_mode mode, aq_dtype x_dtype, char *buf,

@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("aq_quantize", "aq_quantize_mse", "aq_dequantize", "aq_qmv", "aq_qmm", "aq_gather_qmv",
               "aq_quantized_matmul", "aq_codes_words", "aq_qweight_bytes", "aq_status_string",
-              "aq_quantize_fp", "aq_dequantize_fp", "aq_qmv_fp", "aq_matmul_fp"):
+              "aq_quantize_fp", "aq_dequantize_fp", "aq_qmv_fp", "aq_matmul_fp", "aq_gather_matmul_fp"):
         assert n in names
 
 
@@ -284,6 +284,24 @@ def test_fp_mode_argument_errors(lib):
     assert mm(mode=NV4, K=48) == UNSUPPORTED
     assert mm(M=16 * 65535 + 1) == UNSUPPORTED
     assert mm(M=1, K=33) == INVALID       # one row: the decode product's checks
+    g = lambda **k: lib.aq_gather_matmul_fp(k.get("x", P), k.get("dt", F16), k.get("T", 4),
+                                            k.get("codes", P), k.get("scales", P), k.get("E", 3),
+                                            k.get("N", 4), k.get("K", 64), k.get("ids", P),
+                                            k.get("topk", 2), k.get("mode", MX4), k.get("T_", 0),
+                                            k.get("y", P), None)
+    assert g(T=0) == INVALID
+    assert g(E=0) == INVALID
+    assert g(topk=0) == INVALID
+    assert g(dt=F32) == INVALID
+    assert g(K=33) == INVALID
+    assert g(mode=4) == INVALID
+    assert g(T_=1) == INVALID             # the mx modes take no tensor scale
+    assert g(ids=None) == INVALID
+    assert g(ids=MIS) == ALIGN
+    assert g(y=MIS) == ALIGN
+    assert g(K=49152 + 32) == UNSUPPORTED
+    assert g(E=65536) == UNSUPPORTED
+    assert g(mode=NV4, K=48) == UNSUPPORTED
     buf = ctypes.create_string_buffer(96)
     assert lib.aq_qmv_fp_describe(4096, 49152 + 32, MX4, F16, buf, 96) == -1
     assert lib.aq_qmv_fp_describe(4096, 100, MX4, F16, buf, 96) == -1

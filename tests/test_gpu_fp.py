@@ -310,6 +310,68 @@ def test_matmul_fp_one_row_is_qmv(aq, mode):
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+# ---- the mixture-of-experts gather --------------------------------------------------------
+def _gather_check(aq, mode, E, N, K, T, topk, xdt, seed, ids=None):
+    """Experts quantized by the oracle; y_ref[t, j] = x[t] @ W_ids[t, j]^T with
+    the oracle's exact weights (a zero row for an id outside [0, E))."""
+    import torch
+    ws = [inputs.weights(N, K, seed=seed, key=(e, N, K)) for e in range(E)]
+    T_exp = _tensor_exp(np.concatenate(ws), mode)
+    cs, ss, wx = [], [], []
+    for w in ws:
+        c, s = _oracle_quantize(w, mode, T_exp)
+        cs.append(c)
+        ss.append(s)
+        wx.append(_oracle_exact(c, s, K, mode, T_exp))
+    if ids is None:
+        ids = inputs.expert_ids(T, E, topk, seed=seed)
+    xb = inputs.activations(T, K, xdt, seed=seed, key=(T, K))
+    xf = inputs.from_bits(xb, xdt)
+    y_ref = np.zeros((T, topk, N))
+    A = np.zeros((T, topk, N))
+    for t in range(T):
+        for j in range(topk):
+            e = int(ids[t, j])
+            if 0 <= e < E:
+                y_ref[t, j], A[t, j] = (v[0] for v in oracle.matmul_dense(xf[t:t + 1], wx[e]))
+    codes = torch.from_numpy(np.stack(cs).view(np.int32)).cuda()
+    scales = torch.from_numpy(np.stack(ss)).cuda()
+    y = aq.aq_gather_matmul_fp(bits_to_dev(xb, xdt), codes, scales, to_dev(ids), mode, T_exp)
+    assert tuple(y.shape) == (T, topk, N)
+    got = out_to_f64(y)
+    ok, ratio = oracle.within_tolerance(got, y_ref, A)
+    assert ok, f"gather_matmul_fp {mode} E{E} N{N} K{K} T{T}: worst error/bound = {ratio:.3f}"
+    bad = (ids < 0) | (ids >= E)
+    assert np.all(got[bad] == 0), "rows of ids outside the table must be zero"
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+def test_gather_matmul_fp(aq, mode, xdt):
+    """8 experts, 40 tokens top-3 (about 15 pairs per expert: one batch of 16
+    or two), N not a multiple of the 32-row workgroup, a partial last step."""
+    _gather_check(aq, mode, 8, 100, 2080, 40, 3, xdt, seed=80)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_gather_matmul_fp_crowded_and_bad_ids(aq, mode):
+    """Every token on expert 1 (several batches of 16 and more than 256 ids,
+    so several id rounds), one expert never chosen, and ids outside the
+    table (zero rows)."""
+    T, topk, E = 100, 3, 4
+    ids = np.full((T, topk), 1, dtype=np.int32)
+    ids[:, 1] = np.arange(T) % 2 * 2          # experts 0 and 2
+    ids[5, 2], ids[17, 0], ids[63, 1] = -1, 4, 1 << 30
+    _gather_check(aq, mode, E, 70, 544, T, topk, "f16", seed=81, ids=ids)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_gather_matmul_fp_moe_shape(aq, mode):
+    """The MoE workload's expert shape ([1408, 2048]) with 16 experts, 32
+    tokens top-6."""
+    _gather_check(aq, mode, 16, 1408, 2048, 32, 6, "f16", seed=82)
+
+
 # ---- the prefill-size matrix ----------------------------------------------------------
 @pytest.fixture(scope="module")
 def prefill_weights():
