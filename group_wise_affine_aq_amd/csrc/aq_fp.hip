@@ -1,5 +1,6 @@
 // aq_fp.hip -- the block-scaled float modes mxfp4, nvfp4 and mxfp8, for
-// gfx950: quantize, dequantize and the M = 1 matrix-vector product.
+// gfx950: quantize, dequantize, the M = 1 matrix-vector product, the
+// product for 2 and more rows of x and the mixture-of-experts gather.
 //
 // The modes (MLX "Quantization", the paragraph on the newer modes;
 // "Quantizing a Model for MLX", "Modes, bits and mixed recipes": groups of
@@ -36,6 +37,8 @@
 // of the affine decode kernel: x resident in registers, a ring of chunk
 // loads per wave across row boundaries, rows parked in LDS; a chunk (32
 // codes) is dotted with x by v_dot2 in binary32 and scaled once per group.
+// From two rows of x on (and for the gather) the products run on the
+// matrix cores, each group's MFMA result scaled once (see mm_fp_rows_kernel).
 #include "aq_device.hpp"
 #include "aq_internal.hpp"
 
