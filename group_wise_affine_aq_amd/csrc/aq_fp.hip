@@ -716,13 +716,34 @@ __device__ __forceinline__ fp_u4 codes_to_b(uint32_t w0, uint32_t w1) {
   return b;
 }
 
-// One pass of a workgroup over its R blocks of 16 rows of W against 16 rows
-// of x: lane (n16, h) gets the byte offset xro of x row n16 in rx
-// (kFpOutside for a missing row: it reads as zero); srow0 is the block's
-// first row in the scale array rs.  Leaves the x rows x W rows sums of the
-// wave's K range in part[wave] (entry [b][n][m] for W row 16 b + n, x row m)
-// and meets the other waves at a barrier; the caller adds the W partial sums.
-template <int MODE, typename XT, int W, int R, int D>
+// DPP row_ror: lane l of each row of 16 lanes receives the value of lane
+// (l + 16 - K16) % 16 of the same row
+template <int K16>
+__device__ __forceinline__ fp_u4 fp_row_ror(fp_u4 v) {
+  if constexpr (K16 == 0) {
+    return v;
+  } else {
+    constexpr int ctl = 0x120 + K16;
+    fp_u4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      r[i] = (uint32_t)__builtin_amdgcn_mov_dpp((int)v[i], ctl, 0xF, 0xF, false);
+    return r;
+  }
+}
+
+// One pass of a workgroup over its R blocks of 16 rows of W against up to
+// XR rows of x: lane (n16, h) gets the byte offset xro of x row n16 % XR in
+// rx (kFpOutside for a missing row: it reads as zero); srow0 is the block's
+// first row in the scale array rs.  XR = 8 or 4 (at most that many rows of
+// x): the A-operand rows XR..15 only feed discarded output rows, so one
+// 16-byte x load carries 16 / XR chunks (lanes XR s .. XR s + XR - 1 of each
+// row of 16 hold chunk slot s) and a row rotation moves a slot into lanes
+// 0 .. XR - 1: a half or a quarter of the x loads.
+// Leaves the x rows x W rows sums of the wave's K range in part[wave] (entry
+// [b][n][m] for W row 16 b + n, x row m; rows m >= XR hold no result) and
+// meets the other waves at a barrier; the caller adds the W partial sums.
+template <int MODE, typename XT, int W, int R, int D, int XR>
 __device__ __forceinline__ void fp_rows_pass(__amdgpu_buffer_rsrc_t rx, uint32_t xro,
                                              __amdgpu_buffer_rsrc_t rc,
                                              __amdgpu_buffer_rsrc_t rs, int64_t srow0,
@@ -730,6 +751,7 @@ __device__ __forceinline__ void fp_rows_pass(__amdgpu_buffer_rsrc_t rx, uint32_t
   using CF = chunk_fmt<MODE>;
   constexpr int CB = 16 * CF::VW;      // code bytes per chunk and row
   constexpr int NSW = CF::SB + 1;      // scale dwords loaded per row and step
+  constexpr int NXL = 16 / XR;         // chunks per x load
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n16 = lane & 15, h = lane >> 4;
   const int nch = (int)(K >> 5);
@@ -742,7 +764,7 @@ __device__ __forceinline__ void fp_rows_pass(__amdgpu_buffer_rsrc_t rx, uint32_t
   struct Step {
     uint32_t cw[R][4 * CF::VW];  // chunk c0 + h of row 16 b + n16, as loaded
     uint32_t sc[R][NSW];         // dwords holding the row's scale bytes of the step
-    fp_u4 xl[4];                 // codes 8h .. 8h + 7 of chunk c0 + j of x row n16
+    fp_u4 xl[4 / NXL];           // codes 8h .. 8h + 7 of chunk c0 + NXL q + n16 / XR of x row n16 % XR
   };
   auto load = [&](Step &st, int s) {
     const bool in = s < s1;  // uniform; past the range every offset lies outside
@@ -764,11 +786,11 @@ __device__ __forceinline__ void fp_rows_pass(__amdgpu_buffer_rsrc_t rx, uint32_t
         st.sc[b][i] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(sa + 4u * i), 0, 0);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = c0 + j;
+    for (int q = 0; q < 4 / NXL; ++q) {
+      const int c = c0 + NXL * q + n16 / XR;
       const uint32_t off =
           in && c < nch ? (uint32_t)(xro + ((int64_t)c * 32 + 8 * h) * 2) : kFpOutside;
-      st.xl[j] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0);
+      st.xl[q] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)off, 0, 0);
     }
   };
 
@@ -778,6 +800,19 @@ __device__ __forceinline__ void fp_rows_pass(__amdgpu_buffer_rsrc_t rx, uint32_t
   const fp_u4 zero4 = {0u, 0u, 0u, 0u};
   auto compute = [&](const Step &st, int s) {
     const int c0 = 4 * s;
+    fp_u4 xa[4];  // the A operand of chunk c0 + j: x rows in lanes 0 .. XR - 1
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (NXL == 1) {
+        xa[j] = st.xl[j];
+      } else if constexpr (NXL == 2) {
+        xa[j] = (j & 1) ? fp_row_ror<8>(st.xl[j >> 1]) : st.xl[j >> 1];
+      } else {  // chunk j in lanes 4j .. 4j + 3
+        xa[j] = j == 0 ? st.xl[0]
+              : j == 1 ? fp_row_ror<12>(st.xl[0])
+              : j == 2 ? fp_row_ror<8>(st.xl[0]) : fp_row_ror<4>(st.xl[0]);
+      }
+    }
 #pragma unroll
     for (int b = 0; b < R; ++b) {
       uint32_t e[4], o[4];  // fp4: word h of each chunk; fp8: words 2h and 2h + 1
@@ -804,14 +839,14 @@ __device__ __forceinline__ void fp_rows_pass(__amdgpu_buffer_rsrc_t rx, uint32_t
           const uint32_t sw = j < 2 ? sl : sh2;
           const fp_h2 g = (j & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, true)
                                   : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
-          const fp_u4 xa = h < 2 ? st.xl[j] : zero4, xb = h < 2 ? zero4 : st.xl[j];
-          const fp_f4 t0 = mfma_x16<XT>(xa, bw), t1 = mfma_x16<XT>(xb, bw);
+          const fp_u4 x0 = h < 2 ? xa[j] : zero4, x1 = h < 2 ? zero4 : xa[j];
+          const fp_f4 t0 = mfma_x16<XT>(x0, bw), t1 = mfma_x16<XT>(x1, bw);
           const float g0 = live ? (float)g[0] : 0.f, g1 = live ? (float)g[1] : 0.f;
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[b][i] = __builtin_fmaf(t1[i], g1, __builtin_fmaf(t0[i], g0, acc[b][i]));
         } else {
           const float g = live ? __builtin_ldexpf(1.0f, (int)((sl >> (8 * j)) & 0xFFu) - 127) : 0.f;
-          const fp_f4 t = mfma_x16<XT>(st.xl[j], bw);
+          const fp_f4 t = mfma_x16<XT>(xa[j], bw);
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[b][i] = __builtin_fmaf(t[i], g, acc[b][i]);
         }
@@ -836,7 +871,7 @@ __device__ __forceinline__ void fp_rows_pass(__amdgpu_buffer_rsrc_t rx, uint32_t
   __syncthreads();
 }
 
-template <int MODE, typename XT, int W, int R, int D>
+template <int MODE, typename XT, int W, int R, int D, int XR>
 __global__ __launch_bounds__(64 * W) void mm_fp_rows_kernel(const uint16_t *__restrict__ x,
                                                             int64_t M,
                                                             const uint32_t *__restrict__ codes,
@@ -857,8 +892,9 @@ __global__ __launch_bounds__(64 * W) void mm_fp_rows_kernel(const uint16_t *__re
   // the dword holding its last byte lies inside its allocation)
   const __amdgpu_buffer_rsrc_t rs = fp_rsrc(scales, (N * rsb + 3) & ~(int64_t)3);
   const __amdgpu_buffer_rsrc_t rx = fp_rsrc(x + m0 * K, mrows * K * 2);
-  fp_rows_pass<MODE, XT, W, R, D>(rx, n16 < mrows ? (uint32_t)(n16 * K * 2) : kFpOutside, rc, rs,
-                                  row0, K, part);
+  const int xm = n16 % XR;
+  fp_rows_pass<MODE, XT, W, R, D, XR>(rx, xm < mrows ? (uint32_t)(xm * K * 2) : kFpOutside, rc,
+                                      rs, row0, K, part);
   for (int t = threadIdx.x; t < R * 256; t += 64 * W) {
     const int b = t >> 8, m = (t >> 4) & 15, nn = t & 15;
     float v = 0.f;
@@ -917,7 +953,7 @@ __global__ __launch_bounds__(64 * W) void gather_fp_rows_kernel(
       const int nb = n - b0 < 16 ? n - b0 : 16;
       const uint32_t xro = n16 < nb ? (uint32_t)(((t0 + list[b0 + n16]) / topk) * K * 2)
                                     : kFpOutside;
-      fp_rows_pass<MODE, XT, W, R, D>(rx, xro, rc, rs, e * N + row0, K, part);
+      fp_rows_pass<MODE, XT, W, R, D, 16>(rx, xro, rc, rs, e * N + row0, K, part);
       for (int t = threadIdx.x; t < R * 256; t += 64 * W) {
         const int b = t >> 8, m = (t >> 4) & 15, nn = t & 15;
         float v = 0.f;
@@ -1019,7 +1055,7 @@ hipError_t qmv_fp_mode(const void *x, int x_dtype, const uint32_t *codes, const 
 // of loads in flight per wave
 template <int MODE> constexpr int kFewDepth = 2;
 
-template <int MODE, typename XT, int R>
+template <int MODE, typename XT, int R, int XR>
 hipError_t mm_fp_rows_r(const void *x, int64_t M, const uint32_t *codes, const uint8_t *scales,
                         int64_t N, int64_t K, int T, void *y, hipStream_t s) {
   constexpr int D = kFewDepth<MODE>;
@@ -1031,7 +1067,7 @@ hipError_t mm_fp_rows_r(const void *x, int64_t M, const uint32_t *codes, const u
   while (w > 2 && steps < 4 * w) w /= 2;
   const dim3 grid((unsigned)blocks, (unsigned)slices);
 #define AQ_MMFP(WW)                                                                           \
-  hipLaunchKernelGGL((mm_fp_rows_kernel<MODE, XT, WW, R, D>), grid, dim3(64 * WW), 0, s,      \
+  hipLaunchKernelGGL((mm_fp_rows_kernel<MODE, XT, WW, R, D, XR>), grid, dim3(64 * WW), 0, s,  \
                      (const uint16_t *)x, M, codes, scales, N, K, T, (uint16_t *)y);          \
   break;
   switch (w) {
@@ -1046,9 +1082,15 @@ hipError_t mm_fp_rows_r(const void *x, int64_t M, const uint32_t *codes, const u
 template <int MODE, typename XT>
 hipError_t mm_fp_rows_mode(const void *x, int64_t M, const uint32_t *codes, const uint8_t *scales,
                            int64_t N, int64_t K, int T, void *y, hipStream_t s) {
-  if ((N + 31) / 32 * ((M + 15) / 16) >= device_cus())
-    return mm_fp_rows_r<MODE, XT, 2>(x, M, codes, scales, N, K, T, y, s);
-  return mm_fp_rows_r<MODE, XT, 1>(x, M, codes, scales, N, K, T, y, s);
+  const bool two = (N + 31) / 32 * ((M + 15) / 16) >= device_cus();
+  if (M <= 4)  // up to 4 rows of x: four chunks per x load
+    return two ? mm_fp_rows_r<MODE, XT, 2, 4>(x, M, codes, scales, N, K, T, y, s)
+               : mm_fp_rows_r<MODE, XT, 1, 4>(x, M, codes, scales, N, K, T, y, s);
+  if (M <= 8)  // up to 8 rows of x: two chunks per x load
+    return two ? mm_fp_rows_r<MODE, XT, 2, 8>(x, M, codes, scales, N, K, T, y, s)
+               : mm_fp_rows_r<MODE, XT, 1, 8>(x, M, codes, scales, N, K, T, y, s);
+  return two ? mm_fp_rows_r<MODE, XT, 2, 16>(x, M, codes, scales, N, K, T, y, s)
+             : mm_fp_rows_r<MODE, XT, 1, 16>(x, M, codes, scales, N, K, T, y, s);
 }
 
 // gather: workgroups of 32 rows of one expert (16 when that leaves compute
