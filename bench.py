@@ -639,6 +639,17 @@ def _quant_dequant(aq, inputs, dev, stream, legs=None):
     res["quantize_mse"] = {"steps": steps, "avg_us": round(us, 2), "bytes": nb,
                            "gbs": round(nb / (us * 1e-6) / 1e9, 1),
                            "weights_per_s": round(N * K / (us * 1e-6), 1)}
+    # a second denominator for these read-and-write passes: torch's device
+    # copy (the runtime's copy kernel) of 512 MiB into another 512 MiB
+    src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    us = _graph_us(torch, stream, [lambda: dst.copy_(src)] * 4)
+    copy_gbs = 2 * src.numel() / (us * 1e-6) / 1e9
+    res["device_copy"] = {"bytes": 2 * src.numel(), "avg_us": round(us, 2),
+                          "gbs": round(copy_gbs, 1)}
+    for key in ("quantize", "dequantize_bf16", "quantize_zp"):
+        res[key]["frac_of_device_copy"] = round(res[key]["gbs"] / copy_gbs, 3)
+    del src, dst
     if legs is not None:
         # the oracle quantizer on the first 1024 rows of the same W
         import oracle
@@ -655,8 +666,8 @@ def _quant_dequant(aq, inputs, dev, stream, legs=None):
           f"({res['quantize_zp']['gbs']} GB/s)", file=sys.stderr, flush=True)
     print(f"# quantize {res['quantize']['avg_us']:.1f} us ({res['quantize']['gbs']} GB/s), "
           f"dequantize {res['dequantize_bf16']['avg_us']:.1f} us ({res['dequantize_bf16']['gbs']} GB/s), "
-          f"range-search quantize ({steps} ranges) {res['quantize_mse']['avg_us']:.1f} us",
-          file=sys.stderr, flush=True)
+          f"range-search quantize ({steps} ranges) {res['quantize_mse']['avg_us']:.1f} us; "
+          f"device copy of 512 MiB {res['device_copy']['gbs']} GB/s", file=sys.stderr, flush=True)
     del w, c, s_, b, out
     torch.cuda.synchronize()
     return res
