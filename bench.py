@@ -236,6 +236,26 @@ def main():
         print(f"# plain read of {m['wbytes']} B: {ps['read_ceiling_us']:.2f} us "
               f"({ps['read_ceiling_gbs']} GB/s); kernel at {ps['frac_of_read_ceiling']:.2f} of it",
               file=sys.stderr, flush=True)
+    # context: the same product with dense bf16 weights (torch's F.linear ->
+    # hipBLASLt), cold copies, on the two 33 MB shapes (112 MB of bf16 each)
+    import torch.nn.functional as F
+    for ps, m in zip(per_shape, mats):
+        if m["N"] * m["K"] < 4096 * 14336:
+            continue
+        nb = m["N"] * m["K"] * 2
+        dcopies = max(2, math.ceil(COLD_BYTES / nb))
+        ws = [torch.empty((m["N"], m["K"]), dtype=torch.bfloat16, device=dev).normal_(0, 0.02)
+              for _ in range(dcopies)]
+        xb = m["x"].to(torch.bfloat16)
+        F.linear(xb, ws[0])  # library set-up outside the capture
+        torch.cuda.synchronize()
+        us = _graph_us(torch, stream, [lambda wc=wc: F.linear(xb, wc) for wc in ws] * 2)
+        ps["dense_bf16_linear_us"] = round(us, 3)
+        ps["speedup_vs_dense_bf16"] = round(us / ps["avg_us"], 2)
+        print(f"# dense bf16 F.linear {m['N']}x{m['K']} ({nb} B): {us:.2f} us; the 4-bit kernel is "
+              f"{us / ps['avg_us']:.2f}x faster", file=sys.stderr, flush=True)
+        del ws
+        torch.cuda.synchronize()
     # the dominant kernel: the instantiation with the most device time per step
     by_kernel = {}
     for ps in per_shape:
