@@ -236,6 +236,13 @@ def main():
         print(f"# plain read of {m['wbytes']} B: {ps['read_ceiling_us']:.2f} us "
               f"({ps['read_ceiling_gbs']} GB/s); kernel at {ps['frac_of_read_ceiling']:.2f} of it",
               file=sys.stderr, flush=True)
+    # the sustained read rate: the same plain reads over 1 GiB per launch, where
+    # the fixed cost of a launch no longer weighs
+    big_us = _read_ceiling_us(aq, torch, 1 << 30, stream)
+    sustained = {"bytes": 1 << 30, "avg_us": round(big_us, 2),
+                 "gbs": round((1 << 30) / (big_us * 1e-6) / 1e9, 1)}
+    print(f"# plain read of 1 GiB: {big_us:.1f} us ({sustained['gbs']} GB/s)", file=sys.stderr,
+          flush=True)
     # context: the same product with dense bf16 weights (torch's F.linear ->
     # hipBLASLt), cold copies, on the two 33 MB shapes (112 MB of bf16 each)
     import torch.nn.functional as F
@@ -284,6 +291,7 @@ def main():
                    "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1)},
         "roofline": roofline,
         "per_shape": per_shape,
+        "sustained_read_1gib": sustained,
     }
 
     if args.copy_probe:
