@@ -259,12 +259,12 @@ def _mm_check(aq, mode, M, N, K, xdt, seed, w=None, T=None):
 
 
 @pytest.mark.parametrize("mode", MODES)
-@pytest.mark.parametrize("M", [2, 3, 8, 16, 17, 40])
+@pytest.mark.parametrize("M", [2, 3, 4, 5, 8, 9, 16, 17, 40, 300])
 @pytest.mark.parametrize("xdt", ["f16", "bf16"])
 def test_matmul_fp_rows(aq, mode, M, xdt):
-    """M rows of x in slices of 16 (17 and 40: a partial last slice); N not a
-    multiple of the 32-row workgroup; K = 2080: 65 chunks, a partial last
-    step of 4 chunks."""
+    """M rows of x in slices of 16 (17, 40, 300: a partial last slice), x loads
+    carrying 4 chunks (M <= 4), 2 (M <= 8) or 1; N not a multiple of the
+    32-row workgroup; K = 2080: 65 chunks, a partial last step of 4 chunks."""
     _mm_check(aq, mode, M, 100, 2080, xdt, seed=70)
 
 
