@@ -559,7 +559,10 @@ __global__ __launch_bounds__(64 * W) void qmvm_kernel(const uint16_t *__restrict
   blk.setup(codes + row0 * (K >> 5) * BITS, nrows, K, kw, wave, lane, lds,
             mk_rsrc(x, (int64_t)M * K * 2));  // rows of x past M read as zero
   const uint32_t xro = (uint32_t)((int64_t)((lane & 15) % Blk::XRS) * K * 2);
-  constexpr int D = kDepth<BITS>;
+  // 4-bit single-block workgroups of 8 waves (long rows, see qmvm_shape) keep
+  // a third step in flight: measured at 4096 x 14336, M = 2 .. 8, 11.3 .. 14.2
+  // us against 12.2 .. 14.3 with two (and 11.5 .. 14.9 on 16 waves)
+  constexpr int D = BITS == 4 && R == 1 && W == 8 && XR < 16 ? 3 : kDepth<BITS>;
   typename Blk::Step st[D];
   // staging first, then the first steps' loads: one round trip covers both
   Blk::stage_sb(scales + row0 * gpr, biases ? biases + row0 * gpr : nullptr, nrows, gpr, lds, wave, lane);
@@ -801,6 +804,14 @@ void qmvm_shape(int M, int bits, int64_t N, int64_t K, int G, int &R, int &W, in
       : rowblocks * 4 >= target ? 4
       : rowblocks * 8 >= target ? 8 : 16;
   if (bits == 8 && W > 2) W /= 2;
+  // Long rows at 4-bit: halve the waves when that gives each wave 8 steps or
+  // more and still leaves 2 waves per SIMD (4096 x 14336: 16 waves of 7 steps
+  // -> 8 waves of 14, with three steps in flight, qmvm_kernel; M = 2 / 4 / 8
+  // 11.3 / 11.8 / 14.2 us against 11.5 / 12.6 / 14.9)
+  const int64_t steps = (K + kStepK - 1) / kStepK;
+  if (bits == 4 && XR < 16 && W == 16 && (steps + 15) / 16 < 8 && (steps + 7) / 8 >= 8 &&
+      rowblocks * 8 >= target / 2)
+    W = 8;
 }
 
 hipError_t launch_qmvm(const void *x, int x_dtype, int M, const uint32_t *codes,
