@@ -442,6 +442,22 @@ def test_qmv_few_rows_tall(aq, bits, G):
         _assert_close(y, y_ref, A, f"qmv tall b{bits} G{G} M{M}")
 
 
+def test_qmv_few_rows_long_rows(aq):
+    """Long rows at 4-bit: 8 waves per workgroup with three steps in flight
+    (rows ragged against 16, K ragged against the 128-code step, so the last
+    wave's range ends inside a step)."""
+    N, K, G, bits = 4100, 10016, 32, 4
+    assert "W=8," in aq.aq_qmv_describe(4, N, K, G, bits, "bf16")
+    _, (c, s, b) = _quantized(N, K, G, bits, seed=17)
+    dev = packed_to_dev(c, s, b)
+    for xdt in ("f16", "bf16"):
+        for M in (2, 4, 5, 8):
+            xb = inputs.activations(M, K, xdt, seed=17, key=(M,))
+            y_ref, A = oracle.matmul(inputs.from_bits(xb, xdt), c, s, b, K, G, bits)
+            y = aq.aq_qmv(bits_to_dev(xb, xdt), *dev, G, bits)
+            _assert_close(y, y_ref, A, f"qmv long rows M{M} {xdt}")
+
+
 @pytest.mark.parametrize("bits", [4, 8])
 @pytest.mark.parametrize("xdt,G,K", [("f16", 32, 2144), ("bf16", 32, 2144), ("bf16", 64, 2112),
                                      ("f16", 128, 384), ("f16", 64, 64)])
