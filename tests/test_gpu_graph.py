@@ -28,7 +28,7 @@ def aq():
 
 
 def _calls(aq):
-    """(name, output tensor, callable writing it) for one call of each kind."""
+    """(name, output tensor(s), callable writing them) for one call of each kind."""
     import torch
     N, K, G, bits = 300, 1024, 64, 4
     w = inputs.weights(N, K, seed=90, key=(90,))
@@ -63,7 +63,37 @@ def _calls(aq):
     yf = torch.empty((T, topk, N), dtype=torch.float16, device=xg.device)
     calls.append(("gather_matmul_fp", yf,
                   lambda: aq.aq_gather_matmul_fp(xg, fce, fse, ids, "mxfp4", 0, y=yf)))
+    # the quantizers, the embedding, the prefill-size gather and the
+    # block-scaled quantize / dequantize
+    wd = to_dev(w)
+    qo = aq.aq_quantize(wd, G, bits)
+    calls.append(("quantize", qo, lambda: aq.aq_quantize(wd, G, bits, *qo)))
+    mo = aq.aq_quantize_mse(wd, G, bits, 5)
+    calls.append(("quantize_mse", mo, lambda: aq.aq_quantize_mse(wd, G, bits, 5, *mo)))
+    zo = aq.aq_quantize_zp(wd, G, bits)
+    calls.append(("quantize_zp", zo, lambda: aq.aq_quantize_zp(wd, G, bits, *zo)))
+    tok = to_dev(inputs.token_ids(33, N, seed=93))
+    ye = torch.empty((33, K), dtype=torch.bfloat16, device=xg.device)
+    calls.append(("embedding", ye, lambda: aq.aq_embedding(tok, c, s, b, G, bits, out=ye)))
+    Tq = 40
+    idq = to_dev(inputs.expert_ids(Tq, E, topk, seed=94))
+    xq = bits_to_dev(inputs.activations(Tq, K, "bf16", seed=94, key=(Tq,)), "bf16")
+    yq2 = torch.empty((Tq, topk, N), dtype=torch.bfloat16, device=xg.device)
+    calls.append(("gather_qmm", yq2,
+                  lambda: aq.aq_gather_qmm(xq, dce, dse, dbe, idq, G, bits, y=yq2)))
+    for mode, t in (("mxfp4", 0), ("nvfp4", -12), ("mxfp8", 0)):
+        fo = aq.aq_quantize_fp(wd, mode, t)
+        calls.append((f"quantize_fp {mode}", fo,
+                      lambda mode=mode, t=t, fo=fo: aq.aq_quantize_fp(wd, mode, t, *fo)))
+        yd = torch.empty((N, K), dtype=torch.bfloat16, device=xg.device)
+        calls.append((f"dequantize_fp {mode}", yd,
+                      lambda mode=mode, t=t, fo=fo, yd=yd:
+                      aq.aq_dequantize_fp(*fo, K, mode, t, out=yd)))
     return calls
+
+
+def _outs(o):
+    return list(o) if isinstance(o, (tuple, list)) else [o]
 
 
 def test_graph_replays_match_eager(aq):
@@ -72,7 +102,7 @@ def test_graph_replays_match_eager(aq):
     for _, _, f in calls:
         f()
     torch.cuda.synchronize()
-    eager = [y.clone() for _, y, _ in calls]
+    eager = [[t.clone() for t in _outs(o)] for _, o, _ in calls]
     stream = torch.cuda.Stream()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
@@ -85,12 +115,14 @@ def test_graph_replays_match_eager(aq):
     torch.cuda.synchronize()
     junk = torch.empty(1 << 20, dtype=torch.float32, device="cuda")
     for rep in range(4):
-        for _, y, _ in calls:  # outputs overwritten between replays
-            y.view(torch.int16).fill_(0x7E00 + rep)
+        for _, o, _ in calls:  # outputs overwritten between replays
+            for t in _outs(o):
+                t.view(torch.uint8).fill_(0x7E + rep)
         junk.uniform_()  # other work on the default stream
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        for (name, y, _), ref in zip(calls, eager):
-            assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), \
-                f"replay {rep}: {name} differs from the eager call"
+        for (name, o, _), refs in zip(calls, eager):
+            for t, ref in zip(_outs(o), refs):
+                assert torch.equal(t.view(torch.uint8), ref.view(torch.uint8)), \
+                    f"replay {rep}: {name} differs from the eager call"
