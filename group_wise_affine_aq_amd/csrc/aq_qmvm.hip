@@ -773,9 +773,21 @@ void qmvm_shape(int M, int bits, int64_t N, int64_t K, int G, int &R, int &W, in
        : (N + 31) / 32 * ((M + 31) / 32) >= device_cus() ? 32 : 16;
   const int64_t S = XR >= 16 ? (M + XR - 1) / XR : 1;  // slices of XR x rows
   if (XR >= 16) {
-    // 16 or 32 rows per slot: two blocks of 16 rows over 4 waves whenever
-    // that still gives a workgroup per compute unit (measured best at
-    // 14336 x 4096 from M = 9 and at 4096 x 14336 from M = 17, both widths)
+    // 16 or 32 rows per slot: four blocks of 16 rows over 4 waves while the
+    // 64-row workgroups still give at least 3/4 of one per compute unit (each
+    // x load then serves 64 rows of W: at 14336 x 4096, M = 16 / 64, 4-bit
+    // 15.9 / 43.9 -> 14.9 / 33.4 us, 8-bit 20.6 / 50.3 -> 18.6 / 41.6; 8
+    // waves were slower; at 4096 x 14336, 64 or 128 workgroups, 1.3-1.8x
+    // slower than two blocks)
+    if ((N + 63) / 64 * S * 4 >= 3 * device_cus() &&
+        qmvm_lds_bytes(4, 4, K, G, XR) <= kMaxStagedLds) {
+      R = 4;
+      W = 4;
+      return;
+    }
+    // else two blocks of 16 rows over 4 waves whenever that still gives a
+    // workgroup per compute unit (measured best at 14336 x 4096 from M = 9
+    // and at 4096 x 14336 from M = 17, both widths)
     if ((N + 31) / 32 * S >= device_cus() && qmvm_lds_bytes(4, 2, K, G, XR) <= kMaxStagedLds) {
       R = 2;
       W = 4;
@@ -827,6 +839,9 @@ hipError_t launch_qmvm(const void *x, int x_dtype, int M, const uint32_t *codes,
     default: return qmvm_go<T, B, 16, XR, RR>(x, M, codes, scales, biases, N, K, G, y, s); \
   }
 #define AQ_QMVM_R(T, B, XR) \
+  if constexpr (XR >= 16) { \
+    if (R == 4) return qmvm_go<T, B, 4, XR, 4>(x, M, codes, scales, biases, N, K, G, y, s); \
+  } \
   if (R == 2) { \
     return qmvm_go<T, B, 4, XR, 2>(x, M, codes, scales, biases, N, K, G, y, s); \
   } else { AQ_QMVM_W(T, B, XR, 1) }

@@ -478,16 +478,19 @@ def test_matmul_few_rows_sliced(aq, xdt, bits, G, K):
 
 @pytest.mark.parametrize("bits,G", [(4, 64), (8, 128), (8, 32), (4, 32)])
 def test_matmul_few_rows_sliced_tall(aq, bits, G):
-    """Tall matrices (two 16-row blocks per workgroup) at 16..64 rows: past 16
+    """Tall matrices at 16..64 rows: two or four 16-row blocks per workgroup
+    (four once the 64-row workgroups fill 3/4 of the chip: 8200 rows at 40 and
+    64 rows of x, 12300 rows at 16 and 20; rows ragged against both); past 16
     rows two sets of 16 x rows per wave (slices of 32; 40 rows leave the
     second slice's second set empty)."""
-    N, K = 8200, 256
-    _, (c, s, b) = _quantized(N, K, G, bits, seed=22)
-    for M in (16, 24, 40, 64):
-        xb = inputs.activations(M, K, "f16", seed=22, key=(bits, G, M))
-        y_ref, A = oracle.matmul(inputs.from_bits(xb, "f16"), c, s, b, K, G, bits)
-        y = aq.aq_quantized_matmul(bits_to_dev(xb, "f16"), *packed_to_dev(c, s, b), G, bits)
-        _assert_close(y, y_ref, A, f"sliced tall b{bits} G{G} M{M}")
+    K = 256
+    for N, Ms in ((8200, (16, 24, 40, 64)), (12300, (16, 20))):
+        _, (c, s, b) = _quantized(N, K, G, bits, seed=22)
+        for M in Ms:
+            xb = inputs.activations(M, K, "f16", seed=22, key=(bits, G, M))
+            y_ref, A = oracle.matmul(inputs.from_bits(xb, "f16"), c, s, b, K, G, bits)
+            y = aq.aq_quantized_matmul(bits_to_dev(xb, "f16"), *packed_to_dev(c, s, b), G, bits)
+            _assert_close(y, y_ref, A, f"sliced tall {N} b{bits} G{G} M{M}")
 
 
 def test_qmv_unit_vectors(aq):
